@@ -1,0 +1,485 @@
+"""Pins that tie the CPU oracle to what the pages and the mathematics fix.
+
+Each ``pin_*`` takes a loaded oracle (``oracle.Oracle``) and raises
+AssertionError when the oracle disagrees with a closed form, an invariant, a
+special case, a value printed on the pages or a brute-force check. The same
+pins run against deliberately mutated oracle builds in
+``test_oracle_pins.py``: every planted mistake must trip at least one of them.
+
+Pages cited: K3 course notes, section "Attention Residual 深度残差" (K3 §9.x);
+"Attention Residuals" survey page on wineandchord.com (WC, by section name).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------------------
+# small helpers (no method arithmetic beyond what each pin states)
+# ----------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_via_torch(x32: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of fp32 values, rounded by torch (nearest-even)."""
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_normal(rng, shape, sigma=1.0) -> np.ndarray:
+    return f64_to_bf16_via_torch((rng.standard_normal(shape) * sigma).astype(np.float32))
+
+
+def widen(a: np.ndarray) -> np.ndarray:
+    return bf16_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def os2_merge(a, b):
+    """The pages' two-group merge (K3 §9.4 eq. OS2; WC merge_summary) on
+    (m, z, u) triples with u the unnormalised numerator."""
+    m = np.maximum(a[0], b[0])
+    sa, sb = np.exp(a[0] - m), np.exp(b[0] - m)
+    return m, sa * a[1] + sb * b[1], sa[..., None] * a[2] + sb[..., None] * b[2]
+
+
+def triple_from(out):
+    """(m, z, u) of a normalised aggregate: z = exp(lse - m), u = z * h."""
+    z = np.exp(out["lse"] - out["m"])
+    return out["m"], z, z[..., None] * out["h"]
+
+
+# ----------------------------------------------------------------------------
+# rounding
+# ----------------------------------------------------------------------------
+
+def pin_round_bf16_bruteforce(orc):
+    """bf16 rounding is nearest with ties to even: checked against the two
+    neighbouring bf16 values of every result, on exact midpoints, and against
+    torch's fp32 -> bf16 conversion."""
+    rng = np.random.default_rng(11)
+    mant = rng.uniform(1.0, 2.0, 4000)
+    expo = rng.integers(-140, 120, 4000)
+    x = np.ldexp(mant, expo)
+    # exact midpoints between consecutive bf16 values (ties)
+    base = rng.integers(0x0080, 0x7F00, 2000).astype(np.uint16)
+    mid = (bf16_to_f64(base) + bf16_to_f64(base + 1)) / 2.0
+    x = np.concatenate([x, mid])
+    bits = orc.round_to(x, "bf16").astype(np.int64)
+    r = bf16_to_f64(bits.astype(np.uint16))
+    up = bf16_to_f64((bits + 1).astype(np.uint16))
+    dn = bf16_to_f64(np.maximum(bits - 1, 0).astype(np.uint16))
+    err = np.abs(x - r)
+    assert np.all(err <= np.abs(x - up)), "bf16 rounding is not nearest (upper neighbour)"
+    ok_dn = (bits == 0) | (err <= np.abs(x - dn))
+    assert np.all(ok_dn), "bf16 rounding is not nearest (lower neighbour)"
+    tie = (err == np.abs(x - up)) | ((bits > 0) & (err == np.abs(x - dn)))
+    assert np.all(bits[tie] % 2 == 0), "bf16 ties are not rounded to even"
+    assert tie[-2000:].all(), "midpoints should be ties"
+    neg = orc.round_to(-x, "bf16").astype(np.int64)
+    assert np.array_equal(neg, bits | 0x8000), "bf16 rounding is not sign-symmetric"
+    x32 = rng.standard_normal(5000).astype(np.float32) * np.float32(37.0)
+    assert np.array_equal(orc.round_to(x32.astype(np.float64), "bf16"), f64_to_bf16_via_torch(x32))
+
+
+def pin_round_f32(orc):
+    """fp32 rounding equals numpy's nearest-even double -> float cast."""
+    rng = np.random.default_rng(12)
+    x = np.ldexp(rng.uniform(-2, 2, 5000), rng.integers(-100, 100, 5000))
+    assert np.array_equal(orc.round_to(x, "f32"), x.astype(np.float32))
+
+
+# ----------------------------------------------------------------------------
+# AGG (eqs. A1-A3)
+# ----------------------------------------------------------------------------
+
+def _cfg1_sources(rng, rows=16, D=256):
+    sig = (1.0, 3.0, 0.3, 10.0)  # per-source standard deviations of the single-aggregate workload
+    return [(rng.standard_normal((rows, D)) * s).astype(np.float32) for s in sig]
+
+
+def pin_zero_query_is_mean(orc):
+    """A zero query gives equal logits, so the output is the plain mean of the
+    sources (K3 §9.2 (3); WC reference check with torch.zeros)."""
+    rng = np.random.default_rng(1)
+    src = _cfg1_sources(rng)
+    gamma = rng.uniform(0.5, 1.5, 256).astype(np.float32)
+    out = orc.aggregate(src, np.zeros(256, np.float32), gamma, want_alpha=True)
+    mean = np.mean([s.astype(np.float64) for s in src], axis=0)
+    big = np.max(np.abs([s.astype(np.float64) for s in src]))
+    assert np.max(np.abs(out["h"] - mean)) <= 8 * np.finfo(np.float64).eps * big
+    assert np.all(out["m"] == 0.0) and np.allclose(out["lse"], math.log(4), rtol=0, atol=1e-15)
+    assert np.allclose(out["alpha"], 0.25, rtol=0, atol=1e-16)
+    # bf16 sources too
+    srcb = [bf16_normal(rng, (8, 64), s) for s in (1.0, 2.0, 0.5)]
+    outb = orc.aggregate(srcb, np.zeros(64, np.float32))
+    meanb = np.mean([bf16_to_f64(s) for s in srcb], axis=0)
+    assert np.max(np.abs(outb["h"] - meanb)) <= 1e-14
+
+
+def pin_single_source_identity(orc):
+    """One source: the softmax weight is exactly 1, so h equals the source bit
+    for bit and m = lse = its score (K3 §9.4 single-source triple)."""
+    rng = np.random.default_rng(2)
+    v = (rng.standard_normal((8, 32)) * 3).astype(np.float32)
+    w = (rng.standard_normal(32) * 0.5).astype(np.float32)
+    out = orc.aggregate([v], w)
+    assert np.array_equal(out["h"], v.astype(np.float64))
+    assert np.array_equal(out["m"], out["lse"])
+    assert np.array_equal(out["scale"], np.abs(v.astype(np.float64)))
+
+
+def pin_closed_form_scores(orc):
+    """Sources that are scaled one-hot vectors c_i * e_{d_i} have
+    mean_d(V^2) = c_i^2 / D, so their RMS-normalised copy is
+    sign(c_i) * e_{d_i} / sqrt(c_i^2/D + eps) * |c_i| and the score is
+    q[d_i] * c_i / sqrt(c_i^2/D + eps). The softmax over two sources is the
+    logistic function of the score difference (A1, A2; WC reference: eps
+    inside the root, mean over the hidden axis)."""
+    D = 16
+    q = np.linspace(-0.9, 1.3, D).astype(np.float32)
+    for eps in (0.0, 0.25, 3.0):
+        for (c0, d0, c1, d1) in [(2.0, 3, -0.5, 7), (4.0, 0, 4.0, 15), (0.125, 5, 8.0, 5)]:
+            V0 = np.zeros((1, D), np.float32); V0[0, d0] = c0
+            V1 = np.zeros((1, D), np.float32); V1[0, d1] = c1
+            s0 = float(q[d0]) * c0 / math.sqrt(c0 * c0 / D + eps)
+            s1 = float(q[d1]) * c1 / math.sqrt(c1 * c1 / D + eps)
+            a0 = 1.0 / (1.0 + math.exp(s1 - s0))
+            a1 = 1.0 / (1.0 + math.exp(s0 - s1))
+            out = orc.aggregate([V0, V1], q, eps=eps, want_alpha=True)
+            exp_h = a0 * V0[0].astype(np.float64) + a1 * V1[0].astype(np.float64)
+            assert np.allclose(out["h"][0], exp_h, rtol=1e-13, atol=1e-15), (eps, c0, c1)
+            assert np.allclose(out["alpha"][0], [a0, a1], rtol=1e-13, atol=0)
+            lse = max(s0, s1) + math.log(math.exp(s0 - max(s0, s1)) + math.exp(s1 - max(s0, s1)))
+            assert abs(out["lse"][0] - lse) <= 1e-13 * (1 + abs(lse))
+            assert abs(out["m"][0] - max(s0, s1)) <= 1e-14 * (1 + abs(lse))
+    # the gain folds into the query: gamma scales each hidden coordinate's weight (K3 §9.2 (1))
+    V0 = np.zeros((1, D), np.float32); V0[0, 2] = 1.0
+    V1 = np.zeros((1, D), np.float32); V1[0, 9] = 1.0
+    gamma = np.ones(D, np.float32); gamma[2] = 3.0
+    out = orc.aggregate([V0, V1], q, gamma, eps=0.0, want_alpha=True)
+    s0, s1 = 3.0 * float(q[2]) * 4.0, float(q[9]) * 4.0
+    assert np.allclose(out["alpha"][0], [1 / (1 + math.exp(s1 - s0)), 1 / (1 + math.exp(s0 - s1))],
+                       rtol=1e-13)
+
+
+def pin_scale_invariance(orc):
+    """Rescaling a source by c > 0 leaves every score, weight, m and lse
+    unchanged: the score reads the direction only (K3 §9.2 (2); WC 'Full
+    AttnRes'). Exact at eps = 0; within 1e-6 at eps = 1e-8 for these scales."""
+    rng = np.random.default_rng(3)
+    src = _cfg1_sources(rng, rows=8, D=64)
+    w = (rng.standard_normal(64) * 0.3).astype(np.float32)
+    # powers of two rescale exactly (exact invariance at eps = 0); other factors
+    # round in fp32, which the looser eps = 1e-8 tolerance absorbs
+    for eps, tol, cases in ((0.0, 1e-13, ((0, 2.0), (2, 0.25), (3, 16.0))),
+                            (1e-8, 1e-6, ((0, 2.0), (2, 0.37), (3, 11.0)))):
+        base = orc.aggregate(src, w, eps=eps, want_alpha=True)
+        for j, c in cases:
+            mod = list(src)
+            mod[j] = (src[j] * np.float32(c)).astype(np.float32)
+            out = orc.aggregate(mod, w, eps=eps, want_alpha=True)
+            assert np.allclose(out["alpha"], base["alpha"], rtol=tol, atol=tol)
+            assert np.allclose(out["lse"], base["lse"], rtol=tol, atol=tol)
+            # the output moves only along the rescaled source: h' - h = a_j (c - 1) V_j
+            diff = out["h"] - base["h"]
+            pred = base["alpha"][:, j:j + 1] * (mod[j].astype(np.float64) - src[j].astype(np.float64))
+            vmax = max(np.abs(a).max() for a in mod)
+            assert np.allclose(diff, pred, rtol=1e-6, atol=10 * tol * vmax)
+
+
+def pin_convex_combination(orc):
+    """Softmax weights make h a convex combination of the raw sources
+    (WC 'Full AttnRes'): min_i V_i <= h <= max_i V_i, weights sum to 1."""
+    rng = np.random.default_rng(4)
+    src = [bf16_normal(rng, (12, 48), s) for s in (1.0, 5.0, 0.1, 2.0, 0.7)]
+    w = (rng.standard_normal(48) * 0.4).astype(np.float32)
+    out = orc.aggregate(src, w, want_alpha=True)
+    V = np.stack([bf16_to_f64(s) for s in src])
+    lo, hi = V.min(0), V.max(0)
+    slack = 1e-12 * np.abs(V).max()
+    assert np.all(out["h"] >= lo - slack) and np.all(out["h"] <= hi + slack)
+    assert np.allclose(out["alpha"].sum(1), 1.0, rtol=0, atol=1e-14)
+    assert np.all(out["alpha"] > 0)
+    assert np.all(np.abs(out["h"]) <= out["scale"] + slack)
+
+
+def pin_permutation(orc):
+    """The source order does not matter for h, m or lse (WC validation list:
+    source permutation)."""
+    rng = np.random.default_rng(5)
+    src = [bf16_normal(rng, (6, 40), s) for s in (1.0, 4.0, 0.2, 9.0, 1.5, 0.8)]
+    w = (rng.standard_normal(40) * 0.3).astype(np.float32)
+    base = orc.aggregate(src, w)
+    for perm in ([5, 4, 3, 2, 1, 0], [2, 0, 5, 1, 3, 4]):
+        out = orc.aggregate([src[i] for i in perm], w)
+        assert np.allclose(out["h"], base["h"], rtol=1e-13, atol=1e-13)
+        assert np.allclose(out["lse"], base["lse"], rtol=1e-14, atol=1e-14)
+        assert np.array_equal(out["m"], base["m"])
+
+
+def pin_identical_sources(orc):
+    """n identical sources: uniform weights, h = V and lse = s + log n."""
+    rng = np.random.default_rng(6)
+    v = bf16_normal(rng, (5, 24), 2.0)
+    w = (rng.standard_normal(24) * 0.5).astype(np.float32)
+    one = orc.aggregate([v], w)
+    for n in (2, 3, 7):
+        out = orc.aggregate([v] * n, w)
+        assert np.allclose(out["h"], bf16_to_f64(v), rtol=1e-15, atol=0)
+        assert np.allclose(out["lse"], one["lse"] + math.log(n), rtol=1e-14, atol=1e-14)
+
+
+def pin_os2_bipartition(orc):
+    """Online-softmax summaries of any two disjoint source groups merge into
+    the summary of the whole (K3 §9.4 OS1/OS2; WC reference check on 7 sources
+    of shape (2, 3, 5) split 3/4, with eps 1e-6)."""
+    rng = np.random.default_rng(0)
+    src = [rng.standard_normal((6, 5)).astype(np.float32) for _ in range(7)]
+    q = rng.standard_normal(5).astype(np.float32)
+    whole = orc.aggregate(src, q, eps=1e-6)
+    for k in range(1, 7):
+        a = orc.aggregate(src[:k], q, eps=1e-6)
+        b = orc.aggregate(src[k:], q, eps=1e-6)
+        m, z, u = os2_merge(triple_from(a), triple_from(b))
+        assert np.allclose(u / z[:, None], whole["h"], rtol=1e-12, atol=1e-12), k
+        assert np.allclose(m + np.log(z), whole["lse"], rtol=1e-13, atol=1e-13), k
+        assert np.array_equal(m, whole["m"]), k
+
+
+# ----------------------------------------------------------------------------
+# Phase 1 / Phase 2 definitions
+# ----------------------------------------------------------------------------
+
+def pin_phase1_is_per_query_aggregate(orc):
+    """Phase 1 is S aggregates of the same fixed sources, one per stacked query
+    (K3 §9.4 step 1)."""
+    rng = np.random.default_rng(7)
+    src = [bf16_normal(rng, (4, 32), s) for s in (1.0, 2.0, 0.5)]
+    W = (rng.standard_normal((5, 32)) * 0.2).astype(np.float32)
+    G = rng.uniform(0.5, 1.5, (5, 32)).astype(np.float32)
+    ph = orc.phase1(src, W, G)
+    for s in range(5):
+        a = orc.aggregate(src, W[s], G[s])
+        assert np.array_equal(ph["o"][s], a["h"]) and np.array_equal(ph["lse"][s], a["lse"])
+        assert np.array_equal(ph["m"][s], a["m"])
+
+
+def pin_phase2_merge_limits(orc):
+    """Merging the Phase-1 group (lse, o) with the partial's single-source
+    triple (s_p, p, 1) by OS2: lse far below s_p gives h = p, far above gives
+    h = o, equal gives the midpoint (K3 §9.4 OS2 and single-source triple)."""
+    rng = np.random.default_rng(8)
+    rows, D = 3, 32
+    o = (rng.standard_normal((rows, D))).astype(np.float32)
+    v = (rng.standard_normal((rows, D)) * 2).astype(np.float32)
+    w = (rng.standard_normal(D) * 0.3).astype(np.float32)
+    sp = orc.aggregate([v], w)["m"]  # score of the single source p = v
+    for shift, expect in ((-200.0, v.astype(np.float64)), (200.0, o.astype(np.float64))):
+        lse = (sp + shift).astype(np.float32)
+        out = orc.phase2(o, lse, w, None, v)
+        assert np.allclose(out["h"], expect, rtol=1e-12, atol=1e-12), shift
+        assert np.array_equal(out["p"], v)
+    # a zero query scores p at exactly 0; with lse = 0 the two groups tie
+    out = orc.phase2(o, np.zeros(rows, np.float32), np.zeros(D, np.float32), None, v)
+    assert np.array_equal(out["h"], 0.5 * o.astype(np.float64) + 0.5 * v.astype(np.float64))
+
+
+def pin_phase2_partial_update(orc):
+    """p <- p + v is kept in the model dtype: fp32 add then one rounding to
+    bf16 (torch's bf16 arithmetic), bit for bit (K3 §9.3/§9.4 listings)."""
+    rng = np.random.default_rng(9)
+    rows, D = 4, 64
+    # magnitudes spread over many binades so exponent gaps exceed 16 sometimes
+    p = f64_to_bf16_via_torch((rng.standard_normal((rows, D)) * np.exp2(rng.integers(-20, 20, (rows, D)))).astype(np.float32))
+    v = f64_to_bf16_via_torch((rng.standard_normal((rows, D)) * np.exp2(rng.integers(-20, 20, (rows, D)))).astype(np.float32))
+    o = bf16_normal(rng, (rows, D))
+    w = (rng.standard_normal(D) * 0.1).astype(np.float32)
+    out = orc.phase2(o, np.zeros(rows, np.float32), w, p, v)
+    tp = torch.from_numpy(p.view(np.int16)).view(torch.bfloat16)
+    tv = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16)
+    ref = (tp + tv).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(out["p"], ref)
+    # and the merge uses the rounded partial: compare with an aggregate over it
+    single = orc.aggregate([ref], w)
+    assert np.allclose(orc.phase2(o, np.full(rows, -1e4, np.float32), w, p, v)["h"],
+                       single["h"], rtol=1e-15, atol=0)
+
+
+# ----------------------------------------------------------------------------
+# stack bookkeeping
+# ----------------------------------------------------------------------------
+
+def _stack_inputs(rng, L, rows, D, dtype, scale_hi=5.0):
+    if dtype == "bf16":
+        x = bf16_normal(rng, (rows, D))
+        v = [bf16_normal(rng, (rows, D), rng.uniform(0.1, scale_hi)) for _ in range(L)]
+    else:
+        x = rng.standard_normal((rows, D)).astype(np.float32)
+        v = [(rng.standard_normal((rows, D)) * rng.uniform(0.1, scale_hi)).astype(np.float32)
+             for _ in range(L)]
+    W = (rng.standard_normal((L + 1, D)) * 0.3).astype(np.float32)
+    return x, v, W
+
+
+def pin_plan_golden(orc):
+    """Block plan and unit conversion against the integers the pages print."""
+    with open(os.path.join(GOLDEN, "plan_examples.json")) as f:
+        g = json.load(f)
+    for c in g["atomic_block_size"]:
+        assert orc.atomic_block_size(c["num_hidden_layers"], c["layers_per_block"]) == c["expect"], c["cite"]
+    for c in g["block_plan"]:
+        nb, starts, ns = orc.block_plan(c["L"], c["S"])
+        assert nb == c["expect_nb"], c["cite"]
+        if "expect_final_sources" in c:
+            assert ns[-1] == c["expect_final_sources"], c["cite"]
+        if "expect_max_sources_at_most" in c:
+            assert ns.max() <= c["expect_max_sources_at_most"], c["cite"]
+        # structural: blocks tile 1..L in order, each at most S long, only the last may be short
+        sizes = np.diff(starts)
+        assert starts[0] == 1 and starts[-1] == c["L"] + 1
+        assert np.all(sizes[:-1] == c["S"]) and 1 <= sizes[-1] <= c["S"]
+    for c in g["new_parameters"]:
+        N = 2 * c["num_hidden_layers"]
+        assert N == c["N"], c["cite"]
+        _, _, ns = orc.block_plan(N, orc.atomic_block_size(c["num_hidden_layers"]))
+        # one query and one gain per aggregation: N sublayers plus the final aggregate
+        assert 2 * len(ns) * c["D"] == c["expect"], c["cite"]
+
+
+def pin_plan_source_counts(orc):
+    """Sublayer l of block k sees the k+1 completed sources plus the partial
+    once it exists (K3 §9.3 listing; WC 'Block AttnRes'); Full (S = 1) sees l."""
+    for L in range(1, 30):
+        for S in range(1, L + 2):
+            nb, starts, ns = orc.block_plan(L, S)
+            assert nb == -(-L // S)
+            for l in range(1, L + 1):
+                k = (l - 1) // S
+                j = (l - 1) % S
+                assert ns[l - 1] == k + 1 + (1 if j >= 1 else 0), (L, S, l)
+            assert ns[L] == nb + 1
+            if S == 1:
+                assert list(ns[:L]) == list(range(1, L + 1))
+
+
+def pin_full_equals_block_s1(orc):
+    """Block with S = 1 is Full AttnRes: sublayer l aggregates
+    [x, v_1, ..., v_{l-1}] and the final query all L+1 sources (WC 'Block
+    AttnRes', N = L limit; K3 §9.3)."""
+    rng = np.random.default_rng(13)
+    L, rows, D = 5, 3, 16
+    x, v, W = _stack_inputs(rng, L, rows, D, "bf16")
+    st = orc.block_stack(x, v, W, S=1)
+    for l in range(1, L + 1):
+        a = orc.aggregate([x] + v[: l - 1], W[l - 1])
+        assert np.array_equal(st["h"][l - 1], a["h"]) and np.array_equal(st["h_lse"][l - 1], a["lse"])
+    a = orc.aggregate([x] + v, W[L])
+    assert np.array_equal(st["y"], a["h"])
+    for k in range(L):
+        assert np.array_equal(st["block_sums"][k], v[k])
+
+
+def pin_one_block_is_standard_residual(orc):
+    """One block (S >= L): the block sum is the plain left-fold sum of the
+    sublayer outputs, the sources are {x, partial}, and with zero queries the
+    final output is (x + sum v)/2, i.e. half the standard residual stream
+    x_N = x_0 + sum f_l (WC 'Block AttnRes', N = 1 limit; K3 §9.1)."""
+    rng = np.random.default_rng(14)
+    L, rows, D = 6, 4, 32
+    x, v, _ = _stack_inputs(rng, L, rows, D, "bf16")
+    W = np.zeros((L + 1, D), np.float32)
+    for S in (L, L + 3):
+        st = orc.block_stack(x, v, W, S=S)
+        t = torch.from_numpy(v[0].view(np.int16)).view(torch.bfloat16)
+        folds = [t]
+        for a in v[1:]:
+            t = t + torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+            folds.append(t)
+        b1 = folds[-1].view(torch.int16).numpy().view(np.uint16)
+        assert st["nb"] == 1 and np.array_equal(st["block_sums"][0], b1)
+        X = bf16_to_f64(x)
+        assert np.array_equal(st["h"][0], X)
+        for l in range(2, L + 1):
+            p = bf16_to_f64(folds[l - 2].view(torch.int16).numpy().view(np.uint16))
+            assert np.allclose(st["h"][l - 1], 0.5 * (X + p), rtol=1e-15, atol=1e-15)
+        assert np.allclose(2 * st["y"], X + bf16_to_f64(b1), rtol=1e-15, atol=1e-15)
+
+
+def pin_two_phase_bruteforce(orc):
+    """Two-phase equals naive (K3 §9.4 equivalence box; WC online softmax):
+    for every L <= 7 and S <= L+1, Phase 1 over the completed sources merged
+    by OS2 with the partial's single-source triple reproduces the naive
+    stack's h_l, in fp64, on tiny rows."""
+    rng = np.random.default_rng(15)
+    for dtype in ("bf16", "f32"):
+        for D in (8, 16):
+            for L in range(1, 8):
+                x, v, W = _stack_inputs(rng, L, 3, D, dtype)
+                for S in range(1, L + 2):
+                    st = orc.block_stack(x, v, W, S=S)
+                    blocks = [x]
+                    for k, start in enumerate(range(1, L + 1, S)):
+                        end = min(start + S - 1, L)
+                        ph = orc.phase1(blocks, W[start - 1:end])
+                        partial = None
+                        for j, l in enumerate(range(start, end + 1)):
+                            tr = (ph["m"][j], np.exp(ph["lse"][j] - ph["m"][j]),
+                                  np.exp(ph["lse"][j] - ph["m"][j])[:, None] * ph["o"][j])
+                            if partial is not None:
+                                single = orc.aggregate([partial], W[l - 1])
+                                tr = os2_merge(tr, (single["m"], np.ones(3), widen(partial)))
+                            h = tr[2] / tr[1][:, None]
+                            assert np.allclose(h, st["h"][l - 1], rtol=1e-12, atol=1e-12), (dtype, D, L, S, l)
+                            if partial is None:
+                                partial = v[l - 1]
+                            else:
+                                partial = orc.round_to(widen(partial) + widen(v[l - 1]), dtype)
+                        assert np.array_equal(st["block_sums"][k], partial), (dtype, L, S, k)
+                        blocks.append(partial)
+                    y = orc.aggregate(blocks, W[L])
+                    assert np.allclose(y["h"], st["y"], rtol=1e-13, atol=1e-13)
+
+
+def pin_phase2_composes_to_naive(orc):
+    """The isolated Phase-2 step, fed the Phase-1 output rounded to fp32 and
+    its lse, reproduces the naive stack's h_l to fp32 accuracy."""
+    rng = np.random.default_rng(16)
+    L, S, rows, D = 6, 4, 3, 32
+    x, v, W = _stack_inputs(rng, L, rows, D, "f32")
+    st = orc.block_stack(x, v, W, S=S)
+    ph = orc.phase1([x], W[0:4])
+    p = None
+    for j in range(1, 4):
+        out = orc.phase2(ph["o"][j].astype(np.float32), ph["lse"][j].astype(np.float32), W[j],
+                         p, v[j - 1])
+        assert np.allclose(out["h"], st["h"][j], rtol=0, atol=2e-6 * out["scale"].max())
+        p = out["p"]
+
+
+def pin_causality(orc):
+    """Depth weights are per token and never mix positions: perturbing one
+    row's inputs changes only that row's outputs (K3 §9.1 importantbox;
+    attnres_is_still_causal in the K3 §9.7 table)."""
+    rng = np.random.default_rng(17)
+    L, S, rows, D = 5, 2, 4, 16
+    x, v, W = _stack_inputs(rng, L, rows, D, "f32")
+    base = orc.block_stack(x, v, W, S=S)
+    v2 = [a.copy() for a in v]
+    v2[1][2] += np.float32(1.5)
+    pert = orc.block_stack(x, v2, W, S=S)
+    other = [0, 1, 3]
+    assert np.array_equal(base["h"][:, other], pert["h"][:, other])
+    assert np.array_equal(base["y"][other], pert["y"][other])
+    assert not np.array_equal(base["y"][2], pert["y"][2])
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
