@@ -1,0 +1,261 @@
+"""Thin Python binding of libattnres (include/attnres.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. torch supplies device memory and the current HIP stream. Functions
+carry the C names; optional outputs may be passed as None to have them
+allocated with torch.empty.
+
+The library is loaded from this package directory (built by
+``python -m depth_wise_attention_rms_amd.build``). There is no fallback: if it
+is missing, or no GPU is present for a compute call, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Callable, Optional, Sequence, Union
+
+import torch  # loads the HIP runtime that the library then binds to (same soname)
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattnres.so")
+
+ATTNRES_F32, ATTNRES_BF16 = 0, 1
+STATUS = {0: "ok", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP", -5: "ECALLBACK"}
+TIMING_KINDS = {"phase1": 0, "phase2": 1, "aggregate": 2, "close": 3, "fold": 4}
+
+EXPORTS = (
+    "attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge", "attnres_table_sublayer",
+    "attnres_stack_workspace_bytes", "attnres_block_stack_forward", "attnres_block_layout",
+    "attnres_atomic_block_size", "attnres_status_string", "attnres_last_error",
+    "attnres_timing_enable", "attnres_timing_reset", "attnres_timing_read",
+)
+
+SUBLAYER_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                               ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p)
+
+
+class AttnResError(RuntimeError):
+    def __init__(self, fn: str, code: int, detail: str):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)} ({code}): {detail}")
+        self.code = code
+        self.detail = detail
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libattnres (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m depth_wise_attention_rms_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, F, D, SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                               ctypes.c_double, ctypes.c_size_t)
+        L.attnres_aggregate.argtypes = [P, I, I64, I64, I, P, P, F, P, P, P, P]
+        L.attnres_phase1_batched.argtypes = [P, I, I64, I64, I, P, P, I, F, P, P, P, P]
+        L.attnres_phase2_merge.argtypes = [P, P, P, P, F, P, P, P, P, I64, I64, I, P]
+        L.attnres_table_sublayer.argtypes = [P, I, P, ctypes.POINTER(P), P]
+        L.attnres_stack_workspace_bytes.argtypes = [I, I, I64, I64, I]
+        L.attnres_stack_workspace_bytes.restype = SZ
+        L.attnres_block_stack_forward.argtypes = [P, I, I, I64, I64, I, P, P, F, P, P, P, P, P, SZ, P]
+        L.attnres_block_layout.argtypes = [I, I, P, P]
+        L.attnres_atomic_block_size.argtypes = [I, I]
+        L.attnres_status_string.argtypes = [I]
+        L.attnres_status_string.restype = ctypes.c_char_p
+        L.attnres_last_error.argtypes = []
+        L.attnres_last_error.restype = ctypes.c_char_p
+        L.attnres_timing_enable.argtypes = [I]
+        L.attnres_timing_reset.argtypes = []
+        L.attnres_timing_read.argtypes = [I, ctypes.POINTER(I64), ctypes.POINTER(D), ctypes.POINTER(D)]
+        for f in ("attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge",
+                  "attnres_table_sublayer", "attnres_block_stack_forward", "attnres_block_layout",
+                  "attnres_atomic_block_size", "attnres_timing_enable", "attnres_timing_reset",
+                  "attnres_timing_read"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise AttnResError(fn, rc, lib().attnres_last_error().decode())
+    return rc
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return ATTNRES_BF16
+    if t == torch.float32:
+        return ATTNRES_F32
+    raise TypeError(f"AttnRes I/O dtype must be bfloat16 or float32, not {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _rows(t: torch.Tensor):
+    D = t.shape[-1]
+    return t.numel() // D if D else 0, D
+
+
+def _ptr_array(ts: Sequence[torch.Tensor]):
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def attnres_aggregate(sources: Sequence[torch.Tensor], w: torch.Tensor, gamma=None, eps=1e-8,
+                      out=None, m_out=None, lse_out=None, stream=None):
+    """AGG over ``sources`` (each [..., D]); returns (out, m_out, lse_out)."""
+    x0 = sources[0]
+    R, D = _rows(x0)
+    if out is None:
+        out = torch.empty_like(x0)
+    arr = _ptr_array(sources)
+    _check("attnres_aggregate", lib().attnres_aggregate(
+        arr, len(sources), R, D, dtype_code(x0.dtype), _ptr(w), _ptr(gamma), eps, _ptr(out),
+        _ptr(m_out), _ptr(lse_out), _stream(stream)))
+    return out, m_out, lse_out
+
+
+def attnres_phase1_batched(blocks: Sequence[torch.Tensor], W: torch.Tensor, Gamma=None, eps=1e-8,
+                           out=None, m_out=None, lse_out=None, stream=None):
+    """Phase 1 for the S = W.shape[0] queries; returns (out [S,R,D], m [S,R], lse [S,R])."""
+    x0 = blocks[0]
+    R, D = _rows(x0)
+    S = W.shape[0]
+    if out is None:
+        out = torch.empty((S, R, D), dtype=x0.dtype, device=x0.device)
+    if lse_out is None:
+        lse_out = torch.empty((S, R), dtype=torch.float32, device=x0.device)
+    arr = _ptr_array(blocks)
+    _check("attnres_phase1_batched", lib().attnres_phase1_batched(
+        arr, len(blocks), R, D, dtype_code(x0.dtype), _ptr(W), _ptr(Gamma), S, eps, _ptr(out),
+        _ptr(m_out), _ptr(lse_out), _stream(stream)))
+    return out, m_out, lse_out
+
+
+def attnres_phase2_merge(o, lse, w, v_prev, p_prev=None, gamma=None, eps=1e-8, p_out=None,
+                         h_out=None, stream=None):
+    """One Phase-2 merge; returns (h_out, p_out). p_out is allocated when p_prev is given."""
+    R, D = _rows(o)
+    if h_out is None:
+        h_out = torch.empty_like(o)
+    if p_prev is not None and p_out is None:
+        p_out = torch.empty_like(o)
+    _check("attnres_phase2_merge", lib().attnres_phase2_merge(
+        _ptr(o), _ptr(lse), _ptr(w), _ptr(gamma), eps, _ptr(p_prev), _ptr(v_prev), _ptr(p_out),
+        _ptr(h_out), R, D, dtype_code(o.dtype), _stream(stream)))
+    return h_out, p_out
+
+
+def attnres_stack_workspace_bytes(L: int, S: int, R: int, D: int, dtype: torch.dtype) -> int:
+    return int(lib().attnres_stack_workspace_bytes(L, S, R, D, dtype_code(dtype)))
+
+
+def attnres_block_layout(L: int, S: int):
+    """(nb, block_start[nb+1], n_sources[L+1]) as Python lists."""
+    bs = (ctypes.c_int * (L + 2))()
+    ns = (ctypes.c_int * (L + 1))()
+    nb = lib().attnres_block_layout(L, S, bs, ns)
+    if nb < 0:
+        _check("attnres_block_layout", nb)
+    return nb, list(bs)[: nb + 1], list(ns)
+
+
+def attnres_atomic_block_size(num_decoder_layers: int, layers_per_block: Optional[int] = None) -> int:
+    rc = lib().attnres_atomic_block_size(num_decoder_layers, layers_per_block or 0)
+    if rc < 0:
+        _check("attnres_atomic_block_size", rc)
+    return rc
+
+
+class NativeSublayer:
+    """A C sublayer callback (function pointer + context) from another library."""
+
+    def __init__(self, fn_ptr: int, ctx, keepalive=()):
+        self.fn_ptr = fn_ptr
+        self.ctx = ctx
+        self.keepalive = keepalive
+
+
+Sublayer = Union[Sequence[torch.Tensor], NativeSublayer, Callable[[int, int], torch.Tensor]]
+
+
+def attnres_block_stack_forward(x: torch.Tensor, W: torch.Tensor, S: int, sublayer: Sublayer,
+                                Gamma=None, eps=1e-8, block_sums=None, y=None, workspace=None,
+                                stream=None):
+    """Block AttnRes stack forward (Full when S == 1). ``sublayer`` is a list of
+    L pre-computed outputs, a NativeSublayer, or a Python callable
+    ``f(l, h_ptr) -> tensor v_l``. Returns (y, block_sums)."""
+    R, D = _rows(x)
+    L = W.shape[0] - 1
+    dt = dtype_code(x.dtype)
+    nb = attnres_block_layout(L, S)[0]
+    if y is None:
+        y = torch.empty_like(x)
+    if block_sums is None and not (S == 1 and isinstance(sublayer, (list, tuple))):
+        block_sums = [torch.empty_like(x) for _ in range(nb)]
+    need = attnres_stack_workspace_bytes(L, S, R, D, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    keep = []
+    if isinstance(sublayer, NativeSublayer):
+        fn = ctypes.c_void_p(sublayer.fn_ptr)
+        ctx = sublayer.ctx
+    elif isinstance(sublayer, (list, tuple)):
+        table = _ptr_array(sublayer)
+        keep.append(table)
+        fn = ctypes.cast(lib().attnres_table_sublayer, ctypes.c_void_p)
+        ctx = ctypes.cast(table, ctypes.c_void_p)
+    elif callable(sublayer):
+        outs = []
+
+        def tramp(_ctx, l, h, v_out, _stream):
+            try:
+                v = sublayer(l, h)
+                outs.append(v)
+                v_out[0] = v.data_ptr()
+                return 0
+            except Exception:  # noqa: BLE001 -- reported to the library as a callback failure
+                return 1
+        cfn = SUBLAYER_FN(tramp)
+        keep += [cfn, outs]
+        fn = ctypes.cast(cfn, ctypes.c_void_p)
+        ctx = None
+    else:
+        raise TypeError("sublayer must be a tensor list, a NativeSublayer or a callable")
+    bs = _ptr_array(block_sums) if block_sums is not None else None
+    _check("attnres_block_stack_forward", lib().attnres_block_stack_forward(
+        _ptr(x), L, S, R, D, dt, _ptr(W), _ptr(Gamma), eps, fn, ctx, bs, _ptr(y),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
+    return y, block_sums
+
+
+def attnres_timing_enable(capacity: int):
+    _check("attnres_timing_enable", lib().attnres_timing_enable(capacity))
+
+
+def attnres_timing_reset():
+    _check("attnres_timing_reset", lib().attnres_timing_reset())
+
+
+def attnres_timing_read(kind: str):
+    """(launches, total_ms, total_algorithmic_bytes) recorded for a kernel kind."""
+    n = ctypes.c_int64(); ms = ctypes.c_double(); b = ctypes.c_double()
+    _check("attnres_timing_read", lib().attnres_timing_read(TIMING_KINDS[kind], ctypes.byref(n),
+                                                            ctypes.byref(ms), ctypes.byref(b)))
+    return n.value, ms.value, b.value

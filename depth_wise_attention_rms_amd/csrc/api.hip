@@ -1,0 +1,503 @@
+// api.hip -- the C ABI of libattnres (declared in include/attnres.h).
+//
+// Host side only: argument validation (everything is checked before anything
+// is enqueued), the integer block plan, workspace carving, the two-phase
+// Block stack orchestration with its sublayer callback, and optional launch
+// timing. All device work is in kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "attnres.h"
+
+#define ATTNRES_API extern "C" __attribute__((visibility("default")))
+
+namespace attnres {
+hipError_t launch_fold(const float* w, const float* g, float* q, int64_t count, hipStream_t st);
+hipError_t launch_phase1(int dtype, const void* const* src, int n, int64_t R, int64_t D,
+                         const float* W, const float* G, int S, float eps, void* out, float* m_out,
+                         float* lse_out, hipStream_t st);
+bool phase1_supported(int dtype, int n, int64_t D);
+hipError_t launch_aggregate(int dtype, const void* const* src, int n, int64_t R, int64_t D,
+                            const float* w, const float* gm, float eps, void* out, float* m_out,
+                            float* lse_out, hipStream_t st);
+hipError_t launch_phase2(int dtype, const void* o, const float* lse, const float* w,
+                         const float* gm, float eps, const void* p_prev, const void* v_prev,
+                         void* p_out, void* h_out, int64_t R, int64_t D, hipStream_t st);
+hipError_t launch_close(int dtype, const void* p, const void* v, void* b, int64_t R, int64_t D,
+                        hipStream_t st);
+}  // namespace attnres
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return ATTNRES_OK;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int esize_of(int dtype) { return dtype == ATTNRES_BF16 ? 2 : dtype == ATTNRES_F32 ? 4 : 0; }
+
+// Common [R,D] shape checks.
+int check_shape(const char* fn, int64_t R, int64_t D, int dtype, float eps) {
+  const int es = esize_of(dtype);
+  if (!es) return fail(ATTNRES_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  if (R < 0) return fail(ATTNRES_EINVAL, "%s: R = %lld < 0", fn, (long long)R);
+  if (D < 1 || (D * es) % 16 != 0)
+    return fail(ATTNRES_EINVAL, "%s: D = %lld must be >= 1 with D*%d a multiple of 16 bytes", fn,
+                (long long)D, es);
+  if (D * es > ATTNRES_MAX_ROW_BYTES)
+    return fail(ATTNRES_EUNSUPPORTED, "%s: row of %lld bytes exceeds %d", fn, (long long)(D * es),
+                ATTNRES_MAX_ROW_BYTES);
+  if (!std::isfinite(eps) || eps < 0.f) return fail(ATTNRES_EINVAL, "%s: eps must be finite and >= 0", fn);
+  return ATTNRES_OK;
+}
+
+int check_ptr(const char* fn, const char* name, const void* p, bool required) {
+  if (!p) return required ? fail(ATTNRES_EINVAL, "%s: %s is NULL", fn, name) : ATTNRES_OK;
+  if (!aligned16(p)) return fail(ATTNRES_EINVAL, "%s: %s is not 16-byte aligned", fn, name);
+  return ATTNRES_OK;
+}
+
+#define TRY(expr)                  \
+  do {                             \
+    int rc_ = (expr);              \
+    if (rc_ != ATTNRES_OK) return rc_; \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// launch timing (instrumentation)
+// ---------------------------------------------------------------------------
+enum Kind { K_PHASE1 = 0, K_PHASE2 = 1, K_AGG = 2, K_CLOSE = 3, K_FOLD = 4, K_COUNT = 5 };
+
+struct Timing {
+  int capacity = 0;
+  std::vector<hipEvent_t> ev;  // 2 per slot
+  std::vector<int> kind;
+  std::vector<double> bytes;
+  int used = 0;
+  int64_t launches[K_COUNT] = {0};
+  double ms[K_COUNT] = {0};
+  double total_bytes[K_COUNT] = {0};
+};
+thread_local Timing g_timing;
+
+struct TimedLaunch {
+  int slot = -1;
+  hipStream_t st;
+  TimedLaunch(int kind, double bytes, hipStream_t s) : st(s) {
+    Timing& t = g_timing;
+    if (t.capacity > 0 && t.used < t.capacity) {
+      slot = t.used++;
+      t.kind[slot] = kind;
+      t.bytes[slot] = bytes;
+      hipEventRecord(t.ev[2 * slot], st);
+    }
+  }
+  ~TimedLaunch() {
+    if (slot >= 0) hipEventRecord(g_timing.ev[2 * slot + 1], st);
+  }
+};
+
+int hip_fail(const char* fn, hipError_t e) {
+  return fail(ATTNRES_EHIP, "%s: %s", fn, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// the three kernel families with their byte accounting
+// ---------------------------------------------------------------------------
+int do_aggregate(const char* fn, const void* const* src, int n, int64_t R, int64_t D, int dtype,
+                 const float* w, const float* g, float eps, void* out, float* m_out,
+                 float* lse_out, hipStream_t st) {
+  if (R == 0) return ATTNRES_OK;
+  const double rb = (double)R * D * esize_of(dtype);
+  TimedLaunch tl(K_AGG, rb * (n + 1) + (double)R * ((m_out ? 4 : 0) + (lse_out ? 4 : 0)), st);
+  hipError_t e = attnres::launch_aggregate(dtype, src, n, R, D, w, g, eps, out, m_out, lse_out, st);
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
+}
+
+int do_phase1(const char* fn, const void* const* src, int n, int64_t R, int64_t D, int dtype,
+              const float* W, const float* G, int S, float eps, void* out, float* m_out,
+              float* lse_out, hipStream_t st) {
+  if (R == 0) return ATTNRES_OK;
+  const int64_t row_bytes = D * esize_of(dtype);
+  if (attnres::phase1_supported(dtype, n, D)) {
+    const double rb = (double)R * row_bytes;
+    TimedLaunch tl(K_PHASE1, rb * (n + S) + (double)R * S * ((m_out ? 4 : 0) + 4), st);
+    hipError_t e = attnres::launch_phase1(dtype, src, n, R, D, W, G, S, eps, out, m_out, lse_out, st);
+    return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
+  }
+  // More sources than the register-resident pass holds: one aggregate per query.
+  for (int s = 0; s < S; ++s) {
+    TRY(do_aggregate(fn, src, n, R, D, dtype, W + (int64_t)s * D, G ? G + (int64_t)s * D : nullptr,
+                     eps, static_cast<char*>(out) + (int64_t)s * R * row_bytes,
+                     m_out ? m_out + (int64_t)s * R : nullptr, lse_out + (int64_t)s * R, st));
+  }
+  return ATTNRES_OK;
+}
+
+int do_phase2(const char* fn, const void* o, const float* lse, const float* w, const float* g,
+              float eps, const void* p_prev, const void* v_prev, void* p_out, void* h_out,
+              int64_t R, int64_t D, int dtype, hipStream_t st) {
+  if (R == 0) return ATTNRES_OK;
+  const double rb = (double)R * D * esize_of(dtype);
+  TimedLaunch tl(K_PHASE2, rb * (p_prev ? 5 : 3) + (double)R * 4, st);
+  hipError_t e = attnres::launch_phase2(dtype, o, lse, w, g, eps, p_prev, v_prev, p_out, h_out, R, D, st);
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
+}
+
+int do_close(const char* fn, const void* p, const void* v, void* b, int64_t R, int64_t D,
+             int dtype, hipStream_t st) {
+  if (R == 0) return ATTNRES_OK;
+  const double rb = (double)R * D * esize_of(dtype);
+  TimedLaunch tl(K_CLOSE, rb * (p ? 3 : 2), st);
+  hipError_t e = attnres::launch_close(dtype, p, v, b, R, D, st);
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
+}
+
+// ---------------------------------------------------------------------------
+// block plan [K3 9.3 forward_naive]
+// ---------------------------------------------------------------------------
+int plan(int L, int S, int* block_start, int* n_sources) {
+  int completed = 1, partial = 0, nb = 0;
+  if (block_start) block_start[0] = 1;
+  for (int l = 1; l <= L; ++l) {
+    if (n_sources) n_sources[l - 1] = completed + partial;
+    partial = 1;
+    if (l % S == 0 || l == L) {
+      ++completed;
+      partial = 0;
+      ++nb;
+      if (block_start) block_start[nb] = l + 1;
+    }
+  }
+  if (n_sources) n_sources[L] = completed;
+  return nb;
+}
+
+// workspace layout of the stack forward, each region 256-byte aligned
+struct StackLayout {
+  size_t q, o, m, lse, p, h, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+StackLayout stack_layout(int L, int S, int64_t R, int64_t D, int es) {
+  StackLayout s;
+  const int Sk = S < L ? S : L;  // widest block
+  const size_t row = (size_t)R * (size_t)D * es;
+  size_t off = 0;
+  s.q = off; off = align256(off + (size_t)(L + 1) * D * sizeof(float));
+  s.o = off; off = align256(off + (Sk > 1 ? (size_t)Sk * row : 0));
+  s.m = off; off = align256(off + (size_t)Sk * R * sizeof(float));
+  s.lse = off; off = align256(off + (size_t)Sk * R * sizeof(float));
+  s.p = off; off = align256(off + (Sk > 2 ? row : 0));
+  s.h = off; off = align256(off + row);
+  s.total = off;
+  return s;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+
+ATTNRES_API const char* attnres_status_string(int code) {
+  switch (code) {
+    case ATTNRES_OK: return "ok";
+    case ATTNRES_EINVAL: return "invalid argument";
+    case ATTNRES_EUNSUPPORTED: return "unsupported by this build";
+    case ATTNRES_EWORKSPACE: return "workspace too small";
+    case ATTNRES_EHIP: return "HIP runtime error";
+    case ATTNRES_ECALLBACK: return "sublayer callback failed";
+    default: return "unknown status";
+  }
+}
+
+ATTNRES_API const char* attnres_last_error(void) { return g_last_error.c_str(); }
+
+ATTNRES_API int attnres_aggregate(const void* const* sources, int n, int64_t R, int64_t D,
+                                  int dtype, const float* w, const float* gamma, float eps,
+                                  void* out, float* m_out, float* lse_out, void* stream) {
+  const char* fn = "attnres_aggregate";
+  TRY(check_shape(fn, R, D, dtype, eps));
+  if (!sources) return fail(ATTNRES_EINVAL, "%s: sources is NULL", fn);
+  if (n < 1 || n > ATTNRES_MAX_SOURCES)
+    return fail(ATTNRES_EINVAL, "%s: n = %d outside 1..%d", fn, n, ATTNRES_MAX_SOURCES);
+  if (R == 0) return ok();  // nothing is accessed
+  for (int i = 0; i < n; ++i) {
+    TRY(check_ptr(fn, "sources[i]", sources[i], true));
+    if (sources[i] == out) return fail(ATTNRES_EINVAL, "%s: out aliases sources[%d]", fn, i);
+  }
+  TRY(check_ptr(fn, "w", w, true));
+  TRY(check_ptr(fn, "gamma", gamma, false));
+  TRY(check_ptr(fn, "out", out, true));
+  TRY(check_ptr(fn, "m_out", m_out, false));
+  TRY(check_ptr(fn, "lse_out", lse_out, false));
+  TRY(do_aggregate(fn, sources, n, R, D, dtype, w, gamma, eps, out, m_out, lse_out,
+                   static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+ATTNRES_API int attnres_phase1_batched(const void* const* blocks, int n, int64_t R, int64_t D,
+                                       int dtype, const float* W, const float* Gamma, int S,
+                                       float eps, void* out, float* m_out, float* lse_out,
+                                       void* stream) {
+  const char* fn = "attnres_phase1_batched";
+  TRY(check_shape(fn, R, D, dtype, eps));
+  if (!blocks) return fail(ATTNRES_EINVAL, "%s: blocks is NULL", fn);
+  if (n < 1 || n > ATTNRES_MAX_SOURCES)
+    return fail(ATTNRES_EINVAL, "%s: n = %d outside 1..%d", fn, n, ATTNRES_MAX_SOURCES);
+  if (S < 1 || S > 1024) return fail(ATTNRES_EINVAL, "%s: S = %d outside 1..1024", fn, S);
+  if (R == 0) return ok();
+  for (int i = 0; i < n; ++i) TRY(check_ptr(fn, "blocks[i]", blocks[i], true));
+  TRY(check_ptr(fn, "W", W, true));
+  TRY(check_ptr(fn, "Gamma", Gamma, false));
+  TRY(check_ptr(fn, "out", out, true));
+  TRY(check_ptr(fn, "m_out", m_out, false));
+  TRY(check_ptr(fn, "lse_out", lse_out, true));
+  TRY(do_phase1(fn, blocks, n, R, D, dtype, W, Gamma, S, eps, out, m_out, lse_out,
+                static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+ATTNRES_API int attnres_phase2_merge(const void* o, const float* lse, const float* w,
+                                     const float* gamma, float eps, const void* p_prev,
+                                     const void* v_prev, void* p_out, void* h_out, int64_t R,
+                                     int64_t D, int dtype, void* stream) {
+  const char* fn = "attnres_phase2_merge";
+  TRY(check_shape(fn, R, D, dtype, eps));
+  if (R == 0) return ok();
+  TRY(check_ptr(fn, "o", o, true));
+  TRY(check_ptr(fn, "lse", lse, true));
+  TRY(check_ptr(fn, "w", w, true));
+  TRY(check_ptr(fn, "gamma", gamma, false));
+  TRY(check_ptr(fn, "p_prev", p_prev, false));
+  TRY(check_ptr(fn, "v_prev", v_prev, true));
+  TRY(check_ptr(fn, "p_out", p_out, p_prev != nullptr));
+  TRY(check_ptr(fn, "h_out", h_out, true));
+  if (!p_prev && p_out) return fail(ATTNRES_EINVAL, "%s: p_out must be NULL when p_prev is NULL", fn);
+  if (h_out == o || h_out == p_prev || h_out == v_prev || h_out == p_out)
+    return fail(ATTNRES_EINVAL, "%s: h_out aliases an input or p_out", fn);
+  if (p_out && (p_out == o || p_out == v_prev))
+    return fail(ATTNRES_EINVAL, "%s: p_out aliases o or v_prev", fn);
+  TRY(do_phase2(fn, o, lse, w, gamma, eps, p_prev, v_prev, p_out, h_out, R, D, dtype,
+                static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+ATTNRES_API int attnres_table_sublayer(void* ctx, int l, const void* h_l, const void** v_out,
+                                       void* stream) {
+  (void)h_l;
+  (void)stream;
+  if (!ctx || !v_out || l < 1) return 1;
+  *v_out = static_cast<const void* const*>(ctx)[l - 1];
+  return 0;
+}
+
+ATTNRES_API int attnres_block_layout(int L, int S, int* block_start, int* n_sources) {
+  if (L < 1 || S < 1) return fail(ATTNRES_EINVAL, "attnres_block_layout: L and S must be >= 1");
+  return plan(L, S, block_start, n_sources);
+}
+
+ATTNRES_API int attnres_atomic_block_size(int num_decoder_layers, int layers_per_block) {
+  if (num_decoder_layers < 1)
+    return fail(ATTNRES_EINVAL, "attnres_atomic_block_size: num_decoder_layers must be >= 1");
+  int per = layers_per_block > 0 ? layers_per_block : (num_decoder_layers + 7) / 8;
+  if (per < 1) per = 1;
+  return 2 * per;
+}
+
+ATTNRES_API size_t attnres_stack_workspace_bytes(int L, int S, int64_t R, int64_t D, int dtype) {
+  const int es = esize_of(dtype);
+  if (!es || L < 1 || S < 1 || R < 0 || D < 1) return 0;
+  return stack_layout(L, S, R, D, es).total;
+}
+
+ATTNRES_API int attnres_block_stack_forward(const void* x, int L, int S, int64_t R, int64_t D,
+                                            int dtype, const float* W, const float* Gamma,
+                                            float eps, attnres_sublayer_fn f, void* f_ctx,
+                                            void* const* block_sums, void* y, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  const char* fn = "attnres_block_stack_forward";
+  TRY(check_shape(fn, R, D, dtype, eps));
+  if (L < 1 || S < 1) return fail(ATTNRES_EINVAL, "%s: L = %d and S = %d must be >= 1", fn, L, S);
+  const int nb = plan(L, S, nullptr, nullptr);
+  if (nb + 1 > ATTNRES_MAX_SOURCES)
+    return fail(ATTNRES_EINVAL, "%s: %d blocks plus the embedding exceed %d sources", fn, nb,
+                ATTNRES_MAX_SOURCES);
+  if (R == 0) return ok();  // nothing is accessed and no sublayer is called
+  TRY(check_ptr(fn, "x", x, true));
+  TRY(check_ptr(fn, "W", W, true));
+  TRY(check_ptr(fn, "Gamma", Gamma, false));
+  TRY(check_ptr(fn, "y", y, true));
+  if (!f) return fail(ATTNRES_EINVAL, "%s: sublayer callback is NULL", fn);
+  if (!block_sums && S != 1)
+    return fail(ATTNRES_EINVAL, "%s: block_sums may be NULL only when S == 1", fn);
+  if (block_sums)
+    for (int k = 0; k < nb; ++k) TRY(check_ptr(fn, "block_sums[k]", block_sums[k], true));
+  const int es = esize_of(dtype);
+  const StackLayout lay = stack_layout(L, S, R, D, es);
+  if (!workspace) return fail(ATTNRES_EINVAL, "%s: workspace is NULL", fn);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(ATTNRES_EINVAL, "%s: workspace is not 256-byte aligned", fn);
+  if (workspace_bytes < lay.total)
+    return fail(ATTNRES_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes,
+                lay.total);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* Q = reinterpret_cast<float*>(ws + lay.q);
+  char* O = ws + lay.o;
+  float* M = reinterpret_cast<float*>(ws + lay.m);
+  float* LSE = reinterpret_cast<float*>(ws + lay.lse);
+  void* P = ws + lay.p;
+  void* H = ws + lay.h;
+  const int64_t row_bytes = D * es;
+  const int64_t tensor_bytes = R * row_bytes;
+
+  {  // fold q~ = w * gamma once for all L+1 queries [K3 9.2 (1)]
+    TimedLaunch tl(K_FOLD, (double)(L + 1) * D * (Gamma ? 12 : 8), st);
+    hipError_t e = attnres::launch_fold(W, Gamma, Q, (int64_t)(L + 1) * D, st);
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
+
+  std::vector<const void*> src;
+  src.reserve(nb + 1);
+  src.push_back(x);
+  auto call = [&](int l, const void* h, const void** v) -> int {
+    const void* out = nullptr;
+    const int rc = f(f_ctx, l, h, &out, stream);
+    if (rc != 0) return fail(ATTNRES_ECALLBACK, "%s: sublayer callback returned %d at l = %d", fn, rc, l);
+    if (!out || !aligned16(out))
+      return fail(ATTNRES_ECALLBACK, "%s: callback gave a NULL or misaligned v at l = %d", fn, l);
+    *v = out;
+    return ATTNRES_OK;
+  };
+
+  for (int k = 0; k < nb; ++k) {
+    const int start = k * S + 1;
+    const int end = (k + 1) * S < L ? (k + 1) * S : L;
+    const int Sk = end - start + 1;
+    const int n = k + 1;
+    const float* Qk = Q + (int64_t)(start - 1) * D;
+    if (Sk == 1) {
+      // a one-sublayer block: a single aggregate over the completed sources
+      TRY(do_aggregate(fn, src.data(), n, R, D, dtype, Qk, nullptr, eps, H, nullptr, nullptr, st));
+      const void* v = nullptr;
+      TRY(call(start, H, &v));
+      if (block_sums) {
+        TRY(do_close(fn, nullptr, v, block_sums[k], R, D, dtype, st));
+        src.push_back(block_sums[k]);
+      } else {
+        src.push_back(v);
+      }
+      continue;
+    }
+    // Phase 1: the block's Sk queries over [b_0 .. b_k] in one pass
+    TRY(do_phase1(fn, src.data(), n, R, D, dtype, Qk, nullptr, Sk, eps, O, M, LSE, st));
+    const void* v_first = nullptr;
+    TRY(call(start, O, &v_first));  // h_start = o_0: no partial yet
+    const void* p_cur = v_first;    // p_1 = v_start (aliased, no copy)
+    const void* v_prev = v_first;
+    for (int j = 1; j < Sk; ++j) {
+      const int l = start + j;
+      const void* o_j = O + (int64_t)j * tensor_bytes;
+      const float* lse_j = LSE + (int64_t)j * R;
+      const float* q_l = Q + (int64_t)(l - 1) * D;
+      if (j == 1) {
+        TRY(do_phase2(fn, o_j, lse_j, q_l, nullptr, eps, nullptr, v_prev, nullptr, H, R, D, dtype, st));
+      } else {
+        TRY(do_phase2(fn, o_j, lse_j, q_l, nullptr, eps, p_cur, v_prev, P, H, R, D, dtype, st));
+        p_cur = P;
+      }
+      const void* v = nullptr;
+      TRY(call(l, H, &v));
+      v_prev = v;
+    }
+    // close: b_{k+1} = p + v_end
+    TRY(do_close(fn, p_cur, v_prev, block_sums[k], R, D, dtype, st));
+    src.push_back(block_sums[k]);
+  }
+  // final aggregate over [b_0 .. b_nb] [K3 9.1 is_final_aggregate]
+  TRY(do_aggregate(fn, src.data(), nb + 1, R, D, dtype, Q + (int64_t)L * D, nullptr, eps, y,
+                   nullptr, nullptr, st));
+  return ok();
+}
+
+ATTNRES_API int attnres_timing_enable(int capacity) {
+  Timing& t = g_timing;
+  for (hipEvent_t e : t.ev) hipEventDestroy(e);
+  t = Timing();
+  if (capacity <= 0) return ok();
+  t.ev.resize(2 * (size_t)capacity);
+  for (auto& e : t.ev) {
+    hipError_t rc = hipEventCreate(&e);
+    if (rc != hipSuccess) {
+      t.ev.clear();
+      t = Timing();
+      return hip_fail("attnres_timing_enable", rc);
+    }
+  }
+  t.kind.assign(capacity, 0);
+  t.bytes.assign(capacity, 0.0);
+  t.capacity = capacity;
+  return ok();
+}
+
+static int collect_timing() {
+  Timing& t = g_timing;
+  for (int s = 0; s < t.used; ++s) {
+    hipError_t e = hipEventSynchronize(t.ev[2 * s + 1]);
+    if (e != hipSuccess) return hip_fail("attnres_timing_read", e);
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, t.ev[2 * s], t.ev[2 * s + 1]);
+    if (e != hipSuccess) return hip_fail("attnres_timing_read", e);
+    t.launches[t.kind[s]] += 1;
+    t.ms[t.kind[s]] += ms;
+    t.total_bytes[t.kind[s]] += t.bytes[s];
+  }
+  t.used = 0;
+  return ATTNRES_OK;
+}
+
+ATTNRES_API int attnres_timing_reset(void) {
+  Timing& t = g_timing;
+  t.used = 0;
+  for (int k = 0; k < K_COUNT; ++k) {
+    t.launches[k] = 0;
+    t.ms[k] = 0;
+    t.total_bytes[k] = 0;
+  }
+  return ok();
+}
+
+ATTNRES_API int attnres_timing_read(int kind, int64_t* launches, double* total_ms,
+                                    double* total_bytes) {
+  if (kind < 0 || kind >= K_COUNT) return fail(ATTNRES_EINVAL, "attnres_timing_read: kind %d", kind);
+  TRY(collect_timing());
+  const Timing& t = g_timing;
+  if (launches) *launches = t.launches[kind];
+  if (total_ms) *total_ms = t.ms[kind];
+  if (total_bytes) *total_bytes = t.total_bytes[kind];
+  return ok();
+}

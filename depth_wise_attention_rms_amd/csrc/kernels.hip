@@ -1,0 +1,618 @@
+// kernels.hip -- gfx950 kernels of the AttnRes depth-aggregation hot path.
+//
+// Pages: K3 course notes, section "Attention Residual 深度残差" (eqs. A1-A3,
+// OS1, OS2; 9.4 two-phase algorithm); "Attention Residuals" survey page on
+// wineandchord.com ("Depth attention & online merge reference"); reading notes
+// on "Attention Residuals" (ranhao.site) 4.2 Inference.
+//
+// Work decomposition. Every kernel is bandwidth-shaped: it streams [R,D] rows
+// and does a short per-row contraction. A token row is owned by W waves
+// (64*W lanes); lane t holds VPL 16-byte vectors of the row, vector c at index
+// c*64*W + t, so each load instruction of a wave covers 1 KiB of contiguous
+// memory. Rows are independent (weights are per token), so a workgroup of
+// RPW*W waves walks RPW rows at a time in a grid-stride loop and no data moves
+// between workgroups. Row-wide sums (sum of squares, dot products) reduce with
+// DPP inside a wave and through LDS across the W waves of a row.
+#include "device.hpp"
+
+#include <float.h>
+
+namespace attnres {
+
+// Row geometry of one launch, computed on the host.
+struct Geom {
+  int64_t R;       // token rows
+  int64_t groups;  // ceil(R / RPW)
+  int V;           // 16-byte vectors per row
+  int W;           // waves per row
+  int RPW;         // rows per workgroup iteration
+  int D;           // elements per row
+  float invD;      // 1 / D
+};
+
+struct Lanes {
+  int lane, slot, wr, t, stride;
+  __device__ __forceinline__ Lanes(int W) {
+    lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    slot = wave / W;
+    wr = wave - slot * W;
+    t = wr * 64 + lane;
+    stride = W * 64;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Query fold q~ = w * gamma in fp32 [K3 9.2 (1)], over `count` elements.
+// ---------------------------------------------------------------------------
+__global__ void fold_kernel(const float* __restrict__ w, const float* __restrict__ g,
+                            float* __restrict__ q, int64_t count) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * blockDim.x)
+    q[i] = g ? w[i] * g[i] : w[i];
+}
+
+// Load EPV fp32 query values for vector `vec` of query row `qrow`, folding the gain.
+template <int EPV>
+__device__ __forceinline__ void load_query(const float* __restrict__ w, const float* __restrict__ g,
+                                           int64_t off, float* q) {
+  #pragma unroll
+  for (int k = 0; k < EPV; k += 4) {
+    float4 a = ldf4(w + off + k);
+    if (g) {
+      float4 b = ldf4(g + off + k);
+      a.x *= b.x; a.y *= b.y; a.z *= b.z; a.w *= b.w;
+    }
+    q[k] = a.x; q[k + 1] = a.y; q[k + 2] = a.z; q[k + 3] = a.w;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase 1 (batched inter-block pass) [K3 9.4 step 1; RH 4.2 Phase 1].
+// The n <= NMAX sources of a row are loaded once and held in registers as
+// fp32; the S queries are processed in batches of SB: per batch one row
+// reduction of SB*NMAX dot products (plus the NMAX sums of squares), then the
+// SB softmaxes over the source axis and SB weighted sums of the raw sources.
+// ---------------------------------------------------------------------------
+struct Phase1Params {
+  const void* src[16];
+  int n;
+  int S;
+  const float* Wq;  // [S][D]
+  const float* G;   // [S][D] or null
+  float eps;
+  void* out;        // [S][R][D]
+  float* m_out;     // [S][R] or null
+  float* lse_out;   // [S][R]
+  Geom g;
+};
+
+template <class T, int VPL, int NMAX, int SB>
+__global__ __launch_bounds__(512) void phase1_kernel(Phase1Params p) {
+  extern __shared__ float lds[];
+  constexpr int EPV = T::kEPV;
+  constexpr int NV = SB * NMAX + NMAX;
+  const Geom& g = p.g;
+  const Lanes ln(g.W);
+  const int64_t rowbytes = (int64_t)g.V * 16;
+  const int n = p.n;
+
+  for (int64_t grp = blockIdx.x; grp < g.groups; grp += gridDim.x) {
+    const int64_t row = grp * g.RPW + ln.slot;
+    const bool rv = row < g.R;
+
+    float x[NMAX][VPL][EPV];
+    #pragma unroll
+    for (int i = 0; i < NMAX; ++i) {
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        const int vec = c * ln.stride + ln.t;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (rv && i < n && vec < g.V)
+          u = ld16(static_cast<const char*>(p.src[i]) + row * rowbytes + (int64_t)vec * 16);
+        T::unpack(u, x[i][c]);
+      }
+    }
+
+    float inv_rms[NMAX];
+    for (int s0 = 0; s0 < p.S; s0 += SB) {
+      float red[NV];
+      #pragma unroll
+      for (int k = 0; k < NV; ++k) red[k] = 0.f;
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        const int vec = c * ln.stride + ln.t;
+        if (vec < g.V) {
+          if (s0 == 0) {
+            #pragma unroll
+            for (int i = 0; i < NMAX; ++i)
+              #pragma unroll
+              for (int e = 0; e < EPV; ++e) red[SB * NMAX + i] += x[i][c][e] * x[i][c][e];
+          }
+          #pragma unroll
+          for (int sb = 0; sb < SB; ++sb) {
+            if (s0 + sb < p.S) {
+              float q[EPV];
+              load_query<EPV>(p.Wq, p.G, (int64_t)(s0 + sb) * g.D + (int64_t)vec * EPV, q);
+              #pragma unroll
+              for (int i = 0; i < NMAX; ++i)
+                #pragma unroll
+                for (int e = 0; e < EPV; ++e) red[sb * NMAX + i] += q[e] * x[i][c][e];
+            }
+          }
+        }
+      }
+      row_reduce<NV>(red, lds, ln.slot, ln.wr, g.W);
+      if (s0 == 0) {
+        #pragma unroll
+        for (int i = 0; i < NMAX; ++i) inv_rms[i] = rsqrtf(red[SB * NMAX + i] * g.invD + p.eps);
+      }
+      #pragma unroll
+      for (int sb = 0; sb < SB; ++sb) {
+        const int s = s0 + sb;
+        if (s < p.S) {
+          float sc[NMAX];
+          float m = -FLT_MAX;
+          #pragma unroll
+          for (int i = 0; i < NMAX; ++i) {
+            sc[i] = red[sb * NMAX + i] * inv_rms[i];
+            if (i < n) m = fmaxf(m, sc[i]);
+          }
+          float z = 0.f;
+          #pragma unroll
+          for (int i = 0; i < NMAX; ++i) {
+            sc[i] = i < n ? __expf(sc[i] - m) : 0.f;
+            z += sc[i];
+          }
+          const float rz = 1.0f / z;
+          #pragma unroll
+          for (int i = 0; i < NMAX; ++i) sc[i] *= rz;
+          if (rv) {
+            if (ln.t == 0) {
+              if (p.m_out) p.m_out[(int64_t)s * g.R + row] = m;
+              p.lse_out[(int64_t)s * g.R + row] = m + __logf(z);
+            }
+            char* orow = static_cast<char*>(p.out) + ((int64_t)s * g.R + row) * rowbytes;
+            #pragma unroll
+            for (int c = 0; c < VPL; ++c) {
+              const int vec = c * ln.stride + ln.t;
+              if (vec < g.V) {
+                float o[EPV];
+                #pragma unroll
+                for (int e = 0; e < EPV; ++e) o[e] = 0.f;
+                #pragma unroll
+                for (int i = 0; i < NMAX; ++i)
+                  #pragma unroll
+                  for (int e = 0; e < EPV; ++e) o[e] += sc[i] * x[i][c][e];
+                st16(orow + (int64_t)vec * 16, T::pack(o));
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Aggregate over any number of sources with one query [K3 (A1)-(A3); WC
+// depth_summary/merge_summary/finish]. Sources are taken in register-resident
+// groups of G; each group's scores are reduced across the row and folded into
+// a running (m, z, numerator) triple by the online-softmax merge (OS2), so
+// every source is read exactly once whatever n is.
+// ---------------------------------------------------------------------------
+struct AggParams {
+  const void* src[64];
+  int n;
+  const float* w;  // [D]
+  const float* gm; // [D] or null
+  float eps;
+  void* out;       // [R][D]
+  float* m_out;    // [R] or null
+  float* lse_out;  // [R] or null
+  Geom g;
+};
+
+template <class T, int VPL, int G>
+__global__ __launch_bounds__(512) void aggregate_kernel(AggParams p) {
+  extern __shared__ float lds[];
+  constexpr int EPV = T::kEPV;
+  constexpr int NV = 2 * G;
+  const Geom& g = p.g;
+  const Lanes ln(g.W);
+  const int64_t rowbytes = (int64_t)g.V * 16;
+
+  // this lane's slice of the folded query, reused for every row
+  float q[VPL][EPV];
+  #pragma unroll
+  for (int c = 0; c < VPL; ++c) {
+    const int vec = c * ln.stride + ln.t;
+    if (vec < g.V) {
+      load_query<EPV>(p.w, p.gm, (int64_t)vec * EPV, q[c]);
+    } else {
+      #pragma unroll
+      for (int e = 0; e < EPV; ++e) q[c][e] = 0.f;
+    }
+  }
+
+  for (int64_t grp = blockIdx.x; grp < g.groups; grp += gridDim.x) {
+    const int64_t row = grp * g.RPW + ln.slot;
+    const bool rv = row < g.R;
+    float num[VPL][EPV];
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c)
+      #pragma unroll
+      for (int e = 0; e < EPV; ++e) num[c][e] = 0.f;
+    float m_run = -FLT_MAX, z_run = 0.f;
+
+    for (int i0 = 0; i0 < p.n; i0 += G) {
+      float x[G][VPL][EPV];
+      #pragma unroll
+      for (int j = 0; j < G; ++j) {
+        #pragma unroll
+        for (int c = 0; c < VPL; ++c) {
+          const int vec = c * ln.stride + ln.t;
+          uint4 u = make_uint4(0, 0, 0, 0);
+          if (rv && i0 + j < p.n && vec < g.V)
+            u = ld16(static_cast<const char*>(p.src[i0 + j]) + row * rowbytes + (int64_t)vec * 16);
+          T::unpack(u, x[j][c]);
+        }
+      }
+      float red[NV];
+      #pragma unroll
+      for (int k = 0; k < NV; ++k) red[k] = 0.f;
+      #pragma unroll
+      for (int j = 0; j < G; ++j)
+        #pragma unroll
+        for (int c = 0; c < VPL; ++c)
+          #pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            red[j] += q[c][e] * x[j][c][e];
+            red[G + j] += x[j][c][e] * x[j][c][e];
+          }
+      row_reduce<NV>(red, lds, ln.slot, ln.wr, g.W);
+      float sc[G];
+      float m_new = m_run;
+      #pragma unroll
+      for (int j = 0; j < G; ++j) {
+        sc[j] = red[j] * rsqrtf(red[G + j] * g.invD + p.eps);
+        if (i0 + j < p.n) m_new = fmaxf(m_new, sc[j]);
+      }
+      const float rescale = __expf(m_run - m_new);
+      z_run *= rescale;
+      #pragma unroll
+      for (int j = 0; j < G; ++j) {
+        sc[j] = (i0 + j < p.n) ? __expf(sc[j] - m_new) : 0.f;
+        z_run += sc[j];
+      }
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c)
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          float a = num[c][e] * rescale;
+          #pragma unroll
+          for (int j = 0; j < G; ++j) a += sc[j] * x[j][c][e];
+          num[c][e] = a;
+        }
+      m_run = m_new;
+    }
+    if (rv) {
+      const float rz = 1.0f / z_run;
+      char* orow = static_cast<char*>(p.out) + row * rowbytes;
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        const int vec = c * ln.stride + ln.t;
+        if (vec < g.V) {
+          float o[EPV];
+          #pragma unroll
+          for (int e = 0; e < EPV; ++e) o[e] = num[c][e] * rz;
+          st16(orow + (int64_t)vec * 16, T::pack(o));
+        }
+      }
+      if (ln.t == 0) {
+        if (p.m_out) p.m_out[row] = m_run;
+        if (p.lse_out) p.lse_out[row] = m_run + __logf(z_run);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase 2 (one intra-block merge step) [K3 9.4 step 2, OS2, single-source
+// triple; RH 4.2 Phase 2]: p = p_prev + v_prev rounded to the I/O dtype (or
+// p = v_prev on the first merge), the score of the rounded p, then
+// h = (e^(lse-M) o + e^(s_p-M) p) / (e^(lse-M) + e^(s_p-M)). The o tile is
+// loaded before the row reduction so its latency overlaps the reduction.
+// ---------------------------------------------------------------------------
+struct Phase2Params {
+  const void* o;
+  const float* lse;
+  const float* w;
+  const float* gm;
+  float eps;
+  const void* p_prev;  // null on the first merge of a block
+  const void* v_prev;
+  void* p_out;         // null iff p_prev is null
+  void* h_out;
+  Geom g;
+};
+
+template <class T, int VPL, bool HAS_PREV>
+__global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
+  extern __shared__ float lds[];
+  constexpr int EPV = T::kEPV;
+  const Geom& g = p.g;
+  const Lanes ln(g.W);
+  const int64_t rowbytes = (int64_t)g.V * 16;
+
+  for (int64_t grp = blockIdx.x; grp < g.groups; grp += gridDim.x) {
+    const int64_t row = grp * g.RPW + ln.slot;
+    const bool rv = row < g.R;
+    const int64_t base = row * rowbytes;
+    uint4 pv[VPL], ov[VPL];
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      const int vec = c * ln.stride + ln.t;
+      const bool ok = rv && vec < g.V;
+      const int64_t off = base + (int64_t)vec * 16;
+      uint4 v = ok ? ld16(static_cast<const char*>(p.v_prev) + off) : make_uint4(0, 0, 0, 0);
+      if (HAS_PREV) {
+        uint4 a = ok ? ld16(static_cast<const char*>(p.p_prev) + off) : make_uint4(0, 0, 0, 0);
+        float fa[EPV], fv[EPV];
+        T::unpack(a, fa);
+        T::unpack(v, fv);
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) fa[e] += fv[e];
+        v = T::pack(fa);  // the partial, rounded to the I/O dtype
+        if (ok) st16(static_cast<char*>(p.p_out) + off, v);
+      }
+      pv[c] = v;
+      ov[c] = ok ? ld16(static_cast<const char*>(p.o) + off) : make_uint4(0, 0, 0, 0);
+    }
+    float red[2] = {0.f, 0.f};
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      const int vec = c * ln.stride + ln.t;
+      if (vec < g.V) {
+        float q[EPV], f[EPV];
+        load_query<EPV>(p.w, p.gm, (int64_t)vec * EPV, q);
+        T::unpack(pv[c], f);
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          red[0] += q[e] * f[e];
+          red[1] += f[e] * f[e];
+        }
+      }
+    }
+    row_reduce<2>(red, lds, ln.slot, ln.wr, g.W);
+    if (rv) {
+      const float sp = red[0] * rsqrtf(red[1] * g.invD + p.eps);
+      const float l = p.lse[row];
+      const float M = fmaxf(l, sp);
+      float a = __expf(l - M), b = __expf(sp - M);
+      const float r = 1.0f / (a + b);
+      a *= r;
+      b *= r;
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        const int vec = c * ln.stride + ln.t;
+        if (vec < g.V) {
+          float fo[EPV], fp[EPV];
+          T::unpack(ov[c], fo);
+          T::unpack(pv[c], fp);
+          #pragma unroll
+          for (int e = 0; e < EPV; ++e) fo[e] = a * fo[e] + b * fp[e];
+          st16(static_cast<char*>(p.h_out) + base + (int64_t)vec * 16, T::pack(fo));
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block close [K3 9.3 listing]: b = p + v rounded to the I/O dtype, or b = v
+// when p is null (a one-sublayer block). Elementwise over `nvec` vectors.
+// ---------------------------------------------------------------------------
+template <class T>
+__global__ void close_kernel(const void* __restrict__ pp, const void* __restrict__ vv,
+                             void* __restrict__ b, int64_t nvec) {
+  constexpr int EPV = T::kEPV;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    uint4 v = ld16(static_cast<const char*>(vv) + i * 16);
+    if (pp) {
+      uint4 a = ld16(static_cast<const char*>(pp) + i * 16);
+      float fa[EPV], fv[EPV];
+      T::unpack(a, fa);
+      T::unpack(v, fv);
+      #pragma unroll
+      for (int e = 0; e < EPV; ++e) fa[e] += fv[e];
+      v = T::pack(fa);
+    }
+    st16(static_cast<char*>(b) + i * 16, v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (called from api.hip).
+// ---------------------------------------------------------------------------
+
+static Geom make_geom(int64_t R, int64_t D, int esize, int vpl, int waves_per_group_max) {
+  Geom g;
+  g.R = R;
+  g.D = (int)D;
+  g.V = (int)(D * esize / 16);
+  g.W = (g.V + 64 * vpl - 1) / (64 * vpl);
+  g.RPW = g.W >= waves_per_group_max ? 1 : waves_per_group_max / g.W;
+  g.groups = (R + g.RPW - 1) / g.RPW;
+  g.invD = 1.0f / (float)D;
+  return g;
+}
+
+static unsigned grid_for(const Geom& g) {
+  // one workgroup per row group; the hardware spreads them over the 256 CUs
+  // (round-robin across the 8 XCDs); cap keeps the grid-stride loop short
+  const int64_t cap = 1 << 20;
+  return (unsigned)(g.groups < cap ? g.groups : cap);
+}
+
+hipError_t launch_fold(const float* w, const float* g, float* q, int64_t count, hipStream_t st) {
+  const int64_t blocks = (count + 255) / 256;
+  hipLaunchKernelGGL(fold_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, st,
+                     w, g, q, count);
+  return hipGetLastError();
+}
+
+template <class T, int VPL, int NMAX, int SB>
+static hipError_t launch_phase1_t(Phase1Params& p, hipStream_t st) {
+  const int nv = SB * NMAX + NMAX;
+  const size_t lds = p.g.W > 1 ? (size_t)p.g.RPW * p.g.W * nv * sizeof(float) : 0;
+  hipLaunchKernelGGL((phase1_kernel<T, VPL, NMAX, SB>), dim3(grid_for(p.g)),
+                     dim3(64 * p.g.W * p.g.RPW), lds, st, p);
+  return hipGetLastError();
+}
+
+// Phase 1 for n <= 16 sources. Returns hipErrorInvalidValue if the shape is
+// beyond the register-resident kernel (the caller then falls back).
+template <class T>
+static hipError_t launch_phase1_dt(const void* const* src, int n, int64_t R, int64_t D,
+                                   const float* W, const float* G, int S, float eps, void* out,
+                                   float* m_out, float* lse_out, hipStream_t st) {
+  Phase1Params p;
+  for (int i = 0; i < 16; ++i) p.src[i] = i < n ? src[i] : nullptr;
+  p.n = n; p.S = S; p.Wq = W; p.G = G; p.eps = eps;
+  p.out = out; p.m_out = m_out; p.lse_out = lse_out;
+  if (n <= 8) {
+    p.g = make_geom(R, D, T::kBytes, 2, 4);
+    if (p.g.W > 8) return hipErrorInvalidValue;
+    // exact source count: no idle register slots; the query batch shrinks as
+    // the resident sources grow so the kernel stays within 256 VGPRs
+    switch (n) {
+      case 1: return launch_phase1_t<T, 2, 1, 8>(p, st);
+      case 2: return launch_phase1_t<T, 2, 2, 8>(p, st);
+      case 3: return launch_phase1_t<T, 2, 3, 8>(p, st);
+      case 4: return launch_phase1_t<T, 2, 4, 8>(p, st);
+      case 5: return launch_phase1_t<T, 2, 5, 4>(p, st);
+      case 6: return launch_phase1_t<T, 2, 6, 4>(p, st);
+      case 7: return launch_phase1_t<T, 2, 7, 2>(p, st);
+      default: return launch_phase1_t<T, 2, 8, 2>(p, st);
+    }
+  }
+  if (n <= 16) {
+    p.g = make_geom(R, D, T::kBytes, 1, 4);
+    if (p.g.W > 8) return hipErrorInvalidValue;
+    return launch_phase1_t<T, 1, 16, 1>(p, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_phase1(int dtype, const void* const* src, int n, int64_t R, int64_t D,
+                         const float* W, const float* G, int S, float eps, void* out, float* m_out,
+                         float* lse_out, hipStream_t st) {
+  return dtype == 1 ? launch_phase1_dt<Bf16>(src, n, R, D, W, G, S, eps, out, m_out, lse_out, st)
+                    : launch_phase1_dt<F32>(src, n, R, D, W, G, S, eps, out, m_out, lse_out, st);
+}
+
+bool phase1_supported(int dtype, int n, int64_t D) {
+  const int es = dtype == 1 ? 2 : 4;
+  if (n < 1 || n > 16) return false;
+  const Geom g = make_geom(1, D, es, n <= 8 ? 2 : 1, 4);
+  return g.W <= 8;
+}
+
+template <class T, int VPL, int G>
+static hipError_t launch_agg_t(AggParams& p, hipStream_t st) {
+  const size_t lds = p.g.W > 1 ? (size_t)p.g.RPW * p.g.W * 2 * G * sizeof(float) : 0;
+  hipLaunchKernelGGL((aggregate_kernel<T, VPL, G>), dim3(grid_for(p.g)), dim3(64 * p.g.W * p.g.RPW),
+                     lds, st, p);
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t launch_aggregate_dt(const void* const* src, int n, int64_t R, int64_t D,
+                                      const float* w, const float* gm, float eps, void* out,
+                                      float* m_out, float* lse_out, hipStream_t st) {
+  AggParams p;
+  for (int i = 0; i < 64; ++i) p.src[i] = i < n ? src[i] : nullptr;
+  p.n = n; p.w = w; p.gm = gm; p.eps = eps; p.out = out; p.m_out = m_out; p.lse_out = lse_out;
+  p.g = make_geom(R, D, T::kBytes, 2, 4);
+  if (p.g.W > 8) {
+    // widest rows: four vectors per lane and groups of four sources
+    p.g = make_geom(R, D, T::kBytes, 4, 4);
+    if (p.g.W > 8) return hipErrorInvalidValue;
+    return launch_agg_t<T, 4, 4>(p, st);
+  }
+  if (n <= 2) return launch_agg_t<T, 2, 2>(p, st);
+  if (n <= 4) return launch_agg_t<T, 2, 4>(p, st);
+  return launch_agg_t<T, 2, 8>(p, st);
+}
+
+hipError_t launch_aggregate(int dtype, const void* const* src, int n, int64_t R, int64_t D,
+                            const float* w, const float* gm, float eps, void* out, float* m_out,
+                            float* lse_out, hipStream_t st) {
+  return dtype == 1 ? launch_aggregate_dt<Bf16>(src, n, R, D, w, gm, eps, out, m_out, lse_out, st)
+                    : launch_aggregate_dt<F32>(src, n, R, D, w, gm, eps, out, m_out, lse_out, st);
+}
+
+template <class T, int VPL, bool HP>
+static hipError_t launch_ph2_t(Phase2Params& p, hipStream_t st) {
+  const size_t lds = p.g.W > 1 ? (size_t)p.g.RPW * p.g.W * 2 * sizeof(float) : 0;
+  hipLaunchKernelGGL((phase2_kernel<T, VPL, HP>), dim3(grid_for(p.g)), dim3(64 * p.g.W * p.g.RPW),
+                     lds, st, p);
+  return hipGetLastError();
+}
+
+template <class T, bool HP>
+static hipError_t launch_ph2_vpl(Phase2Params& p, int vpl, hipStream_t st) {
+  switch (vpl) {
+    case 1: return launch_ph2_t<T, 1, HP>(p, st);
+    case 2: return launch_ph2_t<T, 2, HP>(p, st);
+    case 3: return launch_ph2_t<T, 3, HP>(p, st);
+    case 4: return launch_ph2_t<T, 4, HP>(p, st);
+    case 5: return launch_ph2_t<T, 5, HP>(p, st);
+    case 6: return launch_ph2_t<T, 6, HP>(p, st);
+    case 7: return launch_ph2_t<T, 7, HP>(p, st);
+    default: return launch_ph2_t<T, 8, HP>(p, st);
+  }
+}
+
+template <class T>
+static hipError_t launch_phase2_dt(const void* o, const float* lse, const float* w,
+                                   const float* gm, float eps, const void* p_prev,
+                                   const void* v_prev, void* p_out, void* h_out, int64_t R,
+                                   int64_t D, hipStream_t st) {
+  Phase2Params p;
+  p.o = o; p.lse = lse; p.w = w; p.gm = gm; p.eps = eps;
+  p.p_prev = p_prev; p.v_prev = v_prev; p.p_out = p_out; p.h_out = h_out;
+  // waves per row: fewest with at most 8 vectors per lane; then the vectors
+  // per lane that cover the row with those waves
+  const int V = (int)(D * T::kBytes / 16);
+  const int W = (V + 511) / 512;
+  const int vpl = (V + 64 * W - 1) / (64 * W);
+  p.g = make_geom(R, D, T::kBytes, vpl, 4);
+  if (p.g.W != W || W > 4) return hipErrorInvalidValue;
+  return p_prev ? launch_ph2_vpl<T, true>(p, vpl, st) : launch_ph2_vpl<T, false>(p, vpl, st);
+}
+
+hipError_t launch_phase2(int dtype, const void* o, const float* lse, const float* w,
+                         const float* gm, float eps, const void* p_prev, const void* v_prev,
+                         void* p_out, void* h_out, int64_t R, int64_t D, hipStream_t st) {
+  return dtype == 1
+             ? launch_phase2_dt<Bf16>(o, lse, w, gm, eps, p_prev, v_prev, p_out, h_out, R, D, st)
+             : launch_phase2_dt<F32>(o, lse, w, gm, eps, p_prev, v_prev, p_out, h_out, R, D, st);
+}
+
+hipError_t launch_close(int dtype, const void* p, const void* v, void* b, int64_t R, int64_t D,
+                        hipStream_t st) {
+  const int64_t nvec = R * D * (dtype == 1 ? 2 : 4) / 16;
+  if (nvec == 0) return hipSuccess;
+  int64_t blocks = (nvec + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (dtype == 1)
+    hipLaunchKernelGGL(close_kernel<Bf16>, dim3((unsigned)blocks), dim3(256), 0, st, p, v, b, nvec);
+  else
+    hipLaunchKernelGGL(close_kernel<F32>, dim3((unsigned)blocks), dim3(256), 0, st, p, v, b, nvec);
+  return hipGetLastError();
+}
+
+}  // namespace attnres

@@ -1,0 +1,212 @@
+/*
+ * attnres.h -- C ABI of libattnres, the gfx950 (MI355X) library for the
+ * Attention Residuals (AttnRes) depth-aggregation hot path.
+ *
+ * Pages cited (title, then section / equation):
+ *   [K3] K3 course notes, section "Attention Residual 深度残差":
+ *        9.1 eqs. (A1)-(A4); 9.2 DepthResidual; 9.3 Full vs Block and
+ *        forward_naive; 9.4 the two-phase algorithm, eqs. (OS1), (OS2);
+ *        9.6 atomic_block_size and config validation.
+ *   [WC] "Attention Residuals" survey page (wineandchord.com): "Block
+ *        AttnRes", "Online softmax keeps the two phases exact", "Depth
+ *        attention & online merge reference", "Inference: block
+ *        representations as a depth KV cache".
+ *   [RH] Reading notes on "Attention Residuals" (ranhao.site), 4.2
+ *        Inference: Phase 1 and Phase 2.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers unless marked (host). A token tensor
+ *     [B, T, D] is passed as R = B*T rows of D contiguous elements ("[R,D]",
+ *     row-major, row r = b*T + t). Rows are independent: attention weights are
+ *     per token and never mix positions [K3 9.1].
+ *   - dtype selects the I/O element type of every [R,D] tensor of a call:
+ *     ATTNRES_F32 or ATTNRES_BF16. Queries, gains and statistics are always
+ *     fp32. Arithmetic is fp32; bf16 results are rounded nearest-even.
+ *   - D*sizeof(dtype) must be a multiple of 16 bytes and at most
+ *     ATTNRES_MAX_ROW_BYTES; every pointer must be 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call validates ALL of its arguments before it enqueues anything,
+ *     then enqueues its kernels asynchronously on `stream` and returns.
+ *     Nothing here allocates, frees or synchronises device memory; the caller
+ *     owns every buffer and the library keeps no pointer after a call returns.
+ *   - Return value: ATTNRES_OK, or a negative status with nothing enqueued
+ *     (for ATTNRES_EINVAL / EUNSUPPORTED / EWORKSPACE) and a detail message in
+ *     attnres_last_error() (thread-local). R == 0 is a successful no-op once
+ *     the shape, count and eps arguments are valid; tensor pointers are then
+ *     not inspected (they may be NULL) and no callback is invoked.
+ *     Asynchronous device faults surface at the caller's next synchronisation.
+ *     NaN / Inf inputs are not checked; their results are unspecified.
+ *   - eps must be finite and >= 0. The score of a source v under the folded
+ *     query q~ = w * gamma is  q~ . v / sqrt(mean_d(v^2) + eps)  [K3 (A1),
+ *     9.2 (1)-(2); WC reference code: eps inside the root, mean over D].
+ */
+#ifndef ATTNRES_H
+#define ATTNRES_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTNRES_F32 0
+#define ATTNRES_BF16 1
+
+#define ATTNRES_OK 0
+#define ATTNRES_EINVAL (-1)       /* an argument is out of its documented domain */
+#define ATTNRES_EUNSUPPORTED (-2) /* valid but beyond this build's limits         */
+#define ATTNRES_EWORKSPACE (-3)   /* workspace smaller than required              */
+#define ATTNRES_EHIP (-4)         /* a HIP launch / runtime call failed            */
+#define ATTNRES_ECALLBACK (-5)    /* the sublayer callback returned nonzero        */
+
+#define ATTNRES_MAX_SOURCES 64     /* sources of one aggregate / Phase-1 call   */
+#define ATTNRES_MAX_ROW_BYTES 32768 /* D * sizeof(dtype) upper bound            */
+
+/* ---------------------------------------------------------------------------
+ * attnres_aggregate -- one depth aggregation per token row [K3 9.1 (A1)-(A3),
+ * 9.2 DepthResidual.forward; WC depth_summary + finish]:
+ *     s_i = q~ . v_i / sqrt(mean_d(v_i^2) + eps),  q~ = w * gamma (fp32)
+ *     a   = softmax_i(s)                            (over the source axis)
+ *     out = sum_i a_i v_i                           (the RAW sources)
+ *   sources (host) : n device pointers, each [R,D] dtype (1 <= n <= 64)
+ *   w, gamma       : [D] fp32 query and RMSNorm gain; gamma NULL means ones
+ *   out            : [R,D] dtype, may not alias a source
+ *   m_out, lse_out : [R] fp32 or NULL: max_i s_i and m + log(sum_i e^(s_i-m))
+ *                    [K3 9.4 (OS1); RH 4.2]
+ * ------------------------------------------------------------------------- */
+int attnres_aggregate(const void* const* sources, int n, int64_t R, int64_t D, int dtype,
+                      const float* w, const float* gamma, float eps, void* out, float* m_out,
+                      float* lse_out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * attnres_phase1_batched -- Phase 1 of two-phase Block AttnRes: the S
+ * pseudo-queries of one block, stacked into [S,D], each aggregate the same
+ * fixed list of completed sources [b_0 .. b_k] in one pass over them; returns
+ * each query's normalised output and its max / log-sum-exp statistics
+ * [K3 9.4 step 1 and _run_block_two_phase; RH 4.2 Phase 1; WC "Inference"].
+ *   blocks (host)  : n device pointers [R,D] dtype (b_0 = the embedding)
+ *   W, Gamma       : [S,D] fp32 queries and gains (Gamma NULL means ones)
+ *   out            : [S,R,D] dtype; out[s] = sum_i a_{s,i} b_i
+ *   m_out, lse_out : [S,R] fp32; m_out may be NULL, lse_out is required
+ *   1 <= S <= 1024.
+ * ------------------------------------------------------------------------- */
+int attnres_phase1_batched(const void* const* blocks, int n, int64_t R, int64_t D, int dtype,
+                           const float* W, const float* Gamma, int S, float eps, void* out,
+                           float* m_out, float* lse_out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * attnres_phase2_merge -- Phase 2 of two-phase Block AttnRes for one
+ * sublayer [K3 9.4 step 2, eq. (OS2), single_source_stats; RH 4.2 Phase 2]:
+ *     p   = p_prev ? round(p_prev + v_prev) : v_prev      (partial, I/O dtype)
+ *     s_p = q~ . p / sqrt(mean_d(p^2) + eps)             (score of the ROUNDED p)
+ *     h   = OS2 merge of the Phase-1 group (lse, o, 1) with (s_p, p, 1), normalised:
+ *           M = max(lse, s_p), h = (e^(lse-M) o + e^(s_p-M) p) / (e^(lse-M) + e^(s_p-M))
+ *   o, lse         : this sublayer's Phase-1 output [R,D] dtype and lse [R] fp32
+ *   w, gamma       : [D] fp32 (gamma NULL means ones)
+ *   p_prev         : [R,D] partial before this sublayer's update, or NULL for the
+ *                    first merge of a block (then p := v_prev, p_out must be NULL)
+ *   v_prev         : [R,D] the previous sublayer's output
+ *   p_out          : [R,D] receives p (may equal p_prev: in-place is safe); it may
+ *                    be NULL only when p_prev is NULL
+ *   h_out          : [R,D] dtype; must not alias o, p_prev, v_prev or p_out
+ * ------------------------------------------------------------------------- */
+int attnres_phase2_merge(const void* o, const float* lse, const float* w, const float* gamma,
+                         float eps, const void* p_prev, const void* v_prev, void* p_out,
+                         void* h_out, int64_t R, int64_t D, int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Sublayer callback of the stack forward: eq. (A4) v_l = f_l(h_l) [K3 9.1].
+ * Called on the calling thread with l = 1..L in order. h_l is a device [R,D]
+ * dtype buffer inside the workspace, valid until the callback returns; the
+ * callback must consume it with work enqueued on `stream` (or synchronise).
+ * It stores in *v_out a 16-byte aligned device pointer to v_l [R,D] dtype and
+ * returns 0; a nonzero return aborts the forward with ATTNRES_ECALLBACK.
+ * The library enqueues its last read of v_l before it invokes the callback for
+ * sublayer l+2, so a 3-slot ring written on the same stream is safe -- except
+ * for S == 1 with block_sums == NULL, where every v_l stays a source (below).
+ * ------------------------------------------------------------------------- */
+typedef int (*attnres_sublayer_fn)(void* ctx, int l, const void* h_l, const void** v_out,
+                                   void* stream);
+
+/* Built-in callback for pre-computed sublayer outputs: ctx is a (host) array
+ * of L device pointers, v_l = ((const void* const*)ctx)[l-1]; h_l is ignored. */
+int attnres_table_sublayer(void* ctx, int l, const void* h_l, const void** v_out, void* stream);
+
+/* Bytes of workspace attnres_block_stack_forward needs for (L, S, R, D, dtype);
+ * 0 for invalid arguments. */
+size_t attnres_stack_workspace_bytes(int L, int S, int64_t R, int64_t D, int dtype);
+
+/* ---------------------------------------------------------------------------
+ * attnres_block_stack_forward -- the Block AttnRes stack forward, two-phase
+ * [K3 9.3 forward_naive semantics, 9.4 _run_block_two_phase; WC "Block
+ * AttnRes", "Online softmax"], Full AttnRes when S == 1 [WC: N = L limit].
+ *   Sublayers l = 1..L are cut into nb = ceil(L/S) blocks of S (the last may
+ *   be short). Block k (0-based) runs Phase 1 with its queries over
+ *   [b_0 .. b_k], hands h = o_0 to its first sublayer, then for each further
+ *   sublayer merges the running partial by Phase 2; after its last sublayer
+ *   b_{k+1} = round(p + v_last) is stored. Finally
+ *   y = aggregate([b_0 .. b_nb]; q~_{L+1}) [K3 9.1 is_final_aggregate].
+ *   x          : [R,D] dtype, the embedding b_0
+ *   W, Gamma   : [L+1, D] fp32; row l-1 belongs to sublayer l, row L to the
+ *                final aggregate (Gamma NULL means ones)
+ *   f, f_ctx   : sublayer callback (see above)
+ *   block_sums : (host) nb device pointers [R,D] receiving b_1..b_nb, or NULL
+ *                only when S == 1 (then b_l is v_l itself and every v_l must
+ *                stay valid for the whole call)
+ *   y          : [R,D] dtype
+ *   workspace  : device scratch of at least attnres_stack_workspace_bytes()
+ *                bytes, 256-byte aligned; contents on return are unspecified
+ *   Limits: 1 <= S, 1 <= L, nb + 1 <= ATTNRES_MAX_SOURCES.
+ *   A failure after work was enqueued (ATTNRES_ECALLBACK, ATTNRES_EHIP) leaves
+ *   that work enqueued and the outputs undefined.
+ * ------------------------------------------------------------------------- */
+int attnres_block_stack_forward(const void* x, int L, int S, int64_t R, int64_t D, int dtype,
+                                const float* W, const float* Gamma, float eps,
+                                attnres_sublayer_fn f, void* f_ctx, void* const* block_sums,
+                                void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * attnres_block_layout -- the integer plan of forward_naive [K3 9.3 listing;
+ * WC "Block AttnRes"]. block_start[k] (host, nb+1 entries or NULL) is the
+ * first sublayer (1-based) of block k, with block_start[nb] = L + 1.
+ * n_sources[l-1] (host, L+1 entries or NULL) is the number of sources sublayer
+ * l attends over (k+1 completed, plus the partial once it exists);
+ * n_sources[L] is the final aggregate's, nb + 1. Returns nb, or a negative
+ * status for L < 1 or S < 1.
+ * ------------------------------------------------------------------------- */
+int attnres_block_layout(int L, int S, int* block_start, int* n_sources);
+
+/* DecoderBlock count -> atomic sublayers per block [K3 9.6 atomic_block_size]:
+ * each DecoderBlock is an attention and an MLP sublayer; layers_per_block <= 0
+ * stands for "None", which targets about eight blocks: max(1, ceil(L/8)).
+ * Returns ATTNRES_EINVAL for num_decoder_layers < 1. */
+int attnres_atomic_block_size(int num_decoder_layers, int layers_per_block);
+
+/* Static description of a status code. */
+const char* attnres_status_string(int code);
+
+/* Detail message of the last failing call on this thread ("" if none). */
+const char* attnres_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Optional launch timing (instrumentation for benchmarks; off by default).
+ * attnres_timing_enable(capacity) makes this thread's subsequent launches
+ * record a HIP event pair around each kernel on its stream, for up to
+ * `capacity` launches (0 disables and releases the events). The library keeps
+ * per-kind totals: kind 0 Phase 1, 1 Phase 2, 2 aggregate, 3 block close,
+ * 4 query fold. attnres_timing_read synchronises the recorded events and
+ * returns, for `kind`, the number of timed launches, their summed duration in
+ * milliseconds and their summed algorithmic bytes (inputs read once plus
+ * outputs written once, queries excluded). attnres_timing_reset clears the
+ * totals and the recorded events.
+ * ------------------------------------------------------------------------- */
+int attnres_timing_enable(int capacity);
+int attnres_timing_reset(void);
+int attnres_timing_read(int kind, int64_t* launches, double* total_ms, double* total_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNRES_H */

@@ -1,0 +1,172 @@
+"""CPU-side tests of the C ABI: the library loads, exports every symbol the
+header declares, rejects invalid arguments before touching the GPU, and its
+integer plan matches the oracle's bit for bit. No compute call runs here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from depth_wise_attention_rms_amd import binding as b
+from depth_wise_attention_rms_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attnres.h")
+
+FAKE = ctypes.c_void_p(0x10000)     # aligned, never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"\b(attnres_[a-z0-9_]+)\s*\(", text))
+    names.discard("attnres_sublayer_fn")
+    return sorted(names)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge",
+                     "attnres_block_stack_forward"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = b.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), f"libattnres.so does not export {name}"
+    assert set(declared_functions()) == set(b.EXPORTS)
+
+
+def test_inputs_library_loads():
+    L = inputs.lib()
+    for name in ("attnres_inputs_fill_normal", "attnres_inputs_gather_rows",
+                 "attnres_inputs_ring_sublayer", "attnres_inputs_record_sublayer"):
+        assert hasattr(L, name)
+
+
+def _last():
+    return b.lib().attnres_last_error().decode()
+
+
+def _agg(n=2, R=4, D=16, dt=1, w=FAKE, out=FAKE, eps=1e-8, srcs=None, m=None, lse=None):
+    arr = (ctypes.c_void_p * max(n, 1))(*([0x20000 + 0x1000 * i for i in range(max(n, 1))] if srcs is None else srcs))
+    return b.lib().attnres_aggregate(arr, n, R, D, dt, w, None, eps, out, m, lse, None)
+
+
+@pytest.mark.parametrize("kwargs,code,msg", [
+    (dict(n=0), -1, "n = 0"),
+    (dict(n=65), -1, "n = 65"),
+    (dict(R=-1), -1, "R = -1"),
+    (dict(D=12), -1, "D = 12"),
+    (dict(D=4, dt=1), -1, "D = 4"),
+    (dict(dt=7), -1, "dtype"),
+    (dict(w=None), -1, "w is NULL"),
+    (dict(out=None), -1, "out is NULL"),
+    (dict(out=MISALIGNED), -1, "not 16-byte aligned"),
+    (dict(eps=-1.0), -1, "eps"),
+    (dict(eps=float("nan")), -1, "eps"),
+    (dict(D=16384 + 8), -2, "exceeds"),
+    (dict(srcs=[0x20000, 0x20008]), -1, "not 16-byte aligned"),
+    (dict(srcs=[0x20000, 0x10000]), -1, "aliases"),
+    (dict(m=MISALIGNED), -1, "m_out"),
+])
+def test_aggregate_rejects_invalid_arguments(kwargs, code, msg):
+    assert _agg(**kwargs) == code
+    assert msg in _last()
+
+
+def test_zero_rows_is_a_successful_noop():
+    assert _agg(R=0) == 0
+    assert b.lib().attnres_phase2_merge(FAKE, FAKE, FAKE, None, 1e-8, None, ctypes.c_void_p(0x50000),
+                                        None, ctypes.c_void_p(0x60000), 0, 16, 1, None) == 0
+
+
+def test_phase1_rejects_invalid_arguments():
+    L = b.lib()
+    arr = (ctypes.c_void_p * 2)(0x20000, 0x30000)
+    assert L.attnres_phase1_batched(arr, 2, 4, 16, 1, FAKE, None, 0, 1e-8, FAKE, None, FAKE, None) == -1
+    assert "S = 0" in _last()
+    assert L.attnres_phase1_batched(arr, 2, 4, 16, 1, FAKE, None, 3, 1e-8, FAKE, None, None, None) == -1
+    assert "lse_out is NULL" in _last()
+
+
+def test_phase2_rejects_invalid_arguments():
+    L = b.lib()
+    f = L.attnres_phase2_merge
+    # p_out required when p_prev is given
+    assert f(FAKE, FAKE, FAKE, None, 1e-8, ctypes.c_void_p(0x50000), FAKE, None,
+             ctypes.c_void_p(0x60000), 4, 16, 1, None) == -1
+    assert "p_out is NULL" in _last()
+    # p_out must be NULL on the first merge
+    assert f(FAKE, FAKE, FAKE, None, 1e-8, None, ctypes.c_void_p(0x50000), ctypes.c_void_p(0x70000),
+             ctypes.c_void_p(0x60000), 4, 16, 1, None) == -1
+    # h_out may not alias an input
+    assert f(FAKE, FAKE, FAKE, None, 1e-8, None, ctypes.c_void_p(0x50000), None, FAKE, 4, 16, 1, None) == -1
+    assert "aliases" in _last()
+
+
+def test_stack_rejects_invalid_arguments():
+    L = b.lib()
+    fn = ctypes.cast(L.attnres_table_sublayer, ctypes.c_void_p)
+    ws_need = L.attnres_stack_workspace_bytes(8, 4, 4, 16, 1)
+    bs = (ctypes.c_void_p * 2)(0x80000, 0x90000)
+    ws = ctypes.c_void_p(0x100000)
+
+    def call(Lr=8, S=4, block_sums=bs, ws_bytes=ws_need, workspace=ws, f=fn):
+        return L.attnres_block_stack_forward(FAKE, Lr, S, 4, 16, 1, FAKE, None, 1e-8, f, None,
+                                             block_sums, ctypes.c_void_p(0xA0000), workspace,
+                                             ws_bytes, None)
+    assert call(S=0) == -1
+    assert call(Lr=0) == -1
+    assert call(block_sums=None) == -1 and "block_sums" in _last()
+    assert call(ws_bytes=ws_need - 1) == -3
+    assert call(workspace=ctypes.c_void_p(0x100010)) == -1 and "256-byte" in _last()
+    assert call(f=None) == -1
+    assert call(Lr=64, S=1, block_sums=None) == -1 and "exceed" in _last()
+
+
+def test_status_strings():
+    L = b.lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.attnres_status_string(code).decode() != "unknown status"
+
+
+def test_plan_matches_oracle_bit_exactly():
+    for L in range(1, 40):
+        for S in range(1, L + 3):
+            nb, starts, ns = b.attnres_block_layout(L, S)
+            onb, ostarts, ons = oracle.block_plan(L, S)
+            assert nb == onb and starts == list(ostarts) and ns == list(ons), (L, S)
+    for Ldec in range(1, 200):
+        for per in (None, 1, 2, 3, 12):
+            assert b.attnres_atomic_block_size(Ldec, per) == oracle.atomic_block_size(Ldec, per)
+
+
+def test_workspace_bytes_cover_the_regions():
+    L = b.lib()
+    R, D = 16384, 4096
+    ws = L.attnres_stack_workspace_bytes(48, 8, R, D, 1)
+    row = R * D * 2
+    assert ws >= 8 * row + row + row + 49 * D * 4 + 2 * 8 * R * 4
+    assert L.attnres_stack_workspace_bytes(0, 8, R, D, 1) == 0
+    assert L.attnres_stack_workspace_bytes(16, 1, 2048, 1024, 1) >= 2048 * 1024 * 2
+
+
+def test_generator_twin_rounding_and_distribution():
+    # bf16 rounding of the twin equals torch's nearest-even fp32 -> bf16 for fp32 values
+    import torch
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(20000) * 7).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(inputs.bf16_bits(x.astype(np.float64)), ref)
+    z = inputs.normal(0, inputs.ROLE_V, 3, np.arange(400000))
+    assert abs(z.mean()) < 0.01 and abs(z.std() - 1) < 0.01
+    u = inputs.uniform(0, inputs.ROLE_SCALE, 0, np.arange(100000))
+    assert u.min() >= 0 and u.max() < 1 and abs(u.mean() - 0.5) < 0.01
+    # distinct streams differ, the same stream repeats
+    assert not np.array_equal(inputs.normal(0, 2, 1, np.arange(10)), inputs.normal(0, 2, 2, np.arange(10)))
+    assert np.array_equal(inputs.normal(5, 2, 1, np.arange(10)), inputs.normal(5, 2, 1, np.arange(10)))

@@ -1,0 +1,304 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Every comparison uses the rule of tests/parity.py (scaled error <= 1e-5 for
+fp32 and 1e-2 for bf16 outputs; stats within 1e-5 (1+|ref|); block sums, the
+single-source aggregate and h_1 bit-exact). Inputs come from the seeded
+generator (device fill kernels or the numpy twin); the oracle reads exactly
+the bits the GPU read. Full-size workloads are checked on sampled rows
+(row 0, row R-1 and seeded others) in the launch configuration the benchmark
+times.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from depth_wise_attention_rms_amd import binding as b
+from depth_wise_attention_rms_amd import inputs
+from depth_wise_attention_rms_amd.workload import EPS, DeviceStack
+from tests.parity import (assert_close_scaled, assert_stats, sample_rows, to_device, to_host,
+                          widen)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    b.lib()
+    inputs.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def host_src(seed, role, layer, rows, D, sigma, dtype):
+    return inputs.tensor_rows(seed, role, layer, np.arange(rows), D, sigma, dtype)
+
+
+# ----------------------------------------------------------------------------
+# generator
+# ----------------------------------------------------------------------------
+
+def test_generator_device_matches_twin():
+    announce("generator")
+    for dtype, rows, D, scale in (("bf16", 64, 1024, 1.0), ("bf16", 7, 7168, 3.7), ("f32", 32, 256, 10.0)):
+        t = torch.empty((rows, D), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
+        inputs.fill_normal(t, 0, inputs.ROLE_V, 5, scale)
+        assert np.array_equal(to_host(t), inputs.tensor_rows(0, inputs.ROLE_V, 5, np.arange(rows), D, scale, dtype))
+    # row-id fill equals the same rows of a full fill
+    full = torch.empty((300, 512), dtype=torch.bfloat16, device="cuda")
+    inputs.fill_normal(full, 3, inputs.ROLE_X, 0, 2.0)
+    ids = torch.tensor([0, 17, 299, 150], dtype=torch.int64, device="cuda")
+    part = torch.empty((4, 512), dtype=torch.bfloat16, device="cuda")
+    inputs.fill_normal(part, 3, inputs.ROLE_X, 0, 2.0, row_ids=ids)
+    assert torch.equal(part, full[ids])
+
+
+# ----------------------------------------------------------------------------
+# aggregate
+# ----------------------------------------------------------------------------
+
+def _run_aggregate(srcs_host, w, gamma, dtype):
+    srcs = [to_device(s) for s in srcs_host]
+    R = srcs_host[0].shape[0]
+    m = torch.empty(R, dtype=torch.float32, device="cuda")
+    lse = torch.empty(R, dtype=torch.float32, device="cuda")
+    out, _, _ = b.attnres_aggregate(srcs, torch.from_numpy(w).cuda(),
+                                    None if gamma is None else torch.from_numpy(gamma).cuda(),
+                                    eps=EPS, m_out=m, lse_out=lse)
+    torch.cuda.synchronize()
+    return to_host(out), to_host(m), to_host(lse)
+
+
+@pytest.mark.parametrize("zero_query", [False, True])
+def test_aggregate_single_config(zero_query):
+    """Single aggregate workload: n = 4 sources N(0, s^2), s in {1, 3, 0.3, 10},
+    B = 2, T = 64, D = 256, fp32, gain U(0.5, 1.5), query N(0, 0.02^2) and an
+    all-zero run."""
+    wl = inputs.WORKLOADS["aggregate_n4"]
+    announce(f"aggregate_n4 zero_query={zero_query}")
+    R, D = wl.R, wl.D
+    srcs = []
+    for i, s in enumerate(wl.src_sigmas):
+        t = torch.empty((R, D), dtype=torch.float32, device="cuda")
+        inputs.fill_normal(t, wl.seed, inputs.ROLE_SRC, i, s)
+        srcs.append(to_host(t))
+    w = np.zeros(D, np.float32) if zero_query else inputs.queries(wl.seed, 1, D)[0]
+    gamma = inputs.gains(wl.seed, D)
+    h, m, lse = _run_aggregate(srcs, w, gamma, "f32")
+    ref = oracle.aggregate(srcs, w, gamma, eps=EPS)
+    assert_close_scaled(h, ref["h"], ref["scale"], "f32", "aggregate h")
+    assert_stats(m, ref["m"], "aggregate m")
+    assert_stats(lse, ref["lse"], "aggregate lse")
+    if zero_query:
+        mean = np.mean([widen(s) for s in srcs], axis=0)
+        assert np.max(np.abs(h - mean) / ref["scale"]) <= 1e-5
+
+
+AGG_CASES = [
+    # (n, R, D, dtype)
+    (1, 37, 520, "bf16"), (2, 37, 520, "bf16"), (3, 300, 1024, "bf16"), (5, 130, 4096, "bf16"),
+    (8, 65, 7168, "bf16"), (9, 65, 4096, "bf16"), (17, 130, 1024, "bf16"), (33, 9, 2048, "bf16"),
+    (64, 5, 264, "bf16"), (4, 3, 12288, "bf16"), (11, 3, 16384, "bf16"), (1, 1, 8, "bf16"),
+    (2, 37, 516, "f32"), (7, 130, 4096, "f32"), (17, 33, 1024, "f32"), (3, 5, 8188, "f32"),
+]
+
+
+@pytest.mark.parametrize("n,R,D,dtype", AGG_CASES)
+def test_aggregate_sweep(n, R, D, dtype):
+    announce(f"aggregate n={n} R={R} D={D} {dtype}")
+    rng_sig = [0.1 + 0.7 * i for i in range(n)]
+    srcs = [host_src(11, inputs.ROLE_SRC, i, R, D, rng_sig[i], dtype) for i in range(n)]
+    w = inputs.queries(11 + n, 1, D, sigma=0.05)[0]
+    gamma = inputs.gains(11, D) if n % 2 else None
+    h, m, lse = _run_aggregate(srcs, w, gamma, dtype)
+    ref = oracle.aggregate(srcs, w, gamma, eps=EPS)
+    assert_close_scaled(h, ref["h"], ref["scale"], dtype, f"aggregate n={n}")
+    assert_stats(m, ref["m"], "m")
+    assert_stats(lse, ref["lse"], "lse")
+    if n == 1:
+        assert np.array_equal(h, srcs[0]), "a one-source aggregate must return the source bit for bit"
+
+
+# ----------------------------------------------------------------------------
+# Phase 1 and Phase 2 in isolation
+# ----------------------------------------------------------------------------
+
+PH1_CASES = [
+    # (n, S, R, D, dtype)
+    (1, 8, 37, 4096, "bf16"), (2, 8, 37, 264, "bf16"), (3, 5, 130, 1024, "bf16"),
+    (4, 12, 65, 7168, "bf16"), (5, 8, 65, 4096, "bf16"), (6, 8, 130, 4096, "bf16"),
+    (7, 3, 33, 7168, "bf16"), (8, 24, 17, 7168, "bf16"), (9, 4, 17, 1024, "bf16"),
+    (12, 12, 9, 4096, "bf16"), (16, 2, 9, 4096, "bf16"), (20, 3, 5, 2048, "bf16"),
+    (6, 8, 3, 16384, "bf16"), (3, 1, 1, 8, "bf16"),
+    (2, 8, 37, 516, "f32"), (6, 8, 65, 4096, "f32"), (8, 5, 9, 2048, "f32"), (13, 4, 9, 1024, "f32"),
+]
+
+
+@pytest.mark.parametrize("n,S,R,D,dtype", PH1_CASES)
+def test_phase1_sweep(n, S, R, D, dtype):
+    announce(f"phase1 n={n} S={S} R={R} D={D} {dtype}")
+    srcs = [host_src(21, inputs.ROLE_SRC, i, R, D, 1.0 + 0.5 * i, dtype) for i in range(n)]
+    W = inputs.queries(21 + S, S, D, sigma=0.05)
+    G = np.stack([inputs.gains(21, D, layer=s) for s in range(S)]) if n % 2 == 0 else None
+    out, m, lse = b.attnres_phase1_batched(
+        [to_device(s) for s in srcs], torch.from_numpy(W).cuda(),
+        None if G is None else torch.from_numpy(G).cuda(), eps=EPS,
+        m_out=torch.empty((S, R), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    ref = oracle.phase1(srcs, W, G, eps=EPS)
+    o_h, m_h, l_h = to_host(out), to_host(m), to_host(lse)
+    for s in range(S):
+        assert_close_scaled(o_h[s], ref["o"][s], ref["scale"][s], dtype, f"phase1 o[{s}]")
+    assert_stats(m_h, ref["m"], "phase1 m")
+    assert_stats(l_h, ref["lse"], "phase1 lse")
+
+
+PH2_CASES = [
+    # (R, D, dtype, has_prev, inplace)
+    (65, 4096, "bf16", False, False), (65, 4096, "bf16", True, False), (65, 4096, "bf16", True, True),
+    (37, 7168, "bf16", True, True), (130, 1000, "bf16", True, False), (3, 16384, "bf16", True, True),
+    (1, 8, "bf16", True, False), (300, 520, "bf16", False, False),
+    (65, 4096, "f32", True, True), (37, 1028, "f32", False, False),
+]
+
+
+@pytest.mark.parametrize("R,D,dtype,has_prev,inplace", PH2_CASES)
+def test_phase2_sweep(R, D, dtype, has_prev, inplace):
+    announce(f"phase2 R={R} D={D} {dtype} prev={has_prev} inplace={inplace}")
+    o = host_src(31, inputs.ROLE_AUX, 1, R, D, 1.0, dtype)
+    v = host_src(31, inputs.ROLE_AUX, 2, R, D, 3.0, dtype)
+    p = host_src(31, inputs.ROLE_AUX, 3, R, D, 2.0, dtype) if has_prev else None
+    lse = (2.0 * inputs.normal(31, inputs.ROLE_AUX, 4, np.arange(R))).astype(np.float32)
+    w = inputs.queries(31, 1, D, sigma=0.3 / math.sqrt(D / 64))[0]
+    gamma = inputs.gains(31, D)
+    o_d, v_d = to_device(o), to_device(v)
+    p_d = None if p is None else to_device(p)
+    p_out = p_d if (inplace and p_d is not None) else None
+    h, p_res = b.attnres_phase2_merge(o_d, torch.from_numpy(lse).cuda(), torch.from_numpy(w).cuda(),
+                                      v_d, p_prev=p_d, gamma=torch.from_numpy(gamma).cuda(), eps=EPS,
+                                      p_out=p_out)
+    torch.cuda.synchronize()
+    ref = oracle.phase2(o, lse, w, p, v, gamma, eps=EPS)
+    assert_close_scaled(to_host(h), ref["h"], ref["scale"], dtype, "phase2 h")
+    if has_prev:
+        assert np.array_equal(to_host(p_res), ref["p"]), "partial p must be bit-exact"
+
+
+# ----------------------------------------------------------------------------
+# stack forward
+# ----------------------------------------------------------------------------
+
+def _check_stack(ds: DeviceStack, rows: np.ndarray, chunk=64, nthreads=None):
+    """Run the stack recording ``rows`` of every h_l, then compare h_l, y and
+    the block sums at those rows with the oracle's naive forward."""
+    wl = ds.wl
+    ds.forward(ds.recorder(rows))
+    torch.cuda.synchronize()
+    ids = torch.from_numpy(rows).cuda()
+    rec = to_host(ds.rec)
+    y = to_host(ds.y[ids])
+    bsums = None if ds.block_sums is None else [to_host(t[ids]) for t in ds.block_sums]
+    xr, vr = ds.host_rows(rows)
+    worst = 0.0
+    for c0 in range(0, len(rows), chunk):
+        sl = slice(c0, c0 + chunk)
+        ref = oracle.block_stack(xr[sl], [a[sl] for a in vr], ds.W_host, wl.S, eps=EPS,
+                                 nthreads=nthreads)
+        for l in range(wl.L):
+            worst = max(worst, assert_close_scaled(rec[l, sl], ref["h"][l], ref["h_scale"][l],
+                                                   wl.dtype, f"{wl.name} h_{l + 1}"))
+        worst = max(worst, assert_close_scaled(y[sl], ref["y"], ref["y_scale"], wl.dtype, f"{wl.name} y"))
+        assert np.array_equal(rec[0, sl], xr[sl]), "h_1 must equal the embedding bit for bit"
+        if bsums is not None:
+            for k in range(ref["nb"]):
+                assert np.array_equal(bsums[k][sl], ref["block_sums"][k]), f"block sum b_{k + 1} differs"
+    return worst
+
+
+def test_stack_bruteforce_grid():
+    """Every L <= 7 and S <= L+1 on 3 rows, D in {8, 16, 64}, both dtypes."""
+    for dtype in ("bf16", "f32"):
+        for D in (8, 16, 64):
+            for L in range(1, 8):
+                for S in range(1, L + 2):
+                    wl = inputs.Workload(f"grid_L{L}_S{S}_D{D}_{dtype}", "stack", B=1, T=3, D=D,
+                                         dtype=dtype, L=L, S=S, seed=L * 100 + S)
+                    ds = DeviceStack(wl, W_host=inputs.queries(L, L + 1, D, sigma=0.4))
+                    _check_stack(ds, np.arange(3))
+
+
+def test_stack_full_config():
+    """Full AttnRes stack: 16 sublayers + embedding, B = 4, T = 512, D = 1024, bf16; all rows."""
+    wl = inputs.WORKLOADS["full_L16"]
+    announce(wl.name)
+    ds = DeviceStack(wl)
+    _check_stack(ds, np.arange(wl.R), chunk=512)
+
+
+def test_stack_block_prefill_config():
+    """Block two-phase prefill: L = 48, S = 8, B = 8, T = 2048, D = 4096, bf16;
+    512 sampled rows, in the benchmark's launch configuration."""
+    wl = inputs.WORKLOADS["block_L48_S8"]
+    announce(wl.name)
+    ds = DeviceStack(wl)
+    _check_stack(ds, sample_rows(wl.R, 512), chunk=128)
+
+
+def test_stack_decode_config():
+    """Block decode regime: L = 96, S = 12, 128 rows, D = 7168, bf16; all rows."""
+    wl = inputs.WORKLOADS["decode_L96_S12"]
+    announce(wl.name)
+    ds = DeviceStack(wl)
+    _check_stack(ds, np.arange(wl.R), chunk=64)
+
+
+def test_stack_long_context_config():
+    """Long-context Block: L = 186, S = 24, T = 131072, D = 7168, bf16, sublayer
+    outputs generated per sublayer into a ring; 256 sampled rows."""
+    wl = inputs.WORKLOADS["long_L186_S24"]
+    announce(wl.name)
+    ds = DeviceStack(wl)
+    _check_stack(ds, sample_rows(wl.R, 256), chunk=32)
+    del ds
+    torch.cuda.empty_cache()
+
+
+def test_stack_is_deterministic():
+    wl = inputs.Workload("det", "stack", B=2, T=1000, D=4096, dtype="bf16", L=20, S=6)
+    announce("determinism")
+    ds = DeviceStack(wl)
+    ds.forward()
+    y1 = ds.y.clone()
+    b1 = [t.clone() for t in ds.block_sums]
+    ds.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, ds.y)
+    assert all(torch.equal(a, c) for a, c in zip(b1, ds.block_sums))
+
+
+def test_stack_zero_rows_and_callback_failure():
+    wl = inputs.Workload("small", "stack", B=1, T=5, D=64, dtype="bf16", L=6, S=3)
+    announce("callback failure")
+    ds = DeviceStack(wl)
+
+    def failing(l, h):
+        if l == 3:
+            raise RuntimeError("planted failure")
+        return ds.v[l - 1]
+    with pytest.raises(b.AttnResError) as e:
+        b.attnres_block_stack_forward(ds.x, ds.W, 3, failing, eps=EPS, block_sums=ds.block_sums,
+                                      y=ds.y, workspace=ds.workspace)
+    assert e.value.code == -5 and "l = 3" in e.value.detail
+    torch.cuda.synchronize()
+    # R == 0 is a no-op
+    x0 = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    y0, _ = b.attnres_block_stack_forward(x0, ds.W, 3, [x0] * 6, eps=EPS)
+    assert y0.shape == (0, 64)
