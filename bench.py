@@ -58,8 +58,12 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="block_L48_S8")
-    ap.add_argument("--cpu-rows", type=int, default=2048,
+    ap.add_argument("--cpu-rows", type=int, default=6144,
                     help="token rows of the CPU-oracle baseline sample (0 disables it)")
+    ap.add_argument("--calibration-copy-gib", type=float, default=0.0,
+                    help="before the steps, copy a tensor of this many GiB with torch (a plain "
+                         "copy kernel of known size, read once and written once) so hardware "
+                         "counters of the same run can be scaled to bytes")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -84,6 +88,15 @@ def main() -> int:
     ds = DeviceStack(wl)
     nb = ds.nb
     stream = torch.cuda.current_stream()
+
+    if args.calibration_copy_gib > 0:
+        n = int(args.calibration_copy_gib * (1 << 30)) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         ds.forward()

@@ -22,6 +22,10 @@ ARCH = "gfx950"
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-Wall", "-Wno-unused-function", "-I", INCLUDE,
+    # fuse a*b+c only inside one expression: a score stored and then offset by
+    # the running max stays separately rounded, so the max source gets exactly
+    # exp(0) = 1 and a one-source aggregate returns its source bit for bit
+    "-ffp-contract=on",
     # keep hipcc from forming packed-fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
@@ -45,9 +49,10 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False, extra_flags=()) -> dict:
+def build(verbose: bool = False, extra_flags=(), out_dir: str = PKG) -> dict:
+    """Compile every library into ``out_dir`` (the package directory by default)."""
     out = {}
-    objdir = os.path.join(PKG, "_build")
+    objdir = os.path.join(out_dir, "_build")
     os.makedirs(objdir, exist_ok=True)
     jobs = []
     for lib, srcs in LIBS.items():
@@ -62,7 +67,7 @@ def build(verbose: bool = False, extra_flags=()) -> dict:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     paths = {}
     for lib, objs in out.items():
-        path = os.path.join(PKG, lib)
+        path = os.path.join(out_dir, lib)
         _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", path + ".tmp"], verbose)
         os.replace(path + ".tmp", path)
         paths[lib] = path

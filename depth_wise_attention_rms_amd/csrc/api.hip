@@ -14,24 +14,14 @@
 #include <vector>
 
 #include "attnres.h"
+#include "launch.hpp"
 
 #define ATTNRES_API extern "C" __attribute__((visibility("default")))
 
-namespace attnres {
-hipError_t launch_fold(const float* w, const float* g, float* q, int64_t count, hipStream_t st);
-hipError_t launch_phase1(int dtype, const void* const* src, int n, int64_t R, int64_t D,
-                         const float* W, const float* G, int S, float eps, void* out, float* m_out,
-                         float* lse_out, hipStream_t st);
-bool phase1_supported(int dtype, int n, int64_t D);
-hipError_t launch_aggregate(int dtype, const void* const* src, int n, int64_t R, int64_t D,
-                            const float* w, const float* gm, float eps, void* out, float* m_out,
-                            float* lse_out, hipStream_t st);
-hipError_t launch_phase2(int dtype, const void* o, const float* lse, const float* w,
-                         const float* gm, float eps, const void* p_prev, const void* v_prev,
-                         void* p_out, void* h_out, int64_t R, int64_t D, hipStream_t st);
-hipError_t launch_close(int dtype, const void* p, const void* v, void* b, int64_t R, int64_t D,
-                        hipStream_t st);
-}  // namespace attnres
+using attnres::AggArgs;
+using attnres::Launch;
+using attnres::Phase1Args;
+using attnres::Phase2Args;
 
 namespace {
 
@@ -67,7 +57,8 @@ int check_shape(const char* fn, int64_t R, int64_t D, int dtype, float eps) {
   if (D * es > ATTNRES_MAX_ROW_BYTES)
     return fail(ATTNRES_EUNSUPPORTED, "%s: row of %lld bytes exceeds %d", fn, (long long)(D * es),
                 ATTNRES_MAX_ROW_BYTES);
-  if (!std::isfinite(eps) || eps < 0.f) return fail(ATTNRES_EINVAL, "%s: eps must be finite and >= 0", fn);
+  if (!std::isfinite(eps) || eps < 0.f)
+    return fail(ATTNRES_EINVAL, "%s: eps must be finite and >= 0", fn);
   return ATTNRES_OK;
 }
 
@@ -77,9 +68,9 @@ int check_ptr(const char* fn, const char* name, const void* p, bool required) {
   return ATTNRES_OK;
 }
 
-#define TRY(expr)                  \
-  do {                             \
-    int rc_ = (expr);              \
+#define TRY(expr)                      \
+  do {                                 \
+    int rc_ = (expr);                  \
     if (rc_ != ATTNRES_OK) return rc_; \
   } while (0)
 
@@ -90,7 +81,7 @@ enum Kind { K_PHASE1 = 0, K_PHASE2 = 1, K_AGG = 2, K_CLOSE = 3, K_FOLD = 4, K_CO
 
 struct Timing {
   int capacity = 0;
-  std::vector<hipEvent_t> ev;  // 2 per slot
+  std::vector<hipEvent_t> ev;  // 2 per slot: the kernel's start and end
   std::vector<int> kind;
   std::vector<double> bytes;
   int used = 0;
@@ -100,67 +91,42 @@ struct Timing {
 };
 thread_local Timing g_timing;
 
-struct TimedLaunch {
-  int slot = -1;
-  hipStream_t st;
-  TimedLaunch(int kind, double bytes, hipStream_t s) : st(s) {
-    Timing& t = g_timing;
-    if (t.capacity > 0 && t.used < t.capacity) {
-      slot = t.used++;
-      t.kind[slot] = kind;
-      t.bytes[slot] = bytes;
-      hipEventRecord(t.ev[2 * slot], st);
-    }
+// The Launch of one kernel: when timing is on and a slot is free, it carries
+// an event pair that the dispatch itself stamps (no extra queue packets).
+Launch timed_launch(int kind, double bytes, hipStream_t st) {
+  Launch L{st, nullptr, nullptr};
+  Timing& t = g_timing;
+  if (t.capacity > 0 && t.used < t.capacity) {
+    const int slot = t.used++;
+    t.kind[slot] = kind;
+    t.bytes[slot] = bytes;
+    L.start = t.ev[2 * slot];
+    L.stop = t.ev[2 * slot + 1];
   }
-  ~TimedLaunch() {
-    if (slot >= 0) hipEventRecord(g_timing.ev[2 * slot + 1], st);
-  }
-};
+  return L;
+}
 
 int hip_fail(const char* fn, hipError_t e) {
   return fail(ATTNRES_EHIP, "%s: %s", fn, hipGetErrorString(e));
 }
 
 // ---------------------------------------------------------------------------
-// the three kernel families with their byte accounting
+// the kernel families with their algorithmic byte accounting: inputs read
+// once plus outputs written once; a fused block close counts its reference
+// traffic (p and v read, b written) in the launch that performs it
 // ---------------------------------------------------------------------------
-int do_aggregate(const char* fn, const void* const* src, int n, int64_t R, int64_t D, int dtype,
-                 const float* w, const float* g, float eps, void* out, float* m_out,
-                 float* lse_out, hipStream_t st) {
-  if (R == 0) return ATTNRES_OK;
-  const double rb = (double)R * D * esize_of(dtype);
-  TimedLaunch tl(K_AGG, rb * (n + 1) + (double)R * ((m_out ? 4 : 0) + (lse_out ? 4 : 0)), st);
-  hipError_t e = attnres::launch_aggregate(dtype, src, n, R, D, w, g, eps, out, m_out, lse_out, st);
-  return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
+double close_bytes(double rb, const void* close_p, const void* close_v) {
+  // the reference close reads p and v and writes b; the launch's own read of
+  // b as a source is counted with its sources (the fusion saves that read)
+  return close_v ? rb * (close_p ? 3 : 2) : 0.0;
 }
 
-int do_phase1(const char* fn, const void* const* src, int n, int64_t R, int64_t D, int dtype,
-              const float* W, const float* G, int S, float eps, void* out, float* m_out,
-              float* lse_out, hipStream_t st) {
-  if (R == 0) return ATTNRES_OK;
-  const int64_t row_bytes = D * esize_of(dtype);
-  if (attnres::phase1_supported(dtype, n, D)) {
-    const double rb = (double)R * row_bytes;
-    TimedLaunch tl(K_PHASE1, rb * (n + S) + (double)R * S * ((m_out ? 4 : 0) + 4), st);
-    hipError_t e = attnres::launch_phase1(dtype, src, n, R, D, W, G, S, eps, out, m_out, lse_out, st);
-    return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
-  }
-  // More sources than the register-resident pass holds: one aggregate per query.
-  for (int s = 0; s < S; ++s) {
-    TRY(do_aggregate(fn, src, n, R, D, dtype, W + (int64_t)s * D, G ? G + (int64_t)s * D : nullptr,
-                     eps, static_cast<char*>(out) + (int64_t)s * R * row_bytes,
-                     m_out ? m_out + (int64_t)s * R : nullptr, lse_out + (int64_t)s * R, st));
-  }
-  return ATTNRES_OK;
-}
-
-int do_phase2(const char* fn, const void* o, const float* lse, const float* w, const float* g,
-              float eps, const void* p_prev, const void* v_prev, void* p_out, void* h_out,
-              int64_t R, int64_t D, int dtype, hipStream_t st) {
-  if (R == 0) return ATTNRES_OK;
-  const double rb = (double)R * D * esize_of(dtype);
-  TimedLaunch tl(K_PHASE2, rb * (p_prev ? 5 : 3) + (double)R * 4, st);
-  hipError_t e = attnres::launch_phase2(dtype, o, lse, w, g, eps, p_prev, v_prev, p_out, h_out, R, D, st);
+int do_aggregate(const char* fn, int dtype, const AggArgs& a, hipStream_t st) {
+  if (a.R == 0) return ATTNRES_OK;
+  const double rb = (double)a.R * a.D * esize_of(dtype);
+  const double bytes = rb * (a.n + 1) + (double)a.R * ((a.m_out ? 4 : 0) + (a.lse_out ? 4 : 0)) +
+                       close_bytes(rb, a.close_p, a.close_v);
+  hipError_t e = attnres::launch_aggregate(dtype, a, timed_launch(K_AGG, bytes, st));
   return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
 }
 
@@ -168,8 +134,38 @@ int do_close(const char* fn, const void* p, const void* v, void* b, int64_t R, i
              int dtype, hipStream_t st) {
   if (R == 0) return ATTNRES_OK;
   const double rb = (double)R * D * esize_of(dtype);
-  TimedLaunch tl(K_CLOSE, rb * (p ? 3 : 2), st);
-  hipError_t e = attnres::launch_close(dtype, p, v, b, R, D, st);
+  hipError_t e = attnres::launch_close(dtype, p, v, b, R, D, timed_launch(K_CLOSE, rb * (p ? 3 : 2), st));
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
+}
+
+int do_phase1(const char* fn, int dtype, const Phase1Args& a, hipStream_t st) {
+  if (a.R == 0) return ATTNRES_OK;
+  const int64_t row_bytes = a.D * esize_of(dtype);
+  if (attnres::phase1_supported(dtype, a.n, a.D)) {
+    const double rb = (double)a.R * row_bytes;
+    const double bytes = rb * (a.n + a.S) + (double)a.R * a.S * ((a.m_out ? 4 : 0) + 4) +
+                         close_bytes(rb, a.close_p, a.close_v);
+    hipError_t e = attnres::launch_phase1(dtype, a, timed_launch(K_PHASE1, bytes, st));
+    return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
+  }
+  // More sources than the register-resident pass holds: close separately,
+  // then one aggregate per query.
+  if (a.close_v) TRY(do_close(fn, a.close_p, a.close_v, a.close_b, a.R, a.D, dtype, st));
+  for (int s = 0; s < a.S; ++s) {
+    AggArgs g{a.src, a.n, a.R, a.D, a.W + (int64_t)s * a.D, a.G ? a.G + (int64_t)s * a.D : nullptr,
+              a.eps, static_cast<char*>(a.out) + (int64_t)s * a.R * row_bytes,
+              a.m_out ? a.m_out + (int64_t)s * a.R : nullptr, a.lse_out + (int64_t)s * a.R,
+              nullptr, nullptr, nullptr};
+    TRY(do_aggregate(fn, dtype, g, st));
+  }
+  return ATTNRES_OK;
+}
+
+int do_phase2(const char* fn, int dtype, const Phase2Args& a, hipStream_t st) {
+  if (a.R == 0) return ATTNRES_OK;
+  const double rb = (double)a.R * a.D * esize_of(dtype);
+  const double bytes = rb * (a.p_prev ? 5 : 3) + (double)a.R * 4;
+  hipError_t e = attnres::launch_phase2(dtype, a, timed_launch(K_PHASE2, bytes, st));
   return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
 }
 
@@ -253,8 +249,8 @@ ATTNRES_API int attnres_aggregate(const void* const* sources, int n, int64_t R, 
   TRY(check_ptr(fn, "out", out, true));
   TRY(check_ptr(fn, "m_out", m_out, false));
   TRY(check_ptr(fn, "lse_out", lse_out, false));
-  TRY(do_aggregate(fn, sources, n, R, D, dtype, w, gamma, eps, out, m_out, lse_out,
-                   static_cast<hipStream_t>(stream)));
+  AggArgs a{sources, n, R, D, w, gamma, eps, out, m_out, lse_out, nullptr, nullptr, nullptr};
+  TRY(do_aggregate(fn, dtype, a, static_cast<hipStream_t>(stream)));
   return ok();
 }
 
@@ -275,8 +271,8 @@ ATTNRES_API int attnres_phase1_batched(const void* const* blocks, int n, int64_t
   TRY(check_ptr(fn, "out", out, true));
   TRY(check_ptr(fn, "m_out", m_out, false));
   TRY(check_ptr(fn, "lse_out", lse_out, true));
-  TRY(do_phase1(fn, blocks, n, R, D, dtype, W, Gamma, S, eps, out, m_out, lse_out,
-                static_cast<hipStream_t>(stream)));
+  Phase1Args a{blocks, n, R, D, W, Gamma, S, eps, out, m_out, lse_out, nullptr, nullptr, nullptr};
+  TRY(do_phase1(fn, dtype, a, static_cast<hipStream_t>(stream)));
   return ok();
 }
 
@@ -300,8 +296,8 @@ ATTNRES_API int attnres_phase2_merge(const void* o, const float* lse, const floa
     return fail(ATTNRES_EINVAL, "%s: h_out aliases an input or p_out", fn);
   if (p_out && (p_out == o || p_out == v_prev))
     return fail(ATTNRES_EINVAL, "%s: p_out aliases o or v_prev", fn);
-  TRY(do_phase2(fn, o, lse, w, gamma, eps, p_prev, v_prev, p_out, h_out, R, D, dtype,
-                static_cast<hipStream_t>(stream)));
+  Phase2Args a{o, lse, w, gamma, eps, p_prev, v_prev, p_out, h_out, R, D};
+  TRY(do_phase2(fn, dtype, a, static_cast<hipStream_t>(stream)));
   return ok();
 }
 
@@ -372,27 +368,35 @@ ATTNRES_API int attnres_block_stack_forward(const void* x, int L, int S, int64_t
   float* LSE = reinterpret_cast<float*>(ws + lay.lse);
   void* P = ws + lay.p;
   void* H = ws + lay.h;
-  const int64_t row_bytes = D * es;
-  const int64_t tensor_bytes = R * row_bytes;
+  const int64_t tensor_bytes = R * D * es;
 
   {  // fold q~ = w * gamma once for all L+1 queries [K3 9.2 (1)]
-    TimedLaunch tl(K_FOLD, (double)(L + 1) * D * (Gamma ? 12 : 8), st);
-    hipError_t e = attnres::launch_fold(W, Gamma, Q, (int64_t)(L + 1) * D, st);
+    hipError_t e = attnres::launch_fold(
+        W, Gamma, Q, (int64_t)(L + 1) * D,
+        timed_launch(K_FOLD, (double)(L + 1) * D * (Gamma ? 12 : 8), st));
     if (e != hipSuccess) return hip_fail(fn, e);
   }
 
-  std::vector<const void*> src;
-  src.reserve(nb + 1);
-  src.push_back(x);
   auto call = [&](int l, const void* h, const void** v) -> int {
     const void* out = nullptr;
     const int rc = f(f_ctx, l, h, &out, stream);
-    if (rc != 0) return fail(ATTNRES_ECALLBACK, "%s: sublayer callback returned %d at l = %d", fn, rc, l);
+    if (rc != 0)
+      return fail(ATTNRES_ECALLBACK, "%s: sublayer callback returned %d at l = %d", fn, rc, l);
     if (!out || !aligned16(out))
       return fail(ATTNRES_ECALLBACK, "%s: callback gave a NULL or misaligned v at l = %d", fn, l);
     *v = out;
     return ATTNRES_OK;
   };
+
+  // src[0..k] are the completed sources seen by block k. The close of block
+  // k-1 (b_k = p + v_last) is fused into block k's first launch, which forms
+  // b_k from (p, v_last) as its last source and stores it to block_sums[k-1].
+  std::vector<const void*> src;
+  src.reserve(nb + 1);
+  src.push_back(x);
+  const void* close_p = nullptr;
+  const void* close_v = nullptr;
+  void* close_b = nullptr;
 
   for (int k = 0; k < nb; ++k) {
     const int start = k * S + 1;
@@ -402,58 +406,63 @@ ATTNRES_API int attnres_block_stack_forward(const void* x, int L, int S, int64_t
     const float* Qk = Q + (int64_t)(start - 1) * D;
     if (Sk == 1) {
       // a one-sublayer block: a single aggregate over the completed sources
-      TRY(do_aggregate(fn, src.data(), n, R, D, dtype, Qk, nullptr, eps, H, nullptr, nullptr, st));
+      AggArgs a{src.data(), n, R, D, Qk, nullptr, eps, H, nullptr, nullptr,
+                close_p, close_v, close_b};
+      TRY(do_aggregate(fn, dtype, a, st));
       const void* v = nullptr;
       TRY(call(start, H, &v));
-      if (block_sums) {
-        TRY(do_close(fn, nullptr, v, block_sums[k], R, D, dtype, st));
+      if (block_sums) {  // b_{k+1} = v, copied by the next launch
+        close_p = nullptr;
+        close_v = v;
+        close_b = block_sums[k];
         src.push_back(block_sums[k]);
-      } else {
+      } else {  // S == 1 without block_sums: the outputs themselves are the sources
+        close_v = nullptr;
         src.push_back(v);
       }
       continue;
     }
     // Phase 1: the block's Sk queries over [b_0 .. b_k] in one pass
-    TRY(do_phase1(fn, src.data(), n, R, D, dtype, Qk, nullptr, Sk, eps, O, M, LSE, st));
+    Phase1Args a1{src.data(), n, R, D, Qk, nullptr, Sk, eps, O, M, LSE, close_p, close_v, close_b};
+    TRY(do_phase1(fn, dtype, a1, st));
     const void* v_first = nullptr;
     TRY(call(start, O, &v_first));  // h_start = o_0: no partial yet
     const void* p_cur = v_first;    // p_1 = v_start (aliased, no copy)
     const void* v_prev = v_first;
     for (int j = 1; j < Sk; ++j) {
       const int l = start + j;
-      const void* o_j = O + (int64_t)j * tensor_bytes;
-      const float* lse_j = LSE + (int64_t)j * R;
-      const float* q_l = Q + (int64_t)(l - 1) * D;
-      if (j == 1) {
-        TRY(do_phase2(fn, o_j, lse_j, q_l, nullptr, eps, nullptr, v_prev, nullptr, H, R, D, dtype, st));
-      } else {
-        TRY(do_phase2(fn, o_j, lse_j, q_l, nullptr, eps, p_cur, v_prev, P, H, R, D, dtype, st));
-        p_cur = P;
-      }
+      Phase2Args a2{O + (int64_t)j * tensor_bytes, LSE + (int64_t)j * R, Q + (int64_t)(l - 1) * D,
+                    nullptr, eps, j == 1 ? nullptr : p_cur, v_prev, j == 1 ? nullptr : P, H, R, D};
+      TRY(do_phase2(fn, dtype, a2, st));
+      if (j > 1) p_cur = P;
       const void* v = nullptr;
       TRY(call(l, H, &v));
       v_prev = v;
     }
-    // close: b_{k+1} = p + v_end
-    TRY(do_close(fn, p_cur, v_prev, block_sums[k], R, D, dtype, st));
+    // b_{k+1} = p + v_end, formed by the next launch
+    close_p = p_cur;
+    close_v = v_prev;
+    close_b = block_sums[k];
     src.push_back(block_sums[k]);
   }
   // final aggregate over [b_0 .. b_nb] [K3 9.1 is_final_aggregate]
-  TRY(do_aggregate(fn, src.data(), nb + 1, R, D, dtype, Q + (int64_t)L * D, nullptr, eps, y,
-                   nullptr, nullptr, st));
+  AggArgs af{src.data(), nb + 1, R, D, Q + (int64_t)L * D, nullptr, eps, y, nullptr, nullptr,
+             close_p, close_v, close_b};
+  TRY(do_aggregate(fn, dtype, af, st));
   return ok();
 }
 
 ATTNRES_API int attnres_timing_enable(int capacity) {
   Timing& t = g_timing;
-  for (hipEvent_t e : t.ev) hipEventDestroy(e);
+  for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
   t = Timing();
   if (capacity <= 0) return ok();
-  t.ev.resize(2 * (size_t)capacity);
+  t.ev.resize(2 * (size_t)capacity, nullptr);
   for (auto& e : t.ev) {
     hipError_t rc = hipEventCreate(&e);
     if (rc != hipSuccess) {
-      t.ev.clear();
+      for (hipEvent_t x : t.ev)
+        if (x) (void)hipEventDestroy(x);
       t = Timing();
       return hip_fail("attnres_timing_enable", rc);
     }
@@ -493,7 +502,8 @@ ATTNRES_API int attnres_timing_reset(void) {
 
 ATTNRES_API int attnres_timing_read(int kind, int64_t* launches, double* total_ms,
                                     double* total_bytes) {
-  if (kind < 0 || kind >= K_COUNT) return fail(ATTNRES_EINVAL, "attnres_timing_read: kind %d", kind);
+  if (kind < 0 || kind >= K_COUNT)
+    return fail(ATTNRES_EINVAL, "attnres_timing_read: kind %d", kind);
   TRY(collect_timing());
   const Timing& t = g_timing;
   if (launches) *launches = t.launches[kind];

@@ -1,9 +1,10 @@
 // kernels.hip -- gfx950 kernels of the AttnRes depth-aggregation hot path.
 //
 // Pages: K3 course notes, section "Attention Residual 深度残差" (eqs. A1-A3,
-// OS1, OS2; 9.4 two-phase algorithm); "Attention Residuals" survey page on
-// wineandchord.com ("Depth attention & online merge reference"); reading notes
-// on "Attention Residuals" (ranhao.site) 4.2 Inference.
+// OS1, OS2; 9.3 forward_naive; 9.4 two-phase algorithm); "Attention
+// Residuals" survey page on wineandchord.com ("Depth attention & online merge
+// reference"); reading notes on "Attention Residuals" (ranhao.site) 4.2
+// Inference.
 //
 // Work decomposition. Every kernel is bandwidth-shaped: it streams [R,D] rows
 // and does a short per-row contraction. A token row is owned by W waves
@@ -12,8 +13,12 @@
 // memory. Rows are independent (weights are per token), so a workgroup of
 // RPW*W waves walks RPW rows at a time in a grid-stride loop and no data moves
 // between workgroups. Row-wide sums (sum of squares, dot products) reduce with
-// DPP inside a wave and through LDS across the W waves of a row.
+// DPP inside a wave and through LDS across the W waves of a row. [R,D] tensors
+// are read and written with non-temporal hints; queries go through the caches.
+#include <hip/hip_ext.h>
+
 #include "device.hpp"
+#include "launch.hpp"
 
 #include <float.h>
 
@@ -42,6 +47,35 @@ struct Lanes {
   }
 };
 
+// The block close b = round(p + v) (or b = v when p is null) performed by a
+// kernel on the fly for its last source [K3 9.3 listing]: the closing block
+// sum is computed from the partial and the last sublayer output, stored once,
+// and used as a source without being read back.
+struct Close {
+  const void* p;  // partial before the block's last sublayer, or null
+  const void* v;  // the block's last sublayer output; null = no close
+  void* b;        // receives the block sum
+};
+
+// Load vector `off` of source i, applying the close when i is the closing one.
+template <class T>
+__device__ __forceinline__ uint4 load_source(const void* src, const Close& cl, bool closing,
+                                             int64_t off) {
+  if (!closing) return ld16_stream(static_cast<const char*>(src) + off);
+  uint4 v = ld16_stream(static_cast<const char*>(cl.v) + off);
+  if (cl.p) {
+    const uint4 a = ld16_stream(static_cast<const char*>(cl.p) + off);
+    float fa[T::kEPV], fv[T::kEPV];
+    T::unpack(a, fa);
+    T::unpack(v, fv);
+    #pragma unroll
+    for (int e = 0; e < T::kEPV; ++e) fa[e] += fv[e];
+    v = T::pack(fa);  // rounded to the I/O dtype, as the block sum is stored
+  }
+  st16_stream(static_cast<char*>(cl.b) + off, v);
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Query fold q~ = w * gamma in fp32 [K3 9.2 (1)], over `count` elements.
 // ---------------------------------------------------------------------------
@@ -52,7 +86,7 @@ __global__ void fold_kernel(const float* __restrict__ w, const float* __restrict
     q[i] = g ? w[i] * g[i] : w[i];
 }
 
-// Load EPV fp32 query values for vector `vec` of query row `qrow`, folding the gain.
+// Load EPV fp32 query values at element offset `off`, folding the gain.
 template <int EPV>
 __device__ __forceinline__ void load_query(const float* __restrict__ w, const float* __restrict__ g,
                                            int64_t off, float* q) {
@@ -84,6 +118,7 @@ struct Phase1Params {
   void* out;        // [S][R][D]
   float* m_out;     // [S][R] or null
   float* lse_out;   // [S][R]
+  Close cl;         // close computing source n-1, or cl.v == null
   Geom g;
 };
 
@@ -96,6 +131,7 @@ __global__ __launch_bounds__(512) void phase1_kernel(Phase1Params p) {
   const Lanes ln(g.W);
   const int64_t rowbytes = (int64_t)g.V * 16;
   const int n = p.n;
+  const bool has_close = p.cl.v != nullptr;
 
   for (int64_t grp = blockIdx.x; grp < g.groups; grp += gridDim.x) {
     const int64_t row = grp * g.RPW + ln.slot;
@@ -109,7 +145,8 @@ __global__ __launch_bounds__(512) void phase1_kernel(Phase1Params p) {
         const int vec = c * ln.stride + ln.t;
         uint4 u = make_uint4(0, 0, 0, 0);
         if (rv && i < n && vec < g.V)
-          u = ld16(static_cast<const char*>(p.src[i]) + row * rowbytes + (int64_t)vec * 16);
+          u = load_source<T>(p.src[i], p.cl, has_close && i == n - 1,
+                             row * rowbytes + (int64_t)vec * 16);
         T::unpack(u, x[i][c]);
       }
     }
@@ -184,7 +221,7 @@ __global__ __launch_bounds__(512) void phase1_kernel(Phase1Params p) {
                 for (int i = 0; i < NMAX; ++i)
                   #pragma unroll
                   for (int e = 0; e < EPV; ++e) o[e] += sc[i] * x[i][c][e];
-                st16(orow + (int64_t)vec * 16, T::pack(o));
+                st16_stream(orow + (int64_t)vec * 16, T::pack(o));
               }
             }
           }
@@ -210,6 +247,7 @@ struct AggParams {
   void* out;       // [R][D]
   float* m_out;    // [R] or null
   float* lse_out;  // [R] or null
+  Close cl;        // close computing source n-1, or cl.v == null
   Geom g;
 };
 
@@ -221,6 +259,7 @@ __global__ __launch_bounds__(512) void aggregate_kernel(AggParams p) {
   const Geom& g = p.g;
   const Lanes ln(g.W);
   const int64_t rowbytes = (int64_t)g.V * 16;
+  const bool has_close = p.cl.v != nullptr;
 
   // this lane's slice of the folded query, reused for every row
   float q[VPL][EPV];
@@ -254,7 +293,8 @@ __global__ __launch_bounds__(512) void aggregate_kernel(AggParams p) {
           const int vec = c * ln.stride + ln.t;
           uint4 u = make_uint4(0, 0, 0, 0);
           if (rv && i0 + j < p.n && vec < g.V)
-            u = ld16(static_cast<const char*>(p.src[i0 + j]) + row * rowbytes + (int64_t)vec * 16);
+            u = load_source<T>(p.src[i0 + j], p.cl, has_close && i0 + j == p.n - 1,
+                               row * rowbytes + (int64_t)vec * 16);
           T::unpack(u, x[j][c]);
         }
       }
@@ -306,7 +346,7 @@ __global__ __launch_bounds__(512) void aggregate_kernel(AggParams p) {
           float o[EPV];
           #pragma unroll
           for (int e = 0; e < EPV; ++e) o[e] = num[c][e] * rz;
-          st16(orow + (int64_t)vec * 16, T::pack(o));
+          st16_stream(orow + (int64_t)vec * 16, T::pack(o));
         }
       }
       if (ln.t == 0) {
@@ -355,19 +395,19 @@ __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
       const int vec = c * ln.stride + ln.t;
       const bool ok = rv && vec < g.V;
       const int64_t off = base + (int64_t)vec * 16;
-      uint4 v = ok ? ld16(static_cast<const char*>(p.v_prev) + off) : make_uint4(0, 0, 0, 0);
+      uint4 v = ok ? ld16_stream(static_cast<const char*>(p.v_prev) + off) : make_uint4(0, 0, 0, 0);
       if (HAS_PREV) {
-        uint4 a = ok ? ld16(static_cast<const char*>(p.p_prev) + off) : make_uint4(0, 0, 0, 0);
+        uint4 a = ok ? ld16_stream(static_cast<const char*>(p.p_prev) + off) : make_uint4(0, 0, 0, 0);
         float fa[EPV], fv[EPV];
         T::unpack(a, fa);
         T::unpack(v, fv);
         #pragma unroll
         for (int e = 0; e < EPV; ++e) fa[e] += fv[e];
         v = T::pack(fa);  // the partial, rounded to the I/O dtype
-        if (ok) st16(static_cast<char*>(p.p_out) + off, v);
+        if (ok) st16_stream(static_cast<char*>(p.p_out) + off, v);
       }
       pv[c] = v;
-      ov[c] = ok ? ld16(static_cast<const char*>(p.o) + off) : make_uint4(0, 0, 0, 0);
+      ov[c] = ok ? ld16_stream(static_cast<const char*>(p.o) + off) : make_uint4(0, 0, 0, 0);
     }
     float red[2] = {0.f, 0.f};
     #pragma unroll
@@ -402,7 +442,7 @@ __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
           T::unpack(pv[c], fp);
           #pragma unroll
           for (int e = 0; e < EPV; ++e) fo[e] = a * fo[e] + b * fp[e];
-          st16(static_cast<char*>(p.h_out) + base + (int64_t)vec * 16, T::pack(fo));
+          st16_stream(static_cast<char*>(p.h_out) + base + (int64_t)vec * 16, T::pack(fo));
         }
       }
     }
@@ -410,8 +450,8 @@ __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// Block close [K3 9.3 listing]: b = p + v rounded to the I/O dtype, or b = v
-// when p is null (a one-sublayer block). Elementwise over `nvec` vectors.
+// Stand-alone block close [K3 9.3 listing]: b = p + v rounded to the I/O
+// dtype, or b = v when p is null. Elementwise over `nvec` vectors.
 // ---------------------------------------------------------------------------
 template <class T>
 __global__ void close_kernel(const void* __restrict__ pp, const void* __restrict__ vv,
@@ -419,9 +459,9 @@ __global__ void close_kernel(const void* __restrict__ pp, const void* __restrict
   constexpr int EPV = T::kEPV;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec;
        i += (int64_t)gridDim.x * blockDim.x) {
-    uint4 v = ld16(static_cast<const char*>(vv) + i * 16);
+    uint4 v = ld16_stream(static_cast<const char*>(vv) + i * 16);
     if (pp) {
-      uint4 a = ld16(static_cast<const char*>(pp) + i * 16);
+      uint4 a = ld16_stream(static_cast<const char*>(pp) + i * 16);
       float fa[EPV], fv[EPV];
       T::unpack(a, fa);
       T::unpack(v, fv);
@@ -429,13 +469,17 @@ __global__ void close_kernel(const void* __restrict__ pp, const void* __restrict
       for (int e = 0; e < EPV; ++e) fa[e] += fv[e];
       v = T::pack(fa);
     }
-    st16(static_cast<char*>(b) + i * 16, v);
+    st16_stream(static_cast<char*>(b) + i * 16, v);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Host-side launchers (called from api.hip).
 // ---------------------------------------------------------------------------
+
+#ifndef ATTNRES_PHASE2_VPL
+#define ATTNRES_PHASE2_VPL 2  // preferred vectors per lane in Phase 2 (rows take up to 4 waves)
+#endif
 
 static Geom make_geom(int64_t R, int64_t D, int esize, int vpl, int waves_per_group_max) {
   Geom g;
@@ -456,61 +500,67 @@ static unsigned grid_for(const Geom& g) {
   return (unsigned)(g.groups < cap ? g.groups : cap);
 }
 
-hipError_t launch_fold(const float* w, const float* g, float* q, int64_t count, hipStream_t st) {
-  const int64_t blocks = (count + 255) / 256;
-  hipLaunchKernelGGL(fold_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, st,
-                     w, g, q, count);
+template <typename K, typename... Args>
+static hipError_t launch(const Launch& L, K kernel, dim3 grid, dim3 block, size_t lds,
+                         Args... args) {
+  if (L.start) {
+    // the start/stop events take the timestamps of this kernel's own dispatch
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, L.stream, L.start, L.stop, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, L.stream, args...);
+  }
   return hipGetLastError();
 }
 
+hipError_t launch_fold(const float* w, const float* g, float* q, int64_t count, const Launch& L) {
+  const int64_t blocks = (count + 255) / 256;
+  return launch(L, fold_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, w,
+                g, q, count);
+}
+
 template <class T, int VPL, int NMAX, int SB>
-static hipError_t launch_phase1_t(Phase1Params& p, hipStream_t st) {
+static hipError_t launch_phase1_t(Phase1Params& p, const Launch& L) {
   const int nv = SB * NMAX + NMAX;
   const size_t lds = p.g.W > 1 ? (size_t)p.g.RPW * p.g.W * nv * sizeof(float) : 0;
-  hipLaunchKernelGGL((phase1_kernel<T, VPL, NMAX, SB>), dim3(grid_for(p.g)),
-                     dim3(64 * p.g.W * p.g.RPW), lds, st, p);
-  return hipGetLastError();
+  return launch(L, phase1_kernel<T, VPL, NMAX, SB>, dim3(grid_for(p.g)),
+                dim3(64 * p.g.W * p.g.RPW), lds, p);
 }
 
 // Phase 1 for n <= 16 sources. Returns hipErrorInvalidValue if the shape is
 // beyond the register-resident kernel (the caller then falls back).
 template <class T>
-static hipError_t launch_phase1_dt(const void* const* src, int n, int64_t R, int64_t D,
-                                   const float* W, const float* G, int S, float eps, void* out,
-                                   float* m_out, float* lse_out, hipStream_t st) {
+static hipError_t launch_phase1_dt(const Phase1Args& a, const Launch& L) {
   Phase1Params p;
-  for (int i = 0; i < 16; ++i) p.src[i] = i < n ? src[i] : nullptr;
-  p.n = n; p.S = S; p.Wq = W; p.G = G; p.eps = eps;
-  p.out = out; p.m_out = m_out; p.lse_out = lse_out;
-  if (n <= 8) {
-    p.g = make_geom(R, D, T::kBytes, 2, 4);
+  for (int i = 0; i < 16; ++i) p.src[i] = i < a.n ? a.src[i] : nullptr;
+  p.n = a.n; p.S = a.S; p.Wq = a.W; p.G = a.G; p.eps = a.eps;
+  p.out = a.out; p.m_out = a.m_out; p.lse_out = a.lse_out;
+  p.cl = Close{a.close_p, a.close_v, a.close_b};
+  if (a.n <= 8) {
+    p.g = make_geom(a.R, a.D, T::kBytes, 2, 4);
     if (p.g.W > 8) return hipErrorInvalidValue;
     // exact source count: no idle register slots; the query batch shrinks as
     // the resident sources grow so the kernel stays within 256 VGPRs
-    switch (n) {
-      case 1: return launch_phase1_t<T, 2, 1, 8>(p, st);
-      case 2: return launch_phase1_t<T, 2, 2, 8>(p, st);
-      case 3: return launch_phase1_t<T, 2, 3, 8>(p, st);
-      case 4: return launch_phase1_t<T, 2, 4, 8>(p, st);
-      case 5: return launch_phase1_t<T, 2, 5, 4>(p, st);
-      case 6: return launch_phase1_t<T, 2, 6, 4>(p, st);
-      case 7: return launch_phase1_t<T, 2, 7, 2>(p, st);
-      default: return launch_phase1_t<T, 2, 8, 2>(p, st);
+    switch (a.n) {
+      case 1: return launch_phase1_t<T, 2, 1, 8>(p, L);
+      case 2: return launch_phase1_t<T, 2, 2, 8>(p, L);
+      case 3: return launch_phase1_t<T, 2, 3, 8>(p, L);
+      case 4: return launch_phase1_t<T, 2, 4, 8>(p, L);
+      case 5: return launch_phase1_t<T, 2, 5, 4>(p, L);
+      case 6: return launch_phase1_t<T, 2, 6, 4>(p, L);
+      case 7: return launch_phase1_t<T, 2, 7, 2>(p, L);
+      default: return launch_phase1_t<T, 2, 8, 2>(p, L);
     }
   }
-  if (n <= 16) {
-    p.g = make_geom(R, D, T::kBytes, 1, 4);
+  if (a.n <= 16) {
+    p.g = make_geom(a.R, a.D, T::kBytes, 1, 4);
     if (p.g.W > 8) return hipErrorInvalidValue;
-    return launch_phase1_t<T, 1, 16, 1>(p, st);
+    return launch_phase1_t<T, 1, 16, 1>(p, L);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_phase1(int dtype, const void* const* src, int n, int64_t R, int64_t D,
-                         const float* W, const float* G, int S, float eps, void* out, float* m_out,
-                         float* lse_out, hipStream_t st) {
-  return dtype == 1 ? launch_phase1_dt<Bf16>(src, n, R, D, W, G, S, eps, out, m_out, lse_out, st)
-                    : launch_phase1_dt<F32>(src, n, R, D, W, G, S, eps, out, m_out, lse_out, st);
+hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L) {
+  return dtype == 1 ? launch_phase1_dt<Bf16>(a, L) : launch_phase1_dt<F32>(a, L);
 }
 
 bool phase1_supported(int dtype, int n, int64_t D) {
@@ -521,98 +571,83 @@ bool phase1_supported(int dtype, int n, int64_t D) {
 }
 
 template <class T, int VPL, int G>
-static hipError_t launch_agg_t(AggParams& p, hipStream_t st) {
+static hipError_t launch_agg_t(AggParams& p, const Launch& L) {
   const size_t lds = p.g.W > 1 ? (size_t)p.g.RPW * p.g.W * 2 * G * sizeof(float) : 0;
-  hipLaunchKernelGGL((aggregate_kernel<T, VPL, G>), dim3(grid_for(p.g)), dim3(64 * p.g.W * p.g.RPW),
-                     lds, st, p);
-  return hipGetLastError();
+  return launch(L, aggregate_kernel<T, VPL, G>, dim3(grid_for(p.g)), dim3(64 * p.g.W * p.g.RPW),
+                lds, p);
 }
 
 template <class T>
-static hipError_t launch_aggregate_dt(const void* const* src, int n, int64_t R, int64_t D,
-                                      const float* w, const float* gm, float eps, void* out,
-                                      float* m_out, float* lse_out, hipStream_t st) {
+static hipError_t launch_aggregate_dt(const AggArgs& a, const Launch& L) {
   AggParams p;
-  for (int i = 0; i < 64; ++i) p.src[i] = i < n ? src[i] : nullptr;
-  p.n = n; p.w = w; p.gm = gm; p.eps = eps; p.out = out; p.m_out = m_out; p.lse_out = lse_out;
-  p.g = make_geom(R, D, T::kBytes, 2, 4);
+  for (int i = 0; i < 64; ++i) p.src[i] = i < a.n ? a.src[i] : nullptr;
+  p.n = a.n; p.w = a.w; p.gm = a.g; p.eps = a.eps;
+  p.out = a.out; p.m_out = a.m_out; p.lse_out = a.lse_out;
+  p.cl = Close{a.close_p, a.close_v, a.close_b};
+  p.g = make_geom(a.R, a.D, T::kBytes, 2, 4);
   if (p.g.W > 8) {
     // widest rows: four vectors per lane and groups of four sources
-    p.g = make_geom(R, D, T::kBytes, 4, 4);
+    p.g = make_geom(a.R, a.D, T::kBytes, 4, 4);
     if (p.g.W > 8) return hipErrorInvalidValue;
-    return launch_agg_t<T, 4, 4>(p, st);
+    return launch_agg_t<T, 4, 4>(p, L);
   }
-  if (n <= 2) return launch_agg_t<T, 2, 2>(p, st);
-  if (n <= 4) return launch_agg_t<T, 2, 4>(p, st);
-  return launch_agg_t<T, 2, 8>(p, st);
+  if (a.n <= 2) return launch_agg_t<T, 2, 2>(p, L);
+  if (a.n <= 4) return launch_agg_t<T, 2, 4>(p, L);
+  return launch_agg_t<T, 2, 8>(p, L);
 }
 
-hipError_t launch_aggregate(int dtype, const void* const* src, int n, int64_t R, int64_t D,
-                            const float* w, const float* gm, float eps, void* out, float* m_out,
-                            float* lse_out, hipStream_t st) {
-  return dtype == 1 ? launch_aggregate_dt<Bf16>(src, n, R, D, w, gm, eps, out, m_out, lse_out, st)
-                    : launch_aggregate_dt<F32>(src, n, R, D, w, gm, eps, out, m_out, lse_out, st);
+hipError_t launch_aggregate(int dtype, const AggArgs& a, const Launch& L) {
+  return dtype == 1 ? launch_aggregate_dt<Bf16>(a, L) : launch_aggregate_dt<F32>(a, L);
 }
 
 template <class T, int VPL, bool HP>
-static hipError_t launch_ph2_t(Phase2Params& p, hipStream_t st) {
+static hipError_t launch_ph2_t(Phase2Params& p, const Launch& L) {
   const size_t lds = p.g.W > 1 ? (size_t)p.g.RPW * p.g.W * 2 * sizeof(float) : 0;
-  hipLaunchKernelGGL((phase2_kernel<T, VPL, HP>), dim3(grid_for(p.g)), dim3(64 * p.g.W * p.g.RPW),
-                     lds, st, p);
-  return hipGetLastError();
+  return launch(L, phase2_kernel<T, VPL, HP>, dim3(grid_for(p.g)), dim3(64 * p.g.W * p.g.RPW),
+                lds, p);
 }
 
 template <class T, bool HP>
-static hipError_t launch_ph2_vpl(Phase2Params& p, int vpl, hipStream_t st) {
+static hipError_t launch_ph2_vpl(Phase2Params& p, int vpl, const Launch& L) {
   switch (vpl) {
-    case 1: return launch_ph2_t<T, 1, HP>(p, st);
-    case 2: return launch_ph2_t<T, 2, HP>(p, st);
-    case 3: return launch_ph2_t<T, 3, HP>(p, st);
-    case 4: return launch_ph2_t<T, 4, HP>(p, st);
-    case 5: return launch_ph2_t<T, 5, HP>(p, st);
-    case 6: return launch_ph2_t<T, 6, HP>(p, st);
-    case 7: return launch_ph2_t<T, 7, HP>(p, st);
-    default: return launch_ph2_t<T, 8, HP>(p, st);
+    case 1: return launch_ph2_t<T, 1, HP>(p, L);
+    case 2: return launch_ph2_t<T, 2, HP>(p, L);
+    case 3: return launch_ph2_t<T, 3, HP>(p, L);
+    case 4: return launch_ph2_t<T, 4, HP>(p, L);
+    case 5: return launch_ph2_t<T, 5, HP>(p, L);
+    case 6: return launch_ph2_t<T, 6, HP>(p, L);
+    case 7: return launch_ph2_t<T, 7, HP>(p, L);
+    default: return launch_ph2_t<T, 8, HP>(p, L);
   }
 }
 
 template <class T>
-static hipError_t launch_phase2_dt(const void* o, const float* lse, const float* w,
-                                   const float* gm, float eps, const void* p_prev,
-                                   const void* v_prev, void* p_out, void* h_out, int64_t R,
-                                   int64_t D, hipStream_t st) {
+static hipError_t launch_phase2_dt(const Phase2Args& a, const Launch& L) {
   Phase2Params p;
-  p.o = o; p.lse = lse; p.w = w; p.gm = gm; p.eps = eps;
-  p.p_prev = p_prev; p.v_prev = v_prev; p.p_out = p_out; p.h_out = h_out;
-  // waves per row: fewest with at most 8 vectors per lane; then the vectors
-  // per lane that cover the row with those waves
-  const int V = (int)(D * T::kBytes / 16);
-  const int W = (V + 511) / 512;
-  const int vpl = (V + 64 * W - 1) / (64 * W);
-  p.g = make_geom(R, D, T::kBytes, vpl, 4);
-  if (p.g.W != W || W > 4) return hipErrorInvalidValue;
-  return p_prev ? launch_ph2_vpl<T, true>(p, vpl, st) : launch_ph2_vpl<T, false>(p, vpl, st);
+  p.o = a.o; p.lse = a.lse; p.w = a.w; p.gm = a.g; p.eps = a.eps;
+  p.p_prev = a.p_prev; p.v_prev = a.v_prev; p.p_out = a.p_out; p.h_out = a.h_out;
+  // ATTNRES_PHASE2_VPL vectors per lane, more when a row would need over 4
+  // waves (rows are at most 2048 vectors, so at most 8 per lane)
+  const int V = (int)(a.D * T::kBytes / 16);
+  int vpl = ATTNRES_PHASE2_VPL;
+  if (64 * 4 * vpl < V) vpl = (V + 255) / 256;
+  p.g = make_geom(a.R, a.D, T::kBytes, vpl, 4);
+  if (p.g.W > 4 || vpl > 8) return hipErrorInvalidValue;
+  return a.p_prev ? launch_ph2_vpl<T, true>(p, vpl, L) : launch_ph2_vpl<T, false>(p, vpl, L);
 }
 
-hipError_t launch_phase2(int dtype, const void* o, const float* lse, const float* w,
-                         const float* gm, float eps, const void* p_prev, const void* v_prev,
-                         void* p_out, void* h_out, int64_t R, int64_t D, hipStream_t st) {
-  return dtype == 1
-             ? launch_phase2_dt<Bf16>(o, lse, w, gm, eps, p_prev, v_prev, p_out, h_out, R, D, st)
-             : launch_phase2_dt<F32>(o, lse, w, gm, eps, p_prev, v_prev, p_out, h_out, R, D, st);
+hipError_t launch_phase2(int dtype, const Phase2Args& a, const Launch& L) {
+  return dtype == 1 ? launch_phase2_dt<Bf16>(a, L) : launch_phase2_dt<F32>(a, L);
 }
 
 hipError_t launch_close(int dtype, const void* p, const void* v, void* b, int64_t R, int64_t D,
-                        hipStream_t st) {
+                        const Launch& L) {
   const int64_t nvec = R * D * (dtype == 1 ? 2 : 4) / 16;
   if (nvec == 0) return hipSuccess;
   int64_t blocks = (nvec + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  if (dtype == 1)
-    hipLaunchKernelGGL(close_kernel<Bf16>, dim3((unsigned)blocks), dim3(256), 0, st, p, v, b, nvec);
-  else
-    hipLaunchKernelGGL(close_kernel<F32>, dim3((unsigned)blocks), dim3(256), 0, st, p, v, b, nvec);
-  return hipGetLastError();
+  if (dtype == 1) return launch(L, close_kernel<Bf16>, dim3((unsigned)blocks), dim3(256), 0, p, v, b, nvec);
+  return launch(L, close_kernel<F32>, dim3((unsigned)blocks), dim3(256), 0, p, v, b, nvec);
 }
 
 }  // namespace attnres

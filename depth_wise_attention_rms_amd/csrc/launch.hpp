@@ -1,0 +1,73 @@
+// launch.hpp -- internal interface between the C ABI (api.hip) and the kernel
+// launchers (kernels.hip). Arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attnres {
+
+// Stream of a launch, plus an optional event pair that receives the start and
+// end timestamps of the kernel's own dispatch (both null when not timed).
+struct Launch {
+  hipStream_t stream;
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
+// A "close" fused into a launch: its last source is not read from src[n-1]
+// but formed as round(close_p + close_v) (or close_v when close_p is null),
+// stored to close_b and used directly. close_v == null means no close.
+struct Phase1Args {
+  const void* const* src;  // (host) n device pointers
+  int n;
+  int64_t R, D;
+  const float* W;  // [S][D]
+  const float* G;  // [S][D] or null
+  int S;
+  float eps;
+  void* out;       // [S][R][D]
+  float* m_out;    // [S][R] or null
+  float* lse_out;  // [S][R]
+  const void* close_p;
+  const void* close_v;
+  void* close_b;
+};
+
+struct AggArgs {
+  const void* const* src;  // (host) n device pointers
+  int n;
+  int64_t R, D;
+  const float* w;  // [D]
+  const float* g;  // [D] or null
+  float eps;
+  void* out;       // [R][D]
+  float* m_out;    // [R] or null
+  float* lse_out;  // [R] or null
+  const void* close_p;
+  const void* close_v;
+  void* close_b;
+};
+
+struct Phase2Args {
+  const void* o;
+  const float* lse;
+  const float* w;
+  const float* g;
+  float eps;
+  const void* p_prev;
+  const void* v_prev;
+  void* p_out;
+  void* h_out;
+  int64_t R, D;
+};
+
+hipError_t launch_fold(const float* w, const float* g, float* q, int64_t count, const Launch& L);
+hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L);
+bool phase1_supported(int dtype, int n, int64_t D);
+hipError_t launch_aggregate(int dtype, const AggArgs& a, const Launch& L);
+hipError_t launch_phase2(int dtype, const Phase2Args& a, const Launch& L);
+hipError_t launch_close(int dtype, const void* p, const void* v, void* b, int64_t R, int64_t D,
+                        const Launch& L);
+
+}  // namespace attnres

@@ -108,6 +108,7 @@ AGG_CASES = [
     (8, 65, 7168, "bf16"), (9, 65, 4096, "bf16"), (17, 130, 1024, "bf16"), (33, 9, 2048, "bf16"),
     (64, 5, 264, "bf16"), (4, 3, 12288, "bf16"), (11, 3, 16384, "bf16"), (1, 1, 8, "bf16"),
     (2, 37, 516, "f32"), (7, 130, 4096, "f32"), (17, 33, 1024, "f32"), (3, 5, 8188, "f32"),
+    (1, 37, 516, "f32"), (1, 3, 8188, "f32"),
 ]
 
 
@@ -139,6 +140,7 @@ PH1_CASES = [
     (12, 12, 9, 4096, "bf16"), (16, 2, 9, 4096, "bf16"), (20, 3, 5, 2048, "bf16"),
     (6, 8, 3, 16384, "bf16"), (3, 1, 1, 8, "bf16"),
     (2, 8, 37, 516, "f32"), (6, 8, 65, 4096, "f32"), (8, 5, 9, 2048, "f32"), (13, 4, 9, 1024, "f32"),
+    (1, 5, 37, 1028, "f32"), (1, 3, 9, 8, "f32"),
 ]
 
 
@@ -159,6 +161,9 @@ def test_phase1_sweep(n, S, R, D, dtype):
         assert_close_scaled(o_h[s], ref["o"][s], ref["scale"][s], dtype, f"phase1 o[{s}]")
     assert_stats(m_h, ref["m"], "phase1 m")
     assert_stats(l_h, ref["lse"], "phase1 lse")
+    if n == 1:
+        for s in range(S):
+            assert np.array_equal(o_h[s], srcs[0]), "one source: every query returns it bit for bit"
 
 
 PH2_CASES = [
