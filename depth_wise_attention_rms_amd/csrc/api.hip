@@ -141,7 +141,7 @@ int do_close(const char* fn, const void* p, const void* v, void* b, int64_t R, i
 int do_phase1(const char* fn, int dtype, const Phase1Args& a, hipStream_t st) {
   if (a.R == 0) return ATTNRES_OK;
   const int64_t row_bytes = a.D * esize_of(dtype);
-  if (attnres::phase1_supported(dtype, a.n, a.D)) {
+  if (attnres::phase1_supported(dtype, a.n, a.S, a.D)) {
     const double rb = (double)a.R * row_bytes;
     const double bytes = rb * (a.n + a.S) + (double)a.R * a.S * ((a.m_out ? 4 : 0) + 4) +
                          close_bytes(rb, a.close_p, a.close_v);

@@ -232,6 +232,342 @@ __global__ __launch_bounds__(512) void phase1_kernel(Phase1Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// Phase 1 on the matrix cores (bf16 I/O; S <= 10 queries, n <= 8 sources,
+// D a multiple of 128 up to 4096). The score contraction Q[S,D] . b_i[D] is
+// a dense product over the hidden axis, so it runs on v_mfma_f32_32x32x16_bf16:
+// rows of the A operand are (query, part) pairs -- each fp32 query is the
+// exact sum of three bf16 parts, so bf16 x bf16 products accumulated in fp32
+// keep fp32 accuracy -- and the B columns are the row's sources. Everything
+// else (sums of squares, softmax, the weighted sums of the raw sources) stays
+// in fp32 on the vector ALUs.
+//
+// One workgroup of 8 waves per CU walks token rows. Wave w owns the hidden
+// slice [w*D/8, (w+1)*D/8) and keeps the query parts of that slice in
+// registers for the whole kernel. A row's sources sit in one of two LDS
+// buffers (each source row padded by 32 bytes so lanes reading different
+// sources at one column hit different banks); while a row is processed, the
+// next row is copied from HBM straight into the other buffer with
+// global_load_lds, so its latency overlaps the work. A fused block close
+// stages its p and v rows and forms b = round(p + v) where it is used.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kP1Waves = 8;
+constexpr int kP1MaxN = 8;
+constexpr int kP1MaxS = 10;
+#ifndef ATTNRES_P1_OUT_BATCH
+#define ATTNRES_P1_OUT_BATCH 4
+#endif
+constexpr int kP1OB = ATTNRES_P1_OUT_BATCH;  // queries per output batch
+
+struct Phase1MParams {
+  const void* src[kP1MaxN];
+  int n;
+  int S;
+  const float* Wq;  // [S][D]
+  const float* G;   // [S][D] or null
+  float eps;
+  void* out;        // [S][R][D]
+  float* m_out;     // [S][R] or null
+  float* lse_out;   // [S][R]
+  Close cl;
+  int64_t R;
+  int D;
+  float invD;
+};
+
+// x rounded to the nearest bf16 (ties to even), as an fp32 value
+__device__ __forceinline__ float bf16_round(float x) { return (float)(__bf16)x; }
+
+// Wait until at most k vector-memory operations of this wave are outstanding.
+// Global loads (including loads into LDS) and stores of one wave report
+// completion in issue order, so this waits for everything issued before the
+// last k operations. LDS and scalar counters are not waited on.
+__device__ __forceinline__ void wait_vm(int k) {
+#define ATTNRES_WAIT_VM(K) __builtin_amdgcn_s_waitcnt(((K) & 0xF) | (((K) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
+  switch (k) {
+    case 0: ATTNRES_WAIT_VM(0); break;
+    case 1: ATTNRES_WAIT_VM(1); break;
+    case 2: ATTNRES_WAIT_VM(2); break;
+    case 3: ATTNRES_WAIT_VM(3); break;
+    case 4: ATTNRES_WAIT_VM(4); break;
+    case 5: ATTNRES_WAIT_VM(5); break;
+    case 6: ATTNRES_WAIT_VM(6); break;
+    case 7: ATTNRES_WAIT_VM(7); break;
+    case 8: ATTNRES_WAIT_VM(8); break;
+    case 9: ATTNRES_WAIT_VM(9); break;
+    default: ATTNRES_WAIT_VM(10); break;
+  }
+#undef ATTNRES_WAIT_VM
+}
+
+// Reductions over the 8-lane groups of a wave (lanes 8g .. 8g+7): swaps within
+// quads, then the mirror of each half row. Every lane gets its group's result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float group8_max(float x) {
+  x = fmaxf(x, dpp_mov<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_mov<0x4E>(x));   // quad_perm [2,3,0,1]
+  return fmaxf(x, dpp_mov<0x141>(x));  // row_half_mirror
+}
+__device__ __forceinline__ float group8_sum(float x) {
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  return x + dpp_mov<0x141>(x);
+}
+
+// Workgroup barrier after this wave's LDS reads and writes have completed.
+// It does not wait for vector memory: a fenced barrier (__syncthreads(), or
+// an LDS-scope fence, which also covers loads into LDS) would make every
+// wave wait for its in-flight prefetch of the next row and its stores. Loads
+// into LDS are waited for explicitly before the barrier that publishes them.
+// The memory clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// A wave-uniform address as a scalar value in the global address space: the
+// compiler then addresses memory as scalar base + 32-bit lane offset instead
+// of keeping a 64-bit per-lane address for every stream (and the accesses
+// stay global, not flat, so they count on the vector-memory counter only).
+typedef __attribute__((address_space(1))) char gchar_t;
+__device__ __forceinline__ gchar_t* uniform_ptr(const void* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (gchar_t*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void st16_stream(gchar_t* p, const uint4& v) {
+  typedef __attribute__((address_space(1))) u32x4_t gu32x4_t;
+  const u32x4_t t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<gu32x4_t*>(p));
+}
+
+// Staged rows of one token row in an LDS buffer ([NC + 1][STRIDE] bf16): the
+// sources (for a close, v in place of the closing source) and, for a close
+// with a partial, p after them. Wave w moves 1 KiB chunks w, w+8, ... of each
+// row, 64 lanes x 16 bytes straight into LDS; the chunk count NCH = D / 512
+// is at most 8, so each wave copies (and later forms the close of) chunk w.
+template <int KS, int NC>
+__device__ __forceinline__ void p1_copy_row(const Phase1MParams& p, int64_t row, bool has_close,
+                                            __bf16* buf, int w, int l) {
+  constexpr int D = 128 * KS, STRIDE = D + 16, NCH = KS / 4;
+  if (w >= NCH) return;
+  const int64_t roff = row * (int64_t)D * 2;
+  const uint32_t loff = (uint32_t)((w * 64 + l) * 16);
+  #pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const void* g = (i == NC - 1 && has_close) ? p.cl.v : p.src[i];
+    __builtin_amdgcn_global_load_lds(uniform_ptr(static_cast<const char*>(g) + roff) + loff,
+                                     buf + (size_t)i * STRIDE + w * 512, 16, 0, 0);
+  }
+  if (has_close && p.cl.p)
+    __builtin_amdgcn_global_load_lds(uniform_ptr(static_cast<const char*>(p.cl.p) + roff) + loff,
+                                     buf + (size_t)NC * STRIDE + w * 512, 16, 0, 0);
+}
+
+// One token row: cur holds its staged rows (copied by this wave's own loads,
+// pending until the wait below), nxt receives the next row's.
+template <int KS, int NC>
+__device__ __forceinline__ void p1_row(const Phase1MParams& p, int64_t row, int wait, __bf16* cur,
+                                       __bf16* nxt, float* cred, float* ssred, const uint4 (&qa)[KS],
+                                       int w, int l) {
+  constexpr int D = 128 * KS, STRIDE = D + 16, NCH = KS / 4;
+  const int tid = w * 64 + l, col = l & 31, kg = l >> 5;
+  const int S = p.S;
+  const bool has_close = p.cl.v != nullptr;
+  const int64_t rowbytes = (int64_t)D * 2;
+
+  wait_vm(wait);  // this wave's part of the row has landed in LDS
+  if (has_close && w < NCH) {
+    // b = round(p + v) (or v) over the chunk this wave copied; stored as the block sum
+    __bf16* bv = cur + (size_t)(NC - 1) * STRIDE + tid * 8;
+    uint4 u = *reinterpret_cast<const uint4*>(bv);
+    if (p.cl.p) {
+      const uint4 a = *reinterpret_cast<const uint4*>(cur + (size_t)NC * STRIDE + tid * 8);
+      float fa[8], fv[8];
+      Bf16::unpack(a, fa);
+      Bf16::unpack(u, fv);
+      #pragma unroll
+      for (int e = 0; e < 8; ++e) fa[e] += fv[e];
+      u = Bf16::pack(fa);
+      *reinterpret_cast<uint4*>(bv) = u;
+    }
+    st16_stream(uniform_ptr(static_cast<char*>(p.cl.b) + row * rowbytes) + (uint32_t)(tid * 16), u);
+  }
+  lds_barrier();
+  const int64_t next = row + gridDim.x;
+  if (next < p.R) p1_copy_row<KS, NC>(p, next, has_close, nxt, w, l);
+
+  // scores: C[(s, j)][i] over this wave's hidden slice, and sums of squares
+  f32x16_t acc0, acc1;
+  #pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    acc0[r] = 0.f;
+    acc1[r] = 0.f;
+  }
+  float ss = 0.f;
+  const bool live = col < NC;
+  const __bf16* bsrc = cur + (size_t)(live ? col : 0) * STRIDE + w * (D / kP1Waves) + 8 * kg;
+  #pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    uint4 b = make_uint4(0, 0, 0, 0);
+    if (live) {
+      b = *reinterpret_cast<const uint4*>(bsrc + 16 * kk);
+      ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b.x),
+                                           __builtin_bit_cast(bf16x2v_t, b.x), ss, false);
+      ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b.y),
+                                           __builtin_bit_cast(bf16x2v_t, b.y), ss, false);
+      ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b.z),
+                                           __builtin_bit_cast(bf16x2v_t, b.z), ss, false);
+      ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b.w),
+                                           __builtin_bit_cast(bf16x2v_t, b.w), ss, false);
+    }
+    if (kk & 1)
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qa[kk]),
+                                                     __builtin_bit_cast(bf16x8_t, b), acc1, 0, 0, 0);
+    else
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qa[kk]),
+                                                     __builtin_bit_cast(bf16x8_t, b), acc0, 0, 0, 0);
+    if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the LDS reads in flight
+  }
+  if (live) {
+    // all 32 rows of A are written; rows past 3S hold exact zeros
+    float* cw = cred + (w * 32 + 4 * kg) * NC + col;
+    #pragma unroll
+    for (int r = 0; r < 16; ++r) cw[(8 * (r / 4) + (r & 3)) * NC] = acc0[r] + acc1[r];
+    ssred[(w * 2 + kg) * NC + col] = ss;
+  }
+  lds_barrier();
+
+  // softmax, computed by every wave for itself: lane 8*s' + i holds the score
+  // of source i for query s = s' (first half) or 8 + s' (second half, S > 8)
+  const int i = l & 7;
+  float a_lo = 0.f, a_hi = 0.f;
+  #pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (h == 1 && S <= 8) break;
+    const int s = 8 * h + (l >> 3);
+    const bool valid = i < NC && s < S;
+    float sc = -INFINITY;
+    if (valid) {
+      float dot = 0.f, sq = 0.f;
+      #pragma unroll
+      for (int ww = 0; ww < kP1Waves; ++ww) {
+        const float* c = cred + (ww * 32 + 3 * s) * NC + i;
+        dot += c[0] + c[NC] + c[2 * NC];
+        sq += ssred[(ww * 2) * NC + i] + ssred[(ww * 2 + 1) * NC + i];
+      }
+      sc = dot * rsqrtf(sq * p.invD + p.eps);
+    }
+    const float m = group8_max(sc);
+    const float e = valid ? __expf(sc - m) : 0.f;
+    const float z = group8_sum(e);
+    const float a = e * (1.0f / z);
+    if (h == 0) a_lo = a; else a_hi = a;
+    if (w == 0 && i == 0 && s < S) {
+      if (p.m_out) p.m_out[(int64_t)s * p.R + row] = m;
+      p.lse_out[(int64_t)s * p.R + row] = m + __logf(z);
+    }
+  }
+
+  // outputs: o_s = sum_i alpha[s][i] b_i over this thread's vector, kP1OB
+  // queries at a time (the wave's lanes own vectors 64w .. 64w+63)
+  if (w < NCH) {
+    uint4 x[NC];
+    #pragma unroll
+    for (int k = 0; k < NC; ++k) x[k] = *reinterpret_cast<const uint4*>(cur + (size_t)k * STRIDE + tid * 8);
+    for (int s0 = 0; s0 < S; s0 += kP1OB) {
+      float o[kP1OB][8];
+      #pragma unroll
+      for (int q = 0; q < kP1OB; ++q)
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) o[q][e] = 0.f;
+      #pragma unroll
+      for (int k = 0; k < NC; ++k) {
+        float xf[8];
+        Bf16::unpack(x[k], xf);
+        #pragma unroll
+        for (int q = 0; q < kP1OB; ++q) {
+          const int s = s0 + q;
+          if (s < S) {
+            const float a = __int_as_float(__builtin_amdgcn_readlane(
+                __float_as_int(s < 8 ? a_lo : a_hi), 8 * (s & 7) + k));
+            #pragma unroll
+            for (int e = 0; e < 8; ++e) o[q][e] += a * xf[e];
+          }
+        }
+      }
+      #pragma unroll
+      for (int q = 0; q < kP1OB; ++q)
+        if (s0 + q < S)
+          st16_stream(uniform_ptr(static_cast<char*>(p.out) + ((int64_t)(s0 + q) * p.R + row) * rowbytes) +
+                          (uint32_t)(tid * 16),
+                      Bf16::pack(o[q]));
+    }
+  }
+}
+
+template <int KS, int NC>
+__global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
+  constexpr int D = 128 * KS, STRIDE = D + 16, NCH = KS / 4;
+  __shared__ __attribute__((aligned(16))) __bf16 bufA[(NC + 1) * STRIDE];
+  __shared__ __attribute__((aligned(16))) __bf16 bufB[(NC + 1) * STRIDE];
+  __shared__ float cred[kP1Waves * 32 * NC];  // partial scores [wave][row of A][source]
+  __shared__ float ssred[kP1Waves * 2 * NC];  // partial sums of squares [wave][half][source]
+
+  const int S = p.S;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int col = l & 31, kg = l >> 5;
+  const bool has_close = p.cl.v != nullptr;
+
+  // A operand: part j of query s = m / 3 (j = m % 3) for this lane's row m
+  uint4 qa[KS];
+  {
+    const int m = col, s = m / 3, j = m - 3 * (m / 3);
+    #pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      float part[8];
+      #pragma unroll
+      for (int e = 0; e < 8; ++e) part[e] = 0.f;
+      if (s < S) {
+        const int d0 = w * (D / kP1Waves) + 16 * kk + 8 * kg;
+        float q[8];
+        load_query<8>(p.Wq, p.G, (int64_t)s * D + d0, q);
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float h1 = bf16_round(q[e]);
+          const float r1 = q[e] - h1;  // exact
+          const float h2 = bf16_round(r1);
+          const float r2 = r1 - h2;    // exact
+          part[e] = j == 0 ? h1 : j == 1 ? h2 : r2;
+        }
+      }
+      qa[kk] = Bf16::pack(part);  // each part is a bf16 value: packing is exact
+    }
+  }
+
+  // The copy of a row into a buffer is followed, before the next wait, only by
+  // this wave's S output stores (and, in wave 0, the statistics stores).
+  const int steady = w < NCH ? S : 0;
+  int64_t row = blockIdx.x;
+  if (row < p.R) p1_copy_row<KS, NC>(p, row, has_close, bufA, w, l);
+  int wait = 0;
+  while (row < p.R) {
+    p1_row<KS, NC>(p, row, wait, bufA, bufB, cred, ssred, qa, w, l);
+    wait = steady;
+    row += gridDim.x;
+    if (row >= p.R) break;
+    p1_row<KS, NC>(p, row, wait, bufB, bufA, cred, ssred, qa, w, l);
+    row += gridDim.x;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Aggregate over any number of sources with one query [K3 (A1)-(A3); WC
 // depth_summary/merge_summary/finish]. Sources are taken in register-resident
 // groups of G; each group's scores are reduced across the row and folded into
@@ -559,11 +895,57 @@ static hipError_t launch_phase1_dt(const Phase1Args& a, const Launch& L) {
   return hipErrorInvalidValue;
 }
 
+static bool phase1_mfma_eligible(int dtype, int n, int S, int64_t D) {
+  return dtype == 1 && n >= 1 && n <= kP1MaxN && S >= 1 && S <= kP1MaxS &&
+         (D == 1024 || D == 2048 || D == 3072 || D == 4096);
+}
+
+template <int KS, int NC>
+static hipError_t launch_phase1_mfma_t(const Phase1MParams& p, const Launch& L) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t grid = p.R < cus ? p.R : cus;  // one workgroup per CU, each walks rows
+  return launch(L, phase1_mfma_kernel<KS, NC>, dim3((unsigned)grid), dim3(64 * kP1Waves), 0, p);
+}
+
+template <int KS>
+static hipError_t launch_phase1_mfma_k(const Phase1MParams& p, const Launch& L) {
+  switch (p.n) {
+    case 1: return launch_phase1_mfma_t<KS, 1>(p, L);
+    case 2: return launch_phase1_mfma_t<KS, 2>(p, L);
+    case 3: return launch_phase1_mfma_t<KS, 3>(p, L);
+    case 4: return launch_phase1_mfma_t<KS, 4>(p, L);
+    case 5: return launch_phase1_mfma_t<KS, 5>(p, L);
+    case 6: return launch_phase1_mfma_t<KS, 6>(p, L);
+    case 7: return launch_phase1_mfma_t<KS, 7>(p, L);
+    default: return launch_phase1_mfma_t<KS, 8>(p, L);
+  }
+}
+
+static hipError_t launch_phase1_mfma(const Phase1Args& a, const Launch& L) {
+  Phase1MParams p;
+  for (int i = 0; i < kP1MaxN; ++i) p.src[i] = i < a.n ? a.src[i] : nullptr;
+  p.n = a.n; p.S = a.S; p.Wq = a.W; p.G = a.G; p.eps = a.eps;
+  p.out = a.out; p.m_out = a.m_out; p.lse_out = a.lse_out;
+  p.cl = Close{a.close_p, a.close_v, a.close_b};
+  p.R = a.R; p.D = (int)a.D; p.invD = 1.0f / (float)a.D;
+  switch (a.D) {
+    case 1024: return launch_phase1_mfma_k<8>(p, L);
+    case 2048: return launch_phase1_mfma_k<16>(p, L);
+    case 3072: return launch_phase1_mfma_k<24>(p, L);
+    default: return launch_phase1_mfma_k<32>(p, L);
+  }
+}
+
 hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L) {
+  if (phase1_mfma_eligible(dtype, a.n, a.S, a.D)) return launch_phase1_mfma(a, L);
   return dtype == 1 ? launch_phase1_dt<Bf16>(a, L) : launch_phase1_dt<F32>(a, L);
 }
 
-bool phase1_supported(int dtype, int n, int64_t D) {
+bool phase1_supported(int dtype, int n, int S, int64_t D) {
+  if (phase1_mfma_eligible(dtype, n, S, D)) return true;
   const int es = dtype == 1 ? 2 : 4;
   if (n < 1 || n > 16) return false;
   const Geom g = make_geom(1, D, es, n <= 8 ? 2 : 1, 4);

@@ -64,7 +64,7 @@ struct Phase2Args {
 
 hipError_t launch_fold(const float* w, const float* g, float* q, int64_t count, const Launch& L);
 hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L);
-bool phase1_supported(int dtype, int n, int64_t D);
+bool phase1_supported(int dtype, int n, int S, int64_t D);
 hipError_t launch_aggregate(int dtype, const AggArgs& a, const Launch& L);
 hipError_t launch_phase2(int dtype, const Phase2Args& a, const Launch& L);
 hipError_t launch_close(int dtype, const void* p, const void* v, void* b, int64_t R, int64_t D,

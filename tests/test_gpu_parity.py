@@ -141,6 +141,11 @@ PH1_CASES = [
     (6, 8, 3, 16384, "bf16"), (3, 1, 1, 8, "bf16"),
     (2, 8, 37, 516, "f32"), (6, 8, 65, 4096, "f32"), (8, 5, 9, 2048, "f32"), (13, 4, 9, 1024, "f32"),
     (1, 5, 37, 1028, "f32"), (1, 3, 9, 8, "f32"),
+    # the matrix-core path (bf16, S <= 10, n <= 8, D in {1024, 2048, 3072, 4096});
+    # R above the CU count gives each workgroup several rows, odd and even
+    (7, 10, 300, 2048, "bf16"), (8, 3, 513, 1024, "bf16"), (2, 1, 260, 3072, "bf16"),
+    (4, 9, 1000, 4096, "bf16"), (8, 8, 37, 4096, "bf16"), (6, 8, 700, 4096, "bf16"),
+    (1, 10, 300, 1024, "bf16"), (3, 7, 777, 3072, "bf16"),
 ]
 
 
@@ -229,15 +234,26 @@ def _check_stack(ds: DeviceStack, rows: np.ndarray, chunk=64, nthreads=None):
 
 
 def test_stack_bruteforce_grid():
-    """Every L <= 7 and S <= L+1 on 3 rows, D in {8, 16, 64}, both dtypes."""
+    """Every L <= 7 and S <= L+1 on 3 rows, D in {8, 16, 64} (and 1024 for bf16,
+    which takes the matrix-core Phase 1), both dtypes."""
     for dtype in ("bf16", "f32"):
-        for D in (8, 16, 64):
+        for D in ((8, 16, 64, 1024) if dtype == "bf16" else (8, 16, 64)):
             for L in range(1, 8):
                 for S in range(1, L + 2):
                     wl = inputs.Workload(f"grid_L{L}_S{S}_D{D}_{dtype}", "stack", B=1, T=3, D=D,
                                          dtype=dtype, L=L, S=S, seed=L * 100 + S)
                     ds = DeviceStack(wl, W_host=inputs.queries(L, L + 1, D, sigma=0.4))
                     _check_stack(ds, np.arange(3))
+
+
+def test_stack_matrix_core_many_rows():
+    """Block stack whose Phase 1 runs on the matrix cores with several token
+    rows per workgroup and fused block closes: L = 20, S = 6, R = 600,
+    D = 2048, bf16; all rows."""
+    wl = inputs.Workload("mfma_rows", "stack", B=2, T=300, D=2048, dtype="bf16", L=20, S=6, seed=7)
+    announce(wl.name)
+    ds = DeviceStack(wl)
+    _check_stack(ds, np.arange(wl.R), chunk=300)
 
 
 def test_stack_full_config():
