@@ -15,6 +15,9 @@ launch over its HIP-event-timed average duration, against 8 TB/s), and the
 fp64 CPU oracle timed on a bounded row sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --write-traffic FETCH_CSV WRITE_CSV   (CPU only: turn two
+           rocprofv3 --pmc counter files of a run with --calibration-copy-gib 1
+           into the HBM-traffic summary that the roofline entry reads)
 """
 from __future__ import annotations
 
@@ -29,6 +32,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBPS = 8000.0
 METRIC = "tokens/s and achieved HBM GB/s (% of peak) for Block AttnRes stack forward"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "phase2_block_L48_S8_traffic.json")
+TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "block_L48_S8_hbm_traffic.txt")
+DOMINANT = "attnres::phase2_kernel"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
 def kernels_digest() -> str:
@@ -52,19 +58,113 @@ def measured_traffic(workload: str):
     return t.get("traffic_bytes_per_launch")
 
 
+def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_gib: float = 1.0) -> dict:
+    """HBM bytes per launch from FETCH_SIZE and WRITE_SIZE counter files (KiB
+    per dispatch), each scaled by what the counter reads for the calibration
+    copy (copy_gib GiB read once and written once) in the same run."""
+    import csv
+    import re
+
+    def per_kernel(path, counter):
+        d = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = re.sub(r"\(.*", "", r["Kernel_Name"].replace("void ", ""))
+                d.setdefault(name, []).append(float(r["Counter_Value"]))
+        return d
+
+    fe, wr = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    true_kib = copy_gib * (1 << 20)
+    f_factor = true_kib / (sum(fe[COPY_KERNEL]) / len(fe[COPY_KERNEL]))
+    w_factor = true_kib / (sum(wr[COPY_KERNEL]) / len(wr[COPY_KERNEL]))
+    mean = lambda v: sum(v) / len(v)
+    rows = []
+    for name in sorted(set(fe) & set(wr)):
+        if not name.startswith("attnres::"):
+            continue
+        fb = mean(fe[name]) * f_factor * 1024
+        wb = mean(wr[name]) * w_factor * 1024
+        rows.append((name, len(fe[name]), mean(fe[name]), mean(wr[name]), fb, wb))
+    dom = [r for r in rows if r[0].startswith(DOMINANT)]
+    launches = sum(r[1] for r in dom)
+    traffic = sum((r[4] + r[5]) * r[1] for r in dom) / launches
+    out = {"workload": workload, "kernel": DOMINANT.split("::")[1],
+           "traffic_bytes_per_launch": traffic,
+           "fetch_factor": f_factor, "write_factor": w_factor,
+           "calibration": f"{COPY_KERNEL}, {copy_gib} GiB read and written once",
+           "kernels_sha256": kernels_digest()}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    with open(TRAFFIC_TABLE, "w") as f:
+        f.write(f"HBM traffic per dispatch, workload {workload} (bench.py --steps 2 --warmup 1 "
+                f"--cpu-rows 0 --calibration-copy-gib {copy_gib:g})\n")
+        f.write("commands (from /tmp, TMPDIR=/tmp):\n"
+                "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -o run -- python3 "
+                f"<repo>/bench.py --steps 2 --warmup 1 --cpu-rows 0 --calibration-copy-gib {copy_gib:g}\n"
+                "  rocprofv3 --pmc WRITE_SIZE ... (same)\n"
+                f"  python bench.py --write-traffic <fetch>/run_counter_collection.csv "
+                f"<write>/run_counter_collection.csv\n")
+        f.write(f"calibration: FETCH_SIZE x {f_factor:.4f}, WRITE_SIZE x {w_factor:.4f} "
+                f"(counter reading of the {copy_gib:g} GiB copy vs its true size)\n\n")
+        f.write(f"{'kernel':52s} {'dispatches':>10s} {'FETCH KiB':>12s} {'WRITE KiB':>12s} "
+                f"{'read MB':>10s} {'write MB':>10s}\n")
+        for name, n, fk, wk, fb, wb in rows:
+            f.write(f"{name:52s} {n:10d} {fk:12.1f} {wk:12.1f} {fb / 1e6:10.2f} {wb / 1e6:10.2f}\n")
+        f.write(f"\n{DOMINANT}: {traffic / 1e6:.2f} MB per launch (mean over its {launches} dispatches)\n")
+        f.write(f"kernel sources sha256 {out['kernels_sha256']}\n")
+    return out
+
+
+def cpu_baseline(ds, wl, seconds: float, chunk: int = 2048) -> dict:
+    """The fp64 oracle's naive forward on consecutive chunks of token rows
+    (cycling over the workload) until ``seconds`` of CPU work have run."""
+    import numpy as np
+    import oracle
+    from depth_wise_attention_rms_amd.workload import EPS
+
+    if not os.path.exists(oracle.LIBRARY):
+        oracle.build()
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    done, spent, start = 0, 0.0, 0
+    while done == 0 or spent < seconds:
+        rows = np.arange(start, min(start + chunk, wl.R))
+        start = 0 if start + chunk >= wl.R else start + chunk
+        xr, vr = ds.host_rows(rows)
+        c0 = time.perf_counter()
+        oracle.block_stack(xr, vr, ds.W_host, wl.S, eps=EPS, want_h=False, nthreads=cores)
+        spent += time.perf_counter() - c0
+        done += len(rows)
+        del xr, vr
+    return {"value": round(done / spent, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} token rows in chunks of {chunk} consecutive rows cycling over the "
+                      f"{wl.R} of the workload, full {wl.L}-sublayer naive forward in fp64 "
+                      f"({cores} threads), {spent:.2f} s of CPU time (host copies excluded)"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="block_L48_S8")
-    ap.add_argument("--cpu-rows", type=int, default=6144,
-                    help="token rows of the CPU-oracle baseline sample (0 disables it)")
+    ap.add_argument("--cpu-rows", type=int, default=1,
+                    help="0 disables the CPU-oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU work of the oracle baseline (whole row chunks until this much has run)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--calibration-copy-gib", type=float, default=0.0,
                     help="before the steps, copy a tensor of this many GiB with torch (a plain "
                          "copy kernel of known size, read once and written once) so hardware "
                          "counters of the same run can be scaled to bytes")
     args = ap.parse_args()
+
+    if args.write_traffic:
+        t = write_traffic(*args.write_traffic, workload=args.workload)
+        print(json.dumps(t))
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -73,7 +173,6 @@ def main() -> int:
               "single-GPU figure", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     from depth_wise_attention_rms_amd import binding
@@ -137,21 +236,7 @@ def main() -> int:
                 "traffic": traffic, "bytes_per_launch": dom["bytes_per_launch"],
                 "avg_launch_us": round(dom["avg_us"], 2)}
 
-    cpu = None
-    if args.cpu_rows > 0:
-        import oracle
-        from depth_wise_attention_rms_amd.workload import EPS
-        rows = np.sort(np.random.default_rng(0).choice(wl.R, size=min(args.cpu_rows, wl.R), replace=False))
-        xr, vr = ds.host_rows(rows)
-        cores = max(1, min(16, len(os.sched_getaffinity(0))))
-        oracle.build() if not os.path.exists(oracle.LIBRARY) else None
-        c0 = time.perf_counter()
-        oracle.block_stack(xr, vr, ds.W_host, wl.S, eps=EPS, want_h=False, nthreads=cores)
-        c1 = time.perf_counter()
-        cpu = {"value": round(len(rows) / (c1 - c0), 1), "unit": "tokens/s", "cores": cores,
-               "kind": "oracle",
-               "sample": f"{len(rows)} of {wl.R} token rows (seed 0), full 48-sublayer naive "
-                         f"forward in fp64, {c1 - c0:.2f} s wall"}
+    cpu = cpu_baseline(ds, wl, args.cpu_seconds) if args.cpu_rows > 0 else None
 
     out = {
         "metric": METRIC,
