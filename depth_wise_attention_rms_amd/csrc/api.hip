@@ -452,14 +452,20 @@ ATTNRES_API int attnres_block_stack_forward(const void* x, int L, int S, int64_t
   return ok();
 }
 
+#ifndef ATTNRES_TIMING_EVENT_FLAGS
+#define ATTNRES_TIMING_EVENT_FLAGS hipEventDisableSystemFence
+#endif
+
 ATTNRES_API int attnres_timing_enable(int capacity) {
   Timing& t = g_timing;
   for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
   t = Timing();
   if (capacity <= 0) return ok();
   t.ev.resize(2 * (size_t)capacity, nullptr);
+  // Timing-only events: no system-scope fence (cache writeback) when they
+  // complete, which would otherwise add several microseconds per launch.
   for (auto& e : t.ev) {
-    hipError_t rc = hipEventCreate(&e);
+    hipError_t rc = hipEventCreateWithFlags(&e, ATTNRES_TIMING_EVENT_FLAGS);
     if (rc != hipSuccess) {
       for (hipEvent_t x : t.ev)
         if (x) (void)hipEventDestroy(x);

@@ -232,35 +232,65 @@ __global__ __launch_bounds__(512) void phase1_kernel(Phase1Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// Phase 1 on the matrix cores (bf16 I/O; S <= 10 queries, n <= 8 sources,
-// D a multiple of 128 up to 4096). The score contraction Q[S,D] . b_i[D] is
-// a dense product over the hidden axis, so it runs on v_mfma_f32_32x32x16_bf16:
-// rows of the A operand are (query, part) pairs -- each fp32 query is the
-// exact sum of three bf16 parts, so bf16 x bf16 products accumulated in fp32
-// keep fp32 accuracy -- and the B columns are the row's sources. Everything
-// else (sums of squares, softmax, the weighted sums of the raw sources) stays
-// in fp32 on the vector ALUs.
+// Phase 1 on the matrix cores (bf16 I/O; S <= 8 queries, n <= 8 sources,
+// D in {1024, 2048, 3072, 4096}). Both contractions of a token row run on the
+// matrix cores with fp32 accumulation, each fp32 operand split exactly into
+// three bf16 parts (h1 = bf16(x), h2 = bf16(x - h1), h3 = x - h1 - h2) so the
+// bf16 x bf16 products keep fp32 accuracy:
+//   scores   t[s][i] = q~_s . b_i over the hidden axis (v_mfma_f32_16x16x32_bf16;
+//            A rows 4s + j hold part j of query s, row 4s + 3 is zero, so the
+//            three partial products of a query land in one lane's registers;
+//            B columns are the row's sources), and
+//   outputs  o_s[d] = sum_i alpha[s][i] b_i[d] over the sources
+//            (v_mfma_f32_32x32x16_bf16, see the output step below).
+// Sums of squares (v_dot2 on the same B fragments), the softmax and the
+// statistics stay on the vector ALUs in fp32.
 //
 // One workgroup of 8 waves per CU walks token rows. Wave w owns the hidden
 // slice [w*D/8, (w+1)*D/8) and keeps the query parts of that slice in
-// registers for the whole kernel. A row's sources sit in one of two LDS
-// buffers (each source row padded by 32 bytes so lanes reading different
-// sources at one column hit different banks); while a row is processed, the
-// next row is copied from HBM straight into the other buffer with
-// global_load_lds, so its latency overlaps the work. A fused block close
-// stages its p and v rows and forms b = round(p + v) where it is used.
+// registers for the whole kernel. A row's sources are copied from HBM
+// straight into a slot of an LDS ring (global_load_lds, 16 bytes per lane),
+// up to three rows ahead of the row being scored and written. Each source row
+// in a slot is padded by 32 bytes so lanes reading different sources at one
+// column hit different banks. A fused block close stages its p and v rows and
+// forms b = round(p + v) in place before the row is scored. At D = 4096 each
+// wave copies, scores and writes only its own slice, so a row needs a single
+// barrier (for the cross-wave score reduction). The outputs are written with
+// plain stores, the copies are non-temporal: with non-temporal output stores
+// the kernel ran about 10% slower.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kP1Waves = 8;
 constexpr int kP1MaxN = 8;
-constexpr int kP1MaxS = 10;
-#ifndef ATTNRES_P1_OUT_BATCH
-#define ATTNRES_P1_OUT_BATCH 4
+constexpr int kP1MaxS = 8;
+#ifndef ATTNRES_P1_FENCE
+#define ATTNRES_P1_FENCE 4
 #endif
-constexpr int kP1OB = ATTNRES_P1_OUT_BATCH;  // queries per output batch
+constexpr int kP1Fence = ATTNRES_P1_FENCE;  // k-steps between scheduling fences (0: none)
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+constexpr int kP1LdsBytes = 160 * 1024;
+
+// Shapes of one instantiation: KS k-steps of 16 per wave (D = 128 KS), NC
+// sources per row.
+template <int KS, int NC>
+struct P1Shape {
+  static constexpr int D = 128 * KS;
+  static constexpr int STRIDE = D + 16;    // bf16 elements per staged row
+  static constexpr int NCH = KS / 4;       // 1 KiB chunks per row; wave w copies chunk w
+  static constexpr int ROWS = NC + 1;      // staged rows per slot: sources, then p of a close
+  static constexpr int SLOT = ROWS * STRIDE;
+  static constexpr int RED = 2 * (kP1Waves * kP1MaxS * NC + kP1Waves * NC);  // floats, two rows
+  // With 8 chunks per row, wave w copies, closes, scores and writes only chunk
+  // w (its hidden slice) of every staged row, so rows need no barrier of their
+  // own: the only exchange between waves is the score reduction.
+  static constexpr bool PRIVATE = NCH == kP1Waves;
+  static constexpr int FIT = (kP1LdsBytes - 4 * RED - 1024) / (2 * SLOT);
+  static constexpr int NBUF = FIT > 4 ? 4 : FIT;  // ring slots (prefetch distance NBUF - 1)
+  static_assert(NBUF >= 2, "a row and its successor must fit in LDS");
+};
 
 struct Phase1MParams {
   const void* src[kP1MaxN];
@@ -280,28 +310,6 @@ struct Phase1MParams {
 
 // x rounded to the nearest bf16 (ties to even), as an fp32 value
 __device__ __forceinline__ float bf16_round(float x) { return (float)(__bf16)x; }
-
-// Wait until at most k vector-memory operations of this wave are outstanding.
-// Global loads (including loads into LDS) and stores of one wave report
-// completion in issue order, so this waits for everything issued before the
-// last k operations. LDS and scalar counters are not waited on.
-__device__ __forceinline__ void wait_vm(int k) {
-#define ATTNRES_WAIT_VM(K) __builtin_amdgcn_s_waitcnt(((K) & 0xF) | (((K) >> 4) << 14) | (0x7 << 4) | (0xF << 8))
-  switch (k) {
-    case 0: ATTNRES_WAIT_VM(0); break;
-    case 1: ATTNRES_WAIT_VM(1); break;
-    case 2: ATTNRES_WAIT_VM(2); break;
-    case 3: ATTNRES_WAIT_VM(3); break;
-    case 4: ATTNRES_WAIT_VM(4); break;
-    case 5: ATTNRES_WAIT_VM(5); break;
-    case 6: ATTNRES_WAIT_VM(6); break;
-    case 7: ATTNRES_WAIT_VM(7); break;
-    case 8: ATTNRES_WAIT_VM(8); break;
-    case 9: ATTNRES_WAIT_VM(9); break;
-    default: ATTNRES_WAIT_VM(10); break;
-  }
-#undef ATTNRES_WAIT_VM
-}
 
 // Reductions over the 8-lane groups of a wave (lanes 8g .. 8g+7): swaps within
 // quads, then the mirror of each half row. Every lane gets its group's result.
@@ -341,83 +349,189 @@ __device__ __forceinline__ gchar_t* uniform_ptr(const void* p) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
   return (gchar_t*)(((uint64_t)hi << 32) | lo);
 }
+typedef __attribute__((address_space(1))) u32x4_t gu32x4_t;
 __device__ __forceinline__ void st16_stream(gchar_t* p, const uint4& v) {
-  typedef __attribute__((address_space(1))) u32x4_t gu32x4_t;
   const u32x4_t t = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(t, reinterpret_cast<gu32x4_t*>(p));
 }
+// Plain (cached) 16-byte store. Phase 1 writes its S outputs with these: with
+// the non-temporal hint its eight output streams per row ran about 10% slower.
+__device__ __forceinline__ void st16_global(gchar_t* p, const uint4& v) {
+  const u32x4_t t = {v.x, v.y, v.z, v.w};
+  *reinterpret_cast<gu32x4_t*>(p) = t;
+}
 
-// Staged rows of one token row in an LDS buffer ([NC + 1][STRIDE] bf16): the
-// sources (for a close, v in place of the closing source) and, for a close
-// with a partial, p after them. Wave w moves 1 KiB chunks w, w+8, ... of each
-// row, 64 lanes x 16 bytes straight into LDS; the chunk count NCH = D / 512
-// is at most 8, so each wave copies (and later forms the close of) chunk w.
+// Address of a __shared__ object as an LDS byte offset.
+typedef __attribute__((address_space(3))) char lchar_t;
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const lchar_t*)p;
+}
+
+// Copy 16 bytes per lane from global memory (wave-uniform base + lane offset)
+// into LDS at the wave-uniform offset lds + 16 * lane, non-temporal (each
+// source row is read once per launch). Issued as inline
+// assembly so that the compiler's own wait-counter bookkeeping, which cannot
+// tell ring slots apart, adds no waits before LDS reads: the kernel waits for
+// these copies itself (p1_wait), before the barrier that publishes them.
+// M0 is written here; nothing else in these kernels uses it.
+__device__ __forceinline__ void dma16(const gchar_t* base, uint32_t lane_off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(lane_off), "s"(base) : "memory");
+}
+
+// Wait until at most k (clamped to the counter's 63) vector-memory operations
+// of this wave are outstanding. Global loads (including loads into LDS) and
+// stores of one wave report completion in issue order, so this waits for
+// everything issued before the last k operations. LDS and scalar counters
+// are not waited on.
+__device__ __forceinline__ void p1_wait(int k) {
+  k = __builtin_amdgcn_readfirstlane(k);  // wave-uniform: a scalar branch, not a lane compare
+#define ATTNRES_W(K) case K: __builtin_amdgcn_s_waitcnt(((K) & 0xF) | (((K) >> 4) << 14) | (0x7 << 4) | (0xF << 8)); break;
+#define ATTNRES_W8(K) ATTNRES_W(K) ATTNRES_W(K + 1) ATTNRES_W(K + 2) ATTNRES_W(K + 3) \
+                      ATTNRES_W(K + 4) ATTNRES_W(K + 5) ATTNRES_W(K + 6) ATTNRES_W(K + 7)
+  switch (k < 63 ? k : 63) {
+    ATTNRES_W8(0) ATTNRES_W8(8) ATTNRES_W8(16) ATTNRES_W8(24)
+    ATTNRES_W8(32) ATTNRES_W8(40) ATTNRES_W8(48) ATTNRES_W8(56)
+    default: break;
+  }
+#undef ATTNRES_W8
+#undef ATTNRES_W
+}
+
+// Stage token row `row` into ring slot `slot`: the sources (for a close, v in
+// place of the closing source) and, for a close with a partial, p after them.
+// Returns the number of copy instructions this wave issued.
 template <int KS, int NC>
-__device__ __forceinline__ void p1_copy_row(const Phase1MParams& p, int64_t row, bool has_close,
-                                            __bf16* buf, int w, int l) {
-  constexpr int D = 128 * KS, STRIDE = D + 16, NCH = KS / 4;
-  if (w >= NCH) return;
-  const int64_t roff = row * (int64_t)D * 2;
+__device__ __forceinline__ int p1_stage(const Phase1MParams& p, int64_t row, const __bf16* slot,
+                                        int w, int l) {
+  using Sh = P1Shape<KS, NC>;
+  if (w >= Sh::NCH) return 0;
+  const int64_t roff = row * (int64_t)Sh::D * 2;
   const uint32_t loff = (uint32_t)((w * 64 + l) * 16);
+  const uint32_t lds = lds_offset(slot) + (uint32_t)(w * 1024);
+  const bool has_close = p.cl.v != nullptr;
   #pragma unroll
   for (int i = 0; i < NC; ++i) {
     const void* g = (i == NC - 1 && has_close) ? p.cl.v : p.src[i];
-    __builtin_amdgcn_global_load_lds(uniform_ptr(static_cast<const char*>(g) + roff) + loff,
-                                     buf + (size_t)i * STRIDE + w * 512, 16, 0, 0);
+    dma16(uniform_ptr(static_cast<const char*>(g) + roff), loff, lds + (uint32_t)(i * Sh::STRIDE * 2));
   }
-  if (has_close && p.cl.p)
-    __builtin_amdgcn_global_load_lds(uniform_ptr(static_cast<const char*>(p.cl.p) + roff) + loff,
-                                     buf + (size_t)NC * STRIDE + w * 512, 16, 0, 0);
+  if (has_close && p.cl.p) {
+    dma16(uniform_ptr(static_cast<const char*>(p.cl.p) + roff), loff,
+          lds + (uint32_t)(NC * Sh::STRIDE * 2));
+    return NC + 1;
+  }
+  return NC;
 }
 
-// One token row: cur holds its staged rows (copied by this wave's own loads,
-// pending until the wait below), nxt receives the next row's.
 template <int KS, int NC>
-__device__ __forceinline__ void p1_row(const Phase1MParams& p, int64_t row, int wait, __bf16* cur,
-                                       __bf16* nxt, float* cred, float* ssred, const uint4 (&qa)[KS],
-                                       int w, int l) {
-  constexpr int D = 128 * KS, STRIDE = D + 16, NCH = KS / 4;
-  const int tid = w * 64 + l, col = l & 31, kg = l >> 5;
+__global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
+  using Sh = P1Shape<KS, NC>;
+  constexpr int D = Sh::D, STRIDE = Sh::STRIDE, NCH = Sh::NCH, NBUF = Sh::NBUF, PF = NBUF - 1;
+  __shared__ __attribute__((aligned(16))) __bf16 ring[NBUF * Sh::SLOT];
+  // partial scores [row parity][wave][query][source] and sums of squares
+  // [row parity][wave][source]; alternating rows use alternate halves, so a
+  // wave may write row r + 1's partials while another still reads row r's
+  __shared__ float cred_buf[2 * kP1Waves * kP1MaxS * NC];
+  __shared__ float ssred_buf[2 * kP1Waves * NC];
+
   const int S = p.S;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int col = l & 15, kg = l >> 4;  // B column (source) and k-group of this lane
   const bool has_close = p.cl.v != nullptr;
+  const bool owner = w < NCH;           // this wave copies, closes and writes chunk w of each row
   const int64_t rowbytes = (int64_t)D * 2;
 
-  wait_vm(wait);  // this wave's part of the row has landed in LDS
-  if (has_close && w < NCH) {
-    // b = round(p + v) (or v) over the chunk this wave copied; stored as the block sum
-    __bf16* bv = cur + (size_t)(NC - 1) * STRIDE + tid * 8;
-    uint4 u = *reinterpret_cast<const uint4*>(bv);
-    if (p.cl.p) {
-      const uint4 a = *reinterpret_cast<const uint4*>(cur + (size_t)NC * STRIDE + tid * 8);
-      float fa[8], fv[8];
-      Bf16::unpack(a, fa);
-      Bf16::unpack(u, fv);
-      #pragma unroll
-      for (int e = 0; e < 8; ++e) fa[e] += fv[e];
-      u = Bf16::pack(fa);
-      *reinterpret_cast<uint4*>(bv) = u;
-    }
-    st16_stream(uniform_ptr(static_cast<char*>(p.cl.b) + row * rowbytes) + (uint32_t)(tid * 16), u);
-  }
-  lds_barrier();
-  const int64_t next = row + gridDim.x;
-  if (next < p.R) p1_copy_row<KS, NC>(p, next, has_close, nxt, w, l);
-
-  // scores: C[(s, j)][i] over this wave's hidden slice, and sums of squares
-  f32x16_t acc0, acc1;
-  #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    acc0[r] = 0.f;
-    acc1[r] = 0.f;
-  }
-  float ss = 0.f;
-  const bool live = col < NC;
-  const __bf16* bsrc = cur + (size_t)(live ? col : 0) * STRIDE + w * (D / kP1Waves) + 8 * kg;
+  // A operand: qa[2 kk + t] is tile t of k-step kk (32 wide), row m = 16 t + l % 16
+  // = part j = m % 4 of query s = m / 4 (part 3 is zero), k-group l / 16.
+  uint4 qa[KS];
   #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
-    uint4 b = make_uint4(0, 0, 0, 0);
-    if (live) {
-      b = *reinterpret_cast<const uint4*>(bsrc + 16 * kk);
+    const int m = 16 * (kk & 1) + col, s = m >> 2, j = m & 3;
+    float part[8];
+    #pragma unroll
+    for (int e = 0; e < 8; ++e) part[e] = 0.f;
+    if (s < S && j < 3) {
+      float q[8];
+      load_query<8>(p.Wq, p.G, (int64_t)s * D + w * (D / kP1Waves) + 32 * (kk >> 1) + 8 * kg, q);
+      #pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float h1 = bf16_round(q[e]);
+        const float r1 = q[e] - h1;  // exact
+        const float h2 = bf16_round(r1);
+        const float r2 = r1 - h2;    // exact
+        part[e] = j == 0 ? h1 : j == 1 ? h2 : r2;
+      }
+    }
+    qa[kk] = Bf16::pack(part);  // each part is a bf16 value: packing is exact
+  }
+
+  // Vector-memory operations this wave has issued (copies, block-sum and
+  // output stores; the statistics stores of wave 0 are left out, which only
+  // makes the waits stricter), and the count right after each in-flight
+  // row's copy was issued, oldest first.
+  int issued = 0;
+  int mark[PF];
+  const int64_t G = gridDim.x;
+  #pragma unroll
+  for (int f = 0; f < PF; ++f) {
+    const int64_t r = blockIdx.x + f * G;
+    if (r < p.R) issued += p1_stage<KS, NC>(p, r, ring + f * Sh::SLOT, w, l);
+    mark[f] = issued;
+  }
+
+  int slot = 0, parity = 0;
+  for (int64_t row = blockIdx.x; row < p.R; row += G) {
+    __bf16* cur = ring + slot * Sh::SLOT;
+    float* cred = cred_buf + parity * (kP1Waves * kP1MaxS * NC);
+    float* ssred = ssred_buf + parity * (kP1Waves * NC);
+    p1_wait(issued - mark[0]);  // this wave's part of the row has landed in LDS
+    #pragma unroll
+    for (int f = 0; f + 1 < PF; ++f) mark[f] = mark[f + 1];
+    if (has_close && owner) {
+      // b = round(p + v) (or v) over the chunk this wave copied; stored as the block sum
+      __bf16* bv = cur + (size_t)(NC - 1) * STRIDE + tid * 8;
+      uint4 u = *reinterpret_cast<const uint4*>(bv);
+      if (p.cl.p) {
+        const uint4 a = *reinterpret_cast<const uint4*>(cur + (size_t)NC * STRIDE + tid * 8);
+        float fa[8], fv[8];
+        Bf16::unpack(a, fa);
+        Bf16::unpack(u, fv);
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) fa[e] += fv[e];
+        u = Bf16::pack(fa);
+        *reinterpret_cast<uint4*>(bv) = u;
+      }
+      st16_stream(uniform_ptr(static_cast<char*>(p.cl.b) + row * rowbytes) + (uint32_t)(tid * 16), u);
+      issued += 1;
+    }
+    if constexpr (!Sh::PRIVATE) {
+      lds_barrier();  // every wave's copy of this row (and the block sum) is in LDS;
+                      // every wave is done with the previous row's slot
+    } else {
+      // this wave's own reads of the previous row's slot (refilled below) are done
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    }
+    {
+      const int64_t ahead = row + PF * G;
+      const int fill = slot == 0 ? NBUF - 1 : slot - 1;  // the previous row's slot
+      if (ahead < p.R) issued += p1_stage<KS, NC>(p, ahead, ring + fill * Sh::SLOT, w, l);
+      mark[PF - 1] = issued;
+    }
+
+    // scores C[(s, j)][i] over this wave's hidden slice (two 16-row tiles of A;
+    // even and odd k-steps accumulate separately), and sums of squares. B
+    // columns past the row's sources read a real source row: a column of C
+    // depends only on its own column of B, and those columns are not used.
+    float ss0 = 0.f, ss1 = 0.f;
+    const __bf16* bsrc = cur + (size_t)(col < NC ? col : NC - 1) * STRIDE + w * (D / kP1Waves) + 8 * kg;
+    f32x4_t c[4];
+    #pragma unroll
+    for (int t = 0; t < 4; ++t) c[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const bool two = S > 4;
+    #pragma unroll
+    for (int kk = 0; kk < KS / 2; ++kk) {
+      const uint4 b = *reinterpret_cast<const uint4*>(bsrc + 32 * kk);
+      float& ss = (kk & 1) ? ss1 : ss0;
       ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b.x),
                                            __builtin_bit_cast(bf16x2v_t, b.x), ss, false);
       ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b.y),
@@ -426,144 +540,134 @@ __device__ __forceinline__ void p1_row(const Phase1MParams& p, int64_t row, int 
                                            __builtin_bit_cast(bf16x2v_t, b.z), ss, false);
       ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b.w),
                                            __builtin_bit_cast(bf16x2v_t, b.w), ss, false);
+      const int e = (kk & 1) * 2;
+      c[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[2 * kk]),
+                                                    __builtin_bit_cast(bf16x8_t, b), c[e], 0, 0, 0);
+      if (two)
+        c[e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[2 * kk + 1]),
+                                                          __builtin_bit_cast(bf16x8_t, b), c[e + 1], 0, 0, 0);
+      if (kP1Fence > 0 && kk % kP1Fence == kP1Fence - 1)
+        __builtin_amdgcn_sched_barrier(0);  // bound the LDS reads in flight
     }
-    if (kk & 1)
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qa[kk]),
-                                                     __builtin_bit_cast(bf16x8_t, b), acc1, 0, 0, 0);
-    else
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, qa[kk]),
-                                                     __builtin_bit_cast(bf16x8_t, b), acc0, 0, 0, 0);
-    if ((kk & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the LDS reads in flight
-  }
-  if (live) {
-    // all 32 rows of A are written; rows past 3S hold exact zeros
-    float* cw = cred + (w * 32 + 4 * kg) * NC + col;
-    #pragma unroll
-    for (int r = 0; r < 16; ++r) cw[(8 * (r / 4) + (r & 3)) * NC] = acc0[r] + acc1[r];
-    ssred[(w * 2 + kg) * NC + col] = ss;
-  }
-  lds_barrier();
+    // sum of squares of source col over this wave's slice: add the four k-groups
+    float ss = ss0 + ss1;
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    if (col < NC) {
+      // D element r of lane l is row 4 (l / 16) + r, column l % 16 of its tile:
+      // parts r = 0, 1, 2 of query 4 t + l / 16 (part 3 is zero)
+      cred[(w * kP1MaxS + kg) * NC + col] = (c[0][0] + c[2][0]) + (c[0][1] + c[2][1]) + (c[0][2] + c[2][2]);
+      if (two)
+        cred[(w * kP1MaxS + 4 + kg) * NC + col] =
+            (c[1][0] + c[3][0]) + (c[1][1] + c[3][1]) + (c[1][2] + c[3][2]);
+      if (kg == 0) ssred[w * NC + col] = ss;
+    }
+    lds_barrier();
 
-  // softmax, computed by every wave for itself: lane 8*s' + i holds the score
-  // of source i for query s = s' (first half) or 8 + s' (second half, S > 8)
-  const int i = l & 7;
-  float a_lo = 0.f, a_hi = 0.f;
-  #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (h == 1 && S <= 8) break;
-    const int s = 8 * h + (l >> 3);
-    const bool valid = i < NC && s < S;
-    float sc = -INFINITY;
-    if (valid) {
-      float dot = 0.f, sq = 0.f;
-      #pragma unroll
-      for (int ww = 0; ww < kP1Waves; ++ww) {
-        const float* c = cred + (ww * 32 + 3 * s) * NC + i;
-        dot += c[0] + c[NC] + c[2 * NC];
-        sq += ssred[(ww * 2) * NC + i] + ssred[(ww * 2 + 1) * NC + i];
-      }
-      sc = dot * rsqrtf(sq * p.invD + p.eps);
-    }
-    const float m = group8_max(sc);
-    const float e = valid ? __expf(sc - m) : 0.f;
-    const float z = group8_sum(e);
-    const float a = e * (1.0f / z);
-    if (h == 0) a_lo = a; else a_hi = a;
-    if (w == 0 && i == 0 && s < S) {
-      if (p.m_out) p.m_out[(int64_t)s * p.R + row] = m;
-      p.lse_out[(int64_t)s * p.R + row] = m + __logf(z);
-    }
-  }
-
-  // outputs: o_s = sum_i alpha[s][i] b_i over this thread's vector, kP1OB
-  // queries at a time (the wave's lanes own vectors 64w .. 64w+63)
-  if (w < NCH) {
-    uint4 x[NC];
-    #pragma unroll
-    for (int k = 0; k < NC; ++k) x[k] = *reinterpret_cast<const uint4*>(cur + (size_t)k * STRIDE + tid * 8);
-    for (int s0 = 0; s0 < S; s0 += kP1OB) {
-      float o[kP1OB][8];
-      #pragma unroll
-      for (int q = 0; q < kP1OB; ++q)
+    // softmax, computed by every wave for itself: lane 8 s + i holds the score
+    // of source i for query s
+    const int i = l & 7, sq_ = l >> 3;
+    float alpha;
+    {
+      const bool valid = i < NC && sq_ < S;
+      float sc = -INFINITY;
+      if (valid) {
+        float dot[kP1Waves], sq[kP1Waves];
         #pragma unroll
-        for (int e = 0; e < 8; ++e) o[q][e] = 0.f;
-      #pragma unroll
-      for (int k = 0; k < NC; ++k) {
-        float xf[8];
-        Bf16::unpack(x[k], xf);
-        #pragma unroll
-        for (int q = 0; q < kP1OB; ++q) {
-          const int s = s0 + q;
-          if (s < S) {
-            const float a = __int_as_float(__builtin_amdgcn_readlane(
-                __float_as_int(s < 8 ? a_lo : a_hi), 8 * (s & 7) + k));
-            #pragma unroll
-            for (int e = 0; e < 8; ++e) o[q][e] += a * xf[e];
-          }
+        for (int ww = 0; ww < kP1Waves; ++ww) {
+          dot[ww] = cred[(ww * kP1MaxS + sq_) * NC + i];
+          sq[ww] = ssred[ww * NC + i];
         }
+        #pragma unroll
+        for (int h = kP1Waves / 2; h >= 1; h /= 2)
+          #pragma unroll
+          for (int ww = 0; ww < h; ++ww) {
+            dot[ww] += dot[ww + h];
+            sq[ww] += sq[ww + h];
+          }
+        sc = dot[0] * rsqrtf(sq[0] * p.invD + p.eps);
       }
-      #pragma unroll
-      for (int q = 0; q < kP1OB; ++q)
-        if (s0 + q < S)
-          st16_stream(uniform_ptr(static_cast<char*>(p.out) + ((int64_t)(s0 + q) * p.R + row) * rowbytes) +
-                          (uint32_t)(tid * 16),
-                      Bf16::pack(o[q]));
+      const float m = group8_max(sc);
+      const float e = valid ? __expf(sc - m) : 0.f;
+      const float z = group8_sum(e);
+      alpha = e * (1.0f / z);
+      if (w == 0 && i == 0 && sq_ < S) {
+        if (p.m_out) p.m_out[(int64_t)sq_ * p.R + row] = m;
+        p.lse_out[(int64_t)sq_ * p.R + row] = m + __logf(z);
+      }
     }
-  }
-}
 
-template <int KS, int NC>
-__global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
-  constexpr int D = 128 * KS, STRIDE = D + 16, NCH = KS / 4;
-  __shared__ __attribute__((aligned(16))) __bf16 bufA[(NC + 1) * STRIDE];
-  __shared__ __attribute__((aligned(16))) __bf16 bufB[(NC + 1) * STRIDE];
-  __shared__ float cred[kP1Waves * 32 * NC];  // partial scores [wave][row of A][source]
-  __shared__ float ssred[kP1Waves * 2 * NC];  // partial sums of squares [wave][half][source]
-
-  const int S = p.S;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int col = l & 31, kg = l >> 5;
-  const bool has_close = p.cl.v != nullptr;
-
-  // A operand: part j of query s = m / 3 (j = m % 3) for this lane's row m
-  uint4 qa[KS];
-  {
-    const int m = col, s = m / 3, j = m - 3 * (m / 3);
-    #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
+    // outputs on the matrix cores: o_s[d] = sum_i alpha[s][i] b_i[d] as
+    // 32x32x16 bf16 products with fp32 accumulation. A row 4 s + j holds
+    // part j of alpha[s][0..7] (the exact three-part bf16 split; row 4 s + 3
+    // and queries past S are zero) in k-group 0 for the first pass and in
+    // k-group 1 for the second. B column n is the 8 sources at one element:
+    // in the e-th product, element e of the vector of lane n (k-group 0) and
+    // of lane n + 32 (k-group 1), so the first pass yields lane n's vector and
+    // the second lane n + 32's. Accumulator r of lane l is row
+    // 8 (r / 4) + 4 (l / 32) + r % 4: query 2 (r / 4) + l / 32, part r % 4 --
+    // every lane ends with 8 consecutive outputs of 4 queries, stored as
+    // 16-byte vectors. Non-finite sources make the whole wave's outputs
+    // unspecified (a zero weight times Inf is NaN).
+    if (owner) {
+      uint4 x[8];
+      #pragma unroll
+      for (int k = 0; k < 8; ++k)
+        x[k] = k < NC ? *reinterpret_cast<const uint4*>(cur + (size_t)k * STRIDE + tid * 8)
+                      : make_uint4(0, 0, 0, 0);
+      const int am = l & 31, as = am >> 2, aj = am & 3;
       float part[8];
       #pragma unroll
-      for (int e = 0; e < 8; ++e) part[e] = 0.f;
-      if (s < S) {
-        const int d0 = w * (D / kP1Waves) + 16 * kk + 8 * kg;
-        float q[8];
-        load_query<8>(p.Wq, p.G, (int64_t)s * D + d0, q);
+      for (int k = 0; k < 8; ++k) {
+        const float a = __shfl(alpha, 8 * as + k);  // alpha[as][k] (lane 8 as + k)
+        const float h1 = bf16_round(a);
+        const float r1 = a - h1;  // exact
+        const float h2 = bf16_round(r1);
+        const float r2 = r1 - h2;  // exact
+        part[k] = (as >= S || k >= NC) ? 0.f : aj == 0 ? h1 : aj == 1 ? h2 : aj == 2 ? r2 : 0.f;
+      }
+      const uint4 af = Bf16::pack(part);  // each part is a bf16 value: packing is exact
+      const uint4 z4 = make_uint4(0, 0, 0, 0);
+      const bool upper = l >= 32;
+      const f32x16_t zero16 = {};
+      #pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+        const uint4 A = (upper == (pass == 1)) ? af : z4;
+        float o[4][8];
         #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float h1 = bf16_round(q[e]);
-          const float r1 = q[e] - h1;  // exact
-          const float h2 = bf16_round(r1);
-          const float r2 = r1 - h2;    // exact
-          part[e] = j == 0 ? h1 : j == 1 ? h2 : r2;
+          // (x_{2t}[e], x_{2t+1}[e]) for t = 0..3
+          uint32_t bt[4];
+          #pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t lo = (e < 2 ? x[2 * t].x : e < 4 ? x[2 * t].y : e < 6 ? x[2 * t].z : x[2 * t].w);
+            const uint32_t hi = (e < 2 ? x[2 * t + 1].x : e < 4 ? x[2 * t + 1].y : e < 6 ? x[2 * t + 1].z
+                                                                                   : x[2 * t + 1].w);
+            bt[t] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+          }
+          const f32x16_t c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, A), __builtin_bit_cast(bf16x8_t, make_uint4(bt[0], bt[1], bt[2], bt[3])),
+              zero16, 0, 0, 0);
+          #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            o[q][e] = (c[4 * q] + c[4 * q + 1]) + c[4 * q + 2];
+            asm volatile("" : "+v"(o[q][e]));  // reduce now: the 16 accumulators die here
+          }
+        }
+        const int vec = w * 64 + am + 32 * pass;  // vector of the row this lane writes
+        #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int sq = 2 * q + (upper ? 1 : 0);
+          if (2 * q < S && sq < S)
+            st16_global(uniform_ptr(static_cast<char*>(p.out) + ((int64_t)(2 * q) * p.R + row) * rowbytes) +
+                            (uint32_t)((upper ? p.R * rowbytes : 0) + vec * 16),
+                        Bf16::pack(o[q]));
         }
       }
-      qa[kk] = Bf16::pack(part);  // each part is a bf16 value: packing is exact
+      issued += 2 * ((S + 1) >> 1);
     }
-  }
-
-  // The copy of a row into a buffer is followed, before the next wait, only by
-  // this wave's S output stores (and, in wave 0, the statistics stores).
-  const int steady = w < NCH ? S : 0;
-  int64_t row = blockIdx.x;
-  if (row < p.R) p1_copy_row<KS, NC>(p, row, has_close, bufA, w, l);
-  int wait = 0;
-  while (row < p.R) {
-    p1_row<KS, NC>(p, row, wait, bufA, bufB, cred, ssred, qa, w, l);
-    wait = steady;
-    row += gridDim.x;
-    if (row >= p.R) break;
-    p1_row<KS, NC>(p, row, wait, bufB, bufA, cred, ssred, qa, w, l);
-    row += gridDim.x;
+    slot = slot == NBUF - 1 ? 0 : slot + 1;
+    parity ^= 1;
   }
 }
 

@@ -141,11 +141,14 @@ PH1_CASES = [
     (6, 8, 3, 16384, "bf16"), (3, 1, 1, 8, "bf16"),
     (2, 8, 37, 516, "f32"), (6, 8, 65, 4096, "f32"), (8, 5, 9, 2048, "f32"), (13, 4, 9, 1024, "f32"),
     (1, 5, 37, 1028, "f32"), (1, 3, 9, 8, "f32"),
-    # the matrix-core path (bf16, S <= 10, n <= 8, D in {1024, 2048, 3072, 4096});
-    # R above the CU count gives each workgroup several rows, odd and even
-    (7, 10, 300, 2048, "bf16"), (8, 3, 513, 1024, "bf16"), (2, 1, 260, 3072, "bf16"),
-    (4, 9, 1000, 4096, "bf16"), (8, 8, 37, 4096, "bf16"), (6, 8, 700, 4096, "bf16"),
-    (1, 10, 300, 1024, "bf16"), (3, 7, 777, 3072, "bf16"),
+    # the matrix-core path (bf16, S <= 8, n <= 8, D in {1024, 2048, 3072, 4096}):
+    # one A tile for S <= 4, two above; R above the CU count gives each
+    # workgroup several rows, so the LDS ring wraps
+    (7, 8, 300, 2048, "bf16"), (8, 3, 513, 1024, "bf16"), (2, 1, 260, 3072, "bf16"),
+    (4, 4, 1000, 4096, "bf16"), (5, 5, 1000, 4096, "bf16"), (8, 8, 37, 4096, "bf16"),
+    (6, 8, 700, 4096, "bf16"), (1, 6, 300, 1024, "bf16"), (3, 7, 777, 3072, "bf16"),
+    # S = 9, 10 with n <= 8 take the vector-ALU kernel
+    (7, 10, 300, 2048, "bf16"), (4, 9, 1000, 4096, "bf16"),
 ]
 
 
