@@ -28,7 +28,7 @@ EXPORTS = (
     "attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge", "attnres_table_sublayer",
     "attnres_stack_workspace_bytes", "attnres_block_stack_forward", "attnres_block_layout",
     "attnres_atomic_block_size", "attnres_status_string", "attnres_last_error",
-    "attnres_timing_enable", "attnres_timing_reset", "attnres_timing_read",
+    "attnres_timing_enable", "attnres_timing_pause", "attnres_timing_reset", "attnres_timing_read",
 )
 
 SUBLAYER_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
@@ -69,12 +69,13 @@ def lib():
         L.attnres_last_error.argtypes = []
         L.attnres_last_error.restype = ctypes.c_char_p
         L.attnres_timing_enable.argtypes = [I]
+        L.attnres_timing_pause.argtypes = [I]
         L.attnres_timing_reset.argtypes = []
         L.attnres_timing_read.argtypes = [I, ctypes.POINTER(I64), ctypes.POINTER(D), ctypes.POINTER(D)]
         for f in ("attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge",
                   "attnres_table_sublayer", "attnres_block_stack_forward", "attnres_block_layout",
-                  "attnres_atomic_block_size", "attnres_timing_enable", "attnres_timing_reset",
-                  "attnres_timing_read"):
+                  "attnres_atomic_block_size", "attnres_timing_enable", "attnres_timing_pause",
+                  "attnres_timing_reset", "attnres_timing_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -247,6 +248,10 @@ def attnres_block_stack_forward(x: torch.Tensor, W: torch.Tensor, S: int, sublay
 
 def attnres_timing_enable(capacity: int):
     _check("attnres_timing_enable", lib().attnres_timing_enable(capacity))
+
+
+def attnres_timing_pause(paused: bool):
+    _check("attnres_timing_pause", lib().attnres_timing_pause(1 if paused else 0))
 
 
 def attnres_timing_reset():

@@ -85,6 +85,7 @@ struct Timing {
   std::vector<int> kind;
   std::vector<double> bytes;
   int used = 0;
+  bool paused = false;
   int64_t launches[K_COUNT] = {0};
   double ms[K_COUNT] = {0};
   double total_bytes[K_COUNT] = {0};
@@ -96,7 +97,7 @@ thread_local Timing g_timing;
 Launch timed_launch(int kind, double bytes, hipStream_t st) {
   Launch L{st, nullptr, nullptr};
   Timing& t = g_timing;
-  if (t.capacity > 0 && t.used < t.capacity) {
+  if (t.capacity > 0 && !t.paused && t.used < t.capacity) {
     const int slot = t.used++;
     t.kind[slot] = kind;
     t.bytes[slot] = bytes;
@@ -493,6 +494,11 @@ static int collect_timing() {
   }
   t.used = 0;
   return ATTNRES_OK;
+}
+
+ATTNRES_API int attnres_timing_pause(int paused) {
+  g_timing.paused = paused != 0;
+  return ok();
 }
 
 ATTNRES_API int attnres_timing_reset(void) {

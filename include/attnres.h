@@ -199,9 +199,12 @@ const char* attnres_last_error(void);
  * returns, for `kind`, the number of timed launches, their summed duration in
  * milliseconds and their summed algorithmic bytes (inputs read once plus
  * outputs written once, queries excluded). attnres_timing_reset clears the
- * totals and the recorded events.
+ * totals and the recorded events. attnres_timing_pause(1) stops recording
+ * (launches run untimed, with no event overhead) until attnres_timing_pause(0);
+ * enabling does not change the paused state.
  * ------------------------------------------------------------------------- */
 int attnres_timing_enable(int capacity);
+int attnres_timing_pause(int paused);
 int attnres_timing_reset(void);
 int attnres_timing_read(int kind, int64_t* launches, double* total_ms, double* total_bytes);
 
