@@ -156,6 +156,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU work of the oracle baseline (whole row chunks until this much has run)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--output-norm", action="store_true",
+                    help="hand every sublayer RMSNorm(h_l) * gamma_l (fused into Phase 2) instead of h_l")
     ap.add_argument("--calibration-copy-gib", type=float, default=0.0,
                     help="before the steps, copy a tensor of this many GiB with torch (a plain "
                          "copy kernel of known size, read once and written once) so hardware "
@@ -174,6 +176,7 @@ def main() -> int:
               "single-GPU figure", file=sys.stderr)
         return 2
 
+    import numpy as np
     import torch
 
     from depth_wise_attention_rms_amd import binding
@@ -187,6 +190,10 @@ def main() -> int:
     assert wl.kind == "stack" and not wl.ring, "the benchmark times a resident-table stack workload"
     ds = DeviceStack(wl)
     nb = ds.nb
+    norm = None
+    if args.output_norm:
+        Gf = np.stack([inputs.gains(wl.seed + 100, wl.D, layer=l) for l in range(wl.L)])
+        norm = (torch.from_numpy(Gf.astype(np.float32)).cuda(), 1e-6)
     stream = torch.cuda.current_stream()
 
     if args.calibration_copy_gib > 0:
@@ -199,7 +206,7 @@ def main() -> int:
         del src, dst
 
     for _ in range(args.warmup):
-        ds.forward()
+        ds.forward(norm=norm)
     torch.cuda.synchronize()
 
     # Kernel durations come from HIP events that each timed kernel's own
@@ -207,7 +214,7 @@ def main() -> int:
     # costs a few microseconds per launch, so only TIMED_STEPS evenly spaced
     # steps of the timed region record every one of their launches; the
     # others run uninstrumented.
-    launches_per_step = 1 + wl.L + 2 * nb + 1
+    launches_per_step = 1 + wl.L + 2 * nb + 1 + (nb if norm else 0)
     stride = max(1, args.steps // TIMED_STEPS)
     instrumented = [i for i in range(args.steps) if i % stride == stride // 2][:TIMED_STEPS]
     binding.attnres_timing_enable(len(instrumented) * launches_per_step + 16)
@@ -220,17 +227,17 @@ def main() -> int:
     for i in range(args.steps):
         if i in instrumented:
             binding.attnres_timing_pause(False)
-            ds.forward()
+            ds.forward(norm=norm)
             binding.attnres_timing_pause(True)
         else:
-            ds.forward()
+            ds.forward(norm=norm)
     ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall_ms = (t1 - t0) * 1e3 / args.steps
     gpu_ms = ev0.elapsed_time(ev1) / args.steps
     kinds = {}
-    for k in ("phase1", "phase2", "aggregate", "close", "fold"):
+    for k in ("phase1", "phase2", "aggregate", "close", "fold", "norm"):
         n, ms, byts = binding.attnres_timing_read(k)
         if n:
             n_step = n / len(instrumented)
@@ -269,7 +276,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded counter-based normals; inputs resident in HBM)",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "D": wl.D, "L": wl.L, "S": wl.S,
-                   "blocks": nb, "global_batch": wl.B, "seq_len": wl.T, "parallelism": "single GPU"},
+                   "blocks": nb, "global_batch": wl.B, "seq_len": wl.T, "parallelism": "single GPU",
+                   "output_norm": bool(norm)},
         "achieved_GBps": round(fwd_gbps, 1),
         "hbm_frac": round(fwd_gbps / PEAK_HBM_GBPS, 4),
         "bytes_per_step": fwd_bytes,

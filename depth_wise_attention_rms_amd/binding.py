@@ -22,11 +22,13 @@ LIB_PATH = os.path.join(PKG, "libattnres.so")
 
 ATTNRES_F32, ATTNRES_BF16 = 0, 1
 STATUS = {0: "ok", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP", -5: "ECALLBACK"}
-TIMING_KINDS = {"phase1": 0, "phase2": 1, "aggregate": 2, "close": 3, "fold": 4}
+TIMING_KINDS = {"phase1": 0, "phase2": 1, "aggregate": 2, "close": 3, "fold": 4, "norm": 5}
 
 EXPORTS = (
-    "attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge", "attnres_table_sublayer",
-    "attnres_stack_workspace_bytes", "attnres_block_stack_forward", "attnres_block_layout",
+    "attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge",
+    "attnres_phase2_merge_norm", "attnres_rmsnorm", "attnres_table_sublayer",
+    "attnres_stack_workspace_bytes", "attnres_block_stack_forward",
+    "attnres_block_stack_forward_norm", "attnres_block_layout",
     "attnres_atomic_block_size", "attnres_status_string", "attnres_last_error",
     "attnres_timing_enable", "attnres_timing_pause", "attnres_timing_reset", "attnres_timing_read",
 )
@@ -58,10 +60,14 @@ def lib():
         L.attnres_aggregate.argtypes = [P, I, I64, I64, I, P, P, F, P, P, P, P]
         L.attnres_phase1_batched.argtypes = [P, I, I64, I64, I, P, P, I, F, P, P, P, P]
         L.attnres_phase2_merge.argtypes = [P, P, P, P, F, P, P, P, P, I64, I64, I, P]
+        L.attnres_phase2_merge_norm.argtypes = [P, P, P, P, F, P, P, P, P, P, F, P, I64, I64, I, P]
+        L.attnres_rmsnorm.argtypes = [P, I64, I64, I, P, F, P, P]
         L.attnres_table_sublayer.argtypes = [P, I, P, ctypes.POINTER(P), P]
         L.attnres_stack_workspace_bytes.argtypes = [I, I, I64, I64, I]
         L.attnres_stack_workspace_bytes.restype = SZ
         L.attnres_block_stack_forward.argtypes = [P, I, I, I64, I64, I, P, P, F, P, P, P, P, P, SZ, P]
+        L.attnres_block_stack_forward_norm.argtypes = [P, I, I, I64, I64, I, P, P, F, P, F, P, P, P, P,
+                                                       P, SZ, P]
         L.attnres_block_layout.argtypes = [I, I, P, P]
         L.attnres_atomic_block_size.argtypes = [I, I]
         L.attnres_status_string.argtypes = [I]
@@ -73,6 +79,7 @@ def lib():
         L.attnres_timing_reset.argtypes = []
         L.attnres_timing_read.argtypes = [I, ctypes.POINTER(I64), ctypes.POINTER(D), ctypes.POINTER(D)]
         for f in ("attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge",
+                  "attnres_phase2_merge_norm", "attnres_rmsnorm", "attnres_block_stack_forward_norm",
                   "attnres_table_sublayer", "attnres_block_stack_forward", "attnres_block_layout",
                   "attnres_atomic_block_size", "attnres_timing_enable", "attnres_timing_pause",
                   "attnres_timing_reset", "attnres_timing_read"):
@@ -163,6 +170,33 @@ def attnres_phase2_merge(o, lse, w, v_prev, p_prev=None, gamma=None, eps=1e-8, p
     return h_out, p_out
 
 
+def attnres_phase2_merge_norm(o, lse, w, v_prev, gamma_f=None, eps_f=1e-6, p_prev=None, gamma=None,
+                              eps=1e-8, p_out=None, h_out=None, hn_out=None, want_h=False, stream=None):
+    """Phase-2 merge with the sublayer's input norm fused in; returns (hn_out, h_out, p_out).
+    h_out is written only when given or ``want_h``."""
+    R, D = _rows(o)
+    if hn_out is None:
+        hn_out = torch.empty_like(o)
+    if h_out is None and want_h:
+        h_out = torch.empty_like(o)
+    if p_prev is not None and p_out is None:
+        p_out = torch.empty_like(o)
+    _check("attnres_phase2_merge_norm", lib().attnres_phase2_merge_norm(
+        _ptr(o), _ptr(lse), _ptr(w), _ptr(gamma), eps, _ptr(p_prev), _ptr(v_prev), _ptr(p_out),
+        _ptr(h_out), _ptr(gamma_f), eps_f, _ptr(hn_out), R, D, dtype_code(o.dtype), _stream(stream)))
+    return hn_out, h_out, p_out
+
+
+def attnres_rmsnorm(x, gamma=None, eps=1e-6, out=None, stream=None):
+    """out = RMSNorm(x) * gamma over the last axis (out may be x)."""
+    R, D = _rows(x)
+    if out is None:
+        out = torch.empty_like(x)
+    _check("attnres_rmsnorm", lib().attnres_rmsnorm(_ptr(x), R, D, dtype_code(x.dtype), _ptr(gamma),
+                                                    eps, _ptr(out), _stream(stream)))
+    return out
+
+
 def attnres_stack_workspace_bytes(L: int, S: int, R: int, D: int, dtype: torch.dtype) -> int:
     return int(lib().attnres_stack_workspace_bytes(L, S, R, D, dtype_code(dtype)))
 
@@ -198,10 +232,13 @@ Sublayer = Union[Sequence[torch.Tensor], NativeSublayer, Callable[[int, int], to
 
 def attnres_block_stack_forward(x: torch.Tensor, W: torch.Tensor, S: int, sublayer: Sublayer,
                                 Gamma=None, eps=1e-8, block_sums=None, y=None, workspace=None,
-                                stream=None):
+                                stream=None, norm=None):
     """Block AttnRes stack forward (Full when S == 1). ``sublayer`` is a list of
     L pre-computed outputs, a NativeSublayer, or a Python callable
-    ``f(l, h_ptr) -> tensor v_l``. Returns (y, block_sums)."""
+    ``f(l, h_ptr) -> tensor v_l``. Returns (y, block_sums). With
+    ``norm=(Gamma_f, eps_f)`` (Gamma_f an [L, D] fp32 tensor or None) the
+    sublayers receive RMSNorm(h_l) * Gamma_f[l-1] instead of h_l
+    (attnres_block_stack_forward_norm)."""
     R, D = _rows(x)
     L = W.shape[0] - 1
     dt = dtype_code(x.dtype)
@@ -240,9 +277,15 @@ def attnres_block_stack_forward(x: torch.Tensor, W: torch.Tensor, S: int, sublay
     else:
         raise TypeError("sublayer must be a tensor list, a NativeSublayer or a callable")
     bs = _ptr_array(block_sums) if block_sums is not None else None
-    _check("attnres_block_stack_forward", lib().attnres_block_stack_forward(
-        _ptr(x), L, S, R, D, dt, _ptr(W), _ptr(Gamma), eps, fn, ctx, bs, _ptr(y),
-        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
+    if norm is None:
+        _check("attnres_block_stack_forward", lib().attnres_block_stack_forward(
+            _ptr(x), L, S, R, D, dt, _ptr(W), _ptr(Gamma), eps, fn, ctx, bs, _ptr(y),
+            ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
+    else:
+        Gamma_f, eps_f = norm
+        _check("attnres_block_stack_forward_norm", lib().attnres_block_stack_forward_norm(
+            _ptr(x), L, S, R, D, dt, _ptr(W), _ptr(Gamma), eps, _ptr(Gamma_f), eps_f, fn, ctx, bs,
+            _ptr(y), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
     return y, block_sums
 
 

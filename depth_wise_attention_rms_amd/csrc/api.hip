@@ -77,7 +77,7 @@ int check_ptr(const char* fn, const char* name, const void* p, bool required) {
 // ---------------------------------------------------------------------------
 // launch timing (instrumentation)
 // ---------------------------------------------------------------------------
-enum Kind { K_PHASE1 = 0, K_PHASE2 = 1, K_AGG = 2, K_CLOSE = 3, K_FOLD = 4, K_COUNT = 5 };
+enum Kind { K_PHASE1 = 0, K_PHASE2 = 1, K_AGG = 2, K_CLOSE = 3, K_FOLD = 4, K_NORM = 5, K_COUNT = 6 };
 
 struct Timing {
   int capacity = 0;
@@ -165,8 +165,17 @@ int do_phase1(const char* fn, int dtype, const Phase1Args& a, hipStream_t st) {
 int do_phase2(const char* fn, int dtype, const Phase2Args& a, hipStream_t st) {
   if (a.R == 0) return ATTNRES_OK;
   const double rb = (double)a.R * a.D * esize_of(dtype);
-  const double bytes = rb * (a.p_prev ? 5 : 3) + (double)a.R * 4;
+  const int writes = (a.h_out ? 1 : 0) + (a.hn_out ? 1 : 0);
+  const double bytes = rb * ((a.p_prev ? 4 : 2) + writes) + (double)a.R * 4;
   hipError_t e = attnres::launch_phase2(dtype, a, timed_launch(K_PHASE2, bytes, st));
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
+}
+
+int do_rmsnorm(const char* fn, int dtype, const void* x, int64_t R, int64_t D, const float* g,
+               float eps, void* out, hipStream_t st) {
+  if (R == 0) return ATTNRES_OK;
+  const double bytes = 2.0 * (double)R * D * esize_of(dtype);
+  hipError_t e = attnres::launch_rmsnorm(dtype, x, R, D, g, eps, out, timed_launch(K_NORM, bytes, st));
   return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
 }
 
@@ -297,8 +306,54 @@ ATTNRES_API int attnres_phase2_merge(const void* o, const float* lse, const floa
     return fail(ATTNRES_EINVAL, "%s: h_out aliases an input or p_out", fn);
   if (p_out && (p_out == o || p_out == v_prev))
     return fail(ATTNRES_EINVAL, "%s: p_out aliases o or v_prev", fn);
-  Phase2Args a{o, lse, w, gamma, eps, p_prev, v_prev, p_out, h_out, R, D};
+  Phase2Args a{o, lse, w, gamma, eps, p_prev, v_prev, p_out, h_out, nullptr, 0.f, nullptr, R, D};
   TRY(do_phase2(fn, dtype, a, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+ATTNRES_API int attnres_phase2_merge_norm(const void* o, const float* lse, const float* w,
+                                          const float* gamma, float eps, const void* p_prev,
+                                          const void* v_prev, void* p_out, void* h_out,
+                                          const float* gamma_f, float eps_f, void* hn_out,
+                                          int64_t R, int64_t D, int dtype, void* stream) {
+  const char* fn = "attnres_phase2_merge_norm";
+  TRY(check_shape(fn, R, D, dtype, eps));
+  if (!std::isfinite(eps_f) || eps_f < 0.f)
+    return fail(ATTNRES_EINVAL, "%s: eps_f must be finite and >= 0", fn);
+  if (R == 0) return ok();
+  TRY(check_ptr(fn, "o", o, true));
+  TRY(check_ptr(fn, "lse", lse, true));
+  TRY(check_ptr(fn, "w", w, true));
+  TRY(check_ptr(fn, "gamma", gamma, false));
+  TRY(check_ptr(fn, "p_prev", p_prev, false));
+  TRY(check_ptr(fn, "v_prev", v_prev, true));
+  TRY(check_ptr(fn, "p_out", p_out, p_prev != nullptr));
+  TRY(check_ptr(fn, "h_out", h_out, false));
+  TRY(check_ptr(fn, "gamma_f", gamma_f, false));
+  TRY(check_ptr(fn, "hn_out", hn_out, true));
+  if (!p_prev && p_out) return fail(ATTNRES_EINVAL, "%s: p_out must be NULL when p_prev is NULL", fn);
+  for (const void* out : {h_out, hn_out}) {
+    if (!out) continue;
+    if (out == o || out == p_prev || out == v_prev || out == p_out)
+      return fail(ATTNRES_EINVAL, "%s: h_out or hn_out aliases an input or p_out", fn);
+  }
+  if (h_out && h_out == hn_out) return fail(ATTNRES_EINVAL, "%s: h_out and hn_out alias", fn);
+  if (p_out && (p_out == o || p_out == v_prev))
+    return fail(ATTNRES_EINVAL, "%s: p_out aliases o or v_prev", fn);
+  Phase2Args a{o, lse, w, gamma, eps, p_prev, v_prev, p_out, h_out, gamma_f, eps_f, hn_out, R, D};
+  TRY(do_phase2(fn, dtype, a, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+ATTNRES_API int attnres_rmsnorm(const void* x, int64_t R, int64_t D, int dtype, const float* gamma,
+                                float eps, void* out, void* stream) {
+  const char* fn = "attnres_rmsnorm";
+  TRY(check_shape(fn, R, D, dtype, eps));
+  if (R == 0) return ok();
+  TRY(check_ptr(fn, "x", x, true));
+  TRY(check_ptr(fn, "gamma", gamma, false));
+  TRY(check_ptr(fn, "out", out, true));
+  TRY(do_rmsnorm(fn, dtype, x, R, D, gamma, eps, out, static_cast<hipStream_t>(stream)));
   return ok();
 }
 
@@ -330,12 +385,52 @@ ATTNRES_API size_t attnres_stack_workspace_bytes(int L, int S, int64_t R, int64_
   return stack_layout(L, S, R, D, es).total;
 }
 
+namespace {
+
+// The output norm handed to the sublayers, when the stack runs with one: the
+// callback for sublayer l receives RMSNorm(h_l) * Gamma_f[l-1] instead of h_l.
+struct OutNorm {
+  bool on;
+  const float* Gamma_f;  // [L, D] or null (ones)
+  float eps_f;
+};
+
+int stack_forward(const char* fn, const void* x, int L, int S, int64_t R, int64_t D, int dtype,
+                  const float* W, const float* Gamma, float eps, attnres_sublayer_fn f, void* f_ctx,
+                  void* const* block_sums, void* y, void* workspace, size_t workspace_bytes,
+                  const OutNorm& nm, void* stream);
+
+}  // namespace
+
 ATTNRES_API int attnres_block_stack_forward(const void* x, int L, int S, int64_t R, int64_t D,
                                             int dtype, const float* W, const float* Gamma,
                                             float eps, attnres_sublayer_fn f, void* f_ctx,
                                             void* const* block_sums, void* y, void* workspace,
                                             size_t workspace_bytes, void* stream) {
-  const char* fn = "attnres_block_stack_forward";
+  return stack_forward("attnres_block_stack_forward", x, L, S, R, D, dtype, W, Gamma, eps, f, f_ctx,
+                       block_sums, y, workspace, workspace_bytes, OutNorm{false, nullptr, 0.f}, stream);
+}
+
+ATTNRES_API int attnres_block_stack_forward_norm(const void* x, int L, int S, int64_t R, int64_t D,
+                                                 int dtype, const float* W, const float* Gamma,
+                                                 float eps, const float* Gamma_f, float eps_f,
+                                                 attnres_sublayer_fn f, void* f_ctx,
+                                                 void* const* block_sums, void* y, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  const char* fn = "attnres_block_stack_forward_norm";
+  if (!std::isfinite(eps_f) || eps_f < 0.f)
+    return fail(ATTNRES_EINVAL, "%s: eps_f must be finite and >= 0", fn);
+  if (R > 0) TRY(check_ptr(fn, "Gamma_f", Gamma_f, false));
+  return stack_forward(fn, x, L, S, R, D, dtype, W, Gamma, eps, f, f_ctx, block_sums, y, workspace,
+                       workspace_bytes, OutNorm{true, Gamma_f, eps_f}, stream);
+}
+
+namespace {
+
+int stack_forward(const char* fn, const void* x, int L, int S, int64_t R, int64_t D, int dtype,
+                  const float* W, const float* Gamma, float eps, attnres_sublayer_fn f, void* f_ctx,
+                  void* const* block_sums, void* y, void* workspace, size_t workspace_bytes,
+                  const OutNorm& nm, void* stream) {
   TRY(check_shape(fn, R, D, dtype, eps));
   if (L < 1 || S < 1) return fail(ATTNRES_EINVAL, "%s: L = %d and S = %d must be >= 1", fn, L, S);
   const int nb = plan(L, S, nullptr, nullptr);
@@ -378,6 +473,12 @@ ATTNRES_API int attnres_block_stack_forward(const void* x, int L, int S, int64_t
     if (e != hipSuccess) return hip_fail(fn, e);
   }
 
+  // the sublayer's input: h_l, or RMSNorm(h_l) * Gamma_f[l-1] written to H
+  // (in place when h_l is already in H)
+  auto normed = [&](int l, const void* h) -> int {
+    return do_rmsnorm(fn, dtype, h, R, D, nm.Gamma_f ? nm.Gamma_f + (int64_t)(l - 1) * D : nullptr,
+                      nm.eps_f, H, st);
+  };
   auto call = [&](int l, const void* h, const void** v) -> int {
     const void* out = nullptr;
     const int rc = f(f_ctx, l, h, &out, stream);
@@ -410,6 +511,7 @@ ATTNRES_API int attnres_block_stack_forward(const void* x, int L, int S, int64_t
       AggArgs a{src.data(), n, R, D, Qk, nullptr, eps, H, nullptr, nullptr,
                 close_p, close_v, close_b};
       TRY(do_aggregate(fn, dtype, a, st));
+      if (nm.on) TRY(normed(start, H));
       const void* v = nullptr;
       TRY(call(start, H, &v));
       if (block_sums) {  // b_{k+1} = v, copied by the next launch
@@ -427,13 +529,21 @@ ATTNRES_API int attnres_block_stack_forward(const void* x, int L, int S, int64_t
     Phase1Args a1{src.data(), n, R, D, Qk, nullptr, Sk, eps, O, M, LSE, close_p, close_v, close_b};
     TRY(do_phase1(fn, dtype, a1, st));
     const void* v_first = nullptr;
-    TRY(call(start, O, &v_first));  // h_start = o_0: no partial yet
+    if (nm.on) {
+      TRY(normed(start, O));
+      TRY(call(start, H, &v_first));
+    } else {
+      TRY(call(start, O, &v_first));  // h_start = o_0: no partial yet
+    }
     const void* p_cur = v_first;    // p_1 = v_start (aliased, no copy)
     const void* v_prev = v_first;
     for (int j = 1; j < Sk; ++j) {
       const int l = start + j;
       Phase2Args a2{O + (int64_t)j * tensor_bytes, LSE + (int64_t)j * R, Q + (int64_t)(l - 1) * D,
-                    nullptr, eps, j == 1 ? nullptr : p_cur, v_prev, j == 1 ? nullptr : P, H, R, D};
+                    nullptr, eps, j == 1 ? nullptr : p_cur, v_prev, j == 1 ? nullptr : P,
+                    nm.on ? nullptr : H,
+                    nm.on && nm.Gamma_f ? nm.Gamma_f + (int64_t)(l - 1) * D : nullptr, nm.eps_f,
+                    nm.on ? H : nullptr, R, D};
       TRY(do_phase2(fn, dtype, a2, st));
       if (j > 1) p_cur = P;
       const void* v = nullptr;
@@ -452,6 +562,8 @@ ATTNRES_API int attnres_block_stack_forward(const void* x, int L, int S, int64_t
   TRY(do_aggregate(fn, dtype, af, st));
   return ok();
 }
+
+}  // namespace
 
 #ifndef ATTNRES_TIMING_EVENT_FLAGS
 #define ATTNRES_TIMING_EVENT_FLAGS hipEventDisableSystemFence

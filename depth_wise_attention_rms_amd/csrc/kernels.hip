@@ -101,6 +101,16 @@ __device__ __forceinline__ void load_query(const float* __restrict__ w, const fl
   }
 }
 
+// EPV gains starting at element `off` (16-byte loads), or ones for a null gain.
+template <int EPV>
+__device__ __forceinline__ void load_gain(const float* __restrict__ g, int64_t off, float* out) {
+  #pragma unroll
+  for (int k = 0; k < EPV; k += 4) {
+    const float4 a = g ? ldf4(g + off + k) : make_float4(1.f, 1.f, 1.f, 1.f);
+    out[k] = a.x; out[k + 1] = a.y; out[k + 2] = a.z; out[k + 3] = a.w;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Phase 1 (batched inter-block pass) [K3 9.4 step 1; RH 4.2 Phase 1].
 // The n <= NMAX sources of a row are loaded once and held in registers as
@@ -817,11 +827,14 @@ struct Phase2Params {
   const void* p_prev;  // null on the first merge of a block
   const void* v_prev;
   void* p_out;         // null iff p_prev is null
-  void* h_out;
+  void* h_out;         // may be null when hn_out is set
+  const float* gf;     // [D] gain of the output norm, or null (ones)
+  float eps_f;
+  void* hn_out;        // RMSNorm(h) * gf, or null (no output norm)
   Geom g;
 };
 
-template <class T, int VPL, bool HAS_PREV>
+template <class T, int VPL, bool HAS_PREV, bool NORM>
 __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
   extern __shared__ float lds[];
   constexpr int EPV = T::kEPV;
@@ -869,25 +882,102 @@ __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
       }
     }
     row_reduce<2>(red, lds, ln.slot, ln.wr, g.W);
-    if (rv) {
-      const float sp = red[0] * rsqrtf(red[1] * g.invD + p.eps);
-      const float l = p.lse[row];
-      const float M = fmaxf(l, sp);
-      float a = __expf(l - M), b = __expf(sp - M);
-      const float r = 1.0f / (a + b);
-      a *= r;
-      b *= r;
+    const float sp = red[0] * rsqrtf(red[1] * g.invD + p.eps);
+    const float l = rv ? p.lse[row] : 0.f;
+    const float M = fmaxf(l, sp);
+    float a = __expf(l - M), b = __expf(sp - M);
+    const float r = 1.0f / (a + b);
+    a *= r;
+    b *= r;
+    uint4 hv[VPL];
+    float hss[1] = {0.f};
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      const int vec = c * ln.stride + ln.t;
+      float fo[EPV], fp[EPV];
+      T::unpack(ov[c], fo);
+      T::unpack(pv[c], fp);
+      #pragma unroll
+      for (int e = 0; e < EPV; ++e) fo[e] = a * fo[e] + b * fp[e];
+      hv[c] = T::pack(fo);  // h rounded to the I/O dtype
+      if (rv && vec < g.V && p.h_out) st16(static_cast<char*>(p.h_out) + base + (int64_t)vec * 16, hv[c]);
+      if (NORM && vec < g.V) {
+        T::unpack(hv[c], fo);
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) hss[0] += fo[e] * fo[e];
+      }
+    }
+    if constexpr (NORM) {
+      // the sublayer's input norm on the rounded h: RMSNorm(h) * gf
+      row_reduce<1>(hss, lds, ln.slot, ln.wr, g.W);
+      const float inv = rsqrtf(hss[0] * g.invD + p.eps_f);
       #pragma unroll
       for (int c = 0; c < VPL; ++c) {
         const int vec = c * ln.stride + ln.t;
-        if (vec < g.V) {
-          float fo[EPV], fp[EPV];
-          T::unpack(ov[c], fo);
-          T::unpack(pv[c], fp);
+        if (rv && vec < g.V) {
+          float f[EPV], gn[EPV];
+          T::unpack(hv[c], f);
+          load_gain<EPV>(p.gf, (int64_t)vec * EPV, gn);
           #pragma unroll
-          for (int e = 0; e < EPV; ++e) fo[e] = a * fo[e] + b * fp[e];
-          st16(static_cast<char*>(p.h_out) + base + (int64_t)vec * 16, T::pack(fo));
+          for (int e = 0; e < EPV; ++e) f[e] = gn[e] * (f[e] * inv);
+          st16(static_cast<char*>(p.hn_out) + base + (int64_t)vec * 16, T::pack(f));
         }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm of a token tensor, the input norm of the sublayer that consumes an
+// aggregate [ZZ block listing: attn(attn_norm(h)), mlp(mlp_norm(h)); WC
+// reference: eps inside the root, mean over the hidden axis]:
+// out = x / sqrt(mean_d x^2 + eps) * gamma, rounded to the I/O dtype. x and
+// out may be the same buffer (each lane reads its vectors before the row's
+// reduction and writes them after it).
+// ---------------------------------------------------------------------------
+struct NormParams {
+  const void* x;
+  const float* g;  // [D] or null (ones)
+  float eps;
+  void* out;
+  Geom geo;
+};
+
+template <class T, int VPL>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(NormParams p) {
+  extern __shared__ float lds[];
+  constexpr int EPV = T::kEPV;
+  const Geom& g = p.geo;
+  const Lanes ln(g.W);
+  const int64_t rowbytes = (int64_t)g.V * 16;
+  for (int64_t grp = blockIdx.x; grp < g.groups; grp += gridDim.x) {
+    const int64_t row = grp * g.RPW + ln.slot;
+    const bool rv = row < g.R;
+    const int64_t base = row * rowbytes;
+    uint4 xv[VPL];
+    float ss[1] = {0.f};
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      const int vec = c * ln.stride + ln.t;
+      const bool ok = rv && vec < g.V;
+      xv[c] = ok ? ld16_stream(static_cast<const char*>(p.x) + base + (int64_t)vec * 16) : make_uint4(0, 0, 0, 0);
+      float f[EPV];
+      T::unpack(xv[c], f);
+      #pragma unroll
+      for (int e = 0; e < EPV; ++e) ss[0] += f[e] * f[e];
+    }
+    row_reduce<1>(ss, lds, ln.slot, ln.wr, g.W);
+    const float inv = rsqrtf(ss[0] * g.invD + p.eps);
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      const int vec = c * ln.stride + ln.t;
+      if (rv && vec < g.V) {
+        float f[EPV], gn[EPV];
+        T::unpack(xv[c], f);
+        load_gain<EPV>(p.g, (int64_t)vec * EPV, gn);
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) f[e] = gn[e] * (f[e] * inv);
+        st16(static_cast<char*>(p.out) + base + (int64_t)vec * 16, T::pack(f));
       }
     }
   }
@@ -1093,7 +1183,10 @@ hipError_t launch_aggregate(int dtype, const AggArgs& a, const Launch& L) {
 template <class T, int VPL, bool HP>
 static hipError_t launch_ph2_t(Phase2Params& p, const Launch& L) {
   const size_t lds = p.g.W > 1 ? (size_t)p.g.RPW * p.g.W * 2 * sizeof(float) : 0;
-  return launch(L, phase2_kernel<T, VPL, HP>, dim3(grid_for(p.g)), dim3(64 * p.g.W * p.g.RPW),
+  if (p.hn_out)
+    return launch(L, phase2_kernel<T, VPL, HP, true>, dim3(grid_for(p.g)), dim3(64 * p.g.W * p.g.RPW),
+                  lds, p);
+  return launch(L, phase2_kernel<T, VPL, HP, false>, dim3(grid_for(p.g)), dim3(64 * p.g.W * p.g.RPW),
                 lds, p);
 }
 
@@ -1116,6 +1209,7 @@ static hipError_t launch_phase2_dt(const Phase2Args& a, const Launch& L) {
   Phase2Params p;
   p.o = a.o; p.lse = a.lse; p.w = a.w; p.gm = a.g; p.eps = a.eps;
   p.p_prev = a.p_prev; p.v_prev = a.v_prev; p.p_out = a.p_out; p.h_out = a.h_out;
+  p.gf = a.gf; p.eps_f = a.eps_f; p.hn_out = a.hn_out;
   // ATTNRES_PHASE2_VPL vectors per lane, more when a row would need over 4
   // waves (rows are at most 2048 vectors, so at most 8 per lane)
   const int V = (int)(a.D * T::kBytes / 16);
@@ -1128,6 +1222,39 @@ static hipError_t launch_phase2_dt(const Phase2Args& a, const Launch& L) {
 
 hipError_t launch_phase2(int dtype, const Phase2Args& a, const Launch& L) {
   return dtype == 1 ? launch_phase2_dt<Bf16>(a, L) : launch_phase2_dt<F32>(a, L);
+}
+
+template <class T, int VPL>
+static hipError_t launch_norm_t(const NormParams& p, const Launch& L) {
+  const size_t lds = p.geo.W > 1 ? (size_t)p.geo.RPW * p.geo.W * sizeof(float) : 0;
+  return launch(L, rmsnorm_kernel<T, VPL>, dim3(grid_for(p.geo)), dim3(64 * p.geo.W * p.geo.RPW), lds, p);
+}
+
+template <class T>
+static hipError_t launch_rmsnorm_dt(const void* x, int64_t R, int64_t D, const float* g, float eps,
+                                    void* out, const Launch& L) {
+  NormParams p{x, g, eps, out, Geom{}};
+  const int V = (int)(D * T::kBytes / 16);
+  int vpl = 2;
+  if (64 * 4 * vpl < V) vpl = (V + 255) / 256;
+  p.geo = make_geom(R, D, T::kBytes, vpl, 4);
+  if (p.geo.W > 4 || vpl > 8) return hipErrorInvalidValue;
+  switch (vpl) {
+    case 1: return launch_norm_t<T, 1>(p, L);
+    case 2: return launch_norm_t<T, 2>(p, L);
+    case 3: return launch_norm_t<T, 3>(p, L);
+    case 4: return launch_norm_t<T, 4>(p, L);
+    case 5: return launch_norm_t<T, 5>(p, L);
+    case 6: return launch_norm_t<T, 6>(p, L);
+    case 7: return launch_norm_t<T, 7>(p, L);
+    default: return launch_norm_t<T, 8>(p, L);
+  }
+}
+
+hipError_t launch_rmsnorm(int dtype, const void* x, int64_t R, int64_t D, const float* g, float eps,
+                          void* out, const Launch& L) {
+  return dtype == 1 ? launch_rmsnorm_dt<Bf16>(x, R, D, g, eps, out, L)
+                    : launch_rmsnorm_dt<F32>(x, R, D, g, eps, out, L);
 }
 
 hipError_t launch_close(int dtype, const void* p, const void* v, void* b, int64_t R, int64_t D,

@@ -58,7 +58,10 @@ struct Phase2Args {
   const void* p_prev;
   const void* v_prev;
   void* p_out;
-  void* h_out;
+  void* h_out;      // may be null when hn_out is set
+  const float* gf;  // [D] or null: gain of the fused output norm
+  float eps_f;
+  void* hn_out;     // RMSNorm(h) * gf, or null
   int64_t R, D;
 };
 
@@ -67,6 +70,8 @@ hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L);
 bool phase1_supported(int dtype, int n, int S, int64_t D);
 hipError_t launch_aggregate(int dtype, const AggArgs& a, const Launch& L);
 hipError_t launch_phase2(int dtype, const Phase2Args& a, const Launch& L);
+hipError_t launch_rmsnorm(int dtype, const void* x, int64_t R, int64_t D, const float* g, float eps,
+                          void* out, const Launch& L);
 hipError_t launch_close(int dtype, const void* p, const void* v, void* b, int64_t R, int64_t D,
                         const Launch& L);
 

@@ -85,10 +85,12 @@ class DeviceStack:
         return binding.NativeSublayer(inputs.fn_ptr("attnres_inputs_record_sublayer"),
                                       ctypes.cast(ctypes.pointer(ctx), ctypes.c_void_p))
 
-    def forward(self, sublayer=None, stream=None):
+    def forward(self, sublayer=None, stream=None, norm=None):
+        """One stack forward; ``norm=(Gamma_f, eps_f)`` hands the sublayers
+        RMSNorm(h_l) * Gamma_f[l-1] instead of h_l."""
         return binding.attnres_block_stack_forward(
             self.x, self.W, self.wl.S, sublayer or self.sublayer, eps=EPS,
-            block_sums=self.block_sums, y=self.y, workspace=self.workspace, stream=stream)
+            block_sums=self.block_sums, y=self.y, workspace=self.workspace, stream=stream, norm=norm)
 
     def host_rows(self, rows: np.ndarray):
         """The generated inputs at token rows ``rows``, copied to the host:

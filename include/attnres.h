@@ -116,6 +116,33 @@ int attnres_phase2_merge(const void* o, const float* lse, const float* w, const 
                          void* h_out, int64_t R, int64_t D, int dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The input norm of the sublayer that consumes an aggregate. In the block
+ * listing of [ZZ] every sublayer applies its own RMSNorm to h first
+ * (attn(attn_norm(h)), mlp(mlp_norm(h))); [WC "Depth attention & online merge
+ * reference"] notes the reference operator's optional fused output RMSNorm.
+ * The norm is the same RMS form as the keys' [WC reference code], with the
+ * sublayer's own gain and eps:
+ *   hn[r][d] = round(gamma_f[d] * h_r[r][d] / sqrt(mean_d h_r[r][:]^2 + eps_f))
+ * where h_r is h rounded to dtype (exactly what the sublayer would receive).
+ *
+ * attnres_phase2_merge_norm: attnres_phase2_merge with the norm fused in.
+ *   gamma_f : [D] fp32, or NULL for ones
+ *   eps_f   : finite, >= 0
+ *   hn_out  : [R,D] dtype, required
+ *   h_out   : [R,D] dtype, or NULL (then h itself is not written)
+ *   Errors as attnres_phase2_merge, plus ATTNRES_EINVAL for a bad eps_f, or
+ *   h_out / hn_out aliasing an input, p_out or each other.
+ * attnres_rmsnorm: hn = RMSNorm(x) * gamma for one [R,D] tensor (x and out
+ *   may be the same buffer); gamma [D] fp32 or NULL for ones.
+ * ------------------------------------------------------------------------- */
+int attnres_phase2_merge_norm(const void* o, const float* lse, const float* w, const float* gamma,
+                              float eps, const void* p_prev, const void* v_prev, void* p_out,
+                              void* h_out, const float* gamma_f, float eps_f, void* hn_out,
+                              int64_t R, int64_t D, int dtype, void* stream);
+int attnres_rmsnorm(const void* x, int64_t R, int64_t D, int dtype, const float* gamma, float eps,
+                    void* out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Sublayer callback of the stack forward: eq. (A4) v_l = f_l(h_l) [K3 9.1].
  * Called on the calling thread with l = 1..L in order. h_l is a device [R,D]
  * dtype buffer inside the workspace, valid until the callback returns; the
@@ -166,6 +193,20 @@ int attnres_block_stack_forward(const void* x, int L, int S, int64_t R, int64_t 
                                 attnres_sublayer_fn f, void* f_ctx, void* const* block_sums,
                                 void* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* attnres_block_stack_forward whose sublayers receive their normalised input
+ * (see attnres_phase2_merge_norm): the callback for sublayer l gets
+ * hn_l = RMSNorm(h_l) * Gamma_f[l-1] in place of h_l, and h_l itself is not
+ * materialised (in Block AttnRes h_l feeds only its sublayer). Gamma_f
+ * [L, D] fp32 or NULL for ones; eps_f finite and >= 0. Workspace, ownership,
+ * limits and errors as attnres_block_stack_forward. The norm is fused into
+ * Phase 2; a block's first sublayer (h = Phase-1 output 0) and one-sublayer
+ * blocks take a separate RMSNorm pass. */
+int attnres_block_stack_forward_norm(const void* x, int L, int S, int64_t R, int64_t D, int dtype,
+                                     const float* W, const float* Gamma, float eps,
+                                     const float* Gamma_f, float eps_f, attnres_sublayer_fn f,
+                                     void* f_ctx, void* const* block_sums, void* y, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * attnres_block_layout -- the integer plan of forward_naive [K3 9.3 listing;
  * WC "Block AttnRes"]. block_start[k] (host, nb+1 entries or NULL) is the
@@ -195,10 +236,11 @@ const char* attnres_last_error(void);
  * record a HIP event pair around each kernel on its stream, for up to
  * `capacity` launches (0 disables and releases the events). The library keeps
  * per-kind totals: kind 0 Phase 1, 1 Phase 2, 2 aggregate, 3 block close,
- * 4 query fold. attnres_timing_read synchronises the recorded events and
- * returns, for `kind`, the number of timed launches, their summed duration in
- * milliseconds and their summed algorithmic bytes (inputs read once plus
- * outputs written once, queries excluded). attnres_timing_reset clears the
+ * 4 query fold, 5 standalone output norm. attnres_timing_read synchronises
+ * the recorded events and returns, for `kind`, the number of timed launches,
+ * their summed duration in milliseconds and their summed algorithmic bytes
+ * (inputs read once plus outputs written once, queries excluded).
+ * attnres_timing_reset clears the
  * totals and the recorded events. attnres_timing_pause(1) stops recording
  * (launches run untimed, with no event overhead) until attnres_timing_pause(0);
  * enabling does not change the paused state.

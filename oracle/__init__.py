@@ -89,12 +89,14 @@ class Oracle:
         L.oracle_atomic_block_size.argtypes = [I, I]
         L.oracle_block_stack.argtypes = [I64, I64, I, I, I, P, P, P, P, D,
                                          P, P, P, P, P, P, P, P, P, I]
+        L.oracle_rmsnorm.argtypes = [I64, I64, I, P, P, D, P, P, I]
         L.oracle_round.argtypes = [D, I]
         L.oracle_round.restype = D
         L.oracle_store_rounded.argtypes = [P, I64, I, P]
         L.oracle_store_rounded.restype = None
         for f in ("oracle_aggregate", "oracle_phase1", "oracle_phase2", "oracle_block_plan",
-                  "oracle_atomic_block_size", "oracle_block_stack", "oracle_max_sources"):
+                  "oracle_atomic_block_size", "oracle_block_stack", "oracle_rmsnorm",
+                  "oracle_max_sources"):
             getattr(L, f).restype = ctypes.c_int
         self.lib = L
         self.path = path
@@ -146,6 +148,18 @@ class Oracle:
                                     nthreads or default_threads())
         _check(rc, "oracle_phase2")
         return {"p": p_out, "h": h, "scale": sc}
+
+    def rmsnorm(self, x, gamma=None, eps=1e-6, nthreads=None):
+        """RMSNorm of the rows of ``x`` (fp32 or bf16 bit patterns): fp64 outputs and per-row rms."""
+        x = np.ascontiguousarray(x)
+        dt = _dtype_code(x)
+        rows, D = x.shape
+        gamma = _f32(gamma)
+        out = np.empty((rows, D)); rms = np.empty(rows)
+        rc = self.lib.oracle_rmsnorm(rows, D, dt, _ptr(x), _ptr(gamma), eps, _ptr(out), _ptr(rms),
+                                     nthreads or default_threads())
+        _check(rc, "oracle_rmsnorm")
+        return {"out": out, "rms": rms}
 
     def block_plan(self, L: int, S: int):
         """(nb, block_start[nb+1], n_sources[L+1]) of the naive Block forward."""
@@ -219,6 +233,10 @@ def phase1(*a, **k):
 
 def phase2(*a, **k):
     return default().phase2(*a, **k)
+
+
+def rmsnorm(*a, **k):
+    return default().rmsnorm(*a, **k)
 
 
 def block_plan(*a, **k):

@@ -24,6 +24,8 @@
  *        axis), "Block AttnRes" (the embedding stays its own source).
  *  [RH]  Reading notes on "Attention Residuals" (ranhao.site), 4.2 Inference:
  *        Phase 1 returns the outputs plus the max and log-sum-exp statistics.
+ *  [ZZ]  "Attention Residuals" notes (zhangzhe.space): the block listing, where
+ *        every sublayer applies its own RMSNorm to the aggregate it receives.
  *
  * Readings where the pages leave a step open (each is listed in the design doc):
  *  - RMS(v) = v / sqrt(mean_d(v^2) + eps)            [WC reference code]
@@ -459,6 +461,51 @@ int oracle_block_stack(int64_t rows, int64_t D, int dtype, int L, int S, const v
   int rc = run_rows(rows, nthreads, stack_rowfn, &c, (size_t)(nb + 4) * (size_t)D);
   free(q);
   return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* RMSNorm: the input norm of the sublayer that consumes an aggregate       */
+/* ------------------------------------------------------------------------ */
+
+/* out[r][d] = gamma[d] * x[r][d] / sqrt(mean_d x[r][:]^2 + eps), in fp64 on
+   the exactly widened input; rms[r] = sqrt(mean_d x[r][:]^2 + eps). The RMS
+   form is the keys' one [WC reference code: eps inside the root, mean over
+   the hidden axis]; each sublayer applies it to its input with its own gain
+   [ZZ block listing: attn(attn_norm(h)), mlp(mlp_norm(h))]. gamma NULL means
+   ones. */
+typedef struct {
+  int64_t D;
+  int dtype;
+  const void* x;
+  const float* gamma;
+  double eps;
+  double *out, *rms;
+} norm_ctx;
+
+static void norm_rowfn(void* pc, int64_t r, double* scratch) {
+  norm_ctx* c = (norm_ctx*)pc;
+  const int64_t D = c->D;
+  (void)scratch;
+  double ss = 0.0;
+  for (int64_t d = 0; d < D; ++d) {
+    const double v = widen(c->x, c->dtype, r * D + d);
+    ss += v * v;
+  }
+  const double rms = sqrt(ss / (double)D + c->eps);
+  for (int64_t d = 0; d < D; ++d) {
+    const double g = c->gamma ? (double)c->gamma[d] : 1.0;
+    c->out[r * D + d] = g * widen(c->x, c->dtype, r * D + d) / rms;
+  }
+  if (c->rms) c->rms[r] = rms;
+}
+
+int oracle_rmsnorm(int64_t rows, int64_t D, int dtype, const void* x, const float* gamma,
+                   double eps, double* out, double* rms, int nthreads) {
+  int rc = check_common(rows, D, dtype);
+  if (rc) return rc;
+  if (!x || !out || !(eps >= 0.0)) return ORACLE_EINVAL;
+  norm_ctx c = {D, dtype, x, gamma, eps, out, rms};
+  return run_rows(rows, nthreads, norm_rowfn, &c, 1);
 }
 
 int oracle_max_sources(void) { return ORACLE_MAX_SOURCES; }

@@ -482,4 +482,40 @@ def pin_causality(orc):
     assert not np.array_equal(base["y"][2], pert["y"][2])
 
 
+def pin_rmsnorm_library(orc):
+    """The sublayer input norm equals torch's rms_norm evaluated in float64
+    (same definition: eps inside the root, mean over the hidden axis, times
+    the gain), with and without a gain."""
+    import torch
+    rng = np.random.default_rng(31)
+    for D, eps in ((64, 1e-6), (256, 1e-8), (40, 0.25)):
+        x = (rng.standard_normal((7, D)) * rng.uniform(0.1, 5.0, (7, 1))).astype(np.float32)
+        g = rng.uniform(0.5, 1.5, D).astype(np.float32)
+        for gain in (g, None):
+            got = orc.rmsnorm(x, gain, eps=eps)["out"]
+            ref = torch.nn.functional.rms_norm(
+                torch.from_numpy(x.astype(np.float64)), (D,),
+                None if gain is None else torch.from_numpy(gain.astype(np.float64)), eps=eps).numpy()
+            np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-15)
+
+
+def pin_rmsnorm_closed_forms(orc):
+    """A constant row c gives gamma * c / sqrt(c^2 + eps) in every element; with
+    eps = 0 and unit gain every row has mean square exactly 1 (up to fp64
+    rounding) and rescaling a row by a power of two leaves it unchanged."""
+    for c, eps in ((3.0, 1e-6), (-0.5, 0.25), (2.0 ** -10, 1e-8)):
+        x = np.full((2, 32), c, dtype=np.float32)
+        g = np.linspace(0.5, 1.5, 32).astype(np.float32)
+        out = orc.rmsnorm(x, g, eps=eps)
+        want = g.astype(np.float64) * c / np.sqrt(c * c + eps)
+        np.testing.assert_allclose(out["out"], np.broadcast_to(want, (2, 32)), rtol=1e-14)
+        np.testing.assert_allclose(out["rms"], np.sqrt(c * c + eps), rtol=1e-14)
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((5, 48)).astype(np.float32)
+    out = orc.rmsnorm(x, None, eps=0.0)["out"]
+    np.testing.assert_allclose((out ** 2).mean(axis=1), 1.0, rtol=1e-13)
+    out4 = orc.rmsnorm((x * np.float32(4.0)).astype(np.float32), None, eps=0.0)["out"]
+    assert np.array_equal(out, out4)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -1,0 +1,149 @@
+"""GPU parity of the sublayer input norm: attnres_rmsnorm, the norm fused into
+the Phase-2 merge, and the stack forward that hands each sublayer
+RMSNorm(h_l) * Gamma_f[l-1] (attnres_block_stack_forward_norm).
+
+References come from the oracle alone: its own aggregate h, rounded to the
+I/O dtype by the oracle, then its fp64 RMSNorm. The GPU normalises its own
+rounded h, which may sit one rounding step away from the oracle's, so the
+norm's scaled error uses scale |gamma_f[d]| * (scale_h[d] + |h[d]|) / rms(h):
+an error of e * scale_h in h, a relative error d in the row's rms and the
+final rounding (2^-9 |hn| for bf16) stay below max(e, d + 2^-9) of it.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from depth_wise_attention_rms_amd import binding as b
+from depth_wise_attention_rms_amd import inputs
+from depth_wise_attention_rms_amd.workload import EPS, DeviceStack
+from tests.parity import assert_close_scaled, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    b.lib()
+    inputs.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def norm_reference(h, scale_h, dtype, gamma_f, eps_f):
+    """(hn_ref, scale_hn) for an aggregate h computed by the oracle."""
+    h_r = oracle.round_to(h, dtype)
+    nr = oracle.rmsnorm(h_r, gamma_f, eps=eps_f)
+    g = np.ones(h.shape[-1]) if gamma_f is None else np.abs(gamma_f.astype(np.float64))
+    scale = g[None, :] * (scale_h + np.abs(h)) / nr["rms"][:, None]
+    return nr["out"], scale
+
+
+NORM_CASES = [
+    # (R, D, dtype, gain, eps, inplace)
+    (37, 4096, "bf16", True, 1e-6, False), (130, 1000, "bf16", False, 1e-8, True),
+    (5, 7168, "bf16", True, 0.25, False), (1, 8, "bf16", True, 1e-6, False),
+    (3, 16384, "bf16", True, 1e-6, True), (65, 4096, "f32", True, 1e-6, True),
+    (9, 1028, "f32", False, 0.0, False),
+]
+
+
+@pytest.mark.parametrize("R,D,dtype,gain,eps_f,inplace", NORM_CASES)
+def test_rmsnorm_matches_oracle(R, D, dtype, gain, eps_f, inplace):
+    announce(f"rmsnorm R={R} D={D} {dtype} gain={gain} eps={eps_f} inplace={inplace}")
+    x = inputs.tensor_rows(41, inputs.ROLE_AUX, 5, np.arange(R), D, 2.5, dtype)
+    g = inputs.gains(41, D) if gain else None
+    xd = to_device(x)
+    out = b.attnres_rmsnorm(xd, None if g is None else torch.from_numpy(g).cuda(), eps=eps_f,
+                            out=xd if inplace else None)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm(x, g, eps=eps_f)["out"]
+    assert_close_scaled(to_host(out), ref, np.abs(ref), dtype, "rmsnorm")
+
+
+def test_rmsnorm_zero_rows_and_validation():
+    announce("rmsnorm edge cases")
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    out = b.attnres_rmsnorm(x, eps=1e-6)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0, "a zero row normalises to zeros"
+    b.attnres_rmsnorm(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), eps=1e-6)
+    with pytest.raises(b.AttnResError):
+        b.attnres_rmsnorm(x, eps=-1.0)
+
+
+PH2N_CASES = [
+    # (R, D, dtype, has_prev, want_h)
+    (65, 4096, "bf16", True, False), (65, 4096, "bf16", False, True), (37, 7168, "bf16", True, True),
+    (130, 1000, "bf16", True, False), (1, 8, "bf16", False, False), (65, 4096, "f32", True, True),
+]
+
+
+@pytest.mark.parametrize("R,D,dtype,has_prev,want_h", PH2N_CASES)
+def test_phase2_merge_norm(R, D, dtype, has_prev, want_h):
+    announce(f"phase2 norm R={R} D={D} {dtype} prev={has_prev} want_h={want_h}")
+    o = inputs.tensor_rows(51, inputs.ROLE_AUX, 1, np.arange(R), D, 1.0, dtype)
+    v = inputs.tensor_rows(51, inputs.ROLE_AUX, 2, np.arange(R), D, 3.0, dtype)
+    p = inputs.tensor_rows(51, inputs.ROLE_AUX, 3, np.arange(R), D, 2.0, dtype) if has_prev else None
+    lse = (2.0 * inputs.normal(51, inputs.ROLE_AUX, 4, np.arange(R))).astype(np.float32)
+    w = inputs.queries(51, 1, D, sigma=0.3 / math.sqrt(D / 64))[0]
+    gf = inputs.gains(52, D)
+    eps_f = 1e-6
+    hn, h, p_res = b.attnres_phase2_merge_norm(
+        to_device(o), torch.from_numpy(lse).cuda(), torch.from_numpy(w).cuda(), to_device(v),
+        gamma_f=torch.from_numpy(gf).cuda(), eps_f=eps_f,
+        p_prev=None if p is None else to_device(p), eps=EPS, want_h=want_h)
+    torch.cuda.synchronize()
+    ref = oracle.phase2(o, lse, w, p, v, None, eps=EPS)
+    hn_ref, scale = norm_reference(ref["h"], ref["scale"], dtype, gf, eps_f)
+    assert_close_scaled(to_host(hn), hn_ref, scale, dtype, "phase2 hn")
+    if want_h:
+        assert_close_scaled(to_host(h), ref["h"], ref["scale"], dtype, "phase2 h")
+    if has_prev:
+        assert np.array_equal(to_host(p_res), ref["p"]), "partial p must be bit-exact"
+
+
+STACK_NORM = [
+    # Block with the matrix-core Phase 1, several rows per workgroup
+    inputs.Workload("norm_block", "stack", B=2, T=150, D=1024, dtype="bf16", L=12, S=4, seed=3),
+    # Full AttnRes (S = 1): every sublayer's h is an aggregate normalised in place
+    inputs.Workload("norm_full", "stack", B=1, T=64, D=256, dtype="bf16", L=6, S=1, seed=4),
+    # S > 8: the vector-ALU Phase 1, and a short last block
+    inputs.Workload("norm_wide", "stack", B=4, T=10, D=512, dtype="bf16", L=14, S=12, seed=5),
+    inputs.Workload("norm_f32", "stack", B=1, T=5, D=64, dtype="f32", L=7, S=3, seed=6),
+]
+
+
+@pytest.mark.parametrize("wl", STACK_NORM, ids=[w.name for w in STACK_NORM])
+def test_stack_forward_norm(wl):
+    """Every sublayer receives RMSNorm(h_l) * Gamma_f[l-1]; y and the block sums
+    are bit-identical to the forward without the norm."""
+    announce(wl.name)
+    ds = DeviceStack(wl)
+    Gf = np.stack([inputs.gains(wl.seed + 100, wl.D, layer=l) for l in range(wl.L)]).astype(np.float32)
+    eps_f = 1e-6
+    ds.forward()
+    torch.cuda.synchronize()
+    y_plain = to_host(ds.y)
+    bs_plain = None if ds.block_sums is None else [to_host(t) for t in ds.block_sums]
+    rows = np.arange(wl.R)
+    ds.forward(ds.recorder(rows), norm=(torch.from_numpy(Gf).cuda(), eps_f))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(ds.y), y_plain), "the norm must not change y"
+    if bs_plain is not None:
+        for k, t in enumerate(ds.block_sums):
+            assert np.array_equal(to_host(t), bs_plain[k]), f"the norm must not change b_{k + 1}"
+    rec = to_host(ds.rec)
+    xr, vr = ds.host_rows(rows)
+    ref = oracle.block_stack(xr, vr, ds.W_host, wl.S, eps=EPS)
+    for l in range(wl.L):
+        hn_ref, scale = norm_reference(ref["h"][l], ref["h_scale"][l], wl.dtype, Gf[l], eps_f)
+        assert_close_scaled(rec[l], hn_ref, scale, wl.dtype, f"{wl.name} hn_{l + 1}")

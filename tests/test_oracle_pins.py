@@ -30,6 +30,13 @@ def test_pin(orc, pin):
 
 # (name, exact text in oracle.c, replacement)
 MUTANTS = [
+    ("norm_sum_not_mean", "const double rms = sqrt(ss / (double)D + c->eps);",
+     "const double rms = sqrt(ss + c->eps);"),
+    ("norm_eps_outside_root", "const double rms = sqrt(ss / (double)D + c->eps);",
+     "const double rms = sqrt(ss / (double)D) + c->eps;"),
+    ("norm_gain_dropped", "const double g = c->gamma ? (double)c->gamma[d] : 1.0;", "const double g = 1.0;"),
+    ("norm_multiplies_by_rms", "c->out[r * D + d] = g * widen(c->x, c->dtype, r * D + d) / rms;",
+     "c->out[r * D + d] = g * widen(c->x, c->dtype, r * D + d) * rms;"),
     ("rms_sum_not_mean", "sqrt(ss / (double)D + eps)", "sqrt(ss + eps)"),
     ("eps_outside_root", "sqrt(ss / (double)D + eps)", "(sqrt(ss / (double)D) + eps)"),
     ("softmax_sign", "a[i] = exp(s[i] - m);", "a[i] = exp(m - s[i]);"),
