@@ -156,6 +156,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU work of the oracle baseline (whole row chunks until this much has run)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one forward into a HIP graph and time its replays (the decode regime is "
+                         "launch-bound); kernel durations then come from an eager pass before the timed region")
     ap.add_argument("--output-norm", action="store_true",
                     help="hand every sublayer RMSNorm(h_l) * gamma_l (fused into Phase 2) instead of h_l")
     ap.add_argument("--calibration-copy-gib", type=float, default=0.0,
@@ -209,6 +212,19 @@ def main() -> int:
         ds.forward(norm=norm)
     torch.cuda.synchronize()
 
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            ds.forward(stream=side, norm=norm)  # warm-up on the capture stream
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            ds.forward(stream=torch.cuda.current_stream(), norm=norm)
+        torch.cuda.synchronize()
+
     # Kernel durations come from HIP events that each timed kernel's own
     # dispatch stamps on its stream (hipExtLaunchKernelGGL). Recording them
     # costs a few microseconds per launch, so only TIMED_STEPS evenly spaced
@@ -220,12 +236,22 @@ def main() -> int:
     binding.attnres_timing_enable(len(instrumented) * launches_per_step + 16)
     binding.attnres_timing_pause(True)
     binding.attnres_timing_reset()
+    n_timed = len(instrumented)
+    if graph is not None:  # kernel events cannot be recorded inside a replay
+        binding.attnres_timing_pause(False)
+        for _ in range(n_timed):
+            ds.forward(norm=norm)
+        binding.attnres_timing_pause(True)
+        torch.cuda.synchronize()
+        instrumented = []
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
-        if i in instrumented:
+        if graph is not None:
+            graph.replay()
+        elif i in instrumented:
             binding.attnres_timing_pause(False)
             ds.forward(norm=norm)
             binding.attnres_timing_pause(True)
@@ -240,9 +266,9 @@ def main() -> int:
     for k in ("phase1", "phase2", "aggregate", "close", "fold", "norm"):
         n, ms, byts = binding.attnres_timing_read(k)
         if n:
-            n_step = n / len(instrumented)
+            n_step = n / n_timed
             kinds[k] = {"launches_per_step": n_step, "avg_us": 1e3 * ms / n,
-                        "ms_per_step": ms / len(instrumented),
+                        "ms_per_step": ms / n_timed,
                         "bytes_per_launch": byts / n, "GBps": byts / (ms * 1e6)}
     binding.attnres_timing_enable(0)
 
@@ -257,7 +283,8 @@ def main() -> int:
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom["GBps"] / PEAK_HBM_GBPS, 4),
                 "traffic": traffic, "bytes_per_launch": dom["bytes_per_launch"],
                 "avg_launch_us": round(dom["avg_us"], 2),
-                "timed_launches": int(round(dom["launches_per_step"] * len(instrumented)))}
+                "timed_launches": int(round(dom["launches_per_step"] * n_timed)),
+                "timed_in": "eager pass before the graph replays" if graph is not None else "timed region"}
 
     cpu = cpu_baseline(ds, wl, args.cpu_seconds) if args.cpu_rows > 0 else None
 
@@ -277,7 +304,7 @@ def main() -> int:
         "data": "synthetic (seeded counter-based normals; inputs resident in HBM)",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "D": wl.D, "L": wl.L, "S": wl.S,
                    "blocks": nb, "global_batch": wl.B, "seq_len": wl.T, "parallelism": "single GPU",
-                   "output_norm": bool(norm)},
+                   "output_norm": bool(norm), "hip_graph": graph is not None},
         "achieved_GBps": round(fwd_gbps, 1),
         "hbm_frac": round(fwd_gbps / PEAK_HBM_GBPS, 4),
         "bytes_per_step": fwd_bytes,
