@@ -159,6 +159,9 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true",
                     help="capture one forward into a HIP graph and time its replays (the decode regime is "
                          "launch-bound); kernel durations then come from an eager pass before the timed region")
+    ap.add_argument("--full-schedule", type=int, default=0, metavar="C",
+                    help="run a Full (S = 1) workload with the two-phase schedule of block size C "
+                         "(attnres_full_stack_forward; C = 1 is the naive schedule)")
     ap.add_argument("--output-norm", action="store_true",
                     help="hand every sublayer RMSNorm(h_l) * gamma_l (fused into Phase 2) instead of h_l")
     ap.add_argument("--calibration-copy-gib", type=float, default=0.0,
@@ -198,6 +201,19 @@ def main() -> int:
         Gf = np.stack([inputs.gains(wl.seed + 100, wl.D, layer=l) for l in range(wl.L)])
         norm = (torch.from_numpy(Gf.astype(np.float32)).cuda(), 1e-6)
     stream = torch.cuda.current_stream()
+    if args.full_schedule:
+        assert wl.S == 1 and not norm, "--full-schedule runs a Full (S = 1) workload without the norm"
+        from depth_wise_attention_rms_amd.workload import EPS
+        fws = torch.empty(max(binding.attnres_full_workspace_bytes(wl.L, args.full_schedule, wl.R, wl.D,
+                                                                   ds.dt), 256),
+                          dtype=torch.uint8, device="cuda")
+
+        def forward(stream=None):
+            binding.attnres_full_stack_forward(ds.x, ds.W, args.full_schedule, ds.sublayer, eps=EPS,
+                                               y=ds.y, workspace=fws, stream=stream)
+    else:
+        def forward(stream=None):
+            ds.forward(stream=stream, norm=norm)
 
     if args.calibration_copy_gib > 0:
         n = int(args.calibration_copy_gib * (1 << 30)) // 2
@@ -209,7 +225,7 @@ def main() -> int:
         del src, dst
 
     for _ in range(args.warmup):
-        ds.forward(norm=norm)
+        forward()
     torch.cuda.synchronize()
 
     graph = None
@@ -217,12 +233,12 @@ def main() -> int:
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
-            ds.forward(stream=side, norm=norm)  # warm-up on the capture stream
+            forward(stream=side)  # warm-up on the capture stream
         stream.wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            ds.forward(stream=torch.cuda.current_stream(), norm=norm)
+            forward(stream=torch.cuda.current_stream())
         torch.cuda.synchronize()
 
     # Kernel durations come from HIP events that each timed kernel's own
@@ -230,7 +246,7 @@ def main() -> int:
     # costs a few microseconds per launch, so only TIMED_STEPS evenly spaced
     # steps of the timed region record every one of their launches; the
     # others run uninstrumented.
-    launches_per_step = 1 + wl.L + 2 * nb + 1 + (nb if norm else 0)
+    launches_per_step = 2 * wl.L + 2 * nb + 8
     stride = max(1, args.steps // TIMED_STEPS)
     instrumented = [i for i in range(args.steps) if i % stride == stride // 2][:TIMED_STEPS]
     binding.attnres_timing_enable(len(instrumented) * launches_per_step + 16)
@@ -240,7 +256,7 @@ def main() -> int:
     if graph is not None:  # kernel events cannot be recorded inside a replay
         binding.attnres_timing_pause(False)
         for _ in range(n_timed):
-            ds.forward(norm=norm)
+            forward()
         binding.attnres_timing_pause(True)
         torch.cuda.synchronize()
         instrumented = []
@@ -253,10 +269,10 @@ def main() -> int:
             graph.replay()
         elif i in instrumented:
             binding.attnres_timing_pause(False)
-            ds.forward(norm=norm)
+            forward()
             binding.attnres_timing_pause(True)
         else:
-            ds.forward(norm=norm)
+            forward()
     ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -277,9 +293,13 @@ def main() -> int:
     tokens_per_s = wl.R / (ms_per_step / 1e3)
     fwd_gbps = fwd_bytes / (ms_per_step * 1e6)
 
-    dom = kinds["phase2"]
-    traffic = measured_traffic(wl.name)
-    roofline = {"bound": "hbm", "kernel": "phase2_kernel", "achieved": round(dom["GBps"], 1),
+    # the dominant kernel: Phase 2 in a Block stack, else the kind with the most time per step
+    dom_kind = "phase2" if "phase2" in kinds else max(kinds, key=lambda k: kinds[k]["ms_per_step"])
+    dom = kinds[dom_kind]
+    dom_name = {"phase1": "phase1_mfma_kernel", "phase2": "phase2_kernel", "aggregate": "aggregate_kernel",
+                "norm": "rmsnorm_kernel", "close": "close_kernel", "fold": "fold_kernel"}[dom_kind]
+    traffic = measured_traffic(wl.name) if dom_kind == "phase2" and not norm else None
+    roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(dom["GBps"], 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom["GBps"] / PEAK_HBM_GBPS, 4),
                 "traffic": traffic, "bytes_per_launch": dom["bytes_per_launch"],
                 "avg_launch_us": round(dom["avg_us"], 2),
@@ -304,7 +324,8 @@ def main() -> int:
         "data": "synthetic (seeded counter-based normals; inputs resident in HBM)",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "D": wl.D, "L": wl.L, "S": wl.S,
                    "blocks": nb, "global_batch": wl.B, "seq_len": wl.T, "parallelism": "single GPU",
-                   "output_norm": bool(norm), "hip_graph": graph is not None},
+                   "output_norm": bool(norm), "hip_graph": graph is not None,
+                   "full_schedule": args.full_schedule or None},
         "achieved_GBps": round(fwd_gbps, 1),
         "hbm_frac": round(fwd_gbps / PEAK_HBM_GBPS, 4),
         "bytes_per_step": fwd_bytes,

@@ -28,7 +28,8 @@ EXPORTS = (
     "attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge",
     "attnres_phase2_merge_norm", "attnres_rmsnorm", "attnres_table_sublayer",
     "attnres_stack_workspace_bytes", "attnres_block_stack_forward",
-    "attnres_block_stack_forward_norm", "attnres_block_layout",
+    "attnres_block_stack_forward_norm", "attnres_merge_sources", "attnres_full_workspace_bytes",
+    "attnres_full_stack_forward", "attnres_block_layout",
     "attnres_atomic_block_size", "attnres_status_string", "attnres_last_error",
     "attnres_timing_enable", "attnres_timing_pause", "attnres_timing_reset", "attnres_timing_read",
 )
@@ -68,6 +69,10 @@ def lib():
         L.attnres_block_stack_forward.argtypes = [P, I, I, I64, I64, I, P, P, F, P, P, P, P, P, SZ, P]
         L.attnres_block_stack_forward_norm.argtypes = [P, I, I, I64, I64, I, P, P, F, P, F, P, P, P, P,
                                                        P, SZ, P]
+        L.attnres_merge_sources.argtypes = [P, P, P, I, I64, I64, I, P, P, F, P, P, P, P]
+        L.attnres_full_workspace_bytes.argtypes = [I, I, I64, I64, I]
+        L.attnres_full_workspace_bytes.restype = SZ
+        L.attnres_full_stack_forward.argtypes = [P, I, I, I64, I64, I, P, P, F, P, P, P, P, SZ, P]
         L.attnres_block_layout.argtypes = [I, I, P, P]
         L.attnres_atomic_block_size.argtypes = [I, I]
         L.attnres_status_string.argtypes = [I]
@@ -80,6 +85,7 @@ def lib():
         L.attnres_timing_read.argtypes = [I, ctypes.POINTER(I64), ctypes.POINTER(D), ctypes.POINTER(D)]
         for f in ("attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge",
                   "attnres_phase2_merge_norm", "attnres_rmsnorm", "attnres_block_stack_forward_norm",
+                  "attnres_merge_sources", "attnres_full_stack_forward",
                   "attnres_table_sublayer", "attnres_block_stack_forward", "attnres_block_layout",
                   "attnres_atomic_block_size", "attnres_timing_enable", "attnres_timing_pause",
                   "attnres_timing_reset", "attnres_timing_read"):
@@ -230,6 +236,33 @@ class NativeSublayer:
 Sublayer = Union[Sequence[torch.Tensor], NativeSublayer, Callable[[int, int], torch.Tensor]]
 
 
+def _sublayer_fn(sublayer: Sublayer):
+    """(function pointer, context, objects to keep alive) of a sublayer argument."""
+    keep = []
+    if isinstance(sublayer, NativeSublayer):
+        return ctypes.c_void_p(sublayer.fn_ptr), sublayer.ctx, keep
+    if isinstance(sublayer, (list, tuple)):
+        table = _ptr_array(sublayer)
+        keep.append(table)
+        return (ctypes.cast(lib().attnres_table_sublayer, ctypes.c_void_p),
+                ctypes.cast(table, ctypes.c_void_p), keep)
+    if callable(sublayer):
+        outs = []
+
+        def tramp(_ctx, l, h, v_out, _stream):
+            try:
+                v = sublayer(l, h)
+                outs.append(v)
+                v_out[0] = v.data_ptr()
+                return 0
+            except Exception:  # noqa: BLE001 -- reported to the library as a callback failure
+                return 1
+        cfn = SUBLAYER_FN(tramp)
+        keep += [cfn, outs]
+        return ctypes.cast(cfn, ctypes.c_void_p), None, keep
+    raise TypeError("sublayer must be a tensor list, a NativeSublayer or a callable")
+
+
 def attnres_block_stack_forward(x: torch.Tensor, W: torch.Tensor, S: int, sublayer: Sublayer,
                                 Gamma=None, eps=1e-8, block_sums=None, y=None, workspace=None,
                                 stream=None, norm=None):
@@ -250,32 +283,7 @@ def attnres_block_stack_forward(x: torch.Tensor, W: torch.Tensor, S: int, sublay
     need = attnres_stack_workspace_bytes(L, S, R, D, x.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    keep = []
-    if isinstance(sublayer, NativeSublayer):
-        fn = ctypes.c_void_p(sublayer.fn_ptr)
-        ctx = sublayer.ctx
-    elif isinstance(sublayer, (list, tuple)):
-        table = _ptr_array(sublayer)
-        keep.append(table)
-        fn = ctypes.cast(lib().attnres_table_sublayer, ctypes.c_void_p)
-        ctx = ctypes.cast(table, ctypes.c_void_p)
-    elif callable(sublayer):
-        outs = []
-
-        def tramp(_ctx, l, h, v_out, _stream):
-            try:
-                v = sublayer(l, h)
-                outs.append(v)
-                v_out[0] = v.data_ptr()
-                return 0
-            except Exception:  # noqa: BLE001 -- reported to the library as a callback failure
-                return 1
-        cfn = SUBLAYER_FN(tramp)
-        keep += [cfn, outs]
-        fn = ctypes.cast(cfn, ctypes.c_void_p)
-        ctx = None
-    else:
-        raise TypeError("sublayer must be a tensor list, a NativeSublayer or a callable")
+    fn, ctx, keep = _sublayer_fn(sublayer)
     bs = _ptr_array(block_sums) if block_sums is not None else None
     if norm is None:
         _check("attnres_block_stack_forward", lib().attnres_block_stack_forward(
@@ -287,6 +295,41 @@ def attnres_block_stack_forward(x: torch.Tensor, W: torch.Tensor, S: int, sublay
             _ptr(x), L, S, R, D, dt, _ptr(W), _ptr(Gamma), eps, _ptr(Gamma_f), eps_f, fn, ctx, bs,
             _ptr(y), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
     return y, block_sums
+
+
+def attnres_merge_sources(o, lse, sources, w, gamma=None, eps=1e-8, out=None, m_out=None, lse_out=None,
+                          stream=None):
+    """Merge a normalised group (o, lse) with more sources; returns (out, m_out, lse_out)."""
+    R, D = _rows(o)
+    if out is None:
+        out = torch.empty_like(o)
+    table = _ptr_array(sources)
+    _check("attnres_merge_sources", lib().attnres_merge_sources(
+        _ptr(o), _ptr(lse), table, len(sources), R, D, dtype_code(o.dtype), _ptr(w), _ptr(gamma), eps,
+        _ptr(out), _ptr(m_out), _ptr(lse_out), _stream(stream)))
+    return out, m_out, lse_out
+
+
+def attnres_full_workspace_bytes(L: int, C: int, R: int, D: int, dtype: torch.dtype) -> int:
+    return int(lib().attnres_full_workspace_bytes(L, C, R, D, dtype_code(dtype)))
+
+
+def attnres_full_stack_forward(x: torch.Tensor, W: torch.Tensor, C: int, sublayer: Sublayer, Gamma=None,
+                               eps=1e-8, y=None, workspace=None, stream=None):
+    """Full AttnRes stack forward with schedule block size C (C = 1: naive). Returns y."""
+    R, D = _rows(x)
+    L = W.shape[0] - 1
+    if y is None:
+        y = torch.empty_like(x)
+    need = attnres_full_workspace_bytes(L, C, R, D, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    fn, ctx, keep = _sublayer_fn(sublayer)
+    _check("attnres_full_stack_forward", lib().attnres_full_stack_forward(
+        _ptr(x), L, C, R, D, dtype_code(x.dtype), _ptr(W), _ptr(Gamma), eps, fn, ctx, _ptr(y),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
+    del keep
+    return y
 
 
 def attnres_timing_enable(capacity: int):

@@ -126,7 +126,8 @@ int do_aggregate(const char* fn, int dtype, const AggArgs& a, hipStream_t st) {
   if (a.R == 0) return ATTNRES_OK;
   const double rb = (double)a.R * a.D * esize_of(dtype);
   const double bytes = rb * (a.n + 1) + (double)a.R * ((a.m_out ? 4 : 0) + (a.lse_out ? 4 : 0)) +
-                       close_bytes(rb, a.close_p, a.close_v);
+                       close_bytes(rb, a.close_p, a.close_v) +
+                       (a.o_init ? rb + (double)a.R * 4 : 0.0);
   hipError_t e = attnres::launch_aggregate(dtype, a, timed_launch(K_AGG, bytes, st));
   return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
 }
@@ -563,7 +564,150 @@ int stack_forward(const char* fn, const void* x, int L, int S, int64_t R, int64_
   return ok();
 }
 
+// Full AttnRes with a two-phase schedule [K3 9.4: with schedule_block_size
+// the Full mixer runs the two-phase algorithm and matches the naive one]:
+// sublayers are taken in chunks of C; Phase 1 scores a chunk's queries over
+// every source that exists before the chunk in one pass, and sublayer j of
+// the chunk merges that summary with the j outputs produced inside the
+// chunk so far, each its own softmax term (OS2 over individual sources).
+struct FullLayout {
+  size_t q, o, m, lse, h, total;
+};
+
+FullLayout full_layout(int L, int C, int64_t R, int64_t D, int es) {
+  FullLayout f;
+  const int Ck = C < L ? C : L;
+  const size_t row = (size_t)R * (size_t)D * es;
+  size_t off = 0;
+  f.q = off; off = align256(off + (size_t)(L + 1) * D * sizeof(float));
+  f.o = off; off = align256(off + (Ck > 1 ? (size_t)Ck * row : 0));
+  f.m = off; off = align256(off + (size_t)Ck * R * sizeof(float));
+  f.lse = off; off = align256(off + (size_t)Ck * R * sizeof(float));
+  f.h = off; off = align256(off + row);
+  f.total = off;
+  return f;
+}
+
 }  // namespace
+
+ATTNRES_API size_t attnres_full_workspace_bytes(int L, int C, int64_t R, int64_t D, int dtype) {
+  const int es = esize_of(dtype);
+  if (!es || L < 1 || C < 1 || R < 0 || D < 1) return 0;
+  return full_layout(L, C, R, D, es).total;
+}
+
+ATTNRES_API int attnres_merge_sources(const void* o, const float* lse, const void* const* sources,
+                                      int n, int64_t R, int64_t D, int dtype, const float* w,
+                                      const float* gamma, float eps, void* out, float* m_out,
+                                      float* lse_out, void* stream) {
+  const char* fn = "attnres_merge_sources";
+  TRY(check_shape(fn, R, D, dtype, eps));
+  if (n < 1 || n > ATTNRES_MAX_SOURCES)
+    return fail(ATTNRES_EINVAL, "%s: n = %d outside [1, %d]", fn, n, ATTNRES_MAX_SOURCES);
+  if (!sources) return fail(ATTNRES_EINVAL, "%s: sources is NULL", fn);
+  if (R == 0) return ok();
+  TRY(check_ptr(fn, "o", o, true));
+  TRY(check_ptr(fn, "lse", lse, true));
+  for (int i = 0; i < n; ++i) TRY(check_ptr(fn, "sources[i]", sources[i], true));
+  TRY(check_ptr(fn, "w", w, true));
+  TRY(check_ptr(fn, "gamma", gamma, false));
+  TRY(check_ptr(fn, "out", out, true));
+  TRY(check_ptr(fn, "m_out", m_out, false));
+  TRY(check_ptr(fn, "lse_out", lse_out, false));
+  if (out == o) return fail(ATTNRES_EINVAL, "%s: out aliases o", fn);
+  for (int i = 0; i < n; ++i)
+    if (out == sources[i]) return fail(ATTNRES_EINVAL, "%s: out aliases a source", fn);
+  AggArgs a{sources, n, R, D, w, gamma, eps, out, m_out, lse_out, nullptr, nullptr, nullptr, o, lse};
+  TRY(do_aggregate(fn, dtype, a, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+ATTNRES_API int attnres_full_stack_forward(const void* x, int L, int C, int64_t R, int64_t D,
+                                           int dtype, const float* W, const float* Gamma, float eps,
+                                           attnres_sublayer_fn f, void* f_ctx, void* y,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "attnres_full_stack_forward";
+  TRY(check_shape(fn, R, D, dtype, eps));
+  if (L < 1 || C < 1) return fail(ATTNRES_EINVAL, "%s: L = %d and C = %d must be >= 1", fn, L, C);
+  if (L + 1 > ATTNRES_MAX_SOURCES)
+    return fail(ATTNRES_EINVAL, "%s: L + 1 = %d sources exceed %d", fn, L + 1, ATTNRES_MAX_SOURCES);
+  if (R == 0) return ok();
+  TRY(check_ptr(fn, "x", x, true));
+  TRY(check_ptr(fn, "W", W, true));
+  TRY(check_ptr(fn, "Gamma", Gamma, false));
+  TRY(check_ptr(fn, "y", y, true));
+  if (!f) return fail(ATTNRES_EINVAL, "%s: sublayer callback is NULL", fn);
+  const int es = esize_of(dtype);
+  const FullLayout lay = full_layout(L, C, R, D, es);
+  if (!workspace) return fail(ATTNRES_EINVAL, "%s: workspace is NULL", fn);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(ATTNRES_EINVAL, "%s: workspace is not 256-byte aligned", fn);
+  if (workspace_bytes < lay.total)
+    return fail(ATTNRES_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes,
+                lay.total);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* Q = reinterpret_cast<float*>(ws + lay.q);
+  char* O = ws + lay.o;
+  float* M = reinterpret_cast<float*>(ws + lay.m);
+  float* LSE = reinterpret_cast<float*>(ws + lay.lse);
+  void* H = ws + lay.h;
+  const int64_t tensor_bytes = R * D * es;
+  {
+    hipError_t e = attnres::launch_fold(
+        W, Gamma, Q, (int64_t)(L + 1) * D,
+        timed_launch(K_FOLD, (double)(L + 1) * D * (Gamma ? 12 : 8), st));
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
+  auto call = [&](int l, const void* h, const void** v) -> int {
+    const void* out = nullptr;
+    const int rc = f(f_ctx, l, h, &out, stream);
+    if (rc != 0)
+      return fail(ATTNRES_ECALLBACK, "%s: sublayer callback returned %d at l = %d", fn, rc, l);
+    if (!out || !aligned16(out))
+      return fail(ATTNRES_ECALLBACK, "%s: callback gave a NULL or misaligned v at l = %d", fn, l);
+    *v = out;
+    return ATTNRES_OK;
+  };
+
+  // src = [x, v_1, ..., v_{l-1}]: every sublayer output is a source of its own
+  std::vector<const void*> src;
+  src.reserve(L + 1);
+  src.push_back(x);
+  for (int s0 = 1; s0 <= L; s0 += C) {
+    const int e0 = s0 + C - 1 < L ? s0 + C - 1 : L;
+    const int Ck = e0 - s0 + 1;
+    const int n = (int)src.size();  // = s0
+    const float* Qk = Q + (int64_t)(s0 - 1) * D;
+    if (Ck == 1) {
+      AggArgs a{src.data(), n, R, D, Qk, nullptr, eps, H, nullptr, nullptr, nullptr, nullptr, nullptr};
+      TRY(do_aggregate(fn, dtype, a, st));
+      const void* v = nullptr;
+      TRY(call(s0, H, &v));
+      src.push_back(v);
+      continue;
+    }
+    Phase1Args a1{src.data(), n, R, D, Qk, nullptr, Ck, eps, O, M, LSE, nullptr, nullptr, nullptr};
+    TRY(do_phase1(fn, dtype, a1, st));
+    const void* v = nullptr;
+    TRY(call(s0, O, &v));  // the first sublayer of the chunk: h = o_0
+    src.push_back(v);
+    for (int j = 1; j < Ck; ++j) {
+      const int l = s0 + j;
+      // merge (lse_j, o_j) with the chunk's outputs v_{s0} .. v_{l-1}
+      AggArgs am{src.data() + n, j, R, D, Q + (int64_t)(l - 1) * D, nullptr, eps, H, nullptr, nullptr,
+                 nullptr, nullptr, nullptr, O + (int64_t)j * tensor_bytes, LSE + (int64_t)j * R};
+      TRY(do_aggregate(fn, dtype, am, st));
+      TRY(call(l, H, &v));
+      src.push_back(v);
+    }
+  }
+  AggArgs af{src.data(), L + 1, R, D, Q + (int64_t)L * D, nullptr, eps, y, nullptr, nullptr,
+             nullptr, nullptr, nullptr};
+  TRY(do_aggregate(fn, dtype, af, st));
+  return ok();
+}
 
 #ifndef ATTNRES_TIMING_EVENT_FLAGS
 #define ATTNRES_TIMING_EVENT_FLAGS hipEventDisableSystemFence

@@ -698,6 +698,8 @@ struct AggParams {
   float* m_out;    // [R] or null
   float* lse_out;  // [R] or null
   Close cl;        // close computing source n-1, or cl.v == null
+  const void* o_init;     // [R][D] normalised output of an earlier group, or null
+  const float* lse_init;  // [R] its log-sum-exp
   Geom g;
 };
 
@@ -728,11 +730,26 @@ __global__ __launch_bounds__(512) void aggregate_kernel(AggParams p) {
     const int64_t row = grp * g.RPW + ln.slot;
     const bool rv = row < g.R;
     float num[VPL][EPV];
-    #pragma unroll
-    for (int c = 0; c < VPL; ++c)
-      #pragma unroll
-      for (int e = 0; e < EPV; ++e) num[c][e] = 0.f;
     float m_run = -FLT_MAX, z_run = 0.f;
+    if (p.o_init) {
+      // start from an earlier group's summary (lse, z = 1, u = o): the
+      // single-triple form of a normalised group [K3 9.4 (OS1)]
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        const int vec = c * ln.stride + ln.t;
+        const uint4 u = (rv && vec < g.V)
+                            ? ld16_stream(static_cast<const char*>(p.o_init) + row * rowbytes + (int64_t)vec * 16)
+                            : make_uint4(0, 0, 0, 0);
+        T::unpack(u, num[c]);
+      }
+      m_run = rv ? p.lse_init[row] : 0.f;
+      z_run = 1.f;
+    } else {
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c)
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) num[c][e] = 0.f;
+    }
 
     for (int i0 = 0; i0 < p.n; i0 += G) {
       float x[G][VPL][EPV];
@@ -1164,6 +1181,7 @@ static hipError_t launch_aggregate_dt(const AggArgs& a, const Launch& L) {
   p.n = a.n; p.w = a.w; p.gm = a.g; p.eps = a.eps;
   p.out = a.out; p.m_out = a.m_out; p.lse_out = a.lse_out;
   p.cl = Close{a.close_p, a.close_v, a.close_b};
+  p.o_init = a.o_init; p.lse_init = a.lse_init;
   p.g = make_geom(a.R, a.D, T::kBytes, 2, 4);
   if (p.g.W > 8) {
     // widest rows: four vectors per lane and groups of four sources

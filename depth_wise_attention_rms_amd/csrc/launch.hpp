@@ -47,6 +47,10 @@ struct AggArgs {
   const void* close_p;
   const void* close_v;
   void* close_b;
+  // optional starting summary of an earlier group: normalised output [R][D]
+  // and its log-sum-exp [R] (both null: start empty)
+  const void* o_init = nullptr;
+  const float* lse_init = nullptr;
 };
 
 struct Phase2Args {

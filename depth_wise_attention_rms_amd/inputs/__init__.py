@@ -156,6 +156,11 @@ WORKLOADS = {
     "full_L16": Workload(
         "full_L16", "stack", B=4, T=512, D=1024, dtype="bf16", L=16, S=1,
         description="Full AttnRes stack (S=1), 16 sublayers + embedding, bf16"),
+    "full_L16_D4096": Workload(
+        "full_L16_D4096", "stack", B=8, T=2048, D=4096, dtype="bf16", L=16, S=1,
+        description="Full AttnRes stack at the Block config's token count and width "
+                    "(16 sublayers + embedding, 17 sources of 128 MiB): the HBM-bound case "
+                    "for the two-phase Full schedule"),
     "block_L48_S8": Workload(
         "block_L48_S8", "stack", B=8, T=2048, D=4096, dtype="bf16", L=48, S=8,
         description="Block AttnRes two-phase prefill, L=48, S=8 (6 blocks), bf16"),

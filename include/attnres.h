@@ -231,6 +231,41 @@ const char* attnres_status_string(int code);
 const char* attnres_last_error(void);
 
 /* ---------------------------------------------------------------------------
+ * Full AttnRes (every sublayer output is a source of its own [K3 9.3 Full;
+ * WC "Full AttnRes"]) with the two-phase schedule [K3 9.4: given a schedule
+ * block size the Full mixer runs the two-phase algorithm and matches the
+ * naive one; WC "Inference": the (S+N)d residual I/O of two-phase Full].
+ *
+ * attnres_merge_sources -- the intra-chunk step: merge the summary of an
+ *   earlier group (its normalised output o [R,D] dtype and log-sum-exp lse
+ *   [R] fp32, as Phase 1 returns them) with n more sources [K3 9.4 (OS2),
+ *   each new source its own term]:
+ *     out = (e^(lse-M) o + sum_i e^(s_i-M) v_i) / (e^(lse-M) + sum_i e^(s_i-M)),
+ *   s_i the usual score of source i under q~ = w * gamma, M the max of lse and
+ *   the s_i. m_out / lse_out [R] (optional) receive the merged statistics.
+ *   1 <= n <= ATTNRES_MAX_SOURCES; out must not alias o or a source.
+ *
+ * attnres_full_stack_forward -- the Full stack forward over L sublayers with
+ *   schedule block size C: chunk [s, s+C-1] runs Phase 1 with its queries over
+ *   [x, v_1 .. v_{s-1}] in one pass, hands h_s = o_0 to its first sublayer,
+ *   and gives sublayer s+j the merge of (lse_j, o_j) with v_s .. v_{s+j-1};
+ *   y = aggregate([x, v_1 .. v_L]; q~_{L+1}). C = 1 is the naive schedule.
+ *   W, Gamma [L+1, D] fp32 as in attnres_block_stack_forward. Every v_l
+ *   returned by the callback is a source to the end of the call and must
+ *   stay valid until then. Workspace: attnres_full_workspace_bytes(L, C, R,
+ *   D, dtype) bytes, 256-byte aligned. Limits: L + 1 <= ATTNRES_MAX_SOURCES.
+ *   Errors as attnres_block_stack_forward.
+ * ------------------------------------------------------------------------- */
+int attnres_merge_sources(const void* o, const float* lse, const void* const* sources, int n,
+                          int64_t R, int64_t D, int dtype, const float* w, const float* gamma,
+                          float eps, void* out, float* m_out, float* lse_out, void* stream);
+size_t attnres_full_workspace_bytes(int L, int C, int64_t R, int64_t D, int dtype);
+int attnres_full_stack_forward(const void* x, int L, int C, int64_t R, int64_t D, int dtype,
+                               const float* W, const float* Gamma, float eps,
+                               attnres_sublayer_fn f, void* f_ctx, void* y, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Optional launch timing (instrumentation for benchmarks; off by default).
  * attnres_timing_enable(capacity) makes this thread's subsequent launches
  * record a HIP event pair around each kernel on its stream, for up to

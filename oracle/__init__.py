@@ -90,12 +90,13 @@ class Oracle:
         L.oracle_block_stack.argtypes = [I64, I64, I, I, I, P, P, P, P, D,
                                          P, P, P, P, P, P, P, P, P, I]
         L.oracle_rmsnorm.argtypes = [I64, I64, I, P, P, D, P, P, I]
+        L.oracle_merge.argtypes = [I64, I64, I, P, P, I, P, P, P, D, P, P, P, P, I]
         L.oracle_round.argtypes = [D, I]
         L.oracle_round.restype = D
         L.oracle_store_rounded.argtypes = [P, I64, I, P]
         L.oracle_store_rounded.restype = None
         for f in ("oracle_aggregate", "oracle_phase1", "oracle_phase2", "oracle_block_plan",
-                  "oracle_atomic_block_size", "oracle_block_stack", "oracle_rmsnorm",
+                  "oracle_atomic_block_size", "oracle_block_stack", "oracle_rmsnorm", "oracle_merge",
                   "oracle_max_sources"):
             getattr(L, f).restype = ctypes.c_int
         self.lib = L
@@ -148,6 +149,21 @@ class Oracle:
                                     nthreads or default_threads())
         _check(rc, "oracle_phase2")
         return {"p": p_out, "h": h, "scale": sc}
+
+    def merge(self, o, lse, sources, w, gamma=None, eps=1e-8, nthreads=None):
+        """Merge a normalised group (o [rows, D], lse [rows]) with more sources."""
+        o = np.ascontiguousarray(o)
+        srcs = [np.ascontiguousarray(a) for a in sources]
+        dt = _dtype_code(o)
+        rows, D = o.shape
+        lse = np.ascontiguousarray(lse, dtype=np.float32)
+        w, gamma = _f32(w), _f32(gamma)
+        h = np.empty((rows, D)); sc = np.empty((rows, D)); m = np.empty(rows); ls = np.empty(rows)
+        rc = self.lib.oracle_merge(rows, D, dt, _ptr(o), _ptr(lse), len(srcs), _ptr_array(srcs), _ptr(w),
+                                   _ptr(gamma), eps, _ptr(h), _ptr(sc), _ptr(m), _ptr(ls),
+                                   nthreads or default_threads())
+        _check(rc, "oracle_merge")
+        return {"h": h, "scale": sc, "m": m, "lse": ls}
 
     def rmsnorm(self, x, gamma=None, eps=1e-6, nthreads=None):
         """RMSNorm of the rows of ``x`` (fp32 or bf16 bit patterns): fp64 outputs and per-row rms."""
@@ -233,6 +249,10 @@ def phase1(*a, **k):
 
 def phase2(*a, **k):
     return default().phase2(*a, **k)
+
+
+def merge(*a, **k):
+    return default().merge(*a, **k)
 
 
 def rmsnorm(*a, **k):

@@ -464,6 +464,77 @@ int oracle_block_stack(int64_t rows, int64_t D, int dtype, int L, int S, const v
 }
 
 /* ------------------------------------------------------------------------ */
+/* Merge of a group summary with more sources (the Full two-phase step)     */
+/* ------------------------------------------------------------------------ */
+
+/* An earlier group enters as its triple (lse, 1, o) -- normalised output o
+   with denominator 1 at the reference point lse [K3 9.4 (OS1)] -- and each new
+   source v_i as (s_i, 1, v_i) with s_i its score [K3 (A1)-(A2)]; (OS2) gives
+     M = max(lse, s_1..s_n),  Z = e^(lse-M) + sum_i e^(s_i-M),
+     h = (e^(lse-M) o + sum_i e^(s_i-M) v_i) / Z,
+   the merged statistics m = M, lse' = M + log Z, and the condition scale
+   (e^(lse-M) |o| + sum_i e^(s_i-M) |v_i|) / Z. */
+typedef struct {
+  int64_t D;
+  int dtype, n;
+  const void* o;
+  const float* lse;
+  const void* const* src;
+  const double* q;
+  double eps;
+  double *h, *scale, *m, *lse_out;
+} merge_ctx;
+
+static void merge_rowfn(void* pc, int64_t r, double* scratch) {
+  merge_ctx* c = (merge_ctx*)pc;
+  const int64_t D = c->D;
+  const double* V[ORACLE_MAX_SOURCES];
+  double s[ORACLE_MAX_SOURCES];
+  for (int i = 0; i < c->n; ++i) {
+    double* dst = scratch + (int64_t)i * D;
+    for (int64_t d = 0; d < D; ++d) dst[d] = widen(c->src[i], c->dtype, r * D + d);
+    V[i] = dst;
+    double one_lse;
+    const double* one[1] = {dst};
+    agg_row(1, one, c->q, D, c->eps, NULL, NULL, &s[i], &one_lse, NULL); /* m of one source = its score */
+  }
+  const double la = (double)c->lse[r];
+  double mm = la;
+  for (int i = 0; i < c->n; ++i) mm = s[i] > mm ? s[i] : mm;
+  const double wo = exp(la - mm);
+  double z = wo;
+  for (int i = 0; i < c->n; ++i) z += exp(s[i] - mm);
+  for (int64_t d = 0; d < D; ++d) {
+    const double ov = widen(c->o, c->dtype, r * D + d);
+    double num = wo * ov, sc = wo * fabs(ov);
+    for (int i = 0; i < c->n; ++i) {
+      const double a = exp(s[i] - mm);
+      num += a * V[i][d];
+      sc += a * fabs(V[i][d]);
+    }
+    if (c->h) c->h[r * D + d] = num / z;
+    if (c->scale) c->scale[r * D + d] = sc / z;
+  }
+  if (c->m) c->m[r] = mm;
+  if (c->lse_out) c->lse_out[r] = mm + log(z);
+}
+
+int oracle_merge(int64_t rows, int64_t D, int dtype, const void* o, const float* lse, int n,
+                 const void* const* sources, const float* w, const float* gamma, double eps,
+                 double* h, double* scale, double* m, double* lse_out, int nthreads) {
+  int rc = check_common(rows, D, dtype);
+  if (rc) return rc;
+  if (n < 1 || n > ORACLE_MAX_SOURCES || !o || !lse || !sources || !w) return ORACLE_EINVAL;
+  double* q = (double*)malloc((size_t)D * sizeof(double));
+  if (!q) return ORACLE_ENOMEM;
+  fold_query(w, gamma, D, q);
+  merge_ctx c = {D, dtype, n, o, lse, sources, q, eps, h, scale, m, lse_out};
+  rc = run_rows(rows, nthreads, merge_rowfn, &c, (size_t)n * (size_t)D);
+  free(q);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* RMSNorm: the input norm of the sublayer that consumes an aggregate       */
 /* ------------------------------------------------------------------------ */
 

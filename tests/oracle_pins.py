@@ -518,4 +518,56 @@ def pin_rmsnorm_closed_forms(orc):
     assert np.array_equal(out, out4)
 
 
+def _merge_inputs(rng, rows=6, D=32, nA=3, nB=2):
+    A = [(rng.standard_normal((rows, D)) * s).astype(np.float32) for s in (1.0, 3.0, 0.4)[:nA]]
+    B = [(rng.standard_normal((rows, D)) * s).astype(np.float32) for s in (2.0, 0.7, 5.0)[:nB]]
+    w = (0.3 * rng.standard_normal(D)).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    return A, B, w, g
+
+
+def pin_merge_is_aggregate_of_union(orc):
+    """Merging the summary (lse, o) of sources A with sources B equals one
+    aggregate over A and B together: the exactness of the online-softmax merge
+    across phases (K3 §9.4 (OS1)/(OS2) and its equivalence box), on which the
+    Full two-phase schedule rests. o and lse are rounded to fp32 on the way,
+    as a kernel stores them."""
+    rng = np.random.default_rng(41)
+    A, B, w, g = _merge_inputs(rng)
+    a = orc.aggregate(A, w, g)
+    o = orc.round_to(a["h"], "f32")
+    lse = a["lse"].astype(np.float32)
+    got = orc.merge(o, lse, B, w, g)
+    want = orc.aggregate(A + B, w, g)
+    assert np.all(np.abs(got["h"] - want["h"]) <= 1e-6 * want["scale"])
+    # lse is invariant; m is only the merge's reference point (max(lse_A, s_B))
+    np.testing.assert_allclose(got["lse"], want["lse"], rtol=0, atol=1e-6 * (1 + np.abs(want["lse"])).max())
+
+
+def pin_merge_one_source_is_phase2(orc):
+    """With a single new source the merge is the Phase-2 step on a first
+    partial p = v (K3 §9.4 single-source triple)."""
+    rng = np.random.default_rng(43)
+    A, B, w, g = _merge_inputs(rng, nB=1)
+    a = orc.aggregate(A, w, g)
+    o = orc.round_to(a["h"], "f32")
+    lse = a["lse"].astype(np.float32)
+    got = orc.merge(o, lse, B, w, g)["h"]
+    ref = orc.phase2(o, lse, w, None, B[0], g)["h"]
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-13)
+
+
+def pin_merge_limits(orc):
+    """A group with lse far below the new sources' scores contributes nothing
+    (the merge is the aggregate of the new sources); far above, the merge
+    returns the group's output."""
+    rng = np.random.default_rng(47)
+    A, B, w, g = _merge_inputs(rng)
+    o = A[0]
+    low = orc.merge(o, np.full(o.shape[0], -1e4, np.float32), B, w, g)["h"]
+    np.testing.assert_allclose(low, orc.aggregate(B, w, g)["h"], rtol=1e-12, atol=1e-12)
+    high = orc.merge(o, np.full(o.shape[0], 1e4, np.float32), B, w, g)["h"]
+    np.testing.assert_allclose(high, o.astype(np.float64), rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

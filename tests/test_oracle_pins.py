@@ -30,6 +30,11 @@ def test_pin(orc, pin):
 
 # (name, exact text in oracle.c, replacement)
 MUTANTS = [
+    ("merge_drops_group", "const double wo = exp(la - mm);", "const double wo = 0.0 * exp(la - mm);"),
+    ("merge_lse_drops_max", "if (c->lse_out) c->lse_out[r] = mm + log(z);",
+     "if (c->lse_out) c->lse_out[r] = log(z);"),
+    ("merge_wrong_source_weight", "const double a = exp(s[i] - mm);",
+     "const double a = exp(s[c->n - 1 - i] - mm);"),
     ("norm_sum_not_mean", "const double rms = sqrt(ss / (double)D + c->eps);",
      "const double rms = sqrt(ss + c->eps);"),
     ("norm_eps_outside_root", "const double rms = sqrt(ss / (double)D + c->eps);",
