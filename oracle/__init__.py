@@ -91,12 +91,14 @@ class Oracle:
                                          P, P, P, P, P, P, P, P, P, I]
         L.oracle_rmsnorm.argtypes = [I64, I64, I, P, P, D, P, P, I]
         L.oracle_merge.argtypes = [I64, I64, I, P, P, I, P, P, P, D, P, P, P, P, I]
+        L.oracle_aggregate_backward.argtypes = [I64, I64, I, I, P, P, P, D, P, P, P, P, I]
         L.oracle_round.argtypes = [D, I]
         L.oracle_round.restype = D
         L.oracle_store_rounded.argtypes = [P, I64, I, P]
         L.oracle_store_rounded.restype = None
         for f in ("oracle_aggregate", "oracle_phase1", "oracle_phase2", "oracle_block_plan",
                   "oracle_atomic_block_size", "oracle_block_stack", "oracle_rmsnorm", "oracle_merge",
+                  "oracle_aggregate_backward",
                   "oracle_max_sources"):
             getattr(L, f).restype = ctypes.c_int
         self.lib = L
@@ -149,6 +151,20 @@ class Oracle:
                                     nthreads or default_threads())
         _check(rc, "oracle_phase2")
         return {"p": p_out, "h": h, "scale": sc}
+
+    def aggregate_backward(self, sources, w, dh, gamma=None, eps=1e-8, nthreads=None):
+        """Gradients of one aggregate for upstream dh [rows, D]: dV [n, rows, D],
+        dw [D] and dgamma [D] (None without a gain), all float64."""
+        srcs, dt, rows, D = _sources(sources)
+        dh = np.ascontiguousarray(dh)
+        w, gamma = _f32(w), _f32(gamma)
+        dV = np.empty((len(srcs), rows, D)); dw = np.empty(D)
+        dg = np.empty(D) if gamma is not None else None
+        rc = self.lib.oracle_aggregate_backward(rows, D, dt, len(srcs), _ptr_array(srcs), _ptr(w),
+                                                _ptr(gamma), eps, _ptr(dh), _ptr(dV), _ptr(dw),
+                                                _ptr(dg), nthreads or default_threads())
+        _check(rc, "oracle_aggregate_backward")
+        return {"dV": dV, "dw": dw, "dgamma": dg}
 
     def merge(self, o, lse, sources, w, gamma=None, eps=1e-8, nthreads=None):
         """Merge a normalised group (o [rows, D], lse [rows]) with more sources."""
@@ -249,6 +265,10 @@ def phase1(*a, **k):
 
 def phase2(*a, **k):
     return default().phase2(*a, **k)
+
+
+def aggregate_backward(*a, **k):
+    return default().aggregate_backward(*a, **k)
 
 
 def merge(*a, **k):

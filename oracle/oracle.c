@@ -464,6 +464,101 @@ int oracle_block_stack(int64_t rows, int64_t D, int dtype, int L, int S, const v
 }
 
 /* ------------------------------------------------------------------------ */
+/* Backward of one aggregate (A1)-(A3), with the scores recomputed          */
+/* ------------------------------------------------------------------------ */
+
+/* Given the upstream gradient dh of h = sum_i a_i V_i, with
+     r_i = sqrt(mean_d V_i^2 + eps),  s_i = q~ . V_i / r_i,  a = softmax(s),
+   the chain rule through (A1)-(A3) gives, per row:
+     g_i    = dh . V_i                           (dL/da_i)
+     ds_i   = a_i (g_i - dh . h)                 (softmax Jacobian)
+     dV_i   = a_i dh + ds_i (q~ / r_i - s_i V_i / (D r_i^2))
+                                                 (weighted sum, then the score
+                                                  through V_i and through r_i)
+     dq~    = sum_i ds_i V_i / r_i,
+   and, through the fold q~ = w * gamma (its fp32 rounding taken as exact),
+     dw = dq~ * gamma,  dgamma = dq~ * w,  summed over rows. */
+typedef struct {
+  int64_t D;
+  int dtype, n;
+  const void* const* src;
+  const void* dh;
+  const double* q;
+  double eps;
+  double* dV;  /* [n][rows][D] */
+  double* dq;  /* [rows][D], per-row dq~ (summed over rows afterwards) */
+  int64_t rows;
+} bwd_ctx;
+
+static void bwd_rowfn(void* pc, int64_t r, double* scratch) {
+  bwd_ctx* c = (bwd_ctx*)pc;
+  const int64_t D = c->D;
+  const int n = c->n;
+  const double* V[ORACLE_MAX_SOURCES];
+  double* g = scratch + (int64_t)n * D; /* [D]: dh, then the recomputed h */
+  double* h = g + D;
+  for (int i = 0; i < n; ++i) {
+    double* dst = scratch + (int64_t)i * D;
+    for (int64_t d = 0; d < D; ++d) dst[d] = widen(c->src[i], c->dtype, r * D + d);
+    V[i] = dst;
+  }
+  for (int64_t d = 0; d < D; ++d) g[d] = widen(c->dh, c->dtype, r * D + d);
+  double a[ORACLE_MAX_SOURCES], s[ORACLE_MAX_SOURCES], rr[ORACLE_MAX_SOURCES];
+  agg_row(n, V, c->q, D, c->eps, h, NULL, NULL, NULL, a);
+  for (int i = 0; i < n; ++i) {
+    double ss = 0.0, dot = 0.0;
+    for (int64_t d = 0; d < D; ++d) ss += V[i][d] * V[i][d];
+    rr[i] = sqrt(ss / (double)D + c->eps);
+    for (int64_t d = 0; d < D; ++d) dot += c->q[d] * V[i][d];
+    s[i] = dot / rr[i];
+  }
+  double gh = 0.0;
+  for (int64_t d = 0; d < D; ++d) gh += g[d] * h[d];
+  double* dq = c->dq + r * D;
+  for (int64_t d = 0; d < D; ++d) dq[d] = 0.0;
+  for (int i = 0; i < n; ++i) {
+    double gi = 0.0;
+    for (int64_t d = 0; d < D; ++d) gi += g[d] * V[i][d];
+    const double ds = a[i] * (gi - gh);
+    double* dv = c->dV + ((int64_t)i * c->rows + r) * D;
+    for (int64_t d = 0; d < D; ++d) {
+      dv[d] = a[i] * g[d] + ds * (c->q[d] / rr[i] - s[i] * V[i][d] / ((double)D * rr[i] * rr[i]));
+      dq[d] += ds * V[i][d] / rr[i];
+    }
+  }
+}
+
+int oracle_aggregate_backward(int64_t rows, int64_t D, int dtype, int n, const void* const* sources,
+                              const float* w, const float* gamma, double eps, const void* dh,
+                              double* dV, double* dw, double* dgamma, int nthreads) {
+  int rc = check_common(rows, D, dtype);
+  if (rc) return rc;
+  if (n < 1 || n > ORACLE_MAX_SOURCES || !sources || !w || !dh || !dV || !dw) return ORACLE_EINVAL;
+  double* q = (double*)malloc((size_t)D * sizeof(double));
+  double* dq = (double*)malloc((size_t)(rows > 0 ? rows : 1) * (size_t)D * sizeof(double));
+  if (!q || !dq) {
+    free(q);
+    free(dq);
+    return ORACLE_ENOMEM;
+  }
+  fold_query(w, gamma, D, q);
+  bwd_ctx c = {D, dtype, n, sources, dh, q, eps, dV, dq, rows};
+  rc = run_rows(rows, nthreads, bwd_rowfn, &c, (size_t)(n + 2) * (size_t)D);
+  if (rc == ORACLE_OK) {
+    for (int64_t d = 0; d < D; ++d) {
+      double t = 0.0;
+      for (int64_t r = 0; r < rows; ++r) t += dq[r * D + d];
+      const double g = gamma ? (double)gamma[d] : 1.0;
+      dw[d] = t * g;
+      if (dgamma) dgamma[d] = t * (double)w[d];
+    }
+  }
+  free(q);
+  free(dq);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Merge of a group summary with more sources (the Full two-phase step)     */
 /* ------------------------------------------------------------------------ */
 

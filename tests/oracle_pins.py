@@ -570,4 +570,73 @@ def pin_merge_limits(orc):
     np.testing.assert_allclose(high, o.astype(np.float64), rtol=1e-12, atol=1e-12)
 
 
+def _grid_values(rng, shape, scale_bits, lo, hi):
+    """fp32 values k * 2^-scale_bits, integer k in [lo, hi): exact in fp32, and
+    stay exact after adding or subtracting 2^-10 when scale_bits >= 10."""
+    return (rng.integers(lo, hi, size=shape).astype(np.float64) * 2.0 ** -scale_bits).astype(np.float32)
+
+
+def pin_backward_finite_differences(orc):
+    """The aggregate backward against central finite differences of
+    L = sum(dh * h) computed by the forward oracle, for every source element,
+    every w and every gain (K3 §9.1 (A1)-(A3) differentiated). Inputs are
+    fp32 grid values, so each +-2^-10 perturbation is exact, w * gamma is exact
+    in fp32, and the fp64 forward makes the difference quotients accurate to
+    about 1e-9 of the gradient scale."""
+    rng = np.random.default_rng(53)
+    rows, D, n = 2, 16, 3
+    V = [_grid_values(rng, (rows, D), 12, -8192, 8192) for _ in range(n)]
+    w = _grid_values(rng, D, 12, -1024, 1024)
+    g = _grid_values(rng, D, 4, 8, 24)  # gains 0.5 .. 1.5
+    dh = _grid_values(rng, (rows, D), 12, -4096, 4096)
+    eps = 1e-3
+    got = orc.aggregate_backward(V, w, dh, g, eps=eps)
+    delta = np.float32(2.0 ** -10)
+
+    def loss(VV, ww, gg):
+        return float((orc.aggregate(VV, ww, gg, eps=eps)["h"] * dh.astype(np.float64)).sum())
+
+    scale = max(np.abs(got["dV"]).max(), np.abs(got["dw"]).max(), np.abs(got["dgamma"]).max())
+    for i in range(n):
+        for r in range(rows):
+            for d in range(D):
+                Vp = [a.copy() for a in V]; Vm = [a.copy() for a in V]
+                Vp[i][r, d] += delta; Vm[i][r, d] -= delta
+                fd = (loss(Vp, w, g) - loss(Vm, w, g)) / (2 * float(delta))
+                assert abs(fd - got["dV"][i, r, d]) <= 1e-6 * scale, (i, r, d, fd, got["dV"][i, r, d])
+    for d in range(D):
+        wp, wm = w.copy(), w.copy()
+        wp[d] += delta; wm[d] -= delta
+        fd = (loss(V, wp, g) - loss(V, wm, g)) / (2 * float(delta))
+        assert abs(fd - got["dw"][d]) <= 1e-6 * scale, ("w", d, fd, got["dw"][d])
+        gp, gm = g.copy(), g.copy()
+        gp[d] += delta; gm[d] -= delta
+        fd = (loss(V, w, gp) - loss(V, w, gm)) / (2 * float(delta))
+        assert abs(fd - got["dgamma"][d]) <= 1e-6 * scale, ("gamma", d, fd, got["dgamma"][d])
+
+
+def pin_backward_special_cases(orc):
+    """One source: h is the source, so dV = dh exactly and the query gets no
+    gradient; a zero upstream gradient gives zero gradients; with eps = 0 the
+    score part of dV_i is orthogonal to V_i (scores ignore a source's scale,
+    K3 §9.2)."""
+    rng = np.random.default_rng(59)
+    V = [rng.standard_normal((3, 32)).astype(np.float32) for _ in range(4)]
+    w = (0.2 * rng.standard_normal(32)).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, 32).astype(np.float32)
+    dh = rng.standard_normal((3, 32)).astype(np.float32)
+    one = orc.aggregate_backward(V[:1], w, dh, g)
+    assert np.array_equal(one["dV"][0], dh.astype(np.float64))
+    assert not np.any(one["dw"]) and not np.any(one["dgamma"])
+    zero = orc.aggregate_backward(V, w, np.zeros_like(dh), g)
+    assert not np.any(zero["dV"]) and not np.any(zero["dw"])
+    full = orc.aggregate_backward(V, w, dh, g, eps=0.0)
+    alpha = orc.aggregate(V, w, g, eps=0.0, want_alpha=True)["alpha"]
+    for i in range(4):
+        score_part = full["dV"][i] - alpha[:, i:i + 1] * dh.astype(np.float64)
+        dot = (score_part * V[i].astype(np.float64)).sum(axis=1)
+        ref = np.abs(score_part).sum(axis=1) * np.abs(V[i]).max()
+        assert np.all(np.abs(dot) <= 1e-12 * ref)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

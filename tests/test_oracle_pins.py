@@ -30,6 +30,12 @@ def test_pin(orc, pin):
 
 # (name, exact text in oracle.c, replacement)
 MUTANTS = [
+    ("bwd_drops_rms_term", "ds * (c->q[d] / rr[i] - s[i] * V[i][d] / ((double)D * rr[i] * rr[i]))",
+     "ds * (c->q[d] / rr[i])"),
+    ("bwd_softmax_no_centering", "const double ds = a[i] * (gi - gh);", "const double ds = a[i] * gi;"),
+    ("bwd_dgamma_uses_gain", "if (dgamma) dgamma[d] = t * (double)w[d];",
+     "if (dgamma) dgamma[d] = t * g;"),
+    ("bwd_dq_raw_sources", "dq[d] += ds * V[i][d] / rr[i];", "dq[d] += ds * V[i][d];"),
     ("merge_drops_group", "const double wo = exp(la - mm);", "const double wo = 0.0 * exp(la - mm);"),
     ("merge_lse_drops_max", "if (c->lse_out) c->lse_out[r] = mm + log(z);",
      "if (c->lse_out) c->lse_out[r] = log(z);"),
