@@ -15,6 +15,8 @@ launch over its HIP-event-timed average duration, against 8 TB/s), and the
 fp64 CPU oracle timed on a bounded row sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --backward N   (the aggregate backward over N sources of
+           the workload's shape: its own JSON line, same keys)
        python bench.py --write-traffic FETCH_CSV WRITE_CSV   (CPU only: turn two
            rocprofv3 --pmc counter files of a run with --calibration-copy-gib 1
            into the HBM-traffic summary that the roofline entry reads)
@@ -46,11 +48,22 @@ def kernels_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per Phase-2 launch from the committed counter summary, or None
-    when it is absent, for another workload, or older than the kernels."""
+def traffic_paths(backward: int):
+    """(summary JSON, table, dominant kernel, bench arguments) of a measured workload."""
+    if backward:
+        stem = f"aggregate_backward_n{backward}_block_L48_S8"
+        return (os.path.join(ROOT, "profiles", f"{stem}_traffic.json"),
+                os.path.join(ROOT, "profiles", f"{stem}_hbm_traffic.txt"),
+                "attnres::aggregate_bwd_kernel", f"--backward {backward} ")
+    return TRAFFIC_FILE, TRAFFIC_TABLE, DOMINANT, ""
+
+
+def measured_traffic(workload: str, backward: int = 0):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when it is absent, for another workload, or older than
+    the kernels."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_paths(backward)[0]) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -59,12 +72,16 @@ def measured_traffic(workload: str):
     return t.get("traffic_bytes_per_launch")
 
 
-def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_gib: float = 1.0) -> dict:
+def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_gib: float = 1.0,
+                  backward: int = 0) -> dict:
     """HBM bytes per launch from FETCH_SIZE and WRITE_SIZE counter files (KiB
     per dispatch), each scaled by what the counter reads for the calibration
-    copy (copy_gib GiB read once and written once) in the same run."""
+    copy (its largest dispatch: copy_gib GiB read once and written once) in
+    the same run."""
     import csv
     import re
+
+    traffic_file, table_file, dominant, bench_args = traffic_paths(backward)
 
     def per_kernel(path, counter):
         d = {}
@@ -78,8 +95,8 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_gib: float
 
     fe, wr = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     true_kib = copy_gib * (1 << 20)
-    f_factor = true_kib / (sum(fe[COPY_KERNEL]) / len(fe[COPY_KERNEL]))
-    w_factor = true_kib / (sum(wr[COPY_KERNEL]) / len(wr[COPY_KERNEL]))
+    f_factor = true_kib / max(fe[COPY_KERNEL])
+    w_factor = true_kib / max(wr[COPY_KERNEL])
     mean = lambda v: sum(v) / len(v)
     rows = []
     for name in sorted(set(fe) & set(wr)):
@@ -88,25 +105,25 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_gib: float
         fb = mean(fe[name]) * f_factor * 1024
         wb = mean(wr[name]) * w_factor * 1024
         rows.append((name, len(fe[name]), mean(fe[name]), mean(wr[name]), fb, wb))
-    dom = [r for r in rows if r[0].startswith(DOMINANT)]
+    dom = [r for r in rows if r[0].startswith(dominant)]
     launches = sum(r[1] for r in dom)
     traffic = sum((r[4] + r[5]) * r[1] for r in dom) / launches
-    out = {"workload": workload, "kernel": DOMINANT.split("::")[1],
+    out = {"workload": workload, "kernel": dominant.split("::")[1],
            "traffic_bytes_per_launch": traffic,
            "fetch_factor": f_factor, "write_factor": w_factor,
            "calibration": f"{COPY_KERNEL}, {copy_gib} GiB read and written once",
            "kernels_sha256": kernels_digest()}
-    with open(TRAFFIC_FILE, "w") as f:
+    with open(traffic_file, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
-    with open(TRAFFIC_TABLE, "w") as f:
-        f.write(f"HBM traffic per dispatch, workload {workload} (bench.py --steps 2 --warmup 1 "
+    with open(table_file, "w") as f:
+        f.write(f"HBM traffic per dispatch, workload {workload} (bench.py {bench_args}--steps 2 --warmup 1 "
                 f"--cpu-rows 0 --calibration-copy-gib {copy_gib:g})\n")
         f.write("commands (from /tmp, TMPDIR=/tmp):\n"
                 "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <fetch> -o run -- python3 "
-                f"<repo>/bench.py --steps 2 --warmup 1 --cpu-rows 0 --calibration-copy-gib {copy_gib:g}\n"
+                f"<repo>/bench.py {bench_args}--steps 2 --warmup 1 --cpu-rows 0 --calibration-copy-gib {copy_gib:g}\n"
                 "  rocprofv3 --pmc WRITE_SIZE ... (same)\n"
-                f"  python bench.py --write-traffic <fetch>/run_counter_collection.csv "
+                f"  python bench.py {bench_args}--write-traffic <fetch>/run_counter_collection.csv "
                 f"<write>/run_counter_collection.csv\n")
         f.write(f"calibration: FETCH_SIZE x {f_factor:.4f}, WRITE_SIZE x {w_factor:.4f} "
                 f"(counter reading of the {copy_gib:g} GiB copy vs its true size)\n\n")
@@ -114,35 +131,144 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_gib: float
                 f"{'read MB':>10s} {'write MB':>10s}\n")
         for name, n, fk, wk, fb, wb in rows:
             f.write(f"{name:52s} {n:10d} {fk:12.1f} {wk:12.1f} {fb / 1e6:10.2f} {wb / 1e6:10.2f}\n")
-        f.write(f"\n{DOMINANT}: {traffic / 1e6:.2f} MB per launch (mean over its {launches} dispatches)\n")
+        f.write(f"\n{dominant}: {traffic / 1e6:.2f} MB per launch (mean over its {launches} dispatches)\n")
         f.write(f"kernel sources sha256 {out['kernels_sha256']}\n")
     return out
 
 
-def cpu_baseline(ds, wl, seconds: float, chunk: int = 2048) -> dict:
-    """The fp64 oracle's naive forward on consecutive chunks of token rows
-    (cycling over the workload) until ``seconds`` of CPU work have run."""
+def calibration_copy(gib: float):
+    """A plain copy kernel of known size (read once, written once), so that
+    hardware counters of the same run can be scaled to bytes."""
+    if gib <= 0:
+        return
+    import torch
+    n = int(gib * (1 << 30)) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def bench_backward(args, wl) -> dict:
+    """One step = one attnres_aggregate_backward over n sources of the
+    workload's shape (R token rows of D, bf16), fp32 gradients written; the
+    main kernel's HIP-event-timed launches give the roofline entry."""
+    import math
     import numpy as np
-    import oracle
+    import torch
+
+    from depth_wise_attention_rms_amd import binding
+    from depth_wise_attention_rms_amd import inputs
     from depth_wise_attention_rms_amd.workload import EPS
 
-    if not os.path.exists(oracle.LIBRARY):
-        oracle.build()
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
-    done, spent, start = 0, 0.0, 0
-    while done == 0 or spent < seconds:
-        rows = np.arange(start, min(start + chunk, wl.R))
-        start = 0 if start + chunk >= wl.R else start + chunk
-        xr, vr = ds.host_rows(rows)
-        c0 = time.perf_counter()
-        oracle.block_stack(xr, vr, ds.W_host, wl.S, eps=EPS, want_h=False, nthreads=cores)
-        spent += time.perf_counter() - c0
-        done += len(rows)
-        del xr, vr
-    return {"value": round(done / spent, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} token rows in chunks of {chunk} consecutive rows cycling over the "
-                      f"{wl.R} of the workload, full {wl.L}-sublayer naive forward in fp64 "
-                      f"({cores} threads), {spent:.2f} s of CPU time (host copies excluded)"}
+    n, R, D = args.backward, wl.R, wl.D
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    calibration_copy(args.calibration_copy_gib)
+
+    def fill(role, layer, scale):
+        return inputs.fill_normal(torch.empty((R, D), dtype=dt, device="cuda"), wl.seed, role, layer, scale)
+
+    srcs = [fill(inputs.ROLE_SRC, i, 0.5 + 0.37 * i) for i in range(n)]
+    dh = fill(inputs.ROLE_AUX, 9, 1.0)
+    w_h = inputs.queries(wl.seed, 1, D, sigma=0.3 / math.sqrt(D / 64))[0]
+    g_h = inputs.gains(wl.seed, D)
+    w, g = torch.from_numpy(w_h).cuda(), torch.from_numpy(g_h).cuda()
+    dV = [torch.empty((R, D), dtype=torch.float32, device="cuda") for _ in range(n)]
+    dw = torch.empty(D, dtype=torch.float32, device="cuda")
+    dg = torch.empty(D, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(binding.attnres_aggregate_backward_workspace_bytes(R, D, dt), 256),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        binding.attnres_aggregate_backward(srcs, w, dh, gamma=g, eps=EPS, dV=dV, dw=dw, dgamma=dg,
+                                           workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stride = max(1, args.steps // TIMED_STEPS)
+    instrumented = [i for i in range(args.steps) if i % stride == stride // 2][:TIMED_STEPS]
+    binding.attnres_timing_enable(3 * len(instrumented) + 4)
+    binding.attnres_timing_pause(True)
+    binding.attnres_timing_reset()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        if i in instrumented:
+            binding.attnres_timing_pause(False)
+            step()
+            binding.attnres_timing_pause(True)
+        else:
+            step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    kinds = {}
+    for k in ("backward", "backward_reduce"):
+        cnt, ms, byts = binding.attnres_timing_read(k)
+        if cnt:
+            kinds[k] = {"launches_per_step": cnt / len(instrumented), "avg_us": 1e3 * ms / cnt,
+                        "ms_per_step": ms / len(instrumented), "bytes_per_launch": byts / cnt,
+                        "GBps": byts / (ms * 1e6)}
+    binding.attnres_timing_enable(0)
+    main_k = kinds["backward"]
+    step_bytes = main_k["bytes_per_launch"]
+    roofline = {"bound": "hbm", "kernel": "aggregate_bwd_kernel", "achieved": round(main_k["GBps"], 1),
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(main_k["GBps"] / PEAK_HBM_GBPS, 4),
+                "traffic": measured_traffic(f"aggregate_backward_n{n}_{wl.name}", n),
+                "bytes_per_launch": step_bytes, "avg_launch_us": round(main_k["avg_us"], 2),
+                "timed_launches": len(instrumented), "timed_in": "timed region"}
+    cpu = None
+    if args.cpu_rows > 0:
+        import oracle
+        if not os.path.exists(oracle.LIBRARY):
+            oracle.build()
+        cores = max(1, min(16, len(os.sched_getaffinity(0))))
+        done, spent, start, chunk = 0, 0.0, 0, 256
+        while done == 0 or spent < args.cpu_seconds:
+            rows = np.arange(start, min(start + chunk, R))
+            start = 0 if start + chunk >= R else start + chunk
+            hs = [inputs.tensor_rows(wl.seed, inputs.ROLE_SRC, i, rows, D, 0.5 + 0.37 * i, wl.dtype)
+                  for i in range(n)]
+            hdh = inputs.tensor_rows(wl.seed, inputs.ROLE_AUX, 9, rows, D, 1.0, wl.dtype)
+            c0 = time.perf_counter()
+            oracle.aggregate_backward(hs, w_h, hdh, g_h, eps=EPS, nthreads=cores)
+            spent += time.perf_counter() - c0
+            done += len(rows)
+        cpu = {"value": round(done / spent, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+               "sample": f"{done} token rows in chunks of {chunk} consecutive rows, the fp64 aggregate "
+                         f"backward over {n} sources ({cores} threads), {spent:.2f} s of CPU time"}
+    return {
+        "metric": f"tokens/s and achieved HBM GB/s (% of peak) for the AttnRes aggregate backward "
+                  f"({n} sources, recomputation, fp32 gradients)",
+        "value": round(R / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "gpu_ms_per_step": round(gpu_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded counter-based normals; inputs resident in HBM)",
+        "config": {"workload": f"aggregate_backward_n{n}_{wl.name}", "B": wl.B, "T": wl.T, "D": D,
+                   "sources": n, "global_batch": wl.B, "seq_len": wl.T, "parallelism": "single GPU"},
+        "achieved_GBps": round(step_bytes / (ms_per_step * 1e6), 1),
+        "hbm_frac": round(step_bytes / (ms_per_step * 1e6) / PEAK_HBM_GBPS, 4),
+        "bytes_per_step": step_bytes,
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kinds.items()},
+        "cpu_baseline": cpu,
+    }
 
 
 def main() -> int:
@@ -164,6 +290,9 @@ def main() -> int:
                          "(attnres_full_stack_forward; C = 1 is the naive schedule)")
     ap.add_argument("--output-norm", action="store_true",
                     help="hand every sublayer RMSNorm(h_l) * gamma_l (fused into Phase 2) instead of h_l")
+    ap.add_argument("--backward", type=int, default=0, metavar="N",
+                    help="time the aggregate backward over N sources of the workload's shape instead "
+                         "of the stack forward")
     ap.add_argument("--calibration-copy-gib", type=float, default=0.0,
                     help="before the steps, copy a tensor of this many GiB with torch (a plain "
                          "copy kernel of known size, read once and written once) so hardware "
@@ -171,7 +300,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.write_traffic:
-        t = write_traffic(*args.write_traffic, workload=args.workload)
+        wname = f"aggregate_backward_n{args.backward}_{args.workload}" if args.backward else args.workload
+        t = write_traffic(*args.write_traffic, workload=wname, backward=args.backward)
         print(json.dumps(t))
         return 0
 
@@ -193,6 +323,9 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     wl = inputs.WORKLOADS[args.workload]
+    if args.backward:
+        print(json.dumps(bench_backward(args, wl)), flush=True)
+        return 0
     assert wl.kind == "stack" and not wl.ring, "the benchmark times a resident-table stack workload"
     ds = DeviceStack(wl)
     nb = ds.nb
@@ -215,14 +348,7 @@ def main() -> int:
         def forward(stream=None):
             ds.forward(stream=stream, norm=norm)
 
-    if args.calibration_copy_gib > 0:
-        n = int(args.calibration_copy_gib * (1 << 30)) // 2
-        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    calibration_copy(args.calibration_copy_gib)
 
     for _ in range(args.warmup):
         forward()

@@ -22,14 +22,16 @@ LIB_PATH = os.path.join(PKG, "libattnres.so")
 
 ATTNRES_F32, ATTNRES_BF16 = 0, 1
 STATUS = {0: "ok", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP", -5: "ECALLBACK"}
-TIMING_KINDS = {"phase1": 0, "phase2": 1, "aggregate": 2, "close": 3, "fold": 4, "norm": 5}
+TIMING_KINDS = {"phase1": 0, "phase2": 1, "aggregate": 2, "close": 3, "fold": 4, "norm": 5,
+                "backward": 6, "backward_reduce": 7}
 
 EXPORTS = (
     "attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge",
     "attnres_phase2_merge_norm", "attnres_rmsnorm", "attnres_table_sublayer",
     "attnres_stack_workspace_bytes", "attnres_block_stack_forward",
     "attnres_block_stack_forward_norm", "attnres_merge_sources", "attnres_full_workspace_bytes",
-    "attnres_full_stack_forward", "attnres_block_layout",
+    "attnres_full_stack_forward", "attnres_aggregate_backward_workspace_bytes",
+    "attnres_aggregate_backward", "attnres_block_layout",
     "attnres_atomic_block_size", "attnres_status_string", "attnres_last_error",
     "attnres_timing_enable", "attnres_timing_pause", "attnres_timing_reset", "attnres_timing_read",
 )
@@ -73,6 +75,9 @@ def lib():
         L.attnres_full_workspace_bytes.argtypes = [I, I, I64, I64, I]
         L.attnres_full_workspace_bytes.restype = SZ
         L.attnres_full_stack_forward.argtypes = [P, I, I, I64, I64, I, P, P, F, P, P, P, P, SZ, P]
+        L.attnres_aggregate_backward_workspace_bytes.argtypes = [I64, I64, I]
+        L.attnres_aggregate_backward_workspace_bytes.restype = SZ
+        L.attnres_aggregate_backward.argtypes = [P, I, I64, I64, I, P, P, F, P, P, I, P, P, P, SZ, P]
         L.attnres_block_layout.argtypes = [I, I, P, P]
         L.attnres_atomic_block_size.argtypes = [I, I]
         L.attnres_status_string.argtypes = [I]
@@ -85,7 +90,7 @@ def lib():
         L.attnres_timing_read.argtypes = [I, ctypes.POINTER(I64), ctypes.POINTER(D), ctypes.POINTER(D)]
         for f in ("attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge",
                   "attnres_phase2_merge_norm", "attnres_rmsnorm", "attnres_block_stack_forward_norm",
-                  "attnres_merge_sources", "attnres_full_stack_forward",
+                  "attnres_merge_sources", "attnres_full_stack_forward", "attnres_aggregate_backward",
                   "attnres_table_sublayer", "attnres_block_stack_forward", "attnres_block_layout",
                   "attnres_atomic_block_size", "attnres_timing_enable", "attnres_timing_pause",
                   "attnres_timing_reset", "attnres_timing_read"):
@@ -330,6 +335,37 @@ def attnres_full_stack_forward(x: torch.Tensor, W: torch.Tensor, C: int, sublaye
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
     del keep
     return y
+
+
+def attnres_aggregate_backward_workspace_bytes(R: int, D: int, dtype: torch.dtype) -> int:
+    return int(lib().attnres_aggregate_backward_workspace_bytes(R, D, dtype_code(dtype)))
+
+
+def attnres_aggregate_backward(sources: Sequence[torch.Tensor], w: torch.Tensor, dh: torch.Tensor,
+                               gamma=None, eps=1e-8, dV=None, dw=None, dgamma=None,
+                               accumulate=False, want_dgamma=None, workspace=None, stream=None):
+    """Gradients of AGG(sources) for upstream ``dh``; returns (dV list of fp32
+    [..., D], dw [D], dgamma [D] or None). dgamma is produced when
+    ``want_dgamma`` (default: a gain is given) or a buffer is passed."""
+    x0 = sources[0]
+    R, D = _rows(x0)
+    dev = x0.device
+    if dV is None:
+        dV = [torch.empty(x0.shape, dtype=torch.float32, device=dev) for _ in sources]
+    if dw is None:
+        dw = torch.empty(D, dtype=torch.float32, device=dev)
+    if want_dgamma is None:
+        want_dgamma = gamma is not None
+    if dgamma is None and want_dgamma:
+        dgamma = torch.empty(D, dtype=torch.float32, device=dev)
+    need = attnres_aggregate_backward_workspace_bytes(R, D, x0.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check("attnres_aggregate_backward", lib().attnres_aggregate_backward(
+        _ptr_array(sources), len(sources), R, D, dtype_code(x0.dtype), _ptr(w), _ptr(gamma), eps,
+        _ptr(dh), _ptr_array(dV), 1 if accumulate else 0, _ptr(dw), _ptr(dgamma),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
+    return dV, dw, dgamma
 
 
 def attnres_timing_enable(capacity: int):

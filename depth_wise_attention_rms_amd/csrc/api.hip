@@ -19,6 +19,8 @@
 #define ATTNRES_API extern "C" __attribute__((visibility("default")))
 
 using attnres::AggArgs;
+using attnres::BwdArgs;
+using attnres::BwdPlan;
 using attnres::Launch;
 using attnres::Phase1Args;
 using attnres::Phase2Args;
@@ -77,7 +79,17 @@ int check_ptr(const char* fn, const char* name, const void* p, bool required) {
 // ---------------------------------------------------------------------------
 // launch timing (instrumentation)
 // ---------------------------------------------------------------------------
-enum Kind { K_PHASE1 = 0, K_PHASE2 = 1, K_AGG = 2, K_CLOSE = 3, K_FOLD = 4, K_NORM = 5, K_COUNT = 6 };
+enum Kind {
+  K_PHASE1 = 0,
+  K_PHASE2 = 1,
+  K_AGG = 2,
+  K_CLOSE = 3,
+  K_FOLD = 4,
+  K_NORM = 5,
+  K_BWD = 6,
+  K_BWD_REDUCE = 7,
+  K_COUNT = 8
+};
 
 struct Timing {
   int capacity = 0;
@@ -706,6 +718,68 @@ ATTNRES_API int attnres_full_stack_forward(const void* x, int L, int C, int64_t 
   AggArgs af{src.data(), L + 1, R, D, Q + (int64_t)L * D, nullptr, eps, y, nullptr, nullptr,
              nullptr, nullptr, nullptr};
   TRY(do_aggregate(fn, dtype, af, st));
+  return ok();
+}
+
+ATTNRES_API size_t attnres_aggregate_backward_workspace_bytes(int64_t R, int64_t D, int dtype) {
+  if (!esize_of(dtype) || R < 0 || D < 1) return 0;
+  return attnres::plan_aggregate_bwd(dtype, R, D).bytes;
+}
+
+ATTNRES_API int attnres_aggregate_backward(const void* const* sources, int n, int64_t R, int64_t D,
+                                           int dtype, const float* w, const float* gamma, float eps,
+                                           const void* dh, float* const* dV, int accumulate,
+                                           float* dw, float* dgamma, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  const char* fn = "attnres_aggregate_backward";
+  TRY(check_shape(fn, R, D, dtype, eps));
+  if (n < 1 || n > ATTNRES_MAX_SOURCES)
+    return fail(ATTNRES_EINVAL, "%s: n = %d outside 1..%d", fn, n, ATTNRES_MAX_SOURCES);
+  // dw / dgamma are produced even for R == 0
+  TRY(check_ptr(fn, "w", w, true));
+  TRY(check_ptr(fn, "gamma", gamma, false));
+  TRY(check_ptr(fn, "dw", dw, true));
+  TRY(check_ptr(fn, "dgamma", dgamma, false));
+  if (dgamma && dgamma == dw) return fail(ATTNRES_EINVAL, "%s: dgamma aliases dw", fn);
+  const BwdPlan pl = attnres::plan_aggregate_bwd(dtype, R, D);
+  if (!pl.supported) return fail(ATTNRES_EUNSUPPORTED, "%s: D = %lld", fn, (long long)D);
+  if (pl.bytes > 0) {
+    TRY(check_ptr(fn, "workspace", workspace, true));
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(ATTNRES_EINVAL, "%s: workspace is not 256-byte aligned", fn);
+    if (workspace_bytes < pl.bytes)
+      return fail(ATTNRES_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn,
+                  workspace_bytes, pl.bytes);
+  }
+  if (R > 0) {
+    if (!sources) return fail(ATTNRES_EINVAL, "%s: sources is NULL", fn);
+    if (!dV) return fail(ATTNRES_EINVAL, "%s: dV is NULL", fn);
+    TRY(check_ptr(fn, "dh", dh, true));
+    for (int i = 0; i < n; ++i) {
+      TRY(check_ptr(fn, "sources[i]", sources[i], true));
+      TRY(check_ptr(fn, "dV[i]", dV[i], true));
+      const void* d = dV[i];
+      if (d == dh || d == w || d == gamma || d == dw || d == dgamma)
+        return fail(ATTNRES_EINVAL, "%s: dV[%d] aliases another argument", fn, i);
+      for (int j = 0; j < n; ++j)
+        if (d == sources[j] || (j < i && d == dV[j]))
+          return fail(ATTNRES_EINVAL, "%s: dV[%d] aliases a source or another dV", fn, i);
+    }
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  BwdArgs a{sources, n, R, D, w, gamma, eps, dh, dV, accumulate, dw, dgamma, workspace};
+  const double rb = (double)R * D * esize_of(dtype);
+  const double gb = (double)R * D * 4 * n * (accumulate ? 2 : 1);
+  hipError_t e = attnres::launch_aggregate_bwd(dtype, a, pl, timed_launch(K_BWD, rb * (n + 1) + gb, st));
+  if (e != hipSuccess) return hip_fail(fn, e);
+  const double pbytes = (double)pl.P * D * 4;
+  if (pl.P2) {
+    e = attnres::launch_bwd_reduce(a, pl, 0, timed_launch(K_BWD_REDUCE, pbytes + pl.P2 * D * 4.0, st));
+    if (e != hipSuccess) return hip_fail(fn, e);
+  }
+  const double fin = (double)(pl.P2 ? pl.P2 : pl.P) * D * 4 + D * 4.0 * ((dgamma ? 2 : 1) * (accumulate ? 2 : 1));
+  e = attnres::launch_bwd_reduce(a, pl, 1, timed_launch(K_BWD_REDUCE, fin, st));
+  if (e != hipSuccess) return hip_fail(fn, e);
   return ok();
 }
 

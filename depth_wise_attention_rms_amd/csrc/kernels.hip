@@ -825,6 +825,381 @@ __global__ __launch_bounds__(512) void aggregate_kernel(AggParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Aggregate backward with recomputation [K3 "Attention Residual" eqs. A1-A3
+// differentiated; the course's fused backward that recomputes the softmax
+// instead of storing it]. Nothing of the forward is kept: per row the scores
+// are recomputed from the sources, and with a_i = softmax(s)_i,
+// g_i = dh . V_i and ds_i = a_i (g_i - sum_j a_j g_j) (dh . h is sum_j a_j g_j,
+// so h itself is never formed):
+//   dV_i = a_i dh + (ds_i / r_i) q~ - (ds_i s_i / (D r_i^2)) V_i
+//   dq~ += (ds_i / r_i) V_i
+// One row reduction yields the 3n sums q~.V_i, V_i.V_i and dh.V_i. With n <= G
+// the sources stay in registers (raw 16-byte vectors) between the reduction
+// and the gradient pass, so each source is read once; beyond G they are
+// streamed twice (groups of G), the per-source statistics kept in LDS.
+// dq~ is summed over rows per (workgroup, row slot) into `partial`, which a
+// fixed-order reduction turns into dw = (sum_rows dq~) * gamma and
+// dgamma = (sum_rows dq~) * w: the summation order depends only on the
+// shape, so the result is deterministic.
+// ---------------------------------------------------------------------------
+struct AggBwdParams {
+  const void* src[64];
+  float* dV[64];       // [R][D] fp32 each
+  int n;
+  int accumulate;      // nonzero: dV_i += gradient
+  const float* w;      // [D]
+  const float* gm;     // [D] or null
+  float eps;
+  const void* dh;      // [R][D] in the I/O dtype
+  float* partial;      // [gridDim.x * RPW][D]
+  Geom g;
+};
+
+// per-source row statistics of the backward: score, 1/r, dh . V
+struct BwdStat {
+  float s, ri, gd;
+};
+
+// A row-uniform value moved into a scalar register (frees a vector register).
+__device__ __forceinline__ float uniformf(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// Opaque to the optimiser: the value must be re-read from these registers,
+// so values derived from it earlier (unpacked copies) are not kept alive.
+__device__ __forceinline__ void pin(uint4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+__device__ __forceinline__ void pin(uint2& v) { asm volatile("" : "+v"(v.x), "+v"(v.y)); }
+
+// Four-element vectors of the backward. A lane's fp32 gradient of one vector
+// is then 16 contiguous bytes, and a wave's gradient store covers 1 KiB with
+// no gaps (with eight-element bf16 vectors each lane would write 32 bytes in
+// two strided halves, which measured 1.6x the algorithmic write traffic).
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+struct Bf16x4 {
+  typedef uint2 raw;
+  static constexpr int kBytes = 8;
+  static __device__ __forceinline__ raw load(const void* p) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+    return make_uint2(v.x, v.y);
+  }
+  static __device__ __forceinline__ raw zero() { return make_uint2(0, 0); }
+  static __device__ __forceinline__ void unpack(const raw& v, float* f) {
+    f[0] = __uint_as_float(v.x << 16);
+    f[1] = __uint_as_float(v.x & 0xffff0000u);
+    f[2] = __uint_as_float(v.y << 16);
+    f[3] = __uint_as_float(v.y & 0xffff0000u);
+  }
+};
+struct F32x4 {
+  typedef uint4 raw;
+  static constexpr int kBytes = 16;
+  static __device__ __forceinline__ raw load(const void* p) { return ld16_stream(p); }
+  static __device__ __forceinline__ raw zero() { return make_uint4(0, 0, 0, 0); }
+  static __device__ __forceinline__ void unpack(const raw& v, float* f) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+};
+
+#ifndef ATTNRES_BWD_DV_NT
+#define ATTNRES_BWD_DV_NT 1  // gradients are written once: non-temporal stores
+#endif
+
+// dV = A dh + B q~ + C x for the 4 elements of one vector, written (or added)
+// as 16 bytes of fp32 at dst.
+template <class F>
+__device__ __forceinline__ void bwd_store_dv(float* __restrict__ dst, const typename F::raw& dhr,
+                                             const float* q, const typename F::raw& xr, float A,
+                                             float B, float C, bool accumulate) {
+  float dh[4], x[4];
+  F::unpack(dhr, dh);
+  F::unpack(xr, x);
+  float o[4];
+  #pragma unroll
+  for (int k = 0; k < 4; ++k) o[k] = A * dh[k] + B * q[k] + C * x[k];
+  if (accumulate) {
+    const uint4 u = ld16_stream(dst);
+    o[0] += __uint_as_float(u.x); o[1] += __uint_as_float(u.y);
+    o[2] += __uint_as_float(u.z); o[3] += __uint_as_float(u.w);
+  }
+  const uint4 u = make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                             __float_as_uint(o[3]));
+#if ATTNRES_BWD_DV_NT
+  st16_stream(dst, u);
+#else
+  st16(dst, u);
+#endif
+}
+
+// dq~ += B x over the 4 elements of one vector
+template <class F>
+__device__ __forceinline__ void bwd_acc_dq(float* dq, const typename F::raw& xr, float B) {
+  float x[4];
+  F::unpack(xr, x);
+  #pragma unroll
+  for (int e = 0; e < 4; ++e) dq[e] += B * x[e];
+}
+
+// Geometry: g.V counts four-element vectors; lane t holds vectors
+// c * 64W + t (c < VPL) of its row.
+#ifndef ATTNRES_BWD_WAVES_PER_EU
+#define ATTNRES_BWD_WAVES_PER_EU 1  // minimum waves per SIMD the register budget must allow
+#endif
+
+template <class F, int VPL, int G, bool RES>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(ATTNRES_BWD_WAVES_PER_EU)))
+void aggregate_bwd_kernel(AggBwdParams p) {
+  extern __shared__ float lds[];
+  typedef typename F::raw raw;
+  constexpr int NV = 3 * G;
+  const Geom& g = p.g;
+  const Lanes ln(g.W);
+  const int64_t rowbytes = (int64_t)g.V * F::kBytes;
+  // per-wave statistics of every source (streamed form only), after the
+  // row-reduction scratch
+  BwdStat* stat = reinterpret_cast<BwdStat*>(lds + (size_t)g.RPW * g.W * NV) +
+                  (size_t)(threadIdx.x >> 6) * 64;
+
+  float q[VPL][4], dq[VPL][4];
+  #pragma unroll
+  for (int c = 0; c < VPL; ++c) {
+    const int vec = c * ln.stride + ln.t;
+    if (vec < g.V) {
+      load_query<4>(p.w, p.gm, (int64_t)vec * 4, q[c]);
+    } else {
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) q[c][e] = 0.f;
+    }
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) dq[c][e] = 0.f;
+  }
+
+  for (int64_t grp = blockIdx.x; grp < g.groups; grp += gridDim.x) {
+    const int64_t row = grp * g.RPW + ln.slot;
+    const bool rv = row < g.R;
+    raw dhr[VPL];
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      const int vec = c * ln.stride + ln.t;
+      dhr[c] = (rv && vec < g.V)
+                   ? F::load(static_cast<const char*>(p.dh) + row * rowbytes + (int64_t)vec * F::kBytes)
+                   : F::zero();
+    }
+
+    // pass 1: the 3 row sums of every source (one group when resident)
+    raw x[G][VPL];
+    float m_run = -FLT_MAX, z_run = 0.f, eg_run = 0.f;  // streamed form: online softmax
+    BwdStat st[G];
+    for (int i0 = 0; i0 < p.n; i0 += G) {
+      #pragma unroll
+      for (int j = 0; j < G; ++j)
+        #pragma unroll
+        for (int c = 0; c < VPL; ++c) {
+          const int vec = c * ln.stride + ln.t;
+          x[j][c] = (rv && i0 + j < p.n && vec < g.V)
+                        ? F::load(static_cast<const char*>(p.src[i0 + j]) + row * rowbytes +
+                                  (int64_t)vec * F::kBytes)
+                        : F::zero();
+        }
+      float red[NV];
+      #pragma unroll
+      for (int k = 0; k < NV; ++k) red[k] = 0.f;
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        float dh[4];
+        F::unpack(dhr[c], dh);
+        #pragma unroll
+        for (int j = 0; j < G; ++j) {
+          float xf[4];
+          F::unpack(x[j][c], xf);
+          #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            red[j] += q[c][e] * xf[e];
+            red[G + j] += xf[e] * xf[e];
+            red[2 * G + j] += dh[e] * xf[e];
+          }
+        }
+      }
+      row_reduce<NV>(red, lds, ln.slot, ln.wr, g.W);
+      #pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const float ri = rsqrtf(uniformf(red[G + j]) * g.invD + p.eps);
+        st[j].ri = uniformf(ri);
+        st[j].s = uniformf(uniformf(red[j]) * ri);
+        st[j].gd = uniformf(red[2 * G + j]);
+      }
+      if (RES) {
+        #pragma unroll
+        for (int j = 0; j < G; ++j)
+          #pragma unroll
+          for (int c = 0; c < VPL; ++c) pin(x[j][c]);
+        #pragma unroll
+        for (int c = 0; c < VPL; ++c) pin(dhr[c]);
+      } else {
+        if (ln.lane == 0) {
+          #pragma unroll
+          for (int j = 0; j < G; ++j)
+            if (i0 + j < p.n) stat[i0 + j] = st[j];
+        }
+        float m_new = m_run;
+        #pragma unroll
+        for (int j = 0; j < G; ++j)
+          if (i0 + j < p.n) m_new = fmaxf(m_new, st[j].s);
+        const float rescale = __expf(m_run - m_new);
+        z_run *= rescale;
+        eg_run *= rescale;
+        #pragma unroll
+        for (int j = 0; j < G; ++j)
+          if (i0 + j < p.n) {
+            const float e = __expf(st[j].s - m_new);
+            z_run += e;
+            eg_run += e * st[j].gd;
+          }
+        m_run = uniformf(m_new);
+        z_run = uniformf(z_run);
+        eg_run = uniformf(eg_run);
+      }
+    }
+    if (!rv) continue;  // uniform per row slot; no barrier follows in this iteration
+
+    if (RES) {
+      // softmax over the n resident sources
+      float m = -FLT_MAX;
+      #pragma unroll
+      for (int j = 0; j < G; ++j)
+        if (j < p.n) m = fmaxf(m, st[j].s);
+      float a[G], z = 0.f;
+      #pragma unroll
+      for (int j = 0; j < G; ++j) {
+        a[j] = j < p.n ? __expf(st[j].s - m) : 0.f;
+        z += a[j];
+      }
+      const float rz = 1.0f / z;
+      float gbar = 0.f;
+      #pragma unroll
+      for (int j = 0; j < G; ++j) {
+        a[j] = uniformf(a[j] * rz);
+        gbar += a[j] * st[j].gd;
+      }
+      #pragma unroll
+      for (int j = 0; j < G; ++j) {
+        if (j >= p.n) continue;
+        // one source at a time: keeps its unpacked values short-lived
+        __builtin_amdgcn_sched_barrier(0);
+        const float ds = a[j] * (st[j].gd - gbar);
+        const float B = uniformf(ds * st[j].ri);
+        const float C = uniformf(-B * st[j].s * st[j].ri * g.invD);
+        float* dst = p.dV[j] + row * g.D;
+        #pragma unroll
+        for (int c = 0; c < VPL; ++c) {
+          const int vec = c * ln.stride + ln.t;
+          if (vec < g.V) {
+            bwd_store_dv<F>(dst + (int64_t)vec * 4, dhr[c], q[c], x[j][c], a[j], B, C,
+                            p.accumulate != 0);
+            bwd_acc_dq<F>(dq[c], x[j][c], B);
+          }
+        }
+      }
+    } else {
+      // pass 2: stream the sources again with the statistics of pass 1
+      const float rz = 1.0f / z_run;
+      const float gbar = eg_run * rz;
+      for (int i = 0; i < p.n; ++i) {
+        const BwdStat si = stat[i];
+        const float a = uniformf(__expf(si.s - m_run) * rz);
+        const float ds = a * (si.gd - gbar);
+        const float B = uniformf(ds * si.ri);
+        const float C = uniformf(-B * si.s * si.ri * g.invD);
+        const char* srow = static_cast<const char*>(p.src[i]) + row * rowbytes;
+        float* dst = p.dV[i] + row * g.D;
+        raw xr[VPL];
+        #pragma unroll
+        for (int c = 0; c < VPL; ++c) {
+          const int vec = c * ln.stride + ln.t;
+          xr[c] = vec < g.V ? F::load(srow + (int64_t)vec * F::kBytes) : F::zero();
+        }
+        #pragma unroll
+        for (int c = 0; c < VPL; ++c) {
+          const int vec = c * ln.stride + ln.t;
+          if (vec < g.V) {
+            bwd_store_dv<F>(dst + (int64_t)vec * 4, dhr[c], q[c], xr[c], a, B, C,
+                            p.accumulate != 0);
+            bwd_acc_dq<F>(dq[c], xr[c], B);
+          }
+        }
+      }
+    }
+  }
+
+  // this (workgroup, row slot)'s sum of dq~ over its rows
+  float* prow = p.partial + ((int64_t)blockIdx.x * g.RPW + ln.slot) * g.D;
+  #pragma unroll
+  for (int c = 0; c < VPL; ++c) {
+    const int vec = c * ln.stride + ln.t;
+    if (vec < g.V)
+      st16(prow + (int64_t)vec * 4, make_uint4(__float_as_uint(dq[c][0]), __float_as_uint(dq[c][1]),
+                                               __float_as_uint(dq[c][2]), __float_as_uint(dq[c][3])));
+  }
+}
+
+// Column sums of a [rows][D] fp32 matrix over consecutive row chunks, each in
+// ascending row order: out[k][d] = sum of in[r][d] for r in chunk k. With
+// FINISH the single chunk's sum t gives dw = t * gamma (t without a gain) and
+// dgamma = t * w, written or added. One thread owns four columns.
+template <bool FINISH>
+__global__ __launch_bounds__(256) void bwd_colsum_kernel(const float* __restrict__ in,
+                                                         int64_t rows, int64_t D, int64_t chunk,
+                                                         float* __restrict__ out,
+                                                         const float* __restrict__ w,
+                                                         const float* __restrict__ gm,
+                                                         float* __restrict__ dw,
+                                                         float* __restrict__ dgamma,
+                                                         int accumulate) {
+  const int64_t d = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (d >= D) return;
+  const int64_t r0 = (int64_t)blockIdx.y * chunk;
+  const int64_t r1 = r0 + chunk < rows ? r0 + chunk : rows;
+  float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+  int64_t r = r0;
+  for (; r + 4 <= r1; r += 4) {
+    const float4 a = ldf4(in + r * D + d), b = ldf4(in + (r + 1) * D + d);
+    const float4 c = ldf4(in + (r + 2) * D + d), e = ldf4(in + (r + 3) * D + d);
+    t.x += a.x; t.y += a.y; t.z += a.z; t.w += a.w;
+    t.x += b.x; t.y += b.y; t.z += b.z; t.w += b.w;
+    t.x += c.x; t.y += c.y; t.z += c.z; t.w += c.w;
+    t.x += e.x; t.y += e.y; t.z += e.z; t.w += e.w;
+  }
+  for (; r < r1; ++r) {
+    const float4 a = ldf4(in + r * D + d);
+    t.x += a.x; t.y += a.y; t.z += a.z; t.w += a.w;
+  }
+  if (!FINISH) {
+    *reinterpret_cast<float4*>(out + (int64_t)blockIdx.y * D + d) = t;
+    return;
+  }
+  const float4 gv = gm ? ldf4(gm + d) : make_float4(1.f, 1.f, 1.f, 1.f);
+  float4 o = make_float4(t.x * gv.x, t.y * gv.y, t.z * gv.z, t.w * gv.w);
+  if (accumulate) {
+    const float4 prev = ldf4(dw + d);
+    o.x += prev.x; o.y += prev.y; o.z += prev.z; o.w += prev.w;
+  }
+  *reinterpret_cast<float4*>(dw + d) = o;
+  if (dgamma) {
+    const float4 wv = ldf4(w + d);
+    float4 og = make_float4(t.x * wv.x, t.y * wv.y, t.z * wv.z, t.w * wv.w);
+    if (accumulate) {
+      const float4 prev = ldf4(dgamma + d);
+      og.x += prev.x; og.y += prev.y; og.z += prev.z; og.w += prev.w;
+    }
+    *reinterpret_cast<float4*>(dgamma + d) = og;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Phase 2 (one intra-block merge step) [K3 9.4 step 2, OS2, single-source
 // triple; RH 4.2 Phase 2]: p = p_prev + v_prev rounded to the I/O dtype (or
 // p = v_prev on the first merge), the score of the rounded p, then
@@ -1283,6 +1658,130 @@ hipError_t launch_close(int dtype, const void* p, const void* v, void* b, int64_
   if (blocks > 8192) blocks = 8192;
   if (dtype == 1) return launch(L, close_kernel<Bf16>, dim3((unsigned)blocks), dim3(256), 0, p, v, b, nvec);
   return launch(L, close_kernel<F32>, dim3((unsigned)blocks), dim3(256), 0, p, v, b, nvec);
+}
+
+// ---------------------------------------------------------------------------
+// aggregate backward: plan (geometry, grid, workspace) and launches
+// ---------------------------------------------------------------------------
+#ifndef ATTNRES_BWD_MAX_GROUPS
+#define ATTNRES_BWD_MAX_GROUPS 1024  // workgroups of the backward (bounds the dq~ partials)
+#endif
+#ifndef ATTNRES_BWD_CHUNK
+#define ATTNRES_BWD_CHUNK 32  // partial rows summed per first-stage thread
+#endif
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+#ifndef ATTNRES_BWD_BF16_VPL
+#define ATTNRES_BWD_BF16_VPL 4  // four-element bf16 vectors per lane (32 bytes of a source)
+#endif
+#ifndef ATTNRES_BWD_F32_VPL
+#define ATTNRES_BWD_F32_VPL 2  // four-element fp32 vectors per lane (32 bytes of a source)
+#endif
+
+// Four-element vectors (V = D / 4 per row): VPL of them per lane, doubled
+// (then quadrupled) for rows too wide for eight waves.
+static Geom bwd_geom(int dtype, int64_t R, int64_t D, int* vpl) {
+  int v = dtype == 1 ? ATTNRES_BWD_BF16_VPL : ATTNRES_BWD_F32_VPL;
+  Geom g = make_geom(R, D, 4, v, 4);
+  while (g.W > 8 && v < 16) {
+    v *= 2;
+    g = make_geom(R, D, 4, v, 4);
+  }
+  *vpl = v;
+  return g;
+}
+
+BwdPlan plan_aggregate_bwd(int dtype, int64_t R, int64_t D) {
+  BwdPlan pl;
+  int vpl = 0;
+  const Geom g = bwd_geom(dtype, R, D, &vpl);
+  pl.vpl = vpl;
+  pl.supported = g.W <= 8;
+  pl.grid = (unsigned)(g.groups < ATTNRES_BWD_MAX_GROUPS ? g.groups : ATTNRES_BWD_MAX_GROUPS);
+  pl.P = (int64_t)pl.grid * g.RPW;
+  pl.chunk = ATTNRES_BWD_CHUNK;
+  pl.P2 = pl.P > pl.chunk ? (pl.P + pl.chunk - 1) / pl.chunk : 0;
+  pl.partial_bytes = align256((size_t)pl.P * D * 4);
+  pl.bytes = pl.partial_bytes + align256((size_t)pl.P2 * D * 4);
+  return pl;
+}
+
+template <class T, int VPL, int G, bool RES>
+static hipError_t launch_bwd_t(const AggBwdParams& p, unsigned grid, const Launch& L) {
+  const int waves = p.g.W * p.g.RPW;
+  const size_t lds = (size_t)p.g.RPW * p.g.W * 3 * G * sizeof(float) +
+                     (RES ? 0 : (size_t)waves * 64 * sizeof(BwdStat));
+  return launch(L, aggregate_bwd_kernel<T, VPL, G, RES>, dim3(grid), dim3(64 * waves), lds, p);
+}
+
+// n <= G sources stay resident; wider rows (more vectors per lane) keep
+// groups of four
+template <class F, int VPL, bool WIDE>
+static hipError_t launch_bwd_vpl(const AggBwdParams& p, int n, unsigned grid, const Launch& L) {
+  if constexpr (WIDE) {
+    if (n <= 4) return launch_bwd_t<F, VPL, 4, true>(p, grid, L);
+    return launch_bwd_t<F, VPL, 4, false>(p, grid, L);
+  } else {
+    // resident groups; sizes measured at 16384 rows of 4096 bf16: exact
+    // groups for 1-4 and 7, a group of 8 for 5 and 6 (exact groups of 5 and 6
+    // ran no faster, 6 about 11% slower)
+    switch (n) {
+      case 1: return launch_bwd_t<F, VPL, 1, true>(p, grid, L);
+      case 2: return launch_bwd_t<F, VPL, 2, true>(p, grid, L);
+      case 3: return launch_bwd_t<F, VPL, 3, true>(p, grid, L);
+      case 4: return launch_bwd_t<F, VPL, 4, true>(p, grid, L);
+      case 7: return launch_bwd_t<F, VPL, 7, true>(p, grid, L);
+      case 5:
+      case 6:
+      case 8: return launch_bwd_t<F, VPL, 8, true>(p, grid, L);
+      default: break;
+    }
+    if (n <= 16) return launch_bwd_t<F, VPL, 16, true>(p, grid, L);
+    return launch_bwd_t<F, VPL, 8, false>(p, grid, L);
+  }
+}
+
+template <class F, int SMALL>
+static hipError_t launch_bwd_dt(const BwdArgs& a, const BwdPlan& pl, const Launch& L) {
+  AggBwdParams p;
+  for (int i = 0; i < 64; ++i) {
+    p.src[i] = i < a.n ? a.src[i] : nullptr;
+    p.dV[i] = i < a.n ? a.dV[i] : nullptr;
+  }
+  p.n = a.n; p.accumulate = a.accumulate;
+  p.w = a.w; p.gm = a.g; p.eps = a.eps; p.dh = a.dh;
+  p.partial = static_cast<float*>(a.workspace);
+  int vpl = 0;
+  p.g = bwd_geom(F::kBytes == 8 ? 1 : 0, a.R, a.D, &vpl);
+  if (vpl == SMALL) return launch_bwd_vpl<F, SMALL, false>(p, a.n, pl.grid, L);
+  if (vpl == 2 * SMALL) return launch_bwd_vpl<F, 2 * SMALL, true>(p, a.n, pl.grid, L);
+  if constexpr (SMALL * 4 <= 8) {
+    if (vpl == 4 * SMALL) return launch_bwd_vpl<F, 4 * SMALL, true>(p, a.n, pl.grid, L);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_aggregate_bwd(int dtype, const BwdArgs& a, const BwdPlan& pl, const Launch& L) {
+  if (pl.grid == 0) return hipSuccess;
+  return dtype == 1 ? launch_bwd_dt<Bf16x4, ATTNRES_BWD_BF16_VPL>(a, pl, L)
+                    : launch_bwd_dt<F32x4, ATTNRES_BWD_F32_VPL>(a, pl, L);
+}
+
+hipError_t launch_bwd_reduce(const BwdArgs& a, const BwdPlan& pl, int stage, const Launch& L) {
+  const float* partial = static_cast<const float*>(a.workspace);
+  float* stage1 = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + pl.partial_bytes);
+  const unsigned bx = (unsigned)((a.D / 4 + 255) / 256);
+  if (stage == 0) {
+    if (pl.P2 == 0) return hipSuccess;
+    return launch(L, bwd_colsum_kernel<false>, dim3(bx, (unsigned)pl.P2), dim3(256), 0, partial,
+                  pl.P, a.D, pl.chunk, stage1, (const float*)nullptr, (const float*)nullptr,
+                  (float*)nullptr, (float*)nullptr, 0);
+  }
+  const float* in = pl.P2 ? stage1 : partial;
+  const int64_t rows = pl.P2 ? pl.P2 : pl.P;
+  return launch(L, bwd_colsum_kernel<true>, dim3(bx, 1), dim3(256), 0, in, rows, a.D, rows,
+                (float*)nullptr, a.w, a.g, a.dw, a.dgamma, a.accumulate);
 }
 
 }  // namespace attnres

@@ -69,6 +69,42 @@ struct Phase2Args {
   int64_t R, D;
 };
 
+// Aggregate backward: sources, query and gain as in AggArgs, upstream gradient
+// dh [R][D] in the I/O dtype, fp32 gradients dV[i] [R][D], dw [D] and dgamma
+// [D] (or null), written or (accumulate != 0) added; workspace holds the
+// per-workgroup dq~ partials and the first reduction stage (BwdPlan::bytes).
+struct BwdArgs {
+  const void* const* src;
+  int n;
+  int64_t R, D;
+  const float* w;
+  const float* g;
+  float eps;
+  const void* dh;
+  float* const* dV;
+  int accumulate;
+  float* dw;
+  float* dgamma;
+  void* workspace;
+};
+
+struct BwdPlan {
+  bool supported;
+  int vpl;
+  unsigned grid;         // workgroups of the main kernel (0 when R == 0)
+  int64_t P;             // dq~ partial rows
+  int64_t chunk;         // rows per first-stage sum
+  int64_t P2;            // first-stage rows (0: the final stage reads the partials)
+  size_t partial_bytes;  // 256-aligned size of the partials
+  size_t bytes;          // workspace bytes
+};
+
+BwdPlan plan_aggregate_bwd(int dtype, int64_t R, int64_t D);
+hipError_t launch_aggregate_bwd(int dtype, const BwdArgs& a, const BwdPlan& pl, const Launch& L);
+// stage 0: partial rows -> chunk sums (no-op when P2 == 0); stage 1: final
+// sum, dw and dgamma
+hipError_t launch_bwd_reduce(const BwdArgs& a, const BwdPlan& pl, int stage, const Launch& L);
+
 hipError_t launch_fold(const float* w, const float* g, float* q, int64_t count, const Launch& L);
 hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L);
 bool phase1_supported(int dtype, int n, int S, int64_t D);

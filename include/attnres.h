@@ -266,12 +266,49 @@ int attnres_full_stack_forward(const void* x, int L, int C, int64_t R, int64_t D
                                size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * attnres_aggregate_backward -- gradients of one aggregate (attnres_aggregate)
+ * for an upstream gradient dh, with recomputation: no forward state is kept;
+ * the scores and weights are recomputed from the sources [K3 9.1 (A1)-(A3)
+ * differentiated; WC "Depth attention & online merge reference" and "Public
+ * implementation boundary": the fused operator computes forward and backward
+ * with online softmax and recomputation]. Per row, with r_i = sqrt(mean_d
+ * v_i^2 + eps), s_i = q~ . v_i / r_i, a = softmax(s), g_i = dh . v_i and
+ * ds_i = a_i (g_i - sum_j a_j g_j):
+ *     dV_i  = a_i dh + ds_i (q~ / r_i - s_i v_i / (D r_i^2))
+ *     dq~   = sum over rows of sum_i ds_i v_i / r_i
+ *     dw    = dq~ * gamma (dq~ without a gain),  dgamma = dq~ * w
+ * (the fold q~ = w * gamma is differentiated as an exact product).
+ *   sources (host) : n device pointers [R,D] dtype (1 <= n <= 64)
+ *   w, gamma       : [D] fp32 (gamma NULL means ones)
+ *   dh             : [R,D] dtype, the gradient of the loss w.r.t. the output
+ *   dV (host)      : n device pointers [R,D] fp32; dV[i] receives the gradient
+ *                    of sources[i]. They must be distinct and alias no input.
+ *   dw             : [D] fp32, required; dgamma : [D] fp32 or NULL (not wanted)
+ *   accumulate     : 0 writes the gradients, nonzero adds them to dV, dw and
+ *                    dgamma (for a source, query or gain used by several
+ *                    aggregates)
+ *   workspace      : device scratch of attnres_aggregate_backward_workspace_bytes
+ *                    (R, D, dtype) bytes, 256-byte aligned, owned by the caller
+ *                    and not read before it is written (EWORKSPACE if smaller).
+ *   Arithmetic is fp32; gradients stay fp32 so that sums over many aggregates
+ *   do not round. The sum over rows runs in a fixed order that depends only
+ *   on (R, D, dtype): results are deterministic. With R == 0, dw and dgamma
+ *   are still written (zeros) or left unchanged (accumulate).
+ * ------------------------------------------------------------------------- */
+size_t attnres_aggregate_backward_workspace_bytes(int64_t R, int64_t D, int dtype);
+int attnres_aggregate_backward(const void* const* sources, int n, int64_t R, int64_t D, int dtype,
+                               const float* w, const float* gamma, float eps, const void* dh,
+                               float* const* dV, int accumulate, float* dw, float* dgamma,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Optional launch timing (instrumentation for benchmarks; off by default).
  * attnres_timing_enable(capacity) makes this thread's subsequent launches
  * record a HIP event pair around each kernel on its stream, for up to
  * `capacity` launches (0 disables and releases the events). The library keeps
  * per-kind totals: kind 0 Phase 1, 1 Phase 2, 2 aggregate, 3 block close,
- * 4 query fold, 5 standalone output norm. attnres_timing_read synchronises
+ * 4 query fold, 5 standalone output norm, 6 aggregate backward (main
+ * kernel), 7 its reduction over rows. attnres_timing_read synchronises
  * the recorded events and returns, for `kind`, the number of timed launches,
  * their summed duration in milliseconds and their summed algorithmic bytes
  * (inputs read once plus outputs written once, queries excluded).
