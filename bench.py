@@ -136,6 +136,32 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_gib: float
     return out
 
 
+def cpu_baseline(ds, wl, seconds: float, chunk: int = 2048) -> dict:
+    """The fp64 oracle's naive forward on consecutive chunks of token rows
+    (cycling over the workload) until ``seconds`` of CPU work have run."""
+    import numpy as np
+    import oracle
+    from depth_wise_attention_rms_amd.workload import EPS
+
+    if not os.path.exists(oracle.LIBRARY):
+        oracle.build()
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    done, spent, start = 0, 0.0, 0
+    while done == 0 or spent < seconds:
+        rows = np.arange(start, min(start + chunk, wl.R))
+        start = 0 if start + chunk >= wl.R else start + chunk
+        xr, vr = ds.host_rows(rows)
+        c0 = time.perf_counter()
+        oracle.block_stack(xr, vr, ds.W_host, wl.S, eps=EPS, want_h=False, nthreads=cores)
+        spent += time.perf_counter() - c0
+        done += len(rows)
+        del xr, vr
+    return {"value": round(done / spent, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} token rows in chunks of {chunk} consecutive rows cycling over the "
+                      f"{wl.R} of the workload, full {wl.L}-sublayer naive forward in fp64 "
+                      f"({cores} threads), {spent:.2f} s of CPU time (host copies excluded)"}
+
+
 def calibration_copy(gib: float):
     """A plain copy kernel of known size (read once, written once), so that
     hardware counters of the same run can be scaled to bytes."""
@@ -405,7 +431,7 @@ def main() -> int:
     wall_ms = (t1 - t0) * 1e3 / args.steps
     gpu_ms = ev0.elapsed_time(ev1) / args.steps
     kinds = {}
-    for k in ("phase1", "phase2", "aggregate", "close", "fold", "norm"):
+    for k in ("phase1", "phase1_stats", "phase2", "aggregate", "close", "fold", "norm"):
         n, ms, byts = binding.attnres_timing_read(k)
         if n:
             n_step = n / n_timed
@@ -422,7 +448,8 @@ def main() -> int:
     # the dominant kernel: Phase 2 in a Block stack, else the kind with the most time per step
     dom_kind = "phase2" if "phase2" in kinds else max(kinds, key=lambda k: kinds[k]["ms_per_step"])
     dom = kinds[dom_kind]
-    dom_name = {"phase1": "phase1_mfma_kernel", "phase2": "phase2_kernel", "aggregate": "aggregate_kernel",
+    dom_name = {"phase1": "phase1_mfma_kernel", "phase1_stats": "phase1_single_kernel",
+                "phase2": "phase2_kernel", "aggregate": "aggregate_kernel",
                 "norm": "rmsnorm_kernel", "close": "close_kernel", "fold": "fold_kernel"}[dom_kind]
     traffic = measured_traffic(wl.name) if dom_kind == "phase2" and not norm else None
     roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(dom["GBps"], 1),
