@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(PKG, "libattnres.so")
 ATTNRES_F32, ATTNRES_BF16 = 0, 1
 STATUS = {0: "ok", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP", -5: "ECALLBACK"}
 TIMING_KINDS = {"phase1": 0, "phase2": 1, "aggregate": 2, "close": 3, "fold": 4, "norm": 5,
-                "backward": 6, "backward_reduce": 7}
+                "backward": 6, "backward_reduce": 7, "phase1_stats": 8}
 
 EXPORTS = (
     "attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge",

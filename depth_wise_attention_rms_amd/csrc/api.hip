@@ -88,7 +88,8 @@ enum Kind {
   K_NORM = 5,
   K_BWD = 6,
   K_BWD_REDUCE = 7,
-  K_COUNT = 8
+  K_PHASE1_STATS = 8,
+  K_COUNT = 9
 };
 
 struct Timing {
@@ -157,9 +158,10 @@ int do_phase1(const char* fn, int dtype, const Phase1Args& a, hipStream_t st) {
   const int64_t row_bytes = a.D * esize_of(dtype);
   if (attnres::phase1_supported(dtype, a.n, a.S, a.D)) {
     const double rb = (double)a.R * row_bytes;
-    const double bytes = rb * (a.n + a.S) + (double)a.R * a.S * ((a.m_out ? 4 : 0) + 4) +
+    const double bytes = rb * (a.n + (a.out ? a.S : 0)) + (double)a.R * a.S * ((a.m_out ? 4 : 0) + 4) +
                          close_bytes(rb, a.close_p, a.close_v);
-    hipError_t e = attnres::launch_phase1(dtype, a, timed_launch(K_PHASE1, bytes, st));
+    hipError_t e = attnres::launch_phase1(dtype, a,
+                                          timed_launch(a.out ? K_PHASE1 : K_PHASE1_STATS, bytes, st));
     return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
   }
   // More sources than the register-resident pass holds: close separately,
@@ -538,21 +540,29 @@ int stack_forward(const char* fn, const void* x, int L, int S, int64_t R, int64_
       }
       continue;
     }
-    // Phase 1: the block's Sk queries over [b_0 .. b_k] in one pass
-    Phase1Args a1{src.data(), n, R, D, Qk, nullptr, Sk, eps, O, M, LSE, close_p, close_v, close_b};
+    // Phase 1: the block's Sk queries over [b_0 .. b_k] in one pass. With the
+    // embedding as the only source every weight is exactly 1, so each output
+    // o_s is b_0 itself: only the statistics are computed and b_0 stands in
+    // for the outputs.
+    const bool one_source = n == 1 && !close_v && attnres::phase1_stats_supported(dtype, 1, Sk, D);
+    auto o_slice = [&](int j) -> const void* {
+      return one_source ? src[0] : static_cast<const void*>(O + (int64_t)j * tensor_bytes);
+    };
+    Phase1Args a1{src.data(), n, R, D, Qk, nullptr, Sk, eps, one_source ? nullptr : O, M, LSE,
+                  close_p, close_v, close_b};
     TRY(do_phase1(fn, dtype, a1, st));
     const void* v_first = nullptr;
     if (nm.on) {
-      TRY(normed(start, O));
+      TRY(normed(start, o_slice(0)));
       TRY(call(start, H, &v_first));
     } else {
-      TRY(call(start, O, &v_first));  // h_start = o_0: no partial yet
+      TRY(call(start, o_slice(0), &v_first));  // h_start = o_0: no partial yet
     }
     const void* p_cur = v_first;    // p_1 = v_start (aliased, no copy)
     const void* v_prev = v_first;
     for (int j = 1; j < Sk; ++j) {
       const int l = start + j;
-      Phase2Args a2{O + (int64_t)j * tensor_bytes, LSE + (int64_t)j * R, Q + (int64_t)(l - 1) * D,
+      Phase2Args a2{o_slice(j), LSE + (int64_t)j * R, Q + (int64_t)(l - 1) * D,
                     nullptr, eps, j == 1 ? nullptr : p_cur, v_prev, j == 1 ? nullptr : P,
                     nm.on ? nullptr : H,
                     nm.on && nm.Gamma_f ? nm.Gamma_f + (int64_t)(l - 1) * D : nullptr, nm.eps_f,
@@ -700,16 +710,22 @@ ATTNRES_API int attnres_full_stack_forward(const void* x, int L, int C, int64_t 
       src.push_back(v);
       continue;
     }
-    Phase1Args a1{src.data(), n, R, D, Qk, nullptr, Ck, eps, O, M, LSE, nullptr, nullptr, nullptr};
+    // the first chunk sees only the embedding: its outputs are x itself
+    const bool one_source = n == 1 && attnres::phase1_stats_supported(dtype, 1, Ck, D);
+    auto o_slice = [&](int j) -> const void* {
+      return one_source ? src[0] : static_cast<const void*>(O + (int64_t)j * tensor_bytes);
+    };
+    Phase1Args a1{src.data(), n, R, D, Qk, nullptr, Ck, eps, one_source ? nullptr : O, M, LSE,
+                  nullptr, nullptr, nullptr};
     TRY(do_phase1(fn, dtype, a1, st));
     const void* v = nullptr;
-    TRY(call(s0, O, &v));  // the first sublayer of the chunk: h = o_0
+    TRY(call(s0, o_slice(0), &v));  // the first sublayer of the chunk: h = o_0
     src.push_back(v);
     for (int j = 1; j < Ck; ++j) {
       const int l = s0 + j;
       // merge (lse_j, o_j) with the chunk's outputs v_{s0} .. v_{l-1}
       AggArgs am{src.data() + n, j, R, D, Q + (int64_t)(l - 1) * D, nullptr, eps, H, nullptr, nullptr,
-                 nullptr, nullptr, nullptr, O + (int64_t)j * tensor_bytes, LSE + (int64_t)j * R};
+                 nullptr, nullptr, nullptr, o_slice(j), LSE + (int64_t)j * R};
       TRY(do_aggregate(fn, dtype, am, st));
       TRY(call(l, H, &v));
       src.push_back(v);

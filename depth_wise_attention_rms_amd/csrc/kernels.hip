@@ -24,6 +24,16 @@
 
 namespace attnres {
 
+// Write target of lanes that own no element (past a ragged row's end, or a
+// row past the last): such a lane stores here instead of skipping the store,
+// so stores need no exec-mask branch, which would make the compiler wait for
+// every outstanding memory operation at each one. Never read.
+__device__ __attribute__((aligned(256))) unsigned char g_store_sink[256];
+
+__device__ __forceinline__ char* store_target(bool owns, char* p) {
+  return owns ? p : reinterpret_cast<char*>(g_store_sink);
+}
+
 // Row geometry of one launch, computed on the host.
 struct Geom {
   int64_t R;       // token rows
@@ -219,6 +229,7 @@ __global__ __launch_bounds__(512) void phase1_kernel(Phase1Params p) {
               if (p.m_out) p.m_out[(int64_t)s * g.R + row] = m;
               p.lse_out[(int64_t)s * g.R + row] = m + __logf(z);
             }
+            if (!p.out) continue;  // statistics only
             char* orow = static_cast<char*>(p.out) + ((int64_t)s * g.R + row) * rowbytes;
             #pragma unroll
             for (int c = 0; c < VPL; ++c) {
@@ -237,6 +248,94 @@ __global__ __launch_bounds__(512) void phase1_kernel(Phase1Params p) {
           }
         }
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase-1 statistics of a block whose only source is the embedding b_0
+// [K3 9.4 step 1 with one source]: every softmax weight is exactly 1, so each
+// output would be b_0 itself and is not formed; only the scores of b_0 under
+// the S <= SQ queries are computed, and m = lse = score (the log of a unit
+// denominator is 0). The folded queries stay in registers for every row, and
+// the next row's vectors are loaded while the current row reduces.
+// ---------------------------------------------------------------------------
+template <class T, int VPL, int SQ, int PD>
+__global__ __launch_bounds__(512) void phase1_single_kernel(Phase1Params p) {
+  extern __shared__ float lds[];
+  constexpr int EPV = T::kEPV;
+  constexpr int NV = SQ + 1;
+  const Geom& g = p.g;
+  const Lanes ln(g.W);
+  const int64_t rowbytes = (int64_t)g.V * 16;
+
+  float q[SQ][VPL][EPV];
+  #pragma unroll
+  for (int s = 0; s < SQ; ++s)
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      const int vec = c * ln.stride + ln.t;
+      if (s < p.S && vec < g.V) {
+        load_query<EPV>(p.Wq, p.G, (int64_t)s * g.D + (int64_t)vec * EPV, q[s][c]);
+      } else {
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) q[s][c][e] = 0.f;
+      }
+    }
+
+  // Loads are unconditional (a row past the end reads row 0, a lane past the
+  // row's end reads vector 0, and both are discarded), so no branch hides
+  // them from the compiler's wait counting and the prefetch stays in flight.
+  auto load_row = [&](int64_t grp, uint4* dst) {
+    const int64_t row = grp * g.RPW + ln.slot;
+    const int64_t rr = (grp < g.groups && row < g.R) ? row : 0;
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      const int vec = c * ln.stride + ln.t;
+      dst[c] = ld16_stream(static_cast<const char*>(p.src[0]) + rr * rowbytes +
+                           (int64_t)(vec < g.V ? vec : 0) * 16);
+    }
+  };
+  // the next PD rows of this workgroup are in flight while a row reduces
+  uint4 ahead[PD][VPL];
+  #pragma unroll
+  for (int d = 0; d < PD; ++d) load_row(blockIdx.x + (int64_t)d * gridDim.x, ahead[d]);
+  for (int64_t grp = blockIdx.x; grp < g.groups; grp += gridDim.x) {
+    const int64_t row = grp * g.RPW + ln.slot;
+    uint4 cur[VPL];
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) cur[c] = ahead[0][c];
+    #pragma unroll
+    for (int d = 0; d + 1 < PD; ++d)
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) ahead[d][c] = ahead[d + 1][c];
+    load_row(grp + (int64_t)PD * gridDim.x, ahead[PD - 1]);
+    float red[NV];
+    #pragma unroll
+    for (int k = 0; k < NV; ++k) red[k] = 0.f;
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      const bool in_row = c * ln.stride + ln.t < g.V;
+      float x[EPV];
+      T::unpack(cur[c], x);
+      #pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        x[e] = in_row ? x[e] : 0.f;
+        red[SQ] += x[e] * x[e];
+        #pragma unroll
+        for (int s = 0; s < SQ; ++s) red[s] += q[s][c][e] * x[e];
+      }
+    }
+    row_reduce<NV>(red, lds, ln.slot, ln.wr, g.W);
+    if (row < g.R && ln.t < SQ && ln.t < p.S) {
+      // lane s writes query s's statistics
+      float dot = red[0];
+      #pragma unroll
+      for (int s = 1; s < SQ; ++s)
+        if (ln.t == s) dot = red[s];
+      const float sc = dot * rsqrtf(red[SQ] * g.invD + p.eps);
+      if (p.m_out) p.m_out[(int64_t)ln.t * g.R + row] = sc;
+      p.lse_out[(int64_t)ln.t * g.R + row] = sc;
     }
   }
 }
@@ -618,8 +717,9 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
     // 8 (r / 4) + 4 (l / 32) + r % 4: query 2 (r / 4) + l / 32, part r % 4 --
     // every lane ends with 8 consecutive outputs of 4 queries, stored as
     // 16-byte vectors. Non-finite sources make the whole wave's outputs
-    // unspecified (a zero weight times Inf is NaN).
-    if (owner) {
+    // unspecified (a zero weight times Inf is NaN). Without an output buffer
+    // (statistics only) the pass is skipped and nothing is counted.
+    if (owner && p.out != nullptr) {
       uint4 x[8];
       #pragma unroll
       for (int k = 0; k < 8; ++k)
@@ -729,6 +829,37 @@ __global__ __launch_bounds__(512) void aggregate_kernel(AggParams p) {
   for (int64_t grp = blockIdx.x; grp < g.groups; grp += gridDim.x) {
     const int64_t row = grp * g.RPW + ln.slot;
     const bool rv = row < g.R;
+    // loads are unconditional (a row past the end reads row 0, a lane past
+    // the row's end reads vector 0; both are discarded), so no branch hides
+    // them from the compiler's wait counting and a group's loads are waited
+    // for together
+    const int64_t base = (rv ? row : 0) * rowbytes;
+    int64_t voff[VPL];
+    bool in_row[VPL];
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      const int vec = c * ln.stride + ln.t;
+      in_row[c] = vec < g.V;
+      voff[c] = base + (int64_t)(in_row[c] ? vec : 0) * 16;
+    }
+    // the closing source b = round(p + v) (or v), formed and stored before
+    // the group loads
+    uint4 bcl[VPL];
+    if (has_close) {
+      const char* pp = static_cast<const char*>(p.cl.p ? p.cl.p : p.cl.v);
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        const uint4 v = ld16_stream(static_cast<const char*>(p.cl.v) + voff[c]);
+        const uint4 a = ld16_stream(pp + voff[c]);
+        float fa[EPV], fv[EPV];
+        T::unpack(a, fa);
+        T::unpack(v, fv);
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) fa[e] = p.cl.p ? fa[e] + fv[e] : fv[e];
+        bcl[c] = T::pack(fa);  // rounded to the I/O dtype, as the block sum is stored
+        if (rv && in_row[c]) st16_stream(static_cast<char*>(p.cl.b) + voff[c], bcl[c]);
+      }
+    }
     float num[VPL][EPV];
     float m_run = -FLT_MAX, z_run = 0.f;
     if (p.o_init) {
@@ -736,13 +867,12 @@ __global__ __launch_bounds__(512) void aggregate_kernel(AggParams p) {
       // single-triple form of a normalised group [K3 9.4 (OS1)]
       #pragma unroll
       for (int c = 0; c < VPL; ++c) {
-        const int vec = c * ln.stride + ln.t;
-        const uint4 u = (rv && vec < g.V)
-                            ? ld16_stream(static_cast<const char*>(p.o_init) + row * rowbytes + (int64_t)vec * 16)
-                            : make_uint4(0, 0, 0, 0);
+        const uint4 u = ld16_stream(static_cast<const char*>(p.o_init) + voff[c]);
         T::unpack(u, num[c]);
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) num[c][e] = in_row[c] ? num[c][e] : 0.f;
       }
-      m_run = rv ? p.lse_init[row] : 0.f;
+      m_run = p.lse_init[rv ? row : 0];
       z_run = 1.f;
     } else {
       #pragma unroll
@@ -753,16 +883,28 @@ __global__ __launch_bounds__(512) void aggregate_kernel(AggParams p) {
 
     for (int i0 = 0; i0 < p.n; i0 += G) {
       float x[G][VPL][EPV];
+      uint4 u[G][VPL];
       #pragma unroll
       for (int j = 0; j < G; ++j) {
+        // slots past n and the closing source (already in bcl) read the
+        // sink's first 16 bytes, which stay in cache
+        const int i = i0 + j;
+        const bool live = i < p.n && !(has_close && i == p.n - 1);
+        const char* sp = static_cast<const char*>(p.src[live ? i : 0]);
+        #pragma unroll
+        for (int c = 0; c < VPL; ++c)
+          u[j][c] = ld16_stream(live ? sp + voff[c] : reinterpret_cast<const char*>(g_store_sink));
+      }
+      #pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const int i = i0 + j;
+        const bool closing = has_close && i == p.n - 1;
         #pragma unroll
         for (int c = 0; c < VPL; ++c) {
-          const int vec = c * ln.stride + ln.t;
-          uint4 u = make_uint4(0, 0, 0, 0);
-          if (rv && i0 + j < p.n && vec < g.V)
-            u = load_source<T>(p.src[i0 + j], p.cl, has_close && i0 + j == p.n - 1,
-                               row * rowbytes + (int64_t)vec * 16);
-          T::unpack(u, x[j][c]);
+          T::unpack(closing ? bcl[c] : u[j][c], x[j][c]);
+          const bool keep = i < p.n && in_row[c];
+          #pragma unroll
+          for (int e = 0; e < EPV; ++e) x[j][c][e] = keep ? x[j][c][e] : 0.f;
         }
       }
       float red[NV];
@@ -911,17 +1053,17 @@ struct F32x4 {
 
 // dV = A dh + B q~ + C x for the 4 elements of one vector, written (or added)
 // as 16 bytes of fp32 at dst.
-template <class F>
+template <class F, bool ACC>
 __device__ __forceinline__ void bwd_store_dv(float* __restrict__ dst, const typename F::raw& dhr,
                                              const float* q, const typename F::raw& xr, float A,
-                                             float B, float C, bool accumulate) {
+                                             float B, float C) {
   float dh[4], x[4];
   F::unpack(dhr, dh);
   F::unpack(xr, x);
   float o[4];
   #pragma unroll
   for (int k = 0; k < 4; ++k) o[k] = A * dh[k] + B * q[k] + C * x[k];
-  if (accumulate) {
+  if constexpr (ACC) {
     const uint4 u = ld16_stream(dst);
     o[0] += __uint_as_float(u.x); o[1] += __uint_as_float(u.y);
     o[2] += __uint_as_float(u.z); o[3] += __uint_as_float(u.w);
@@ -950,7 +1092,9 @@ __device__ __forceinline__ void bwd_acc_dq(float* dq, const typename F::raw& xr,
 #define ATTNRES_BWD_WAVES_PER_EU 1  // minimum waves per SIMD the register budget must allow
 #endif
 
-template <class F, int VPL, int G, bool RES>
+// ACC: the gradients are added to dV (a compile-time choice, so the plain
+// form has no branch around its stores).
+template <class F, int VPL, int G, bool RES, bool ACC>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(ATTNRES_BWD_WAVES_PER_EU)))
 void aggregate_bwd_kernel(AggBwdParams p) {
   extern __shared__ float lds[];
@@ -1096,12 +1240,13 @@ void aggregate_bwd_kernel(AggBwdParams p) {
         float* dst = p.dV[j] + row * g.D;
         #pragma unroll
         for (int c = 0; c < VPL; ++c) {
+          // a lane past the row's end holds zeros (nothing added to dq~) and
+          // stores to the sink
           const int vec = c * ln.stride + ln.t;
-          if (vec < g.V) {
-            bwd_store_dv<F>(dst + (int64_t)vec * 4, dhr[c], q[c], x[j][c], a[j], B, C,
-                            p.accumulate != 0);
-            bwd_acc_dq<F>(dq[c], x[j][c], B);
-          }
+          float* to = reinterpret_cast<float*>(
+              store_target(vec < g.V, reinterpret_cast<char*>(dst + (int64_t)vec * 4)));
+          bwd_store_dv<F, ACC>(to, dhr[c], q[c], x[j][c], a[j], B, C);
+          bwd_acc_dq<F>(dq[c], x[j][c], B);
         }
       }
     } else {
@@ -1120,16 +1265,16 @@ void aggregate_bwd_kernel(AggBwdParams p) {
         #pragma unroll
         for (int c = 0; c < VPL; ++c) {
           const int vec = c * ln.stride + ln.t;
-          xr[c] = vec < g.V ? F::load(srow + (int64_t)vec * F::kBytes) : F::zero();
+          xr[c] = F::load(srow + (int64_t)(vec < g.V ? vec : 0) * F::kBytes);
+          if (!(vec < g.V)) xr[c] = F::zero();
         }
         #pragma unroll
         for (int c = 0; c < VPL; ++c) {
           const int vec = c * ln.stride + ln.t;
-          if (vec < g.V) {
-            bwd_store_dv<F>(dst + (int64_t)vec * 4, dhr[c], q[c], xr[c], a, B, C,
-                            p.accumulate != 0);
-            bwd_acc_dq<F>(dq[c], xr[c], B);
-          }
+          float* to = reinterpret_cast<float*>(
+              store_target(vec < g.V, reinterpret_cast<char*>(dst + (int64_t)vec * 4)));
+          bwd_store_dv<F, ACC>(to, dhr[c], q[c], xr[c], a, B, C);
+          bwd_acc_dq<F>(dq[c], xr[c], B);
         }
       }
     }
@@ -1234,48 +1379,72 @@ __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
   const Lanes ln(g.W);
   const int64_t rowbytes = (int64_t)g.V * 16;
 
+  // this sublayer's folded query (and the output norm's gain), resident for
+  // every row; zero past the row's end
+  float q[VPL][EPV], gn[NORM ? VPL : 1][EPV];
+  #pragma unroll
+  for (int c = 0; c < VPL; ++c) {
+    const int vec = c * ln.stride + ln.t;
+    if (vec < g.V) {
+      load_query<EPV>(p.w, p.gm, (int64_t)vec * EPV, q[c]);
+      if (NORM) load_gain<EPV>(p.gf, (int64_t)vec * EPV, gn[c]);
+    } else {
+      #pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        q[c][e] = 0.f;
+        if (NORM) gn[c][e] = 0.f;
+      }
+    }
+  }
+
   for (int64_t grp = blockIdx.x; grp < g.groups; grp += gridDim.x) {
     const int64_t row = grp * g.RPW + ln.slot;
     const bool rv = row < g.R;
-    const int64_t base = row * rowbytes;
-    uint4 pv[VPL], ov[VPL];
+    const int64_t base = (rv ? row : 0) * rowbytes;
+    // every load of the row is issued first and unconditionally (a row past
+    // the end reads row 0, a lane past the row's end reads vector 0; both are
+    // discarded), so no branch hides a load from the compiler's wait counting
+    // and one wait covers them all
+    uint4 vv[VPL], pp[VPL], ov[VPL];
     #pragma unroll
     for (int c = 0; c < VPL; ++c) {
       const int vec = c * ln.stride + ln.t;
-      const bool ok = rv && vec < g.V;
-      const int64_t off = base + (int64_t)vec * 16;
-      uint4 v = ok ? ld16_stream(static_cast<const char*>(p.v_prev) + off) : make_uint4(0, 0, 0, 0);
-      if (HAS_PREV) {
-        uint4 a = ok ? ld16_stream(static_cast<const char*>(p.p_prev) + off) : make_uint4(0, 0, 0, 0);
-        float fa[EPV], fv[EPV];
-        T::unpack(a, fa);
-        T::unpack(v, fv);
-        #pragma unroll
-        for (int e = 0; e < EPV; ++e) fa[e] += fv[e];
-        v = T::pack(fa);  // the partial, rounded to the I/O dtype
-        if (ok) st16(static_cast<char*>(p.p_out) + off, v);
-      }
-      pv[c] = v;
-      ov[c] = ok ? ld16_stream(static_cast<const char*>(p.o) + off) : make_uint4(0, 0, 0, 0);
+      const int64_t off = base + (int64_t)(vec < g.V ? vec : 0) * 16;
+      vv[c] = ld16_stream(static_cast<const char*>(p.v_prev) + off);
+      if (HAS_PREV) pp[c] = ld16_stream(static_cast<const char*>(p.p_prev) + off);
+      ov[c] = ld16_stream(static_cast<const char*>(p.o) + off);
     }
+    const float l = p.lse[rv ? row : 0];
+
+    uint4 pv[VPL];
     float red[2] = {0.f, 0.f};
     #pragma unroll
     for (int c = 0; c < VPL; ++c) {
       const int vec = c * ln.stride + ln.t;
-      if (vec < g.V) {
-        float q[EPV], f[EPV];
-        load_query<EPV>(p.w, p.gm, (int64_t)vec * EPV, q);
-        T::unpack(pv[c], f);
+      const bool ok = rv && vec < g.V;
+      if (HAS_PREV) {
+        float fa[EPV], fv[EPV];
+        T::unpack(pp[c], fa);
+        T::unpack(vv[c], fv);
         #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          red[0] += q[e] * f[e];
-          red[1] += f[e] * f[e];
-        }
+        for (int e = 0; e < EPV; ++e) fa[e] += fv[e];
+        pv[c] = T::pack(fa);  // the partial, rounded to the I/O dtype
+        st16(store_target(ok, static_cast<char*>(p.p_out) + base + (int64_t)vec * 16), pv[c]);
+      } else {
+        pv[c] = vv[c];
+      }
+      const bool in_row = vec < g.V;
+      float f[EPV];
+      T::unpack(pv[c], f);
+      #pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        f[e] = in_row ? f[e] : 0.f;
+        red[0] += q[c][e] * f[e];
+        red[1] += f[e] * f[e];
       }
     }
     row_reduce<2>(red, lds, ln.slot, ln.wr, g.W);
     const float sp = red[0] * rsqrtf(red[1] * g.invD + p.eps);
-    const float l = rv ? p.lse[row] : 0.f;
     const float M = fmaxf(l, sp);
     float a = __expf(l - M), b = __expf(sp - M);
     const float r = 1.0f / (a + b);
@@ -1292,7 +1461,8 @@ __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
       #pragma unroll
       for (int e = 0; e < EPV; ++e) fo[e] = a * fo[e] + b * fp[e];
       hv[c] = T::pack(fo);  // h rounded to the I/O dtype
-      if (rv && vec < g.V && p.h_out) st16(static_cast<char*>(p.h_out) + base + (int64_t)vec * 16, hv[c]);
+      if (p.h_out)
+        st16(store_target(rv && vec < g.V, static_cast<char*>(p.h_out) + base + (int64_t)vec * 16), hv[c]);
       if (NORM && vec < g.V) {
         T::unpack(hv[c], fo);
         #pragma unroll
@@ -1306,14 +1476,12 @@ __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
       #pragma unroll
       for (int c = 0; c < VPL; ++c) {
         const int vec = c * ln.stride + ln.t;
-        if (rv && vec < g.V) {
-          float f[EPV], gn[EPV];
-          T::unpack(hv[c], f);
-          load_gain<EPV>(p.gf, (int64_t)vec * EPV, gn);
-          #pragma unroll
-          for (int e = 0; e < EPV; ++e) f[e] = gn[e] * (f[e] * inv);
-          st16(static_cast<char*>(p.hn_out) + base + (int64_t)vec * 16, T::pack(f));
-        }
+        float f[EPV];
+        T::unpack(hv[c], f);
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) f[e] = gn[c][e] * (f[e] * inv);
+        st16(store_target(rv && vec < g.V, static_cast<char*>(p.hn_out) + base + (int64_t)vec * 16),
+             T::pack(f));
       }
     }
   }
@@ -1529,9 +1697,47 @@ static hipError_t launch_phase1_mfma(const Phase1Args& a, const Launch& L) {
   }
 }
 
+#ifndef ATTNRES_P1_SINGLE_VPL
+#define ATTNRES_P1_SINGLE_VPL 2  // 16-byte vectors per lane of the one-source statistics pass
+#endif
+#ifndef ATTNRES_P1_SINGLE_GROUPS
+#define ATTNRES_P1_SINGLE_GROUPS 2048  // workgroups of the one-source statistics pass
+#endif
+#ifndef ATTNRES_P1_SINGLE_AHEAD
+#define ATTNRES_P1_SINGLE_AHEAD 1  // rows loaded ahead by the one-source statistics pass
+#endif
+
+template <class T>
+static hipError_t launch_phase1_single(const Phase1Args& a, const Launch& L) {
+  Phase1Params p;
+  for (int i = 0; i < 16; ++i) p.src[i] = i < a.n ? a.src[i] : nullptr;
+  p.n = a.n; p.S = a.S; p.Wq = a.W; p.G = a.G; p.eps = a.eps;
+  p.out = nullptr; p.m_out = a.m_out; p.lse_out = a.lse_out;
+  p.cl = Close{nullptr, nullptr, nullptr};
+  p.g = make_geom(a.R, a.D, T::kBytes, ATTNRES_P1_SINGLE_VPL, 4);
+  const size_t lds = p.g.W > 1 ? (size_t)p.g.RPW * p.g.W * 9 * sizeof(float) : 0;
+  const int64_t grid = p.g.groups < ATTNRES_P1_SINGLE_GROUPS ? p.g.groups : ATTNRES_P1_SINGLE_GROUPS;
+  return launch(L, phase1_single_kernel<T, ATTNRES_P1_SINGLE_VPL, 8, ATTNRES_P1_SINGLE_AHEAD>,
+                dim3((unsigned)grid),
+                dim3(64 * p.g.W * p.g.RPW), lds, p);
+}
+
+static bool phase1_single_eligible(int dtype, const Phase1Args& a) {
+  return !a.out && a.n == 1 && !a.close_v && a.S <= 8 &&
+         make_geom(1, a.D, dtype == 1 ? 2 : 4, ATTNRES_P1_SINGLE_VPL, 4).W <= 8;
+}
+
 hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L) {
+  if (phase1_single_eligible(dtype, a))
+    return dtype == 1 ? launch_phase1_single<Bf16>(a, L) : launch_phase1_single<F32>(a, L);
   if (phase1_mfma_eligible(dtype, a.n, a.S, a.D)) return launch_phase1_mfma(a, L);
   return dtype == 1 ? launch_phase1_dt<Bf16>(a, L) : launch_phase1_dt<F32>(a, L);
+}
+
+bool phase1_stats_supported(int dtype, int n, int S, int64_t D) {
+  if (phase1_mfma_eligible(dtype, n, S, D)) return true;
+  if (n < 1 || n > 8) return false;
+  return make_geom(1, D, dtype == 1 ? 2 : 4, 2, 4).W <= 8;
 }
 
 bool phase1_supported(int dtype, int n, int S, int64_t D) {
@@ -1574,13 +1780,17 @@ hipError_t launch_aggregate(int dtype, const AggArgs& a, const Launch& L) {
 }
 
 template <class T, int VPL, bool HP>
+#ifndef ATTNRES_PHASE2_MAX_GROUPS
+#define ATTNRES_PHASE2_MAX_GROUPS (1 << 20)  // workgroups of a Phase-2 launch (rows per group beyond: grid-stride)
+#endif
+
 static hipError_t launch_ph2_t(Phase2Params& p, const Launch& L) {
   const size_t lds = p.g.W > 1 ? (size_t)p.g.RPW * p.g.W * 2 * sizeof(float) : 0;
+  const unsigned grid = (unsigned)(p.g.groups < ATTNRES_PHASE2_MAX_GROUPS ? p.g.groups
+                                                                           : ATTNRES_PHASE2_MAX_GROUPS);
   if (p.hn_out)
-    return launch(L, phase2_kernel<T, VPL, HP, true>, dim3(grid_for(p.g)), dim3(64 * p.g.W * p.g.RPW),
-                  lds, p);
-  return launch(L, phase2_kernel<T, VPL, HP, false>, dim3(grid_for(p.g)), dim3(64 * p.g.W * p.g.RPW),
-                lds, p);
+    return launch(L, phase2_kernel<T, VPL, HP, true>, dim3(grid), dim3(64 * p.g.W * p.g.RPW), lds, p);
+  return launch(L, phase2_kernel<T, VPL, HP, false>, dim3(grid), dim3(64 * p.g.W * p.g.RPW), lds, p);
 }
 
 template <class T, bool HP>
@@ -1712,7 +1922,9 @@ static hipError_t launch_bwd_t(const AggBwdParams& p, unsigned grid, const Launc
   const int waves = p.g.W * p.g.RPW;
   const size_t lds = (size_t)p.g.RPW * p.g.W * 3 * G * sizeof(float) +
                      (RES ? 0 : (size_t)waves * 64 * sizeof(BwdStat));
-  return launch(L, aggregate_bwd_kernel<T, VPL, G, RES>, dim3(grid), dim3(64 * waves), lds, p);
+  if (p.accumulate)
+    return launch(L, aggregate_bwd_kernel<T, VPL, G, RES, true>, dim3(grid), dim3(64 * waves), lds, p);
+  return launch(L, aggregate_bwd_kernel<T, VPL, G, RES, false>, dim3(grid), dim3(64 * waves), lds, p);
 }
 
 // n <= G sources stay resident; wider rows (more vectors per lane) keep

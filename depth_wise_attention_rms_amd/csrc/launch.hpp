@@ -26,7 +26,7 @@ struct Phase1Args {
   const float* G;  // [S][D] or null
   int S;
   float eps;
-  void* out;       // [S][R][D]
+  void* out;       // [S][R][D], or null: statistics only (phase1_stats_supported shapes)
   float* m_out;    // [S][R] or null
   float* lse_out;  // [S][R]
   const void* close_p;
@@ -108,6 +108,8 @@ hipError_t launch_bwd_reduce(const BwdArgs& a, const BwdPlan& pl, int stage, con
 hipError_t launch_fold(const float* w, const float* g, float* q, int64_t count, const Launch& L);
 hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L);
 bool phase1_supported(int dtype, int n, int S, int64_t D);
+// Phase 1 with out == null (statistics only) is available for these shapes
+bool phase1_stats_supported(int dtype, int n, int S, int64_t D);
 hipError_t launch_aggregate(int dtype, const AggArgs& a, const Launch& L);
 hipError_t launch_phase2(int dtype, const Phase2Args& a, const Launch& L);
 hipError_t launch_rmsnorm(int dtype, const void* x, int64_t R, int64_t D, const float* g, float eps,

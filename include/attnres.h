@@ -308,7 +308,9 @@ int attnres_aggregate_backward(const void* const* sources, int n, int64_t R, int
  * `capacity` launches (0 disables and releases the events). The library keeps
  * per-kind totals: kind 0 Phase 1, 1 Phase 2, 2 aggregate, 3 block close,
  * 4 query fold, 5 standalone output norm, 6 aggregate backward (main
- * kernel), 7 its reduction over rows. attnres_timing_read synchronises
+ * kernel), 7 its reduction over rows, 8 Phase-1 statistics of a block whose
+ * only source is the embedding (a stack forward's first block: its outputs
+ * are the embedding itself and are not formed). attnres_timing_read synchronises
  * the recorded events and returns, for `kind`, the number of timed launches,
  * their summed duration in milliseconds and their summed algorithmic bytes
  * (inputs read once plus outputs written once, queries excluded).
