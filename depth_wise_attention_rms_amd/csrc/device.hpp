@@ -104,8 +104,11 @@ __device__ __forceinline__ float wave_sum(float x) {
 // Reduce NV per-lane partial sums across the W waves that share a token row.
 // Each wave reduces its lanes with wave_sum; lane 0 of each wave writes the
 // wave's sums to `lds` ([slots][W][NV] floats, one slot per row handled by the
-// workgroup); after a barrier every lane sums the W entries in wave order.
-// Must be reached by every thread of the workgroup (it contains barriers).
+// workgroup). After a barrier, lane k of every wave sums entry k over the W
+// waves in wave order and the totals are broadcast from lane k, so a lane
+// reads W values instead of W x NV (for NV > 64 every lane sums every entry).
+// Either way the order of the additions is the same. Must be reached by every
+// thread of the workgroup (it contains barriers).
 template <int NV>
 __device__ __forceinline__ void row_reduce(float (&v)[NV], float* lds, int slot, int wave_in_row,
                                            int W) {
@@ -113,16 +116,28 @@ __device__ __forceinline__ void row_reduce(float (&v)[NV], float* lds, int slot,
   for (int k = 0; k < NV; ++k) v[k] = wave_sum(v[k]);
   if (W == 1) return;
   float* base = lds + (size_t)slot * W * NV;
-  if ((threadIdx.x & 63) == 0) {
+  const int lane = threadIdx.x & 63;
+  if (lane == 0) {
     #pragma unroll
     for (int k = 0; k < NV; ++k) base[wave_in_row * NV + k] = v[k];
   }
   __syncthreads();
-  #pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    float s = base[k];
-    for (int w = 1; w < W; ++w) s += base[w * NV + k];
-    v[k] = s;
+  if constexpr (NV <= 64) {
+    float s = 0.f;
+    if (lane < NV) {
+      s = base[lane];
+      for (int w = 1; w < W; ++w) s += base[w * NV + lane];
+    }
+    #pragma unroll
+    for (int k = 0; k < NV; ++k)
+      v[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), k));
+  } else {
+    #pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      float s = base[k];
+      for (int w = 1; w < W; ++w) s += base[w * NV + k];
+      v[k] = s;
+    }
   }
   __syncthreads();
 }

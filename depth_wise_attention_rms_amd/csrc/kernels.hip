@@ -1345,6 +1345,212 @@ __global__ __launch_bounds__(256) void bwd_colsum_kernel(const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// Phase 1 streamed over any number of sources [K3 9.4 step 1; RH 4.2 Phase 1]:
+// up to SQ queries stay in registers while the row's sources stream through in
+// register groups of G. Each group's SQ x G scores come from one row
+// reduction, and every query folds them into its own running (m, z,
+// numerator) by the online-softmax merge (OS2), so each source is read once
+// for all SQ queries whatever n is. Used where the matrix-core kernel does not
+// apply: more than 8 sources, more than 8 queries (in passes of SQ), fp32 I/O,
+// or other row widths. Loads are unconditional and stores branch-free (see
+// the aggregate kernel).
+// ---------------------------------------------------------------------------
+struct Phase1SParams {
+  const void* src[64];
+  int n;
+  int S;            // queries of this pass (<= SQ)
+  const float* Wq;  // [S][D]
+  const float* G;   // [S][D] or null
+  float eps;
+  void* out;        // [S][R][D]
+  float* m_out;     // [S][R] or null
+  float* lse_out;   // [S][R]
+  Close cl;         // close computing source n-1, or cl.v == null
+  Geom g;
+};
+
+template <class T, int VPL, int G, int SQ, int PD>
+__global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
+  extern __shared__ float lds[];
+  constexpr int EPV = T::kEPV;
+  constexpr int NV = SQ * G + G;
+  const Geom& g = p.g;
+  const Lanes ln(g.W);
+  const int64_t rowbytes = (int64_t)g.V * 16;
+  const bool has_close = p.cl.v != nullptr;
+
+  float q[SQ][VPL][EPV];
+  #pragma unroll
+  for (int s = 0; s < SQ; ++s)
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      const int vec = c * ln.stride + ln.t;
+      if (s < p.S && vec < g.V) {
+        load_query<EPV>(p.Wq, p.G, (int64_t)s * g.D + (int64_t)vec * EPV, q[s][c]);
+      } else {
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) q[s][c][e] = 0.f;
+      }
+    }
+
+  // Byte offsets of this lane's vectors in row `grp`'s slot (row 0 past the
+  // end, vector 0 past the row's end: loads stay in bounds and unconditional).
+  bool in_row[VPL];
+  #pragma unroll
+  for (int c = 0; c < VPL; ++c) in_row[c] = c * ln.stride + ln.t < g.V;
+  auto row_off = [&](int64_t grp, int c) -> int64_t {
+    const int64_t row = grp * g.RPW + ln.slot;
+    const int64_t rr = (grp < g.groups && row < g.R) ? row : 0;
+    return rr * rowbytes + (int64_t)(in_row[c] ? c * ln.stride + ln.t : 0) * 16;
+  };
+  // Raw vectors of sources i0 .. i0 + G - 1 of row `grp`; slots past n and
+  // the closing source read the sink's first 16 bytes.
+  auto issue = [&](int64_t grp, int i0, uint4 (&u)[G][VPL]) {
+    #pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int i = i0 + j;
+      const bool live = i < p.n && !(has_close && i == p.n - 1);
+      const char* sp = static_cast<const char*>(p.src[live ? i : 0]);
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c)
+        u[j][c] = ld16_stream(live ? sp + row_off(grp, c) : reinterpret_cast<const char*>(g_store_sink));
+    }
+  };
+
+  // The next PD groups' loads are in flight while a group reduces. Groups are
+  // taken in one sequence over this workgroup's rows (row k's groups, then
+  // row k + 1's): flat index f is group f % gpr of the workgroup's row f / gpr.
+  const int gpr = (p.n + G - 1) / G;
+  auto issue_flat = [&](int64_t f, uint4 (&u)[G][VPL]) {
+    const int64_t k = f / gpr;
+    issue(blockIdx.x + k * gridDim.x, (int)(f - k * gpr) * G, u);
+  };
+  uint4 ring[PD][G][VPL];
+  #pragma unroll
+  for (int d = 0; d < PD; ++d) issue_flat(d, ring[d]);
+  int64_t f_next = PD;
+  for (int64_t grp = blockIdx.x; grp < g.groups; grp += gridDim.x) {
+    const int64_t row = grp * g.RPW + ln.slot;
+    const bool rv = row < g.R;
+    // the closing source b = round(p + v) (or v), formed and stored first
+    uint4 bcl[VPL];
+    if (has_close) {
+      const char* pp = static_cast<const char*>(p.cl.p ? p.cl.p : p.cl.v);
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        const int64_t off = row_off(grp, c);
+        const uint4 v = ld16_stream(static_cast<const char*>(p.cl.v) + off);
+        const uint4 a = ld16_stream(pp + off);
+        float fa[EPV], fv[EPV];
+        T::unpack(a, fa);
+        T::unpack(v, fv);
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) fa[e] = p.cl.p ? fa[e] + fv[e] : fv[e];
+        bcl[c] = T::pack(fa);
+        st16_stream(store_target(rv && in_row[c], static_cast<char*>(p.cl.b) + off), bcl[c]);
+      }
+    }
+
+    float m_run[SQ], z_run[SQ], num[SQ][VPL][EPV];
+    #pragma unroll
+    for (int s = 0; s < SQ; ++s) {
+      m_run[s] = -FLT_MAX;
+      z_run[s] = 0.f;
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c)
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) num[s][c][e] = 0.f;
+    }
+    for (int i0 = 0; i0 < p.n; i0 += G) {
+      uint4 u[G][VPL];
+      #pragma unroll
+      for (int j = 0; j < G; ++j)
+        #pragma unroll
+        for (int c = 0; c < VPL; ++c) {
+          u[j][c] = ring[0][j][c];
+          #pragma unroll
+          for (int d = 0; d + 1 < PD; ++d) ring[d][j][c] = ring[d + 1][j][c];
+        }
+      issue_flat(f_next++, ring[PD - 1]);
+      float x[G][VPL][EPV];
+      #pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const int i = i0 + j;
+        const bool closing = has_close && i == p.n - 1;
+        #pragma unroll
+        for (int c = 0; c < VPL; ++c) {
+          T::unpack(closing ? bcl[c] : u[j][c], x[j][c]);
+          const bool keep = i < p.n && in_row[c];
+          #pragma unroll
+          for (int e = 0; e < EPV; ++e) x[j][c][e] = keep ? x[j][c][e] : 0.f;
+        }
+      }
+      float red[NV];
+      #pragma unroll
+      for (int k = 0; k < NV; ++k) red[k] = 0.f;
+      #pragma unroll
+      for (int j = 0; j < G; ++j)
+        #pragma unroll
+        for (int c = 0; c < VPL; ++c)
+          #pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            red[SQ * G + j] += x[j][c][e] * x[j][c][e];
+            #pragma unroll
+            for (int s = 0; s < SQ; ++s) red[s * G + j] += q[s][c][e] * x[j][c][e];
+          }
+      row_reduce<NV>(red, lds, ln.slot, ln.wr, g.W);
+      float ri[G];
+      #pragma unroll
+      for (int j = 0; j < G; ++j) ri[j] = rsqrtf(red[SQ * G + j] * g.invD + p.eps);
+      #pragma unroll
+      for (int s = 0; s < SQ; ++s) {
+        float sc[G];
+        float m_new = m_run[s];
+        #pragma unroll
+        for (int j = 0; j < G; ++j) {
+          sc[j] = red[s * G + j] * ri[j];
+          if (i0 + j < p.n) m_new = fmaxf(m_new, sc[j]);
+        }
+        const float rescale = __expf(m_run[s] - m_new);
+        z_run[s] *= rescale;
+        #pragma unroll
+        for (int j = 0; j < G; ++j) {
+          sc[j] = (i0 + j < p.n) ? __expf(sc[j] - m_new) : 0.f;
+          z_run[s] += sc[j];
+        }
+        #pragma unroll
+        for (int c = 0; c < VPL; ++c)
+          #pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            float a = num[s][c][e] * rescale;
+            #pragma unroll
+            for (int j = 0; j < G; ++j) a += sc[j] * x[j][c][e];
+            num[s][c][e] = a;
+          }
+        m_run[s] = m_new;
+      }
+    }
+    #pragma unroll
+    for (int s = 0; s < SQ; ++s) {
+      if (s >= p.S) continue;
+      const float rz = 1.0f / z_run[s];
+      char* orow = static_cast<char*>(p.out) + (int64_t)s * g.R * rowbytes;
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        float o[EPV];
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) o[e] = num[s][c][e] * rz;
+        st16(store_target(rv && in_row[c], orow + row_off(grp, c)), T::pack(o));
+      }
+      if (rv && ln.t == 0) {
+        if (p.m_out) p.m_out[(int64_t)s * g.R + row] = m_run[s];
+        p.lse_out[(int64_t)s * g.R + row] = m_run[s] + __logf(z_run[s]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Phase 2 (one intra-block merge step) [K3 9.4 step 2, OS2, single-source
 // triple; RH 4.2 Phase 2]: p = p_prev + v_prev rounded to the I/O dtype (or
 // p = v_prev on the first merge), the score of the rounded p, then
@@ -1597,8 +1803,9 @@ static unsigned grid_for(const Geom& g) {
 template <typename K, typename... Args>
 static hipError_t launch(const Launch& L, K kernel, dim3 grid, dim3 block, size_t lds,
                          Args... args) {
-  if (L.start) {
+  if (L.start || L.stop) {
     // the start/stop events take the timestamps of this kernel's own dispatch
+    // (either may be null: a sequence of launches is timed first to last)
     hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, L.stream, L.start, L.stop, 0, args...);
   } else {
     hipLaunchKernelGGL(kernel, grid, block, lds, L.stream, args...);
@@ -1727,10 +1934,101 @@ static bool phase1_single_eligible(int dtype, const Phase1Args& a) {
          make_geom(1, a.D, dtype == 1 ? 2 : 4, ATTNRES_P1_SINGLE_VPL, 4).W <= 8;
 }
 
+#ifndef ATTNRES_P1_STREAM_GROUPS
+#define ATTNRES_P1_STREAM_GROUPS 512  // workgroups of a streamed Phase-1 pass (each walks many rows)
+#endif
+
+// Streamed Phase 1: elements per lane E = VPL x (elements per vector); the
+// query tile, the SQ numerators and a group of G sources each take E registers
+// per query or source, so wider rows take fewer queries per pass.
+#ifndef ATTNRES_P1_STREAM_AHEAD
+#define ATTNRES_P1_STREAM_AHEAD 3  // source groups in flight ahead of the one being reduced
+#endif
+
+template <class T, int VPL, int G, int SQ, int PD>
+static hipError_t launch_phase1_stream_t(Phase1SParams& p, const Phase1Args& a, const Launch& L) {
+  const size_t lds = p.g.W > 1 ? (size_t)p.g.RPW * p.g.W * (SQ * G + G) * sizeof(float) : 0;
+  const int64_t row_bytes = a.D * T::kBytes;
+  for (int s0 = 0; s0 < a.S; s0 += SQ) {
+    // later passes read the block sum the first pass stored
+    if (s0 > 0 && p.cl.v) {
+      p.src[a.n - 1] = p.cl.b;
+      p.cl = Close{nullptr, nullptr, nullptr};
+    }
+    p.S = a.S - s0 < SQ ? a.S - s0 : SQ;
+    p.Wq = a.W + (int64_t)s0 * a.D;
+    p.G = a.G ? a.G + (int64_t)s0 * a.D : nullptr;
+    p.out = static_cast<char*>(a.out) + (int64_t)s0 * a.R * row_bytes;
+    p.m_out = a.m_out ? a.m_out + (int64_t)s0 * a.R : nullptr;
+    p.lse_out = a.lse_out + (int64_t)s0 * a.R;
+    // timed from the first pass's start to the last pass's end
+    const Launch Ls{L.stream, s0 == 0 ? L.start : nullptr, s0 + SQ >= a.S ? L.stop : nullptr};
+    const int64_t grid = p.g.groups < ATTNRES_P1_STREAM_GROUPS ? p.g.groups : ATTNRES_P1_STREAM_GROUPS;
+    hipError_t e = launch(Ls, phase1_stream_kernel<T, VPL, G, SQ, PD>, dim3((unsigned)grid),
+                          dim3(64 * p.g.W * p.g.RPW), lds, p);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// The smallest of 8, 16 or 32 elements per lane whose row fits eight waves;
+// returns the vectors per lane (0: the row is too wide).
+static int stream_vpl(int esize, int64_t D, int* E) {
+  const int epv = 16 / esize;
+  for (int e = 8; e <= 32; e *= 2) {
+    const int vpl = e / epv;
+    if (make_geom(1, D, esize, vpl, 8).W <= 8) {
+      *E = e;
+      return vpl;
+    }
+  }
+  return 0;
+}
+
+template <class T>
+static hipError_t launch_phase1_stream(const Phase1Args& a, const Launch& L) {
+  Phase1SParams p;
+  for (int i = 0; i < 64; ++i) p.src[i] = i < a.n ? a.src[i] : nullptr;
+  p.n = a.n; p.eps = a.eps;
+  p.cl = Close{a.close_p, a.close_v, a.close_b};
+  int E = 0;
+  const int vpl = stream_vpl(T::kBytes, a.D, &E);
+  if (!vpl) return hipErrorInvalidValue;
+  p.g = make_geom(a.R, a.D, T::kBytes, vpl, 8);
+  constexpr int epv = T::kEPV;
+  // The kernel is bound by vector-ALU issue, which scales with the query
+  // tile, so the tile is the smallest that covers S (or the largest that fits
+  // the registers, in passes); smaller tiles leave room for larger source
+  // groups. bf16 keeps ATTNRES_P1_STREAM_AHEAD groups in flight at 8 and 16
+  // elements per lane; fp32 vectors (and the widest rows) take twice the
+  // registers and keep one.
+  constexpr int PD = T::kBytes == 2 ? ATTNRES_P1_STREAM_AHEAD : 1;
+  if (E == 8) {
+    if (a.S <= 2) return launch_phase1_stream_t<T, 8 / epv, 4, 2, PD>(p, a, L);
+    if (a.S <= 4) return launch_phase1_stream_t<T, 8 / epv, 4, 4, PD>(p, a, L);
+    return launch_phase1_stream_t<T, 8 / epv, 2, 8, PD>(p, a, L);
+  }
+  if (E == 16) {
+    if (a.S <= 1) return launch_phase1_stream_t<T, 16 / epv, 2, 1, PD>(p, a, L);
+    if (a.S <= 2) return launch_phase1_stream_t<T, 16 / epv, 2, 2, PD>(p, a, L);
+    return launch_phase1_stream_t<T, 16 / epv, 1, 4, PD>(p, a, L);
+  }
+  if constexpr (T::kBytes == 2) {
+    if (a.S >= 2) return launch_phase1_stream_t<T, 32 / epv, 1, 2, 1>(p, a, L);
+  }
+  return launch_phase1_stream_t<T, 32 / epv, 1, 1, 1>(p, a, L);
+}
+
+#ifndef ATTNRES_P1_STREAM
+#define ATTNRES_P1_STREAM 1  // 0: the register-resident vector-ALU Phase 1 where it applies
+#endif
+
 hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L) {
   if (phase1_single_eligible(dtype, a))
     return dtype == 1 ? launch_phase1_single<Bf16>(a, L) : launch_phase1_single<F32>(a, L);
   if (phase1_mfma_eligible(dtype, a.n, a.S, a.D)) return launch_phase1_mfma(a, L);
+  if (a.out && (ATTNRES_P1_STREAM || a.n > 16))
+    return dtype == 1 ? launch_phase1_stream<Bf16>(a, L) : launch_phase1_stream<F32>(a, L);
   return dtype == 1 ? launch_phase1_dt<Bf16>(a, L) : launch_phase1_dt<F32>(a, L);
 }
 
@@ -1742,10 +2040,9 @@ bool phase1_stats_supported(int dtype, int n, int S, int64_t D) {
 
 bool phase1_supported(int dtype, int n, int S, int64_t D) {
   if (phase1_mfma_eligible(dtype, n, S, D)) return true;
-  const int es = dtype == 1 ? 2 : 4;
-  if (n < 1 || n > 16) return false;
-  const Geom g = make_geom(1, D, es, n <= 8 ? 2 : 1, 4);
-  return g.W <= 8;
+  if (n < 1 || n > 64) return false;
+  int E = 0;
+  return stream_vpl(dtype == 1 ? 2 : 4, D, &E) != 0;
 }
 
 template <class T, int VPL, int G>

@@ -147,8 +147,15 @@ PH1_CASES = [
     (7, 8, 300, 2048, "bf16"), (8, 3, 513, 1024, "bf16"), (2, 1, 260, 3072, "bf16"),
     (4, 4, 1000, 4096, "bf16"), (5, 5, 1000, 4096, "bf16"), (8, 8, 37, 4096, "bf16"),
     (6, 8, 700, 4096, "bf16"), (1, 6, 300, 1024, "bf16"), (3, 7, 777, 3072, "bf16"),
-    # S = 9, 10 with n <= 8 take the vector-ALU kernel
+    # everything else takes the streamed kernel (S = 9, 10 with n <= 8, more
+    # than 8 sources, fp32, other widths): query tiles of 2, 4 or 8 at 8
+    # elements per lane (bf16 D <= 4096, fp32 D <= 2048), 1, 2 or 4 at 16,
+    # 2 (bf16) or 1 (fp32) at 32, in passes when S exceeds the tile; R well above the 512-workgroup grid makes every workgroup walk
+    # many rows with the next source group in flight across row ends
     (7, 10, 300, 2048, "bf16"), (4, 9, 1000, 4096, "bf16"),
+    (12, 8, 2000, 4096, "bf16"), (10, 24, 1500, 7168, "bf16"), (64, 3, 40, 1024, "bf16"),
+    (9, 5, 777, 1000, "bf16"), (3, 3, 300, 8192, "f32"), (11, 17, 600, 2048, "f32"),
+    (33, 6, 1100, 256, "bf16"), (12, 1, 200, 7168, "bf16"), (9, 2, 300, 7168, "bf16"),
 ]
 
 
