@@ -1351,14 +1351,27 @@ __global__ __launch_bounds__(256) void bwd_colsum_kernel(const float* __restrict
 // reduction, and every query folds them into its own running (m, z,
 // numerator) by the online-softmax merge (OS2), so each source is read once
 // for all SQ queries whatever n is. Used where the matrix-core kernel does not
-// apply: more than 8 sources, more than 8 queries (in passes of SQ), fp32 I/O,
-// or other row widths. Loads are unconditional and stores branch-free (see
-// the aggregate kernel).
+// apply: more than 8 sources, more than 8 queries, fp32 I/O, or other row
+// widths. Loads are unconditional and stores branch-free (see the aggregate
+// kernel).
+//
+// More than SQ queries run in passes of SQ. When the rows alone do not fill
+// the grid (few rows, as in decode), the passes run side by side in one
+// launch: workgroup b runs pass (b / 8) % passes for row walker
+// b % 8 + 8 (b / (8 passes)). Consecutive workgroups go to the 8 XCDs in
+// turn, so all passes of one walker sit on one XCD and walk the same rows at
+// about the same time, and the later reads of a row's sources are served by
+// that XCD's L2. Every pass of the launch forms a fused block close in
+// registers; pass 0 stores it. With many rows the passes run as consecutive
+// launches, which measured twice as fast at 131072 rows of 7168 as 6 side-by-
+// side passes; launches after the first read the stored block sum.
 // ---------------------------------------------------------------------------
 struct Phase1SParams {
   const void* src[64];
   int n;
-  int S;            // queries of this pass (<= SQ)
+  int S;            // queries of the launch (all its passes)
+  int passes;       // passes of the launch: ceil(S / SQ)
+  int walkers;      // row walkers per pass (a multiple of 8)
   const float* Wq;  // [S][D]
   const float* G;   // [S][D] or null
   float eps;
@@ -1378,6 +1391,11 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
   const Lanes ln(g.W);
   const int64_t rowbytes = (int64_t)g.V * 16;
   const bool has_close = p.cl.v != nullptr;
+  const int rest = (int)(blockIdx.x >> 3);
+  const int pass = rest % p.passes;
+  const int64_t walker = (int64_t)(blockIdx.x & 7) + 8 * (int64_t)(rest / p.passes);
+  const int s0 = pass * SQ;
+  const int Sp = p.S - s0 < SQ ? p.S - s0 : SQ;  // queries of this pass
 
   float q[SQ][VPL][EPV];
   #pragma unroll
@@ -1385,8 +1403,8 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
     #pragma unroll
     for (int c = 0; c < VPL; ++c) {
       const int vec = c * ln.stride + ln.t;
-      if (s < p.S && vec < g.V) {
-        load_query<EPV>(p.Wq, p.G, (int64_t)s * g.D + (int64_t)vec * EPV, q[s][c]);
+      if (s < Sp && vec < g.V) {
+        load_query<EPV>(p.Wq, p.G, (int64_t)(s0 + s) * g.D + (int64_t)vec * EPV, q[s][c]);
       } else {
         #pragma unroll
         for (int e = 0; e < EPV; ++e) q[s][c][e] = 0.f;
@@ -1423,13 +1441,13 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
   const int gpr = (p.n + G - 1) / G;
   auto issue_flat = [&](int64_t f, uint4 (&u)[G][VPL]) {
     const int64_t k = f / gpr;
-    issue(blockIdx.x + k * gridDim.x, (int)(f - k * gpr) * G, u);
+    issue(walker + k * p.walkers, (int)(f - k * gpr) * G, u);
   };
   uint4 ring[PD][G][VPL];
   #pragma unroll
   for (int d = 0; d < PD; ++d) issue_flat(d, ring[d]);
   int64_t f_next = PD;
-  for (int64_t grp = blockIdx.x; grp < g.groups; grp += gridDim.x) {
+  for (int64_t grp = walker; grp < g.groups; grp += p.walkers) {
     const int64_t row = grp * g.RPW + ln.slot;
     const bool rv = row < g.R;
     // the closing source b = round(p + v) (or v), formed and stored first
@@ -1447,7 +1465,7 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
         #pragma unroll
         for (int e = 0; e < EPV; ++e) fa[e] = p.cl.p ? fa[e] + fv[e] : fv[e];
         bcl[c] = T::pack(fa);
-        st16_stream(store_target(rv && in_row[c], static_cast<char*>(p.cl.b) + off), bcl[c]);
+        st16_stream(store_target(rv && in_row[c] && pass == 0, static_cast<char*>(p.cl.b) + off), bcl[c]);
       }
     }
 
@@ -1532,9 +1550,9 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
     }
     #pragma unroll
     for (int s = 0; s < SQ; ++s) {
-      if (s >= p.S) continue;
+      if (s >= Sp) continue;
       const float rz = 1.0f / z_run[s];
-      char* orow = static_cast<char*>(p.out) + (int64_t)s * g.R * rowbytes;
+      char* orow = static_cast<char*>(p.out) + (int64_t)(s0 + s) * g.R * rowbytes;
       #pragma unroll
       for (int c = 0; c < VPL; ++c) {
         float o[EPV];
@@ -1543,8 +1561,8 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
         st16(store_target(rv && in_row[c], orow + row_off(grp, c)), T::pack(o));
       }
       if (rv && ln.t == 0) {
-        if (p.m_out) p.m_out[(int64_t)s * g.R + row] = m_run[s];
-        p.lse_out[(int64_t)s * g.R + row] = m_run[s] + __logf(z_run[s]);
+        if (p.m_out) p.m_out[(int64_t)(s0 + s) * g.R + row] = m_run[s];
+        p.lse_out[(int64_t)(s0 + s) * g.R + row] = m_run[s] + __logf(z_run[s]);
       }
     }
   }
@@ -1560,6 +1578,8 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
 // stores: both are read again soon (p by the next merge, h by the sublayer)
 // and are rewritten in place every sublayer, so keeping them cacheable lets
 // the last-level cache serve them (about 8% faster than non-temporal stores).
+// Tensors far larger than that cache (NT: a row-set of more than
+// ATTNRES_PHASE2_NT_BYTES) are written non-temporally like every other stream.
 // ---------------------------------------------------------------------------
 struct Phase2Params {
   const void* o;
@@ -1577,7 +1597,13 @@ struct Phase2Params {
   Geom g;
 };
 
-template <class T, int VPL, bool HAS_PREV, bool NORM>
+template <bool NT>
+__device__ __forceinline__ void st16_out(char* p, const uint4& v) {
+  if constexpr (NT) st16_stream(p, v);
+  else st16(p, v);
+}
+
+template <class T, int VPL, bool HAS_PREV, bool NORM, bool NT>
 __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
   extern __shared__ float lds[];
   constexpr int EPV = T::kEPV;
@@ -1635,7 +1661,7 @@ __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
         #pragma unroll
         for (int e = 0; e < EPV; ++e) fa[e] += fv[e];
         pv[c] = T::pack(fa);  // the partial, rounded to the I/O dtype
-        st16(store_target(ok, static_cast<char*>(p.p_out) + base + (int64_t)vec * 16), pv[c]);
+        st16_out<NT>(store_target(ok, static_cast<char*>(p.p_out) + base + (int64_t)vec * 16), pv[c]);
       } else {
         pv[c] = vv[c];
       }
@@ -1668,7 +1694,8 @@ __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
       for (int e = 0; e < EPV; ++e) fo[e] = a * fo[e] + b * fp[e];
       hv[c] = T::pack(fo);  // h rounded to the I/O dtype
       if (p.h_out)
-        st16(store_target(rv && vec < g.V, static_cast<char*>(p.h_out) + base + (int64_t)vec * 16), hv[c]);
+        st16_out<NT>(store_target(rv && vec < g.V, static_cast<char*>(p.h_out) + base + (int64_t)vec * 16),
+                     hv[c]);
       if (NORM && vec < g.V) {
         T::unpack(hv[c], fo);
         #pragma unroll
@@ -1686,8 +1713,8 @@ __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
         T::unpack(hv[c], f);
         #pragma unroll
         for (int e = 0; e < EPV; ++e) f[e] = gn[c][e] * (f[e] * inv);
-        st16(store_target(rv && vec < g.V, static_cast<char*>(p.hn_out) + base + (int64_t)vec * 16),
-             T::pack(f));
+        st16_out<NT>(store_target(rv && vec < g.V, static_cast<char*>(p.hn_out) + base + (int64_t)vec * 16),
+                     T::pack(f));
       }
     }
   }
@@ -1777,6 +1804,10 @@ __global__ void close_kernel(const void* __restrict__ pp, const void* __restrict
 // Host-side launchers (called from api.hip).
 // ---------------------------------------------------------------------------
 
+#ifndef ATTNRES_PHASE2_NT_BYTES
+// [R, D] tensors larger than this are written non-temporally by Phase 2
+#define ATTNRES_PHASE2_NT_BYTES (1024.0 * 1024.0 * 1024.0)
+#endif
 #ifndef ATTNRES_PHASE2_VPL
 #define ATTNRES_PHASE2_VPL 2  // preferred vectors per lane in Phase 2 (rows take up to 4 waves)
 #endif
@@ -1949,23 +1980,33 @@ template <class T, int VPL, int G, int SQ, int PD>
 static hipError_t launch_phase1_stream_t(Phase1SParams& p, const Phase1Args& a, const Launch& L) {
   const size_t lds = p.g.W > 1 ? (size_t)p.g.RPW * p.g.W * (SQ * G + G) * sizeof(float) : 0;
   const int64_t row_bytes = a.D * T::kBytes;
-  for (int s0 = 0; s0 < a.S; s0 += SQ) {
-    // later passes read the block sum the first pass stored
+  // Passes per launch: as many as fit side by side in about
+  // ATTNRES_P1_STREAM_GROUPS workgroups, one walker per row group each.
+  const int passes = (a.S + SQ - 1) / SQ;
+  const int64_t busy = p.g.groups < ATTNRES_P1_STREAM_GROUPS ? p.g.groups : ATTNRES_P1_STREAM_GROUPS;
+  int per = (int)(ATTNRES_P1_STREAM_GROUPS / busy);
+  per = per < 1 ? 1 : per > passes ? passes : per;
+  for (int s0 = 0; s0 < a.S; s0 += per * SQ) {
+    // later launches read the block sum the first one stored
     if (s0 > 0 && p.cl.v) {
       p.src[a.n - 1] = p.cl.b;
       p.cl = Close{nullptr, nullptr, nullptr};
     }
-    p.S = a.S - s0 < SQ ? a.S - s0 : SQ;
+    p.S = a.S - s0 < per * SQ ? a.S - s0 : per * SQ;
+    p.passes = (p.S + SQ - 1) / SQ;
+    int64_t walkers = ATTNRES_P1_STREAM_GROUPS / p.passes;
+    if (walkers > p.g.groups) walkers = p.g.groups;
+    walkers = (walkers + 7) / 8 * 8;  // a multiple of the 8 XCDs
+    p.walkers = (int)walkers;
     p.Wq = a.W + (int64_t)s0 * a.D;
     p.G = a.G ? a.G + (int64_t)s0 * a.D : nullptr;
     p.out = static_cast<char*>(a.out) + (int64_t)s0 * a.R * row_bytes;
     p.m_out = a.m_out ? a.m_out + (int64_t)s0 * a.R : nullptr;
     p.lse_out = a.lse_out + (int64_t)s0 * a.R;
-    // timed from the first pass's start to the last pass's end
-    const Launch Ls{L.stream, s0 == 0 ? L.start : nullptr, s0 + SQ >= a.S ? L.stop : nullptr};
-    const int64_t grid = p.g.groups < ATTNRES_P1_STREAM_GROUPS ? p.g.groups : ATTNRES_P1_STREAM_GROUPS;
-    hipError_t e = launch(Ls, phase1_stream_kernel<T, VPL, G, SQ, PD>, dim3((unsigned)grid),
-                          dim3(64 * p.g.W * p.g.RPW), lds, p);
+    // timed from the first launch's start to the last launch's end
+    const Launch Ls{L.stream, s0 == 0 ? L.start : nullptr, s0 + per * SQ >= a.S ? L.stop : nullptr};
+    hipError_t e = launch(Ls, phase1_stream_kernel<T, VPL, G, SQ, PD>,
+                          dim3((unsigned)(walkers * p.passes)), dim3(64 * p.g.W * p.g.RPW), lds, p);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -2085,9 +2126,13 @@ static hipError_t launch_ph2_t(Phase2Params& p, const Launch& L) {
   const size_t lds = p.g.W > 1 ? (size_t)p.g.RPW * p.g.W * 2 * sizeof(float) : 0;
   const unsigned grid = (unsigned)(p.g.groups < ATTNRES_PHASE2_MAX_GROUPS ? p.g.groups
                                                                            : ATTNRES_PHASE2_MAX_GROUPS);
-  if (p.hn_out)
-    return launch(L, phase2_kernel<T, VPL, HP, true>, dim3(grid), dim3(64 * p.g.W * p.g.RPW), lds, p);
-  return launch(L, phase2_kernel<T, VPL, HP, false>, dim3(grid), dim3(64 * p.g.W * p.g.RPW), lds, p);
+  const dim3 block(64 * p.g.W * p.g.RPW);
+  if ((double)p.g.R * p.g.V * 16 > (double)ATTNRES_PHASE2_NT_BYTES) {
+    if (p.hn_out) return launch(L, phase2_kernel<T, VPL, HP, true, true>, dim3(grid), block, lds, p);
+    return launch(L, phase2_kernel<T, VPL, HP, false, true>, dim3(grid), block, lds, p);
+  }
+  if (p.hn_out) return launch(L, phase2_kernel<T, VPL, HP, true, false>, dim3(grid), block, lds, p);
+  return launch(L, phase2_kernel<T, VPL, HP, false, false>, dim3(grid), block, lds, p);
 }
 
 template <class T, bool HP>

@@ -19,7 +19,7 @@ import oracle
 from depth_wise_attention_rms_amd import binding as b
 from depth_wise_attention_rms_amd import inputs
 from depth_wise_attention_rms_amd.workload import EPS, DeviceStack
-from tests.parity import assert_close_scaled, to_device, to_host
+from tests.parity import assert_close_scaled, sample_rows, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -147,3 +147,40 @@ def test_stack_forward_norm(wl):
     for l in range(wl.L):
         hn_ref, scale = norm_reference(ref["h"][l], ref["h_scale"][l], wl.dtype, Gf[l], eps_f)
         assert_close_scaled(rec[l], hn_ref, scale, wl.dtype, f"{wl.name} hn_{l + 1}")
+
+
+@pytest.mark.parametrize("norm", [False, True])
+def test_phase2_merge_large_rows_nontemporal(norm):
+    """Phase 2 on [R, D] tensors above 1 GiB (R = 75000, D = 7168, bf16),
+    where p, h and hn are written with non-temporal stores: sampled rows
+    against the oracle, p bit-exact."""
+    R, D, dtype = 75000, 7168, "bf16"
+    announce(f"phase2 large R={R} D={D} norm={norm}")
+    dev = []
+    for layer, sigma in ((1, 1.0), (2, 3.0), (3, 2.0)):
+        t = torch.empty((R, D), dtype=torch.bfloat16, device="cuda")
+        dev.append(inputs.fill_normal(t, 53, inputs.ROLE_AUX, layer, sigma))
+    o_d, v_d, p_d = dev
+    lse = (2.0 * inputs.normal(53, inputs.ROLE_AUX, 4, np.arange(R))).astype(np.float32)
+    w = inputs.queries(53, 1, D, sigma=0.3 / math.sqrt(D / 64))[0]
+    gf = inputs.gains(54, D)
+    eps_f = 1e-6
+    lse_d, w_d = torch.from_numpy(lse).cuda(), torch.from_numpy(w).cuda()
+    if norm:
+        hn, h, p_res = b.attnres_phase2_merge_norm(o_d, lse_d, w_d, v_d, gamma_f=torch.from_numpy(gf).cuda(),
+                                                   eps_f=eps_f, p_prev=p_d, eps=EPS, want_h=True)
+    else:
+        h, p_res = b.attnres_phase2_merge(o_d, lse_d, w_d, v_d, p_prev=p_d, eps=EPS)
+    torch.cuda.synchronize()
+    rows = sample_rows(R, 512)
+    ids = torch.from_numpy(rows).cuda()
+    o, v, p = (inputs.tensor_rows(53, inputs.ROLE_AUX, k, rows, D, s, dtype)
+               for k, s in ((1, 1.0), (2, 3.0), (3, 2.0)))
+    ref = oracle.phase2(o, lse[rows], w, p, v, None, eps=EPS)
+    assert_close_scaled(to_host(h[ids]), ref["h"], ref["scale"], dtype, "phase2 h (large)")
+    assert np.array_equal(to_host(p_res[ids]), ref["p"]), "partial p must be bit-exact"
+    if norm:
+        hn_ref, scale = norm_reference(ref["h"], ref["scale"], dtype, gf, eps_f)
+        assert_close_scaled(to_host(hn[ids]), hn_ref, scale, dtype, "phase2 hn (large)")
+    del dev, o_d, v_d, p_d, h, p_res
+    torch.cuda.empty_cache()

@@ -291,6 +291,22 @@ def test_stack_decode_config():
     _check_stack(ds, np.arange(wl.R), chunk=64)
 
 
+@pytest.mark.parametrize("B,T,S", [(1, 200, 24), (2, 100, 12), (1, 40, 24)])
+def test_stack_streamed_phase1_passes(B, T, S):
+    """Streamed Phase 1 with more queries than one register tile at D = 7168
+    (4 per pass), with fused block closes: at 200 rows two passes run side by
+    side per launch and the later launches read the stored block sum; at 40
+    rows all six passes share one launch. L = 2 S + 3: block 2 runs all S
+    queries over two sources, one of them closed on the fly, and block 3 is
+    short."""
+    L = 2 * S + 3
+    wl = inputs.Workload(f"p1_passes_R{B * T}_S{S}", "stack", B=B, T=T, D=7168, dtype="bf16", L=L, S=S,
+                         seed=S + T)
+    announce(wl.name)
+    ds = DeviceStack(wl)
+    _check_stack(ds, np.arange(wl.R), chunk=100)
+
+
 def test_stack_long_context_config():
     """Long-context Block: L = 186, S = 24, T = 131072, D = 7168, bf16, sublayer
     outputs generated per sublayer into a ring; 256 sampled rows."""
