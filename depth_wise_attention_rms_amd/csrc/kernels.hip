@@ -396,7 +396,7 @@ struct P1Shape {
   // w (its hidden slice) of every staged row, so rows need no barrier of their
   // own: the only exchange between waves is the score reduction.
   static constexpr bool PRIVATE = NCH == kP1Waves;
-  static constexpr int FIT = (kP1LdsBytes - 4 * RED - 1024) / (2 * SLOT);
+  static constexpr int FIT = (kP1LdsBytes - 4 * RED - 4 * kP1Waves * 64 - 1024) / (2 * SLOT);
   static constexpr int NBUF = FIT > 4 ? 4 : FIT;  // ring slots (prefetch distance NBUF - 1)
   static_assert(NBUF >= 2, "a row and its successor must fit in LDS");
 };
@@ -542,6 +542,9 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
   // wave may write row r + 1's partials while another still reads row r's
   __shared__ float cred_buf[2 * kP1Waves * kP1MaxS * NC];
   __shared__ float ssred_buf[2 * kP1Waves * NC];
+  // each wave's softmax weights, lane 8 s + i = alpha[s][i]; written and read
+  // back by the same wave only (its LDS accesses complete in order)
+  __shared__ __attribute__((aligned(16))) float alpha_buf[kP1Waves * 64];
 
   const int S = p.S;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -636,7 +639,9 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
     f32x4_t c[4];
     #pragma unroll
     for (int t = 0; t < 4; ++t) c[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const bool two = S > 4;
+    // Both A tiles every k-step (the second is zero for S <= 4): a branch here
+    // would keep the compiler from issuing the next LDS reads ahead of the
+    // current products.
     #pragma unroll
     for (int kk = 0; kk < KS / 2; ++kk) {
       const uint4 b = *reinterpret_cast<const uint4*>(bsrc + 32 * kk);
@@ -652,9 +657,8 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
       const int e = (kk & 1) * 2;
       c[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[2 * kk]),
                                                     __builtin_bit_cast(bf16x8_t, b), c[e], 0, 0, 0);
-      if (two)
-        c[e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[2 * kk + 1]),
-                                                          __builtin_bit_cast(bf16x8_t, b), c[e + 1], 0, 0, 0);
+      c[e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[2 * kk + 1]),
+                                                        __builtin_bit_cast(bf16x8_t, b), c[e + 1], 0, 0, 0);
       if (kP1Fence > 0 && kk % kP1Fence == kP1Fence - 1)
         __builtin_amdgcn_sched_barrier(0);  // bound the LDS reads in flight
     }
@@ -666,9 +670,7 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
       // D element r of lane l is row 4 (l / 16) + r, column l % 16 of its tile:
       // parts r = 0, 1, 2 of query 4 t + l / 16 (part 3 is zero)
       cred[(w * kP1MaxS + kg) * NC + col] = (c[0][0] + c[2][0]) + (c[0][1] + c[2][1]) + (c[0][2] + c[2][2]);
-      if (two)
-        cred[(w * kP1MaxS + 4 + kg) * NC + col] =
-            (c[1][0] + c[3][0]) + (c[1][1] + c[3][1]) + (c[1][2] + c[3][2]);
+      cred[(w * kP1MaxS + 4 + kg) * NC + col] = (c[1][0] + c[3][0]) + (c[1][1] + c[3][1]) + (c[1][2] + c[3][2]);
       if (kg == 0) ssred[w * NC + col] = ss;
     }
     lds_barrier();
@@ -726,10 +728,16 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
         x[k] = k < NC ? *reinterpret_cast<const uint4*>(cur + (size_t)k * STRIDE + tid * 8)
                       : make_uint4(0, 0, 0, 0);
       const int am = l & 31, as = am >> 2, aj = am & 3;
+      // alpha[as][0..7] (lanes 8 as .. 8 as + 7) through this wave's LDS row
+      float* arow = alpha_buf + w * 64;
+      arow[l] = alpha;
+      const float4 a0 = *reinterpret_cast<const float4*>(arow + 8 * as);
+      const float4 a1 = *reinterpret_cast<const float4*>(arow + 8 * as + 4);
+      const float al[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
       float part[8];
       #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float a = __shfl(alpha, 8 * as + k);  // alpha[as][k] (lane 8 as + k)
+        const float a = al[k];
         const float h1 = bf16_round(a);
         const float r1 = a - h1;  // exact
         const float h2 = bf16_round(r1);
@@ -1972,6 +1980,15 @@ static bool phase1_single_eligible(int dtype, const Phase1Args& a) {
 // Streamed Phase 1: elements per lane E = VPL x (elements per vector); the
 // query tile, the SQ numerators and a group of G sources each take E registers
 // per query or source, so wider rows take fewer queries per pass.
+// At 16 elements per lane with 4 queries (D = 7168 bf16), sources in pairs
+// with one pair in flight: 7% faster at 131072 rows and 10% at 128 rows than
+// single sources three ahead (the registers hold one or the other).
+#ifndef ATTNRES_P1_STREAM_G16
+#define ATTNRES_P1_STREAM_G16 2
+#endif
+#ifndef ATTNRES_P1_STREAM_AHEAD16
+#define ATTNRES_P1_STREAM_AHEAD16 1
+#endif
 #ifndef ATTNRES_P1_STREAM_AHEAD
 #define ATTNRES_P1_STREAM_AHEAD 3  // source groups in flight ahead of the one being reduced
 #endif
@@ -2041,8 +2058,9 @@ static hipError_t launch_phase1_stream(const Phase1Args& a, const Launch& L) {
   // tile, so the tile is the smallest that covers S (or the largest that fits
   // the registers, in passes); smaller tiles leave room for larger source
   // groups. bf16 keeps ATTNRES_P1_STREAM_AHEAD groups in flight at 8 and 16
-  // elements per lane; fp32 vectors (and the widest rows) take twice the
-  // registers and keep one.
+  // elements per lane (the 4-query tile at 16: ATTNRES_P1_STREAM_G16 sources
+  // per group, ATTNRES_P1_STREAM_AHEAD16 groups ahead); fp32 vectors (and the
+  // widest rows) take twice the registers and keep one.
   constexpr int PD = T::kBytes == 2 ? ATTNRES_P1_STREAM_AHEAD : 1;
   if (E == 8) {
     if (a.S <= 2) return launch_phase1_stream_t<T, 8 / epv, 4, 2, PD>(p, a, L);
@@ -2052,7 +2070,8 @@ static hipError_t launch_phase1_stream(const Phase1Args& a, const Launch& L) {
   if (E == 16) {
     if (a.S <= 1) return launch_phase1_stream_t<T, 16 / epv, 2, 1, PD>(p, a, L);
     if (a.S <= 2) return launch_phase1_stream_t<T, 16 / epv, 2, 2, PD>(p, a, L);
-    return launch_phase1_stream_t<T, 16 / epv, 1, 4, PD>(p, a, L);
+    return launch_phase1_stream_t<T, 16 / epv, ATTNRES_P1_STREAM_G16, 4,
+                                  T::kBytes == 2 ? ATTNRES_P1_STREAM_AHEAD16 : 1>(p, a, L);
   }
   if constexpr (T::kBytes == 2) {
     if (a.S >= 2) return launch_phase1_stream_t<T, 32 / epv, 1, 2, 1>(p, a, L);
