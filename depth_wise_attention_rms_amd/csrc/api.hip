@@ -156,6 +156,18 @@ int do_close(const char* fn, const void* p, const void* v, void* b, int64_t R, i
 int do_phase1(const char* fn, int dtype, const Phase1Args& a, hipStream_t st) {
   if (a.R == 0) return ATTNRES_OK;
   const int64_t row_bytes = a.D * esize_of(dtype);
+  if (a.out && a.gemm_ws && attnres::phase1_gemm_eligible(dtype, a.n, a.S, a.D, a.R)) {
+    // the scores pass reads materialised sources: close first
+    if (a.close_v) TRY(do_close(fn, a.close_p, a.close_v, a.close_b, a.R, a.D, dtype, st));
+    Phase1Args g = a;
+    g.close_p = nullptr;
+    g.close_v = nullptr;
+    g.close_b = nullptr;
+    const double rb = (double)a.R * row_bytes;
+    const double bytes = rb * (a.n + a.S) + (double)a.R * a.S * ((a.m_out ? 4 : 0) + 4);
+    hipError_t e = attnres::launch_phase1_gemm(g, a.gemm_ws, timed_launch(K_PHASE1, bytes, st));
+    return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
+  }
   if (attnres::phase1_supported(dtype, a.n, a.S, a.D)) {
     const double rb = (double)a.R * row_bytes;
     const double bytes = rb * (a.n + (a.out ? a.S : 0)) + (double)a.R * a.S * ((a.m_out ? 4 : 0) + 4) +
@@ -216,7 +228,7 @@ int plan(int L, int S, int* block_start, int* n_sources) {
 
 // workspace layout of the stack forward, each region 256-byte aligned
 struct StackLayout {
-  size_t q, o, m, lse, p, h, total;
+  size_t q, o, m, lse, p, h, g, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -232,6 +244,11 @@ StackLayout stack_layout(int L, int S, int64_t R, int64_t D, int es) {
   s.lse = off; off = align256(off + (size_t)Sk * R * sizeof(float));
   s.p = off; off = align256(off + (Sk > 2 ? row : 0));
   s.h = off; off = align256(off + row);
+  // the scores/outputs Phase 1 (query parts and softmax weights) where the
+  // widest block's shape takes it
+  s.g = off;
+  if (Sk > 1 && attnres::phase1_gemm_shape(es == 2 ? 1 : 0, Sk, D, R))
+    off = align256(off + attnres::phase1_gemm_workspace(Sk, R, D));
   s.total = off;
   return s;
 }
@@ -549,7 +566,7 @@ int stack_forward(const char* fn, const void* x, int L, int S, int64_t R, int64_
       return one_source ? src[0] : static_cast<const void*>(O + (int64_t)j * tensor_bytes);
     };
     Phase1Args a1{src.data(), n, R, D, Qk, nullptr, Sk, eps, one_source ? nullptr : O, M, LSE,
-                  close_p, close_v, close_b};
+                  close_p, close_v, close_b, lay.g < lay.total ? ws + lay.g : nullptr};
     TRY(do_phase1(fn, dtype, a1, st));
     const void* v_first = nullptr;
     if (nm.on) {

@@ -1577,6 +1577,264 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Phase 1 for many queries over wide rows [K3 9.4 step 1; RH 4.2 Phase 1],
+// bf16, n <= 8 sources, up to 32 queries, in two passes over the sources:
+//
+// Scores. For a tile of rows, the scores of every query against every source
+// of every row form one product C = Qp B, where Qp is [32 MT, D]: row
+// 32 t + 4 s' + j holds part j of query 8 t + s' (parts: the exact three-way
+// bf16 split of the fp32 query, row j = 3 zero), and B is [D, rows x 8]:
+// column 8 r + i is source i of row r. It runs on the matrix cores
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation): each wave owns 4 rows (32
+// columns) and all MT tiles of Qp, whose 128-element chunks are staged in LDS
+// once per workgroup of 8 waves (32 rows) and read by all of them. The
+// hidden axis of a chunk is mapped so that k-group h of a lane holds
+// elements 64 h + 8 ks .. 64 h + 8 ks + 7 in k-step ks (A and B alike), so a
+// lane reads 128 contiguous bytes of its source per chunk. Sums of squares
+// come from the same B registers (v_dot2). After the last chunk each lane
+// holds, for its column, the three parts of 4 queries per tile; their sum
+// scaled by the source's 1 / rms is the score, and the 8 lanes of a row hold
+// its 8 sources, so the softmax is an 8-lane reduction. The weights alpha
+// [S][R][8] (zero past n) and the statistics m, lse are written.
+//
+// Outputs. o_s = sum_i alpha[s][i] b_i, one row per wave group: the row's n
+// sources stay in registers and every query's output is formed from them.
+//
+// Together the passes move (2 n + S) D-vectors per row where query passes of
+// 4 in registers would move (passes x n + S). A block close runs before them
+// as a launch of its own.
+// ---------------------------------------------------------------------------
+constexpr int kGWaves = 8;    // waves per scores workgroup, 4 rows each
+constexpr int kGChunk = 128;  // hidden elements per staged chunk of Qp
+constexpr int kGPad = 8;      // LDS row padding (elements)
+
+struct QSplitParams {
+  const float* W;  // [S][D]
+  const float* G;  // [S][D] or null
+  int S, MT;
+  int64_t D;
+  __bf16* qp;      // [32 MT][D]
+};
+
+__global__ void qsplit_kernel(QSplitParams p) {
+  const int64_t total = (int64_t)p.MT * 32 * p.D;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = idx / p.D, d = idx - m * p.D;
+    const int s = 8 * (int)(m >> 5) + (int)((m & 31) >> 2), j = (int)(m & 3);
+    float part = 0.f;
+    if (s < p.S && j < 3) {
+      const int64_t off = (int64_t)s * p.D + d;
+      const float q = p.G ? p.W[off] * p.G[off] : p.W[off];
+      const float h1 = bf16_round(q);
+      const float r1 = q - h1;  // exact
+      const float h2 = bf16_round(r1);
+      part = j == 0 ? h1 : j == 1 ? h2 : r1 - h2;  // r1 - h2 is exact and a bf16 value
+    }
+    p.qp[idx] = (__bf16)part;
+  }
+}
+
+struct P1GParams {
+  const void* src[8];
+  int n;
+  int S;
+  const __bf16* qp;  // [32 MT][D]
+  float eps;
+  float invD;
+  int64_t R;
+  int D;
+  float* alpha;      // [S][R][8]
+  float* m_out;      // [S][R] or null
+  float* lse_out;    // [S][R]
+};
+
+// One chunk of the scores product: issue the next chunk's Qp staging loads
+// and source loads (into st and bn), then the current chunk's products from
+// b and the Qp chunk in LDS buffer `cur` (this lane reads row `col`, k-group
+// `h`), then stage the next Qp chunk in buffer `nxt`.
+template <int MT>
+__device__ __forceinline__ void gemm_chunk(const uint4 (&b)[8], uint4 (&bn)[8], u32x4_t (&st)[MT],
+                                           f32x16_t (&acc)[MT], float& ss0, float& ss1,
+                                           const __bf16* const (&aptr)[MT], const int (&aoff)[MT],
+                                           int cn, const char* bp, const __bf16* cur, __bf16* nxt,
+                                           int col, int h) {
+  constexpr int AROW = kGChunk + kGPad;
+  const __bf16* ab = cur + col * AROW + 64 * h;
+  #pragma unroll
+  for (int u = 0; u < MT; ++u) st[u] = *reinterpret_cast<const u32x4_t*>(aptr[u] + cn * kGChunk);
+  #pragma unroll
+  for (int ks = 0; ks < 8; ++ks) bn[ks] = ld16_stream(bp + (int64_t)cn * (kGChunk * 2) + 16 * ks);
+  __builtin_amdgcn_sched_barrier(0);  // the prefetch stays ahead of this chunk's work
+  #pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    float& ss = (ks & 1) ? ss1 : ss0;
+    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b[ks].x),
+                                         __builtin_bit_cast(bf16x2v_t, b[ks].x), ss, false);
+    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b[ks].y),
+                                         __builtin_bit_cast(bf16x2v_t, b[ks].y), ss, false);
+    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b[ks].z),
+                                         __builtin_bit_cast(bf16x2v_t, b[ks].z), ss, false);
+    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b[ks].w),
+                                         __builtin_bit_cast(bf16x2v_t, b[ks].w), ss, false);
+    #pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const uint4 a = *reinterpret_cast<const uint4*>(ab + t * 32 * AROW + 8 * ks);
+      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b[ks]), acc[t], 0, 0, 0);
+    }
+  }
+  #pragma unroll
+  for (int u = 0; u < MT; ++u) *reinterpret_cast<u32x4_t*>(nxt + aoff[u]) = st[u];
+  lds_barrier();  // this chunk's Qp reads are done; the next chunk's are in LDS
+}
+
+template <int MT>
+__global__ __launch_bounds__(512) void phase1_gemm_scores_kernel(P1GParams p) {
+  constexpr int AROW = kGChunk + kGPad;
+  __shared__ __attribute__((aligned(16))) __bf16 abuf[2][MT * 32 * AROW];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int col = l & 31, h = l >> 5;    // B column and k-group
+  const int rl = col >> 3, i = col & 7;  // row of the wave's 4, source
+  const int64_t rowbytes = (int64_t)p.D * 2;
+  const int nchunks = p.D / kGChunk;
+  const int64_t tiles = (p.R + 31) / 32;
+
+  // this lane's 128-byte slice of each chunk of its column's source in tile
+  // t (row 0 past the end, source 0 past n: read, then discarded)
+  const char* src_i = static_cast<const char*>(p.src[i < p.n ? i : 0]) + h * 128;
+  auto bptr_of = [&](int64_t t) -> const char* {
+    const int64_t r = t * 32 + w * 4 + rl;
+    return src_i + (r < p.R ? r : 0) * rowbytes;
+  };
+  // Qp staging: thread tid copies 16-byte unit tid + 512 u (u < MT) of a chunk
+  const __bf16* aptr[MT];
+  int aoff[MT];
+  #pragma unroll
+  for (int u = 0; u < MT; ++u) {
+    const int idx = tid + 512 * u, a = idx >> 4, c16 = idx & 15;
+    aptr[u] = p.qp + (int64_t)a * p.D + 8 * c16;
+    aoff[u] = a * AROW + 8 * c16;
+  }
+
+  // The chunk loop runs across tiles without a break: the last chunk of a
+  // tile loads chunk 0 of the workgroup's next tile, and the LDS buffers
+  // alternate throughout. Every load is issued unconditionally.
+  // (the staging registers are native vectors: struct copies between global
+  // memory, registers and LDS would keep them in scratch memory)
+  uint4 b[8], bn[8];
+  u32x4_t st[MT];
+  int buf = 0;
+  const char* bptr = bptr_of(blockIdx.x);
+  #pragma unroll
+  for (int u = 0; u < MT; ++u) st[u] = *reinterpret_cast<const u32x4_t*>(aptr[u]);
+  #pragma unroll
+  for (int ks = 0; ks < 8; ++ks) b[ks] = ld16_stream(bptr + 16 * ks);
+  #pragma unroll
+  for (int u = 0; u < MT; ++u) *reinterpret_cast<u32x4_t*>(&abuf[0][aoff[u]]) = st[u];
+  lds_barrier();
+
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const int64_t row = tile * 32 + w * 4 + rl;
+    const bool rv = row < p.R;
+    const char* bnext = bptr_of(tile + gridDim.x);
+    f32x16_t acc[MT];
+    #pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = f32x16_t{};
+    float ss0 = 0.f, ss1 = 0.f;
+    // chunks in pairs (D is a multiple of 256), the two register sets
+    // trading roles; the tile's last chunk prefetches the next tile's first
+    for (int c = 0; c < nchunks; c += 2) {
+      gemm_chunk<MT>(b, bn, st, acc, ss0, ss1, aptr, aoff, c + 1, bptr, abuf[buf], abuf[buf ^ 1], col, h);
+      buf ^= 1;
+      const bool last = c + 2 == nchunks;
+      gemm_chunk<MT>(bn, b, st, acc, ss0, ss1, aptr, aoff, last ? 0 : c + 2, last ? bnext : bptr,
+                     abuf[buf], abuf[buf ^ 1], col, h);
+      buf ^= 1;
+    }
+    bptr = bnext;
+
+    // scores, softmax over the row's 8 lanes, weights and statistics
+    float ss = ss0 + ss1;
+    ss += __shfl_xor(ss, 32);  // the two k-groups of this column
+    const float inv = rsqrtf(ss * p.invD + p.eps);
+    const bool valid = i < p.n;
+    #pragma unroll
+    for (int t = 0; t < MT; ++t)
+      #pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // accumulators 4 g .. 4 g + 2 of lane half h: parts 0..2 of query 8 t + 2 g + h
+        const int s = 8 * t + 2 * g + h;
+        const float sc = ((acc[t][4 * g] + acc[t][4 * g + 1]) + acc[t][4 * g + 2]) * inv;
+        const float m = group8_max(valid ? sc : -INFINITY);
+        const float e = valid ? __expf(sc - m) : 0.f;
+        const float z = group8_sum(e);
+        if (rv && s < p.S) {
+          p.alpha[((int64_t)s * p.R + row) * 8 + i] = e * (1.0f / z);
+          if (i == 0) {
+            if (p.m_out) p.m_out[(int64_t)s * p.R + row] = m;
+            p.lse_out[(int64_t)s * p.R + row] = m + __logf(z);
+          }
+        }
+      }
+  }
+}
+
+struct P1OParams {
+  const void* src[8];
+  int S;
+  const float* alpha;  // [S][R][8]
+  void* out;           // [S][R][D]
+  Geom g;
+};
+
+template <int NC, bool NT>
+__global__ __launch_bounds__(512) void phase1_gemm_outputs_kernel(P1OParams p) {
+  constexpr int VPL = 2;
+  const Geom& g = p.g;
+  const Lanes ln(g.W);
+  const int64_t rowbytes = (int64_t)g.V * 16;
+  for (int64_t grp = blockIdx.x; grp < g.groups; grp += gridDim.x) {
+    // one row per wave group: uniform across the wave, so the weights are
+    // scalar loads
+    const int64_t row = __builtin_amdgcn_readfirstlane((int)(grp * g.RPW + ln.slot));
+    const bool rv = row < g.R;
+    const int64_t base = (rv ? row : 0) * rowbytes;
+    float x[NC][VPL][8];
+    bool own[VPL];
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      const int vec = c * ln.stride + ln.t;
+      own[c] = rv && vec < g.V;
+      const int64_t off = base + (int64_t)(vec < g.V ? vec : 0) * 16;
+      #pragma unroll
+      for (int i = 0; i < NC; ++i) Bf16::unpack(ld16_stream(static_cast<const char*>(p.src[i]) + off), x[i][c]);
+    }
+    const float* arow = p.alpha + (rv ? row : 0) * 8;
+    for (int s = 0; s < p.S; ++s) {
+      const float4 a0 = *reinterpret_cast<const float4*>(arow + (int64_t)s * g.R * 8);
+      const float4 a1 = *reinterpret_cast<const float4*>(arow + (int64_t)s * g.R * 8 + 4);
+      const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      char* orow = static_cast<char*>(p.out) + (int64_t)s * g.R * rowbytes + base;
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        float o[8];
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float acc = a[0] * x[0][c][e];
+          #pragma unroll
+          for (int i = 1; i < NC; ++i) acc = fmaf(a[i], x[i][c][e], acc);
+          o[e] = acc;
+        }
+        char* dst = store_target(own[c], orow + (int64_t)(c * ln.stride + ln.t) * 16);
+        if constexpr (NT) st16_stream(dst, Bf16::pack(o));
+        else st16(dst, Bf16::pack(o));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Phase 2 (one intra-block merge step) [K3 9.4 step 2, OS2, single-source
 // triple; RH 4.2 Phase 2]: p = p_prev + v_prev rounded to the I/O dtype (or
 // p = v_prev on the first merge), the score of the rounded p, then
@@ -1813,9 +2071,11 @@ __global__ void close_kernel(const void* __restrict__ pp, const void* __restrict
 // ---------------------------------------------------------------------------
 
 #ifndef ATTNRES_PHASE2_NT_BYTES
-// [R, D] tensors larger than this are written non-temporally by Phase 2
+// [R, D] tensors larger than this are written non-temporally by Phase 2 and
+// by the Phase-1 outputs pass
 #define ATTNRES_PHASE2_NT_BYTES (1024.0 * 1024.0 * 1024.0)
 #endif
+
 #ifndef ATTNRES_PHASE2_VPL
 #define ATTNRES_PHASE2_VPL 2  // preferred vectors per lane in Phase 2 (rows take up to 4 waves)
 #endif
@@ -2077,6 +2337,92 @@ static hipError_t launch_phase1_stream(const Phase1Args& a, const Launch& L) {
     if (a.S >= 2) return launch_phase1_stream_t<T, 32 / epv, 1, 2, 1>(p, a, L);
   }
   return launch_phase1_stream_t<T, 32 / epv, 1, 1, 1>(p, a, L);
+}
+
+#ifndef ATTNRES_P1_GEMM_MIN_ROWS
+#define ATTNRES_P1_GEMM_MIN_ROWS 4096  // fewer rows: the streamed kernel (its passes run side by side)
+#endif
+
+static int gemm_tiles(int S) { return (S + 7) / 8; }
+
+bool phase1_gemm_shape(int dtype, int S, int64_t D, int64_t R) {
+  return dtype == 1 && S >= 1 && S <= 32 && D % (2 * kGChunk) == 0 && D <= 8192 &&
+         R >= ATTNRES_P1_GEMM_MIN_ROWS;
+}
+
+bool phase1_gemm_eligible(int dtype, int n, int S, int64_t D, int64_t R) {
+  return n >= 1 && n <= 8 && phase1_gemm_shape(dtype, S, D, R) && !phase1_mfma_eligible(dtype, n, S, D);
+}
+
+static size_t gemm_qp_bytes(int S, int64_t D) {
+  return ((size_t)32 * gemm_tiles(S) * D * 2 + 255) & ~(size_t)255;
+}
+
+size_t phase1_gemm_workspace(int S, int64_t R, int64_t D) {
+  return gemm_qp_bytes(S, D) + (size_t)S * R * 8 * sizeof(float);
+}
+
+template <int MT>
+static hipError_t launch_gemm_scores(const P1GParams& g, const Launch& L) {
+  const int64_t tiles = (g.R + 31) / 32;
+  const unsigned grid = (unsigned)(tiles < (1 << 20) ? tiles : (1 << 20));
+  return launch(L, phase1_gemm_scores_kernel<MT>, dim3(grid), dim3(64 * kGWaves), 0, g);
+}
+
+template <int NC>
+static hipError_t launch_gemm_outputs(const P1OParams& o, bool nt, const Launch& L) {
+  const unsigned grid = grid_for(o.g);
+  const dim3 block(64 * o.g.W * o.g.RPW);
+  if (nt) return launch(L, phase1_gemm_outputs_kernel<NC, true>, dim3(grid), block, 0, o);
+  return launch(L, phase1_gemm_outputs_kernel<NC, false>, dim3(grid), block, 0, o);
+}
+
+// Phase 1 as a query split, a matrix-core scores pass and an outputs pass
+// (see phase1_gemm_scores_kernel). The sources must be materialised (no
+// fused close); `ws` holds phase1_gemm_workspace(S, R, D) bytes.
+hipError_t launch_phase1_gemm(const Phase1Args& a, void* ws, const Launch& L) {
+  if (a.close_v || !a.out || !phase1_gemm_eligible(1, a.n, a.S, a.D, a.R)) return hipErrorInvalidValue;
+  const int MT = gemm_tiles(a.S);
+  __bf16* qp = static_cast<__bf16*>(ws);
+  float* alpha = reinterpret_cast<float*>(static_cast<char*>(ws) + gemm_qp_bytes(a.S, a.D));
+  // timed from the split's start to the outputs pass's end
+  const Launch first{L.stream, L.start, nullptr}, mid{L.stream, nullptr, nullptr}, last{L.stream, nullptr, L.stop};
+  {
+    QSplitParams q{a.W, a.G, a.S, MT, a.D, qp};
+    const int64_t blocks = ((int64_t)MT * 32 * a.D + 255) / 256;
+    hipError_t e = launch(first, qsplit_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, q);
+    if (e != hipSuccess) return e;
+  }
+  {
+    P1GParams g;
+    for (int i = 0; i < 8; ++i) g.src[i] = i < a.n ? a.src[i] : a.src[0];
+    g.n = a.n; g.S = a.S; g.qp = qp; g.eps = a.eps; g.invD = 1.0f / (float)a.D;
+    g.R = a.R; g.D = (int)a.D; g.alpha = alpha; g.m_out = a.m_out; g.lse_out = a.lse_out;
+    hipError_t e;
+    switch (MT) {
+      case 1: e = launch_gemm_scores<1>(g, mid); break;
+      case 2: e = launch_gemm_scores<2>(g, mid); break;
+      case 3: e = launch_gemm_scores<3>(g, mid); break;
+      default: e = launch_gemm_scores<4>(g, mid); break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  P1OParams o;
+  for (int i = 0; i < 8; ++i) o.src[i] = i < a.n ? a.src[i] : a.src[0];
+  o.S = a.S; o.alpha = alpha; o.out = a.out;
+  o.g = make_geom(a.R, a.D, 2, 2, 8);
+  if (o.g.W > 8) return hipErrorInvalidValue;
+  const bool nt = (double)a.R * a.D * 2 > (double)ATTNRES_PHASE2_NT_BYTES;
+  switch (a.n) {
+    case 1: return launch_gemm_outputs<1>(o, nt, last);
+    case 2: return launch_gemm_outputs<2>(o, nt, last);
+    case 3: return launch_gemm_outputs<3>(o, nt, last);
+    case 4: return launch_gemm_outputs<4>(o, nt, last);
+    case 5: return launch_gemm_outputs<5>(o, nt, last);
+    case 6: return launch_gemm_outputs<6>(o, nt, last);
+    case 7: return launch_gemm_outputs<7>(o, nt, last);
+    default: return launch_gemm_outputs<8>(o, nt, last);
+  }
 }
 
 #ifndef ATTNRES_P1_STREAM

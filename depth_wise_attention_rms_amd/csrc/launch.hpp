@@ -32,6 +32,9 @@ struct Phase1Args {
   const void* close_p;
   const void* close_v;
   void* close_b;
+  // workspace of phase1_gemm_workspace(S, R, D) bytes, or null: with it,
+  // shapes phase1_gemm_eligible() accepts take the scores/outputs passes
+  void* gemm_ws = nullptr;
 };
 
 struct AggArgs {
@@ -107,6 +110,13 @@ hipError_t launch_bwd_reduce(const BwdArgs& a, const BwdPlan& pl, int stage, con
 
 hipError_t launch_fold(const float* w, const float* g, float* q, int64_t count, const Launch& L);
 hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L);
+// Phase 1 as a matrix-core scores pass and an outputs pass (bf16, n <= 8,
+// S <= 32, D a multiple of 256 up to 8192, many rows); needs materialised
+// sources (no fused close) and a workspace of phase1_gemm_workspace bytes.
+bool phase1_gemm_shape(int dtype, int S, int64_t D, int64_t R);
+bool phase1_gemm_eligible(int dtype, int n, int S, int64_t D, int64_t R);
+size_t phase1_gemm_workspace(int S, int64_t R, int64_t D);
+hipError_t launch_phase1_gemm(const Phase1Args& a, void* ws, const Launch& L);
 bool phase1_supported(int dtype, int n, int S, int64_t D);
 // Phase 1 with out == null (statistics only) is available for these shapes
 bool phase1_stats_supported(int dtype, int n, int S, int64_t D);

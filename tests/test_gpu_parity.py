@@ -307,6 +307,34 @@ def test_stack_streamed_phase1_passes(B, T, S):
     _check_stack(ds, np.arange(wl.R), chunk=100)
 
 
+GEMM_STACKS = [
+    # (B, T, D, S, L): Phase 1 on the matrix-core scores pass and the outputs
+    # pass (bf16, more than 8 queries or a width outside the register-tile
+    # kernel, at least 4096 rows); ragged row tiles; 24 queries (3 Qp tiles)
+    # then a 5-query block; sources 2..8 with S = 12, then 9 sources, which
+    # fall back to the streamed kernel; 32 queries (4 tiles) at D = 1024; 9
+    # queries at D = 4096
+    (1, 4100, 7168, 24, 53),
+    (2, 2048, 7168, 12, 99),
+    (4, 2048, 1024, 32, 71),
+    (1, 4096, 4096, 9, 20),
+]
+
+
+@pytest.mark.parametrize("B,T,D,S,L", GEMM_STACKS)
+def test_stack_gemm_phase1(B, T, D, S, L):
+    """Block stacks whose Phase 1 runs as the scores/outputs passes, with the
+    block close as its own launch: sampled rows of every h_l, y and the block
+    sums against the oracle's naive forward."""
+    wl = inputs.Workload(f"gemm_p1_R{B * T}_D{D}_S{S}_L{L}", "stack", B=B, T=T, D=D, dtype="bf16", L=L, S=S,
+                         seed=L + S)
+    announce(wl.name)
+    ds = DeviceStack(wl)
+    _check_stack(ds, sample_rows(wl.R, 192), chunk=64)
+    del ds
+    torch.cuda.empty_cache()
+
+
 def test_stack_long_context_config():
     """Long-context Block: L = 186, S = 24, T = 131072, D = 7168, bf16, sublayer
     outputs generated per sublayer into a ring; 256 sampled rows."""
