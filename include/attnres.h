@@ -161,7 +161,13 @@ typedef int (*attnres_sublayer_fn)(void* ctx, int l, const void* h_l, const void
 int attnres_table_sublayer(void* ctx, int l, const void* h_l, const void** v_out, void* stream);
 
 /* Bytes of workspace attnres_block_stack_forward needs for (L, S, R, D, dtype);
- * 0 for invalid arguments. */
+ * 0 for invalid arguments. It holds the folded queries, one block's Phase-1
+ * outputs and statistics, the partial sum and h; for bf16 stacks of at least
+ * 4096 rows whose widest block has more than 8 queries or a width outside
+ * {1024, 2048, 3072, 4096} (D a multiple of 256 up to 8192, at most 32
+ * queries), also the query parts [32 ceil(S/8), D] bf16 and the softmax
+ * weights [S, R, 8] fp32 of the matrix-core scores pass, which then runs
+ * Phase 1 for blocks of at most 8 sources. */
 size_t attnres_stack_workspace_bytes(int L, int S, int64_t R, int64_t D, int dtype);
 
 /* ---------------------------------------------------------------------------
