@@ -1587,10 +1587,10 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
 // column 8 r + i is source i of row r. It runs on the matrix cores
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulation): each wave owns 4 rows (32
 // columns) and all MT tiles of Qp, whose 128-element chunks are staged in LDS
-// once per workgroup of 8 waves (32 rows) and read by all of them. The
-// hidden axis of a chunk is mapped so that k-group h of a lane holds
-// elements 64 h + 8 ks .. 64 h + 8 ks + 7 in k-step ks (A and B alike), so a
-// lane reads 128 contiguous bytes of its source per chunk. Sums of squares
+// once per workgroup of 8 waves (32 rows) and read by all of them. In k-step
+// ks of a chunk, k-group h holds elements 16 ks + 8 h .. 16 ks + 8 h + 7 (A
+// and B alike), so the two lanes of a column read 32 adjacent bytes of its
+// source and each 128-byte line is complete after 4 loads. Sums of squares
 // come from the same B registers (v_dot2). After the last chunk each lane
 // holds, for its column, the three parts of 4 queries per tile; their sum
 // scaled by the source's 1 / rms is the score, and the 8 lanes of a row hold
@@ -1660,11 +1660,11 @@ __device__ __forceinline__ void gemm_chunk(const uint4 (&b)[8], uint4 (&bn)[8], 
                                            int cn, const char* bp, const __bf16* cur, __bf16* nxt,
                                            int col, int h) {
   constexpr int AROW = kGChunk + kGPad;
-  const __bf16* ab = cur + col * AROW + 64 * h;
+  const __bf16* ab = cur + col * AROW + 8 * h;
   #pragma unroll
   for (int u = 0; u < MT; ++u) st[u] = *reinterpret_cast<const u32x4_t*>(aptr[u] + cn * kGChunk);
   #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) bn[ks] = ld16_stream(bp + (int64_t)cn * (kGChunk * 2) + 16 * ks);
+  for (int ks = 0; ks < 8; ++ks) bn[ks] = ld16_stream(bp + (int64_t)cn * (kGChunk * 2) + 32 * ks);
   __builtin_amdgcn_sched_barrier(0);  // the prefetch stays ahead of this chunk's work
   #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
@@ -1679,7 +1679,7 @@ __device__ __forceinline__ void gemm_chunk(const uint4 (&b)[8], uint4 (&bn)[8], 
                                          __builtin_bit_cast(bf16x2v_t, b[ks].w), ss, false);
     #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      const uint4 a = *reinterpret_cast<const uint4*>(ab + t * 32 * AROW + 8 * ks);
+      const uint4 a = *reinterpret_cast<const uint4*>(ab + t * 32 * AROW + 16 * ks);
       acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                        __builtin_bit_cast(bf16x8_t, b[ks]), acc[t], 0, 0, 0);
     }
@@ -1700,9 +1700,9 @@ __global__ __launch_bounds__(512) void phase1_gemm_scores_kernel(P1GParams p) {
   const int nchunks = p.D / kGChunk;
   const int64_t tiles = (p.R + 31) / 32;
 
-  // this lane's 128-byte slice of each chunk of its column's source in tile
+  // this lane's 16-byte pieces of each chunk of its column's source in tile
   // t (row 0 past the end, source 0 past n: read, then discarded)
-  const char* src_i = static_cast<const char*>(p.src[i < p.n ? i : 0]) + h * 128;
+  const char* src_i = static_cast<const char*>(p.src[i < p.n ? i : 0]) + h * 16;
   auto bptr_of = [&](int64_t t) -> const char* {
     const int64_t r = t * 32 + w * 4 + rl;
     return src_i + (r < p.R ? r : 0) * rowbytes;
@@ -1729,7 +1729,7 @@ __global__ __launch_bounds__(512) void phase1_gemm_scores_kernel(P1GParams p) {
   #pragma unroll
   for (int u = 0; u < MT; ++u) st[u] = *reinterpret_cast<const u32x4_t*>(aptr[u]);
   #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) b[ks] = ld16_stream(bptr + 16 * ks);
+  for (int ks = 0; ks < 8; ++ks) b[ks] = ld16_stream(bptr + 32 * ks);
   #pragma unroll
   for (int u = 0; u < MT; ++u) *reinterpret_cast<u32x4_t*>(&abuf[0][aoff[u]]) = st[u];
   lds_barrier();
