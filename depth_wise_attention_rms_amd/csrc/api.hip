@@ -247,7 +247,8 @@ StackLayout stack_layout(int L, int S, int64_t R, int64_t D, int es) {
   // the scores/outputs Phase 1 (query parts and softmax weights) where the
   // widest block's shape takes it
   s.g = off;
-  if (Sk > 1 && attnres::phase1_gemm_shape(es == 2 ? 1 : 0, Sk, D, R))
+  if (Sk > 1 && attnres::phase1_gemm_shape(es == 2 ? 1 : 0, Sk, D, R) &&
+      !attnres::phase1_mfma_eligible(es == 2 ? 1 : 0, 1, Sk, D))
     off = align256(off + attnres::phase1_gemm_workspace(Sk, R, D));
   s.total = off;
   return s;

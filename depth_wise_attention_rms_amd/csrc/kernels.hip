@@ -2159,7 +2159,7 @@ static hipError_t launch_phase1_dt(const Phase1Args& a, const Launch& L) {
   return hipErrorInvalidValue;
 }
 
-static bool phase1_mfma_eligible(int dtype, int n, int S, int64_t D) {
+bool phase1_mfma_eligible(int dtype, int n, int S, int64_t D) {
   return dtype == 1 && n >= 1 && n <= kP1MaxN && S >= 1 && S <= kP1MaxS &&
          (D == 1024 || D == 2048 || D == 3072 || D == 4096);
 }

@@ -114,6 +114,8 @@ hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L);
 // S <= 32, D a multiple of 256 up to 8192, many rows); needs materialised
 // sources (no fused close) and a workspace of phase1_gemm_workspace bytes.
 bool phase1_gemm_shape(int dtype, int S, int64_t D, int64_t R);
+// the register-tile matrix-core Phase 1 (bf16, n <= 8, S <= 8, D in {1024, 2048, 3072, 4096})
+bool phase1_mfma_eligible(int dtype, int n, int S, int64_t D);
 bool phase1_gemm_eligible(int dtype, int n, int S, int64_t D, int64_t R);
 size_t phase1_gemm_workspace(int S, int64_t R, int64_t D);
 hipError_t launch_phase1_gemm(const Phase1Args& a, void* ws, const Launch& L);

@@ -156,6 +156,34 @@ def test_workspace_bytes_cover_the_regions():
     assert L.attnres_stack_workspace_bytes(16, 1, 2048, 1024, 1) >= 2048 * 1024 * 2
 
 
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("L_,S,R,D,dt,scores_pass", [
+    (186, 24, 131072, 7168, 1, True),    # long context: the matrix-core scores pass
+    (96, 12, 128, 7168, 1, False),       # decode: too few rows, streamed Phase 1
+    (48, 8, 16384, 4096, 1, False),      # register-tile Phase 1
+    (20, 9, 4096, 4096, 1, True),        # 9 queries at D = 4096
+    (20, 9, 4096, 4096, 0, False),       # fp32 never takes it
+    (20, 9, 4096, 4000, 1, False),       # D not a multiple of 256
+    (40, 33, 8192, 1024, 1, False),      # more than 32 queries
+])
+def test_workspace_bytes_layout(L_, S, R, D, dt, scores_pass):
+    """The stack workspace is the 256-byte-aligned regions the header lists:
+    folded queries, one block's Phase-1 outputs and statistics, the partial,
+    h, and -- where the widest block takes the matrix-core scores pass -- the
+    query parts [32 ceil(S/8), D] bf16 and the weights [S, R, 8] fp32."""
+    es = 2 if dt == 1 else 4
+    Sk = min(S, L_)
+    row = R * D * es
+    want = _a256((L_ + 1) * D * 4) + _a256(Sk * row if Sk > 1 else 0) + 2 * _a256(Sk * R * 4)
+    want += _a256(row if Sk > 2 else 0) + _a256(row)
+    if scores_pass:
+        want += _a256(_a256(32 * ((Sk + 7) // 8) * D * 2) + Sk * R * 8 * 4)
+    assert b.lib().attnres_stack_workspace_bytes(L_, S, R, D, dt) == want
+
+
 def test_generator_twin_rounding_and_distribution():
     # bf16 rounding of the twin equals torch's nearest-even fp32 -> bf16 for fp32 values
     import torch
