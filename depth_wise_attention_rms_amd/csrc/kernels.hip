@@ -2346,8 +2346,9 @@ static hipError_t launch_phase1_stream(const Phase1Args& a, const Launch& L) {
 static int gemm_tiles(int S) { return (S + 7) / 8; }
 
 bool phase1_gemm_shape(int dtype, int S, int64_t D, int64_t R) {
+  // (the outputs pass keeps its row index in a 32-bit scalar register)
   return dtype == 1 && S >= 1 && S <= 32 && D % (2 * kGChunk) == 0 && D <= 8192 &&
-         R >= ATTNRES_P1_GEMM_MIN_ROWS;
+         R >= ATTNRES_P1_GEMM_MIN_ROWS && R <= INT32_MAX;
 }
 
 bool phase1_gemm_eligible(int dtype, int n, int S, int64_t D, int64_t R) {
