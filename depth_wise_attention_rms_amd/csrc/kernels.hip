@@ -1582,19 +1582,21 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
 //
 // Scores. For a tile of rows, the scores of every query against every source
 // of every row form one product C = Qp B, where Qp is [32 MT, D]: row
-// 32 t + 4 s' + j holds part j of query 8 t + s' (parts: the exact three-way
-// bf16 split of the fp32 query, row j = 3 zero), and B is [D, rows x 8]:
-// column 8 r + i is source i of row r. It runs on the matrix cores
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulation): each wave owns 4 rows (32
-// columns) and all MT tiles of Qp, whose 128-element chunks are staged in LDS
-// once per workgroup of 8 waves (32 rows) and read by all of them. In k-step
-// ks of a chunk, k-group h holds elements 16 ks + 8 h .. 16 ks + 8 h + 7 (A
-// and B alike), so the two lanes of a column read 32 adjacent bytes of its
-// source and each 128-byte line is complete after 4 loads. Sums of squares
-// come from the same B registers (v_dot2). After the last chunk each lane
-// holds, for its column, the three parts of 4 queries per tile; their sum
-// scaled by the source's 1 / rms is the score, and the 8 lanes of a row hold
-// its 8 sources, so the softmax is an 8-lane reduction. The weights alpha
+// 4 q + j holds part j of query q (parts: the exact three-way bf16 split of
+// the fp32 query, row j = 3 zero), and B is [D, rows x 8]: column 8 r + i is
+// source i of row r. It runs on the matrix cores (v_mfma_f32_16x16x32_bf16,
+// fp32 accumulation): each wave owns 2 rows (16 columns) and all 2 MT 16-row
+// tiles of Qp (4 queries each), whose 128-element chunks are staged in LDS
+// once per workgroup of 16 waves (32 rows) and read by all of them. In k-step
+// ks of a chunk, k-group g of a lane holds elements 32 ks + 8 g ..
+// 32 ks + 8 g + 7 (A and B alike), so the four lanes of a column read 64
+// adjacent bytes of its source per load: each load touches 2 lines per row
+// and source where 32x32 tiles (2 lanes per column) touched 4, which took a
+// block of the long-context shape from 14.5 to 11.6 ms. Sums of squares come
+// from the same B registers (v_dot2). After the last chunk each lane holds,
+// for its column, the three parts of one query per tile; their sum scaled by
+// the source's 1 / rms is the score, and the 8 lanes of a row hold its 8
+// sources, so the softmax is an 8-lane reduction. The weights alpha
 // [S][R][8] (zero past n) and the statistics m, lse are written.
 //
 // Outputs. o_s = sum_i alpha[s][i] b_i, one row per wave group: the row's n
@@ -1604,7 +1606,7 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
 // 4 in registers would move (passes x n + S). A block close runs before them
 // as a launch of its own.
 // ---------------------------------------------------------------------------
-constexpr int kGWaves = 8;    // waves per scores workgroup, 4 rows each
+constexpr int kGWaves = 16;   // waves per scores workgroup, 2 rows each
 constexpr int kGChunk = 128;  // hidden elements per staged chunk of Qp
 constexpr int kGPad = 8;      // LDS row padding (elements)
 
@@ -1651,23 +1653,24 @@ struct P1GParams {
 
 // One chunk of the scores product: issue the next chunk's Qp staging loads
 // and source loads (into st and bn), then the current chunk's products from
-// b and the Qp chunk in LDS buffer `cur` (this lane reads row `col`, k-group
-// `h`), then stage the next Qp chunk in buffer `nxt`.
+// b and the Qp chunk in LDS buffer `cur` (this lane reads row `col` of each
+// 16-row tile, k-group `g4`), then stage the next Qp chunk in buffer `nxt`.
 template <int MT>
-__device__ __forceinline__ void gemm_chunk(const uint4 (&b)[8], uint4 (&bn)[8], u32x4_t (&st)[MT],
-                                           f32x16_t (&acc)[MT], float& ss0, float& ss1,
-                                           const __bf16* const (&aptr)[MT], const int (&aoff)[MT],
-                                           int cn, const char* bp, const __bf16* cur, __bf16* nxt,
-                                           int col, int h) {
+__device__ __forceinline__ void gemm_chunk(const uint4 (&b)[4], uint4 (&bn)[4], u32x4_t (&st)[(MT + 1) / 2],
+                                           f32x4_t (&acc)[2 * MT], float& ss0, float& ss1,
+                                           const __bf16* const (&aptr)[(MT + 1) / 2],
+                                           const int (&aoff)[(MT + 1) / 2], int cn, const char* bp,
+                                           const __bf16* cur, __bf16* nxt, int col, int g4) {
   constexpr int AROW = kGChunk + kGPad;
-  const __bf16* ab = cur + col * AROW + 8 * h;
+  constexpr int U = (MT + 1) / 2;
+  const __bf16* ab = cur + col * AROW + 8 * g4;
   #pragma unroll
-  for (int u = 0; u < MT; ++u) st[u] = *reinterpret_cast<const u32x4_t*>(aptr[u] + cn * kGChunk);
+  for (int u = 0; u < U; ++u) st[u] = *reinterpret_cast<const u32x4_t*>(aptr[u] + cn * kGChunk);
   #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) bn[ks] = ld16_stream(bp + (int64_t)cn * (kGChunk * 2) + 32 * ks);
+  for (int ks = 0; ks < 4; ++ks) bn[ks] = ld16_stream(bp + (int64_t)cn * (kGChunk * 2) + 64 * ks);
   __builtin_amdgcn_sched_barrier(0);  // the prefetch stays ahead of this chunk's work
   #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
+  for (int ks = 0; ks < 4; ++ks) {
     float& ss = (ks & 1) ? ss1 : ss0;
     ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b[ks].x),
                                          __builtin_bit_cast(bf16x2v_t, b[ks].x), ss, false);
@@ -1678,105 +1681,109 @@ __device__ __forceinline__ void gemm_chunk(const uint4 (&b)[8], uint4 (&bn)[8], 
     ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b[ks].w),
                                          __builtin_bit_cast(bf16x2v_t, b[ks].w), ss, false);
     #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const uint4 a = *reinterpret_cast<const uint4*>(ab + t * 32 * AROW + 16 * ks);
-      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+    for (int t = 0; t < 2 * MT; ++t) {
+      const uint4 a = *reinterpret_cast<const uint4*>(ab + t * 16 * AROW + 32 * ks);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                        __builtin_bit_cast(bf16x8_t, b[ks]), acc[t], 0, 0, 0);
     }
   }
   #pragma unroll
-  for (int u = 0; u < MT; ++u) *reinterpret_cast<u32x4_t*>(nxt + aoff[u]) = st[u];
+  for (int u = 0; u < U; ++u) *reinterpret_cast<u32x4_t*>(nxt + aoff[u]) = st[u];
   lds_barrier();  // this chunk's Qp reads are done; the next chunk's are in LDS
 }
 
 template <int MT>
-__global__ __launch_bounds__(512) void phase1_gemm_scores_kernel(P1GParams p) {
+__global__ __launch_bounds__(1024) void phase1_gemm_scores_kernel(P1GParams p) {
   constexpr int AROW = kGChunk + kGPad;
+  constexpr int U = (MT + 1) / 2;  // Qp staging units per thread
   __shared__ __attribute__((aligned(16))) __bf16 abuf[2][MT * 32 * AROW];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int col = l & 31, h = l >> 5;    // B column and k-group
-  const int rl = col >> 3, i = col & 7;  // row of the wave's 4, source
+  const int col = l & 15, g4 = l >> 4;   // B column and k-group
+  const int rl = col >> 3, i = col & 7;  // row of the wave's 2, source
   const int64_t rowbytes = (int64_t)p.D * 2;
   const int nchunks = p.D / kGChunk;
   const int64_t tiles = (p.R + 31) / 32;
 
   // this lane's 16-byte pieces of each chunk of its column's source in tile
   // t (row 0 past the end, source 0 past n: read, then discarded)
-  const char* src_i = static_cast<const char*>(p.src[i < p.n ? i : 0]) + h * 16;
+  const char* src_i = static_cast<const char*>(p.src[i < p.n ? i : 0]) + g4 * 16;
   auto bptr_of = [&](int64_t t) -> const char* {
-    const int64_t r = t * 32 + w * 4 + rl;
+    const int64_t r = t * 32 + w * 2 + rl;
     return src_i + (r < p.R ? r : 0) * rowbytes;
   };
-  // Qp staging: thread tid copies 16-byte unit tid + 512 u (u < MT) of a chunk
-  const __bf16* aptr[MT];
-  int aoff[MT];
+  // Qp staging: thread tid copies 16-byte unit tid + 1024 u of a chunk's
+  // 512 MT units; for odd MT the units past the end repeat the 512 below them
+  // (the same value written to the same place twice)
+  const __bf16* aptr[U];
+  int aoff[U];
   #pragma unroll
-  for (int u = 0; u < MT; ++u) {
-    const int idx = tid + 512 * u, a = idx >> 4, c16 = idx & 15;
+  for (int u = 0; u < U; ++u) {
+    int idx = tid + 1024 * u;
+    if (idx >= 512 * MT) idx -= 512;
+    const int a = idx >> 4, c16 = idx & 15;
     aptr[u] = p.qp + (int64_t)a * p.D + 8 * c16;
     aoff[u] = a * AROW + 8 * c16;
   }
 
   // The chunk loop runs across tiles without a break: the last chunk of a
   // tile loads chunk 0 of the workgroup's next tile, and the LDS buffers
-  // alternate throughout. Every load is issued unconditionally.
-  // (the staging registers are native vectors: struct copies between global
-  // memory, registers and LDS would keep them in scratch memory)
-  uint4 b[8], bn[8];
-  u32x4_t st[MT];
+  // alternate throughout. Every load is issued unconditionally. (The staging
+  // registers are native vectors: struct copies between global memory,
+  // registers and LDS would keep them in scratch memory.)
+  uint4 b[4], bn[4];
+  u32x4_t st[U];
   int buf = 0;
   const char* bptr = bptr_of(blockIdx.x);
   #pragma unroll
-  for (int u = 0; u < MT; ++u) st[u] = *reinterpret_cast<const u32x4_t*>(aptr[u]);
+  for (int u = 0; u < U; ++u) st[u] = *reinterpret_cast<const u32x4_t*>(aptr[u]);
   #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) b[ks] = ld16_stream(bptr + 32 * ks);
+  for (int ks = 0; ks < 4; ++ks) b[ks] = ld16_stream(bptr + 64 * ks);
   #pragma unroll
-  for (int u = 0; u < MT; ++u) *reinterpret_cast<u32x4_t*>(&abuf[0][aoff[u]]) = st[u];
+  for (int u = 0; u < U; ++u) *reinterpret_cast<u32x4_t*>(&abuf[0][aoff[u]]) = st[u];
   lds_barrier();
 
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-    const int64_t row = tile * 32 + w * 4 + rl;
+    const int64_t row = tile * 32 + w * 2 + rl;
     const bool rv = row < p.R;
     const char* bnext = bptr_of(tile + gridDim.x);
-    f32x16_t acc[MT];
+    f32x4_t acc[2 * MT];
     #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = f32x16_t{};
+    for (int t = 0; t < 2 * MT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float ss0 = 0.f, ss1 = 0.f;
     // chunks in pairs (D is a multiple of 256), the two register sets
     // trading roles; the tile's last chunk prefetches the next tile's first
     for (int c = 0; c < nchunks; c += 2) {
-      gemm_chunk<MT>(b, bn, st, acc, ss0, ss1, aptr, aoff, c + 1, bptr, abuf[buf], abuf[buf ^ 1], col, h);
+      gemm_chunk<MT>(b, bn, st, acc, ss0, ss1, aptr, aoff, c + 1, bptr, abuf[buf], abuf[buf ^ 1], col, g4);
       buf ^= 1;
       const bool last = c + 2 == nchunks;
       gemm_chunk<MT>(bn, b, st, acc, ss0, ss1, aptr, aoff, last ? 0 : c + 2, last ? bnext : bptr,
-                     abuf[buf], abuf[buf ^ 1], col, h);
+                     abuf[buf], abuf[buf ^ 1], col, g4);
       buf ^= 1;
     }
     bptr = bnext;
 
     // scores, softmax over the row's 8 lanes, weights and statistics
     float ss = ss0 + ss1;
-    ss += __shfl_xor(ss, 32);  // the two k-groups of this column
+    ss += __shfl_xor(ss, 16);  // the four k-groups of this column
+    ss += __shfl_xor(ss, 32);
     const float inv = rsqrtf(ss * p.invD + p.eps);
     const bool valid = i < p.n;
     #pragma unroll
-    for (int t = 0; t < MT; ++t)
-      #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // accumulators 4 g .. 4 g + 2 of lane half h: parts 0..2 of query 8 t + 2 g + h
-        const int s = 8 * t + 2 * g + h;
-        const float sc = ((acc[t][4 * g] + acc[t][4 * g + 1]) + acc[t][4 * g + 2]) * inv;
-        const float m = group8_max(valid ? sc : -INFINITY);
-        const float e = valid ? __expf(sc - m) : 0.f;
-        const float z = group8_sum(e);
-        if (rv && s < p.S) {
-          p.alpha[((int64_t)s * p.R + row) * 8 + i] = e * (1.0f / z);
-          if (i == 0) {
-            if (p.m_out) p.m_out[(int64_t)s * p.R + row] = m;
-            p.lse_out[(int64_t)s * p.R + row] = m + __logf(z);
-          }
+    for (int t = 0; t < 2 * MT; ++t) {
+      // accumulators 0..2 of k-group g4: parts 0..2 of query 4 t + g4
+      const int s = 4 * t + g4;
+      const float sc = ((acc[t][0] + acc[t][1]) + acc[t][2]) * inv;
+      const float m = group8_max(valid ? sc : -INFINITY);
+      const float e = valid ? __expf(sc - m) : 0.f;
+      const float z = group8_sum(e);
+      if (rv && s < p.S) {
+        p.alpha[((int64_t)s * p.R + row) * 8 + i] = e * (1.0f / z);
+        if (i == 0) {
+          if (p.m_out) p.m_out[(int64_t)s * p.R + row] = m;
+          p.lse_out[(int64_t)s * p.R + row] = m + __logf(z);
         }
       }
+    }
   }
 }
 
