@@ -216,11 +216,6 @@ def bench_backward(args, wl) -> dict:
     torch.cuda.synchronize()
     stride = max(1, args.steps // TIMED_STEPS)
     instrumented = [i for i in range(args.steps) if i % stride == stride // 2][:TIMED_STEPS]
-    if wl.ring:
-        # Sublayer outputs are generated on the device between the merges, so
-        # the step's wall time holds generator kernels too: every timed step
-        # records its AttnRes launches, and the rate is taken from their sum.
-        instrumented = list(range(args.steps))
     binding.attnres_timing_enable(3 * len(instrumented) + 4)
     binding.attnres_timing_pause(True)
     binding.attnres_timing_reset()
@@ -289,8 +284,7 @@ def bench_backward(args, wl) -> dict:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
-        "data": "synthetic (seeded counter-based normals; inputs resident in HBM"
-                + ("; sublayer outputs generated per sublayer into a 3-slot ring)" if wl.ring else ")"),
+        "data": "synthetic (seeded counter-based normals; inputs resident in HBM)",
         "config": {"workload": f"aggregate_backward_n{n}_{wl.name}", "B": wl.B, "T": wl.T, "D": D,
                    "sources": n, "global_batch": wl.B, "seq_len": wl.T, "parallelism": "single GPU"},
         "achieved_GBps": round(step_bytes / (ms_per_step * 1e6), 1),
@@ -299,6 +293,110 @@ def bench_backward(args, wl) -> dict:
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kinds.items()},
+        "cpu_baseline": cpu,
+    }
+
+
+def bench_aggregate(args, wl) -> dict:
+    """One step = the single-aggregate workload's two attnres_aggregate calls
+    over its n sources (the N(0, 0.02^2) query, then the all-zero query), with
+    m and lse; R token rows of D in the workload's dtype. At 128 rows a call
+    is bound by kernel latency, not bytes."""
+    import numpy as np
+    import torch
+
+    from depth_wise_attention_rms_amd import binding
+    from depth_wise_attention_rms_amd import inputs
+    from depth_wise_attention_rms_amd.workload import EPS
+
+    R, D, n = wl.R, wl.D, wl.n
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    srcs = [inputs.fill_normal(torch.empty((R, D), dtype=dt, device="cuda"), wl.seed, inputs.ROLE_SRC, i, sg)
+            for i, sg in enumerate(wl.src_sigmas)]
+    w_h = inputs.queries(wl.seed, 1, D)[0]
+    g_h = inputs.gains(wl.seed, D)
+    queries = [torch.from_numpy(w_h).cuda(), torch.zeros(D, dtype=torch.float32, device="cuda")]
+    g = torch.from_numpy(g_h).cuda()
+    outs = [torch.empty((R, D), dtype=dt, device="cuda") for _ in queries]
+    ms_ = [torch.empty(R, dtype=torch.float32, device="cuda") for _ in queries]
+    ls_ = [torch.empty(R, dtype=torch.float32, device="cuda") for _ in queries]
+
+    def step():
+        for k, w in enumerate(queries):
+            binding.attnres_aggregate(srcs, w, g, eps=EPS, out=outs[k], m_out=ms_[k], lse_out=ls_[k])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stride = max(1, args.steps // TIMED_STEPS)
+    instrumented = [i for i in range(args.steps) if i % stride == stride // 2][:TIMED_STEPS]
+    binding.attnres_timing_enable(2 * len(instrumented) + 4)
+    binding.attnres_timing_pause(True)
+    binding.attnres_timing_reset()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        if i in instrumented:
+            binding.attnres_timing_pause(False)
+            step()
+            binding.attnres_timing_pause(True)
+        else:
+            step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    cnt, ms, byts = binding.attnres_timing_read("aggregate")
+    binding.attnres_timing_enable(0)
+    agg = {"launches_per_step": cnt / len(instrumented), "avg_us": 1e3 * ms / cnt,
+           "ms_per_step": ms / len(instrumented), "bytes_per_launch": byts / cnt, "GBps": byts / (ms * 1e6)}
+    step_bytes = agg["bytes_per_launch"] * agg["launches_per_step"]
+    roofline = {"bound": "hbm", "kernel": "aggregate_kernel", "achieved": round(agg["GBps"], 1),
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(agg["GBps"] / PEAK_HBM_GBPS, 4),
+                "traffic": None, "bytes_per_launch": agg["bytes_per_launch"],
+                "avg_launch_us": round(agg["avg_us"], 2), "timed_launches": int(cnt), "timed_in": "timed region"}
+    cpu = None
+    if args.cpu_rows > 0:
+        import oracle
+        if not os.path.exists(oracle.LIBRARY):
+            oracle.build()
+        hs = [inputs.tensor_rows(wl.seed, inputs.ROLE_SRC, i, np.arange(R), D, sg, wl.dtype)
+              for i, sg in enumerate(wl.src_sigmas)]
+        done, spent = 0, 0.0
+        while done == 0 or spent < args.cpu_seconds:
+            c0 = time.perf_counter()
+            for w in (w_h, np.zeros(D, np.float32)):
+                oracle.aggregate(hs, w, g_h, eps=EPS, nthreads=1)
+            spent += time.perf_counter() - c0
+            done += R
+        cpu = {"value": round(done / spent, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"the workload's {R} token rows, both queries per step, {done // R} steps of the fp64 "
+                         f"aggregate, {spent:.2f} s of CPU time"}
+    return {
+        "metric": f"tokens/s and achieved HBM GB/s (% of peak) for the AttnRes aggregate ({n} sources, "
+                  "a query and the all-zero query per step)",
+        "value": round(R / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "gpu_ms_per_step": round(gpu_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.dtype == "f32" else "bf16",
+        "data": "synthetic (seeded counter-based normals; inputs resident in HBM)",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "D": D, "sources": n, "global_batch": wl.B,
+                   "seq_len": wl.T, "parallelism": "single GPU"},
+        "achieved_GBps": round(step_bytes / (ms_per_step * 1e6), 1),
+        "hbm_frac": round(step_bytes / (ms_per_step * 1e6) / PEAK_HBM_GBPS, 4),
+        "bytes_per_step": step_bytes,
+        "roofline": roofline,
+        "kernels": {"aggregate": {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in agg.items()}},
         "cpu_baseline": cpu,
     }
 
@@ -357,6 +455,9 @@ def main() -> int:
     wl = inputs.WORKLOADS[args.workload]
     if args.backward:
         print(json.dumps(bench_backward(args, wl)), flush=True)
+        return 0
+    if wl.kind == "aggregate":
+        print(json.dumps(bench_aggregate(args, wl)), flush=True)
         return 0
     assert wl.kind == "stack", "the benchmark times a stack workload"
     assert not (wl.ring and (args.graph or args.full_schedule)), \
