@@ -156,7 +156,7 @@ int do_close(const char* fn, const void* p, const void* v, void* b, int64_t R, i
 int do_phase1(const char* fn, int dtype, const Phase1Args& a, hipStream_t st) {
   if (a.R == 0) return ATTNRES_OK;
   const int64_t row_bytes = a.D * esize_of(dtype);
-  if (a.out && a.gemm_ws && attnres::phase1_gemm_eligible(dtype, a.n, a.S, a.D, a.R)) {
+  if (a.gemm_ws && attnres::phase1_gemm_eligible(dtype, a.n, a.S, a.D, a.R)) {
     // the scores pass reads materialised sources: close first
     if (a.close_v) TRY(do_close(fn, a.close_p, a.close_v, a.close_b, a.R, a.D, dtype, st));
     Phase1Args g = a;
@@ -164,8 +164,9 @@ int do_phase1(const char* fn, int dtype, const Phase1Args& a, hipStream_t st) {
     g.close_v = nullptr;
     g.close_b = nullptr;
     const double rb = (double)a.R * row_bytes;
-    const double bytes = rb * (a.n + a.S) + (double)a.R * a.S * ((a.m_out ? 4 : 0) + 4);
-    hipError_t e = attnres::launch_phase1_gemm(g, a.gemm_ws, timed_launch(K_PHASE1, bytes, st));
+    const double bytes = rb * (a.n + (a.out ? a.S : 0)) + (double)a.R * a.S * ((a.m_out ? 4 : 0) + 4);
+    hipError_t e = attnres::launch_phase1_gemm(
+        g, a.gemm_ws, timed_launch(a.out ? K_PHASE1 : K_PHASE1_STATS, bytes, st));
     return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
   }
   if (attnres::phase1_supported(dtype, a.n, a.S, a.D)) {

@@ -2386,15 +2386,17 @@ static hipError_t launch_gemm_outputs(const P1OParams& o, bool nt, const Launch&
 }
 
 // Phase 1 as a query split, a matrix-core scores pass and an outputs pass
-// (see phase1_gemm_scores_kernel). The sources must be materialised (no
+// (see phase1_gemm_scores_kernel); without an output buffer (statistics
+// only) the outputs pass is skipped. The sources must be materialised (no
 // fused close); `ws` holds phase1_gemm_workspace(S, R, D) bytes.
 hipError_t launch_phase1_gemm(const Phase1Args& a, void* ws, const Launch& L) {
-  if (a.close_v || !a.out || !phase1_gemm_eligible(1, a.n, a.S, a.D, a.R)) return hipErrorInvalidValue;
+  if (a.close_v || !phase1_gemm_eligible(1, a.n, a.S, a.D, a.R)) return hipErrorInvalidValue;
   const int MT = gemm_tiles(a.S);
   __bf16* qp = static_cast<__bf16*>(ws);
   float* alpha = reinterpret_cast<float*>(static_cast<char*>(ws) + gemm_qp_bytes(a.S, a.D));
   // timed from the split's start to the outputs pass's end
-  const Launch first{L.stream, L.start, nullptr}, mid{L.stream, nullptr, nullptr}, last{L.stream, nullptr, L.stop};
+  const Launch first{L.stream, L.start, nullptr}, last{L.stream, nullptr, L.stop};
+  const Launch mid{L.stream, nullptr, a.out ? nullptr : L.stop};
   {
     QSplitParams q{a.W, a.G, a.S, MT, a.D, qp};
     const int64_t blocks = ((int64_t)MT * 32 * a.D + 255) / 256;
@@ -2415,6 +2417,7 @@ hipError_t launch_phase1_gemm(const Phase1Args& a, void* ws, const Launch& L) {
     }
     if (e != hipSuccess) return e;
   }
+  if (!a.out) return hipSuccess;
   P1OParams o;
   for (int i = 0; i < 8; ++i) o.src[i] = i < a.n ? a.src[i] : a.src[0];
   o.S = a.S; o.alpha = alpha; o.out = a.out;

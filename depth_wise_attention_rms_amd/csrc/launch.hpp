@@ -111,8 +111,9 @@ hipError_t launch_bwd_reduce(const BwdArgs& a, const BwdPlan& pl, int stage, con
 hipError_t launch_fold(const float* w, const float* g, float* q, int64_t count, const Launch& L);
 hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L);
 // Phase 1 as a matrix-core scores pass and an outputs pass (bf16, n <= 8,
-// S <= 32, D a multiple of 256 up to 8192, many rows); needs materialised
-// sources (no fused close) and a workspace of phase1_gemm_workspace bytes.
+// S <= 32, D a multiple of 256 up to 8192, many rows; statistics only when
+// out is null); needs materialised sources (no fused close) and a workspace
+// of phase1_gemm_workspace bytes.
 bool phase1_gemm_shape(int dtype, int S, int64_t D, int64_t R);
 // the register-tile matrix-core Phase 1 (bf16, n <= 8, S <= 8, D in {1024, 2048, 3072, 4096})
 bool phase1_mfma_eligible(int dtype, int n, int S, int64_t D);
