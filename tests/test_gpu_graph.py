@@ -32,6 +32,9 @@ GRAPH_CASES = [
     inputs.WORKLOADS["decode_L96_S12"],
     inputs.Workload("graph_block", "stack", B=2, T=64, D=1024, dtype="bf16", L=16, S=4, seed=9),
     inputs.Workload("graph_full", "stack", B=1, T=32, D=256, dtype="bf16", L=5, S=1, seed=10),
+    # 4096 rows of 7168 with 12 queries: Phase 1 as the query split, the
+    # matrix-core scores pass and the outputs pass, with a separate close
+    inputs.Workload("graph_gemm", "stack", B=1, T=4096, D=7168, dtype="bf16", L=15, S=12, seed=11),
 ]
 
 
