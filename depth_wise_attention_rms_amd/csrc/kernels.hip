@@ -776,10 +776,10 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
         #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int sq = 2 * q + (upper ? 1 : 0);
-          if (2 * q < S && sq < S)
-            st16_global(uniform_ptr(static_cast<char*>(p.out) + ((int64_t)(2 * q) * p.R + row) * rowbytes) +
-                            (uint32_t)((upper ? p.R * rowbytes : 0) + vec * 16),
-                        Bf16::pack(o[q]));
+          // a 64-bit address per lane: the two queries of a pair are R rows
+          // apart, which a 32-bit lane offset cannot hold beyond 4 GB
+          char* dst = static_cast<char*>(p.out) + ((int64_t)sq * p.R + row) * rowbytes + vec * 16;
+          if (2 * q < S && sq < S) st16_global((gchar_t*)reinterpret_cast<uintptr_t>(dst), Bf16::pack(o[q]));
         }
       }
       issued += 2 * ((S + 1) >> 1);
