@@ -436,6 +436,21 @@ __device__ __forceinline__ float group8_sum(float x) {
   x += dpp_mov<0x4E>(x);
   return x + dpp_mov<0x141>(x);
 }
+// The same over aligned groups of N = 1, 2, 4 or 8 lanes.
+template <int N>
+__device__ __forceinline__ float groupn_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp_mov<0xB1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp_mov<0x4E>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp_mov<0x141>(x));
+  return x;
+}
+template <int N>
+__device__ __forceinline__ float groupn_sum(float x) {
+  if constexpr (N >= 2) x += dpp_mov<0xB1>(x);
+  if constexpr (N >= 4) x += dpp_mov<0x4E>(x);
+  if constexpr (N >= 8) x += dpp_mov<0x141>(x);
+  return x;
+}
 
 // Workgroup barrier after this wave's LDS reads and writes have completed.
 // It does not wait for vector memory: a fenced barrier (__syncthreads(), or
@@ -1585,9 +1600,9 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
 // 4 q + j holds part j of query q (parts: the exact three-way bf16 split of
 // the fp32 query, row j = 3 zero), and B is [D, rows x 8]: column 8 r + i is
 // source i of row r. It runs on the matrix cores (v_mfma_f32_16x16x32_bf16,
-// fp32 accumulation): each wave owns 2 rows (16 columns) and all 2 MT 16-row
-// tiles of Qp (4 queries each), whose 128-element chunks are staged in LDS
-// once per workgroup of 16 waves (32 rows) and read by all of them. In k-step
+// fp32 accumulation): each wave owns 16 columns and all 2 MT 16-row tiles
+// of Qp (4 queries each), whose 128-element chunks are staged in LDS once per
+// workgroup of 16 waves and read by all of them. In k-step
 // ks of a chunk, k-group g of a lane holds elements 32 ks + 8 g ..
 // 32 ks + 8 g + 7 (A and B alike), so the four lanes of a column read 64
 // adjacent bytes of its source per load: each load touches 2 lines per row
@@ -1595,9 +1610,11 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
 // block of the long-context shape from 14.5 to 11.6 ms. Sums of squares come
 // from the same B registers (v_dot2). After the last chunk each lane holds,
 // for its column, the three parts of one query per tile; their sum scaled by
-// the source's 1 / rms is the score, and the 8 lanes of a row hold its 8
-// sources, so the softmax is an 8-lane reduction. The weights alpha
-// [S][R][8] (zero past n) and the statistics m, lse are written.
+// the source's 1 / rms is the score. A row takes NPR columns, the smallest of
+// 1, 2, 4 or 8 that holds its n sources (so a tile holds 16 / NPR rows per
+// wave), and the softmax is an NPR-lane reduction. The weights alpha
+// [S][R][8] (entries i < NPR; zero from n on) and the statistics m, lse are
+// written.
 //
 // Outputs. o_s = sum_i alpha[s][i] b_i, one row per wave group: the row's n
 // sources stay in registers and every query's output is formed from them.
@@ -1692,23 +1709,25 @@ __device__ __forceinline__ void gemm_chunk(const uint4 (&b)[4], uint4 (&bn)[4], 
   lds_barrier();  // this chunk's Qp reads are done; the next chunk's are in LDS
 }
 
-template <int MT>
+template <int MT, int NPR>
 __global__ __launch_bounds__(1024) void phase1_gemm_scores_kernel(P1GParams p) {
   constexpr int AROW = kGChunk + kGPad;
-  constexpr int U = (MT + 1) / 2;  // Qp staging units per thread
+  constexpr int U = (MT + 1) / 2;       // Qp staging units per thread
+  constexpr int RW = 16 / NPR;          // rows per wave: NPR source columns each
+  constexpr int RT = kGWaves * RW;      // rows per tile
   __shared__ __attribute__((aligned(16))) __bf16 abuf[2][MT * 32 * AROW];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int col = l & 15, g4 = l >> 4;   // B column and k-group
-  const int rl = col >> 3, i = col & 7;  // row of the wave's 2, source
+  const int col = l & 15, g4 = l >> 4;        // B column and k-group
+  const int rl = col / NPR, i = col % NPR;    // row of the wave's RW, source
   const int64_t rowbytes = (int64_t)p.D * 2;
   const int nchunks = p.D / kGChunk;
-  const int64_t tiles = (p.R + 31) / 32;
+  const int64_t tiles = (p.R + RT - 1) / RT;
 
   // this lane's 16-byte pieces of each chunk of its column's source in tile
   // t (row 0 past the end, source 0 past n: read, then discarded)
   const char* src_i = static_cast<const char*>(p.src[i < p.n ? i : 0]) + g4 * 16;
   auto bptr_of = [&](int64_t t) -> const char* {
-    const int64_t r = t * 32 + w * 2 + rl;
+    const int64_t r = t * RT + w * RW + rl;
     return src_i + (r < p.R ? r : 0) * rowbytes;
   };
   // Qp staging: thread tid copies 16-byte unit tid + 1024 u of a chunk's
@@ -1743,7 +1762,7 @@ __global__ __launch_bounds__(1024) void phase1_gemm_scores_kernel(P1GParams p) {
   lds_barrier();
 
   for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-    const int64_t row = tile * 32 + w * 2 + rl;
+    const int64_t row = tile * RT + w * RW + rl;
     const bool rv = row < p.R;
     const char* bnext = bptr_of(tile + gridDim.x);
     f32x4_t acc[2 * MT];
@@ -1762,7 +1781,7 @@ __global__ __launch_bounds__(1024) void phase1_gemm_scores_kernel(P1GParams p) {
     }
     bptr = bnext;
 
-    // scores, softmax over the row's 8 lanes, weights and statistics
+    // scores, softmax over the row's NPR lanes, weights and statistics
     float ss = ss0 + ss1;
     ss += __shfl_xor(ss, 16);  // the four k-groups of this column
     ss += __shfl_xor(ss, 32);
@@ -1773,9 +1792,9 @@ __global__ __launch_bounds__(1024) void phase1_gemm_scores_kernel(P1GParams p) {
       // accumulators 0..2 of k-group g4: parts 0..2 of query 4 t + g4
       const int s = 4 * t + g4;
       const float sc = ((acc[t][0] + acc[t][1]) + acc[t][2]) * inv;
-      const float m = group8_max(valid ? sc : -INFINITY);
+      const float m = groupn_max<NPR>(valid ? sc : -INFINITY);
       const float e = valid ? __expf(sc - m) : 0.f;
-      const float z = group8_sum(e);
+      const float z = groupn_sum<NPR>(e);
       if (rv && s < p.S) {
         p.alpha[((int64_t)s * p.R + row) * 8 + i] = e * (1.0f / z);
         if (i == 0) {
@@ -2370,11 +2389,21 @@ size_t phase1_gemm_workspace(int S, int64_t R, int64_t D) {
   return gemm_qp_bytes(S, D) + (size_t)S * R * 8 * sizeof(float);
 }
 
+template <int MT, int NPR>
+static hipError_t launch_gemm_scores_t(const P1GParams& g, const Launch& L) {
+  const int64_t tiles = (g.R + kGWaves * (16 / NPR) - 1) / (kGWaves * (16 / NPR));
+  const unsigned grid = (unsigned)(tiles < (1 << 20) ? tiles : (1 << 20));
+  return launch(L, phase1_gemm_scores_kernel<MT, NPR>, dim3(grid), dim3(64 * kGWaves), 0, g);
+}
+
+// Source columns per row: the smallest of 1, 2, 4 or 8 that holds the n
+// sources, so a 16-column tile takes 16 / NPR rows.
 template <int MT>
 static hipError_t launch_gemm_scores(const P1GParams& g, const Launch& L) {
-  const int64_t tiles = (g.R + 31) / 32;
-  const unsigned grid = (unsigned)(tiles < (1 << 20) ? tiles : (1 << 20));
-  return launch(L, phase1_gemm_scores_kernel<MT>, dim3(grid), dim3(64 * kGWaves), 0, g);
+  if (g.n <= 1) return launch_gemm_scores_t<MT, 1>(g, L);
+  if (g.n <= 2) return launch_gemm_scores_t<MT, 2>(g, L);
+  if (g.n <= 4) return launch_gemm_scores_t<MT, 4>(g, L);
+  return launch_gemm_scores_t<MT, 8>(g, L);
 }
 
 template <int NC>
