@@ -44,17 +44,18 @@ def widen(a: np.ndarray) -> np.ndarray:
 
 
 def os2_merge(a, b):
-    """The pages' two-group merge (K3 §9.4 eq. OS2; WC merge_summary) on
-    (m, z, u) triples with u the unnormalised numerator."""
-    m = np.maximum(a[0], b[0])
-    sa, sb = np.exp(a[0] - m), np.exp(b[0] - m)
-    return m, sa * a[1] + sb * b[1], sa[..., None] * a[2] + sb[..., None] * b[2]
+    """Merge two group summaries given as (lse, o): log-sum-exp lse of the
+    group's scores and its normalised output o (K3 §9.4 eq. OS2, here with each
+    group's denominator folded into lse). The merged lse is the log-add-exp of
+    the two; each group's share of the merged softmax mass is e^(lse_g - lse)."""
+    lse = np.logaddexp(a[0], b[0])
+    wa, wb = np.exp(a[0] - lse), np.exp(b[0] - lse)
+    return lse, wa[..., None] * a[1] + wb[..., None] * b[1]
 
 
-def triple_from(out):
-    """(m, z, u) of a normalised aggregate: z = exp(lse - m), u = z * h."""
-    z = np.exp(out["lse"] - out["m"])
-    return out["m"], z, z[..., None] * out["h"]
+def summary_of(out):
+    """(lse, o) of an oracle aggregate."""
+    return out["lse"], out["h"]
 
 
 # ----------------------------------------------------------------------------
@@ -241,7 +242,8 @@ def pin_identical_sources(orc):
 def pin_os2_bipartition(orc):
     """Online-softmax summaries of any two disjoint source groups merge into
     the summary of the whole (K3 §9.4 OS1/OS2; WC reference check on 7 sources
-    of shape (2, 3, 5) split 3/4, with eps 1e-6)."""
+    of shape (2, 3, 5) split 3/4, with eps 1e-6). The running max of the whole
+    is the larger of the two groups' maxima."""
     rng = np.random.default_rng(0)
     src = [rng.standard_normal((6, 5)).astype(np.float32) for _ in range(7)]
     q = rng.standard_normal(5).astype(np.float32)
@@ -249,10 +251,119 @@ def pin_os2_bipartition(orc):
     for k in range(1, 7):
         a = orc.aggregate(src[:k], q, eps=1e-6)
         b = orc.aggregate(src[k:], q, eps=1e-6)
-        m, z, u = os2_merge(triple_from(a), triple_from(b))
-        assert np.allclose(u / z[:, None], whole["h"], rtol=1e-12, atol=1e-12), k
-        assert np.allclose(m + np.log(z), whole["lse"], rtol=1e-13, atol=1e-13), k
-        assert np.array_equal(m, whole["m"]), k
+        lse, h = os2_merge(summary_of(a), summary_of(b))
+        assert np.allclose(h, whole["h"], rtol=1e-12, atol=1e-12), k
+        assert np.allclose(lse, whole["lse"], rtol=1e-13, atol=1e-13), k
+        assert np.array_equal(np.maximum(a["m"], b["m"]), whole["m"]), k
+
+
+# ----------------------------------------------------------------------------
+# the condition scale sum_i a_i |V_i[d]| (every parity tolerance divides by it)
+# ----------------------------------------------------------------------------
+
+def pin_scale_aggregate_closed_forms(orc):
+    """The per-element condition scale of an aggregate is sum_i a_i |V_i[d]|,
+    the convex combination (A3) applied to the magnitudes. Three closed forms
+    fix it independently of the oracle's own weights:
+    - a zero query gives equal weights 1/n, so the scale is mean_i |V_i[d]|
+      (K3 §9.2 zero init);
+    - two dense sources c_0 * 1 and c_1 * (+1, -1, +1, ...) have mean square
+      c_i^2, so their scores are sign(c_i) * (sum_d q[d] sign_i[d]) /
+      sqrt(1 + eps / c_i^2) and their weights the logistic function of the
+      difference (A1, A2); the scale is a_0 |c_0| + a_1 |c_1| in every element;
+    - scaled one-hot sources on distinct coordinates give a_i |c_i| at
+      coordinate d_i and zero elsewhere."""
+    rng = np.random.default_rng(61)
+    src = _cfg1_sources(rng, rows=8, D=64)
+    out = orc.aggregate(src, np.zeros(64, np.float32))
+    want = np.mean([np.abs(a.astype(np.float64)) for a in src], axis=0)
+    big = max(np.abs(a).max() for a in src)
+    assert np.max(np.abs(out["scale"] - want)) <= 8 * np.finfo(np.float64).eps * big
+    D = 32
+    q = np.linspace(-0.4, 0.9, D).astype(np.float32)
+    alt = np.where(np.arange(D) % 2 == 0, 1.0, -1.0)
+    for eps in (0.0, 1e-8, 0.5):
+        for c0, c1 in ((1.0, 3.0), (-2.0, 0.25), (5.0, -4.0)):
+            V0 = np.full((1, D), c0, np.float32)
+            V1 = (c1 * alt).astype(np.float32)[None, :]
+            s0 = math.copysign(1.0, c0) * float(q.astype(np.float64).sum()) / math.sqrt(1 + eps / c0 ** 2)
+            s1 = math.copysign(1.0, c1) * float((q.astype(np.float64) * alt).sum()) / math.sqrt(1 + eps / c1 ** 2)
+            a0 = 1.0 / (1.0 + math.exp(s1 - s0))
+            a1 = 1.0 / (1.0 + math.exp(s0 - s1))
+            got = orc.aggregate([V0, V1], q, eps=eps)["scale"][0]
+            np.testing.assert_allclose(got, a0 * abs(c0) + a1 * abs(c1), rtol=1e-12, atol=0)
+    V0 = np.zeros((1, D), np.float32); V0[0, 4] = 3.0
+    V1 = np.zeros((1, D), np.float32); V1[0, 11] = -0.5
+    s0 = float(q[4]) * 3.0 / math.sqrt(9.0 / D)
+    s1 = float(q[11]) * -0.5 / math.sqrt(0.25 / D)
+    a0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    want = np.zeros(D); want[4] = a0 * 3.0; want[11] = (1.0 - a0) * 0.5
+    np.testing.assert_allclose(orc.aggregate([V0, V1], q, eps=0.0)["scale"][0], want, rtol=1e-12, atol=0)
+
+
+def pin_scale_phase2_closed_forms(orc):
+    """The Phase-2 scale is the merged softmax's weights on |o| and |p|. With
+    a zero query the partial scores exactly 0, so a Phase-1 lse of l gives the
+    group weight 1/(1 + e^-l) and the partial 1/(1 + e^l) (K3 §9.4 OS2 and the
+    single-source triple); lse -200 and +200 leave |p| and |o| alone."""
+    rng = np.random.default_rng(62)
+    rows, D = 4, 32
+    o = (rng.standard_normal((rows, D)) * 2).astype(np.float32)
+    v = (rng.standard_normal((rows, D)) * 0.7).astype(np.float32)
+    ao, av = np.abs(o.astype(np.float64)), np.abs(v.astype(np.float64))
+    zero = np.zeros(D, np.float32)
+    for l in (0.0, math.log(3.0), -1.25, 7.0):
+        lse = np.full(rows, l, np.float32)
+        lf = float(lse[0])
+        wo = 1.0 / (1.0 + math.exp(-lf))
+        got = orc.phase2(o, lse, zero, None, v)["scale"]
+        np.testing.assert_allclose(got, wo * ao + (1.0 - wo) * av, rtol=1e-13, atol=0)
+    w = (rng.standard_normal(D) * 0.3).astype(np.float32)
+    sp = orc.aggregate([v], w)["m"]
+    for shift, want in ((-200.0, av), (200.0, ao)):
+        got = orc.phase2(o, (sp + shift).astype(np.float32), w, None, v)["scale"]
+        np.testing.assert_allclose(got, want, rtol=1e-13, atol=0)
+
+
+def pin_scale_merge_closed_form(orc):
+    """The merge scale is (e^lse |o| + sum_i e^s_i |v_i|) / (e^lse + sum_i e^s_i).
+    With a zero query every new source scores 0, so for a group lse of l it is
+    (e^l |o| + sum_i |v_i|) / (e^l + n) (K3 §9.4 OS2, each new source its own
+    term)."""
+    rng = np.random.default_rng(63)
+    A, B, _, g = _merge_inputs(rng, nB=3)
+    o = A[1]
+    zero = np.zeros(o.shape[1], np.float32)
+    sumv = sum(np.abs(b.astype(np.float64)) for b in B)
+    for l in (0.0, 1.5, -2.0):
+        lse = np.full(o.shape[0], l, np.float32)
+        e = math.exp(float(lse[0]))
+        got = orc.merge(o, lse, B, zero, g)["scale"]
+        want = (e * np.abs(o.astype(np.float64)) + sumv) / (e + len(B))
+        np.testing.assert_allclose(got, want, rtol=1e-13, atol=0)
+
+
+def pin_scale_stack_zero_queries(orc):
+    """With zero queries every aggregate of the stack weighs its sources
+    equally, so the scale of h_l is the mean of |source| over the sources the
+    plan gives sublayer l, and y's over the completed blocks (K3 §9.3 listing,
+    §9.2 zero init). Checked on two blocks with a short last one."""
+    rng = np.random.default_rng(64)
+    L, S, rows, D = 5, 3, 3, 16
+    x, v, _ = _stack_inputs(rng, L, rows, D, "f32")
+    W = np.zeros((L + 1, D), np.float32)
+    st = orc.block_stack(x, v, W, S=S)
+    X = np.abs(x.astype(np.float64))
+    V = [a.astype(np.float64) for a in v]
+    p1 = [V[0], V[0] + V[1]]          # partials inside block 1 (fp32 sums, rounded)
+    b1 = orc.round_to(orc.round_to(V[0] + V[1], "f32").astype(np.float64) + V[2], "f32").astype(np.float64)
+    p1[1] = orc.round_to(p1[1], "f32").astype(np.float64)
+    want = [X, (X + np.abs(p1[0])) / 2, (X + np.abs(p1[1])) / 2,
+            (X + np.abs(b1)) / 2, (X + np.abs(b1) + np.abs(V[3])) / 3]
+    for l in range(L):
+        np.testing.assert_allclose(st["h_scale"][l], want[l], rtol=1e-14, atol=0, err_msg=f"h_{l + 1}")
+    b2 = orc.round_to(V[3] + V[4], "f32").astype(np.float64)
+    np.testing.assert_allclose(st["y_scale"], (X + np.abs(b1) + np.abs(b2)) / 3, rtol=1e-14, atol=0)
 
 
 # ----------------------------------------------------------------------------
@@ -432,12 +543,12 @@ def pin_two_phase_bruteforce(orc):
                         ph = orc.phase1(blocks, W[start - 1:end])
                         partial = None
                         for j, l in enumerate(range(start, end + 1)):
-                            tr = (ph["m"][j], np.exp(ph["lse"][j] - ph["m"][j]),
-                                  np.exp(ph["lse"][j] - ph["m"][j])[:, None] * ph["o"][j])
+                            summ = (ph["lse"][j], ph["o"][j])
                             if partial is not None:
+                                # one source: its lse is its score and its output is itself
                                 single = orc.aggregate([partial], W[l - 1])
-                                tr = os2_merge(tr, (single["m"], np.ones(3), widen(partial)))
-                            h = tr[2] / tr[1][:, None]
+                                summ = os2_merge(summ, (single["m"], widen(partial)))
+                            h = summ[1]
                             assert np.allclose(h, st["h"][l - 1], rtol=1e-12, atol=1e-12), (dtype, D, L, S, l)
                             if partial is None:
                                 partial = v[l - 1]

@@ -70,6 +70,16 @@ MUTANTS = [
     ("final_query_wrong_row", "agg_row(n, src, c->q + (int64_t)c->L * D,", "agg_row(n, src, c->q + (int64_t)(c->L - 1) * D,"),
     ("auto_block_size_floor", "((num_hidden_layers + 7) / 8 > 1 ? (num_hidden_layers + 7) / 8 : 1)",
      "(num_hidden_layers / 8 > 1 ? num_hidden_layers / 8 : 1)"),
+    ("agg_scale_drops_weights", "sc += a[i] * fabs(V[i][d]);", "sc += fabs(V[i][d]);"),
+    ("agg_scale_signed", "sc += a[i] * fabs(V[i][d]);", "sc += a[i] * V[i][d];"),
+    ("agg_scale_wrong_source", "sc += a[i] * fabs(V[i][d]);", "sc += a[n - 1 - i] * fabs(V[i][d]);"),
+    ("ph2_scale_drops_weights", "c->scale[r * D + d] = (wa * fabs(ov) + wb * fabs(p[d])) / den;",
+     "c->scale[r * D + d] = fabs(ov) + fabs(p[d]);"),
+    ("ph2_scale_weights_swapped", "c->scale[r * D + d] = (wa * fabs(ov) + wb * fabs(p[d])) / den;",
+     "c->scale[r * D + d] = (wb * fabs(ov) + wa * fabs(p[d])) / den;"),
+    ("merge_scale_drops_weights", "sc += a * fabs(V[i][d]);", "sc += fabs(V[i][d]);"),
+    ("merge_scale_drops_group", "double num = wo * ov, sc = wo * fabs(ov);", "double num = wo * ov, sc = 0.0;"),
+    ("stack_scale_is_h", "if (c->h_scale) memcpy(c->h_scale + ho * D, srow,", "if (c->h_scale) memcpy(c->h_scale + ho * D, hrow,"),
     ("phase1_same_query", "fold_query(W + (int64_t)s * D, Gamma ? Gamma + (int64_t)s * D : NULL, D, q + (int64_t)s * D);",
      "fold_query(W, Gamma, D, q + (int64_t)s * D);"),
 ]
