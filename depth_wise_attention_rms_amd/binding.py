@@ -31,7 +31,8 @@ EXPORTS = (
     "attnres_stack_workspace_bytes", "attnres_block_stack_forward",
     "attnres_block_stack_forward_norm", "attnres_merge_sources", "attnres_full_workspace_bytes",
     "attnres_full_stack_forward", "attnres_aggregate_backward_workspace_bytes",
-    "attnres_aggregate_backward", "attnres_block_layout",
+    "attnres_aggregate_backward", "attnres_aggregate_backward_noalloc",
+    "attnres_noalloc_scratch_bytes", "attnres_block_layout",
     "attnres_atomic_block_size", "attnres_status_string", "attnres_last_error",
     "attnres_timing_enable", "attnres_timing_pause", "attnres_timing_reset", "attnres_timing_read",
 )
@@ -78,6 +79,9 @@ def lib():
         L.attnres_aggregate_backward_workspace_bytes.argtypes = [I64, I64, I]
         L.attnres_aggregate_backward_workspace_bytes.restype = SZ
         L.attnres_aggregate_backward.argtypes = [P, I, I64, I64, I, P, P, F, P, P, I, P, P, P, SZ, P]
+        L.attnres_aggregate_backward_noalloc.argtypes = [P, I, I64, I64, I, P, P, F, P, P, I, P, P, P]
+        L.attnres_noalloc_scratch_bytes.argtypes = []
+        L.attnres_noalloc_scratch_bytes.restype = SZ
         L.attnres_block_layout.argtypes = [I, I, P, P]
         L.attnres_atomic_block_size.argtypes = [I, I]
         L.attnres_status_string.argtypes = [I]
@@ -91,7 +95,7 @@ def lib():
         for f in ("attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge",
                   "attnres_phase2_merge_norm", "attnres_rmsnorm", "attnres_block_stack_forward_norm",
                   "attnres_merge_sources", "attnres_full_stack_forward", "attnres_aggregate_backward",
-                  "attnres_table_sublayer", "attnres_block_stack_forward", "attnres_block_layout",
+                  "attnres_aggregate_backward_noalloc", "attnres_table_sublayer", "attnres_block_stack_forward", "attnres_block_layout",
                   "attnres_atomic_block_size", "attnres_timing_enable", "attnres_timing_pause",
                   "attnres_timing_reset", "attnres_timing_read"):
             getattr(L, f).restype = ctypes.c_int
@@ -365,6 +369,25 @@ def attnres_aggregate_backward(sources: Sequence[torch.Tensor], w: torch.Tensor,
         _ptr_array(sources), len(sources), R, D, dtype_code(x0.dtype), _ptr(w), _ptr(gamma), eps,
         _ptr(dh), _ptr_array(dV), 1 if accumulate else 0, _ptr(dw), _ptr(dgamma),
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
+    return dV, dw, dgamma
+
+
+def attnres_noalloc_scratch_bytes() -> int:
+    return int(lib().attnres_noalloc_scratch_bytes())
+
+
+def attnres_aggregate_backward_noalloc(sources: Sequence[torch.Tensor], w: torch.Tensor,
+                                       dh: torch.Tensor, dV: Sequence[torch.Tensor], dw: torch.Tensor,
+                                       gamma=None, eps=1e-8, dgamma=None, accumulate=False,
+                                       stream=None):
+    """attnres_aggregate_backward with the library's fixed scratch instead of a
+    workspace. Every output buffer is the caller's (nothing is allocated here
+    either); returns (dV, dw, dgamma)."""
+    x0 = sources[0]
+    R, D = _rows(x0)
+    _check("attnres_aggregate_backward_noalloc", lib().attnres_aggregate_backward_noalloc(
+        _ptr_array(sources), len(sources), R, D, dtype_code(x0.dtype), _ptr(w), _ptr(gamma), eps,
+        _ptr(dh), _ptr_array(dV), 1 if accumulate else 0, _ptr(dw), _ptr(dgamma), _stream(stream)))
     return dV, dw, dgamma
 
 

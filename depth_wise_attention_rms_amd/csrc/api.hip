@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -761,12 +762,13 @@ ATTNRES_API size_t attnres_aggregate_backward_workspace_bytes(int64_t R, int64_t
   return attnres::plan_aggregate_bwd(dtype, R, D).bytes;
 }
 
-ATTNRES_API int attnres_aggregate_backward(const void* const* sources, int n, int64_t R, int64_t D,
-                                           int dtype, const float* w, const float* gamma, float eps,
-                                           const void* dh, float* const* dV, int accumulate,
-                                           float* dw, float* dgamma, void* workspace,
-                                           size_t workspace_bytes, void* stream) {
-  const char* fn = "attnres_aggregate_backward";
+namespace {
+
+// Every argument of the aggregate backward except its workspace, checked
+// before anything is enqueued; fills the launch plan.
+int validate_backward(const char* fn, const void* const* sources, int n, int64_t R, int64_t D,
+                      int dtype, const float* w, const float* gamma, float eps, const void* dh,
+                      float* const* dV, float* dw, float* dgamma, BwdPlan* plan) {
   TRY(check_shape(fn, R, D, dtype, eps));
   if (n < 1 || n > ATTNRES_MAX_SOURCES)
     return fail(ATTNRES_EINVAL, "%s: n = %d outside 1..%d", fn, n, ATTNRES_MAX_SOURCES);
@@ -776,16 +778,8 @@ ATTNRES_API int attnres_aggregate_backward(const void* const* sources, int n, in
   TRY(check_ptr(fn, "dw", dw, true));
   TRY(check_ptr(fn, "dgamma", dgamma, false));
   if (dgamma && dgamma == dw) return fail(ATTNRES_EINVAL, "%s: dgamma aliases dw", fn);
-  const BwdPlan pl = attnres::plan_aggregate_bwd(dtype, R, D);
-  if (!pl.supported) return fail(ATTNRES_EUNSUPPORTED, "%s: D = %lld", fn, (long long)D);
-  if (pl.bytes > 0) {
-    TRY(check_ptr(fn, "workspace", workspace, true));
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-      return fail(ATTNRES_EINVAL, "%s: workspace is not 256-byte aligned", fn);
-    if (workspace_bytes < pl.bytes)
-      return fail(ATTNRES_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn,
-                  workspace_bytes, pl.bytes);
-  }
+  *plan = attnres::plan_aggregate_bwd(dtype, R, D);
+  if (!plan->supported) return fail(ATTNRES_EUNSUPPORTED, "%s: D = %lld", fn, (long long)D);
   if (R > 0) {
     if (!sources) return fail(ATTNRES_EINVAL, "%s: sources is NULL", fn);
     if (!dV) return fail(ATTNRES_EINVAL, "%s: dV is NULL", fn);
@@ -801,20 +795,120 @@ ATTNRES_API int attnres_aggregate_backward(const void* const* sources, int n, in
           return fail(ATTNRES_EINVAL, "%s: dV[%d] aliases a source or another dV", fn, i);
     }
   }
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  BwdArgs a{sources, n, R, D, w, gamma, eps, dh, dV, accumulate, dw, dgamma, workspace};
-  const double rb = (double)R * D * esize_of(dtype);
-  const double gb = (double)R * D * 4 * n * (accumulate ? 2 : 1);
-  hipError_t e = attnres::launch_aggregate_bwd(dtype, a, pl, timed_launch(K_BWD, rb * (n + 1) + gb, st));
+  return ATTNRES_OK;
+}
+
+// The backward's three launches: the main kernel (dV and the per-workgroup
+// dq~ partials in the workspace), then the two fixed-order reduction stages.
+int launch_backward(const char* fn, int dtype, const BwdArgs& a, const BwdPlan& pl,
+                    hipStream_t st) {
+  const double rb = (double)a.R * a.D * esize_of(dtype);
+  const double gb = (double)a.R * a.D * 4 * a.n * (a.accumulate ? 2 : 1);
+  hipError_t e = attnres::launch_aggregate_bwd(dtype, a, pl, timed_launch(K_BWD, rb * (a.n + 1) + gb, st));
   if (e != hipSuccess) return hip_fail(fn, e);
-  const double pbytes = (double)pl.P * D * 4;
+  const double pbytes = (double)pl.P * a.D * 4;
   if (pl.P2) {
-    e = attnres::launch_bwd_reduce(a, pl, 0, timed_launch(K_BWD_REDUCE, pbytes + pl.P2 * D * 4.0, st));
+    e = attnres::launch_bwd_reduce(a, pl, 0, timed_launch(K_BWD_REDUCE, pbytes + pl.P2 * a.D * 4.0, st));
     if (e != hipSuccess) return hip_fail(fn, e);
   }
-  const double fin = (double)(pl.P2 ? pl.P2 : pl.P) * D * 4 + D * 4.0 * ((dgamma ? 2 : 1) * (accumulate ? 2 : 1));
+  const double fin = (double)(pl.P2 ? pl.P2 : pl.P) * a.D * 4 +
+                     a.D * 4.0 * ((a.dgamma ? 2 : 1) * (a.accumulate ? 2 : 1));
   e = attnres::launch_bwd_reduce(a, pl, 1, timed_launch(K_BWD_REDUCE, fin, st));
   if (e != hipSuccess) return hip_fail(fn, e);
+  return ATTNRES_OK;
+}
+
+}  // namespace
+
+ATTNRES_API int attnres_aggregate_backward(const void* const* sources, int n, int64_t R, int64_t D,
+                                           int dtype, const float* w, const float* gamma, float eps,
+                                           const void* dh, float* const* dV, int accumulate,
+                                           float* dw, float* dgamma, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  const char* fn = "attnres_aggregate_backward";
+  BwdPlan pl;
+  TRY(validate_backward(fn, sources, n, R, D, dtype, w, gamma, eps, dh, dV, dw, dgamma, &pl));
+  if (pl.bytes > 0) {
+    TRY(check_ptr(fn, "workspace", workspace, true));
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(ATTNRES_EINVAL, "%s: workspace is not 256-byte aligned", fn);
+    if (workspace_bytes < pl.bytes)
+      return fail(ATTNRES_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn,
+                  workspace_bytes, pl.bytes);
+  }
+  BwdArgs a{sources, n, R, D, w, gamma, eps, dh, dV, accumulate, dw, dgamma, workspace};
+  TRY(launch_backward(fn, dtype, a, pl, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// The aggregate backward without a workspace argument, for callers that
+// cannot allocate. Its dq~ partials live in `scratch`, a device array of a
+// fixed size that the HIP runtime places on each GPU when it loads this
+// library's code there and keeps until the process ends. On the host the
+// name `scratch` is only a stand-in for the array: its device address comes
+// from hipGetSymbolAddress, looked up once per device with that device
+// current, and only that address is ever handed to a kernel.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[ATTNRES_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, null until looked up
+
+// The device address of `scratch` on the device that `stream` runs on, which
+// must be the calling thread's current device.
+int scratch_address(const char* fn, hipStream_t stream, void** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  if (stream) {
+    hipDevice_t sd = -1;
+    e = hipStreamGetDevice(stream, &sd);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (sd != cur)
+      return fail(ATTNRES_EINVAL, "%s: the stream belongs to device %d, but device %d is current", fn,
+                  (int)sd, cur);
+  }
+  if (cur < 0 || cur >= kMaxDevices)
+    return fail(ATTNRES_EUNSUPPORTED, "%s: device %d beyond the %d this build tracks", fn, cur,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[cur]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (!p) return fail(ATTNRES_EHIP, "%s: no device address for the scratch array", fn);
+    g_scratch_ptr[cur] = p;
+  }
+  *out = g_scratch_ptr[cur];
+  return ATTNRES_OK;
+}
+
+}  // namespace
+
+ATTNRES_API size_t attnres_noalloc_scratch_bytes(void) { return ATTNRES_NOALLOC_SCRATCH_BYTES; }
+
+ATTNRES_API int attnres_aggregate_backward_noalloc(const void* const* sources, int n, int64_t R,
+                                                   int64_t D, int dtype, const float* w,
+                                                   const float* gamma, float eps, const void* dh,
+                                                   float* const* dV, int accumulate, float* dw,
+                                                   float* dgamma, void* stream) {
+  const char* fn = "attnres_aggregate_backward_noalloc";
+  BwdPlan pl;
+  TRY(validate_backward(fn, sources, n, R, D, dtype, w, gamma, eps, dh, dV, dw, dgamma, &pl));
+  if (pl.bytes > (size_t)ATTNRES_NOALLOC_SCRATCH_BYTES)
+    return fail(ATTNRES_EUNSUPPORTED,
+                "%s: D = %lld needs %zu bytes of scratch, above the fixed %zu; use "
+                "attnres_aggregate_backward with a workspace",
+                fn, (long long)D, pl.bytes, (size_t)ATTNRES_NOALLOC_SCRATCH_BYTES);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  TRY(scratch_address(fn, st, &ws));
+  BwdArgs a{sources, n, R, D, w, gamma, eps, dh, dV, accumulate, dw, dgamma, ws};
+  TRY(launch_backward(fn, dtype, a, pl, st));
   return ok();
 }
 

@@ -308,6 +308,38 @@ int attnres_aggregate_backward(const void* const* sources, int n, int64_t R, int
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * attnres_aggregate_backward_noalloc -- attnres_aggregate_backward without a
+ * workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving or training loops, and harnesses
+ * that forbid hipMalloc. It allocates nothing (no hipMalloc, no hipFree, no
+ * allocating library routine) and runs the same kernels with the same
+ * results: every argument, output and error is as for
+ * attnres_aggregate_backward.
+ *   Its scratch (the per-workgroup dq~ partials) is a fixed device array of
+ *   ATTNRES_NOALLOC_SCRATCH_BYTES (33 MiB) that each GPU holds from the
+ *   library's first use there until the process ends. It covers every row
+ *   of at most 8192 elements, whatever R is. A bf16 row with D > 8192 needs
+ *   more once R fills the backward's grid (a few thousand rows); such a call
+ *   is rejected with ATTNRES_EUNSUPPORTED before anything is enqueued (the
+ *   rule: attnres_aggregate_backward_workspace_bytes(R, D, dtype) >
+ *   ATTNRES_NOALLOC_SCRATCH_BYTES).
+ *   `stream` must belong to the calling thread's current device
+ *   (ATTNRES_EINVAL otherwise).
+ *   All calls on one GPU share that GPU's array and nothing guards it: two
+ *   calls whose work overlaps on one GPU (on different streams, or from
+ *   different threads without ordering) race and give undefined results.
+ *   Calls ordered on one stream are safe; the array keeps the last call's
+ *   contents, and every call writes its partials before reading them.
+ * attnres_noalloc_scratch_bytes returns ATTNRES_NOALLOC_SCRATCH_BYTES.
+ * ------------------------------------------------------------------------- */
+#define ATTNRES_NOALLOC_SCRATCH_BYTES (33u << 20)
+size_t attnres_noalloc_scratch_bytes(void);
+int attnres_aggregate_backward_noalloc(const void* const* sources, int n, int64_t R, int64_t D,
+                                       int dtype, const float* w, const float* gamma, float eps,
+                                       const void* dh, float* const* dV, int accumulate, float* dw,
+                                       float* dgamma, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Optional launch timing (instrumentation for benchmarks; off by default).
  * attnres_timing_enable(capacity) makes this thread's subsequent launches
  * record a HIP event pair around each kernel on its stream, for up to

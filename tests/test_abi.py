@@ -198,3 +198,25 @@ def test_generator_twin_rounding_and_distribution():
     # distinct streams differ, the same stream repeats
     assert not np.array_equal(inputs.normal(0, 2, 1, np.arange(10)), inputs.normal(0, 2, 2, np.arange(10)))
     assert np.array_equal(inputs.normal(5, 2, 1, np.arange(10)), inputs.normal(5, 2, 1, np.arange(10)))
+
+
+def test_noalloc_backward_validates_on_the_host():
+    """The no-allocation backward checks its arguments and its scratch limit
+    before it looks up any device."""
+    L = b.lib()
+    assert L.attnres_noalloc_scratch_bytes() == 33 << 20
+    src = (ctypes.c_void_p * 1)(0x20000)
+    dv = (ctypes.c_void_p * 1)(0x40000)
+    # a bf16 row of 8200 elements needs more scratch than the fixed array holds
+    rc = L.attnres_aggregate_backward_noalloc(src, 1, 4096, 8200, 1, FAKE, None, 1e-8, ctypes.c_void_p(0x30000),
+                                              dv, 0, ctypes.c_void_p(0x50000), None, None)
+    assert rc == -2 and "scratch" in _last()
+    assert b.lib().attnres_aggregate_backward_workspace_bytes(4096, 8200, 1) > (33 << 20)
+    assert b.lib().attnres_aggregate_backward_workspace_bytes(1 << 27, 8192, 1) <= (33 << 20)
+    assert b.lib().attnres_aggregate_backward_workspace_bytes(1 << 27, 8192, 0) <= (33 << 20)
+    rc = L.attnres_aggregate_backward_noalloc(src, 0, 64, 1024, 1, FAKE, None, 1e-8, ctypes.c_void_p(0x30000),
+                                              dv, 0, ctypes.c_void_p(0x50000), None, None)
+    assert rc == -1 and "n = 0" in _last()
+    rc = L.attnres_aggregate_backward_noalloc(src, 1, 64, 1024, 1, FAKE, None, 1e-8, ctypes.c_void_p(0x30000),
+                                              dv, 0, None, None, None)
+    assert rc == -1 and "dw is NULL" in _last()
