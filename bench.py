@@ -145,7 +145,7 @@ def cpu_baseline(ds, wl, seconds: float, chunk: int = 2048) -> dict:
 
     if not os.path.exists(oracle.LIBRARY):
         oracle.build()
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    cores, host = oracle_threads()
     done, spent, start = 0, 0.0, 0
     while done == 0 or spent < seconds:
         rows = np.arange(start, min(start + chunk, wl.R))
@@ -156,10 +156,20 @@ def cpu_baseline(ds, wl, seconds: float, chunk: int = 2048) -> dict:
         spent += time.perf_counter() - c0
         done += len(rows)
         del xr, vr
-    return {"value": round(done / spent, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": round(done / spent, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle", **host,
             "sample": f"{done} token rows in chunks of {chunk} consecutive rows cycling over the "
                       f"{wl.R} of the workload, full {wl.L}-sublayer naive forward in fp64 "
                       f"({cores} threads), {spent:.2f} s of CPU time (host copies excluded)"}
+
+
+def oracle_threads():
+    """(threads, host facts) of the CPU baseline: every core this process may
+    run on, up to the host's CPU share of one GPU (OMP_NUM_THREADS, 16 when
+    unset: a one-GPU job gets 16 of the host's cores)."""
+    affinity = len(os.sched_getaffinity(0))
+    share = int(os.environ.get("OMP_NUM_THREADS", "16") or 16)
+    threads = max(1, min(affinity, share))
+    return threads, {"nproc": affinity, "hardware_concurrency": os.cpu_count(), "cpu_share": share}
 
 
 def calibration_copy(gib: float):
@@ -255,7 +265,7 @@ def bench_backward(args, wl) -> dict:
         import oracle
         if not os.path.exists(oracle.LIBRARY):
             oracle.build()
-        cores = max(1, min(16, len(os.sched_getaffinity(0))))
+        cores, host = oracle_threads()
         done, spent, start, chunk = 0, 0.0, 0, 256
         while done == 0 or spent < args.cpu_seconds:
             rows = np.arange(start, min(start + chunk, R))
@@ -267,7 +277,7 @@ def bench_backward(args, wl) -> dict:
             oracle.aggregate_backward(hs, w_h, hdh, g_h, eps=EPS, nthreads=cores)
             spent += time.perf_counter() - c0
             done += len(rows)
-        cpu = {"value": round(done / spent, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        cpu = {"value": round(done / spent, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle", **host,
                "sample": f"{done} token rows in chunks of {chunk} consecutive rows, the fp64 aggregate "
                          f"backward over {n} sources ({cores} threads), {spent:.2f} s of CPU time"}
     return {
@@ -418,6 +428,9 @@ def main() -> int:
     ap.add_argument("--full-schedule", type=int, default=0, metavar="C",
                     help="run a Full (S = 1) workload with the two-phase schedule of block size C "
                          "(attnres_full_stack_forward; C = 1 is the naive schedule)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="the decode schedule: each block's Phase 1 on a side stream during the previous "
+                         "block (attnres_block_stack_forward_overlap)")
     ap.add_argument("--output-norm", action="store_true",
                     help="hand every sublayer RMSNorm(h_l) * gamma_l (fused into Phase 2) instead of h_l")
     ap.add_argument("--backward", type=int, default=0, metavar="N",
@@ -462,6 +475,7 @@ def main() -> int:
     assert wl.kind == "stack", "the benchmark times a stack workload"
     assert not (wl.ring and (args.graph or args.full_schedule)), \
         "a generated-ring workload runs the plain eager stack forward"
+    assert not (args.overlap and args.full_schedule), "--overlap runs the Block schedule"
     ds = DeviceStack(wl)
     nb = ds.nb
     norm = None
@@ -480,8 +494,10 @@ def main() -> int:
             binding.attnres_full_stack_forward(ds.x, ds.W, args.full_schedule, ds.sublayer, eps=EPS,
                                                y=ds.y, workspace=fws, stream=stream)
     else:
+        side_stream = torch.cuda.Stream() if args.overlap else None
+
         def forward(stream=None):
-            ds.forward(stream=stream, norm=norm)
+            ds.forward(stream=stream, norm=norm, side_stream=side_stream)
 
     calibration_copy(args.calibration_copy_gib)
 
@@ -549,8 +565,8 @@ def main() -> int:
         n, ms, byts = binding.attnres_timing_read(k)
         if n:
             n_step = n / n_timed
-            kinds[k] = {"launches_per_step": n_step, "avg_us": 1e3 * ms / n,
-                        "ms_per_step": ms / n_timed,
+            kinds[k] = {"kernel": binding.attnres_timing_kernels(k), "launches_per_step": n_step,
+                        "avg_us": 1e3 * ms / n, "ms_per_step": ms / n_timed,
                         "bytes_per_launch": byts / n, "GBps": byts / (ms * 1e6)}
     binding.attnres_timing_enable(0)
 
@@ -566,16 +582,22 @@ def main() -> int:
     # the dominant kernel: Phase 2 in a Block stack, else the kind with the most time per step
     dom_kind = "phase2" if "phase2" in kinds else max(kinds, key=lambda k: kinds[k]["ms_per_step"])
     dom = kinds[dom_kind]
-    dom_name = {"phase1": "phase1_mfma_kernel", "phase1_stats": "phase1_single_kernel",
-                "phase2": "phase2_kernel", "aggregate": "aggregate_kernel",
-                "norm": "rmsnorm_kernel", "close": "close_kernel", "fold": "fold_kernel"}[dom_kind]
-    traffic = measured_traffic(wl.name) if dom_kind == "phase2" and not norm else None
-    roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(dom["GBps"], 1),
+    traffic = measured_traffic(wl.name) if dom_kind == "phase2" and not norm and not args.overlap else None
+    roofline = {"bound": "hbm", "kernel": dom["kernel"], "achieved": round(dom["GBps"], 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom["GBps"] / PEAK_HBM_GBPS, 4),
                 "traffic": traffic, "bytes_per_launch": dom["bytes_per_launch"],
                 "avg_launch_us": round(dom["avg_us"], 2),
                 "timed_launches": int(round(dom["launches_per_step"] * n_timed)),
                 "timed_in": "eager pass before the graph replays" if graph is not None else "timed region"}
+    # the two phases of the Block schedule, each against the peak with its own
+    # bytes and time (the target names both), and the lower of the two
+    phases = {k: kinds[k] for k in ("phase1", "phase2") if k in kinds}
+    if phases:
+        roofline["phases"] = {k: {"kernel": v["kernel"], "achieved": round(v["GBps"], 1),
+                                  "frac": round(v["GBps"] / PEAK_HBM_GBPS, 4),
+                                  "bytes_per_launch": v["bytes_per_launch"], "avg_launch_us": round(v["avg_us"], 2),
+                                  "launches_per_step": v["launches_per_step"]} for k, v in phases.items()}
+        roofline["min_phase_frac"] = min(p["frac"] for p in roofline["phases"].values())
 
     cpu = cpu_baseline(ds, wl, args.cpu_seconds) if args.cpu_rows > 0 else None
 
@@ -597,7 +619,7 @@ def main() -> int:
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "D": wl.D, "L": wl.L, "S": wl.S,
                    "blocks": nb, "global_batch": wl.B, "seq_len": wl.T, "parallelism": "single GPU",
                    "output_norm": bool(norm), "hip_graph": graph is not None,
-                   "full_schedule": args.full_schedule or None},
+                   "full_schedule": args.full_schedule or None, "overlap": bool(args.overlap)},
         "attnres_kernel_ms_per_step": round(attnres_ms, 4),
         "rate_from": "sum of AttnRes kernel durations (HIP events), sublayer-output generation excluded"
                      if wl.ring else "wall time per step",

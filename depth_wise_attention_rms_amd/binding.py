@@ -29,12 +29,14 @@ EXPORTS = (
     "attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge",
     "attnres_phase2_merge_norm", "attnres_rmsnorm", "attnres_table_sublayer",
     "attnres_stack_workspace_bytes", "attnres_block_stack_forward",
-    "attnres_block_stack_forward_norm", "attnres_merge_sources", "attnres_full_workspace_bytes",
+    "attnres_block_stack_forward_norm", "attnres_stack_overlap_workspace_bytes",
+    "attnres_block_stack_forward_overlap", "attnres_merge_sources", "attnres_full_workspace_bytes",
     "attnres_full_stack_forward", "attnres_aggregate_backward_workspace_bytes",
     "attnres_aggregate_backward", "attnres_aggregate_backward_noalloc",
     "attnres_noalloc_scratch_bytes", "attnres_block_layout",
     "attnres_atomic_block_size", "attnres_status_string", "attnres_last_error",
     "attnres_timing_enable", "attnres_timing_pause", "attnres_timing_reset", "attnres_timing_read",
+    "attnres_timing_kernels", "attnres_timing_trace",
 )
 
 SUBLAYER_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
@@ -72,6 +74,10 @@ def lib():
         L.attnres_block_stack_forward.argtypes = [P, I, I, I64, I64, I, P, P, F, P, P, P, P, P, SZ, P]
         L.attnres_block_stack_forward_norm.argtypes = [P, I, I, I64, I64, I, P, P, F, P, F, P, P, P, P,
                                                        P, SZ, P]
+        L.attnres_stack_overlap_workspace_bytes.argtypes = [I, I, I64, I64, I]
+        L.attnres_stack_overlap_workspace_bytes.restype = SZ
+        L.attnres_block_stack_forward_overlap.argtypes = [P, I, I, I64, I64, I, P, P, F, I, P, F, P, P, P,
+                                                          P, P, SZ, P, P]
         L.attnres_merge_sources.argtypes = [P, P, P, I, I64, I64, I, P, P, F, P, P, P, P]
         L.attnres_full_workspace_bytes.argtypes = [I, I, I64, I64, I]
         L.attnres_full_workspace_bytes.restype = SZ
@@ -92,10 +98,15 @@ def lib():
         L.attnres_timing_pause.argtypes = [I]
         L.attnres_timing_reset.argtypes = []
         L.attnres_timing_read.argtypes = [I, ctypes.POINTER(I64), ctypes.POINTER(D), ctypes.POINTER(D)]
+        L.attnres_timing_trace.argtypes = [I, P, P, P, P]
+        L.attnres_timing_trace.restype = I
+        L.attnres_timing_kernels.argtypes = [I]
+        L.attnres_timing_kernels.restype = ctypes.c_char_p
         for f in ("attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge",
                   "attnres_phase2_merge_norm", "attnres_rmsnorm", "attnres_block_stack_forward_norm",
                   "attnres_merge_sources", "attnres_full_stack_forward", "attnres_aggregate_backward",
                   "attnres_aggregate_backward_noalloc", "attnres_table_sublayer", "attnres_block_stack_forward", "attnres_block_layout",
+                  "attnres_block_stack_forward_overlap",
                   "attnres_atomic_block_size", "attnres_timing_enable", "attnres_timing_pause",
                   "attnres_timing_reset", "attnres_timing_read"):
             getattr(L, f).restype = ctypes.c_int
@@ -274,20 +285,25 @@ def _sublayer_fn(sublayer: Sublayer):
 
 def attnres_block_stack_forward(x: torch.Tensor, W: torch.Tensor, S: int, sublayer: Sublayer,
                                 Gamma=None, eps=1e-8, block_sums=None, y=None, workspace=None,
-                                stream=None, norm=None):
+                                stream=None, norm=None, keep_sources=None):
     """Block AttnRes stack forward (Full when S == 1). ``sublayer`` is a list of
     L pre-computed outputs, a NativeSublayer, or a Python callable
     ``f(l, h_ptr) -> tensor v_l``. Returns (y, block_sums). With
     ``norm=(Gamma_f, eps_f)`` (Gamma_f an [L, D] fp32 tensor or None) the
     sublayers receive RMSNorm(h_l) * Gamma_f[l-1] instead of h_l
-    (attnres_block_stack_forward_norm)."""
+    (attnres_block_stack_forward_norm). ``keep_sources`` (S == 1 only): the
+    sublayer outputs stay valid for the whole call, so they serve as the
+    sources themselves and no block sums are formed (default: True for a
+    list of outputs)."""
     R, D = _rows(x)
     L = W.shape[0] - 1
     dt = dtype_code(x.dtype)
     nb = attnres_block_layout(L, S)[0]
     if y is None:
         y = torch.empty_like(x)
-    if block_sums is None and not (S == 1 and isinstance(sublayer, (list, tuple))):
+    if keep_sources is None:
+        keep_sources = isinstance(sublayer, (list, tuple))
+    if block_sums is None and not (S == 1 and keep_sources):
         block_sums = [torch.empty_like(x) for _ in range(nb)]
     need = attnres_stack_workspace_bytes(L, S, R, D, x.dtype)
     if workspace is None:
@@ -303,6 +319,38 @@ def attnres_block_stack_forward(x: torch.Tensor, W: torch.Tensor, S: int, sublay
         _check("attnres_block_stack_forward_norm", lib().attnres_block_stack_forward_norm(
             _ptr(x), L, S, R, D, dt, _ptr(W), _ptr(Gamma), eps, _ptr(Gamma_f), eps_f, fn, ctx, bs,
             _ptr(y), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
+    return y, block_sums
+
+
+def attnres_stack_overlap_workspace_bytes(L: int, S: int, R: int, D: int, dtype: torch.dtype) -> int:
+    return int(lib().attnres_stack_overlap_workspace_bytes(L, S, R, D, dtype_code(dtype)))
+
+
+def attnres_block_stack_forward_overlap(x: torch.Tensor, W: torch.Tensor, S: int, sublayer: Sublayer,
+                                        side_stream, Gamma=None, eps=1e-8, block_sums=None, y=None,
+                                        workspace=None, stream=None, norm=None):
+    """The stack forward with the decode schedule: each block's Phase 1 runs on
+    ``side_stream`` during the previous block (a torch.cuda.Stream of the same
+    device). Arguments and result as attnres_block_stack_forward; block sums
+    are always produced."""
+    R, D = _rows(x)
+    L = W.shape[0] - 1
+    dt = dtype_code(x.dtype)
+    nb = attnres_block_layout(L, S)[0]
+    if y is None:
+        y = torch.empty_like(x)
+    if block_sums is None:
+        block_sums = [torch.empty_like(x) for _ in range(nb)]
+    need = attnres_stack_overlap_workspace_bytes(L, S, R, D, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    fn, ctx, keep = _sublayer_fn(sublayer)
+    Gamma_f, eps_f = norm if norm is not None else (None, 0.0)
+    _check("attnres_block_stack_forward_overlap", lib().attnres_block_stack_forward_overlap(
+        _ptr(x), L, S, R, D, dt, _ptr(W), _ptr(Gamma), eps, 1 if norm is not None else 0,
+        _ptr(Gamma_f), eps_f, fn, ctx, _ptr_array(block_sums), _ptr(y),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream), _stream(side_stream)))
+    del keep
     return y, block_sums
 
 
@@ -409,3 +457,25 @@ def attnres_timing_read(kind: str):
     _check("attnres_timing_read", lib().attnres_timing_read(TIMING_KINDS[kind], ctypes.byref(n),
                                                             ctypes.byref(ms), ctypes.byref(b)))
     return n.value, ms.value, b.value
+
+
+def attnres_timing_trace(max_launches: int = 4096):
+    """[(kind name, stream handle, start ms, end ms)] of the timed launches, in
+    enqueue order, relative to the first one's start."""
+    import numpy as np
+    kinds = np.zeros(max_launches, np.int32)
+    streams = np.zeros(max_launches, np.uint64)
+    t0 = np.zeros(max_launches, np.float64)
+    t1 = np.zeros(max_launches, np.float64)
+    n = lib().attnres_timing_trace(max_launches, kinds.ctypes.data, streams.ctypes.data, t0.ctypes.data,
+                                   t1.ctypes.data)
+    if n < 0:
+        _check("attnres_timing_trace", n)
+    names = {v: k for k, v in TIMING_KINDS.items()}
+    return [(names.get(int(kinds[i]), str(kinds[i])), int(streams[i]), float(t0[i]), float(t1[i]))
+            for i in range(n)]
+
+
+def attnres_timing_kernels(kind: str) -> str:
+    """Comma-separated names of the kernels the timed launches of a kind ran."""
+    return lib().attnres_timing_kernels(TIMING_KINDS[kind]).decode()

@@ -93,11 +93,36 @@ enum Kind {
   K_COUNT = 9
 };
 
+// the kernel a kind's launches run, unless the launch names another
+const char* kind_kernel(int kind) {
+  switch (kind) {
+    case K_PHASE2: return "phase2_kernel";
+    case K_AGG: return "aggregate_kernel";
+    case K_CLOSE: return "close_kernel";
+    case K_FOLD: return "fold_kernel";
+    case K_NORM: return "rmsnorm_kernel";
+    case K_BWD: return "aggregate_bwd_kernel";
+    case K_BWD_REDUCE: return "bwd_colsum_kernel";
+    default: return "phase1_kernel";
+  }
+}
+
 struct Timing {
   int capacity = 0;
   std::vector<hipEvent_t> ev;  // 2 per slot: the kernel's start and end
   std::vector<int> kind;
   std::vector<double> bytes;
+  std::vector<const char*> name;  // kernel(s) of the slot's launch
+  std::vector<hipStream_t> stream;
+  std::string names[K_COUNT];     // distinct kernel names per kind, comma-separated
+  // the last collected launches in record order: kind, stream and start / end
+  // relative to the first one's start (ms)
+  struct Span {
+    int kind;
+    uintptr_t stream;
+    double start, end;
+  };
+  std::vector<Span> trace;
   int used = 0;
   bool paused = false;
   int64_t launches[K_COUNT] = {0};
@@ -108,13 +133,15 @@ thread_local Timing g_timing;
 
 // The Launch of one kernel: when timing is on and a slot is free, it carries
 // an event pair that the dispatch itself stamps (no extra queue packets).
-Launch timed_launch(int kind, double bytes, hipStream_t st) {
+Launch timed_launch(int kind, double bytes, hipStream_t st, const char* kernel = nullptr) {
   Launch L{st, nullptr, nullptr};
   Timing& t = g_timing;
   if (t.capacity > 0 && !t.paused && t.used < t.capacity) {
     const int slot = t.used++;
     t.kind[slot] = kind;
     t.bytes[slot] = bytes;
+    t.name[slot] = kernel ? kernel : kind_kernel(kind);
+    t.stream[slot] = st;
     L.start = t.ev[2 * slot];
     L.stop = t.ev[2 * slot + 1];
   }
@@ -167,15 +194,17 @@ int do_phase1(const char* fn, int dtype, const Phase1Args& a, hipStream_t st) {
     const double rb = (double)a.R * row_bytes;
     const double bytes = rb * (a.n + (a.out ? a.S : 0)) + (double)a.R * a.S * ((a.m_out ? 4 : 0) + 4);
     hipError_t e = attnres::launch_phase1_gemm(
-        g, a.gemm_ws, timed_launch(a.out ? K_PHASE1 : K_PHASE1_STATS, bytes, st));
+        g, a.gemm_ws, timed_launch(a.out ? K_PHASE1 : K_PHASE1_STATS, bytes, st,
+                                   attnres::phase1_kernel_name(dtype, g, true)));
     return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
   }
   if (attnres::phase1_supported(dtype, a.n, a.S, a.D)) {
     const double rb = (double)a.R * row_bytes;
     const double bytes = rb * (a.n + (a.out ? a.S : 0)) + (double)a.R * a.S * ((a.m_out ? 4 : 0) + 4) +
                          close_bytes(rb, a.close_p, a.close_v);
-    hipError_t e = attnres::launch_phase1(dtype, a,
-                                          timed_launch(a.out ? K_PHASE1 : K_PHASE1_STATS, bytes, st));
+    hipError_t e = attnres::launch_phase1(
+        dtype, a, timed_launch(a.out ? K_PHASE1 : K_PHASE1_STATS, bytes, st,
+                               attnres::phase1_kernel_name(dtype, a, false)));
     return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
   }
   // More sources than the register-resident pass holds: close separately,
@@ -195,7 +224,7 @@ int do_phase2(const char* fn, int dtype, const Phase2Args& a, hipStream_t st) {
   if (a.R == 0) return ATTNRES_OK;
   const double rb = (double)a.R * a.D * esize_of(dtype);
   const int writes = (a.h_out ? 1 : 0) + (a.hn_out ? 1 : 0);
-  const double bytes = rb * ((a.p_prev ? 4 : 2) + writes) + (double)a.R * 4;
+  const double bytes = rb * ((a.p_prev ? 4 : 2) + (a.xs ? 1 : 0) + writes) + (double)a.R * 4;
   hipError_t e = attnres::launch_phase2(dtype, a, timed_launch(K_PHASE2, bytes, st));
   return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
 }
@@ -206,6 +235,22 @@ int do_rmsnorm(const char* fn, int dtype, const void* x, int64_t R, int64_t D, c
   const double bytes = 2.0 * (double)R * D * esize_of(dtype);
   hipError_t e = attnres::launch_rmsnorm(dtype, x, R, D, g, eps, out, timed_launch(K_NORM, bytes, st));
   return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
+}
+
+// The folded queries q~ = w * gamma of all L+1 aggregations [K3 9.2 (1)],
+// formed once per forward into `ws_q`; without gains q~ is w itself, read in
+// place (no launch).
+int fold_queries(const char* fn, const float* W, const float* Gamma, int L, int64_t D, float* ws_q,
+                 hipStream_t st, const float** Q) {
+  if (!Gamma) {
+    *Q = W;
+    return ATTNRES_OK;
+  }
+  hipError_t e = attnres::launch_fold(W, Gamma, ws_q, (int64_t)(L + 1) * D,
+                                      timed_launch(K_FOLD, (double)(L + 1) * D * 12, st));
+  if (e != hipSuccess) return hip_fail(fn, e);
+  *Q = ws_q;
+  return ATTNRES_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -462,6 +507,45 @@ ATTNRES_API int attnres_block_stack_forward_norm(const void* x, int L, int S, in
 
 namespace {
 
+int stack_forward_overlap(const char* fn, const void* x, int L, int S, int64_t R, int64_t D,
+                          int dtype, const float* W, const float* Gamma, float eps,
+                          attnres_sublayer_fn f, void* f_ctx, void* const* block_sums, void* y,
+                          void* workspace, size_t workspace_bytes, const OutNorm& nm, void* stream,
+                          void* side_stream);
+struct OverlapLayout;
+size_t overlap_total(int L, int S, int64_t R, int64_t D, int es);
+
+}  // namespace
+
+ATTNRES_API size_t attnres_stack_overlap_workspace_bytes(int L, int S, int64_t R, int64_t D,
+                                                         int dtype) {
+  const int es = esize_of(dtype);
+  if (!es || L < 1 || S < 1 || R < 0 || D < 1) return 0;
+  return overlap_total(L, S, R, D, es);
+}
+
+ATTNRES_API int attnres_block_stack_forward_overlap(const void* x, int L, int S, int64_t R,
+                                                    int64_t D, int dtype, const float* W,
+                                                    const float* Gamma, float eps, int out_norm,
+                                                    const float* Gamma_f, float eps_f,
+                                                    attnres_sublayer_fn f, void* f_ctx,
+                                                    void* const* block_sums, void* y,
+                                                    void* workspace, size_t workspace_bytes,
+                                                    void* stream, void* side_stream) {
+  const char* fn = "attnres_block_stack_forward_overlap";
+  if (out_norm) {
+    if (!std::isfinite(eps_f) || eps_f < 0.f)
+      return fail(ATTNRES_EINVAL, "%s: eps_f must be finite and >= 0", fn);
+    if (R > 0) TRY(check_ptr(fn, "Gamma_f", Gamma_f, false));
+  }
+  return stack_forward_overlap(fn, x, L, S, R, D, dtype, W, Gamma, eps, f, f_ctx, block_sums, y,
+                               workspace, workspace_bytes,
+                               OutNorm{out_norm != 0, out_norm ? Gamma_f : nullptr, eps_f}, stream,
+                               side_stream);
+}
+
+namespace {
+
 int stack_forward(const char* fn, const void* x, int L, int S, int64_t R, int64_t D, int dtype,
                   const float* W, const float* Gamma, float eps, attnres_sublayer_fn f, void* f_ctx,
                   void* const* block_sums, void* y, void* workspace, size_t workspace_bytes,
@@ -493,7 +577,6 @@ int stack_forward(const char* fn, const void* x, int L, int S, int64_t R, int64_
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  float* Q = reinterpret_cast<float*>(ws + lay.q);
   char* O = ws + lay.o;
   float* M = reinterpret_cast<float*>(ws + lay.m);
   float* LSE = reinterpret_cast<float*>(ws + lay.lse);
@@ -501,12 +584,8 @@ int stack_forward(const char* fn, const void* x, int L, int S, int64_t R, int64_
   void* H = ws + lay.h;
   const int64_t tensor_bytes = R * D * es;
 
-  {  // fold q~ = w * gamma once for all L+1 queries [K3 9.2 (1)]
-    hipError_t e = attnres::launch_fold(
-        W, Gamma, Q, (int64_t)(L + 1) * D,
-        timed_launch(K_FOLD, (double)(L + 1) * D * (Gamma ? 12 : 8), st));
-    if (e != hipSuccess) return hip_fail(fn, e);
-  }
+  const float* Q = nullptr;
+  TRY(fold_queries(fn, W, Gamma, L, D, reinterpret_cast<float*>(ws + lay.q), st, &Q));
 
   // the sublayer's input: h_l, or RMSNorm(h_l) * Gamma_f[l-1] written to H
   // (in place when h_l is already in H)
@@ -606,6 +685,265 @@ int stack_forward(const char* fn, const void* x, int L, int S, int64_t R, int64_
   return ok();
 }
 
+// ---------------------------------------------------------------------------
+// The decode schedule: block k+1's Phase 1 runs on a side stream while block
+// k's sublayers run on the main stream [WC "Kimi Linear and K3 integration",
+// decode: the batched inter-block pass on a side stream]. The merge of
+// source groups is exact [K3 9.4 (OS2)], so that Phase 1 needs only the
+// sources that exist when block k starts, [b_0 .. b_k]; the block sum
+// b_{k+1} that block k closes with is merged in afterwards as one more
+// single-source term: block k+1's first sublayer gets OS2((lse_0, o_0),
+// b_{k+1}) from one launch that also performs the close, and each further
+// sublayer's Phase-2 step merges three terms, (lse_j, o_j), b_{k+1} and the
+// partial. Two Phase-1 slots alternate between the streams.
+// ---------------------------------------------------------------------------
+#ifndef ATTNRES_OVERLAP_SIDE_GROUPS
+#define ATTNRES_OVERLAP_SIDE_GROUPS 128  // workgroup budget of a side-stream Phase 1: half the CUs
+#endif
+
+struct OverlapLayout {
+  size_t q, o[2], m[2], lse[2], p, h, g, total;
+};
+
+OverlapLayout overlap_layout(int L, int S, int64_t R, int64_t D, int es) {
+  OverlapLayout s;
+  const int Sk = S < L ? S : L;  // widest block
+  const size_t row = (size_t)R * (size_t)D * es;
+  size_t off = 0;
+  s.q = off; off = align256(off + (size_t)(L + 1) * D * sizeof(float));
+  for (int b = 0; b < 2; ++b) {
+    s.o[b] = off; off = align256(off + (size_t)Sk * row);
+    s.m[b] = off; off = align256(off + (size_t)Sk * R * sizeof(float));
+    s.lse[b] = off; off = align256(off + (size_t)Sk * R * sizeof(float));
+  }
+  s.p = off; off = align256(off + (Sk > 2 ? row : 0));
+  s.h = off; off = align256(off + row);
+  s.g = off;
+  if (Sk > 1 && attnres::phase1_gemm_shape(es == 2 ? 1 : 0, Sk, D, R) &&
+      !attnres::phase1_mfma_eligible(es == 2 ? 1 : 0, 1, Sk, D))
+    off = align256(off + attnres::phase1_gemm_workspace(Sk, R, D));
+  s.total = off;
+  return s;
+}
+
+size_t overlap_total(int L, int S, int64_t R, int64_t D, int es) {
+  return overlap_layout(L, S, R, D, es).total;
+}
+
+// The two ordering events of the decode schedule, per thread and device,
+// created at first use and reused by every later call (timing disabled).
+struct OverlapEvents {
+  hipEvent_t main_ready = nullptr;  // main stream: the sources and the next slot are ready
+  hipEvent_t side_done = nullptr;   // side stream: a block's Phase 1 is written
+};
+thread_local OverlapEvents g_overlap_events[64];
+
+int overlap_events(const char* fn, int dev, OverlapEvents** out) {
+  if (dev < 0 || dev >= 64)
+    return fail(ATTNRES_EUNSUPPORTED, "%s: device %d beyond the 64 this build tracks", fn, dev);
+  OverlapEvents& e = g_overlap_events[dev];
+  for (hipEvent_t* ev : {&e.main_ready, &e.side_done}) {
+    if (*ev) continue;
+    hipError_t rc = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+    if (rc != hipSuccess) {
+      *ev = nullptr;
+      return hip_fail(fn, rc);
+    }
+  }
+  *out = &e;
+  return ATTNRES_OK;
+}
+
+int stream_device(const char* fn, hipStream_t st, int* dev) {
+  hipError_t e;
+  if (st) {
+    hipDevice_t d = -1;
+    e = hipStreamGetDevice(st, &d);
+    *dev = (int)d;
+  } else {
+    e = hipGetDevice(dev);
+  }
+  return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
+}
+
+int stack_forward_overlap(const char* fn, const void* x, int L, int S, int64_t R, int64_t D,
+                          int dtype, const float* W, const float* Gamma, float eps,
+                          attnres_sublayer_fn f, void* f_ctx, void* const* block_sums, void* y,
+                          void* workspace, size_t workspace_bytes, const OutNorm& nm, void* stream,
+                          void* side_stream) {
+  TRY(check_shape(fn, R, D, dtype, eps));
+  if (L < 1 || S < 1) return fail(ATTNRES_EINVAL, "%s: L = %d and S = %d must be >= 1", fn, L, S);
+  const int nb = plan(L, S, nullptr, nullptr);
+  if (nb + 1 > ATTNRES_MAX_SOURCES)
+    return fail(ATTNRES_EINVAL, "%s: %d blocks plus the embedding exceed %d sources", fn, nb,
+                ATTNRES_MAX_SOURCES);
+  if (R == 0) return ok();
+  TRY(check_ptr(fn, "x", x, true));
+  TRY(check_ptr(fn, "W", W, true));
+  TRY(check_ptr(fn, "Gamma", Gamma, false));
+  TRY(check_ptr(fn, "y", y, true));
+  if (!f) return fail(ATTNRES_EINVAL, "%s: sublayer callback is NULL", fn);
+  if (!block_sums) return fail(ATTNRES_EINVAL, "%s: block_sums is NULL", fn);
+  for (int k = 0; k < nb; ++k) TRY(check_ptr(fn, "block_sums[k]", block_sums[k], true));
+  if (!side_stream || side_stream == stream)
+    return fail(ATTNRES_EINVAL, "%s: side_stream must be a stream other than stream", fn);
+  const int es = esize_of(dtype);
+  const OverlapLayout lay = overlap_layout(L, S, R, D, es);
+  if (!workspace) return fail(ATTNRES_EINVAL, "%s: workspace is NULL", fn);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(ATTNRES_EINVAL, "%s: workspace is not 256-byte aligned", fn);
+  if (workspace_bytes < lay.total)
+    return fail(ATTNRES_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes,
+                lay.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStream_t side = static_cast<hipStream_t>(side_stream);
+  int dev_main = -1, dev_side = -1;
+  TRY(stream_device(fn, st, &dev_main));
+  TRY(stream_device(fn, side, &dev_side));
+  if (dev_main != dev_side)
+    return fail(ATTNRES_EINVAL, "%s: stream is on device %d, side_stream on device %d", fn,
+                dev_main, dev_side);
+  OverlapEvents* ev = nullptr;
+  TRY(overlap_events(fn, dev_main, &ev));
+
+  char* ws = static_cast<char*>(workspace);
+  void* P = ws + lay.p;
+  void* H = ws + lay.h;
+  void* gemm_ws = lay.g < lay.total ? ws + lay.g : nullptr;
+  const int64_t tensor_bytes = R * D * es;
+  auto hip_ok = [&](hipError_t e) { return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e); };
+
+  const float* Q = nullptr;
+  TRY(fold_queries(fn, W, Gamma, L, D, reinterpret_cast<float*>(ws + lay.q), st, &Q));
+  auto normed = [&](int l, const void* h) -> int {
+    return do_rmsnorm(fn, dtype, h, R, D, nm.Gamma_f ? nm.Gamma_f + (int64_t)(l - 1) * D : nullptr,
+                      nm.eps_f, H, st);
+  };
+  auto call = [&](int l, const void* h, const void** v) -> int {
+    const void* out = nullptr;
+    const int rc = f(f_ctx, l, h, &out, stream);
+    if (rc != 0)
+      return fail(ATTNRES_ECALLBACK, "%s: sublayer callback returned %d at l = %d", fn, rc, l);
+    if (!out || !aligned16(out))
+      return fail(ATTNRES_ECALLBACK, "%s: callback gave a NULL or misaligned v at l = %d", fn, l);
+    *v = out;
+    return ATTNRES_OK;
+  };
+  auto block_range = [&](int k, int* start, int* Sk) {
+    *start = k * S + 1;
+    const int end = (k + 1) * S < L ? (k + 1) * S : L;
+    *Sk = end - *start + 1;
+  };
+
+  std::vector<const void*> src;
+  src.reserve(nb + 1);
+  src.push_back(x);
+  // Phase 1 of block k over the first n = k completed sources into slot k & 1
+  // (for k == 0, over [b_0] on the main stream). Returns, through one_source,
+  // whether the outputs were elided (one source: each output is b_0 itself).
+  bool one_src[2] = {false, false};
+  auto phase1_into_slot = [&](int k, int n, hipStream_t on) -> int {
+    int start, Sk;
+    block_range(k, &start, &Sk);
+    const int b = k & 1;
+    char* O = ws + lay.o[b];
+    float* M = reinterpret_cast<float*>(ws + lay.m[b]);
+    float* LSE = reinterpret_cast<float*>(ws + lay.lse[b]);
+    const float* Qk = Q + (int64_t)(start - 1) * D;
+    if (Sk == 1) {
+      one_src[b] = false;
+      AggArgs a{src.data(), n, R, D, Qk, nullptr, eps, O, nullptr, LSE, nullptr, nullptr, nullptr};
+      return do_aggregate(fn, dtype, a, on);
+    }
+    one_src[b] = n == 1 && attnres::phase1_stats_supported(dtype, 1, Sk, D);
+    Phase1Args a1{src.data(), n, R, D, Qk, nullptr, Sk, eps, one_src[b] ? nullptr : O, M, LSE,
+                  nullptr, nullptr, nullptr, gemm_ws};
+    // off the critical path, Phase 1 leaves most of the chip to the main stream
+    if (on != st) a1.max_groups = ATTNRES_OVERLAP_SIDE_GROUPS;
+    return do_phase1(fn, dtype, a1, on);
+  };
+  auto o_slice = [&](int k, int j) -> const void* {
+    const int b = k & 1;
+    return one_src[b] ? src[0] : static_cast<const void*>(ws + lay.o[b] + (int64_t)j * tensor_bytes);
+  };
+  auto lse_slice = [&](int k, int j) -> const float* {
+    return reinterpret_cast<const float*>(ws + lay.lse[k & 1]) + (int64_t)j * R;
+  };
+
+  const void* close_p = nullptr;
+  const void* close_v = nullptr;
+  for (int k = 0; k < nb; ++k) {
+    int start, Sk;
+    block_range(k, &start, &Sk);
+    const void* xs = nullptr;  // the newest completed source, merged as its own term
+    if (k == 0) {
+      // block 0: its Phase 1 over [b_0] on the main stream, then (when a next
+      // block exists) the side stream starts block 1's Phase 1 over [b_0]
+      if (Sk == 1) {
+        AggArgs a{src.data(), 1, R, D, Q, nullptr, eps, H, nullptr, nullptr, nullptr, nullptr, nullptr};
+        TRY(do_aggregate(fn, dtype, a, st));
+      } else {
+        TRY(phase1_into_slot(0, 1, st));
+      }
+      if (nb > 1) {
+        TRY(hip_ok(hipEventRecord(ev->main_ready, st)));
+        TRY(hip_ok(hipStreamWaitEvent(side, ev->main_ready, 0)));
+        TRY(phase1_into_slot(1, 1, side));
+        TRY(hip_ok(hipEventRecord(ev->side_done, side)));
+      }
+    } else {
+      // block k: its Phase 1 over [b_0 .. b_{k-1}] ran on the side stream;
+      // close b_k = p + v_last and merge it into query 0's summary
+      TRY(hip_ok(hipStreamWaitEvent(st, ev->side_done, 0)));
+      src.push_back(block_sums[k - 1]);
+      xs = block_sums[k - 1];
+      AggArgs am{src.data() + k, 1, R, D, Q + (int64_t)(start - 1) * D, nullptr, eps, H, nullptr,
+                 nullptr, close_p, close_v, block_sums[k - 1], o_slice(k, 0), lse_slice(k, 0)};
+      TRY(do_aggregate(fn, dtype, am, st));
+      if (k + 1 < nb) {
+        // b_k is stored and slot (k+1) & 1 was last read by block k-1:
+        // block k+1's Phase 1 over [b_0 .. b_k] can start
+        TRY(hip_ok(hipEventRecord(ev->main_ready, st)));
+        TRY(hip_ok(hipStreamWaitEvent(side, ev->main_ready, 0)));
+        TRY(phase1_into_slot(k + 1, k + 1, side));
+        TRY(hip_ok(hipEventRecord(ev->side_done, side)));
+      }
+    }
+    const void* h0 = (k == 0 && Sk > 1) ? o_slice(0, 0) : H;
+    const void* v_first = nullptr;
+    if (nm.on) {
+      TRY(normed(start, h0));
+      TRY(call(start, H, &v_first));
+    } else {
+      TRY(call(start, h0, &v_first));
+    }
+    const void* p_cur = v_first;
+    const void* v_prev = v_first;
+    for (int j = 1; j < Sk; ++j) {
+      const int l = start + j;
+      Phase2Args a2{o_slice(k, j), lse_slice(k, j), Q + (int64_t)(l - 1) * D,
+                    nullptr, eps, j == 1 ? nullptr : p_cur, v_prev, j == 1 ? nullptr : P,
+                    nm.on ? nullptr : H,
+                    nm.on && nm.Gamma_f ? nm.Gamma_f + (int64_t)(l - 1) * D : nullptr, nm.eps_f,
+                    nm.on ? H : nullptr, R, D, xs};
+      TRY(do_phase2(fn, dtype, a2, st));
+      if (j > 1) p_cur = P;
+      const void* v = nullptr;
+      TRY(call(l, H, &v));
+      v_prev = v;
+    }
+    // b_{k+1} = p + v_end (or v alone for a one-sublayer block), formed by
+    // the next block's first launch or the final aggregate
+    close_p = Sk > 1 ? p_cur : nullptr;
+    close_v = v_prev;
+  }
+  src.push_back(block_sums[nb - 1]);
+  AggArgs af{src.data(), nb + 1, R, D, Q + (int64_t)L * D, nullptr, eps, y, nullptr, nullptr,
+             close_p, close_v, block_sums[nb - 1]};
+  TRY(do_aggregate(fn, dtype, af, st));
+  return ok();
+}
+
 // Full AttnRes with a two-phase schedule [K3 9.4: with schedule_block_size
 // the Full mixer runs the two-phase algorithm and matches the naive one]:
 // sublayers are taken in chunks of C; Phase 1 scores a chunk's queries over
@@ -690,18 +1028,13 @@ ATTNRES_API int attnres_full_stack_forward(const void* x, int L, int C, int64_t 
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  float* Q = reinterpret_cast<float*>(ws + lay.q);
   char* O = ws + lay.o;
   float* M = reinterpret_cast<float*>(ws + lay.m);
   float* LSE = reinterpret_cast<float*>(ws + lay.lse);
   void* H = ws + lay.h;
   const int64_t tensor_bytes = R * D * es;
-  {
-    hipError_t e = attnres::launch_fold(
-        W, Gamma, Q, (int64_t)(L + 1) * D,
-        timed_launch(K_FOLD, (double)(L + 1) * D * (Gamma ? 12 : 8), st));
-    if (e != hipSuccess) return hip_fail(fn, e);
-  }
+  const float* Q = nullptr;
+  TRY(fold_queries(fn, W, Gamma, L, D, reinterpret_cast<float*>(ws + lay.q), st, &Q));
   auto call = [&](int l, const void* h, const void** v) -> int {
     const void* out = nullptr;
     const int rc = f(f_ctx, l, h, &out, stream);
@@ -935,21 +1268,31 @@ ATTNRES_API int attnres_timing_enable(int capacity) {
   }
   t.kind.assign(capacity, 0);
   t.bytes.assign(capacity, 0.0);
+  t.name.assign(capacity, nullptr);
+  t.stream.assign(capacity, nullptr);
   t.capacity = capacity;
   return ok();
 }
 
 static int collect_timing() {
   Timing& t = g_timing;
+  if (t.used > 0) t.trace.clear();
   for (int s = 0; s < t.used; ++s) {
     hipError_t e = hipEventSynchronize(t.ev[2 * s + 1]);
     if (e != hipSuccess) return hip_fail("attnres_timing_read", e);
-    float ms = 0.f;
+    float ms = 0.f, t0 = 0.f, t1 = 0.f;
     e = hipEventElapsedTime(&ms, t.ev[2 * s], t.ev[2 * s + 1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t0, t.ev[0], t.ev[2 * s]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t1, t.ev[0], t.ev[2 * s + 1]);
     if (e != hipSuccess) return hip_fail("attnres_timing_read", e);
+    t.trace.push_back({t.kind[s], reinterpret_cast<uintptr_t>(t.stream[s]), t0, t1});
     t.launches[t.kind[s]] += 1;
     t.ms[t.kind[s]] += ms;
     t.total_bytes[t.kind[s]] += t.bytes[s];
+    std::string& names = t.names[t.kind[s]];
+    const std::string nm = t.name[s] ? t.name[s] : "";
+    if (("," + names + ",").find("," + nm + ",") == std::string::npos)
+      names += (names.empty() ? "" : ",") + nm;
   }
   t.used = 0;
   return ATTNRES_OK;
@@ -967,8 +1310,32 @@ ATTNRES_API int attnres_timing_reset(void) {
     t.launches[k] = 0;
     t.ms[k] = 0;
     t.total_bytes[k] = 0;
+    t.names[k].clear();
   }
   return ok();
+}
+
+ATTNRES_API int attnres_timing_trace(int max, int* kinds, uint64_t* streams, double* start_ms,
+                                     double* end_ms) {
+  TRY(collect_timing());
+  const Timing& t = g_timing;
+  const int n = (int)t.trace.size() < max ? (int)t.trace.size() : max;
+  for (int i = 0; i < n; ++i) {
+    if (kinds) kinds[i] = t.trace[i].kind;
+    if (streams) streams[i] = t.trace[i].stream;
+    if (start_ms) start_ms[i] = t.trace[i].start;
+    if (end_ms) end_ms[i] = t.trace[i].end;
+  }
+  return n;
+}
+
+ATTNRES_API const char* attnres_timing_kernels(int kind) {
+  if (kind < 0 || kind >= K_COUNT) {
+    fail(ATTNRES_EINVAL, "attnres_timing_kernels: kind %d", kind);
+    return "";
+  }
+  if (collect_timing() != ATTNRES_OK) return "";
+  return g_timing.names[kind].c_str();
 }
 
 ATTNRES_API int attnres_timing_read(int kind, int64_t* launches, double* total_ms,

@@ -1886,6 +1886,7 @@ struct Phase2Params {
   const float* gf;     // [D] gain of the output norm, or null (ones)
   float eps_f;
   void* hn_out;        // RMSNorm(h) * gf, or null (no output norm)
+  const void* xs;      // a completed source merged as one more single-source term, or null
   Geom g;
 };
 
@@ -1895,7 +1896,7 @@ __device__ __forceinline__ void st16_out(char* p, const uint4& v) {
   else st16(p, v);
 }
 
-template <class T, int VPL, bool HAS_PREV, bool NORM, bool NT>
+template <class T, int VPL, bool HAS_PREV, bool NORM, bool NT, bool EXTRA = false>
 __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
   extern __shared__ float lds[];
   constexpr int EPV = T::kEPV;
@@ -1929,7 +1930,7 @@ __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
     // the end reads row 0, a lane past the row's end reads vector 0; both are
     // discarded), so no branch hides a load from the compiler's wait counting
     // and one wait covers them all
-    uint4 vv[VPL], pp[VPL], ov[VPL];
+    uint4 vv[VPL], pp[VPL], ov[VPL], xv[EXTRA ? VPL : 1];
     #pragma unroll
     for (int c = 0; c < VPL; ++c) {
       const int vec = c * ln.stride + ln.t;
@@ -1937,11 +1938,15 @@ __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
       vv[c] = ld16_stream(static_cast<const char*>(p.v_prev) + off);
       if (HAS_PREV) pp[c] = ld16_stream(static_cast<const char*>(p.p_prev) + off);
       ov[c] = ld16_stream(static_cast<const char*>(p.o) + off);
+      if (EXTRA) xv[c] = ld16_stream(static_cast<const char*>(p.xs) + off);
     }
     const float l = p.lse[rv ? row : 0];
 
     uint4 pv[VPL];
-    float red[2] = {0.f, 0.f};
+    // q~.p and p.p, then (with the extra source) q~.x and x.x
+    float red[EXTRA ? 4 : 2];
+    #pragma unroll
+    for (int k = 0; k < (EXTRA ? 4 : 2); ++k) red[k] = 0.f;
     #pragma unroll
     for (int c = 0; c < VPL; ++c) {
       const int vec = c * ln.stride + ln.t;
@@ -1966,14 +1971,27 @@ __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
         red[0] += q[c][e] * f[e];
         red[1] += f[e] * f[e];
       }
+      if constexpr (EXTRA) {
+        T::unpack(xv[c], f);
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          f[e] = in_row ? f[e] : 0.f;
+          red[2] += q[c][e] * f[e];
+          red[3] += f[e] * f[e];
+        }
+      }
     }
-    row_reduce<2>(red, lds, ln.slot, ln.wr, g.W);
+    row_reduce<EXTRA ? 4 : 2>(red, lds, ln.slot, ln.wr, g.W);
     const float sp = red[0] * rsqrtf(red[1] * g.invD + p.eps);
-    const float M = fmaxf(l, sp);
-    float a = __expf(l - M), b = __expf(sp - M);
-    const float r = 1.0f / (a + b);
+    // the extra source's score (a completed source the Phase-1 group did not
+    // include): OS2 over three terms, the group, the source and the partial
+    const float sx = EXTRA ? red[2] * rsqrtf(red[3] * g.invD + p.eps) : -FLT_MAX;
+    const float M = fmaxf(fmaxf(l, sp), sx);
+    float a = __expf(l - M), b = __expf(sp - M), cx = EXTRA ? __expf(sx - M) : 0.f;
+    const float r = 1.0f / (a + b + cx);
     a *= r;
     b *= r;
+    cx *= r;
     uint4 hv[VPL];
     float hss[1] = {0.f};
     #pragma unroll
@@ -1984,6 +2002,11 @@ __global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
       T::unpack(pv[c], fp);
       #pragma unroll
       for (int e = 0; e < EPV; ++e) fo[e] = a * fo[e] + b * fp[e];
+      if constexpr (EXTRA) {
+        T::unpack(xv[c], fp);
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) fo[e] += cx * fp[e];
+      }
       hv[c] = T::pack(fo);  // h rounded to the I/O dtype
       if (p.h_out)
         st16_out<NT>(store_target(rv && vec < g.V, static_cast<char*>(p.h_out) + base + (int64_t)vec * 16),
@@ -2286,8 +2309,9 @@ static hipError_t launch_phase1_stream_t(Phase1SParams& p, const Phase1Args& a, 
   // Passes per launch: as many as fit side by side in about
   // ATTNRES_P1_STREAM_GROUPS workgroups, one walker per row group each.
   const int passes = (a.S + SQ - 1) / SQ;
-  const int64_t busy = p.g.groups < ATTNRES_P1_STREAM_GROUPS ? p.g.groups : ATTNRES_P1_STREAM_GROUPS;
-  int per = (int)(ATTNRES_P1_STREAM_GROUPS / busy);
+  const int64_t budget = a.max_groups > 0 ? a.max_groups : ATTNRES_P1_STREAM_GROUPS;
+  const int64_t busy = p.g.groups < budget ? p.g.groups : budget;
+  int per = (int)(budget / busy);
   per = per < 1 ? 1 : per > passes ? passes : per;
   for (int s0 = 0; s0 < a.S; s0 += per * SQ) {
     // later launches read the block sum the first one stored
@@ -2297,7 +2321,7 @@ static hipError_t launch_phase1_stream_t(Phase1SParams& p, const Phase1Args& a, 
     }
     p.S = a.S - s0 < per * SQ ? a.S - s0 : per * SQ;
     p.passes = (p.S + SQ - 1) / SQ;
-    int64_t walkers = ATTNRES_P1_STREAM_GROUPS / p.passes;
+    int64_t walkers = budget / p.passes;
     if (walkers > p.g.groups) walkers = p.g.groups;
     walkers = (walkers + 7) / 8 * 8;  // a multiple of the 8 XCDs
     p.walkers = (int)walkers;
@@ -2478,6 +2502,14 @@ hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L) {
   return dtype == 1 ? launch_phase1_dt<Bf16>(a, L) : launch_phase1_dt<F32>(a, L);
 }
 
+const char* phase1_kernel_name(int dtype, const Phase1Args& a, bool gemm) {
+  if (gemm) return a.out ? "phase1_gemm_scores_kernel+phase1_gemm_outputs_kernel" : "phase1_gemm_scores_kernel";
+  if (phase1_single_eligible(dtype, a)) return "phase1_single_kernel";
+  if (phase1_mfma_eligible(dtype, a.n, a.S, a.D)) return "phase1_mfma_kernel";
+  if (a.out && (ATTNRES_P1_STREAM || a.n > 16)) return "phase1_stream_kernel";
+  return "phase1_kernel";
+}
+
 bool phase1_stats_supported(int dtype, int n, int S, int64_t D) {
   if (phase1_mfma_eligible(dtype, n, S, D)) return true;
   if (n < 1 || n > 8) return false;
@@ -2529,6 +2561,18 @@ template <class T, int VPL, bool HP>
 
 static hipError_t launch_ph2_t(Phase2Params& p, const Launch& L) {
   const size_t lds = p.g.W > 1 ? (size_t)p.g.RPW * p.g.W * 2 * sizeof(float) : 0;
+  if (p.xs) {
+    // with an extra source: four row sums; written with plain stores (this
+    // variant serves the few-row decode schedule)
+    const size_t lds4 = 2 * lds;
+    const unsigned grid4 = (unsigned)(p.g.groups < ATTNRES_PHASE2_MAX_GROUPS ? p.g.groups
+                                                                              : ATTNRES_PHASE2_MAX_GROUPS);
+    if (p.hn_out)
+      return launch(L, phase2_kernel<T, VPL, HP, true, false, true>, dim3(grid4),
+                    dim3(64 * p.g.W * p.g.RPW), lds4, p);
+    return launch(L, phase2_kernel<T, VPL, HP, false, false, true>, dim3(grid4),
+                  dim3(64 * p.g.W * p.g.RPW), lds4, p);
+  }
   const unsigned grid = (unsigned)(p.g.groups < ATTNRES_PHASE2_MAX_GROUPS ? p.g.groups
                                                                            : ATTNRES_PHASE2_MAX_GROUPS);
   const dim3 block(64 * p.g.W * p.g.RPW);
@@ -2542,6 +2586,15 @@ static hipError_t launch_ph2_t(Phase2Params& p, const Launch& L) {
 
 template <class T, bool HP>
 static hipError_t launch_ph2_vpl(Phase2Params& p, int vpl, const Launch& L) {
+  if (p.xs) {
+    // the extra-source variant exists for 2, 4 and 8 vectors per lane
+    switch (vpl) {
+      case 2: return launch_ph2_t<T, 2, HP>(p, L);
+      case 4: return launch_ph2_t<T, 4, HP>(p, L);
+      case 8: return launch_ph2_t<T, 8, HP>(p, L);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (vpl) {
     case 1: return launch_ph2_t<T, 1, HP>(p, L);
     case 2: return launch_ph2_t<T, 2, HP>(p, L);
@@ -2559,12 +2612,14 @@ static hipError_t launch_phase2_dt(const Phase2Args& a, const Launch& L) {
   Phase2Params p;
   p.o = a.o; p.lse = a.lse; p.w = a.w; p.gm = a.g; p.eps = a.eps;
   p.p_prev = a.p_prev; p.v_prev = a.v_prev; p.p_out = a.p_out; p.h_out = a.h_out;
-  p.gf = a.gf; p.eps_f = a.eps_f; p.hn_out = a.hn_out;
+  p.gf = a.gf; p.eps_f = a.eps_f; p.hn_out = a.hn_out; p.xs = a.xs;
   // ATTNRES_PHASE2_VPL vectors per lane, more when a row would need over 4
-  // waves (rows are at most 2048 vectors, so at most 8 per lane)
+  // waves (rows are at most 2048 vectors, so at most 8 per lane); with an
+  // extra source the next of 2, 4 or 8
   const int V = (int)(a.D * T::kBytes / 16);
   int vpl = ATTNRES_PHASE2_VPL;
   if (64 * 4 * vpl < V) vpl = (V + 255) / 256;
+  if (a.xs) vpl = vpl <= 2 ? 2 : vpl <= 4 ? 4 : 8;
   p.g = make_geom(a.R, a.D, T::kBytes, vpl, 4);
   if (p.g.W > 4 || vpl > 8) return hipErrorInvalidValue;
   return a.p_prev ? launch_ph2_vpl<T, true>(p, vpl, L) : launch_ph2_vpl<T, false>(p, vpl, L);

@@ -35,6 +35,9 @@ struct Phase1Args {
   // workspace of phase1_gemm_workspace(S, R, D) bytes, or null: with it,
   // shapes phase1_gemm_eligible() accepts take the scores/outputs passes
   void* gemm_ws = nullptr;
+  // the streamed kernel's workgroup budget per launch (0: its default); a
+  // smaller one runs query passes one after another instead of side by side
+  int max_groups = 0;
 };
 
 struct AggArgs {
@@ -70,6 +73,9 @@ struct Phase2Args {
   float eps_f;
   void* hn_out;     // RMSNorm(h) * gf, or null
   int64_t R, D;
+  // a completed source [R][D] merged as one more single-source term (the
+  // decode schedule's newest block sum, which its Phase-1 group left out), or null
+  const void* xs = nullptr;
 };
 
 // Aggregate backward: sources, query and gain as in AggArgs, upstream gradient
@@ -121,6 +127,8 @@ bool phase1_gemm_eligible(int dtype, int n, int S, int64_t D, int64_t R);
 size_t phase1_gemm_workspace(int S, int64_t R, int64_t D);
 hipError_t launch_phase1_gemm(const Phase1Args& a, void* ws, const Launch& L);
 bool phase1_supported(int dtype, int n, int S, int64_t D);
+// name of the kernel(s) a Phase-1 launch runs (gemm: the scores/outputs path)
+const char* phase1_kernel_name(int dtype, const Phase1Args& a, bool gemm);
 // Phase 1 with out == null (statistics only) is available for these shapes
 bool phase1_stats_supported(int dtype, int n, int S, int64_t D);
 hipError_t launch_aggregate(int dtype, const AggArgs& a, const Launch& L);

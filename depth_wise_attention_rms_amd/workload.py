@@ -25,7 +25,10 @@ def torch_dtype(dt: str):
 
 
 class DeviceStack:
-    def __init__(self, wl: inputs.Workload, device="cuda", W_host: Optional[np.ndarray] = None):
+    def __init__(self, wl: inputs.Workload, device="cuda", W_host: Optional[np.ndarray] = None,
+                 gains: bool = False):
+        """``gains``: give every query its own RMSNorm gain [L+1, D] ~ U(0.5, 1.5)
+        (self.Gamma_host) instead of ones."""
         assert wl.kind == "stack"
         self.wl = wl
         self.device = device
@@ -33,6 +36,9 @@ class DeviceStack:
         self.dt = torch_dtype(wl.dtype)
         self.W_host = W_host if W_host is not None else inputs.queries(wl.seed, L + 1, D)
         self.W = torch.from_numpy(self.W_host).to(device)
+        self.Gamma_host = (np.stack([inputs.gains(wl.seed + 7, D, layer=l) for l in range(L + 1)])
+                           .astype(np.float32) if gains else None)
+        self.Gamma = None if self.Gamma_host is None else torch.from_numpy(self.Gamma_host).to(device)
         self.x = torch.empty((R, D), dtype=self.dt, device=device)
         inputs.fill_normal(self.x, wl.seed, inputs.ROLE_X, 0, wl.x_sigma)
         self.scales = wl.scales()
@@ -66,6 +72,7 @@ class DeviceStack:
         self.y = torch.empty((R, D), dtype=self.dt, device=device)
         need = binding.attnres_stack_workspace_bytes(L, S, R, D, self.dt)
         self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        self.overlap_workspace = None
 
     def recorder(self, rows: np.ndarray):
         """A sublayer callback that records token rows ``rows`` of every h_l
@@ -85,12 +92,27 @@ class DeviceStack:
         return binding.NativeSublayer(inputs.fn_ptr("attnres_inputs_record_sublayer"),
                                       ctypes.cast(ctypes.pointer(ctx), ctypes.c_void_p))
 
-    def forward(self, sublayer=None, stream=None, norm=None):
+    def forward(self, sublayer=None, stream=None, norm=None, side_stream=None):
         """One stack forward; ``norm=(Gamma_f, eps_f)`` hands the sublayers
-        RMSNorm(h_l) * Gamma_f[l-1] instead of h_l."""
+        RMSNorm(h_l) * Gamma_f[l-1] instead of h_l. With ``side_stream`` the
+        forward runs the decode schedule (attnres_block_stack_forward_overlap),
+        each block's Phase 1 on that stream."""
+        wl = self.wl
+        if side_stream is not None:
+            if self.block_sums is None:
+                self.block_sums = [torch.empty((wl.R, wl.D), dtype=self.dt, device=self.device)
+                                   for _ in range(self.nb)]
+            if self.overlap_workspace is None:
+                need = binding.attnres_stack_overlap_workspace_bytes(wl.L, wl.S, wl.R, wl.D, self.dt)
+                self.overlap_workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+            return binding.attnres_block_stack_forward_overlap(
+                self.x, self.W, wl.S, sublayer or self.sublayer, side_stream, Gamma=self.Gamma, eps=EPS,
+                block_sums=self.block_sums, y=self.y, workspace=self.overlap_workspace, stream=stream,
+                norm=norm)
         return binding.attnres_block_stack_forward(
-            self.x, self.W, self.wl.S, sublayer or self.sublayer, eps=EPS,
-            block_sums=self.block_sums, y=self.y, workspace=self.workspace, stream=stream, norm=norm)
+            self.x, self.W, wl.S, sublayer or self.sublayer, Gamma=self.Gamma, eps=EPS,
+            block_sums=self.block_sums, y=self.y, workspace=self.workspace, stream=stream, norm=norm,
+            keep_sources=not wl.ring)
 
     def host_rows(self, rows: np.ndarray):
         """The generated inputs at token rows ``rows``, copied to the host:

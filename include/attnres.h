@@ -214,6 +214,48 @@ int attnres_block_stack_forward_norm(const void* x, int L, int S, int64_t R, int
                                      size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * attnres_block_stack_forward_overlap -- the stack forward with the decode
+ * schedule [WC "Kimi Linear and K3 integration", decode: the batched
+ * inter-block pass runs on a side stream, overlapped with the main stream's
+ * work; K3 9.4 (OS2): merging source groups is exact]. Block k+1's Phase 1
+ * needs every completed source, but the merge of groups lets it start early:
+ * while block k's sublayers run on `stream`, `side_stream` scores block
+ * k+1's queries over [b_0 .. b_k]; the block sum b_{k+1} that block k closes
+ * with then joins as one more single-source term (one launch that performs
+ * the close and gives block k+1's first sublayer its input, and a
+ * three-term merge in each later Phase-2 step). Results equal the naive
+ * forward's (the same reading as attnres_block_stack_forward; only the
+ * grouping of the softmax terms differs). Meant for decode (few rows), where
+ * a Phase-1 launch on the main stream is latency on the critical path; with
+ * many rows the three-term merges read one more [R,D] tensor per sublayer.
+ *   Arguments as attnres_block_stack_forward, plus:
+ *   out_norm       : nonzero: sublayer l receives RMSNorm(h_l) * Gamma_f[l-1]
+ *                    with eps_f, as attnres_block_stack_forward_norm; zero:
+ *                    h_l (Gamma_f and eps_f are then ignored)
+ *   block_sums     : (host) nb device pointers, required (also for S == 1)
+ *   workspace      : attnres_stack_overlap_workspace_bytes(L, S, R, D, dtype)
+ *                    bytes, 256-byte aligned (two Phase-1 slots)
+ *   stream         : the main stream; the callback is handed this stream
+ *   side_stream    : a second stream of the same device and the same
+ *                    (default) priority, not `stream` (ATTNRES_EINVAL
+ *                    otherwise). The library orders the two streams with
+ *                    two HIP events of its own (per thread and device,
+ *                    created at the first call, timing disabled; no device
+ *                    memory). Every side-stream launch is joined back into
+ *                    `stream` before the call returns, so work the caller
+ *                    enqueues on `stream` afterwards sees all results, and a
+ *                    capture of `stream` into a HIP graph takes the side
+ *                    stream's work along.
+ * ------------------------------------------------------------------------- */
+size_t attnres_stack_overlap_workspace_bytes(int L, int S, int64_t R, int64_t D, int dtype);
+int attnres_block_stack_forward_overlap(const void* x, int L, int S, int64_t R, int64_t D,
+                                        int dtype, const float* W, const float* Gamma, float eps,
+                                        int out_norm, const float* Gamma_f, float eps_f,
+                                        attnres_sublayer_fn f, void* f_ctx,
+                                        void* const* block_sums, void* y, void* workspace,
+                                        size_t workspace_bytes, void* stream, void* side_stream);
+
+/* ---------------------------------------------------------------------------
  * attnres_block_layout -- the integer plan of forward_naive [K3 9.3 listing;
  * WC "Block AttnRes"]. block_start[k] (host, nb+1 entries or NULL) is the
  * first sublayer (1-based) of block k, with block_start[nb] = L + 1.
@@ -361,6 +403,17 @@ int attnres_timing_enable(int capacity);
 int attnres_timing_pause(int paused);
 int attnres_timing_reset(void);
 int attnres_timing_read(int kind, int64_t* launches, double* total_ms, double* total_bytes);
+/* The kernels that the timed launches of `kind` ran since the last reset:
+ * distinct names, comma-separated ("" if none, or for an invalid kind); a
+ * launch of several kernels is named "first+second". Valid until the next
+ * timing call on this thread. */
+const char* attnres_timing_kernels(int kind);
+/* The launches timed since the previous collection (attnres_timing_read,
+ * _kernels or _trace collect), in the order they were enqueued: for up to
+ * `max` of them their kind, their stream and the start and end of the kernel
+ * in milliseconds after the first one's start (any output may be NULL).
+ * Returns the number written, or a negative status. */
+int attnres_timing_trace(int max, int* kinds, uint64_t* streams, double* start_ms, double* end_ms);
 
 #ifdef __cplusplus
 }

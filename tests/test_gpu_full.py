@@ -71,6 +71,7 @@ FULL_CASES = [
     ("full_L24_C8", 24, 8, 1, 40, 256, "bf16"),
     ("full_L9_C1", 9, 1, 1, 50, 256, "bf16"),
     ("full_L5_C16", 5, 16, 1, 33, 128, "bf16"),
+    ("full_L12_C4_gains", 12, 4, 2, 100, 1024, "bf16"),
 ]
 
 
@@ -78,15 +79,15 @@ FULL_CASES = [
 def test_full_two_phase_matches_naive(name, L, C, B, T, D, dtype):
     announce(name)
     wl = inputs.Workload(name, "stack", B=B, T=T, D=D, dtype=dtype, L=L, S=1, seed=L * 10 + C)
-    ds = DeviceStack(wl)
+    ds = DeviceStack(wl, gains=name.endswith("_gains"))
     rows = np.arange(wl.R)
     rec = ds.recorder(rows)
-    y = b.attnres_full_stack_forward(ds.x, ds.W, C, rec, eps=EPS)
+    y = b.attnres_full_stack_forward(ds.x, ds.W, C, rec, Gamma=ds.Gamma, eps=EPS)
     torch.cuda.synchronize()
     xr, vr = ds.host_rows(rows)
     for c0 in range(0, wl.R, 512):
         sl = slice(c0, c0 + 512)
-        ref = oracle.block_stack(xr[sl], [a[sl] for a in vr], ds.W_host, 1, eps=EPS)
+        ref = oracle.block_stack(xr[sl], [a[sl] for a in vr], ds.W_host, 1, Gamma=ds.Gamma_host, eps=EPS)
         recs = to_host(ds.rec[:, sl])
         for l in range(L):
             assert_close_scaled(recs[l], ref["h"][l], ref["h_scale"][l], dtype, f"{name} h_{l + 1}")

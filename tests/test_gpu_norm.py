@@ -19,6 +19,7 @@ import oracle
 from depth_wise_attention_rms_amd import binding as b
 from depth_wise_attention_rms_amd import inputs
 from depth_wise_attention_rms_amd.workload import EPS, DeviceStack
+from tests.stack_check import norm_reference
 from tests.parity import assert_close_scaled, sample_rows, to_device, to_host
 
 pytestmark = pytest.mark.gpu
@@ -36,15 +37,6 @@ def _gpu():
 
 def announce(msg):
     print(f"[gpu-case] {msg}", flush=True)
-
-
-def norm_reference(h, scale_h, dtype, gamma_f, eps_f):
-    """(hn_ref, scale_hn) for an aggregate h computed by the oracle."""
-    h_r = oracle.round_to(h, dtype)
-    nr = oracle.rmsnorm(h_r, gamma_f, eps=eps_f)
-    g = np.ones(h.shape[-1]) if gamma_f is None else np.abs(gamma_f.astype(np.float64))
-    scale = g[None, :] * (scale_h + np.abs(h)) / nr["rms"][:, None]
-    return nr["out"], scale
 
 
 NORM_CASES = [

@@ -20,6 +20,7 @@ from depth_wise_attention_rms_amd import inputs
 from depth_wise_attention_rms_amd.workload import EPS, DeviceStack
 from tests.parity import (assert_close_scaled, assert_stats, sample_rows, to_device, to_host,
                           widen)
+from tests.stack_check import check_stack as _check_stack
 
 pytestmark = pytest.mark.gpu
 
@@ -216,33 +217,6 @@ def test_phase2_sweep(R, D, dtype, has_prev, inplace):
 # stack forward
 # ----------------------------------------------------------------------------
 
-def _check_stack(ds: DeviceStack, rows: np.ndarray, chunk=64, nthreads=None):
-    """Run the stack recording ``rows`` of every h_l, then compare h_l, y and
-    the block sums at those rows with the oracle's naive forward."""
-    wl = ds.wl
-    ds.forward(ds.recorder(rows))
-    torch.cuda.synchronize()
-    ids = torch.from_numpy(rows).cuda()
-    rec = to_host(ds.rec)
-    y = to_host(ds.y[ids])
-    bsums = None if ds.block_sums is None else [to_host(t[ids]) for t in ds.block_sums]
-    xr, vr = ds.host_rows(rows)
-    worst = 0.0
-    for c0 in range(0, len(rows), chunk):
-        sl = slice(c0, c0 + chunk)
-        ref = oracle.block_stack(xr[sl], [a[sl] for a in vr], ds.W_host, wl.S, eps=EPS,
-                                 nthreads=nthreads)
-        for l in range(wl.L):
-            worst = max(worst, assert_close_scaled(rec[l, sl], ref["h"][l], ref["h_scale"][l],
-                                                   wl.dtype, f"{wl.name} h_{l + 1}"))
-        worst = max(worst, assert_close_scaled(y[sl], ref["y"], ref["y_scale"], wl.dtype, f"{wl.name} y"))
-        assert np.array_equal(rec[0, sl], xr[sl]), "h_1 must equal the embedding bit for bit"
-        if bsums is not None:
-            for k in range(ref["nb"]):
-                assert np.array_equal(bsums[k][sl], ref["block_sums"][k]), f"block sum b_{k + 1} differs"
-    return worst
-
-
 def test_stack_bruteforce_grid():
     """Every L <= 7 and S <= L+1 on 3 rows, D in {8, 16, 64} (and 1024 for bf16,
     which takes the matrix-core Phase 1), both dtypes."""
@@ -337,11 +311,34 @@ def test_stack_gemm_phase1(B, T, D, S, L):
 
 def test_stack_long_context_config():
     """Long-context Block: L = 186, S = 24, T = 131072, D = 7168, bf16, sublayer
-    outputs generated per sublayer into a ring; 256 sampled rows."""
+    outputs generated per sublayer into a ring; 512 sampled rows."""
     wl = inputs.WORKLOADS["long_L186_S24"]
     announce(wl.name)
     ds = DeviceStack(wl)
-    _check_stack(ds, sample_rows(wl.R, 256), chunk=32)
+    _check_stack(ds, sample_rows(wl.R, 512), chunk=64)
+    del ds
+    torch.cuda.empty_cache()
+
+
+GAIN_STACKS = [
+    # (B, T, D, S, L): every query with its own RMSNorm gain, folded on the
+    # GPU once per forward; the matrix-core Phase 1, the streamed Phase 1 at
+    # D = 7168 with S > 8, and the matrix-core scores pass
+    (2, 300, 2048, 6, 20),
+    (1, 40, 7168, 12, 25),
+    (1, 4096, 7168, 12, 15),
+]
+
+
+@pytest.mark.parametrize("B,T,D,S,L", GAIN_STACKS)
+def test_stack_with_gains(B, T, D, S, L):
+    """Block stacks with non-unit gains: sampled rows of every h_l, y and the
+    block sums against the oracle's naive forward with the same gains."""
+    wl = inputs.Workload(f"gain_R{B * T}_D{D}_S{S}_L{L}", "stack", B=B, T=T, D=D, dtype="bf16", L=L, S=S,
+                         seed=L + 2 * S)
+    announce(wl.name)
+    ds = DeviceStack(wl, gains=True)
+    _check_stack(ds, sample_rows(wl.R, 192), chunk=64)
     del ds
     torch.cuda.empty_cache()
 
