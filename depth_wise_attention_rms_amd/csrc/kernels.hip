@@ -478,8 +478,8 @@ __device__ __forceinline__ void st16_stream(gchar_t* p, const uint4& v) {
   const u32x4_t t = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(t, reinterpret_cast<gu32x4_t*>(p));
 }
-// Plain (cached) 16-byte store. Phase 1 writes its S outputs with these: with
-// the non-temporal hint its eight output streams per row ran about 10% slower.
+// Plain (cached) 16-byte store: Phase 1's first outputs (see
+// ATTNRES_P1_OUT_NT_FROM).
 __device__ __forceinline__ void st16_global(gchar_t* p, const uint4& v) {
   const u32x4_t t = {v.x, v.y, v.z, v.w};
   *reinterpret_cast<gu32x4_t*>(p) = t;
@@ -498,9 +498,17 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // tell ring slots apart, adds no waits before LDS reads: the kernel waits for
 // these copies itself (p1_wait), before the barrier that publishes them.
 // M0 is written here; nothing else in these kernels uses it.
+#ifndef ATTNRES_P1_SRC_NT
+#define ATTNRES_P1_SRC_NT 1  // source copies carry the non-temporal hint
+#endif
 __device__ __forceinline__ void dma16(const gchar_t* base, uint32_t lane_off, uint32_t lds) {
+#if ATTNRES_P1_SRC_NT
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(lane_off), "s"(base) : "memory");
+#else
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(lane_off), "s"(base) : "memory");
+#endif
 }
 
 // Wait until at most k (clamped to the counter's 63) vector-memory operations
@@ -546,6 +554,18 @@ __device__ __forceinline__ int p1_stage(const Phase1MParams& p, int64_t row, con
   }
   return NC;
 }
+
+#ifndef ATTNRES_P1_B_NT
+#define ATTNRES_P1_B_NT 1  // the fused close stores the block sum non-temporally
+#endif
+// Outputs of queries from this index on are stored non-temporally. The first
+// two are read right after the launch (output 0 by the block's first
+// sublayer, output 1 by its first Phase-2 merge) and stay cacheable; storing
+// the later ones past the last-level cache measured 1-2% faster for Phase 1
+// and for that merge (all eight non-temporal: 6% slower).
+#ifndef ATTNRES_P1_OUT_NT_FROM
+#define ATTNRES_P1_OUT_NT_FROM 2
+#endif
 
 template <int KS, int NC>
 __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
@@ -628,7 +648,11 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
         u = Bf16::pack(fa);
         *reinterpret_cast<uint4*>(bv) = u;
       }
+#if ATTNRES_P1_B_NT
       st16_stream(uniform_ptr(static_cast<char*>(p.cl.b) + row * rowbytes) + (uint32_t)(tid * 16), u);
+#else
+      st16_global(uniform_ptr(static_cast<char*>(p.cl.b) + row * rowbytes) + (uint32_t)(tid * 16), u);
+#endif
       issued += 1;
     }
     if constexpr (!Sh::PRIVATE) {
@@ -794,7 +818,12 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
           // a 64-bit address per lane: the two queries of a pair are R rows
           // apart, which a 32-bit lane offset cannot hold beyond 4 GB
           char* dst = static_cast<char*>(p.out) + ((int64_t)sq * p.R + row) * rowbytes + vec * 16;
-          if (2 * q < S && sq < S) st16_global((gchar_t*)reinterpret_cast<uintptr_t>(dst), Bf16::pack(o[q]));
+          if (2 * q < S && sq < S) {
+            if (sq >= ATTNRES_P1_OUT_NT_FROM)
+              st16_stream((gchar_t*)reinterpret_cast<uintptr_t>(dst), Bf16::pack(o[q]));
+            else
+              st16_global((gchar_t*)reinterpret_cast<uintptr_t>(dst), Bf16::pack(o[q]));
+          }
         }
       }
       issued += 2 * ((S + 1) >> 1);
@@ -1896,8 +1925,15 @@ __device__ __forceinline__ void st16_out(char* p, const uint4& v) {
   else st16(p, v);
 }
 
+#ifndef ATTNRES_PHASE2_MAX_WAVES
+#define ATTNRES_PHASE2_MAX_WAVES 8  // waves per row in Phase 2 (more vectors per lane beyond)
+#endif
+#ifndef ATTNRES_PHASE2_LB
+#define ATTNRES_PHASE2_LB 512  // launch bound of the Phase-2 kernel (64 * max waves per workgroup)
+#endif
+
 template <class T, int VPL, bool HAS_PREV, bool NORM, bool NT, bool EXTRA = false>
-__global__ __launch_bounds__(256) void phase2_kernel(Phase2Params p) {
+__global__ __launch_bounds__(ATTNRES_PHASE2_LB) void phase2_kernel(Phase2Params p) {
   extern __shared__ float lds[];
   constexpr int EPV = T::kEPV;
   const Geom& g = p.g;
@@ -2126,7 +2162,7 @@ __global__ void close_kernel(const void* __restrict__ pp, const void* __restrict
 #endif
 
 #ifndef ATTNRES_PHASE2_VPL
-#define ATTNRES_PHASE2_VPL 2  // preferred vectors per lane in Phase 2 (rows take up to 4 waves)
+#define ATTNRES_PHASE2_VPL 2  // preferred vectors per lane in Phase 2 (rows take up to 8 waves)
 #endif
 
 static Geom make_geom(int64_t R, int64_t D, int esize, int vpl, int waves_per_group_max) {
@@ -2617,11 +2653,12 @@ static hipError_t launch_phase2_dt(const Phase2Args& a, const Launch& L) {
   // waves (rows are at most 2048 vectors, so at most 8 per lane); with an
   // extra source the next of 2, 4 or 8
   const int V = (int)(a.D * T::kBytes / 16);
+  constexpr int MW = ATTNRES_PHASE2_MAX_WAVES;
   int vpl = ATTNRES_PHASE2_VPL;
-  if (64 * 4 * vpl < V) vpl = (V + 255) / 256;
+  if (64 * MW * vpl < V) vpl = (V + 64 * MW - 1) / (64 * MW);
   if (a.xs) vpl = vpl <= 2 ? 2 : vpl <= 4 ? 4 : 8;
   p.g = make_geom(a.R, a.D, T::kBytes, vpl, 4);
-  if (p.g.W > 4 || vpl > 8) return hipErrorInvalidValue;
+  if (p.g.W > MW || vpl > 8 || 64 * p.g.W * p.g.RPW > ATTNRES_PHASE2_LB) return hipErrorInvalidValue;
   return a.p_prev ? launch_ph2_vpl<T, true>(p, vpl, L) : launch_ph2_vpl<T, false>(p, vpl, L);
 }
 
