@@ -13,6 +13,9 @@
  *        representations as a depth KV cache".
  *   [RH] Reading notes on "Attention Residuals" (ranhao.site), 4.2
  *        Inference: Phase 1 and Phase 2.
+ *   [ZZ] "Attention Residuals" notes (zhangzhe.space): the block_attn_res
+ *        listing, where every sublayer applies its own RMSNorm to the
+ *        aggregate it receives (attn(attn_norm(h)), mlp(mlp_norm(h))).
  *
  * Conventions shared by every entry point
  *   - Tensor pointers are DEVICE pointers unless marked (host). A token tensor

@@ -23,6 +23,7 @@ import torch
 import oracle
 from depth_wise_attention_rms_amd import binding as b
 from depth_wise_attention_rms_amd import inputs
+from tests.bwd_scale import bwd_scales
 from tests.parity import to_device, to_host, widen
 
 pytestmark = pytest.mark.gpu
@@ -42,25 +43,6 @@ def _gpu():
 
 def announce(msg):
     print(f"[gpu-case] {msg}", flush=True)
-
-
-def bwd_scales(V, q, dh, eps):
-    """Condition scales of dV [n,R,D], dq~ [D] for fp64 V [n,R,D], q [D], dh [R,D]."""
-    D = V.shape[-1]
-    r = np.sqrt((V * V).mean(-1) + eps)                     # [n,R]
-    s = (V @ q) / r
-    a = np.exp(s - s.max(0)); a /= a.sum(0)
-    g = (V * dh[None]).sum(-1)
-    ds = a * (g - (a * g).sum(0))
-    gmag = (np.abs(V) * np.abs(dh)[None]).sum(-1)
-    smag = (np.abs(V) @ np.abs(q)) / r
-    DS = (np.abs(ds) + a * (gmag + (a * gmag).sum(0))
-          + 2 * a * (np.abs(g) + 2 * (a * np.abs(g)).sum(0)) * smag.max(0))
-    sc_dV = (a[..., None] * np.abs(dh)[None]
-             + DS[..., None] * (np.abs(q)[None, None] / r[..., None]
-                                + np.abs(s)[..., None] * np.abs(V) / (D * r[..., None] ** 2)))
-    sc_dq = (DS[..., None] * np.abs(V) / r[..., None]).sum((0, 1))
-    return sc_dV, sc_dq
 
 
 def scaled_err(got, ref, scale):

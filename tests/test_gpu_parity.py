@@ -309,6 +309,42 @@ def test_stack_gemm_phase1(B, T, D, S, L):
     torch.cuda.empty_cache()
 
 
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("L", [12, 24, 30, 54])
+def test_scores_pass_statistics(L):
+    """The matrix-core scores pass's fp32 statistics at the 1e-5 bar: a stack of
+    4100 rows of 7168 with 12 queries whose last block has L // 12 + 1 sources
+    (1: statistics only, one column per row; 2, 3 and 5: two, four and eight
+    columns per row; the short last blocks hold 6 queries). After the forward
+    the workspace holds that block's m and lse [Sk, R] at the offsets of the
+    header's layout (folded queries, outputs, m, lse), compared on every row
+    with the oracle's Phase 1 over the block sums the GPU stored."""
+    S, D = 12, 7168
+    wl = inputs.Workload(f"scores_stats_L{L}", "stack", B=1, T=4100, D=D, dtype="bf16", L=L, S=S, seed=L + 5)
+    announce(wl.name)
+    ds = DeviceStack(wl)
+    ds.forward()
+    torch.cuda.synchronize()
+    R, nb = wl.R, ds.nb
+    start = (nb - 1) * S + 1
+    Sk = L - start + 1
+    Skw = min(S, L)
+    off_m = _a256((L + 1) * D * 4) + _a256(Skw * R * D * 2 if Skw > 1 else 0)
+    off_lse = off_m + _a256(Skw * R * 4)
+    ws = ds.workspace
+    m = ws[off_m:off_m + Sk * R * 4].view(torch.float32).view(Sk, R)
+    lse = ws[off_lse:off_lse + Sk * R * 4].view(torch.float32).view(Sk, R)
+    blocks = [to_host(ds.x)] + [to_host(t) for t in ds.block_sums[:nb - 1]]
+    ref = oracle.phase1(blocks, ds.W_host[start - 1:L], eps=EPS)
+    assert_stats(to_host(m), ref["m"], f"{wl.name} m")
+    assert_stats(to_host(lse), ref["lse"], f"{wl.name} lse")
+    del ds
+    torch.cuda.empty_cache()
+
+
 def test_stack_long_context_config():
     """Long-context Block: L = 186, S = 24, T = 131072, D = 7168, bf16, sublayer
     outputs generated per sublayer into a ring; 512 sampled rows."""
