@@ -33,6 +33,7 @@ EXPORTS = (
     "attnres_block_stack_forward_overlap", "attnres_merge_sources", "attnres_full_workspace_bytes",
     "attnres_full_stack_forward", "attnres_aggregate_backward_workspace_bytes",
     "attnres_aggregate_backward", "attnres_aggregate_backward_noalloc",
+    "attnres_table_sublayer_bwd", "attnres_stack_backward_workspace_bytes", "attnres_block_stack_backward",
     "attnres_noalloc_scratch_bytes", "attnres_block_layout",
     "attnres_atomic_block_size", "attnres_status_string", "attnres_last_error",
     "attnres_timing_enable", "attnres_timing_pause", "attnres_timing_reset", "attnres_timing_read",
@@ -86,6 +87,11 @@ def lib():
         L.attnres_aggregate_backward_workspace_bytes.restype = SZ
         L.attnres_aggregate_backward.argtypes = [P, I, I64, I64, I, P, P, F, P, P, I, P, P, P, SZ, P]
         L.attnres_aggregate_backward_noalloc.argtypes = [P, I, I64, I64, I, P, P, F, P, P, I, P, P, P]
+        L.attnres_table_sublayer_bwd.argtypes = [P, I, P, ctypes.POINTER(P), P]
+        L.attnres_stack_backward_workspace_bytes.argtypes = [I, I, I64, I64, I]
+        L.attnres_stack_backward_workspace_bytes.restype = SZ
+        L.attnres_block_stack_backward.argtypes = [P, P, I, I, I64, I64, I, P, P, F, P, P, P, P, P, P, P,
+                                                   P, P, SZ, P]
         L.attnres_noalloc_scratch_bytes.argtypes = []
         L.attnres_noalloc_scratch_bytes.restype = SZ
         L.attnres_block_layout.argtypes = [I, I, P, P]
@@ -105,7 +111,8 @@ def lib():
         for f in ("attnres_aggregate", "attnres_phase1_batched", "attnres_phase2_merge",
                   "attnres_phase2_merge_norm", "attnres_rmsnorm", "attnres_block_stack_forward_norm",
                   "attnres_merge_sources", "attnres_full_stack_forward", "attnres_aggregate_backward",
-                  "attnres_aggregate_backward_noalloc", "attnres_table_sublayer", "attnres_block_stack_forward", "attnres_block_layout",
+                  "attnres_aggregate_backward_noalloc", "attnres_table_sublayer",
+                  "attnres_table_sublayer_bwd", "attnres_block_stack_backward", "attnres_block_stack_forward", "attnres_block_layout",
                   "attnres_block_stack_forward_overlap",
                   "attnres_atomic_block_size", "attnres_timing_enable", "attnres_timing_pause",
                   "attnres_timing_reset", "attnres_timing_read"):
@@ -418,6 +425,44 @@ def attnres_aggregate_backward(sources: Sequence[torch.Tensor], w: torch.Tensor,
         _ptr(dh), _ptr_array(dV), 1 if accumulate else 0, _ptr(dw), _ptr(dgamma),
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)))
     return dV, dw, dgamma
+
+
+def attnres_stack_backward_workspace_bytes(L: int, S: int, R: int, D: int, dtype: torch.dtype) -> int:
+    return int(lib().attnres_stack_backward_workspace_bytes(L, S, R, D, dtype_code(dtype)))
+
+
+def attnres_block_stack_backward(x: torch.Tensor, v: Sequence[torch.Tensor], W: torch.Tensor, S: int,
+                                 dy: torch.Tensor, dh: Sequence[torch.Tensor], block_sums=None,
+                                 Gamma=None, eps=1e-8, dx=None, dv=None, dW=None, dGamma=None,
+                                 want_dgamma=None, workspace=None, stream=None):
+    """Gradients of the Block stack forward for upstream gradients dh_l (a list
+    of L tensors, served by the built-in table callback) and dy. Returns
+    (dx, dv list, dW, dGamma or None), all fp32."""
+    R, D = _rows(x)
+    L = W.shape[0] - 1
+    dev = x.device
+    if dx is None:
+        dx = torch.empty((R, D), dtype=torch.float32, device=dev)
+    if dv is None:
+        dv = [torch.empty((R, D), dtype=torch.float32, device=dev) for _ in range(L)]
+    if dW is None:
+        dW = torch.empty((L + 1, D), dtype=torch.float32, device=dev)
+    if want_dgamma is None:
+        want_dgamma = Gamma is not None
+    if dGamma is None and want_dgamma:
+        dGamma = torch.empty((L + 1, D), dtype=torch.float32, device=dev)
+    need = attnres_stack_backward_workspace_bytes(L, S, R, D, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    table = _ptr_array(dh)
+    vt = _ptr_array(v)
+    bs = _ptr_array(block_sums) if block_sums is not None else None
+    _check("attnres_block_stack_backward", lib().attnres_block_stack_backward(
+        _ptr(x), vt, L, S, R, D, dtype_code(x.dtype), _ptr(W), _ptr(Gamma), eps, bs, _ptr(dy),
+        ctypes.cast(lib().attnres_table_sublayer_bwd, ctypes.c_void_p), ctypes.cast(table, ctypes.c_void_p),
+        _ptr(dx), _ptr_array(dv), _ptr(dW), _ptr(dGamma), ctypes.c_void_p(workspace.data_ptr()),
+        workspace.numel(), _stream(stream)))
+    return dx, dv, dW, dGamma
 
 
 def attnres_noalloc_scratch_bytes() -> int:

@@ -21,6 +21,7 @@
 
 using attnres::AggArgs;
 using attnres::BwdArgs;
+using attnres::MergeBwdArgs;
 using attnres::BwdPlan;
 using attnres::Launch;
 using attnres::Phase1Args;
@@ -1242,6 +1243,225 @@ ATTNRES_API int attnres_aggregate_backward_noalloc(const void* const* sources, i
   TRY(scratch_address(fn, st, &ws));
   BwdArgs a{sources, n, R, D, w, gamma, eps, dh, dV, accumulate, dw, dgamma, ws};
   TRY(launch_backward(fn, dtype, a, pl, st));
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Backward of the Block stack through the two-phase schedule, with
+// recomputation [K3 9.1 (A1)-(A3), 9.4 (OS1)-(OS2) differentiated; WC
+// "Depth attention & online merge reference" and "Public implementation
+// boundary": forward and backward with online softmax and recomputation].
+// ---------------------------------------------------------------------------
+namespace {
+
+struct BwdStackLayout {
+  size_t o, m, lse, p, a, dl, g, gbytes, bw, total;
+};
+
+BwdStackLayout bwd_stack_layout(int L, int S, int64_t R, int64_t D, int dtype) {
+  BwdStackLayout s;
+  const int es = esize_of(dtype);
+  const int Sk = S < L ? S : L;
+  const size_t row = (size_t)R * (size_t)D * es;
+  size_t off = 0;
+  s.o = off; off = align256(off + (size_t)Sk * row);
+  s.m = off; off = align256(off + (size_t)Sk * R * sizeof(float));
+  s.lse = off; off = align256(off + (size_t)Sk * R * sizeof(float));
+  s.p = off; off = align256(off + (Sk > 2 ? (size_t)(Sk - 2) * row : 0));
+  s.a = off; off = align256(off + (size_t)Sk * R * sizeof(float));
+  s.dl = off; off = align256(off + (size_t)Sk * R * sizeof(float));
+  s.g = off;
+  s.gbytes = 0;
+  if (Sk > 1 && attnres::phase1_gemm_shape(dtype, Sk, D, R) &&
+      !attnres::phase1_mfma_eligible(dtype, 1, Sk, D))
+    s.gbytes = attnres::phase1_gemm_workspace(Sk, R, D);
+  off = align256(off + s.gbytes);
+  s.bw = off; off = align256(off + attnres::plan_aggregate_bwd(dtype, R, D).bytes);
+  s.total = off;
+  return s;
+}
+
+}  // namespace
+
+ATTNRES_API int attnres_table_sublayer_bwd(void* ctx, int l, const float* dv_l, const void** dh_out,
+                                           void* stream) {
+  (void)dv_l;
+  (void)stream;
+  if (!ctx || !dh_out || l < 1) return 1;
+  *dh_out = static_cast<const void* const*>(ctx)[l - 1];
+  return 0;
+}
+
+ATTNRES_API size_t attnres_stack_backward_workspace_bytes(int L, int S, int64_t R, int64_t D,
+                                                          int dtype) {
+  if (!esize_of(dtype) || L < 1 || S < 1 || R < 0 || D < 1) return 0;
+  return bwd_stack_layout(L, S, R, D, dtype).total;
+}
+
+ATTNRES_API int attnres_block_stack_backward(
+    const void* x, const void* const* v, int L, int S, int64_t R, int64_t D, int dtype,
+    const float* W, const float* Gamma, float eps, const void* const* block_sums, const void* dy,
+    attnres_sublayer_bwd_fn fb, void* fb_ctx, float* dx, float* const* dv, float* dW, float* dGamma,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "attnres_block_stack_backward";
+  TRY(check_shape(fn, R, D, dtype, eps));
+  if (L < 1 || S < 1) return fail(ATTNRES_EINVAL, "%s: L = %d and S = %d must be >= 1", fn, L, S);
+  const int nb = plan(L, S, nullptr, nullptr);
+  if (nb + 1 > ATTNRES_MAX_SOURCES)
+    return fail(ATTNRES_EINVAL, "%s: %d blocks plus the embedding exceed %d sources", fn, nb,
+                ATTNRES_MAX_SOURCES);
+  const BwdPlan pl = attnres::plan_aggregate_bwd(dtype, R, D);
+  if (!pl.supported) return fail(ATTNRES_EUNSUPPORTED, "%s: D = %lld", fn, (long long)D);
+  TRY(check_ptr(fn, "W", W, true));
+  TRY(check_ptr(fn, "Gamma", Gamma, false));
+  TRY(check_ptr(fn, "dW", dW, true));
+  TRY(check_ptr(fn, "dGamma", dGamma, false));
+  if (dGamma && !Gamma) return fail(ATTNRES_EINVAL, "%s: dGamma requires Gamma", fn);
+  if (R > 0) {
+    TRY(check_ptr(fn, "x", x, true));
+    TRY(check_ptr(fn, "dy", dy, true));
+    TRY(check_ptr(fn, "dx", dx, true));
+    if (!v || !dv) return fail(ATTNRES_EINVAL, "%s: v and dv are required", fn);
+    for (int l = 0; l < L; ++l) {
+      TRY(check_ptr(fn, "v[l]", v[l], true));
+      TRY(check_ptr(fn, "dv[l]", dv[l], true));
+      if ((const void*)dv[l] == (const void*)dx)
+        return fail(ATTNRES_EINVAL, "%s: dv[%d] aliases dx", fn, l);
+      for (int m = 0; m < l; ++m)
+        if (dv[m] == dv[l]) return fail(ATTNRES_EINVAL, "%s: dv[%d] aliases dv[%d]", fn, l, m);
+    }
+    if (!block_sums && S != 1)
+      return fail(ATTNRES_EINVAL, "%s: block_sums may be NULL only when S == 1", fn);
+    if (block_sums)
+      for (int k = 0; k < nb; ++k) TRY(check_ptr(fn, "block_sums[k]", block_sums[k], true));
+    if (!fb) return fail(ATTNRES_EINVAL, "%s: sublayer backward callback is NULL", fn);
+  }
+  const BwdStackLayout lay = bwd_stack_layout(L, S, R, D, dtype);
+  if (!workspace) return fail(ATTNRES_EINVAL, "%s: workspace is NULL", fn);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(ATTNRES_EINVAL, "%s: workspace is not 256-byte aligned", fn);
+  if (workspace_bytes < lay.total)
+    return fail(ATTNRES_EWORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes,
+                lay.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  void* bw = ws + lay.bw;
+  const int64_t tensor_bytes = R * D * esize_of(dtype);
+  const double rb = (double)R * D * esize_of(dtype), gb = (double)R * D * 4;
+  auto qrow = [&](const float* M0, int l) -> const float* { return M0 ? M0 + (int64_t)(l - 1) * D : nullptr; };
+  auto frow = [&](float* M0, int l) -> float* { return M0 ? M0 + (int64_t)(l - 1) * D : nullptr; };
+
+  // the reductions of the query gradient (dq~ partials in bw -> dw, dgamma)
+  auto reduce_q = [&](const float* w, const float* g, float* dw_, float* dg_, int acc) -> int {
+    BwdArgs a{nullptr, 0, R, D, w, g, eps, nullptr, nullptr, acc, dw_, dg_, bw};
+    const double pbytes = (double)pl.P * D * 4;
+    hipError_t e;
+    if (pl.P2) {
+      e = attnres::launch_bwd_reduce(a, pl, 0, timed_launch(K_BWD_REDUCE, pbytes + pl.P2 * D * 4.0, st));
+      if (e != hipSuccess) return hip_fail(fn, e);
+    }
+    e = attnres::launch_bwd_reduce(
+        a, pl, 1, timed_launch(K_BWD_REDUCE, (double)(pl.P2 ? pl.P2 : pl.P) * D * 4 + D * 4.0 * (dg_ ? 2 : 1), st));
+    return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
+  };
+  // one aggregate backward over srcs[0..n) into their gradients g[0..n)
+  auto agg_bwd = [&](const void* const* srcs, float* const* grads, int n, int l, const void* dh,
+                     const float* scale, const float* dlse, int acc_v, int acc_q) -> int {
+    BwdArgs a{srcs, n, R, D, qrow(W, l), qrow(Gamma, l), eps, dh, grads, acc_v, frow(dW, l),
+              frow(dGamma, l), bw, scale, dlse, acc_q};
+    hipError_t e = attnres::launch_aggregate_bwd(
+        dtype, a, pl, timed_launch(K_BWD, rb * (n + 1) + gb * n * (acc_v ? 2 : 1), st));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return reduce_q(qrow(W, l), qrow(Gamma, l), frow(dW, l), frow(dGamma, l), acc_q);
+  };
+  auto callback = [&](int l, const float* dvl, const void** dh) -> int {
+    const void* out = nullptr;
+    const int rc = fb(fb_ctx, l, dvl, &out, stream);
+    if (rc != 0)
+      return fail(ATTNRES_ECALLBACK, "%s: sublayer backward callback returned %d at l = %d", fn, rc, l);
+    if (!out || !aligned16(out))
+      return fail(ATTNRES_ECALLBACK, "%s: callback gave a NULL or misaligned dh at l = %d", fn, l);
+    *dh = out;
+    return ATTNRES_OK;
+  };
+
+  if (R == 0) {
+    // no rows: every query gradient is zero (the reductions over no rows)
+    for (int l = 1; l <= L + 1; ++l)
+      TRY(reduce_q(qrow(W, l), qrow(Gamma, l), frow(dW, l), frow(dGamma, l), 0));
+    return ok();
+  }
+
+  // block k's completed sources b_0..b_k and their gradients: b_0 = x with
+  // gradient dx; b_k (k >= 1) is the sum of block k-1's outputs, and its
+  // gradient is exactly that of block k-1's last output, dv[end_{k-1} - 1]
+  std::vector<const void*> b(nb + 1);
+  std::vector<float*> db(nb + 1);
+  b[0] = x;
+  db[0] = dx;
+  for (int k = 0; k < nb; ++k) {
+    const int end = (k + 1) * S < L ? (k + 1) * S : L;
+    b[k + 1] = block_sums ? block_sums[k] : v[k];  // S == 1 without sums: b_{k+1} = v_{k+1}
+    db[k + 1] = dv[end - 1];
+  }
+
+  // the final aggregate y = AGG(b_0 .. b_nb; q~_{L+1}) writes every db first
+  TRY(agg_bwd(b.data(), db.data(), nb + 1, L + 1, dy, nullptr, nullptr, 0, 0));
+
+  for (int k = nb - 1; k >= 0; --k) {
+    const int start = k * S + 1;
+    const int end = (k + 1) * S < L ? (k + 1) * S : L;
+    const int Sk = end - start + 1;
+    const int n = k + 1;
+    std::vector<const void*> dh(Sk, nullptr);
+    // db_{k+1} = dv_end is complete: the sublayer's own backward gives dh_end
+    TRY(callback(end, dv[end - 1], &dh[Sk - 1]));
+    if (Sk == 1) {
+      // a one-sublayer block: h = AGG(b_0 .. b_k)
+      TRY(agg_bwd(b.data(), db.data(), n, start, dh[0], nullptr, nullptr, 1, 0));
+      continue;
+    }
+    // recompute the block's Phase 1 (o_j, lse_j) and its partials p_2 .. p_{Sk-1}
+    const bool one_source = n == 1 && attnres::phase1_stats_supported(dtype, 1, Sk, D);
+    char* O = ws + lay.o;
+    float* LSE = reinterpret_cast<float*>(ws + lay.lse);
+    float* A = reinterpret_cast<float*>(ws + lay.a);
+    float* DL = reinterpret_cast<float*>(ws + lay.dl);
+    {
+      const float* Wk = W + (int64_t)(start - 1) * D;
+      const float* Gk = Gamma ? Gamma + (int64_t)(start - 1) * D : nullptr;
+      Phase1Args a1{b.data(), n, R, D, Wk, Gk, Sk, eps, one_source ? nullptr : O,
+                    reinterpret_cast<float*>(ws + lay.m), LSE, nullptr, nullptr, nullptr,
+                    lay.gbytes ? ws + lay.g : nullptr};
+      TRY(do_phase1(fn, dtype, a1, st));
+    }
+    auto o_slice = [&](int j) -> const void* {
+      return one_source ? b[0] : static_cast<const void*>(O + (int64_t)j * tensor_bytes);
+    };
+    auto p_slice = [&](int j) -> const void* {  // the partial seen by sublayer start + j (j >= 1)
+      return j == 1 ? v[start - 1] : static_cast<const void*>(ws + lay.p + (int64_t)(j - 2) * tensor_bytes);
+    };
+    for (int j = 2; j < Sk; ++j)
+      TRY(do_close(fn, p_slice(j - 1), v[start + j - 2], const_cast<void*>(p_slice(j)), R, D, dtype, st));
+    // Phase-2 merges in reverse: sublayer start + j merged (lse_j, o_j) with p_j;
+    // its backward turns dh into the gradient of p_j, which (with the gradient
+    // from the partial's later uses, dv[start + j - 1]) is that of v_{start+j-1}
+    for (int j = Sk - 1; j >= 1; --j) {
+      const int l = start + j;
+      MergeBwdArgs mb{o_slice(j), LSE + (int64_t)j * R, p_slice(j), qrow(W, l), qrow(Gamma, l), eps,
+                      dh[j], dv[l - 1], dv[l - 2], A + (int64_t)j * R, DL + (int64_t)j * R, R, D, bw};
+      hipError_t e = attnres::launch_merge_bwd(
+          dtype, mb, pl, timed_launch(K_BWD, rb * 3 + gb * 2 + R * 8.0, st, "merge_bwd_kernel"));
+      if (e != hipSuccess) return hip_fail(fn, e);
+      TRY(reduce_q(qrow(W, l), qrow(Gamma, l), frow(dW, l), frow(dGamma, l), 0));
+      TRY(callback(l - 1, dv[l - 2], &dh[j - 1]));
+    }
+    // Phase-1 backward: query j's output received a_j dh_j (dh_0 itself: h = o_0)
+    // and its log-sum-exp dlse_j; the gradients of b_0 .. b_k accumulate
+    for (int j = 0; j < Sk; ++j)
+      TRY(agg_bwd(b.data(), db.data(), n, start + j, dh[j], j ? A + (int64_t)j * R : nullptr,
+                  j ? DL + (int64_t)j * R : nullptr, 1, j ? 1 : 0));
+  }
   return ok();
 }
 

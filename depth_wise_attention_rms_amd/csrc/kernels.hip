@@ -1045,6 +1045,8 @@ struct AggBwdParams {
   const float* gm;     // [D] or null
   float eps;
   const void* dh;      // [R][D] in the I/O dtype
+  const float* dh_scale;  // [R] or null: the upstream gradient is dh_scale[r] * dh[r]
+  const float* dlse;      // [R] or null: gradient of the group's log-sum-exp, added to every score's
   float* partial;      // [gridDim.x * RPW][D]
   Geom g;
 };
@@ -1221,12 +1223,13 @@ void aggregate_bwd_kernel(AggBwdParams p) {
         }
       }
       row_reduce<NV>(red, lds, ln.slot, ln.wr, g.W);
+      const float gscale = p.dh_scale ? p.dh_scale[rv ? row : 0] : 1.f;
       #pragma unroll
       for (int j = 0; j < G; ++j) {
         const float ri = rsqrtf(uniformf(red[G + j]) * g.invD + p.eps);
         st[j].ri = uniformf(ri);
         st[j].s = uniformf(uniformf(red[j]) * ri);
-        st[j].gd = uniformf(red[2 * G + j]);
+        st[j].gd = uniformf(gscale * uniformf(red[2 * G + j]));
       }
       if (RES) {
         #pragma unroll
@@ -1261,6 +1264,10 @@ void aggregate_bwd_kernel(AggBwdParams p) {
       }
     }
     if (!rv) continue;  // uniform per row slot; no barrier follows in this iteration
+    // the upstream gradient's row scale (its weight in a merge downstream) and
+    // the gradient of the group's log-sum-exp: d lse / d s_i = a_i
+    const float gs = uniformf(p.dh_scale ? p.dh_scale[row] : 1.f);
+    const float dl = uniformf(p.dlse ? p.dlse[row] : 0.f);
 
     if (RES) {
       // softmax over the n resident sources
@@ -1286,9 +1293,10 @@ void aggregate_bwd_kernel(AggBwdParams p) {
         if (j >= p.n) continue;
         // one source at a time: keeps its unpacked values short-lived
         __builtin_amdgcn_sched_barrier(0);
-        const float ds = a[j] * (st[j].gd - gbar);
+        const float ds = a[j] * (st[j].gd - gbar + dl);
         const float B = uniformf(ds * st[j].ri);
         const float C = uniformf(-B * st[j].s * st[j].ri * g.invD);
+        const float A = uniformf(a[j] * gs);
         float* dst = p.dV[j] + row * g.D;
         #pragma unroll
         for (int c = 0; c < VPL; ++c) {
@@ -1297,7 +1305,7 @@ void aggregate_bwd_kernel(AggBwdParams p) {
           const int vec = c * ln.stride + ln.t;
           float* to = reinterpret_cast<float*>(
               store_target(vec < g.V, reinterpret_cast<char*>(dst + (int64_t)vec * 4)));
-          bwd_store_dv<F, ACC>(to, dhr[c], q[c], x[j][c], a[j], B, C);
+          bwd_store_dv<F, ACC>(to, dhr[c], q[c], x[j][c], A, B, C);
           bwd_acc_dq<F>(dq[c], x[j][c], B);
         }
       }
@@ -1308,9 +1316,10 @@ void aggregate_bwd_kernel(AggBwdParams p) {
       for (int i = 0; i < p.n; ++i) {
         const BwdStat si = stat[i];
         const float a = uniformf(__expf(si.s - m_run) * rz);
-        const float ds = a * (si.gd - gbar);
+        const float ds = a * (si.gd - gbar + dl);
         const float B = uniformf(ds * si.ri);
         const float C = uniformf(-B * si.s * si.ri * g.invD);
+        const float A = uniformf(a * gs);
         const char* srow = static_cast<const char*>(p.src[i]) + row * rowbytes;
         float* dst = p.dV[i] + row * g.D;
         raw xr[VPL];
@@ -1325,7 +1334,7 @@ void aggregate_bwd_kernel(AggBwdParams p) {
           const int vec = c * ln.stride + ln.t;
           float* to = reinterpret_cast<float*>(
               store_target(vec < g.V, reinterpret_cast<char*>(dst + (int64_t)vec * 4)));
-          bwd_store_dv<F, ACC>(to, dhr[c], q[c], xr[c], a, B, C);
+          bwd_store_dv<F, ACC>(to, dhr[c], q[c], xr[c], A, B, C);
           bwd_acc_dq<F>(dq[c], xr[c], B);
         }
       }
@@ -1333,6 +1342,142 @@ void aggregate_bwd_kernel(AggBwdParams p) {
   }
 
   // this (workgroup, row slot)'s sum of dq~ over its rows
+  float* prow = p.partial + ((int64_t)blockIdx.x * g.RPW + ln.slot) * g.D;
+  #pragma unroll
+  for (int c = 0; c < VPL; ++c) {
+    const int vec = c * ln.stride + ln.t;
+    if (vec < g.V)
+      st16(prow + (int64_t)vec * 4, make_uint4(__float_as_uint(dq[c][0]), __float_as_uint(dq[c][1]),
+                                               __float_as_uint(dq[c][2]), __float_as_uint(dq[c][3])));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward of one Phase-2 merge [K3 9.4 (OS2) and the single-source triple,
+// differentiated; recomputation as in the aggregate backward]. The merge is
+// a two-term softmax: h = a o + c p with (a, c) = softmax(lse, s_p) and
+// s_p = q~ . p / r_p, r_p = sqrt(mean_d p^2 + eps). Per row, with the
+// upstream gradient dh and gh = dh . h = a (dh . o) + c (dh . p):
+//   d lse = a (dh . o - gh),   d s_p = c (dh . p - gh)
+//   dp    = c dh + (d s_p / r_p) q~ - (d s_p s_p / (D r_p^2)) p
+//   dq~  += (d s_p / r_p) p
+// and the group's output o receives a dh (returned as the weight a, so the
+// Phase-1 backward scales dh itself). One row reduction gives q~.p, p.p,
+// dh.o and dh.p; g_out = g_in + dp (the partial's gradient accumulated from
+// its later uses, the partial chain p_{j+1} = p_j + v_j).
+// ---------------------------------------------------------------------------
+struct MergeBwdParams {
+  const void* o;
+  const float* lse;
+  const void* ps;
+  const float* w;
+  const float* gm;
+  float eps;
+  const void* dh;
+  const float* g_in;
+  float* g_out;
+  float* a_out;
+  float* dlse_out;
+  float* partial;  // [gridDim.x * RPW][D]
+  Geom g;
+};
+
+template <class F, int VPL>
+__global__ __launch_bounds__(512) void merge_bwd_kernel(MergeBwdParams p) {
+  extern __shared__ float lds[];
+  typedef typename F::raw raw;
+  const Geom& g = p.g;
+  const Lanes ln(g.W);
+  const int64_t rowbytes = (int64_t)g.V * F::kBytes;
+  float q[VPL][4], dq[VPL][4];
+  #pragma unroll
+  for (int c = 0; c < VPL; ++c) {
+    const int vec = c * ln.stride + ln.t;
+    if (vec < g.V) {
+      load_query<4>(p.w, p.gm, (int64_t)vec * 4, q[c]);
+    } else {
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) q[c][e] = 0.f;
+    }
+    #pragma unroll
+    for (int e = 0; e < 4; ++e) dq[c][e] = 0.f;
+  }
+  for (int64_t grp = blockIdx.x; grp < g.groups; grp += gridDim.x) {
+    const int64_t row = grp * g.RPW + ln.slot;
+    const bool rv = row < g.R;
+    const int64_t base = (rv ? row : 0) * rowbytes;
+    raw orw[VPL], prw[VPL], dhr[VPL];
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      const int vec = c * ln.stride + ln.t;
+      const int64_t off = base + (int64_t)(vec < g.V ? vec : 0) * F::kBytes;
+      orw[c] = F::load(static_cast<const char*>(p.o) + off);
+      prw[c] = F::load(static_cast<const char*>(p.ps) + off);
+      dhr[c] = F::load(static_cast<const char*>(p.dh) + off);
+    }
+    float red[4] = {0.f, 0.f, 0.f, 0.f};  // q~.p, p.p, dh.o, dh.p
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      const bool in_row = c * ln.stride + ln.t < g.V;
+      float fo[4], fp[4], fd[4];
+      F::unpack(orw[c], fo);
+      F::unpack(prw[c], fp);
+      F::unpack(dhr[c], fd);
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pe = in_row ? fp[e] : 0.f, de = in_row ? fd[e] : 0.f;
+        red[0] += q[c][e] * pe;
+        red[1] += pe * pe;
+        red[2] += de * fo[e];
+        red[3] += de * pe;
+      }
+    }
+    row_reduce<4>(red, lds, ln.slot, ln.wr, g.W);
+    if (!rv) continue;  // uniform per row slot; no barrier follows in this iteration
+    const float rp = rsqrtf(red[1] * g.invD + p.eps);  // 1 / r_p
+    const float sp = red[0] * rp;
+    const float l = p.lse[row];
+    const float M = fmaxf(l, sp);
+    float a = __expf(l - M), cw = __expf(sp - M);
+    const float rz = 1.0f / (a + cw);
+    a *= rz;
+    cw *= rz;
+    const float gh = a * red[2] + cw * red[3];
+    const float dl = a * (red[2] - gh);
+    const float dsp = cw * (red[3] - gh);
+    const float B = uniformf(dsp * rp);
+    const float C = uniformf(-B * sp * rp * g.invD);
+    const float A = uniformf(cw);
+    float* gout = p.g_out + row * g.D;
+    const float* gin = p.g_in ? p.g_in + row * g.D : nullptr;
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      const int vec = c * ln.stride + ln.t;
+      if (vec < g.V) {
+        float fp[4], fd[4], o4[4];
+        F::unpack(prw[c], fp);
+        F::unpack(dhr[c], fd);
+        if (gin) {
+          const uint4 u = ld16_stream(gin + (int64_t)vec * 4);
+          o4[0] = __uint_as_float(u.x); o4[1] = __uint_as_float(u.y);
+          o4[2] = __uint_as_float(u.z); o4[3] = __uint_as_float(u.w);
+        } else {
+          o4[0] = o4[1] = o4[2] = o4[3] = 0.f;
+        }
+        #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o4[e] += A * fd[e] + B * q[c][e] + C * fp[e];
+          dq[c][e] += B * fp[e];
+        }
+        st16_stream(gout + (int64_t)vec * 4, make_uint4(__float_as_uint(o4[0]), __float_as_uint(o4[1]),
+                                                        __float_as_uint(o4[2]), __float_as_uint(o4[3])));
+      }
+    }
+    if (ln.t == 0) {
+      p.a_out[row] = a;
+      p.dlse_out[row] = dl;
+    }
+  }
   float* prow = p.partial + ((int64_t)blockIdx.x * g.RPW + ln.slot) * g.D;
   #pragma unroll
   for (int c = 0; c < VPL; ++c) {
@@ -2802,6 +2947,7 @@ static hipError_t launch_bwd_dt(const BwdArgs& a, const BwdPlan& pl, const Launc
   }
   p.n = a.n; p.accumulate = a.accumulate;
   p.w = a.w; p.gm = a.g; p.eps = a.eps; p.dh = a.dh;
+  p.dh_scale = a.dh_scale; p.dlse = a.dlse;
   p.partial = static_cast<float*>(a.workspace);
   int vpl = 0;
   p.g = bwd_geom(F::kBytes == 8 ? 1 : 0, a.R, a.D, &vpl);
@@ -2832,7 +2978,36 @@ hipError_t launch_bwd_reduce(const BwdArgs& a, const BwdPlan& pl, int stage, con
   const float* in = pl.P2 ? stage1 : partial;
   const int64_t rows = pl.P2 ? pl.P2 : pl.P;
   return launch(L, bwd_colsum_kernel<true>, dim3(bx, 1), dim3(256), 0, in, rows, a.D, rows,
-                (float*)nullptr, a.w, a.g, a.dw, a.dgamma, a.accumulate);
+                (float*)nullptr, a.w, a.g, a.dw, a.dgamma,
+                a.accumulate_q < 0 ? a.accumulate : a.accumulate_q);
+}
+
+template <class F, int VPL>
+static hipError_t launch_merge_bwd_t(const MergeBwdParams& p, unsigned grid, const Launch& L) {
+  const size_t lds = p.g.W > 1 ? (size_t)p.g.RPW * p.g.W * 4 * sizeof(float) : 0;
+  return launch(L, merge_bwd_kernel<F, VPL>, dim3(grid), dim3(64 * p.g.W * p.g.RPW), lds, p);
+}
+
+template <class F, int SMALL>
+static hipError_t launch_merge_bwd_dt(const MergeBwdArgs& a, const BwdPlan& pl, const Launch& L) {
+  MergeBwdParams p;
+  p.o = a.o; p.lse = a.lse; p.ps = a.ps; p.w = a.w; p.gm = a.g; p.eps = a.eps; p.dh = a.dh;
+  p.g_in = a.g_in; p.g_out = a.g_out; p.a_out = a.a_out; p.dlse_out = a.dlse_out;
+  p.partial = static_cast<float*>(a.workspace);
+  int vpl = 0;
+  p.g = bwd_geom(F::kBytes == 8 ? 1 : 0, a.R, a.D, &vpl);
+  if (vpl == SMALL) return launch_merge_bwd_t<F, SMALL>(p, pl.grid, L);
+  if (vpl == 2 * SMALL) return launch_merge_bwd_t<F, 2 * SMALL>(p, pl.grid, L);
+  if constexpr (SMALL * 4 <= 8) {
+    if (vpl == 4 * SMALL) return launch_merge_bwd_t<F, 4 * SMALL>(p, pl.grid, L);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_merge_bwd(int dtype, const MergeBwdArgs& a, const BwdPlan& pl, const Launch& L) {
+  if (pl.grid == 0) return hipSuccess;
+  return dtype == 1 ? launch_merge_bwd_dt<Bf16x4, ATTNRES_BWD_BF16_VPL>(a, pl, L)
+                    : launch_merge_bwd_dt<F32x4, ATTNRES_BWD_F32_VPL>(a, pl, L);
 }
 
 }  // namespace attnres

@@ -95,6 +95,33 @@ struct BwdArgs {
   float* dw;
   float* dgamma;
   void* workspace;
+  // [R] or null: the upstream gradient of row r is dh_scale[r] * dh[r]
+  const float* dh_scale = nullptr;
+  // [R] or null: gradient of the group's log-sum-exp, added to each score's
+  const float* dlse = nullptr;
+  // dw / dgamma written (0) or added (1); -1: as accumulate
+  int accumulate_q = -1;
+};
+
+// Backward of one Phase-2 merge, h = a o + c p with (a, c) = softmax(lse,
+// s_p) and s_p the score of p: from the upstream gradient dh it forms the
+// gradient of p (through the weighted sum and through s_p), added to g_in
+// into g_out, the group's weight a and the gradient of lse per row, and the
+// per-workgroup dq~ partials in `workspace` (BwdPlan of the same shape).
+struct MergeBwdArgs {
+  const void* o;      // [R][D] dtype
+  const float* lse;   // [R]
+  const void* ps;     // [R][D] dtype: the partial p
+  const float* w;     // [D]
+  const float* g;     // [D] or null
+  float eps;
+  const void* dh;     // [R][D] dtype
+  const float* g_in;  // [R][D] fp32 or null (zero)
+  float* g_out;       // [R][D] fp32
+  float* a_out;       // [R]
+  float* dlse_out;    // [R]
+  int64_t R, D;
+  void* workspace;
 };
 
 struct BwdPlan {
@@ -113,6 +140,7 @@ hipError_t launch_aggregate_bwd(int dtype, const BwdArgs& a, const BwdPlan& pl, 
 // stage 0: partial rows -> chunk sums (no-op when P2 == 0); stage 1: final
 // sum, dw and dgamma
 hipError_t launch_bwd_reduce(const BwdArgs& a, const BwdPlan& pl, int stage, const Launch& L);
+hipError_t launch_merge_bwd(int dtype, const MergeBwdArgs& a, const BwdPlan& pl, const Launch& L);
 
 hipError_t launch_fold(const float* w, const float* g, float* q, int64_t count, const Launch& L);
 hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L);

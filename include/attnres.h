@@ -353,6 +353,59 @@ int attnres_aggregate_backward(const void* const* sources, int n, int64_t R, int
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * attnres_block_stack_backward -- the gradients of the Block stack forward
+ * through its two-phase schedule, with recomputation [K3 9.1 (A1)-(A4) and
+ * 9.4 (OS1)-(OS2) differentiated; WC "Depth attention & online merge
+ * reference", "Public implementation boundary": a fused forward and backward
+ * with online softmax and recomputation]. The loss reaches the stack through
+ * every aggregate: L = sum_l <dh_l, h_l> + <dy, y>, where the sublayers
+ * supply dh_l. Blocks are walked in reverse; per block the library
+ *   - recomputes its Phase 1 (o_j, lse_j over [b_0 .. b_k]) and partials;
+ *   - for each sublayer from the last to the second, runs the backward of
+ *     its Phase-2 merge h = OS2((lse_j, o_j), (s_p, p_j)): the gradient of
+ *     p_j (through the weighted sum and through s_p) joins that of the
+ *     partial's later uses, which is exactly dv of the sublayer before;
+ *   - then the Phase-1 backward of each query: its output received a_j dh_j
+ *     (a_j the group's merge weight; dh itself for the first sublayer, whose
+ *     h is o_0) and its log-sum-exp the merge's d lse_j;
+ *   - block sum b_k's gradient is that of block k-1's last output.
+ * Rounding to the I/O dtype (outputs, partials, block sums) is taken as the
+ * identity in the backward.
+ *   x, v (host)   : the forward's embedding [R,D] and its L sublayer outputs
+ *   W, Gamma      : [L+1, D] fp32 as in the forward (Gamma NULL means ones)
+ *   block_sums    : (host) the forward's nb block sums, or NULL when S == 1
+ *                   (then b_l = v_l)
+ *   dy            : [R,D] dtype, the upstream gradient of y
+ *   fb, fb_ctx    : the sublayer backward, called with l = L down to 1 once
+ *                   dv_l (fp32 [R,D], the gradient of v_l) is complete; it
+ *                   returns in *dh_out the upstream gradient of h_l, [R,D]
+ *                   dtype, which must stay valid until the callback for the
+ *                   previous block's last sublayer returns (or the call
+ *                   ends); attnres_table_sublayer_bwd serves a table of L
+ *                   given gradients
+ *   dx            : [R,D] fp32, the gradient of x (written)
+ *   dv (host)     : L device pointers [R,D] fp32, distinct, receiving dv_l
+ *                   (written; the callback reads dv_l from dv[l-1])
+ *   dW, dGamma    : [L+1, D] fp32, written; dGamma NULL when not wanted
+ *                   (and required NULL when Gamma is NULL)
+ *   workspace     : attnres_stack_backward_workspace_bytes(L, S, R, D, dtype)
+ *                   bytes, 256-byte aligned
+ * Errors as attnres_block_stack_forward (ATTNRES_ECALLBACK for a failing
+ * sublayer backward). With R == 0, dW and dGamma are written as zeros.
+ * ------------------------------------------------------------------------- */
+typedef int (*attnres_sublayer_bwd_fn)(void* ctx, int l, const float* dv_l, const void** dh_out,
+                                       void* stream);
+int attnres_table_sublayer_bwd(void* ctx, int l, const float* dv_l, const void** dh_out,
+                               void* stream);
+size_t attnres_stack_backward_workspace_bytes(int L, int S, int64_t R, int64_t D, int dtype);
+int attnres_block_stack_backward(const void* x, const void* const* v, int L, int S, int64_t R,
+                                 int64_t D, int dtype, const float* W, const float* Gamma, float eps,
+                                 const void* const* block_sums, const void* dy,
+                                 attnres_sublayer_bwd_fn fb, void* fb_ctx, float* dx,
+                                 float* const* dv, float* dW, float* dGamma, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * attnres_aggregate_backward_noalloc -- attnres_aggregate_backward without a
  * workspace argument, for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving or training loops, and harnesses

@@ -242,6 +242,71 @@ class Oracle:
                 "y_lse": yl, "block_sums": bsums, "nb": nb}
 
 
+    def block_stack_backward(self, x, v, W, S, dh, dy, Gamma=None, eps=1e-8, agg_fn=None, nthreads=None):
+        """Gradients of L = sum_l <dh_l, h_l> + <dy, y> through the naive Block
+        stack forward (K3 9.3 forward_naive, final aggregate of K3 9.1): the
+        aggregate backward of every aggregate, composed over the sources
+        forward_naive gives it. Sublayer l of block k aggregates the embedding
+        x, the completed block sums b_1..b_k and (from its block's second
+        sublayer on) the partial, the rounded left fold of the block's earlier
+        outputs; y aggregates x and every block sum. A block sum's gradient
+        goes to each output of its block and a partial's to each output it
+        sums (rounding to the I/O dtype taken as the identity). Returns dx
+        [rows, D], dv [L, rows, D], dW [L+1, D] and dGamma [L+1, D] (None
+        without gains), float64. ``agg_fn(srcs, w, dh, gamma, eps)`` may
+        replace the aggregate backward (same result keys) to compose other
+        per-aggregate quantities the same way."""
+        x = np.ascontiguousarray(x)
+        v = [np.ascontiguousarray(a) for a in v]
+        L = len(v)
+        rows, D = x.shape
+        dt = "bf16" if _dtype_code(x) == BF16 else "f32"
+        W = _f32(W)
+        Gamma = _f32(Gamma)
+        if agg_fn is None:
+            agg_fn = lambda srcs, w, d, g, e: self.aggregate_backward(srcs, w, d, g, eps=e, nthreads=nthreads)
+        st = self.block_stack(x, v, W, S, Gamma, eps, want_h=False, nthreads=nthreads)
+        bsums = list(st["block_sums"])
+        nb = st["nb"]
+        dx = np.zeros((rows, D))
+        dv = np.zeros((L, rows, D))
+        db = np.zeros((nb + 1, rows, D))
+        dW = np.zeros((L + 1, D))
+        dG = np.zeros((L + 1, D)) if Gamma is not None else None
+        wide = lambda a: (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64) \
+            if a.dtype == np.uint16 else a.astype(np.float64)
+        for l in range(1, L + 1):
+            k, j = (l - 1) // S, (l - 1) % S
+            start = k * S + 1
+            srcs = [x] + bsums[:k]
+            if j >= 1:
+                part = v[start - 1]
+                for t in range(start + 1, l):
+                    part = self.round_to(wide(part) + wide(v[t - 1]), dt)
+                srcs = srcs + [part]
+            out = agg_fn(srcs, W[l - 1], dh[l - 1], None if Gamma is None else Gamma[l - 1], eps)
+            dx += out["dV"][0]
+            for i in range(1, k + 1):
+                db[i] += out["dV"][i]
+            if j >= 1:
+                for t in range(start, l):  # the partial sums outputs start .. l-1
+                    dv[t - 1] += out["dV"][-1]
+            dW[l - 1] = out["dw"]
+            if dG is not None:
+                dG[l - 1] = out["dgamma"]
+        out = agg_fn([x] + bsums, W[L], dy, None if Gamma is None else Gamma[L], eps)
+        dx += out["dV"][0]
+        for i in range(1, nb + 1):
+            db[i] += out["dV"][i]
+        dW[L] = out["dw"]
+        if dG is not None:
+            dG[L] = out["dgamma"]
+        for i in range(1, nb + 1):  # block sum b_i sums the outputs of block i-1
+            for t in range((i - 1) * S + 1, min(i * S, L) + 1):
+                dv[t - 1] += db[i]
+        return {"dx": dx, "dv": dv, "dW": dW, "dGamma": dG}
+
+
 _default: Optional[Oracle] = None
 
 
@@ -293,3 +358,7 @@ def round_to(*a, **k):
 
 def block_stack(*a, **k):
     return default().block_stack(*a, **k)
+
+
+def block_stack_backward(*a, **k):
+    return default().block_stack_backward(*a, **k)

@@ -726,6 +726,58 @@ def pin_backward_finite_differences(orc):
         assert abs(fd - got["dgamma"][d]) <= 1e-6 * scale, ("gamma", d, fd, got["dgamma"][d])
 
 
+def pin_stack_backward_finite_differences(orc):
+    """The stack backward (the aggregate backward composed over the naive
+    Block forward) against central differences of
+    L = sum_l <dh_l, h_l> + <dy, y> computed by the oracle's naive stack
+    forward (K3 9.3), for every element of x, of every sublayer output, of
+    every query and of every gain. Five sublayers in blocks of two exercise
+    the partials, the block sums and a one-sublayer last block. Inputs are
+    fp32 grid values, so partials, block sums and the +-2^-10 steps are exact
+    and the loss is smooth in every input."""
+    rng = np.random.default_rng(67)
+    L, S, rows, D, eps = 5, 2, 2, 8, 1e-3
+    x = _grid_values(rng, (rows, D), 12, -4096, 4096)
+    v = [_grid_values(rng, (rows, D), 12, -4096, 4096) for _ in range(L)]
+    W = _grid_values(rng, (L + 1, D), 12, -2048, 2048)
+    G = _grid_values(rng, (L + 1, D), 4, 8, 24)
+    dh = [_grid_values(rng, (rows, D), 12, -4096, 4096) for _ in range(L)]
+    dy = _grid_values(rng, (rows, D), 12, -4096, 4096)
+    got = orc.block_stack_backward(x, v, W, S, dh, dy, Gamma=G, eps=eps)
+    delta = np.float32(2.0 ** -10)
+
+    def loss(xx, vv, WW, GG):
+        st = orc.block_stack(xx, vv, WW, S, Gamma=GG, eps=eps)
+        return float(sum((st["h"][l] * dh[l].astype(np.float64)).sum() for l in range(L))
+                     + (st["y"] * dy.astype(np.float64)).sum())
+
+    scale = max(np.abs(got["dx"]).max(), np.abs(got["dv"]).max(), np.abs(got["dW"]).max(),
+                np.abs(got["dGamma"]).max())
+
+    def check(fd, val, what):
+        assert abs(fd - val) <= 1e-6 * scale, (what, fd, val)
+
+    for r in range(rows):
+        for d in range(D):
+            xp, xm = x.copy(), x.copy()
+            xp[r, d] += delta; xm[r, d] -= delta
+            check((loss(xp, v, W, G) - loss(xm, v, W, G)) / (2 * float(delta)), got["dx"][r, d], ("x", r, d))
+            for l in range(L):
+                vp = [a.copy() for a in v]; vm = [a.copy() for a in v]
+                vp[l][r, d] += delta; vm[l][r, d] -= delta
+                check((loss(x, vp, W, G) - loss(x, vm, W, G)) / (2 * float(delta)), got["dv"][l, r, d],
+                      ("v", l, r, d))
+    for l in range(L + 1):
+        for d in range(D):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[l, d] += delta; Wm[l, d] -= delta
+            check((loss(x, v, Wp, G) - loss(x, v, Wm, G)) / (2 * float(delta)), got["dW"][l, d], ("W", l, d))
+            Gp, Gm = G.copy(), G.copy()
+            Gp[l, d] += delta; Gm[l, d] -= delta
+            check((loss(x, v, W, Gp) - loss(x, v, W, Gm)) / (2 * float(delta)), got["dGamma"][l, d],
+                  ("Gamma", l, d))
+
+
 def pin_backward_special_cases(orc):
     """One source: h is the source, so dV = dh exactly and the query gets no
     gradient; a zero upstream gradient gives zero gradients; with eps = 0 the

@@ -1,0 +1,143 @@
+"""GPU parity of the stack backward through the two-phase schedule
+(attnres_block_stack_backward): the gradients of
+L = sum_l <dh_l, h_l> + <dy, y> with respect to x, every sublayer output v_l,
+the queries W and the gains, against the oracle's aggregate backward composed
+over the naive Block forward (oracle.block_stack_backward, pinned by finite
+differences of the oracle's own stack forward).
+
+Tolerance: the scaled rule of every parity test, 1e-5 for fp32 and 1e-2 for
+bf16 runs, relative to the condition scale of tests/bwd_scale.py composed
+through the same bookkeeping as the gradients (each aggregate's source scales
+added where its source gradients go). The GPU differentiates the two-phase
+forward at its rounded intermediate values (Phase-1 outputs in the I/O dtype),
+the oracle the naive forward in fp64: they differ by rounding, which the bar
+absorbs.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from depth_wise_attention_rms_amd import binding as b
+from depth_wise_attention_rms_amd import inputs
+from depth_wise_attention_rms_amd.workload import EPS, DeviceStack
+from tests.bwd_scale import bwd_scales
+from tests.parity import TOL, scaled_error, to_host, widen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    b.lib()
+    inputs.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def _scale_fn(srcs, w, dh, g, eps):
+    V = np.stack([widen(a) for a in srcs])
+    q = (w * g).astype(np.float32).astype(np.float64) if g is not None else w.astype(np.float64)
+    sc_dV, sc_dq = bwd_scales(V, q, widen(dh), eps)
+    return {"dV": sc_dV,
+            "dw": sc_dq * (np.abs(g.astype(np.float64)) if g is not None else 1.0),
+            "dgamma": sc_dq * np.abs(w.astype(np.float64)) if g is not None else None}
+
+
+def _check(name, got, ref, scale, dtype):
+    err = scaled_error(got.astype(np.float64), ref, scale)
+    assert err <= TOL[dtype], f"{name}: max scaled error {err:.3e} > {TOL[dtype]:.0e}"
+    return err
+
+
+def run_case(wl, gains, rows_chunk=None):
+    ds = DeviceStack(wl, gains=gains)
+    ds.forward()
+    torch.cuda.synchronize()
+    R, D, L = wl.R, wl.D, wl.L
+    dh = [inputs.fill_normal(torch.empty((R, D), dtype=ds.dt, device="cuda"), wl.seed + 1, inputs.ROLE_AUX, l, 1.0)
+          for l in range(L)]
+    dy = inputs.fill_normal(torch.empty((R, D), dtype=ds.dt, device="cuda"), wl.seed + 2, inputs.ROLE_AUX, 99, 1.0)
+    dx, dv, dW, dG = b.attnres_block_stack_backward(ds.x, ds.v, ds.W, wl.S, dy, dh, block_sums=ds.block_sums,
+                                                    Gamma=ds.Gamma, eps=EPS)
+    torch.cuda.synchronize()
+    xr, vr = ds.host_rows(np.arange(R))
+    dhr = [to_host(t) for t in dh]
+    dyr = to_host(dy)
+    ref = oracle.block_stack_backward(xr, vr, ds.W_host, wl.S, dhr, dyr, Gamma=ds.Gamma_host, eps=EPS)
+    sc = oracle.block_stack_backward(xr, vr, ds.W_host, wl.S, dhr, dyr, Gamma=ds.Gamma_host, eps=EPS,
+                                     agg_fn=_scale_fn)
+    worst = _check(f"{wl.name} dx", to_host(dx), ref["dx"], sc["dx"], wl.dtype)
+    for l in range(L):
+        worst = max(worst, _check(f"{wl.name} dv_{l + 1}", to_host(dv[l]), ref["dv"][l], sc["dv"][l], wl.dtype))
+    worst = max(worst, _check(f"{wl.name} dW", to_host(dW), ref["dW"], sc["dW"], wl.dtype))
+    if gains:
+        worst = max(worst, _check(f"{wl.name} dGamma", to_host(dG), ref["dGamma"], sc["dGamma"], wl.dtype))
+    return worst
+
+
+def test_stack_backward_grid():
+    """Every L <= 6 and S <= L+1 on 3 rows: partials, block sums, one-sublayer
+    blocks, Full (S = 1), a first block whose Phase 1 sees only the embedding;
+    both dtypes, D in {8, 64}, with and without gains."""
+    for dtype in ("f32", "bf16"):
+        for D in (8, 64):
+            for L in range(1, 7):
+                for S in range(1, L + 2):
+                    wl = inputs.Workload(f"bwd_L{L}_S{S}_D{D}_{dtype}", "stack", B=1, T=3, D=D, dtype=dtype,
+                                         L=L, S=S, seed=L * 10 + S)
+                    run_case(wl, gains=(L + S + D) % 2 == 0)
+
+
+BWD_STACKS = [
+    # (B, T, D, S, L, dtype, gains): the register-tile Phase-1 recompute with
+    # several rows per workgroup; the streamed Phase 1 (12 queries at
+    # D = 7168, one-sublayer last block); the scores-pass Phase 1 (4100 rows
+    # of 7168); fp32; the workload of the block prefill at reduced depth
+    (2, 300, 2048, 6, 20, "bf16", True),
+    (1, 40, 7168, 12, 25, "bf16", False),
+    (1, 4100, 7168, 12, 15, "bf16", True),
+    (1, 65, 1024, 5, 13, "f32", True),
+    (1, 512, 4096, 8, 16, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("B,T,D,S,L,dtype,gains", BWD_STACKS)
+def test_stack_backward_shapes(B, T, D, S, L, dtype, gains):
+    wl = inputs.Workload(f"bwd_R{B * T}_D{D}_S{S}_L{L}_{dtype}", "stack", B=B, T=T, D=D, dtype=dtype, L=L, S=S,
+                         seed=L + S + 3)
+    announce(f"{wl.name} gains={gains}")
+    worst = run_case(wl, gains)
+    print(f"[gpu-case] {wl.name}: worst scaled error {worst:.3e}", flush=True)
+    torch.cuda.empty_cache()
+
+
+def test_stack_backward_zero_rows_and_callback_failure():
+    announce("stack backward edge cases")
+    wl = inputs.Workload("bwd_small", "stack", B=1, T=5, D=64, dtype="bf16", L=6, S=3, seed=4)
+    ds = DeviceStack(wl, gains=True)
+    ds.forward()
+    dh = [torch.zeros((5, 64), dtype=torch.bfloat16, device="cuda") for _ in range(6)]
+    dy = torch.zeros((5, 64), dtype=torch.bfloat16, device="cuda")
+    dx, dv, dW, dG = b.attnres_block_stack_backward(ds.x, ds.v, ds.W, 3, dy, dh, block_sums=ds.block_sums,
+                                                    Gamma=ds.Gamma, eps=EPS)
+    torch.cuda.synchronize()
+    # a zero upstream gradient gives zero gradients
+    assert not torch.any(dx) and not any(torch.any(t) for t in dv)
+    assert not torch.any(dW) and not torch.any(dG)
+    # R == 0 writes zero query gradients
+    x0 = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    dW0 = torch.full((7, 64), 3.0, dtype=torch.float32, device="cuda")
+    b.attnres_block_stack_backward(x0, [x0] * 6, ds.W, 3, x0, [x0] * 6, block_sums=[x0] * 2, eps=EPS, dW=dW0,
+                                   dx=torch.empty((0, 64), dtype=torch.float32, device="cuda"),
+                                   dv=[torch.empty((0, 64), dtype=torch.float32, device="cuda") for _ in range(6)])
+    torch.cuda.synchronize()
+    assert not torch.any(dW0)
