@@ -307,6 +307,102 @@ def bench_backward(args, wl) -> dict:
     }
 
 
+def bench_stack_backward(args, wl) -> dict:
+    """One step = one attnres_block_stack_backward of the workload's stack
+    (its forward run once before, for the block sums) with seeded upstream
+    gradients dh_l and dy in the I/O dtype served from a table, fp32
+    gradients of x, every v_l and the queries written."""
+    import numpy as np
+    import torch
+
+    from depth_wise_attention_rms_amd import binding
+    from depth_wise_attention_rms_amd import inputs
+    from depth_wise_attention_rms_amd.workload import EPS, DeviceStack
+
+    ds = DeviceStack(wl)
+    ds.forward()
+    R, D, L = wl.R, wl.D, wl.L
+    dh = [inputs.fill_normal(torch.empty((R, D), dtype=ds.dt, device="cuda"), wl.seed + 1, inputs.ROLE_AUX, l, 1.0)
+          for l in range(L)]
+    dy = inputs.fill_normal(torch.empty((R, D), dtype=ds.dt, device="cuda"), wl.seed + 2, inputs.ROLE_AUX, 99, 1.0)
+    dx = torch.empty((R, D), dtype=torch.float32, device="cuda")
+    dv = [torch.empty((R, D), dtype=torch.float32, device="cuda") for _ in range(L)]
+    dW = torch.empty((L + 1, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(binding.attnres_stack_backward_workspace_bytes(L, wl.S, R, D, ds.dt), 256),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        binding.attnres_block_stack_backward(ds.x, ds.v, ds.W, wl.S, dy, dh, block_sums=ds.block_sums, eps=EPS,
+                                             dx=dx, dv=dv, dW=dW, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stride = max(1, args.steps // TIMED_STEPS)
+    instrumented = [i for i in range(args.steps) if i % stride == stride // 2][:TIMED_STEPS]
+    binding.attnres_timing_enable(len(instrumented) * (12 * L + 64))
+    binding.attnres_timing_pause(True)
+    binding.attnres_timing_reset()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        if i in instrumented:
+            binding.attnres_timing_pause(False)
+            step()
+            binding.attnres_timing_pause(True)
+        else:
+            step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    kinds = {}
+    for k in ("phase1", "phase1_stats", "close", "backward", "backward_reduce"):
+        cnt, ms, byts = binding.attnres_timing_read(k)
+        if cnt:
+            kinds[k] = {"kernel": binding.attnres_timing_kernels(k), "launches_per_step": cnt / len(instrumented),
+                        "avg_us": 1e3 * ms / cnt, "ms_per_step": ms / len(instrumented),
+                        "bytes_per_launch": byts / cnt, "GBps": byts / (ms * 1e6)}
+    binding.attnres_timing_enable(0)
+    step_bytes = sum(v["bytes_per_launch"] * v["launches_per_step"] for v in kinds.values())
+    dom_kind = max(kinds, key=lambda k: kinds[k]["ms_per_step"])
+    dom = kinds[dom_kind]
+    roofline = {"bound": "hbm", "kernel": dom["kernel"], "achieved": round(dom["GBps"], 1),
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(dom["GBps"] / PEAK_HBM_GBPS, 4),
+                "traffic": None, "bytes_per_launch": dom["bytes_per_launch"],
+                "avg_launch_us": round(dom["avg_us"], 2),
+                "timed_launches": int(round(dom["launches_per_step"] * len(instrumented))),
+                "timed_in": "timed region"}
+    return {
+        "metric": "tokens/s and achieved HBM GB/s (% of peak) for the Block AttnRes stack backward "
+                  "(two-phase schedule, recomputation, fp32 gradients)",
+        "value": round(R / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "gpu_ms_per_step": round(gpu_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded counter-based normals; inputs resident in HBM)",
+        "config": {"workload": f"stack_backward_{wl.name}", "B": wl.B, "T": wl.T, "D": D, "L": L, "S": wl.S,
+                   "global_batch": wl.B, "seq_len": wl.T, "parallelism": "single GPU"},
+        "achieved_GBps": round(step_bytes / (ms_per_step * 1e6), 1),
+        "hbm_frac": round(step_bytes / (ms_per_step * 1e6) / PEAK_HBM_GBPS, 4),
+        "bytes_per_step": step_bytes,
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kinds.items()},
+        "cpu_baseline": None,
+    }
+
+
 def bench_aggregate(args, wl) -> dict:
     """One step = the single-aggregate workload's two attnres_aggregate calls
     over its n sources (the N(0, 0.02^2) query, then the all-zero query), with
@@ -436,6 +532,8 @@ def main() -> int:
     ap.add_argument("--backward", type=int, default=0, metavar="N",
                     help="time the aggregate backward over N sources of the workload's shape instead "
                          "of the stack forward")
+    ap.add_argument("--stack-backward", action="store_true",
+                    help="time the stack backward through the two-phase schedule instead of the forward")
     ap.add_argument("--calibration-copy-gib", type=float, default=0.0,
                     help="before the steps, copy a tensor of this many GiB with torch (a plain "
                          "copy kernel of known size, read once and written once) so hardware "
@@ -468,6 +566,9 @@ def main() -> int:
     wl = inputs.WORKLOADS[args.workload]
     if args.backward:
         print(json.dumps(bench_backward(args, wl)), flush=True)
+        return 0
+    if args.stack_backward:
+        print(json.dumps(bench_stack_backward(args, wl)), flush=True)
         return 0
     if wl.kind == "aggregate":
         print(json.dumps(bench_aggregate(args, wl)), flush=True)

@@ -1276,7 +1276,11 @@ BwdStackLayout bwd_stack_layout(int L, int S, int64_t R, int64_t D, int dtype) {
       !attnres::phase1_mfma_eligible(dtype, 1, Sk, D))
     s.gbytes = attnres::phase1_gemm_workspace(Sk, R, D);
   off = align256(off + s.gbytes);
-  s.bw = off; off = align256(off + attnres::plan_aggregate_bwd(dtype, R, D).bytes);
+  {
+    const size_t a = attnres::plan_aggregate_bwd(dtype, R, D).bytes;
+    const size_t b = attnres::phase1_bwd_workspace(R, D);
+    s.bw = off; off = align256(off + (a > b ? a : b));
+  }
   s.total = off;
   return s;
 }
@@ -1457,10 +1461,33 @@ ATTNRES_API int attnres_block_stack_backward(
       TRY(callback(l - 1, dv[l - 2], &dh[j - 1]));
     }
     // Phase-1 backward: query j's output received a_j dh_j (dh_0 itself: h = o_0)
-    // and its log-sum-exp dlse_j; the gradients of b_0 .. b_k accumulate
-    for (int j = 0; j < Sk; ++j)
-      TRY(agg_bwd(b.data(), db.data(), n, start + j, dh[j], j ? A + (int64_t)j * R : nullptr,
-                  j ? DL + (int64_t)j * R : nullptr, 1, j ? 1 : 0));
+    // and its log-sum-exp dlse_j; the gradients of b_0 .. b_k accumulate. Up
+    // to 8 queries share one pass over the sources where the shape allows.
+    if (attnres::phase1_bwd_eligible(dtype, n, D)) {
+      constexpr int QB = 4;  // queries per pass
+      for (int j0 = 0; j0 < Sk; j0 += QB) {
+        const int Sq = Sk - j0 < QB ? Sk - j0 : QB;
+        const float* scl[QB];
+        const float* dls[QB];
+        int accq[QB];
+        for (int j = 0; j < Sq; ++j) {
+          scl[j] = j0 + j ? A + (int64_t)(j0 + j) * R : nullptr;
+          dls[j] = j0 + j ? DL + (int64_t)(j0 + j) * R : nullptr;
+          accq[j] = j0 + j ? 1 : 0;
+        }
+        const int l0 = start + j0;
+        attnres::Phase1BwdArgs pb{b.data(), n, R, D, Sq, dh.data() + j0, scl, dls, qrow(W, l0), qrow(Gamma, l0),
+                                  eps, db.data(), frow(dW, l0), frow(dGamma, l0), accq};
+        hipError_t e = attnres::launch_phase1_bwd(
+            pb, bw, timed_launch(K_BWD, rb * (n + Sq) + gb * n * 2, st, "phase1_bwd_kernel"),
+            timed_launch(K_BWD_REDUCE, (double)Sq * D * 4 * 2, st));
+        if (e != hipSuccess) return hip_fail(fn, e);
+      }
+    } else {
+      for (int j = 0; j < Sk; ++j)
+        TRY(agg_bwd(b.data(), db.data(), n, start + j, dh[j], j ? A + (int64_t)j * R : nullptr,
+                    j ? DL + (int64_t)j * R : nullptr, 1, j ? 1 : 0));
+    }
   }
   return ok();
 }

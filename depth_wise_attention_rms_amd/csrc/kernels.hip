@@ -1488,6 +1488,220 @@ __global__ __launch_bounds__(512) void merge_bwd_kernel(MergeBwdParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Batched Phase-1 backward [K3 9.4 step 1 and 9.1 (A1)-(A3) differentiated]:
+// the S queries of a block, each an aggregate over the same n sources, take
+// their gradients in one pass over the sources. Query j's output received
+// a_j dh_j (a_j the merge weight of its group, dh_j the upstream gradient of
+// its sublayer) and its log-sum-exp the merge's d lse_j. Per row and query,
+// with s_ji = q~_j . V_i / r_i, alpha = softmax_i(s_j), g_ji = a_j dh_j . V_i:
+//   ds_ji = alpha_ji (g_ji - sum_i alpha_ji g_ji + d lse_j)
+//   dV_i += sum_j [ alpha_ji a_j dh_j + (ds_ji / r_i) q~_j ]
+//           - (sum_j ds_ji s_ji / (D r_i^2)) V_i
+//   dq~_j += sum_i (ds_ji / r_i) V_i   (per-workgroup partial rows)
+// One workgroup row at a time, two 4-element vectors per lane (rows of at
+// most 2 x 64 x 8 vectors); the 2 S n + n row sums are reduced one query at a
+// time into an LDS table, from which every lane forms the (row-uniform,
+// scalar) coefficients.
+// Sources and upstream gradients are read once; each dV_i is read and written
+// once (added to), instead of once per query.
+// ---------------------------------------------------------------------------
+constexpr int kP1BwdQ = 4;  // queries per launch (their dq~ sums stay in registers)
+constexpr int kP1BwdVpl = 2;  // four-element vectors per lane
+constexpr int kP1BwdMaxN = 6;  // sources
+
+struct P1BwdParams {
+  const void* src[kP1BwdMaxN];
+  int n;
+  int S;
+  const void* dh[kP1BwdQ];
+  const float* dh_scale[kP1BwdQ];  // [R] or null (1)
+  const float* dlse[kP1BwdQ];      // [R] or null (0)
+  const float* w[kP1BwdQ];         // [D] each
+  const float* gm[kP1BwdQ];        // [D] or null
+  float eps;
+  float* dV[kP1BwdMaxN];           // [R][D] fp32, added to
+  float* partial;                  // [S][gridDim.x][D]
+  Geom g;
+};
+
+template <int NC>
+__global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
+  typedef Bf16x4 F;
+  typedef F::raw raw;
+  constexpr int VPL = kP1BwdVpl;
+  constexpr int NR = 3 * NC;  // per reduction: q~.V and dh.V for one query, V.V
+  extern __shared__ float lds[];  // row reduction scratch [W][NR]
+  __shared__ float tq[kP1BwdQ * NC], tg[kP1BwdQ * NC], tv[NC];
+  const Geom& g = p.g;
+  const int t = threadIdx.x, wr = t >> 6, stride = 64 * g.W;
+  const int64_t rowbytes = (int64_t)g.V * F::kBytes;
+  bool in_row[VPL];
+  int64_t voff[VPL];
+  #pragma unroll
+  for (int c = 0; c < VPL; ++c) {
+    const int vec = c * stride + t;
+    in_row[c] = vec < g.V;
+    voff[c] = (int64_t)(in_row[c] ? vec : 0) * F::kBytes;
+  }
+  float dq[kP1BwdQ][VPL][4];
+  #pragma unroll
+  for (int j = 0; j < kP1BwdQ; ++j)
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c)
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) dq[j][c][e] = 0.f;
+
+  for (int64_t row = blockIdx.x; row < g.R; row += gridDim.x) {
+    raw x[NC][VPL], d[kP1BwdQ][VPL];
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      #pragma unroll
+      for (int i = 0; i < NC; ++i)
+        x[i][c] = F::load(static_cast<const char*>(p.src[i]) + row * rowbytes + voff[c]);
+      #pragma unroll
+      for (int j = 0; j < kP1BwdQ; ++j)
+        d[j][c] = F::load(static_cast<const char*>(p.dh[j < p.S ? j : 0]) + row * rowbytes + voff[c]);
+    }
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c)
+      if (!in_row[c]) {  // lanes past the row's end hold zeros (their loads read vector 0)
+        #pragma unroll
+        for (int i = 0; i < NC; ++i) x[i][c] = F::zero();
+        #pragma unroll
+        for (int j = 0; j < kP1BwdQ; ++j) d[j][c] = F::zero();
+      }
+    // the row sums, one query per reduction; V.V with the first
+    for (int j = 0; j < p.S; ++j) {
+      float red[NR];
+      #pragma unroll
+      for (int k = 0; k < NR; ++k) red[k] = 0.f;
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        float q[4], dh[4];
+        load_query<4>(p.w[j], p.gm[j], voff[c] / F::kBytes * 4, q);
+        F::unpack(d[j][c], dh);
+        #pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          float xf[4];
+          F::unpack(x[i][c], xf);
+          #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            red[i] += q[e] * xf[e];
+            red[NC + i] += dh[e] * xf[e];
+            if (j == 0) red[2 * NC + i] += xf[e] * xf[e];
+          }
+        }
+      }
+      row_reduce<NR>(red, lds, 0, wr, g.W);
+      if (t == 0) {
+        #pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          tq[j * NC + i] = red[i];
+          tg[j * NC + i] = red[NC + i];
+          if (j == 0) tv[i] = red[2 * NC + i];
+        }
+      }
+    }
+    __syncthreads();  // the table is complete
+
+    // per-row coefficients are uniform: scalar registers
+    float ri[NC], cc[NC], acc[NC][VPL][4];
+    #pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      ri[i] = uniformf(rsqrtf(uniformf(tv[i]) * g.invD + p.eps));
+      cc[i] = 0.f;
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c)
+        #pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][c][e] = 0.f;
+    }
+    for (int j = 0; j < p.S; ++j) {
+      const float gs = p.dh_scale[j] ? p.dh_scale[j][row] : 1.f;
+      const float dl = p.dlse[j] ? p.dlse[j][row] : 0.f;
+      float sc[NC], al[NC];
+      float m = -FLT_MAX;
+      #pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        sc[i] = uniformf(uniformf(tq[j * NC + i]) * ri[i]);
+        m = fmaxf(m, sc[i]);
+      }
+      float z = 0.f;
+      #pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        al[i] = uniformf(__expf(sc[i] - m));
+        z += al[i];
+      }
+      const float rz = uniformf(1.0f / z);
+      float gbar = 0.f;
+      #pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        al[i] = uniformf(al[i] * rz);
+        gbar += al[i] * (gs * uniformf(tg[j * NC + i]));
+      }
+      gbar = uniformf(gbar);
+      float dqj[VPL][4];
+      float q[VPL][4], dh[VPL][4];
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        load_query<4>(p.w[j], p.gm[j], voff[c] / F::kBytes * 4, q[c]);
+        F::unpack(d[j][c], dh[c]);
+        #pragma unroll
+        for (int e = 0; e < 4; ++e) dqj[c][e] = 0.f;
+      }
+      #pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const float ds = al[i] * (gs * uniformf(tg[j * NC + i]) - gbar + dl);
+        const float A = uniformf(al[i] * gs), B = uniformf(ds * ri[i]);
+        cc[i] = uniformf(cc[i] + B * sc[i] * ri[i] * g.invD);
+        #pragma unroll
+        for (int c = 0; c < VPL; ++c) {
+          float xf[4];
+          F::unpack(x[i][c], xf);
+          #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[i][c][e] += A * dh[c][e] + B * q[c][e];
+            dqj[c][e] += B * xf[e];
+          }
+        }
+      }
+      // a query index is wave-uniform: unrolled selects keep dq in registers
+      #pragma unroll
+      for (int jj = 0; jj < kP1BwdQ; ++jj)
+        if (jj == j)
+          #pragma unroll
+          for (int c = 0; c < VPL; ++c)
+            #pragma unroll
+            for (int e = 0; e < 4; ++e) dq[jj][c][e] += dqj[c][e];
+    }
+    #pragma unroll
+    for (int i = 0; i < NC; ++i)
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        if (!in_row[c]) continue;
+        float* dst = p.dV[i] + row * g.D + voff[c] / F::kBytes * 4;
+        const uint4 u = ld16_stream(dst);
+        float xf[4];
+        F::unpack(x[i][c], xf);
+        float o[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
+        #pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] += acc[i][c][e] - cc[i] * xf[e];
+        st16_stream(dst, make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                                    __float_as_uint(o[3])));
+      }
+  }
+  #pragma unroll
+  for (int j = 0; j < kP1BwdQ; ++j)
+    if (j < p.S)
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c)
+        if (in_row[c]) {
+          float* prow = p.partial + ((int64_t)j * gridDim.x + blockIdx.x) * g.D + voff[c] / F::kBytes * 4;
+          st16(prow, make_uint4(__float_as_uint(dq[j][c][0]), __float_as_uint(dq[j][c][1]),
+                                __float_as_uint(dq[j][c][2]), __float_as_uint(dq[j][c][3])));
+        }
+}
+
 // Column sums of a [rows][D] fp32 matrix over consecutive row chunks, each in
 // ascending row order: out[k][d] = sum of in[r][d] for r in chunk k. With
 // FINISH the single chunk's sum t gives dw = t * gamma (t without a gain) and
@@ -2980,6 +3194,90 @@ hipError_t launch_bwd_reduce(const BwdArgs& a, const BwdPlan& pl, int stage, con
   return launch(L, bwd_colsum_kernel<true>, dim3(bx, 1), dim3(256), 0, in, rows, a.D, rows,
                 (float*)nullptr, a.w, a.g, a.dw, a.dgamma,
                 a.accumulate_q < 0 ? a.accumulate : a.accumulate_q);
+}
+
+#ifndef ATTNRES_P1BWD_GROUPS
+#define ATTNRES_P1BWD_GROUPS 256  // workgroups of the batched Phase-1 backward (each walks rows)
+#endif
+
+// up to 6 sources: beyond, the register budget of two vectors per lane spills
+bool phase1_bwd_eligible(int dtype, int n, int64_t D) {
+  const int64_t V = D / 4;
+  return dtype == 1 && n >= 1 && n <= kP1BwdMaxN && D % 4 == 0 && V <= 64 * 8 * kP1BwdVpl;
+}
+
+size_t phase1_bwd_workspace(int64_t R, int64_t D) {
+  const int64_t grid = R < ATTNRES_P1BWD_GROUPS ? (R > 0 ? R : 1) : ATTNRES_P1BWD_GROUPS;
+  const int64_t chunks = (grid + ATTNRES_BWD_CHUNK - 1) / ATTNRES_BWD_CHUNK;
+  return align256((size_t)kP1BwdQ * grid * D * 4) + align256((size_t)chunks * D * 4);
+}
+
+template <int NC>
+static hipError_t launch_p1bwd_t(const P1BwdParams& p, unsigned grid, const Launch& L) {
+  const size_t lds = (size_t)p.g.W * 3 * NC * sizeof(float);
+  return launch(L, phase1_bwd_kernel<NC>, dim3(grid), dim3(64 * p.g.W), lds, p);
+}
+
+hipError_t launch_phase1_bwd(const Phase1BwdArgs& a, void* ws, const Launch& L, const Launch& Lred) {
+  if (!phase1_bwd_eligible(1, a.n, a.D) || a.S < 1 || a.S > kP1BwdQ) return hipErrorInvalidValue;
+  if (a.R == 0) return hipSuccess;
+  P1BwdParams p;
+  for (int i = 0; i < kP1BwdMaxN; ++i) {
+    p.src[i] = i < a.n ? a.src[i] : a.src[0];
+    p.dV[i] = i < a.n ? a.dV[i] : nullptr;
+  }
+  p.n = a.n; p.S = a.S; p.eps = a.eps;
+  for (int j = 0; j < kP1BwdQ; ++j) {
+    const int jj = j < a.S ? j : 0;
+    p.dh[j] = a.dh[jj];
+    p.dh_scale[j] = j < a.S ? a.dh_scale[j] : nullptr;
+    p.dlse[j] = j < a.S ? a.dlse[j] : nullptr;
+    p.w[j] = a.w + (int64_t)jj * a.D;
+    p.gm[j] = a.g ? a.g + (int64_t)jj * a.D : nullptr;
+  }
+  const unsigned grid = (unsigned)(a.R < ATTNRES_P1BWD_GROUPS ? a.R : ATTNRES_P1BWD_GROUPS);
+  p.partial = static_cast<float*>(ws);
+  p.g = make_geom(a.R, a.D, 4, kP1BwdVpl, 1);  // four-element vectors (V = D / 4)
+  p.g.RPW = 1;
+  p.g.groups = a.R;
+  hipError_t e;
+  switch (a.n) {
+    case 1: e = launch_p1bwd_t<1>(p, grid, L); break;
+    case 2: e = launch_p1bwd_t<2>(p, grid, L); break;
+    case 3: e = launch_p1bwd_t<3>(p, grid, L); break;
+    case 4: e = launch_p1bwd_t<4>(p, grid, L); break;
+    case 5: e = launch_p1bwd_t<5>(p, grid, L); break;
+    default: e = launch_p1bwd_t<6>(p, grid, L); break;
+  }
+  if (e != hipSuccess) return e;
+  // each query's partial rows [grid][D] -> dw, dgamma (written or added)
+  float* stage1 = reinterpret_cast<float*>(static_cast<char*>(ws) + align256((size_t)kP1BwdQ * grid * a.D * 4));
+  const unsigned bx = (unsigned)((a.D / 4 + 255) / 256);
+  const int64_t chunk = ATTNRES_BWD_CHUNK;
+  const int64_t P2 = grid > chunk ? ((int64_t)grid + chunk - 1) / chunk : 0;
+  // timed from the first reduction's start to the last one's end
+  const Launch first{Lred.stream, Lred.start, nullptr}, mid{Lred.stream, nullptr, nullptr};
+  for (int j = 0; j < a.S; ++j) {
+    const Launch& L0 = j == 0 ? first : mid;
+    const Launch L1{Lred.stream, nullptr, j + 1 == a.S ? Lred.stop : nullptr};
+    const Launch& L1a = (j == 0 && !P2) ? Launch{Lred.stream, Lred.start, L1.stop} : L1;
+    const float* part = p.partial + (int64_t)j * grid * a.D;
+    const float* wj = a.w + (int64_t)j * a.D;
+    const float* gj = a.g ? a.g + (int64_t)j * a.D : nullptr;
+    float* dwj = a.dw + (int64_t)j * a.D;
+    float* dgj = a.dgamma ? a.dgamma + (int64_t)j * a.D : nullptr;
+    if (P2) {
+      e = launch(L0, bwd_colsum_kernel<false>, dim3(bx, (unsigned)P2), dim3(256), 0, part, (int64_t)grid, a.D,
+                 chunk, stage1, (const float*)nullptr, (const float*)nullptr, (float*)nullptr, (float*)nullptr, 0);
+      if (e != hipSuccess) return e;
+    }
+    const float* in = P2 ? stage1 : part;
+    const int64_t rows = P2 ? P2 : grid;
+    e = launch(L1a, bwd_colsum_kernel<true>, dim3(bx, 1), dim3(256), 0, in, rows, a.D, rows, (float*)nullptr,
+               wj, gj, dwj, dgj, a.accumulate_q[j]);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <class F, int VPL>

@@ -142,6 +142,32 @@ hipError_t launch_aggregate_bwd(int dtype, const BwdArgs& a, const BwdPlan& pl, 
 hipError_t launch_bwd_reduce(const BwdArgs& a, const BwdPlan& pl, int stage, const Launch& L);
 hipError_t launch_merge_bwd(int dtype, const MergeBwdArgs& a, const BwdPlan& pl, const Launch& L);
 
+// Batched Phase-1 backward: S <= 4 queries (consecutive rows of w, g, dw,
+// dgamma) over the same n <= 6 bf16 sources in one pass; query j's upstream
+// gradient is dh_scale[j][r] * dh[j][r] (dh_scale[j] null: 1) and its
+// log-sum-exp's gradient dlse[j] (null: 0). dV[i] fp32 are added to; dw /
+// dgamma rows are written (accumulate_q[j] == 0) or added. Rows of at most
+// 4096 elements (phase1_bwd_eligible). `ws` holds phase1_bwd_workspace bytes.
+struct Phase1BwdArgs {
+  const void* const* src;
+  int n;
+  int64_t R, D;
+  int S;
+  const void* const* dh;
+  const float* const* dh_scale;
+  const float* const* dlse;
+  const float* w;   // [S][D]
+  const float* g;   // [S][D] or null
+  float eps;
+  float* const* dV;
+  float* dw;        // [S][D]
+  float* dgamma;    // [S][D] or null
+  const int* accumulate_q;  // [S]
+};
+bool phase1_bwd_eligible(int dtype, int n, int64_t D);
+size_t phase1_bwd_workspace(int64_t R, int64_t D);
+hipError_t launch_phase1_bwd(const Phase1BwdArgs& a, void* ws, const Launch& L, const Launch& Lred);
+
 hipError_t launch_fold(const float* w, const float* g, float* q, int64_t count, const Launch& L);
 hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L);
 // Phase 1 as a matrix-core scores pass and an outputs pass (bf16, n <= 8,
