@@ -182,9 +182,17 @@ int do_close(const char* fn, const void* p, const void* v, void* b, int64_t R, i
   return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
 }
 
+int do_rmsnorm(const char* fn, int dtype, const void* x, int64_t R, int64_t D, const float* g,
+               float eps, void* out, hipStream_t st);
+
 int do_phase1(const char* fn, int dtype, const Phase1Args& a, hipStream_t st) {
   if (a.R == 0) return ATTNRES_OK;
   const int64_t row_bytes = a.D * esize_of(dtype);
+  // output 0's input norm, where the kernel that runs does not write it
+  auto norm_after = [&]() -> int {
+    if (!a.nf_out) return ATTNRES_OK;
+    return do_rmsnorm(fn, dtype, a.out ? a.out : a.src[0], a.R, a.D, a.nf_g, a.nf_eps, a.nf_out, st);
+  };
   if (a.gemm_ws && attnres::phase1_gemm_eligible(dtype, a.n, a.S, a.D, a.R)) {
     // the scores pass reads materialised sources: close first
     if (a.close_v) TRY(do_close(fn, a.close_p, a.close_v, a.close_b, a.R, a.D, dtype, st));
@@ -197,16 +205,21 @@ int do_phase1(const char* fn, int dtype, const Phase1Args& a, hipStream_t st) {
     hipError_t e = attnres::launch_phase1_gemm(
         g, a.gemm_ws, timed_launch(a.out ? K_PHASE1 : K_PHASE1_STATS, bytes, st,
                                    attnres::phase1_kernel_name(dtype, g, true)));
-    return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return norm_after();
   }
   if (attnres::phase1_supported(dtype, a.n, a.S, a.D)) {
+    const bool fused = a.nf_out && attnres::phase1_norm_fused(dtype, a, false);
+    Phase1Args b = a;
+    if (!fused) b.nf_out = nullptr;
     const double rb = (double)a.R * row_bytes;
-    const double bytes = rb * (a.n + (a.out ? a.S : 0)) + (double)a.R * a.S * ((a.m_out ? 4 : 0) + 4) +
-                         close_bytes(rb, a.close_p, a.close_v);
+    const double bytes = rb * (a.n + (a.out ? a.S : 0) + (fused && !a.out ? 1 : 0)) +
+                         (double)a.R * a.S * ((a.m_out ? 4 : 0) + 4) + close_bytes(rb, a.close_p, a.close_v);
     hipError_t e = attnres::launch_phase1(
-        dtype, a, timed_launch(a.out ? K_PHASE1 : K_PHASE1_STATS, bytes, st,
+        dtype, b, timed_launch(a.out ? K_PHASE1 : K_PHASE1_STATS, bytes, st,
                                attnres::phase1_kernel_name(dtype, a, false)));
-    return e == hipSuccess ? ATTNRES_OK : hip_fail(fn, e);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return fused ? ATTNRES_OK : norm_after();
   }
   // More sources than the register-resident pass holds: close separately,
   // then one aggregate per query.
@@ -216,6 +229,11 @@ int do_phase1(const char* fn, int dtype, const Phase1Args& a, hipStream_t st) {
               a.eps, static_cast<char*>(a.out) + (int64_t)s * a.R * row_bytes,
               a.m_out ? a.m_out + (int64_t)s * a.R : nullptr, a.lse_out + (int64_t)s * a.R,
               nullptr, nullptr, nullptr};
+    if (s == 0) {  // the aggregate kernel writes output 0's input norm itself
+      g.nf_g = a.nf_g;
+      g.nf_eps = a.nf_eps;
+      g.nf_out = a.nf_out;
+    }
     TRY(do_aggregate(fn, dtype, g, st));
   }
   return ATTNRES_OK;
@@ -588,12 +606,6 @@ int stack_forward(const char* fn, const void* x, int L, int S, int64_t R, int64_
   const float* Q = nullptr;
   TRY(fold_queries(fn, W, Gamma, L, D, reinterpret_cast<float*>(ws + lay.q), st, &Q));
 
-  // the sublayer's input: h_l, or RMSNorm(h_l) * Gamma_f[l-1] written to H
-  // (in place when h_l is already in H)
-  auto normed = [&](int l, const void* h) -> int {
-    return do_rmsnorm(fn, dtype, h, R, D, nm.Gamma_f ? nm.Gamma_f + (int64_t)(l - 1) * D : nullptr,
-                      nm.eps_f, H, st);
-  };
   auto call = [&](int l, const void* h, const void** v) -> int {
     const void* out = nullptr;
     const int rc = f(f_ctx, l, h, &out, stream);
@@ -625,8 +637,12 @@ int stack_forward(const char* fn, const void* x, int L, int S, int64_t R, int64_
       // a one-sublayer block: a single aggregate over the completed sources
       AggArgs a{src.data(), n, R, D, Qk, nullptr, eps, H, nullptr, nullptr,
                 close_p, close_v, close_b};
+      if (nm.on) {  // the aggregate writes its sublayer's input norm to H itself
+        a.nf_g = nm.Gamma_f ? nm.Gamma_f + (int64_t)(start - 1) * D : nullptr;
+        a.nf_eps = nm.eps_f;
+        a.nf_out = H;
+      }
       TRY(do_aggregate(fn, dtype, a, st));
-      if (nm.on) TRY(normed(start, H));
       const void* v = nullptr;
       TRY(call(start, H, &v));
       if (block_sums) {  // b_{k+1} = v, copied by the next launch
@@ -650,14 +666,15 @@ int stack_forward(const char* fn, const void* x, int L, int S, int64_t R, int64_
     };
     Phase1Args a1{src.data(), n, R, D, Qk, nullptr, Sk, eps, one_source ? nullptr : O, M, LSE,
                   close_p, close_v, close_b, lay.g < lay.total ? ws + lay.g : nullptr};
+    if (nm.on) {  // output 0's input norm to H, fused where the Phase-1 kernel allows
+      a1.nf_g = nm.Gamma_f ? nm.Gamma_f + (int64_t)(start - 1) * D : nullptr;
+      a1.nf_eps = nm.eps_f;
+      a1.nf_out = H;
+    }
     TRY(do_phase1(fn, dtype, a1, st));
     const void* v_first = nullptr;
-    if (nm.on) {
-      TRY(normed(start, o_slice(0)));
-      TRY(call(start, H, &v_first));
-    } else {
-      TRY(call(start, o_slice(0), &v_first));  // h_start = o_0: no partial yet
-    }
+    // h_start = o_0: no partial yet
+    TRY(call(start, nm.on ? H : o_slice(0), &v_first));
     const void* p_cur = v_first;    // p_1 = v_start (aliased, no copy)
     const void* v_prev = v_first;
     for (int j = 1; j < Sk; ++j) {
@@ -816,9 +833,13 @@ int stack_forward_overlap(const char* fn, const void* x, int L, int S, int64_t R
 
   const float* Q = nullptr;
   TRY(fold_queries(fn, W, Gamma, L, D, reinterpret_cast<float*>(ws + lay.q), st, &Q));
-  auto normed = [&](int l, const void* h) -> int {
-    return do_rmsnorm(fn, dtype, h, R, D, nm.Gamma_f ? nm.Gamma_f + (int64_t)(l - 1) * D : nullptr,
-                      nm.eps_f, H, st);
+  // with the norm, a block's first launch writes its first sublayer's input
+  // norm RMSNorm(h) * Gamma_f[l-1] to H itself
+  auto with_norm = [&](int l, auto& args) {
+    if (!nm.on) return;
+    args.nf_g = nm.Gamma_f ? nm.Gamma_f + (int64_t)(l - 1) * D : nullptr;
+    args.nf_eps = nm.eps_f;
+    args.nf_out = H;
   };
   auto call = [&](int l, const void* h, const void** v) -> int {
     const void* out = nullptr;
@@ -843,7 +864,7 @@ int stack_forward_overlap(const char* fn, const void* x, int L, int S, int64_t R
   // (for k == 0, over [b_0] on the main stream). Returns, through one_source,
   // whether the outputs were elided (one source: each output is b_0 itself).
   bool one_src[2] = {false, false};
-  auto phase1_into_slot = [&](int k, int n, hipStream_t on) -> int {
+  auto phase1_into_slot = [&](int k, int n, hipStream_t on, bool norm0 = false) -> int {
     int start, Sk;
     block_range(k, &start, &Sk);
     const int b = k & 1;
@@ -861,6 +882,7 @@ int stack_forward_overlap(const char* fn, const void* x, int L, int S, int64_t R
                   nullptr, nullptr, nullptr, gemm_ws};
     // off the critical path, Phase 1 leaves most of the chip to the main stream
     if (on != st) a1.max_groups = ATTNRES_OVERLAP_SIDE_GROUPS;
+    if (norm0) with_norm(start, a1);
     return do_phase1(fn, dtype, a1, on);
   };
   auto o_slice = [&](int k, int j) -> const void* {
@@ -882,9 +904,10 @@ int stack_forward_overlap(const char* fn, const void* x, int L, int S, int64_t R
       // block exists) the side stream starts block 1's Phase 1 over [b_0]
       if (Sk == 1) {
         AggArgs a{src.data(), 1, R, D, Q, nullptr, eps, H, nullptr, nullptr, nullptr, nullptr, nullptr};
+        with_norm(start, a);
         TRY(do_aggregate(fn, dtype, a, st));
       } else {
-        TRY(phase1_into_slot(0, 1, st));
+        TRY(phase1_into_slot(0, 1, st, true));
       }
       if (nb > 1) {
         TRY(hip_ok(hipEventRecord(ev->main_ready, st)));
@@ -900,6 +923,7 @@ int stack_forward_overlap(const char* fn, const void* x, int L, int S, int64_t R
       xs = block_sums[k - 1];
       AggArgs am{src.data() + k, 1, R, D, Q + (int64_t)(start - 1) * D, nullptr, eps, H, nullptr,
                  nullptr, close_p, close_v, block_sums[k - 1], o_slice(k, 0), lse_slice(k, 0)};
+      with_norm(start, am);
       TRY(do_aggregate(fn, dtype, am, st));
       if (k + 1 < nb) {
         // b_k is stored and slot (k+1) & 1 was last read by block k-1:
@@ -910,14 +934,9 @@ int stack_forward_overlap(const char* fn, const void* x, int L, int S, int64_t R
         TRY(hip_ok(hipEventRecord(ev->side_done, side)));
       }
     }
-    const void* h0 = (k == 0 && Sk > 1) ? o_slice(0, 0) : H;
+    const void* h0 = (k == 0 && Sk > 1 && !nm.on) ? o_slice(0, 0) : H;
     const void* v_first = nullptr;
-    if (nm.on) {
-      TRY(normed(start, h0));
-      TRY(call(start, H, &v_first));
-    } else {
-      TRY(call(start, h0, &v_first));
-    }
+    TRY(call(start, h0, &v_first));
     const void* p_cur = v_first;
     const void* v_prev = v_first;
     for (int j = 1; j < Sk; ++j) {

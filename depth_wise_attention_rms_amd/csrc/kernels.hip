@@ -139,6 +139,9 @@ struct Phase1Params {
   float* m_out;     // [S][R] or null
   float* lse_out;   // [S][R]
   Close cl;         // close computing source n-1, or cl.v == null
+  const float* nf_g = nullptr;  // the sublayer input norm of output 0 (see Phase1Args::nf_out)
+  float nf_eps = 0.f;
+  void* nf_out = nullptr;
   Geom g;
 };
 
@@ -327,6 +330,23 @@ __global__ __launch_bounds__(512) void phase1_single_kernel(Phase1Params p) {
       }
     }
     row_reduce<NV>(red, lds, ln.slot, ln.wr, g.W);
+    if (p.nf_out && row < g.R) {
+      // output 0 is the source itself: its sublayer's input norm, from the
+      // same sum of squares [ZZ block listing: attn(attn_norm(h))]
+      const float inv = rsqrtf(red[SQ] * g.invD + p.nf_eps);
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        const int vec = c * ln.stride + ln.t;
+        if (vec < g.V) {
+          float x[EPV], gn[EPV];
+          T::unpack(cur[c], x);
+          load_gain<EPV>(p.nf_g, (int64_t)vec * EPV, gn);
+          #pragma unroll
+          for (int e = 0; e < EPV; ++e) x[e] = gn[e] * (x[e] * inv);
+          st16(static_cast<char*>(p.nf_out) + row * rowbytes + (int64_t)vec * 16, T::pack(x));
+        }
+      }
+    }
     if (row < g.R && ln.t < SQ && ln.t < p.S) {
       // lane s writes query s's statistics
       float dot = red[0];
@@ -364,9 +384,9 @@ __global__ __launch_bounds__(512) void phase1_single_kernel(Phase1Params p) {
 // column hit different banks. A fused block close stages its p and v rows and
 // forms b = round(p + v) in place before the row is scored. At D = 4096 each
 // wave copies, scores and writes only its own slice, so a row needs a single
-// barrier (for the cross-wave score reduction). The outputs are written with
-// plain stores, the copies are non-temporal: with non-temporal output stores
-// the kernel ran about 10% slower.
+// barrier (for the cross-wave score reduction). The copies are
+// non-temporal; the outputs are written with plain stores for the first two
+// and non-temporal ones after (ATTNRES_P1_OUT_NT_FROM).
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
@@ -852,6 +872,9 @@ struct AggParams {
   Close cl;        // close computing source n-1, or cl.v == null
   const void* o_init;     // [R][D] normalised output of an earlier group, or null
   const float* lse_init;  // [R] its log-sum-exp
+  const float* nf_g = nullptr;  // with nf_out: the output is written as its sublayer's
+  float nf_eps = 0.f;           // input norm to nf_out (and not to out)
+  void* nf_out = nullptr;
   Geom g;
 };
 
@@ -997,7 +1020,40 @@ __global__ __launch_bounds__(512) void aggregate_kernel(AggParams p) {
         }
       m_run = m_new;
     }
-    if (rv) {
+    if (p.nf_out) {
+      // the sublayer input norm of the rounded output [ZZ block listing:
+      // attn(attn_norm(h))]: its sum of squares over the row, then gamma_f h / rms
+      const float rz = 1.0f / z_run;
+      uint4 hv[VPL];
+      float hss[1] = {0.f};
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        float o[EPV];
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) o[e] = num[c][e] * rz;
+        hv[c] = T::pack(o);
+        T::unpack(hv[c], o);
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) hss[0] += in_row[c] ? o[e] * o[e] : 0.f;
+      }
+      row_reduce<1>(hss, lds, ln.slot, ln.wr, g.W);
+      if (rv) {
+        const float inv = rsqrtf(hss[0] * g.invD + p.nf_eps);
+        char* orow = static_cast<char*>(p.nf_out) + row * rowbytes;
+        #pragma unroll
+        for (int c = 0; c < VPL; ++c) {
+          const int vec = c * ln.stride + ln.t;
+          if (vec < g.V) {
+            float o[EPV], gn[EPV];
+            T::unpack(hv[c], o);
+            load_gain<EPV>(p.nf_g, (int64_t)vec * EPV, gn);
+            #pragma unroll
+            for (int e = 0; e < EPV; ++e) o[e] = gn[e] * (o[e] * inv);
+            st16(orow + (int64_t)vec * 16, T::pack(o));
+          }
+        }
+      }
+    } else if (rv) {
       const float rz = 1.0f / z_run;
       char* orow = static_cast<char*>(p.out) + row * rowbytes;
       #pragma unroll
@@ -1010,10 +1066,10 @@ __global__ __launch_bounds__(512) void aggregate_kernel(AggParams p) {
           st16_stream(orow + (int64_t)vec * 16, T::pack(o));
         }
       }
-      if (ln.t == 0) {
-        if (p.m_out) p.m_out[row] = m_run;
-        if (p.lse_out) p.lse_out[row] = m_run + __logf(z_run);
-      }
+    }
+    if (rv && ln.t == 0) {
+      if (p.m_out) p.m_out[row] = m_run;
+      if (p.lse_out) p.lse_out[row] = m_run + __logf(z_run);
     }
   }
 }
@@ -2664,6 +2720,7 @@ static hipError_t launch_phase1_single(const Phase1Args& a, const Launch& L) {
   p.n = a.n; p.S = a.S; p.Wq = a.W; p.G = a.G; p.eps = a.eps;
   p.out = nullptr; p.m_out = a.m_out; p.lse_out = a.lse_out;
   p.cl = Close{nullptr, nullptr, nullptr};
+  p.nf_g = a.nf_g; p.nf_eps = a.nf_eps; p.nf_out = a.nf_out;
   p.g = make_geom(a.R, a.D, T::kBytes, ATTNRES_P1_SINGLE_VPL, 4);
   const size_t lds = p.g.W > 1 ? (size_t)p.g.RPW * p.g.W * 9 * sizeof(float) : 0;
   const int64_t grid = p.g.groups < ATTNRES_P1_SINGLE_GROUPS ? p.g.groups : ATTNRES_P1_SINGLE_GROUPS;
@@ -2897,6 +2954,14 @@ hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L) {
   return dtype == 1 ? launch_phase1_dt<Bf16>(a, L) : launch_phase1_dt<F32>(a, L);
 }
 
+// Only the one-source statistics kernel writes the norm itself: it holds the
+// source and its sum of squares anyway. In the register-tile kernel the
+// cross-wave sum of output 0's squares cost more time per row (a barrier, or
+// registers held across rows) than the separate pass it would save.
+bool phase1_norm_fused(int dtype, const Phase1Args& a, bool gemm) {
+  return !gemm && phase1_single_eligible(dtype, a);
+}
+
 const char* phase1_kernel_name(int dtype, const Phase1Args& a, bool gemm) {
   if (gemm) return a.out ? "phase1_gemm_scores_kernel+phase1_gemm_outputs_kernel" : "phase1_gemm_scores_kernel";
   if (phase1_single_eligible(dtype, a)) return "phase1_single_kernel";
@@ -2933,6 +2998,7 @@ static hipError_t launch_aggregate_dt(const AggArgs& a, const Launch& L) {
   p.out = a.out; p.m_out = a.m_out; p.lse_out = a.lse_out;
   p.cl = Close{a.close_p, a.close_v, a.close_b};
   p.o_init = a.o_init; p.lse_init = a.lse_init;
+  p.nf_g = a.nf_g; p.nf_eps = a.nf_eps; p.nf_out = a.nf_out;
   p.g = make_geom(a.R, a.D, T::kBytes, 2, 4);
   if (p.g.W > 8) {
     // widest rows: four vectors per lane and groups of four sources

@@ -38,6 +38,13 @@ struct Phase1Args {
   // the streamed kernel's workgroup budget per launch (0: its default); a
   // smaller one runs query passes one after another instead of side by side
   int max_groups = 0;
+  // with nf_out: output 0 (the block's first sublayer's h, or the source
+  // itself when out is null) is also written as that sublayer's input norm
+  // round(nf_g * h / sqrt(mean_d h^2 + nf_eps)) to nf_out -- by the kernels
+  // phase1_norm_fused() names; output 0 itself is then not written
+  const float* nf_g = nullptr;
+  float nf_eps = 0.f;
+  void* nf_out = nullptr;
 };
 
 struct AggArgs {
@@ -57,6 +64,11 @@ struct AggArgs {
   // and its log-sum-exp [R] (both null: start empty)
   const void* o_init = nullptr;
   const float* lse_init = nullptr;
+  // with nf_out: the output is written as its sublayer's input norm
+  // round(nf_g * h / sqrt(mean_d h^2 + nf_eps)) to nf_out instead of to out
+  const float* nf_g = nullptr;
+  float nf_eps = 0.f;
+  void* nf_out = nullptr;
 };
 
 struct Phase2Args {
@@ -181,6 +193,9 @@ bool phase1_gemm_eligible(int dtype, int n, int S, int64_t D, int64_t R);
 size_t phase1_gemm_workspace(int S, int64_t R, int64_t D);
 hipError_t launch_phase1_gemm(const Phase1Args& a, void* ws, const Launch& L);
 bool phase1_supported(int dtype, int n, int S, int64_t D);
+// whether the kernel a Phase-1 launch runs writes the input norm of output 0
+// itself (Phase1Args::nf_out)
+bool phase1_norm_fused(int dtype, const Phase1Args& a, bool gemm);
 // name of the kernel(s) a Phase-1 launch runs (gemm: the scores/outputs path)
 const char* phase1_kernel_name(int dtype, const Phase1Args& a, bool gemm);
 // Phase 1 with out == null (statistics only) is available for these shapes
