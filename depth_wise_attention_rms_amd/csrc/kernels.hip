@@ -3124,12 +3124,16 @@ hipError_t launch_rmsnorm(int dtype, const void* x, int64_t R, int64_t D, const 
                     : launch_rmsnorm_dt<F32>(x, R, D, g, eps, out, L);
 }
 
+#ifndef ATTNRES_CLOSE_MAX_GROUPS
+#define ATTNRES_CLOSE_MAX_GROUPS (1 << 20)  // workgroups of a standalone close: one vector per lane (grid-stride beyond)
+#endif
+
 hipError_t launch_close(int dtype, const void* p, const void* v, void* b, int64_t R, int64_t D,
                         const Launch& L) {
   const int64_t nvec = R * D * (dtype == 1 ? 2 : 4) / 16;
   if (nvec == 0) return hipSuccess;
   int64_t blocks = (nvec + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
+  if (blocks > ATTNRES_CLOSE_MAX_GROUPS) blocks = ATTNRES_CLOSE_MAX_GROUPS;
   if (dtype == 1) return launch(L, close_kernel<Bf16>, dim3((unsigned)blocks), dim3(256), 0, p, v, b, nvec);
   return launch(L, close_kernel<F32>, dim3((unsigned)blocks), dim3(256), 0, p, v, b, nvec);
 }
