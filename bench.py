@@ -48,13 +48,17 @@ def kernels_digest() -> str:
     return h.hexdigest()
 
 
-def traffic_paths(backward: int):
+def traffic_paths(backward: int, workload: str = "block_L48_S8"):
     """(summary JSON, table, dominant kernel, bench arguments) of a measured workload."""
     if backward:
         stem = f"aggregate_backward_n{backward}_block_L48_S8"
         return (os.path.join(ROOT, "profiles", f"{stem}_traffic.json"),
                 os.path.join(ROOT, "profiles", f"{stem}_hbm_traffic.txt"),
                 "attnres::aggregate_bwd_kernel", f"--backward {backward} ")
+    if workload != "block_L48_S8":
+        return (os.path.join(ROOT, "profiles", f"phase2_{workload}_traffic.json"),
+                os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.txt"), DOMINANT,
+                f"--workload {workload} ")
     return TRAFFIC_FILE, TRAFFIC_TABLE, DOMINANT, ""
 
 
@@ -63,7 +67,7 @@ def measured_traffic(workload: str, backward: int = 0):
     summary, or None when it is absent, for another workload, or older than
     the kernels."""
     try:
-        with open(traffic_paths(backward)[0]) as f:
+        with open(traffic_paths(backward, workload)[0]) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -81,7 +85,7 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_gib: float
     import csv
     import re
 
-    traffic_file, table_file, dominant, bench_args = traffic_paths(backward)
+    traffic_file, table_file, dominant, bench_args = traffic_paths(backward, workload)
 
     def per_kernel(path, counter):
         d = {}
