@@ -150,6 +150,7 @@ def cpu_baseline(ds, wl, seconds: float, chunk: int = 2048) -> dict:
     if not os.path.exists(oracle.LIBRARY):
         oracle.build()
     cores, host = oracle_threads()
+    chunk = min(chunk, wl.R)
     done, spent, start = 0, 0.0, 0
     while done == 0 or spent < seconds:
         rows = np.arange(start, min(start + chunk, wl.R))
@@ -161,8 +162,9 @@ def cpu_baseline(ds, wl, seconds: float, chunk: int = 2048) -> dict:
         done += len(rows)
         del xr, vr
     return {"value": round(done / spent, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle", **host,
-            "sample": f"{done} token rows in chunks of {chunk} consecutive rows cycling over the "
-                      f"{wl.R} of the workload, full {wl.L}-sublayer naive forward in fp64 "
+            "sample": (f"{done} token rows in chunks of {chunk} consecutive rows cycling over the "
+                       if chunk < wl.R else f"{done} token rows: the workload's {wl.R} rows repeated, ") +
+                      f"full {wl.L}-sublayer naive forward in fp64 "
                       f"({cores} threads), {spent:.2f} s of CPU time (host copies excluded)"}
 
 
