@@ -310,12 +310,12 @@ StackLayout stack_layout(int L, int S, int64_t R, int64_t D, int es) {
   s.lse = off; off = align256(off + (size_t)Sk * R * sizeof(float));
   s.p = off; off = align256(off + (Sk > 2 ? row : 0));
   s.h = off; off = align256(off + row);
-  // the scores/outputs Phase 1 (query parts and softmax weights) where the
-  // widest block's shape takes it
+  // the scores/outputs Phase 1 (query parts and softmax weights) where some
+  // block's Phase 1 takes it (block k scores over k sources, up to nb)
   s.g = off;
-  if (Sk > 1 && attnres::phase1_gemm_shape(es == 2 ? 1 : 0, Sk, D, R) &&
-      !attnres::phase1_mfma_eligible(es == 2 ? 1 : 0, 1, Sk, D))
-    off = align256(off + attnres::phase1_gemm_workspace(Sk, R, D));
+  const int nb = plan(L, S, nullptr, nullptr);
+  if (attnres::phase1_gemm_needed(es == 2 ? 1 : 0, Sk, D, R, nb))
+    off = align256(off + attnres::phase1_gemm_workspace(Sk, R, D, nb));
   s.total = off;
   return s;
 }
@@ -737,9 +737,9 @@ OverlapLayout overlap_layout(int L, int S, int64_t R, int64_t D, int es) {
   s.p = off; off = align256(off + (Sk > 2 ? row : 0));
   s.h = off; off = align256(off + row);
   s.g = off;
-  if (Sk > 1 && attnres::phase1_gemm_shape(es == 2 ? 1 : 0, Sk, D, R) &&
-      !attnres::phase1_mfma_eligible(es == 2 ? 1 : 0, 1, Sk, D))
-    off = align256(off + attnres::phase1_gemm_workspace(Sk, R, D));
+  const int nb = plan(L, S, nullptr, nullptr);
+  if (attnres::phase1_gemm_needed(es == 2 ? 1 : 0, Sk, D, R, nb))
+    off = align256(off + attnres::phase1_gemm_workspace(Sk, R, D, nb));
   s.total = off;
   return s;
 }
@@ -971,7 +971,7 @@ int stack_forward_overlap(const char* fn, const void* x, int L, int S, int64_t R
 // the chunk merges that summary with the j outputs produced inside the
 // chunk so far, each its own softmax term (OS2 over individual sources).
 struct FullLayout {
-  size_t q, o, m, lse, h, total;
+  size_t q, o, m, lse, h, g, total;
 };
 
 FullLayout full_layout(int L, int C, int64_t R, int64_t D, int es) {
@@ -984,6 +984,14 @@ FullLayout full_layout(int L, int C, int64_t R, int64_t D, int es) {
   f.m = off; off = align256(off + (size_t)Ck * R * sizeof(float));
   f.lse = off; off = align256(off + (size_t)Ck * R * sizeof(float));
   f.h = off; off = align256(off + row);
+  // the scores/outputs Phase 1 where some chunk takes it: the chunk from
+  // sublayer s0 scores over s0 sources
+  f.g = off;
+  int nmax = 0;
+  for (int s0 = 1; s0 <= L; s0 += C)
+    if (L - s0 + 1 >= 2 && C >= 2) nmax = s0;
+  if (nmax > 0 && attnres::phase1_gemm_needed(es == 2 ? 1 : 0, Ck, D, R, nmax))
+    off = align256(off + attnres::phase1_gemm_workspace(Ck, R, D, nmax));
   f.total = off;
   return f;
 }
@@ -1052,6 +1060,7 @@ ATTNRES_API int attnres_full_stack_forward(const void* x, int L, int C, int64_t 
   float* M = reinterpret_cast<float*>(ws + lay.m);
   float* LSE = reinterpret_cast<float*>(ws + lay.lse);
   void* H = ws + lay.h;
+  void* gemm_ws = lay.g < lay.total ? ws + lay.g : nullptr;
   const int64_t tensor_bytes = R * D * es;
   const float* Q = nullptr;
   TRY(fold_queries(fn, W, Gamma, L, D, reinterpret_cast<float*>(ws + lay.q), st, &Q));
@@ -1089,7 +1098,7 @@ ATTNRES_API int attnres_full_stack_forward(const void* x, int L, int C, int64_t 
       return one_source ? src[0] : static_cast<const void*>(O + (int64_t)j * tensor_bytes);
     };
     Phase1Args a1{src.data(), n, R, D, Qk, nullptr, Ck, eps, one_source ? nullptr : O, M, LSE,
-                  nullptr, nullptr, nullptr};
+                  nullptr, nullptr, nullptr, gemm_ws};
     TRY(do_phase1(fn, dtype, a1, st));
     const void* v = nullptr;
     TRY(call(s0, o_slice(0), &v));  // the first sublayer of the chunk: h = o_0
@@ -1291,9 +1300,9 @@ BwdStackLayout bwd_stack_layout(int L, int S, int64_t R, int64_t D, int dtype) {
   s.dl = off; off = align256(off + (size_t)Sk * R * sizeof(float));
   s.g = off;
   s.gbytes = 0;
-  if (Sk > 1 && attnres::phase1_gemm_shape(dtype, Sk, D, R) &&
-      !attnres::phase1_mfma_eligible(dtype, 1, Sk, D))
-    s.gbytes = attnres::phase1_gemm_workspace(Sk, R, D);
+  const int nb = plan(L, S, nullptr, nullptr);
+  if (attnres::phase1_gemm_needed(dtype, Sk, D, R, nb))
+    s.gbytes = attnres::phase1_gemm_workspace(Sk, R, D, nb);
   off = align256(off + s.gbytes);
   {
     const size_t a = attnres::plan_aggregate_bwd(dtype, R, D).bytes;

@@ -456,12 +456,14 @@ __device__ __forceinline__ float group8_sum(float x) {
   x += dpp_mov<0x4E>(x);
   return x + dpp_mov<0x141>(x);
 }
-// The same over aligned groups of N = 1, 2, 4 or 8 lanes.
+// The same over aligned groups of N = 1, 2, 4, 8 or 16 lanes (16: a
+// row_mirror joins the two halves of a DPP row).
 template <int N>
 __device__ __forceinline__ float groupn_max(float x) {
   if constexpr (N >= 2) x = fmaxf(x, dpp_mov<0xB1>(x));
   if constexpr (N >= 4) x = fmaxf(x, dpp_mov<0x4E>(x));
   if constexpr (N >= 8) x = fmaxf(x, dpp_mov<0x141>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp_mov<0x140>(x));
   return x;
 }
 template <int N>
@@ -469,6 +471,7 @@ __device__ __forceinline__ float groupn_sum(float x) {
   if constexpr (N >= 2) x += dpp_mov<0xB1>(x);
   if constexpr (N >= 4) x += dpp_mov<0x4E>(x);
   if constexpr (N >= 8) x += dpp_mov<0x141>(x);
+  if constexpr (N >= 16) x += dpp_mov<0x140>(x);
   return x;
 }
 
@@ -2037,7 +2040,7 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
 
 // ---------------------------------------------------------------------------
 // Phase 1 for many queries over wide rows [K3 9.4 step 1; RH 4.2 Phase 1],
-// bf16, n <= 8 sources, up to 32 queries, in two passes over the sources:
+// bf16, n <= 16 sources, up to 32 queries, in two passes over the sources:
 //
 // Scores. For a tile of rows, the scores of every query against every source
 // of every row form one product C = Qp B, where Qp is [32 MT, D]: row
@@ -2055,13 +2058,14 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
 // from the same B registers (v_dot2). After the last chunk each lane holds,
 // for its column, the three parts of one query per tile; their sum scaled by
 // the source's 1 / rms is the score. A row takes NPR columns, the smallest of
-// 1, 2, 4 or 8 that holds its n sources (so a tile holds 16 / NPR rows per
-// wave), and the softmax is an NPR-lane reduction. The weights alpha
-// [S][R][8] (entries i < NPR; zero from n on) and the statistics m, lse are
-// written.
+// 1, 2, 4, 8 or 16 that holds its n sources (so a tile holds 16 / NPR rows
+// per wave), and the softmax is an NPR-lane reduction. The weights alpha
+// [S][R][AST] (AST = 8, or 16 for n > 8; entries i < NPR, zero from n on)
+// and the statistics m, lse are written.
 //
 // Outputs. o_s = sum_i alpha[s][i] b_i, one row per wave group: the row's n
-// sources stay in registers and every query's output is formed from them.
+// sources stay in registers and every query's output is formed from them
+// (as fp32 for n <= 8; packed, one vector per lane, for n > 8).
 //
 // Together the passes move (2 n + S) D-vectors per row where query passes of
 // 4 in registers would move (passes x n + S). A block close runs before them
@@ -2099,7 +2103,7 @@ __global__ void qsplit_kernel(QSplitParams p) {
 }
 
 struct P1GParams {
-  const void* src[8];
+  const void* src[16];
   int n;
   int S;
   const __bf16* qp;  // [32 MT][D]
@@ -2107,7 +2111,7 @@ struct P1GParams {
   float invD;
   int64_t R;
   int D;
-  float* alpha;      // [S][R][8]
+  float* alpha;      // [S][R][AST], AST = 8 (NPR <= 8) or 16
   float* m_out;      // [S][R] or null
   float* lse_out;    // [S][R]
 };
@@ -2159,6 +2163,7 @@ __global__ __launch_bounds__(1024) void phase1_gemm_scores_kernel(P1GParams p) {
   constexpr int U = (MT + 1) / 2;       // Qp staging units per thread
   constexpr int RW = 16 / NPR;          // rows per wave: NPR source columns each
   constexpr int RT = kGWaves * RW;      // rows per tile
+  constexpr int AST = NPR > 8 ? 16 : 8; // row stride of the weights
   __shared__ __attribute__((aligned(16))) __bf16 abuf[2][MT * 32 * AROW];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int col = l & 15, g4 = l >> 4;        // B column and k-group
@@ -2240,7 +2245,7 @@ __global__ __launch_bounds__(1024) void phase1_gemm_scores_kernel(P1GParams p) {
       const float e = valid ? __expf(sc - m) : 0.f;
       const float z = groupn_sum<NPR>(e);
       if (rv && s < p.S) {
-        p.alpha[((int64_t)s * p.R + row) * 8 + i] = e * (1.0f / z);
+        p.alpha[((int64_t)s * p.R + row) * AST + i] = e * (1.0f / z);
         if (i == 0) {
           if (p.m_out) p.m_out[(int64_t)s * p.R + row] = m;
           p.lse_out[(int64_t)s * p.R + row] = m + __logf(z);
@@ -2251,9 +2256,9 @@ __global__ __launch_bounds__(1024) void phase1_gemm_scores_kernel(P1GParams p) {
 }
 
 struct P1OParams {
-  const void* src[8];
+  const void* src[16];
   int S;
-  const float* alpha;  // [S][R][8]
+  const float* alpha;  // [S][R][8] (n <= 8) or [S][R][16]
   void* out;           // [S][R][D]
   Geom g;
 };
@@ -2300,6 +2305,73 @@ __global__ __launch_bounds__(512) void phase1_gemm_outputs_kernel(P1OParams p) {
         if constexpr (NT) st16_stream(dst, Bf16::pack(o));
         else st16(dst, Bf16::pack(o));
       }
+    }
+  }
+}
+
+// The outputs pass for 9..16 sources: the row's sources stay packed in
+// registers, one 16-byte vector per lane (up to 16 waves per row, so rows of
+// up to 8192 elements); kept as fp32 they would not fit beside the
+// accumulators. Queries go in pairs, so each source is unpacked once per
+// pair: the pair's 32 weights are one load (lane 16 q + i holds weight i of
+// query q; the weights are [S][R][16]) and reach the products as scalars.
+// Each output sums its terms in source order, as the narrower pass does.
+template <int NC, bool NT>
+__global__ __launch_bounds__(1024) void phase1_gemm_outputs_wide_kernel(P1OParams p) {
+  const Geom& g = p.g;
+  const Lanes ln(g.W);
+  const int64_t rowbytes = (int64_t)g.V * 16;
+  for (int64_t grp = blockIdx.x; grp < g.groups; grp += gridDim.x) {
+    // one row per wave group: uniform across the wave
+    const int64_t row = __builtin_amdgcn_readfirstlane((int)(grp * g.RPW + ln.slot));
+    const bool rv = row < g.R;
+    const int64_t base = (rv ? row : 0) * rowbytes;
+    const int vec = ln.t;
+    const bool own = rv && vec < g.V;
+    // each source row as a wave-uniform base plus a 32-bit lane offset, so
+    // no 64-bit address per lane and source is kept
+    const uint32_t loff = (uint32_t)(vec < g.V ? vec : 0) * 16u;
+    u32x4_t x[NC];
+    #pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const gchar_t* b = uniform_ptr(static_cast<const char*>(p.src[i]) + base);
+      x[i] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4_t*>(b + loff));
+    }
+    char* dst0 = static_cast<char*>(p.out) + base + (int64_t)vec * 16;
+    for (int s0 = 0; s0 < p.S; s0 += 2) {
+      // the empty asm makes the packed sources look new to every pair, so
+      // their unpacking is not hoisted out of this loop as NC x 8 floats
+      #pragma unroll
+      for (int i = 0; i < NC; ++i) asm volatile("" : "+v"(x[i]));
+      const int sq = s0 + (ln.lane >> 4);
+      const float wv = (ln.lane < 32 && sq < p.S)
+                           ? p.alpha[((int64_t)sq * g.R + (rv ? row : 0)) * 16 + (ln.lane & 15)]
+                           : 0.f;
+      float o0[8], o1[8];
+      #pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        float f[8];
+        Bf16::unpack(uint4{x[i][0], x[i][1], x[i][2], x[i][3]}, f);
+        const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), i));
+        const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), 16 + i));
+        #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          o0[e] = i == 0 ? a0 * f[e] : fmaf(a0, f[e], o0[e]);
+          o1[e] = i == 0 ? a1 * f[e] : fmaf(a1, f[e], o1[e]);
+        }
+        // one source at a time: otherwise the scheduler unpacks them all
+        // up front and runs out of registers
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      char* dst = store_target(own, dst0 + (int64_t)s0 * g.R * rowbytes);
+      if constexpr (NT) st16_stream(dst, Bf16::pack(o0));
+      else st16(dst, Bf16::pack(o0));
+      // unconditional (a missing second query stores to the sink): under a
+      // branch the compiler would sink o1's products into it and keep every
+      // unpacked source alive until then
+      dst = store_target(own && s0 + 1 < p.S, dst0 + (int64_t)(s0 + 1) * g.R * rowbytes);
+      if constexpr (NT) st16_stream(dst, Bf16::pack(o1));
+      else st16(dst, Bf16::pack(o1));
     }
   }
 }
@@ -2846,6 +2918,7 @@ static hipError_t launch_phase1_stream(const Phase1Args& a, const Launch& L) {
 #endif
 
 static int gemm_tiles(int S) { return (S + 7) / 8; }
+constexpr int kGMaxN = 16;  // sources per row of the scores/outputs passes
 
 bool phase1_gemm_shape(int dtype, int S, int64_t D, int64_t R) {
   // (the outputs pass keeps its row index in a 32-bit scalar register)
@@ -2854,15 +2927,22 @@ bool phase1_gemm_shape(int dtype, int S, int64_t D, int64_t R) {
 }
 
 bool phase1_gemm_eligible(int dtype, int n, int S, int64_t D, int64_t R) {
-  return n >= 1 && n <= 8 && phase1_gemm_shape(dtype, S, D, R) && !phase1_mfma_eligible(dtype, n, S, D);
+  return n >= 1 && n <= kGMaxN && phase1_gemm_shape(dtype, S, D, R) && !phase1_mfma_eligible(dtype, n, S, D);
+}
+
+bool phase1_gemm_needed(int dtype, int S, int64_t D, int64_t R, int nmax) {
+  if (S < 2 || !phase1_gemm_shape(dtype, S, D, R)) return false;
+  for (int n = 1; n <= nmax && n <= kGMaxN; ++n)
+    if (phase1_gemm_eligible(dtype, n, S, D, R)) return true;
+  return false;
 }
 
 static size_t gemm_qp_bytes(int S, int64_t D) {
   return ((size_t)32 * gemm_tiles(S) * D * 2 + 255) & ~(size_t)255;
 }
 
-size_t phase1_gemm_workspace(int S, int64_t R, int64_t D) {
-  return gemm_qp_bytes(S, D) + (size_t)S * R * 8 * sizeof(float);
+size_t phase1_gemm_workspace(int S, int64_t R, int64_t D, int nmax) {
+  return gemm_qp_bytes(S, D) + (size_t)S * R * (nmax > 8 ? 16 : 8) * sizeof(float);
 }
 
 template <int MT, int NPR>
@@ -2872,28 +2952,34 @@ static hipError_t launch_gemm_scores_t(const P1GParams& g, const Launch& L) {
   return launch(L, phase1_gemm_scores_kernel<MT, NPR>, dim3(grid), dim3(64 * kGWaves), 0, g);
 }
 
-// Source columns per row: the smallest of 1, 2, 4 or 8 that holds the n
+// Source columns per row: the smallest of 1, 2, 4, 8 or 16 that holds the n
 // sources, so a 16-column tile takes 16 / NPR rows.
 template <int MT>
 static hipError_t launch_gemm_scores(const P1GParams& g, const Launch& L) {
   if (g.n <= 1) return launch_gemm_scores_t<MT, 1>(g, L);
   if (g.n <= 2) return launch_gemm_scores_t<MT, 2>(g, L);
   if (g.n <= 4) return launch_gemm_scores_t<MT, 4>(g, L);
-  return launch_gemm_scores_t<MT, 8>(g, L);
+  if (g.n <= 8) return launch_gemm_scores_t<MT, 8>(g, L);
+  return launch_gemm_scores_t<MT, 16>(g, L);
 }
 
 template <int NC>
 static hipError_t launch_gemm_outputs(const P1OParams& o, bool nt, const Launch& L) {
   const unsigned grid = grid_for(o.g);
   const dim3 block(64 * o.g.W * o.g.RPW);
-  if (nt) return launch(L, phase1_gemm_outputs_kernel<NC, true>, dim3(grid), block, 0, o);
-  return launch(L, phase1_gemm_outputs_kernel<NC, false>, dim3(grid), block, 0, o);
+  if constexpr (NC > 8) {
+    if (nt) return launch(L, phase1_gemm_outputs_wide_kernel<NC, true>, dim3(grid), block, 0, o);
+    return launch(L, phase1_gemm_outputs_wide_kernel<NC, false>, dim3(grid), block, 0, o);
+  } else {
+    if (nt) return launch(L, phase1_gemm_outputs_kernel<NC, true>, dim3(grid), block, 0, o);
+    return launch(L, phase1_gemm_outputs_kernel<NC, false>, dim3(grid), block, 0, o);
+  }
 }
 
 // Phase 1 as a query split, a matrix-core scores pass and an outputs pass
 // (see phase1_gemm_scores_kernel); without an output buffer (statistics
 // only) the outputs pass is skipped. The sources must be materialised (no
-// fused close); `ws` holds phase1_gemm_workspace(S, R, D) bytes.
+// fused close); `ws` holds phase1_gemm_workspace(S, R, D, n) bytes.
 hipError_t launch_phase1_gemm(const Phase1Args& a, void* ws, const Launch& L) {
   if (a.close_v || !phase1_gemm_eligible(1, a.n, a.S, a.D, a.R)) return hipErrorInvalidValue;
   const int MT = gemm_tiles(a.S);
@@ -2910,7 +2996,7 @@ hipError_t launch_phase1_gemm(const Phase1Args& a, void* ws, const Launch& L) {
   }
   {
     P1GParams g;
-    for (int i = 0; i < 8; ++i) g.src[i] = i < a.n ? a.src[i] : a.src[0];
+    for (int i = 0; i < kGMaxN; ++i) g.src[i] = i < a.n ? a.src[i] : a.src[0];
     g.n = a.n; g.S = a.S; g.qp = qp; g.eps = a.eps; g.invD = 1.0f / (float)a.D;
     g.R = a.R; g.D = (int)a.D; g.alpha = alpha; g.m_out = a.m_out; g.lse_out = a.lse_out;
     hipError_t e;
@@ -2924,10 +3010,12 @@ hipError_t launch_phase1_gemm(const Phase1Args& a, void* ws, const Launch& L) {
   }
   if (!a.out) return hipSuccess;
   P1OParams o;
-  for (int i = 0; i < 8; ++i) o.src[i] = i < a.n ? a.src[i] : a.src[0];
+  for (int i = 0; i < kGMaxN; ++i) o.src[i] = i < a.n ? a.src[i] : a.src[0];
   o.S = a.S; o.alpha = alpha; o.out = a.out;
-  o.g = make_geom(a.R, a.D, 2, 2, 8);
-  if (o.g.W > 8) return hipErrorInvalidValue;
+  // two vectors per lane up to 8 sources (at most 8 waves per row), one
+  // vector per lane beyond (at most 16)
+  o.g = a.n > 8 ? make_geom(a.R, a.D, 2, 1, 16) : make_geom(a.R, a.D, 2, 2, 8);
+  if (o.g.W > (a.n > 8 ? 16 : 8)) return hipErrorInvalidValue;
   const bool nt = (double)a.R * a.D * 2 > (double)ATTNRES_PHASE2_NT_BYTES;
   switch (a.n) {
     case 1: return launch_gemm_outputs<1>(o, nt, last);
@@ -2937,7 +3025,15 @@ hipError_t launch_phase1_gemm(const Phase1Args& a, void* ws, const Launch& L) {
     case 5: return launch_gemm_outputs<5>(o, nt, last);
     case 6: return launch_gemm_outputs<6>(o, nt, last);
     case 7: return launch_gemm_outputs<7>(o, nt, last);
-    default: return launch_gemm_outputs<8>(o, nt, last);
+    case 8: return launch_gemm_outputs<8>(o, nt, last);
+    case 9: return launch_gemm_outputs<9>(o, nt, last);
+    case 10: return launch_gemm_outputs<10>(o, nt, last);
+    case 11: return launch_gemm_outputs<11>(o, nt, last);
+    case 12: return launch_gemm_outputs<12>(o, nt, last);
+    case 13: return launch_gemm_outputs<13>(o, nt, last);
+    case 14: return launch_gemm_outputs<14>(o, nt, last);
+    case 15: return launch_gemm_outputs<15>(o, nt, last);
+    default: return launch_gemm_outputs<16>(o, nt, last);
   }
 }
 

@@ -32,7 +32,7 @@ struct Phase1Args {
   const void* close_p;
   const void* close_v;
   void* close_b;
-  // workspace of phase1_gemm_workspace(S, R, D) bytes, or null: with it,
+  // workspace of phase1_gemm_workspace(S, R, D, n) bytes, or null: with it,
   // shapes phase1_gemm_eligible() accepts take the scores/outputs passes
   void* gemm_ws = nullptr;
   // the streamed kernel's workgroup budget per launch (0: its default); a
@@ -182,15 +182,19 @@ hipError_t launch_phase1_bwd(const Phase1BwdArgs& a, void* ws, const Launch& L, 
 
 hipError_t launch_fold(const float* w, const float* g, float* q, int64_t count, const Launch& L);
 hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L);
-// Phase 1 as a matrix-core scores pass and an outputs pass (bf16, n <= 8,
+// Phase 1 as a matrix-core scores pass and an outputs pass (bf16, n <= 16,
 // S <= 32, D a multiple of 256 up to 8192, many rows; statistics only when
 // out is null); needs materialised sources (no fused close) and a workspace
-// of phase1_gemm_workspace bytes.
+// of phase1_gemm_workspace(S, R, D, nmax) bytes for launches of up to nmax
+// sources.
 bool phase1_gemm_shape(int dtype, int S, int64_t D, int64_t R);
 // the register-tile matrix-core Phase 1 (bf16, n <= 8, S <= 8, D in {1024, 2048, 3072, 4096})
 bool phase1_mfma_eligible(int dtype, int n, int S, int64_t D);
 bool phase1_gemm_eligible(int dtype, int n, int S, int64_t D, int64_t R);
-size_t phase1_gemm_workspace(int S, int64_t R, int64_t D);
+// whether some Phase 1 of S queries over 1..nmax sources takes the
+// scores/outputs passes (a stack reserves their workspace then)
+bool phase1_gemm_needed(int dtype, int S, int64_t D, int64_t R, int nmax);
+size_t phase1_gemm_workspace(int S, int64_t R, int64_t D, int nmax);
 hipError_t launch_phase1_gemm(const Phase1Args& a, void* ws, const Launch& L);
 bool phase1_supported(int dtype, int n, int S, int64_t D);
 // whether the kernel a Phase-1 launch runs writes the input norm of output 0

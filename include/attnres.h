@@ -166,11 +166,12 @@ int attnres_table_sublayer(void* ctx, int l, const void* h_l, const void** v_out
 /* Bytes of workspace attnres_block_stack_forward needs for (L, S, R, D, dtype);
  * 0 for invalid arguments. It holds the folded queries, one block's Phase-1
  * outputs and statistics, the partial sum and h; for bf16 stacks of at least
- * 4096 rows whose widest block has more than 8 queries or a width outside
- * {1024, 2048, 3072, 4096} (D a multiple of 256 up to 8192, at most 32
- * queries), also the query parts [32 ceil(S/8), D] bf16 and the softmax
- * weights [S, R, 8] fp32 of the matrix-core scores pass, which then runs
- * Phase 1 for blocks of at most 8 sources. */
+ * 4096 rows (D a multiple of 256 up to 8192, at most 32 queries) whose
+ * widest block has more than 8 queries or a width outside {1024, 2048, 3072,
+ * 4096}, or that have more than 8 blocks, also the query parts
+ * [32 ceil(S/8), D] bf16 and the softmax weights [S, R, 8] fp32 ([S, R, 16]
+ * with more than 8 blocks) of the matrix-core scores pass, which then runs
+ * Phase 1 for blocks of at most 16 sources. */
 size_t attnres_stack_workspace_bytes(int L, int S, int64_t R, int64_t D, int dtype);
 
 /* ---------------------------------------------------------------------------
@@ -304,8 +305,10 @@ const char* attnres_last_error(void);
  *   W, Gamma [L+1, D] fp32 as in attnres_block_stack_forward. Every v_l
  *   returned by the callback is a source to the end of the call and must
  *   stay valid until then. Workspace: attnres_full_workspace_bytes(L, C, R,
- *   D, dtype) bytes, 256-byte aligned. Limits: L + 1 <= ATTNRES_MAX_SOURCES.
- *   Errors as attnres_block_stack_forward.
+ *   D, dtype) bytes, 256-byte aligned; for bf16 stacks of at least 4096 rows
+ *   it also holds the matrix-core scores pass's query parts and weights when
+ *   a chunk of up to 16 sources takes that pass. Limits: L + 1 <=
+ *   ATTNRES_MAX_SOURCES. Errors as attnres_block_stack_forward.
  * ------------------------------------------------------------------------- */
 int attnres_merge_sources(const void* o, const float* lse, const void* const* sources, int n,
                           int64_t R, int64_t D, int dtype, const float* w, const float* gamma,

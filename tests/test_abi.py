@@ -160,28 +160,52 @@ def _a256(x):
     return (x + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("L_,S,R,D,dt,scores_pass", [
-    (186, 24, 131072, 7168, 1, True),    # long context: the matrix-core scores pass
-    (96, 12, 128, 7168, 1, False),       # decode: too few rows, streamed Phase 1
-    (48, 8, 16384, 4096, 1, False),      # register-tile Phase 1
-    (20, 9, 4096, 4096, 1, True),        # 9 queries at D = 4096
-    (20, 9, 4096, 4096, 0, False),       # fp32 never takes it
-    (20, 9, 4096, 4000, 1, False),       # D not a multiple of 256
-    (40, 33, 8192, 1024, 1, False),      # more than 32 queries
+@pytest.mark.parametrize("L_,S,R,D,dt,ast", [
+    (186, 24, 131072, 7168, 1, 8),       # long context: the matrix-core scores pass, 8 blocks
+    (96, 12, 128, 7168, 1, 0),           # decode: too few rows, streamed Phase 1
+    (48, 8, 16384, 4096, 1, 0),          # register-tile Phase 1
+    (72, 8, 8192, 4096, 1, 16),          # 9 blocks: the last Phase 1 has 9 sources
+    (40, 4, 4096, 1024, 1, 16),          # 10 blocks
+    (20, 9, 4096, 4096, 1, 8),           # 9 queries at D = 4096
+    (20, 9, 4096, 4096, 0, 0),           # fp32 never takes it
+    (20, 9, 4096, 4000, 1, 0),           # D not a multiple of 256
+    (40, 33, 8192, 1024, 1, 0),          # more than 32 queries
 ])
-def test_workspace_bytes_layout(L_, S, R, D, dt, scores_pass):
+def test_workspace_bytes_layout(L_, S, R, D, dt, ast):
     """The stack workspace is the 256-byte-aligned regions the header lists:
     folded queries, one block's Phase-1 outputs and statistics, the partial,
-    h, and -- where the widest block takes the matrix-core scores pass -- the
-    query parts [32 ceil(S/8), D] bf16 and the weights [S, R, 8] fp32."""
+    h, and -- where some block takes the matrix-core scores pass -- the query
+    parts [32 ceil(S/8), D] bf16 and the weights [S, R, ast] fp32 (ast = 16
+    when a Phase 1 has more than 8 sources)."""
     es = 2 if dt == 1 else 4
     Sk = min(S, L_)
     row = R * D * es
     want = _a256((L_ + 1) * D * 4) + _a256(Sk * row if Sk > 1 else 0) + 2 * _a256(Sk * R * 4)
     want += _a256(row if Sk > 2 else 0) + _a256(row)
-    if scores_pass:
-        want += _a256(_a256(32 * ((Sk + 7) // 8) * D * 2) + Sk * R * 8 * 4)
+    if ast:
+        want += _a256(_a256(32 * ((Sk + 7) // 8) * D * 2) + Sk * R * ast * 4)
     assert b.lib().attnres_stack_workspace_bytes(L_, S, R, D, dt) == want
+
+
+@pytest.mark.parametrize("L_,C,R,D,dt,ast", [
+    (16, 4, 16384, 4096, 1, 16),   # chunks over 1, 5, 9 and 13 sources: the last two take the scores pass
+    (16, 4, 2048, 1024, 1, 0),     # too few rows
+    (8, 4, 16384, 4096, 1, 0),     # chunks over 1 and 5 sources: the register-tile Phase 1
+    (12, 3, 8192, 7168, 1, 16),    # D = 7168: every chunk, 10 sources at most
+    (17, 4, 4096, 1024, 1, 16),    # the last chunk has one sublayer: no Phase 1 over 17 sources
+    (16, 1, 16384, 4096, 1, 0),    # the naive schedule
+])
+def test_full_workspace_bytes_layout(L_, C, R, D, dt, ast):
+    """The Full workspace: folded queries, one chunk's Phase-1 outputs and
+    statistics, h and -- where some chunk takes the scores pass -- its query
+    parts and weights [C, R, ast] fp32."""
+    es = 2 if dt == 1 else 4
+    Ck = min(C, L_)
+    row = R * D * es
+    want = _a256((L_ + 1) * D * 4) + _a256(Ck * row if Ck > 1 else 0) + 2 * _a256(Ck * R * 4) + _a256(row)
+    if ast:
+        want += _a256(_a256(32 * ((Ck + 7) // 8) * D * 2) + Ck * R * ast * 4)
+    assert b.lib().attnres_full_workspace_bytes(L_, C, R, D, dt) == want
 
 
 def test_generator_twin_rounding_and_distribution():

@@ -72,6 +72,13 @@ FULL_CASES = [
     ("full_L9_C1", 9, 1, 1, 50, 256, "bf16"),
     ("full_L5_C16", 5, 16, 1, 33, 128, "bf16"),
     ("full_L12_C4_gains", 12, 4, 2, 100, 1024, "bf16"),
+    # at least 4096 rows: chunks of 9..16 sources on the matrix-core scores
+    # pass and the packed outputs pass (odd query counts included), beside
+    # the register-tile Phase 1 for the first chunks; D = 7168 takes the
+    # scores pass for every chunk
+    ("full_L16_C4_scores", 16, 4, 1, 4100, 1024, "bf16"),
+    ("full_L20_C5_scores_gains", 20, 5, 1, 4096, 2048, "bf16"),
+    ("full_L12_C3_D7168", 12, 3, 1, 4096, 7168, "bf16"),
 ]
 
 

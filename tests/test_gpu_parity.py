@@ -285,13 +285,18 @@ GEMM_STACKS = [
     # (B, T, D, S, L): Phase 1 on the matrix-core scores pass and the outputs
     # pass (bf16, more than 8 queries or a width outside the register-tile
     # kernel, at least 4096 rows); ragged row tiles; 24 queries (3 Qp tiles)
-    # then a 5-query block; sources 2..8 with S = 12, then 9 sources, which
-    # fall back to the streamed kernel; 32 queries (4 tiles) at D = 1024; 9
-    # queries at D = 4096
+    # then a 5-query block; sources 2..8 with S = 12, then 9 sources (16
+    # columns per row, the packed outputs pass); 32 queries (4 tiles) at
+    # D = 1024; 9 queries at D = 4096; 16 blocks of 4 at D = 1024 (the
+    # register-tile Phase 1 up to 8 sources, then 9..16 on the scores pass);
+    # 15 blocks of 3 queries at D = 7168 (every column count, odd query
+    # count in the packed outputs pass)
     (1, 4100, 7168, 24, 53),
     (2, 2048, 7168, 12, 99),
     (4, 2048, 1024, 32, 71),
     (1, 4096, 4096, 9, 20),
+    (1, 4100, 1024, 4, 64),
+    (1, 4096, 7168, 3, 45),
 ]
 
 
@@ -313,17 +318,20 @@ def _a256(x):
     return (x + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("L", [12, 24, 30, 54])
-def test_scores_pass_statistics(L):
+@pytest.mark.parametrize("L,S,D", [(12, 12, 7168), (24, 12, 7168), (30, 12, 7168), (54, 12, 7168),
+                                   (39, 4, 1024), (62, 4, 1024)])
+def test_scores_pass_statistics(L, S, D):
     """The matrix-core scores pass's fp32 statistics at the 1e-5 bar: a stack of
-    4100 rows of 7168 with 12 queries whose last block has L // 12 + 1 sources
-    (1: statistics only, one column per row; 2, 3 and 5: two, four and eight
-    columns per row; the short last blocks hold 6 queries). After the forward
-    the workspace holds that block's m and lse [Sk, R] at the offsets of the
-    header's layout (folded queries, outputs, m, lse), compared on every row
-    with the oracle's Phase 1 over the block sums the GPU stored."""
-    S, D = 12, 7168
-    wl = inputs.Workload(f"scores_stats_L{L}", "stack", B=1, T=4100, D=D, dtype="bf16", L=L, S=S, seed=L + 5)
+    4100 rows whose last block's Phase 1 has nb sources: with 12 queries of
+    7168, L // 12 + 1 (1: statistics only, one column per row; 2, 3 and 5:
+    two, four and eight columns per row; the short last blocks hold 6
+    queries); with 4 queries of 1024, 10 and 16 (sixteen columns per row).
+    After the forward the workspace holds that block's m and lse [Sk, R] at
+    the offsets of the header's layout (folded queries, outputs, m, lse),
+    compared on every row with the oracle's Phase 1 over the block sums the
+    GPU stored."""
+    wl = inputs.Workload(f"scores_stats_L{L}_S{S}_D{D}", "stack", B=1, T=4100, D=D, dtype="bf16", L=L, S=S,
+                         seed=L + 5)
     announce(wl.name)
     ds = DeviceStack(wl)
     ds.forward()
