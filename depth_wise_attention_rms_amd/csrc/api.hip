@@ -313,9 +313,8 @@ StackLayout stack_layout(int L, int S, int64_t R, int64_t D, int es) {
   // the scores/outputs Phase 1 (query parts and softmax weights) where some
   // block's Phase 1 takes it (block k scores over k sources, up to nb)
   s.g = off;
-  const int nb = plan(L, S, nullptr, nullptr);
-  if (attnres::phase1_gemm_needed(es == 2 ? 1 : 0, Sk, D, R, nb))
-    off = align256(off + attnres::phase1_gemm_workspace(Sk, R, D, nb));
+  const int ng = attnres::phase1_gemm_needed(es == 2 ? 1 : 0, Sk, D, R, plan(L, S, nullptr, nullptr));
+  if (ng) off = align256(off + attnres::phase1_gemm_workspace(Sk, R, D, ng));
   s.total = off;
   return s;
 }
@@ -737,9 +736,8 @@ OverlapLayout overlap_layout(int L, int S, int64_t R, int64_t D, int es) {
   s.p = off; off = align256(off + (Sk > 2 ? row : 0));
   s.h = off; off = align256(off + row);
   s.g = off;
-  const int nb = plan(L, S, nullptr, nullptr);
-  if (attnres::phase1_gemm_needed(es == 2 ? 1 : 0, Sk, D, R, nb))
-    off = align256(off + attnres::phase1_gemm_workspace(Sk, R, D, nb));
+  const int ng = attnres::phase1_gemm_needed(es == 2 ? 1 : 0, Sk, D, R, plan(L, S, nullptr, nullptr));
+  if (ng) off = align256(off + attnres::phase1_gemm_workspace(Sk, R, D, ng));
   s.total = off;
   return s;
 }
@@ -990,8 +988,8 @@ FullLayout full_layout(int L, int C, int64_t R, int64_t D, int es) {
   int nmax = 0;
   for (int s0 = 1; s0 <= L; s0 += C)
     if (L - s0 + 1 >= 2 && C >= 2) nmax = s0;
-  if (nmax > 0 && attnres::phase1_gemm_needed(es == 2 ? 1 : 0, Ck, D, R, nmax))
-    off = align256(off + attnres::phase1_gemm_workspace(Ck, R, D, nmax));
+  const int ng = nmax > 0 ? attnres::phase1_gemm_needed(es == 2 ? 1 : 0, Ck, D, R, nmax) : 0;
+  if (ng) off = align256(off + attnres::phase1_gemm_workspace(Ck, R, D, ng));
   f.total = off;
   return f;
 }
@@ -1300,9 +1298,8 @@ BwdStackLayout bwd_stack_layout(int L, int S, int64_t R, int64_t D, int dtype) {
   s.dl = off; off = align256(off + (size_t)Sk * R * sizeof(float));
   s.g = off;
   s.gbytes = 0;
-  const int nb = plan(L, S, nullptr, nullptr);
-  if (attnres::phase1_gemm_needed(dtype, Sk, D, R, nb))
-    s.gbytes = attnres::phase1_gemm_workspace(Sk, R, D, nb);
+  const int ng = attnres::phase1_gemm_needed(dtype, Sk, D, R, plan(L, S, nullptr, nullptr));
+  if (ng) s.gbytes = attnres::phase1_gemm_workspace(Sk, R, D, ng);
   off = align256(off + s.gbytes);
   {
     const size_t a = attnres::plan_aggregate_bwd(dtype, R, D).bytes;

@@ -2073,7 +2073,7 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
 // ---------------------------------------------------------------------------
 constexpr int kGWaves = 16;   // waves per scores workgroup, 2 rows each
 constexpr int kGChunk = 128;  // hidden elements per staged chunk of Qp
-constexpr int kGPad = 8;      // LDS row padding (elements)
+constexpr int kGPad = 16;     // LDS row padding (elements): 8 left bank conflicts on the Qp reads
 
 struct QSplitParams {
   const float* W;  // [S][D]
@@ -2926,15 +2926,21 @@ bool phase1_gemm_shape(int dtype, int S, int64_t D, int64_t R) {
          R >= ATTNRES_P1_GEMM_MIN_ROWS && R <= INT32_MAX;
 }
 
+// More than 8 sources take the two passes only with at least 4 queries: the
+// scores pass reads the sources once more, which with fewer queries costs
+// more than the streamed kernel's arithmetic (the Full schedule at C = 2 went
+// 4.49 -> 4.83 ms that way).
 bool phase1_gemm_eligible(int dtype, int n, int S, int64_t D, int64_t R) {
-  return n >= 1 && n <= kGMaxN && phase1_gemm_shape(dtype, S, D, R) && !phase1_mfma_eligible(dtype, n, S, D);
+  return n >= 1 && n <= kGMaxN && (n <= 8 || S >= 4) && phase1_gemm_shape(dtype, S, D, R) &&
+         !phase1_mfma_eligible(dtype, n, S, D);
 }
 
-bool phase1_gemm_needed(int dtype, int S, int64_t D, int64_t R, int nmax) {
-  if (S < 2 || !phase1_gemm_shape(dtype, S, D, R)) return false;
+int phase1_gemm_needed(int dtype, int S, int64_t D, int64_t R, int nmax) {
+  int most = 0;
+  if (S < 2 || !phase1_gemm_shape(dtype, S, D, R)) return 0;
   for (int n = 1; n <= nmax && n <= kGMaxN; ++n)
-    if (phase1_gemm_eligible(dtype, n, S, D, R)) return true;
-  return false;
+    if (phase1_gemm_eligible(dtype, n, S, D, R)) most = n;
+  return most;
 }
 
 static size_t gemm_qp_bytes(int S, int64_t D) {

@@ -191,9 +191,10 @@ bool phase1_gemm_shape(int dtype, int S, int64_t D, int64_t R);
 // the register-tile matrix-core Phase 1 (bf16, n <= 8, S <= 8, D in {1024, 2048, 3072, 4096})
 bool phase1_mfma_eligible(int dtype, int n, int S, int64_t D);
 bool phase1_gemm_eligible(int dtype, int n, int S, int64_t D, int64_t R);
-// whether some Phase 1 of S queries over 1..nmax sources takes the
-// scores/outputs passes (a stack reserves their workspace then)
-bool phase1_gemm_needed(int dtype, int S, int64_t D, int64_t R, int nmax);
+// the most sources of a Phase 1 of S queries over 1..nmax sources that takes
+// the scores/outputs passes, 0 if none does (a stack reserves their workspace
+// for that many sources)
+int phase1_gemm_needed(int dtype, int S, int64_t D, int64_t R, int nmax);
 size_t phase1_gemm_workspace(int S, int64_t R, int64_t D, int nmax);
 hipError_t launch_phase1_gemm(const Phase1Args& a, void* ws, const Launch& L);
 bool phase1_supported(int dtype, int n, int S, int64_t D);

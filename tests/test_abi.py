@@ -166,6 +166,7 @@ def _a256(x):
     (48, 8, 16384, 4096, 1, 0),          # register-tile Phase 1
     (72, 8, 8192, 4096, 1, 16),          # 9 blocks: the last Phase 1 has 9 sources
     (40, 4, 4096, 1024, 1, 16),          # 10 blocks
+    (40, 3, 4096, 1024, 1, 0),           # 14 blocks of 3 queries: register tile up to 8 sources, streamed beyond
     (20, 9, 4096, 4096, 1, 8),           # 9 queries at D = 4096
     (20, 9, 4096, 4096, 0, 0),           # fp32 never takes it
     (20, 9, 4096, 4000, 1, 0),           # D not a multiple of 256
@@ -191,7 +192,7 @@ def test_workspace_bytes_layout(L_, S, R, D, dt, ast):
     (16, 4, 16384, 4096, 1, 16),   # chunks over 1, 5, 9 and 13 sources: the last two take the scores pass
     (16, 4, 2048, 1024, 1, 0),     # too few rows
     (8, 4, 16384, 4096, 1, 0),     # chunks over 1 and 5 sources: the register-tile Phase 1
-    (12, 3, 8192, 7168, 1, 16),    # D = 7168: every chunk, 10 sources at most
+    (12, 3, 8192, 7168, 1, 8),     # D = 7168: chunks of up to 8 sources; 10 with 3 queries stay streamed
     (17, 4, 4096, 1024, 1, 16),    # the last chunk has one sublayer: no Phase 1 over 17 sources
     (16, 1, 16384, 4096, 1, 0),    # the naive schedule
 ])
