@@ -1559,13 +1559,23 @@ __global__ __launch_bounds__(512) void merge_bwd_kernel(MergeBwdParams p) {
 //           - (sum_j ds_ji s_ji / (D r_i^2)) V_i
 //   dq~_j += sum_i (ds_ji / r_i) V_i   (per-workgroup partial rows)
 // One workgroup row at a time, two 4-element vectors per lane (rows of at
-// most 2 x 64 x 8 vectors); the 2 S n + n row sums are reduced one query at a
-// time into an LDS table, from which every lane forms the (row-uniform,
-// scalar) coefficients.
+// most 2 x 64 x 8 vectors), up to 4 queries per launch (a template
+// parameter, so no argument array is indexed at run time):
+//  - every load of a row is issued first, the dV_i it adds to included;
+//  - each wave reduces the 2 S n + n row sums one (query, source) pair at a
+//    time (q~.V in fp32, dh.V and V.V as v_dot2 on the bf16 pairs) into an
+//    LDS table, double-buffered by row parity: one barrier per row;
+//  - the coefficients are formed one (query, source) pair per lane (lane
+//    8 j + i; the softmax over a query's sources is an 8-lane reduction) and
+//    broadcast as scalars: computed as uniform values, every lane would run
+//    the whole table;
+//  - the folded queries and the dq~ sums live in LDS, each lane owning its
+//    elements (no barrier); from global memory, each use of a query would
+//    wait for its load.
 // Sources and upstream gradients are read once; each dV_i is read and written
 // once (added to), instead of once per query.
 // ---------------------------------------------------------------------------
-constexpr int kP1BwdQ = 4;  // queries per launch (their dq~ sums stay in registers)
+constexpr int kP1BwdQ = 4;  // queries per launch (their queries and dq~ sums in LDS)
 constexpr int kP1BwdVpl = 2;  // four-element vectors per lane
 constexpr int kP1BwdMaxN = 6;  // sources
 
@@ -1584,181 +1594,253 @@ struct P1BwdParams {
   Geom g;
 };
 
-template <int NC>
+template <int NC, int SQ>
 __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
   typedef Bf16x4 F;
   typedef F::raw raw;
   constexpr int VPL = kP1BwdVpl;
-  constexpr int NR = 3 * NC;  // per reduction: q~.V and dh.V for one query, V.V
-  extern __shared__ float lds[];  // row reduction scratch [W][NR]
-  __shared__ float tq[kP1BwdQ * NC], tg[kP1BwdQ * NC], tv[NC];
+  // q~_j = w_j * gamma_j for this lane's four elements: both loads are issued
+  // unconditionally (w stands in for a missing gain), since a load under a
+  // branch makes the compiler wait for every load in flight
+  auto query = [&](int j, int64_t el, float* q) {
+    const float4 a = ldf4(p.w[j] + el);
+    const float4 b = ldf4((p.gm[j] ? p.gm[j] : p.w[j]) + el);
+    const bool hg = p.gm[j] != nullptr;
+    q[0] = hg ? a.x * b.x : a.x;
+    q[1] = hg ? a.y * b.y : a.y;
+    q[2] = hg ? a.z * b.z : a.z;
+    q[3] = hg ? a.w * b.w : a.w;
+  };
+  // row sums: q~_j.x_i [SQ][NC], dh_j.x_i [SQ][NC], x_i.x_i [NC]
+  constexpr int NR = (2 * SQ + 1) * NC;
+  // [SQ][D] folded queries, [SQ][D] dq~ sums of this workgroup's rows, then
+  // the wave sums [2 (row parity)][W][NR]
+  extern __shared__ float lds[];
   const Geom& g = p.g;
-  const int t = threadIdx.x, wr = t >> 6, stride = 64 * g.W;
+  float* qs = lds;
+  float* dqs = lds + SQ * g.D;
+  float* wsum = lds + 2 * SQ * g.D;
+  const int t = threadIdx.x, wr = t >> 6, lane = t & 63, stride = 64 * g.W;
   const int64_t rowbytes = (int64_t)g.V * F::kBytes;
   bool in_row[VPL];
-  int64_t voff[VPL];
+  int vec[VPL];
   #pragma unroll
   for (int c = 0; c < VPL; ++c) {
-    const int vec = c * stride + t;
-    in_row[c] = vec < g.V;
-    voff[c] = (int64_t)(in_row[c] ? vec : 0) * F::kBytes;
+    vec[c] = c * stride + t;
+    in_row[c] = vec[c] < g.V;
+    if (!in_row[c]) vec[c] = 0;  // reads vector 0; its values are discarded
   }
-  float dq[kP1BwdQ][VPL][4];
+  // each lane owns its elements of the queries and of the dq~ sums: no
+  // barrier is needed for either. The queries are read from LDS in every
+  // row (from global memory, each first use would wait for its load).
   #pragma unroll
-  for (int j = 0; j < kP1BwdQ; ++j)
+  for (int j = 0; j < SQ; ++j)
     #pragma unroll
     for (int c = 0; c < VPL; ++c)
-      #pragma unroll
-      for (int e = 0; e < 4; ++e) dq[j][c][e] = 0.f;
+      if (in_row[c]) {
+        float q[4];
+        query(j, (int64_t)vec[c] * 4, q);
+        *reinterpret_cast<float4*>(qs + j * g.D + vec[c] * 4) = make_float4(q[0], q[1], q[2], q[3]);
+        *reinterpret_cast<float4*>(dqs + j * g.D + vec[c] * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+  // this lane's query elements (lanes past the row's end read element 0)
+  auto qload = [&](int j, int c, float* q) {
+    const float4 v = *reinterpret_cast<const float4*>(qs + j * g.D + vec[c] * 4);
+    q[0] = v.x; q[1] = v.y; q[2] = v.z; q[3] = v.w;
+  };
 
-  for (int64_t row = blockIdx.x; row < g.R; row += gridDim.x) {
-    raw x[NC][VPL], d[kP1BwdQ][VPL];
+  int parity = 0;
+  for (int64_t row = blockIdx.x; row < g.R; row += gridDim.x, parity ^= 1) {
+    // every load of the row first: sources, upstream gradients, and the
+    // source gradients this row adds to (used after the reduction)
+    raw x[NC][VPL], d[SQ][VPL];
+    uint4 dv[NC][VPL];
     #pragma unroll
     for (int c = 0; c < VPL; ++c) {
+      const int64_t off = row * rowbytes + (int64_t)vec[c] * F::kBytes;
       #pragma unroll
-      for (int i = 0; i < NC; ++i)
-        x[i][c] = F::load(static_cast<const char*>(p.src[i]) + row * rowbytes + voff[c]);
+      for (int i = 0; i < NC; ++i) x[i][c] = F::load(static_cast<const char*>(p.src[i]) + off);
       #pragma unroll
-      for (int j = 0; j < kP1BwdQ; ++j)
-        d[j][c] = F::load(static_cast<const char*>(p.dh[j < p.S ? j : 0]) + row * rowbytes + voff[c]);
+      for (int j = 0; j < SQ; ++j) d[j][c] = F::load(static_cast<const char*>(p.dh[j]) + off);
+      #pragma unroll
+      for (int i = 0; i < NC; ++i) dv[i][c] = ld16_stream(p.dV[i] + row * g.D + (int64_t)vec[c] * 4);
     }
+    // lanes past the row's end read vector 0: a zero source there zeroes
+    // every term those lanes add (scores, gradient dots, sums of squares, dq~)
     #pragma unroll
     for (int c = 0; c < VPL; ++c)
-      if (!in_row[c]) {  // lanes past the row's end hold zeros (their loads read vector 0)
-        #pragma unroll
-        for (int i = 0; i < NC; ++i) x[i][c] = F::zero();
-        #pragma unroll
-        for (int j = 0; j < kP1BwdQ; ++j) d[j][c] = F::zero();
-      }
-    // the row sums, one query per reduction; V.V with the first
-    for (int j = 0; j < p.S; ++j) {
-      float red[NR];
       #pragma unroll
-      for (int k = 0; k < NR; ++k) red[k] = 0.f;
+      for (int i = 0; i < NC; ++i) {
+        x[i][c].x = in_row[c] ? x[i][c].x : 0u;
+        x[i][c].y = in_row[c] ? x[i][c].y : 0u;
+      }
+    // The sources and upstream gradients stay packed (bf16) and are unpacked
+    // where they are used: the empty asm makes them look new to every query,
+    // so the compiler does not keep their fp32 unpacking alive across queries.
+    auto launder = [&]() {
       #pragma unroll
       for (int c = 0; c < VPL; ++c) {
-        float q[4], dh[4];
-        load_query<4>(p.w[j], p.gm[j], voff[c] / F::kBytes * 4, q);
-        F::unpack(d[j][c], dh);
         #pragma unroll
-        for (int i = 0; i < NC; ++i) {
-          float xf[4];
-          F::unpack(x[i][c], xf);
-          #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            red[i] += q[e] * xf[e];
-            red[NC + i] += dh[e] * xf[e];
-            if (j == 0) red[2 * NC + i] += xf[e] * xf[e];
-          }
-        }
-      }
-      row_reduce<NR>(red, lds, 0, wr, g.W);
-      if (t == 0) {
+        for (int i = 0; i < NC; ++i) asm volatile("" : "+v"(x[i][c].x), "+v"(x[i][c].y));
         #pragma unroll
-        for (int i = 0; i < NC; ++i) {
-          tq[j * NC + i] = red[i];
-          tg[j * NC + i] = red[NC + i];
-          if (j == 0) tv[i] = red[2 * NC + i];
-        }
+        for (int j = 0; j < SQ; ++j) asm volatile("" : "+v"(d[j][c].x), "+v"(d[j][c].y));
       }
-    }
-    __syncthreads();  // the table is complete
-
-    // per-row coefficients are uniform: scalar registers
-    float ri[NC], cc[NC], acc[NC][VPL][4];
+    };
+    // the row sums, one (query, source) pair at a time: each wave reduces
+    // its lanes and writes its sums to LDS
+    float* ws = wsum + (parity * g.W + wr) * NR;
+    float xx[NC];
     #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      ri[i] = uniformf(rsqrtf(uniformf(tv[i]) * g.invD + p.eps));
-      cc[i] = 0.f;
+    for (int i = 0; i < NC; ++i) xx[i] = 0.f;
+    #pragma unroll
+    for (int j = 0; j < SQ; ++j) {
+      launder();
+      // q~.x in fp32 (q~ is fp32); dh.x and x.x directly on the bf16 pairs
+      // (v_dot2_f32_bf16: exact products, fp32 accumulation)
+      float qf[VPL][4];
       #pragma unroll
-      for (int c = 0; c < VPL; ++c)
-        #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][c][e] = 0.f;
-    }
-    for (int j = 0; j < p.S; ++j) {
-      const float gs = p.dh_scale[j] ? p.dh_scale[j][row] : 1.f;
-      const float dl = p.dlse[j] ? p.dlse[j][row] : 0.f;
-      float sc[NC], al[NC];
-      float m = -FLT_MAX;
+      for (int c = 0; c < VPL; ++c) qload(j, c, qf[c]);
       #pragma unroll
       for (int i = 0; i < NC; ++i) {
-        sc[i] = uniformf(uniformf(tq[j * NC + i]) * ri[i]);
-        m = fmaxf(m, sc[i]);
-      }
-      float z = 0.f;
-      #pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        al[i] = uniformf(__expf(sc[i] - m));
-        z += al[i];
-      }
-      const float rz = uniformf(1.0f / z);
-      float gbar = 0.f;
-      #pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        al[i] = uniformf(al[i] * rz);
-        gbar += al[i] * (gs * uniformf(tg[j * NC + i]));
-      }
-      gbar = uniformf(gbar);
-      float dqj[VPL][4];
-      float q[VPL][4], dh[VPL][4];
-      #pragma unroll
-      for (int c = 0; c < VPL; ++c) {
-        load_query<4>(p.w[j], p.gm[j], voff[c] / F::kBytes * 4, q[c]);
-        F::unpack(d[j][c], dh[c]);
-        #pragma unroll
-        for (int e = 0; e < 4; ++e) dqj[c][e] = 0.f;
-      }
-      #pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        const float ds = al[i] * (gs * uniformf(tg[j * NC + i]) - gbar + dl);
-        const float A = uniformf(al[i] * gs), B = uniformf(ds * ri[i]);
-        cc[i] = uniformf(cc[i] + B * sc[i] * ri[i] * g.invD);
+        float a = 0.f, b = 0.f;
         #pragma unroll
         for (int c = 0; c < VPL; ++c) {
           float xf[4];
           F::unpack(x[i][c], xf);
           #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[i][c][e] += A * dh[c][e] + B * q[c][e];
-            dqj[c][e] += B * xf[e];
+          for (int e = 0; e < 4; ++e) a += qf[c][e] * xf[e];
+          b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, x[i][c].x),
+                                              __builtin_bit_cast(bf16x2v_t, d[j][c].x), b, false);
+          b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, x[i][c].y),
+                                              __builtin_bit_cast(bf16x2v_t, d[j][c].y), b, false);
+          if (j == 0) {
+            xx[i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, x[i][c].x),
+                                                    __builtin_bit_cast(bf16x2v_t, x[i][c].x), xx[i], false);
+            xx[i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, x[i][c].y),
+                                                    __builtin_bit_cast(bf16x2v_t, x[i][c].y), xx[i], false);
           }
         }
+        a = wave_sum(a);
+        b = wave_sum(b);
+        if (lane == 0) {
+          ws[j * NC + i] = a;
+          ws[(SQ + j) * NC + i] = b;
+        }
       }
-      // a query index is wave-uniform: unrolled selects keep dq in registers
-      #pragma unroll
-      for (int jj = 0; jj < kP1BwdQ; ++jj)
-        if (jj == j)
-          #pragma unroll
-          for (int c = 0; c < VPL; ++c)
-            #pragma unroll
-            for (int e = 0; e < 4; ++e) dq[jj][c][e] += dqj[c][e];
     }
+    #pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const float v = wave_sum(xx[i]);
+      if (lane == 0) ws[2 * SQ * NC + i] = v;
+    }
+    // one barrier per row: the sums alternate between two halves by row
+    // parity, so a wave may write the next row's sums while another still
+    // reads these
+    __syncthreads();
+    // The per-row coefficients, one (query, source) pair per lane: lane
+    // 8 j + i takes query j and source i; the softmax over a query's sources
+    // is a reduction over its 8-lane group. (Computed as uniform values they
+    // would cost every lane the whole table.)
+    const int jl = lane >> 3, il = lane & 7;
+    const bool valid = jl < SQ && il < NC;
+    float tq = 0.f, tg = 0.f, tv = 0.f;
+    if (valid) {
+      const float* w0 = wsum + parity * g.W * NR;
+      for (int w = 0; w < g.W; ++w) {
+        tq += w0[w * NR + jl * NC + il];
+        tg += w0[w * NR + (SQ + jl) * NC + il];
+        tv += w0[w * NR + 2 * SQ * NC + il];
+      }
+    }
+    // the query's row scale and log-sum-exp gradient (uniform per query)
+    float gs = 1.f, dl = 0.f;
+    #pragma unroll
+    for (int j = 0; j < SQ; ++j) {
+      const float gj = p.dh_scale[j] ? p.dh_scale[j][row] : 1.f;
+      const float dj = p.dlse[j] ? p.dlse[j][row] : 0.f;
+      gs = jl == j ? gj : gs;
+      dl = jl == j ? dj : dl;
+    }
+    const float rl = rsqrtf(tv * g.invD + p.eps);
+    const float sc = valid ? tq * rl : -FLT_MAX;
+    const float mx = group8_max(sc);
+    const float ex = valid ? __expf(sc - mx) : 0.f;
+    const float al = ex * (1.0f / group8_sum(ex));
+    const float gbar = group8_sum(al * (gs * tg));
+    const float Al = al * gs;
+    const float Bl = al * (gs * tg - gbar + dl) * rl;
+    // cc_i = sum over queries of B sc r / D: the lanes i, 8 + i, 16 + i, 24 + i
+    float ccl = valid ? Bl * sc * rl * g.invD : 0.f;
+    ccl += __shfl_xor(ccl, 8);
+    ccl += __shfl_xor(ccl, 16);
+    auto lane_val = [&](float v, int k) {
+      return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
+    };
+    float cc[NC];
+    #pragma unroll
+    for (int i = 0; i < NC; ++i) cc[i] = lane_val(ccl, i);
+    #pragma unroll
+    for (int j = 0; j < SQ; ++j) {
+      float A[NC], B[NC];
+      #pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        A[i] = lane_val(Al, 8 * j + i);
+        B[i] = lane_val(Bl, 8 * j + i);
+      }
+      launder();
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c) {
+        float q[4], dh[4], dq[4] = {0.f, 0.f, 0.f, 0.f};
+        qload(j, c, q);
+        F::unpack(d[j][c], dh);
+        #pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          float xf[4];
+          F::unpack(x[i][c], xf);
+          float o[4] = {__uint_as_float(dv[i][c].x), __uint_as_float(dv[i][c].y), __uint_as_float(dv[i][c].z),
+                        __uint_as_float(dv[i][c].w)};
+          #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[e] += A[i] * dh[e] + B[i] * q[e];
+            dq[e] += B[i] * xf[e];
+          }
+          dv[i][c] = make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                                __float_as_uint(o[3]));
+        }
+        if (in_row[c]) {
+          float4* acc = reinterpret_cast<float4*>(dqs + j * g.D + vec[c] * 4);
+          float4 a = *acc;
+          a.x += dq[0]; a.y += dq[1]; a.z += dq[2]; a.w += dq[3];
+          *acc = a;
+        }
+      }
+    }
+    launder();
     #pragma unroll
     for (int i = 0; i < NC; ++i)
       #pragma unroll
       for (int c = 0; c < VPL; ++c) {
-        if (!in_row[c]) continue;
-        float* dst = p.dV[i] + row * g.D + voff[c] / F::kBytes * 4;
-        const uint4 u = ld16_stream(dst);
         float xf[4];
         F::unpack(x[i][c], xf);
-        float o[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)};
+        float o[4] = {__uint_as_float(dv[i][c].x), __uint_as_float(dv[i][c].y), __uint_as_float(dv[i][c].z),
+                      __uint_as_float(dv[i][c].w)};
         #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] += acc[i][c][e] - cc[i] * xf[e];
+        for (int e = 0; e < 4; ++e) o[e] -= cc[i] * xf[e];
+        char* dst = store_target(in_row[c], reinterpret_cast<char*>(p.dV[i] + row * g.D + (int64_t)vec[c] * 4));
         st16_stream(dst, make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
                                     __float_as_uint(o[3])));
       }
   }
   #pragma unroll
-  for (int j = 0; j < kP1BwdQ; ++j)
-    if (j < p.S)
-      #pragma unroll
-      for (int c = 0; c < VPL; ++c)
-        if (in_row[c]) {
-          float* prow = p.partial + ((int64_t)j * gridDim.x + blockIdx.x) * g.D + voff[c] / F::kBytes * 4;
-          st16(prow, make_uint4(__float_as_uint(dq[j][c][0]), __float_as_uint(dq[j][c][1]),
-                                __float_as_uint(dq[j][c][2]), __float_as_uint(dq[j][c][3])));
-        }
+  for (int j = 0; j < SQ; ++j)
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c)
+      if (in_row[c]) {
+        float* prow = p.partial + ((int64_t)j * gridDim.x + blockIdx.x) * g.D + vec[c] * 4;
+        const float4 a = *reinterpret_cast<const float4*>(dqs + j * g.D + vec[c] * 4);
+        st16(prow, make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z),
+                              __float_as_uint(a.w)));
+      }
 }
 
 // Column sums of a [rows][D] fp32 matrix over consecutive row chunks, each in
@@ -3369,7 +3451,7 @@ hipError_t launch_bwd_reduce(const BwdArgs& a, const BwdPlan& pl, int stage, con
 }
 
 #ifndef ATTNRES_P1BWD_GROUPS
-#define ATTNRES_P1BWD_GROUPS 256  // workgroups of the batched Phase-1 backward (each walks rows)
+#define ATTNRES_P1BWD_GROUPS 512  // workgroups of the batched Phase-1 backward (each walks rows)
 #endif
 
 // up to 6 sources: beyond, the register budget of two vectors per lane spills
@@ -3384,10 +3466,20 @@ size_t phase1_bwd_workspace(int64_t R, int64_t D) {
   return align256((size_t)kP1BwdQ * grid * D * 4) + align256((size_t)chunks * D * 4);
 }
 
+template <int NC, int SQ>
+static hipError_t launch_p1bwd_q(const P1BwdParams& p, unsigned grid, const Launch& L) {
+  const size_t lds = ((size_t)2 * SQ * p.g.D + (size_t)2 * p.g.W * (2 * SQ + 1) * NC) * sizeof(float);
+  return launch(L, phase1_bwd_kernel<NC, SQ>, dim3(grid), dim3(64 * p.g.W), lds, p);
+}
+
 template <int NC>
 static hipError_t launch_p1bwd_t(const P1BwdParams& p, unsigned grid, const Launch& L) {
-  const size_t lds = (size_t)p.g.W * 3 * NC * sizeof(float);
-  return launch(L, phase1_bwd_kernel<NC>, dim3(grid), dim3(64 * p.g.W), lds, p);
+  switch (p.S) {
+    case 1: return launch_p1bwd_q<NC, 1>(p, grid, L);
+    case 2: return launch_p1bwd_q<NC, 2>(p, grid, L);
+    case 3: return launch_p1bwd_q<NC, 3>(p, grid, L);
+    default: return launch_p1bwd_q<NC, 4>(p, grid, L);
+  }
 }
 
 hipError_t launch_phase1_bwd(const Phase1BwdArgs& a, void* ws, const Launch& L, const Launch& Lred) {

@@ -69,7 +69,7 @@ def test_traffic_from_counters(tmp_path, monkeypatch):
     1 GiB gives factor 2."""
     b = load_bench()
     out_json, out_txt = tmp_path / "t.json", tmp_path / "t.txt"
-    monkeypatch.setattr(b, "traffic_paths", lambda backward: (str(out_json), str(out_txt),
+    monkeypatch.setattr(b, "traffic_paths", lambda backward, workload="block_L48_S8": (str(out_json), str(out_txt),
                                                               "attnres::phase2_kernel", ""))
     gib_kib = float(1 << 20)
 
