@@ -2154,8 +2154,7 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
 // as a launch of its own.
 // ---------------------------------------------------------------------------
 constexpr int kGWaves = 16;   // waves per scores workgroup, 2 rows each
-constexpr int kGChunk = 128;  // hidden elements per staged chunk of Qp
-constexpr int kGPad = 16;     // LDS row padding (elements): 8 left bank conflicts on the Qp reads
+constexpr int kGChunk = 128;  // rows are a whole number of 2 x 128 elements
 
 struct QSplitParams {
   const float* W;  // [S][D]
@@ -2198,143 +2197,166 @@ struct P1GParams {
   float* lse_out;    // [S][R]
 };
 
-// One chunk of the scores product: issue the next chunk's Qp staging loads
-// and source loads (into st and bn), then the current chunk's products from
-// b and the Qp chunk in LDS buffer `cur` (this lane reads row `col` of each
-// 16-row tile, k-group `g4`), then stage the next Qp chunk in buffer `nxt`.
-template <int MT>
-__device__ __forceinline__ void gemm_chunk(const uint4 (&b)[4], uint4 (&bn)[4], u32x4_t (&st)[(MT + 1) / 2],
-                                           f32x4_t (&acc)[2 * MT], float& ss0, float& ss1,
-                                           const __bf16* const (&aptr)[(MT + 1) / 2],
-                                           const int (&aoff)[(MT + 1) / 2], int cn, const char* bp,
-                                           const __bf16* cur, __bf16* nxt, int col, int g4) {
-  constexpr int AROW = kGChunk + kGPad;
-  constexpr int U = (MT + 1) / 2;
-  const __bf16* ab = cur + col * AROW + 8 * g4;
-  #pragma unroll
-  for (int u = 0; u < U; ++u) st[u] = *reinterpret_cast<const u32x4_t*>(aptr[u] + cn * kGChunk);
-  #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) bn[ks] = ld16_stream(bp + (int64_t)cn * (kGChunk * 2) + 64 * ks);
-  __builtin_amdgcn_sched_barrier(0);  // the prefetch stays ahead of this chunk's work
-  #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    float& ss = (ks & 1) ? ss1 : ss0;
-    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b[ks].x),
-                                         __builtin_bit_cast(bf16x2v_t, b[ks].x), ss, false);
-    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b[ks].y),
-                                         __builtin_bit_cast(bf16x2v_t, b[ks].y), ss, false);
-    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b[ks].z),
-                                         __builtin_bit_cast(bf16x2v_t, b[ks].z), ss, false);
-    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b[ks].w),
-                                         __builtin_bit_cast(bf16x2v_t, b[ks].w), ss, false);
-    #pragma unroll
-    for (int t = 0; t < 2 * MT; ++t) {
-      const uint4 a = *reinterpret_cast<const uint4*>(ab + t * 16 * AROW + 32 * ks);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                       __builtin_bit_cast(bf16x8_t, b[ks]), acc[t], 0, 0, 0);
-    }
-  }
-  #pragma unroll
-  for (int u = 0; u < U; ++u) *reinterpret_cast<u32x4_t*>(nxt + aoff[u]) = st[u];
-  lds_barrier();  // this chunk's Qp reads are done; the next chunk's are in LDS
+// The scores pass stages its operands in LDS. A step is 64 hidden elements:
+// 128 bytes of each of a wave's 16 source columns and of each of the 32 MT Qp
+// rows. Both are copied with global_load_lds_dwordx4, 16 bytes per lane, so
+// that one instruction moves whole 128-byte lines (eight of them per KiB):
+// loading the sources straight into the matrix-core operand layout left each
+// load touching 16 half-lines, and the address unit then stalled on the L1.
+// A copy lane fetches piece s ^ f(r) of its row r (f(r) = (r >> 1) & 7) into
+// slot s, so the operand reads (16 lanes, one per row, the same piece) meet 16
+// different bank groups.
+constexpr int kGStep = 64;  // hidden elements per step
+constexpr int kGRing = 3;   // source steps per wave in LDS (two copies in flight)
+
+__device__ __forceinline__ int gswz(int r) { return (r >> 1) & 7; }
+
+// 16 bytes per lane from a per-lane global address into LDS at
+// lds + 16 * lane; `nt` marks a stream read once. Issued as inline assembly,
+// so the compiler adds no waits for it: the kernel counts its own copies
+// (p1_wait). M0 is written here and nowhere else in the kernel.
+template <bool NTC>
+__device__ __forceinline__ void dma16_lane(const char* g, uint32_t lds) {
+  if constexpr (NTC)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(g) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(g) : "memory");
 }
 
 template <int MT, int NPR>
 __global__ __launch_bounds__(1024) void phase1_gemm_scores_kernel(P1GParams p) {
-  constexpr int AROW = kGChunk + kGPad;
-  constexpr int U = (MT + 1) / 2;       // Qp staging units per thread
   constexpr int RW = 16 / NPR;          // rows per wave: NPR source columns each
   constexpr int RT = kGWaves * RW;      // rows per tile
   constexpr int AST = NPR > 8 ? 16 : 8; // row stride of the weights
-  __shared__ __attribute__((aligned(16))) __bf16 abuf[2][MT * 32 * AROW];
+  constexpr int AB = MT * 32 * 128;     // bytes of one Qp step
+  __shared__ __attribute__((aligned(16))) char abuf[2][AB];
+  __shared__ __attribute__((aligned(16))) char bbuf[kGWaves][kGRing][16 * 128];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int col = l & 15, g4 = l >> 4;        // B column and k-group
   const int rl = col / NPR, i = col % NPR;    // row of the wave's RW, source
   const int64_t rowbytes = (int64_t)p.D * 2;
-  const int nchunks = p.D / kGChunk;
+  const int nsteps = p.D / kGStep;
   const int64_t tiles = (p.R + RT - 1) / RT;
+  // this workgroup's tiles blockIdx.x, blockIdx.x + gridDim.x, ...: their
+  // steps form one sequence k = tile step * nsteps + step
+  const int64_t my_tiles = blockIdx.x < tiles ? (tiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  const int64_t steps = my_tiles * nsteps;
+  const int aw = w < 4 * MT ? 1 : 0;  // waves 0 .. 4 MT - 1 copy 8 Qp rows each per step
 
-  // this lane's 16-byte pieces of each chunk of its column's source in tile
-  // t (row 0 past the end, source 0 past n: read, then discarded)
-  const char* src_i = static_cast<const char*>(p.src[i < p.n ? i : 0]) + g4 * 16;
-  auto bptr_of = [&](int64_t t) -> const char* {
-    const int64_t r = t * RT + w * RW + rl;
-    return src_i + (r < p.R ? r : 0) * rowbytes;
-  };
-  // Qp staging: thread tid copies 16-byte unit tid + 1024 u of a chunk's
-  // 512 MT units; for odd MT the units past the end repeat the 512 below them
-  // (the same value written to the same place twice)
-  const __bf16* aptr[U];
-  int aoff[U];
+  // Copy lanes. Sources: instruction m (0, 1) of a step moves columns
+  // 8 m .. 8 m + 7 of the wave, 8 lanes (one line) per column; a column past
+  // n reads source 0 and a row past R reads row 0 (both discarded).
+  const int cs = l & 7;
+  const char* bsrc[2];
+  int brl[2];
   #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    int idx = tid + 1024 * u;
-    if (idx >= 512 * MT) idx -= 512;
-    const int a = idx >> 4, c16 = idx & 15;
-    aptr[u] = p.qp + (int64_t)a * p.D + 8 * c16;
-    aoff[u] = a * AROW + 8 * c16;
+  for (int m = 0; m < 2; ++m) {
+    const int c = 8 * m + (l >> 3);
+    const int ic = c % NPR;
+    brl[m] = c / NPR;
+    bsrc[m] = static_cast<const char*>(p.src[ic < p.n ? ic : 0]) + 16 * (cs ^ gswz(c));
   }
+  auto bcopy = [&](int64_t k) {
+    const int64_t tj = k / nsteps;
+    const int st = (int)(k - tj * nsteps);
+    const int64_t tile = blockIdx.x + tj * gridDim.x;
+    const uint32_t dst = lds_offset(&bbuf[w][(int)(k % kGRing)][0]);
+    #pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int64_t r = tile * RT + w * RW + brl[m];
+      dma16_lane<true>(bsrc[m] + (r < p.R ? r : 0) * rowbytes + (int64_t)st * 128, dst + 1024u * m);
+    }
+  };
+  // Qp: rows 8 w .. 8 w + 7 (the same for every tile, so cached)
+  const int ar = 8 * (aw ? w : 0) + (l >> 3);
+  const char* asrc = reinterpret_cast<const char*>(p.qp) + (int64_t)ar * rowbytes + 16 * (cs ^ gswz(ar));
+  auto acopy = [&](int64_t k) {
+    if (aw) dma16_lane<false>(asrc + (int64_t)(k % nsteps) * 128, lds_offset(&abuf[(int)(k & 1)][w * 1024]));
+  };
 
-  // The chunk loop runs across tiles without a break: the last chunk of a
-  // tile loads chunk 0 of the workgroup's next tile, and the LDS buffers
-  // alternate throughout. Every load is issued unconditionally. (The staging
-  // registers are native vectors: struct copies between global memory,
-  // registers and LDS would keep them in scratch memory.)
-  uint4 b[4], bn[4];
-  u32x4_t st[U];
-  int buf = 0;
-  const char* bptr = bptr_of(blockIdx.x);
-  #pragma unroll
-  for (int u = 0; u < U; ++u) st[u] = *reinterpret_cast<const u32x4_t*>(aptr[u]);
-  #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) b[ks] = ld16_stream(bptr + 64 * ks);
-  #pragma unroll
-  for (int u = 0; u < U; ++u) *reinterpret_cast<u32x4_t*>(&abuf[0][aoff[u]]) = st[u];
+  // Order of a wave's copies: A(0), B(0), B(1), then per step k: A(k+1),
+  // B(k+2). Step k needs B(k), after which at most 4 + aw copies were
+  // issued (4 + aw at k = 0, 4 + 2 aw later: waiting for fewer is only
+  // stricter); its barrier needs A(k+1), after which come the 2 copies of
+  // B(k+2) (and, at a tile's end, the weight stores).
+  acopy(0);
+  bcopy(0);
+  bcopy(1);
+  p1_wait(4);
   lds_barrier();
 
-  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-    const int64_t row = tile * RT + w * RW + rl;
-    const bool rv = row < p.R;
-    const char* bnext = bptr_of(tile + gridDim.x);
-    f32x4_t acc[2 * MT];
-    #pragma unroll
-    for (int t = 0; t < 2 * MT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float ss0 = 0.f, ss1 = 0.f;
-    // chunks in pairs (D is a multiple of 256), the two register sets
-    // trading roles; the tile's last chunk prefetches the next tile's first
-    for (int c = 0; c < nchunks; c += 2) {
-      gemm_chunk<MT>(b, bn, st, acc, ss0, ss1, aptr, aoff, c + 1, bptr, abuf[buf], abuf[buf ^ 1], col, g4);
-      buf ^= 1;
-      const bool last = c + 2 == nchunks;
-      gemm_chunk<MT>(bn, b, st, acc, ss0, ss1, aptr, aoff, last ? 0 : c + 2, last ? bnext : bptr,
-                     abuf[buf], abuf[buf ^ 1], col, g4);
-      buf ^= 1;
-    }
-    bptr = bnext;
+  f32x4_t acc[2 * MT];
+  #pragma unroll
+  for (int t = 0; t < 2 * MT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float ss0 = 0.f, ss1 = 0.f;
+  int st = 0;  // step within the current tile
+  int64_t tile = blockIdx.x;
+  const int sw = gswz(col);  // the swizzle of this lane's operand row (A: 16 t + col; B: col)
 
-    // scores, softmax over the row's NPR lanes, weights and statistics
-    float ss = ss0 + ss1;
-    ss += __shfl_xor(ss, 16);  // the four k-groups of this column
-    ss += __shfl_xor(ss, 32);
-    const float inv = rsqrtf(ss * p.invD + p.eps);
-    const bool valid = i < p.n;
+  for (int64_t k = 0; k < steps; ++k) {
+    acopy(k + 1);
+    bcopy(k + 2);
+    p1_wait(4 + aw);
+    asm volatile("" ::: "memory");  // the LDS reads below stay after the wait
+    const char* bb = &bbuf[w][(int)(k % kGRing)][col * 128];
+    const char* ab = &abuf[(int)(k & 1)][col * 128];
     #pragma unroll
-    for (int t = 0; t < 2 * MT; ++t) {
-      // accumulators 0..2 of k-group g4: parts 0..2 of query 4 t + g4
-      const int s = 4 * t + g4;
-      const float sc = ((acc[t][0] + acc[t][1]) + acc[t][2]) * inv;
-      const float m = groupn_max<NPR>(valid ? sc : -INFINITY);
-      const float e = valid ? __expf(sc - m) : 0.f;
-      const float z = groupn_sum<NPR>(e);
-      if (rv && s < p.S) {
-        p.alpha[((int64_t)s * p.R + row) * AST + i] = e * (1.0f / z);
-        if (i == 0) {
-          if (p.m_out) p.m_out[(int64_t)s * p.R + row] = m;
-          p.lse_out[(int64_t)s * p.R + row] = m + __logf(z);
-        }
+    for (int ks = 0; ks < 2; ++ks) {
+      const int slot = 16 * ((4 * ks + g4) ^ sw);
+      const uint4 b = *reinterpret_cast<const uint4*>(bb + slot);
+      float& ss = ks ? ss1 : ss0;
+      ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b.x), __builtin_bit_cast(bf16x2v_t, b.x),
+                                           ss, false);
+      ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b.y), __builtin_bit_cast(bf16x2v_t, b.y),
+                                           ss, false);
+      ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b.z), __builtin_bit_cast(bf16x2v_t, b.z),
+                                           ss, false);
+      ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, b.w), __builtin_bit_cast(bf16x2v_t, b.w),
+                                           ss, false);
+      #pragma unroll
+      for (int t = 0; t < 2 * MT; ++t) {
+        const uint4 a = *reinterpret_cast<const uint4*>(ab + t * 16 * 128 + slot);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                         __builtin_bit_cast(bf16x8_t, b), acc[t], 0, 0, 0);
       }
     }
+    if (++st == nsteps) {
+      // scores, softmax over the row's NPR lanes, weights and statistics
+      st = 0;
+      const int64_t row = tile * RT + w * RW + rl;
+      const bool rv = row < p.R;
+      float ss = ss0 + ss1;
+      ss += __shfl_xor(ss, 16);  // the four k-groups of this column
+      ss += __shfl_xor(ss, 32);
+      const float inv = rsqrtf(ss * p.invD + p.eps);
+      const bool valid = i < p.n;
+      #pragma unroll
+      for (int t = 0; t < 2 * MT; ++t) {
+        // accumulators 0..2 of k-group g4: parts 0..2 of query 4 t + g4
+        const int s = 4 * t + g4;
+        const float sc = ((acc[t][0] + acc[t][1]) + acc[t][2]) * inv;
+        const float m = groupn_max<NPR>(valid ? sc : -INFINITY);
+        const float e = valid ? __expf(sc - m) : 0.f;
+        const float z = groupn_sum<NPR>(e);
+        if (rv && s < p.S) {
+          p.alpha[((int64_t)s * p.R + row) * AST + i] = e * (1.0f / z);
+          if (i == 0) {
+            if (p.m_out) p.m_out[(int64_t)s * p.R + row] = m;
+            p.lse_out[(int64_t)s * p.R + row] = m + __logf(z);
+          }
+        }
+        acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      ss0 = 0.f;
+      ss1 = 0.f;
+      tile += gridDim.x;
+    }
+    p1_wait(2);
+    lds_barrier();  // A(k+1) is in LDS; every read of A(k) and B(k) is done
   }
+  p1_wait(0);  // no copy may still be landing in LDS when the workgroup ends
 }
 
 struct P1OParams {
