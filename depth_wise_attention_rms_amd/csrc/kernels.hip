@@ -2207,7 +2207,12 @@ struct P1GParams {
 // slot s, so the operand reads (16 lanes, one per row, the same piece) meet 16
 // different bank groups.
 constexpr int kGStep = 64;  // hidden elements per step
-constexpr int kGRing = 3;   // source steps per wave in LDS (two copies in flight)
+#ifndef ATTNRES_GEMM_RING
+#define ATTNRES_GEMM_RING 4
+#endif
+// source steps per wave in LDS (kGRing - 1 copies in flight); 16 waves x 4 x
+// 2 KiB plus the Qp buffers of 4 tiles is the 160 KiB of a CU
+constexpr int kGRing = ATTNRES_GEMM_RING;
 
 __device__ __forceinline__ int gswz(int r) { return (r >> 1) & 7; }
 
@@ -2276,15 +2281,17 @@ __global__ __launch_bounds__(1024) void phase1_gemm_scores_kernel(P1GParams p) {
     if (aw) dma16_lane<false>(asrc + (int64_t)(k % nsteps) * 128, lds_offset(&abuf[(int)(k & 1)][w * 1024]));
   };
 
-  // Order of a wave's copies: A(0), B(0), B(1), then per step k: A(k+1),
-  // B(k+2). Step k needs B(k), after which at most 4 + aw copies were
-  // issued (4 + aw at k = 0, 4 + 2 aw later: waiting for fewer is only
-  // stricter); its barrier needs A(k+1), after which come the 2 copies of
-  // B(k+2) (and, at a tile's end, the weight stores).
+  // Order of a wave's copies (2 instructions per B step, aw per A step):
+  // A(0), B(0) .. B(P - 1), then per step k: A(k+1), B(k+P), with P =
+  // kGRing - 1. Step k needs B(k), after which at least 2 P + aw copies were
+  // issued (2 P + aw at k = 0, up to 2 P + P aw later: waiting for fewer is
+  // only stricter); its barrier needs A(k+1), after which come the 2 copies
+  // of B(k+P) (and, at a tile's end, the weight stores).
+  constexpr int P = kGRing - 1;
   acopy(0);
-  bcopy(0);
-  bcopy(1);
-  p1_wait(4);
+  #pragma unroll
+  for (int j = 0; j < P; ++j) bcopy(j);
+  p1_wait(2 * P);
   lds_barrier();
 
   f32x4_t acc[2 * MT];
@@ -2297,8 +2304,8 @@ __global__ __launch_bounds__(1024) void phase1_gemm_scores_kernel(P1GParams p) {
 
   for (int64_t k = 0; k < steps; ++k) {
     acopy(k + 1);
-    bcopy(k + 2);
-    p1_wait(4 + aw);
+    bcopy(k + P);
+    p1_wait(2 * P + aw);
     asm volatile("" ::: "memory");  // the LDS reads below stay after the wait
     const char* bb = &bbuf[w][(int)(k % kGRing)][col * 128];
     const char* ab = &abuf[(int)(k & 1)][col * 128];
