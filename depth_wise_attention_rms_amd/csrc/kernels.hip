@@ -2130,14 +2130,11 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
 // the fp32 query, row j = 3 zero), and B is [D, rows x 8]: column 8 r + i is
 // source i of row r. It runs on the matrix cores (v_mfma_f32_16x16x32_bf16,
 // fp32 accumulation): each wave owns 16 columns and all 2 MT 16-row tiles
-// of Qp (4 queries each), whose 128-element chunks are staged in LDS once per
-// workgroup of 16 waves and read by all of them. In k-step
-// ks of a chunk, k-group g of a lane holds elements 32 ks + 8 g ..
-// 32 ks + 8 g + 7 (A and B alike), so the four lanes of a column read 64
-// adjacent bytes of its source per load: each load touches 2 lines per row
-// and source where 32x32 tiles (2 lanes per column) touched 4, which took a
-// block of the long-context shape from 14.5 to 11.6 ms. Sums of squares come
-// from the same B registers (v_dot2). After the last chunk each lane holds,
+// of Qp (4 queries each). Both operands pass through LDS in steps of 64
+// hidden elements (see phase1_gemm_scores_kernel). In k-step ks of a step,
+// k-group g of a lane holds elements 32 ks + 8 g .. 32 ks + 8 g + 7 (A and B
+// alike). Sums of squares come from the same B registers (v_dot2). After the
+// last step each lane holds,
 // for its column, the three parts of one query per tile; their sum scaled by
 // the source's 1 / rms is the score. A row takes NPR columns, the smallest of
 // 1, 2, 4, 8 or 16 that holds its n sources (so a tile holds 16 / NPR rows
@@ -2153,7 +2150,7 @@ __global__ __launch_bounds__(512) void phase1_stream_kernel(Phase1SParams p) {
 // 4 in registers would move (passes x n + S). A block close runs before them
 // as a launch of its own.
 // ---------------------------------------------------------------------------
-constexpr int kGWaves = 16;   // waves per scores workgroup, 2 rows each
+constexpr int kGWaves = 16;   // waves per scores workgroup, 16 source columns each
 constexpr int kGChunk = 128;  // rows are a whole number of 2 x 128 elements
 
 struct QSplitParams {
