@@ -1470,8 +1470,20 @@ ATTNRES_API int attnres_block_stack_backward(
     auto p_slice = [&](int j) -> const void* {  // the partial seen by sublayer start + j (j >= 1)
       return j == 1 ? v[start - 1] : static_cast<const void*>(ws + lay.p + (int64_t)(j - 2) * tensor_bytes);
     };
-    for (int j = 2; j < Sk; ++j)
-      TRY(do_close(fn, p_slice(j - 1), v[start + j - 2], const_cast<void*>(p_slice(j)), R, D, dtype, st));
+    if (Sk >= 3 && Sk - 1 <= attnres::kPartialsMax) {
+      // p_2 .. p_{Sk-1} in one pass over v_start .. v_{start+Sk-2}
+      std::vector<const void*> in(Sk - 1);
+      std::vector<void*> out(Sk - 1, nullptr);
+      for (int t = 0; t < Sk - 1; ++t) in[t] = v[start - 1 + t];
+      for (int t = 1; t < Sk - 1; ++t) out[t] = const_cast<void*>(p_slice(t + 1));
+      hipError_t e = attnres::launch_partials(
+          dtype, in.data(), out.data(), Sk - 1, R, D,
+          timed_launch(K_CLOSE, (double)R * D * esize_of(dtype) * (2 * Sk - 3), st, "partials_kernel"));
+      if (e != hipSuccess) return hip_fail(fn, e);
+    } else {
+      for (int j = 2; j < Sk; ++j)
+        TRY(do_close(fn, p_slice(j - 1), v[start + j - 2], const_cast<void*>(p_slice(j)), R, D, dtype, st));
+    }
     // Phase-2 merges in reverse: sublayer start + j merged (lse_j, o_j) with p_j;
     // its backward turns dh into the gradient of p_j, which (with the gradient
     // from the partial's later uses, dv[start + j - 1]) is that of v_{start+j-1}

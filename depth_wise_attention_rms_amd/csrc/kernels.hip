@@ -2746,6 +2746,51 @@ __global__ void close_kernel(const void* __restrict__ pp, const void* __restrict
   }
 }
 
+// A block's partial sums in one pass [K3 9.3 listing: p grows by each
+// sublayer output, rounded to the I/O dtype after every add]: from
+// in[0] = p_1 and the later outputs in[1..n-1], out[t] = p_{t+1} =
+// round(p_t + in[t]) for t = 1..n-1, the same adds and roundings as a chain
+// of block closes, with each partial read from registers instead of memory.
+// Inputs are loaded eight at a time and unconditionally (an index past n
+// reads the last input again and is discarded).
+struct PartialsParams {
+  const void* in[kPartialsMax];
+  void* out[kPartialsMax];  // out[0] unused
+  int n;
+  int64_t nvec;  // 16-byte vectors per tensor
+};
+
+template <class T>
+__global__ void partials_kernel(PartialsParams p) {
+  constexpr int EPV = T::kEPV;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < p.nvec;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t off = i * 16;
+    float fa[EPV];
+    T::unpack(ld16_stream(static_cast<const char*>(p.in[0]) + off), fa);
+    for (int t0 = 1; t0 < p.n; t0 += 8) {
+      uint4 x[8];
+      #pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int t = t0 + u < p.n ? t0 + u : p.n - 1;
+        x[u] = ld16_stream(static_cast<const char*>(p.in[t]) + off);
+      }
+      #pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (t0 + u < p.n) {  // uniform across the grid
+          float fv[EPV];
+          T::unpack(x[u], fv);
+          #pragma unroll
+          for (int e = 0; e < EPV; ++e) fa[e] += fv[e];
+          const uint4 v = T::pack(fa);  // the partial, rounded to the I/O dtype
+          T::unpack(v, fa);
+          st16_stream(static_cast<char*>(p.out[t0 + u]) + off, v);
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launchers (called from api.hip).
 // ---------------------------------------------------------------------------
@@ -3337,6 +3382,23 @@ hipError_t launch_rmsnorm(int dtype, const void* x, int64_t R, int64_t D, const 
 #ifndef ATTNRES_CLOSE_MAX_GROUPS
 #define ATTNRES_CLOSE_MAX_GROUPS (1 << 20)  // workgroups of a standalone close: one vector per lane (grid-stride beyond)
 #endif
+
+hipError_t launch_partials(int dtype, const void* const* in, void* const* out, int n, int64_t R, int64_t D,
+                           const Launch& L) {
+  if (n < 2 || n > kPartialsMax) return hipErrorInvalidValue;
+  PartialsParams p;
+  for (int t = 0; t < kPartialsMax; ++t) {
+    p.in[t] = t < n ? in[t] : in[0];
+    p.out[t] = t < n ? out[t] : nullptr;
+  }
+  p.n = n;
+  p.nvec = R * D * (dtype == 1 ? 2 : 4) / 16;
+  if (p.nvec == 0) return hipSuccess;
+  int64_t blocks = (p.nvec + 255) / 256;
+  if (blocks > ATTNRES_CLOSE_MAX_GROUPS) blocks = ATTNRES_CLOSE_MAX_GROUPS;
+  if (dtype == 1) return launch(L, partials_kernel<Bf16>, dim3((unsigned)blocks), dim3(256), 0, p);
+  return launch(L, partials_kernel<F32>, dim3((unsigned)blocks), dim3(256), 0, p);
+}
 
 hipError_t launch_close(int dtype, const void* p, const void* v, void* b, int64_t R, int64_t D,
                         const Launch& L) {

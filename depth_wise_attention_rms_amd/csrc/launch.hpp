@@ -209,6 +209,11 @@ hipError_t launch_aggregate(int dtype, const AggArgs& a, const Launch& L);
 hipError_t launch_phase2(int dtype, const Phase2Args& a, const Launch& L);
 hipError_t launch_rmsnorm(int dtype, const void* x, int64_t R, int64_t D, const float* g, float eps,
                           void* out, const Launch& L);
+// A block's partials in one pass: out[t] = round(p + in[t]) chained from
+// p = in[0], t = 1..n-1 (2 <= n <= kPartialsMax; out[0] unused).
+constexpr int kPartialsMax = 64;
+hipError_t launch_partials(int dtype, const void* const* in, void* const* out, int n, int64_t R, int64_t D,
+                           const Launch& L);
 hipError_t launch_close(int dtype, const void* p, const void* v, void* b, int64_t R, int64_t D,
                         const Launch& L);
 
