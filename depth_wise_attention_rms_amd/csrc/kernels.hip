@@ -1847,6 +1847,9 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
 // ascending row order: out[k][d] = sum of in[r][d] for r in chunk k. With
 // FINISH the single chunk's sum t gives dw = t * gamma (t without a gain) and
 // dgamma = t * w, written or added. One thread owns four columns.
+// blockIdx.z selects one of several queries whose partial rows lie qin
+// floats apart (their chunk sums qout apart; w, gamma, dw and dgamma rows D
+// apart); bit q of acc_mask says whether query q adds to dw / dgamma.
 template <bool FINISH>
 __global__ __launch_bounds__(256) void bwd_colsum_kernel(const float* __restrict__ in,
                                                          int64_t rows, int64_t D, int64_t chunk,
@@ -1855,9 +1858,19 @@ __global__ __launch_bounds__(256) void bwd_colsum_kernel(const float* __restrict
                                                          const float* __restrict__ gm,
                                                          float* __restrict__ dw,
                                                          float* __restrict__ dgamma,
-                                                         int accumulate) {
+                                                         unsigned acc_mask, int64_t qin, int64_t qout) {
   const int64_t d = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (d >= D) return;
+  const int q = blockIdx.z;
+  in += q * qin;
+  if (!FINISH) out += q * qout;
+  if (FINISH) {
+    if (w) w += q * D;
+    if (gm) gm += q * D;
+    dw += q * D;
+    if (dgamma) dgamma += q * D;
+  }
+  const int accumulate = (acc_mask >> q) & 1u;
   const int64_t r0 = (int64_t)blockIdx.y * chunk;
   const int64_t r1 = r0 + chunk < rows ? r0 + chunk : rows;
   float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -3529,13 +3542,13 @@ hipError_t launch_bwd_reduce(const BwdArgs& a, const BwdPlan& pl, int stage, con
     if (pl.P2 == 0) return hipSuccess;
     return launch(L, bwd_colsum_kernel<false>, dim3(bx, (unsigned)pl.P2), dim3(256), 0, partial,
                   pl.P, a.D, pl.chunk, stage1, (const float*)nullptr, (const float*)nullptr,
-                  (float*)nullptr, (float*)nullptr, 0);
+                  (float*)nullptr, (float*)nullptr, 0u, (int64_t)0, (int64_t)0);
   }
   const float* in = pl.P2 ? stage1 : partial;
   const int64_t rows = pl.P2 ? pl.P2 : pl.P;
   return launch(L, bwd_colsum_kernel<true>, dim3(bx, 1), dim3(256), 0, in, rows, a.D, rows,
                 (float*)nullptr, a.w, a.g, a.dw, a.dgamma,
-                a.accumulate_q < 0 ? a.accumulate : a.accumulate_q);
+                (unsigned)((a.accumulate_q < 0 ? a.accumulate : a.accumulate_q) ? 1 : 0), (int64_t)0, (int64_t)0);
 }
 
 #ifndef ATTNRES_P1BWD_GROUPS
@@ -3551,7 +3564,7 @@ bool phase1_bwd_eligible(int dtype, int n, int64_t D) {
 size_t phase1_bwd_workspace(int64_t R, int64_t D) {
   const int64_t grid = R < ATTNRES_P1BWD_GROUPS ? (R > 0 ? R : 1) : ATTNRES_P1BWD_GROUPS;
   const int64_t chunks = (grid + ATTNRES_BWD_CHUNK - 1) / ATTNRES_BWD_CHUNK;
-  return align256((size_t)kP1BwdQ * grid * D * 4) + align256((size_t)chunks * D * 4);
+  return align256((size_t)kP1BwdQ * grid * D * 4) + align256((size_t)kP1BwdQ * chunks * D * 4);
 }
 
 template <int NC, int SQ>
@@ -3607,29 +3620,22 @@ hipError_t launch_phase1_bwd(const Phase1BwdArgs& a, void* ws, const Launch& L, 
   const unsigned bx = (unsigned)((a.D / 4 + 255) / 256);
   const int64_t chunk = ATTNRES_BWD_CHUNK;
   const int64_t P2 = grid > chunk ? ((int64_t)grid + chunk - 1) / chunk : 0;
-  // timed from the first reduction's start to the last one's end
-  const Launch first{Lred.stream, Lred.start, nullptr}, mid{Lred.stream, nullptr, nullptr};
-  for (int j = 0; j < a.S; ++j) {
-    const Launch& L0 = j == 0 ? first : mid;
-    const Launch L1{Lred.stream, nullptr, j + 1 == a.S ? Lred.stop : nullptr};
-    const Launch& L1a = (j == 0 && !P2) ? Launch{Lred.stream, Lred.start, L1.stop} : L1;
-    const float* part = p.partial + (int64_t)j * grid * a.D;
-    const float* wj = a.w + (int64_t)j * a.D;
-    const float* gj = a.g ? a.g + (int64_t)j * a.D : nullptr;
-    float* dwj = a.dw + (int64_t)j * a.D;
-    float* dgj = a.dgamma ? a.dgamma + (int64_t)j * a.D : nullptr;
-    if (P2) {
-      e = launch(L0, bwd_colsum_kernel<false>, dim3(bx, (unsigned)P2), dim3(256), 0, part, (int64_t)grid, a.D,
-                 chunk, stage1, (const float*)nullptr, (const float*)nullptr, (float*)nullptr, (float*)nullptr, 0);
-      if (e != hipSuccess) return e;
-    }
-    const float* in = P2 ? stage1 : part;
-    const int64_t rows = P2 ? P2 : grid;
-    e = launch(L1a, bwd_colsum_kernel<true>, dim3(bx, 1), dim3(256), 0, in, rows, a.D, rows, (float*)nullptr,
-               wj, gj, dwj, dgj, a.accumulate_q[j]);
+  // every query in one launch per stage (blockIdx.z = query), timed from the
+  // first stage's start to the second's end
+  unsigned mask = 0;
+  for (int j = 0; j < a.S; ++j) mask |= (a.accumulate_q[j] ? 1u : 0u) << j;
+  const int64_t qpart = (int64_t)grid * a.D;
+  if (P2) {
+    e = launch(Launch{Lred.stream, Lred.start, nullptr}, bwd_colsum_kernel<false>, dim3(bx, (unsigned)P2, a.S),
+               dim3(256), 0, (const float*)p.partial, (int64_t)grid, a.D, chunk, stage1, (const float*)nullptr,
+               (const float*)nullptr, (float*)nullptr, (float*)nullptr, 0u, qpart, P2 * a.D);
     if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  const float* in = P2 ? stage1 : p.partial;
+  const int64_t rows = P2 ? P2 : grid;
+  return launch(Launch{Lred.stream, P2 ? nullptr : Lred.start, Lred.stop}, bwd_colsum_kernel<true>,
+                dim3(bx, 1, a.S), dim3(256), 0, in, rows, a.D, rows, (float*)nullptr, a.w, a.g, a.dw, a.dgamma,
+                mask, P2 ? P2 * a.D : qpart, (int64_t)0);
 }
 
 template <class F, int VPL>
