@@ -1577,7 +1577,7 @@ __global__ __launch_bounds__(512) void merge_bwd_kernel(MergeBwdParams p) {
 // ---------------------------------------------------------------------------
 constexpr int kP1BwdQ = 4;  // queries per launch (their queries and dq~ sums in LDS)
 constexpr int kP1BwdVpl = 2;  // four-element vectors per lane
-constexpr int kP1BwdMaxN = 6;  // sources
+constexpr int kP1BwdMaxN = 8;  // sources
 
 struct P1BwdParams {
   const void* src[kP1BwdMaxN];
@@ -3555,7 +3555,8 @@ hipError_t launch_bwd_reduce(const BwdArgs& a, const BwdPlan& pl, int stage, con
 #define ATTNRES_P1BWD_GROUPS 512  // workgroups of the batched Phase-1 backward (each walks rows)
 #endif
 
-// up to 6 sources: beyond, the register budget of two vectors per lane spills
+// up to 8 sources (the coefficients take one 8-lane group per query); rows
+// of at most 2 x 64 x 8 four-element vectors
 bool phase1_bwd_eligible(int dtype, int n, int64_t D) {
   const int64_t V = D / 4;
   return dtype == 1 && n >= 1 && n <= kP1BwdMaxN && D % 4 == 0 && V <= 64 * 8 * kP1BwdVpl;
@@ -3612,7 +3613,9 @@ hipError_t launch_phase1_bwd(const Phase1BwdArgs& a, void* ws, const Launch& L, 
     case 3: e = launch_p1bwd_t<3>(p, grid, L); break;
     case 4: e = launch_p1bwd_t<4>(p, grid, L); break;
     case 5: e = launch_p1bwd_t<5>(p, grid, L); break;
-    default: e = launch_p1bwd_t<6>(p, grid, L); break;
+    case 6: e = launch_p1bwd_t<6>(p, grid, L); break;
+    case 7: e = launch_p1bwd_t<7>(p, grid, L); break;
+    default: e = launch_p1bwd_t<8>(p, grid, L); break;
   }
   if (e != hipSuccess) return e;
   // each query's partial rows [grid][D] -> dw, dgamma (written or added)

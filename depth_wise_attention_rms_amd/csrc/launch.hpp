@@ -155,7 +155,7 @@ hipError_t launch_bwd_reduce(const BwdArgs& a, const BwdPlan& pl, int stage, con
 hipError_t launch_merge_bwd(int dtype, const MergeBwdArgs& a, const BwdPlan& pl, const Launch& L);
 
 // Batched Phase-1 backward: S <= 4 queries (consecutive rows of w, g, dw,
-// dgamma) over the same n <= 6 bf16 sources in one pass; query j's upstream
+// dgamma) over the same n <= 8 bf16 sources in one pass; query j's upstream
 // gradient is dh_scale[j][r] * dh[j][r] (dh_scale[j] null: 1) and its
 // log-sum-exp's gradient dlse[j] (null: 0). dV[i] fp32 are added to; dw /
 // dgamma rows are written (accumulate_q[j] == 0) or added. Rows of at most

@@ -107,6 +107,9 @@ BWD_STACKS = [
     (1, 4100, 7168, 12, 15, "bf16", True),
     (1, 65, 1024, 5, 13, "f32", True),
     (1, 512, 4096, 8, 16, "bf16", False),
+    # nine blocks of two: the batched Phase-1 backward over 7 and 8 sources,
+    # one aggregate backward per query over 9
+    (1, 70, 1024, 2, 17, "bf16", True),
 ]
 
 
