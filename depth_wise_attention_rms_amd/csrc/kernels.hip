@@ -403,8 +403,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kP1LdsBytes = 160 * 1024;
 
 // Shapes of one instantiation: KS k-steps of 16 per wave (D = 128 KS), NC
-// sources per row.
-template <int KS, int NC>
+// sources per row; NF: output 0 is written as its sublayer's input norm.
+template <int KS, int NC, bool NF = false>
 struct P1Shape {
   static constexpr int D = 128 * KS;
   static constexpr int STRIDE = D + 16;    // bf16 elements per staged row
@@ -416,9 +416,13 @@ struct P1Shape {
   // w (its hidden slice) of every staged row, so rows need no barrier of their
   // own: the only exchange between waves is the score reduction.
   static constexpr bool PRIVATE = NCH == kP1Waves;
-  static constexpr int FIT = (kP1LdsBytes - 4 * RED - 4 * kP1Waves * 64 - 1024) / (2 * SLOT);
+  // with NF: the gain [D] and the Gram partials [two rows][wave][NC][NC], fp32
+  static constexpr int GRAM = 2 * kP1Waves * NC * NC;
+  static constexpr int NFB = NF ? D + GRAM : 0;
+  static constexpr int FIT = (kP1LdsBytes - 4 * RED - 4 * kP1Waves * 64 - 1024 - 4 * NFB) / (2 * SLOT);
   static constexpr int NBUF = FIT > 4 ? 4 : FIT;  // ring slots (prefetch distance NBUF - 1)
-  static_assert(NBUF >= 2, "a row and its successor must fit in LDS");
+  static constexpr bool FITS = NBUF >= 2;         // a row and its successor fit in LDS
+  static_assert(NF || FITS, "a row and its successor must fit in LDS");
 };
 
 struct Phase1MParams {
@@ -435,6 +439,9 @@ struct Phase1MParams {
   int64_t R;
   int D;
   float invD;
+  const float* nf_g;  // with nf_out: output 0 goes to nf_out as its input norm
+  float nf_eps;       // round(nf_g * h / sqrt(mean_d h^2 + nf_eps)), h = output 0
+  void* nf_out;       // rounded (nf_g null: a gain of 1), and not to out
 };
 
 // x rounded to the nearest bf16 (ties to even), as an fp32 value
@@ -590,9 +597,9 @@ __device__ __forceinline__ int p1_stage(const Phase1MParams& p, int64_t row, con
 #define ATTNRES_P1_OUT_NT_FROM 2
 #endif
 
-template <int KS, int NC>
+template <int KS, int NC, bool NF>
 __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
-  using Sh = P1Shape<KS, NC>;
+  using Sh = P1Shape<KS, NC, NF>;
   constexpr int D = Sh::D, STRIDE = Sh::STRIDE, NCH = Sh::NCH, NBUF = Sh::NBUF, PF = NBUF - 1;
   __shared__ __attribute__((aligned(16))) __bf16 ring[NBUF * Sh::SLOT];
   // partial scores [row parity][wave][query][source] and sums of squares
@@ -603,6 +610,10 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
   // each wave's softmax weights, lane 8 s + i = alpha[s][i]; written and read
   // back by the same wave only (its LDS accesses complete in order)
   __shared__ __attribute__((aligned(16))) float alpha_buf[kP1Waves * 64];
+  // NF: the gain, and each wave's Gram partials of the row's sources over its
+  // hidden slice, [row parity][wave][source k][source i]
+  __shared__ __attribute__((aligned(16))) float gam_buf[NF ? D : 4];
+  __shared__ float gram_buf[NF ? Sh::GRAM : 1];
 
   const int S = p.S;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
@@ -633,6 +644,13 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
       }
     }
     qa[kk] = Bf16::pack(part);  // each part is a bf16 value: packing is exact
+  }
+
+  if constexpr (NF) {
+    // the gain, once per workgroup; read only after the first row's barrier.
+    // These loads are waited for here, before the first copy is issued.
+    for (int k = tid; k < D / 4; k += 64 * kP1Waves)
+      *reinterpret_cast<float4*>(gam_buf + 4 * k) = p.nf_g ? ldf4(p.nf_g + 4 * k) : make_float4(1.f, 1.f, 1.f, 1.f);
   }
 
   // Vector-memory operations this wave has issued (copies, block-sum and
@@ -701,6 +719,7 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
     f32x4_t c[4];
     #pragma unroll
     for (int t = 0; t < 4; ++t) c[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t gacc = f32x4_t{0.f, 0.f, 0.f, 0.f};  // NF: G[k][i] = b_k . b_i over the slice
     // Both A tiles every k-step (the second is zero for S <= 4): a branch here
     // would keep the compiler from issuing the next LDS reads ahead of the
     // current products.
@@ -721,6 +740,9 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
                                                     __builtin_bit_cast(bf16x8_t, b), c[e], 0, 0, 0);
       c[e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[2 * kk + 1]),
                                                         __builtin_bit_cast(bf16x8_t, b), c[e + 1], 0, 0, 0);
+      if constexpr (NF)  // a lane's B fragment (column col, k-group kg) is also the A fragment of row col
+        gacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b),
+                                                      __builtin_bit_cast(bf16x8_t, b), gacc, 0, 0, 0);
       if (kP1Fence > 0 && kk % kP1Fence == kP1Fence - 1)
         __builtin_amdgcn_sched_barrier(0);  // bound the LDS reads in flight
     }
@@ -734,6 +756,12 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
       cred[(w * kP1MaxS + kg) * NC + col] = (c[0][0] + c[2][0]) + (c[0][1] + c[2][1]) + (c[0][2] + c[2][2]);
       cred[(w * kP1MaxS + 4 + kg) * NC + col] = (c[1][0] + c[3][0]) + (c[1][1] + c[3][1]) + (c[1][2] + c[3][2]);
       if (kg == 0) ssred[w * NC + col] = ss;
+      if constexpr (NF) {
+        float* gr = gram_buf + parity * (kP1Waves * NC * NC) + w * (NC * NC);
+        #pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * kg + r < NC) gr[(4 * kg + r) * NC + col] = gacc[r];
+      }
     }
     lds_barrier();
 
@@ -768,6 +796,25 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
         if (p.m_out) p.m_out[(int64_t)sq_ * p.R + row] = m;
         p.lse_out[(int64_t)sq_ * p.R + row] = m + __logf(z);
       }
+    }
+    // NF: the sum of squares of output 0 over the whole row, as
+    // alpha_0^T G alpha_0 from the reduced Gram matrix (lane 8 k + i takes
+    // one term); every wave forms it for itself. It is taken from the fp32
+    // output rather than the rounded one the norm is applied to: the two
+    // differ by a relative O(2^-8 / sqrt(D)).
+    float nf_inv = 0.f;
+    if constexpr (NF) {
+      const int gk = l >> 3, gi = l & 7;
+      const float ak = __shfl(alpha, gk), ai = __shfl(alpha, gi);  // lanes 0..7 hold query 0's weights
+      float t = 0.f;
+      if (gk < NC && gi < NC) {
+        const float* gr = gram_buf + parity * (kP1Waves * NC * NC) + gk * NC + gi;
+        float gs = 0.f;
+        #pragma unroll
+        for (int ww = 0; ww < kP1Waves; ++ww) gs += gr[ww * (NC * NC)];
+        t = ak * (ai * gs);
+      }
+      nf_inv = rsqrtf(wave_sum(t) * p.invD + p.nf_eps);
     }
 
     // outputs on the matrix cores: o_s[d] = sum_i alpha[s][i] b_i[d] as
@@ -835,17 +882,39 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
           }
         }
         const int vec = w * 64 + am + 32 * pass;  // vector of the row this lane writes
+        // The lane's 64-bit offset from query 2q's row (query 2q + 1, in the
+        // upper lanes, lies R rows further: beyond 4 GB for large tensors),
+        // the same for every q; formed per row, so that the compiler does not
+        // hold one per query and pass across the row loop.
+        int64_t loff = (upper ? p.R * rowbytes : 0) + (int64_t)vec * 16;
+        asm volatile("" : "+v"(loff));
         #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int sq = 2 * q + (upper ? 1 : 0);
-          // a 64-bit address per lane: the two queries of a pair are R rows
-          // apart, which a 32-bit lane offset cannot hold beyond 4 GB
-          char* dst = static_cast<char*>(p.out) + ((int64_t)sq * p.R + row) * rowbytes + vec * 16;
+          gchar_t* dst = uniform_ptr(static_cast<char*>(p.out) + ((int64_t)(2 * q) * p.R + row) * rowbytes) + loff;
+          if constexpr (NF) {
+            if (q == 0) {
+              // output 0 goes to nf_out as round(gain * round(h) * inv); query
+              // 1 (the upper lanes) is stored by the same instruction, so
+              // the wave issues one store here whatever S is
+              float f[8];
+              Bf16::unpack(Bf16::pack(o[0]), f);
+              const float4 g0 = *reinterpret_cast<const float4*>(gam_buf + vec * 8);
+              const float4 g1 = *reinterpret_cast<const float4*>(gam_buf + vec * 8 + 4);
+              const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+              #pragma unroll
+              for (int e = 0; e < 8; ++e) f[e] = gg[e] * (f[e] * nf_inv);
+              const uint4 hv = upper ? Bf16::pack(o[0]) : Bf16::pack(f);
+              gchar_t* nd = uniform_ptr(static_cast<char*>(p.nf_out) + row * rowbytes) + (uint32_t)(vec * 16);
+              if (!upper || S > 1) st16_global(upper ? dst : nd, hv);
+              continue;
+            }
+          }
           if (2 * q < S && sq < S) {
             if (sq >= ATTNRES_P1_OUT_NT_FROM)
-              st16_stream((gchar_t*)reinterpret_cast<uintptr_t>(dst), Bf16::pack(o[q]));
+              st16_stream(dst, Bf16::pack(o[q]));
             else
-              st16_global((gchar_t*)reinterpret_cast<uintptr_t>(dst), Bf16::pack(o[q]));
+              st16_global(dst, Bf16::pack(o[q]));
           }
         }
       }
@@ -2909,7 +2978,38 @@ static hipError_t launch_phase1_mfma_t(const Phase1MParams& p, const Launch& L) 
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const int64_t grid = p.R < cus ? p.R : cus;  // one workgroup per CU, each walks rows
-  return launch(L, phase1_mfma_kernel<KS, NC>, dim3((unsigned)grid), dim3(64 * kP1Waves), 0, p);
+  if (p.nf_out) {
+    if constexpr (P1Shape<KS, NC, true>::FITS)
+      return launch(L, phase1_mfma_kernel<KS, NC, true>, dim3((unsigned)grid), dim3(64 * kP1Waves), 0, p);
+    else
+      return hipErrorInvalidValue;
+  }
+  return launch(L, phase1_mfma_kernel<KS, NC, false>, dim3((unsigned)grid), dim3(64 * kP1Waves), 0, p);
+}
+
+template <int KS>
+static bool phase1_mfma_norm_fits_k(int n) {
+  switch (n) {
+    case 1: return P1Shape<KS, 1, true>::FITS;
+    case 2: return P1Shape<KS, 2, true>::FITS;
+    case 3: return P1Shape<KS, 3, true>::FITS;
+    case 4: return P1Shape<KS, 4, true>::FITS;
+    case 5: return P1Shape<KS, 5, true>::FITS;
+    case 6: return P1Shape<KS, 6, true>::FITS;
+    case 7: return P1Shape<KS, 7, true>::FITS;
+    default: return P1Shape<KS, 8, true>::FITS;
+  }
+}
+
+// Whether the register-tile kernel holds the gain and the Gram partials of
+// the fused input norm beside two ring slots (not at D = 4096 with 8 sources).
+static bool phase1_mfma_norm_fits(int n, int64_t D) {
+  switch (D) {
+    case 1024: return phase1_mfma_norm_fits_k<8>(n);
+    case 2048: return phase1_mfma_norm_fits_k<16>(n);
+    case 3072: return phase1_mfma_norm_fits_k<24>(n);
+    default: return phase1_mfma_norm_fits_k<32>(n);
+  }
 }
 
 template <int KS>
@@ -2933,6 +3033,8 @@ static hipError_t launch_phase1_mfma(const Phase1Args& a, const Launch& L) {
   p.out = a.out; p.m_out = a.m_out; p.lse_out = a.lse_out;
   p.cl = Close{a.close_p, a.close_v, a.close_b};
   p.R = a.R; p.D = (int)a.D; p.invD = 1.0f / (float)a.D;
+  p.nf_g = a.nf_g; p.nf_eps = a.nf_eps; p.nf_out = a.out ? a.nf_out : nullptr;
+  if (a.nf_out && (!a.out || !phase1_mfma_norm_fits(a.n, a.D))) return hipErrorInvalidValue;
   switch (a.D) {
     case 1024: return launch_phase1_mfma_k<8>(p, L);
     case 2048: return launch_phase1_mfma_k<16>(p, L);
@@ -3222,12 +3324,14 @@ hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L) {
   return dtype == 1 ? launch_phase1_dt<Bf16>(a, L) : launch_phase1_dt<F32>(a, L);
 }
 
-// Only the one-source statistics kernel writes the norm itself: it holds the
-// source and its sum of squares anyway. In the register-tile kernel the
-// cross-wave sum of output 0's squares cost more time per row (a barrier, or
-// registers held across rows) than the separate pass it would save.
+// The one-source statistics kernel writes the norm from the sum of squares
+// it forms anyway; the register-tile kernel takes output 0's sum of squares
+// from the Gram matrix of the row's sources, reduced with the scores, so the
+// norm needs no exchange between waves of its own.
 bool phase1_norm_fused(int dtype, const Phase1Args& a, bool gemm) {
-  return !gemm && phase1_single_eligible(dtype, a);
+  if (gemm) return false;
+  if (phase1_single_eligible(dtype, a)) return true;
+  return a.out && phase1_mfma_eligible(dtype, a.n, a.S, a.D) && phase1_mfma_norm_fits(a.n, a.D);
 }
 
 const char* phase1_kernel_name(int dtype, const Phase1Args& a, bool gemm) {

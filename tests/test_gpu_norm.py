@@ -111,6 +111,11 @@ STACK_NORM = [
     # S > 8: the vector-ALU Phase 1, and a short last block
     inputs.Workload("norm_wide", "stack", B=4, T=10, D=512, dtype="bf16", L=14, S=12, seed=5),
     inputs.Workload("norm_f32", "stack", B=1, T=5, D=64, dtype="f32", L=7, S=3, seed=6),
+    # the register-tile Phase 1 writing output 0's norm itself, at D = 4096 with
+    # 2..7 sources (8 sources there take the separate norm pass) and D = 3072;
+    # more rows than workgroups, ragged
+    inputs.Workload("norm_block_4096", "stack", B=1, T=600, D=4096, dtype="bf16", L=32, S=4, seed=7),
+    inputs.Workload("norm_block_3072", "stack", B=3, T=100, D=3072, dtype="bf16", L=18, S=6, seed=8),
 ]
 
 
