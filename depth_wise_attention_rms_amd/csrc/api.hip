@@ -185,6 +185,11 @@ int do_close(const char* fn, const void* p, const void* v, void* b, int64_t R, i
 int do_rmsnorm(const char* fn, int dtype, const void* x, int64_t R, int64_t D, const float* g,
                float eps, void* out, hipStream_t st);
 
+// whether do_phase1 takes the scores/outputs passes for this launch
+bool takes_gemm(int dtype, const Phase1Args& a) {
+  return a.gemm_ws && attnres::phase1_gemm_eligible(dtype, a.n, a.S, a.D, a.R);
+}
+
 int do_phase1(const char* fn, int dtype, const Phase1Args& a, hipStream_t st) {
   if (a.R == 0) return ATTNRES_OK;
   const int64_t row_bytes = a.D * esize_of(dtype);
@@ -193,7 +198,7 @@ int do_phase1(const char* fn, int dtype, const Phase1Args& a, hipStream_t st) {
     if (!a.nf_out) return ATTNRES_OK;
     return do_rmsnorm(fn, dtype, a.out ? a.out : a.src[0], a.R, a.D, a.nf_g, a.nf_eps, a.nf_out, st);
   };
-  if (a.gemm_ws && attnres::phase1_gemm_eligible(dtype, a.n, a.S, a.D, a.R)) {
+  if (takes_gemm(dtype, a)) {
     // the scores pass reads materialised sources: close first
     if (a.close_v) TRY(do_close(fn, a.close_p, a.close_v, a.close_b, a.R, a.D, dtype, st));
     Phase1Args g = a;
@@ -670,15 +675,27 @@ int stack_forward(const char* fn, const void* x, int L, int S, int64_t R, int64_
       a1.nf_eps = nm.eps_f;
       a1.nf_out = H;
     }
+    // Outputs 0 and 1 straight into H and P where the kernel allows: those
+    // two are rewritten for every sublayer and stay in the last-level cache,
+    // slices of O do not. P's last reader is this launch's close, which
+    // reads each row before the row's outputs are written; output 1 is read
+    // once, by the first merge, which writes no partial.
+    // (P has room only where some block has more than two sublayers.)
+    const bool o01 = !one_source && attnres::phase1_out01_supported(dtype, a1, takes_gemm(dtype, a1));
+    const bool o0_in_h = o01 && !nm.on;
+    const bool o1_in_p = o01 && (S < L ? S : L) > 2;
+    if (o0_in_h) a1.out0 = H;
+    if (o1_in_p) a1.out1 = P;
+    auto o_at = [&](int j) -> const void* { return j == 1 && o1_in_p ? P : o_slice(j); };
     TRY(do_phase1(fn, dtype, a1, st));
     const void* v_first = nullptr;
     // h_start = o_0: no partial yet
-    TRY(call(start, nm.on ? H : o_slice(0), &v_first));
+    TRY(call(start, nm.on || o0_in_h ? H : o_slice(0), &v_first));
     const void* p_cur = v_first;    // p_1 = v_start (aliased, no copy)
     const void* v_prev = v_first;
     for (int j = 1; j < Sk; ++j) {
       const int l = start + j;
-      Phase2Args a2{o_slice(j), LSE + (int64_t)j * R, Q + (int64_t)(l - 1) * D,
+      Phase2Args a2{o_at(j), LSE + (int64_t)j * R, Q + (int64_t)(l - 1) * D,
                     nullptr, eps, j == 1 ? nullptr : p_cur, v_prev, j == 1 ? nullptr : P,
                     nm.on ? nullptr : H,
                     nm.on && nm.Gamma_f ? nm.Gamma_f + (int64_t)(l - 1) * D : nullptr, nm.eps_f,

@@ -442,6 +442,8 @@ struct Phase1MParams {
   const float* nf_g;  // with nf_out: output 0 goes to nf_out as its input norm
   float nf_eps;       // round(nf_g * h / sqrt(mean_d h^2 + nf_eps)), h = output 0
   void* nf_out;       // rounded (nf_g null: a gain of 1), and not to out
+  void* out0;         // [R][D] or null: without nf_out, output 0 goes here instead of to out
+  void* out1;         // [R][D] or null: output 1 goes here instead of to out
 };
 
 // x rounded to the nearest bf16 (ties to even), as an fp32 value
@@ -596,6 +598,7 @@ __device__ __forceinline__ int p1_stage(const Phase1MParams& p, int64_t row, con
 #ifndef ATTNRES_P1_OUT_NT_FROM
 #define ATTNRES_P1_OUT_NT_FROM 2
 #endif
+static_assert(ATTNRES_P1_OUT_NT_FROM >= 2, "queries 0 and 1 share one store instruction");
 
 template <int KS, int NC, bool NF>
 __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
@@ -892,23 +895,28 @@ __global__ __launch_bounds__(512, 1) void phase1_mfma_kernel(Phase1MParams p) {
         for (int q = 0; q < 4; ++q) {
           const int sq = 2 * q + (upper ? 1 : 0);
           gchar_t* dst = uniform_ptr(static_cast<char*>(p.out) + ((int64_t)(2 * q) * p.R + row) * rowbytes) + loff;
-          if constexpr (NF) {
-            if (q == 0) {
-              // output 0 goes to nf_out as round(gain * round(h) * inv); query
-              // 1 (the upper lanes) is stored by the same instruction, so
-              // the wave issues one store here whatever S is
+          if (q == 0) {
+            // Output 0 (the lower lanes) goes to out0 or, with NF, to nf_out
+            // as round(gain * round(h) * inv); query 1 (the upper lanes) is
+            // stored by the same instruction, so the wave issues one store
+            // here whatever S is.
+            uint4 hv = Bf16::pack(o[0]);
+            if constexpr (NF) {
               float f[8];
-              Bf16::unpack(Bf16::pack(o[0]), f);
+              Bf16::unpack(hv, f);
               const float4 g0 = *reinterpret_cast<const float4*>(gam_buf + vec * 8);
               const float4 g1 = *reinterpret_cast<const float4*>(gam_buf + vec * 8 + 4);
               const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
               #pragma unroll
               for (int e = 0; e < 8; ++e) f[e] = gg[e] * (f[e] * nf_inv);
-              const uint4 hv = upper ? Bf16::pack(o[0]) : Bf16::pack(f);
-              gchar_t* nd = uniform_ptr(static_cast<char*>(p.nf_out) + row * rowbytes) + (uint32_t)(vec * 16);
-              if (!upper || S > 1) st16_global(upper ? dst : nd, hv);
-              continue;
+              if (!upper) hv = Bf16::pack(f);
             }
+            void* const base0 = NF ? p.nf_out : p.out0 ? p.out0 : p.out;
+            gchar_t* d0 = uniform_ptr(static_cast<char*>(base0) + row * rowbytes) + (uint32_t)(vec * 16);
+            gchar_t* d1 = p.out1 ? uniform_ptr(static_cast<char*>(p.out1) + row * rowbytes) + (uint32_t)(vec * 16)
+                                 : dst;
+            if (!upper || S > 1) st16_global(upper ? d1 : d0, hv);
+            continue;
           }
           if (2 * q < S && sq < S) {
             if (sq >= ATTNRES_P1_OUT_NT_FROM)
@@ -3034,6 +3042,8 @@ static hipError_t launch_phase1_mfma(const Phase1Args& a, const Launch& L) {
   p.cl = Close{a.close_p, a.close_v, a.close_b};
   p.R = a.R; p.D = (int)a.D; p.invD = 1.0f / (float)a.D;
   p.nf_g = a.nf_g; p.nf_eps = a.nf_eps; p.nf_out = a.out ? a.nf_out : nullptr;
+  p.out0 = a.out0;
+  p.out1 = a.out1;
   if (a.nf_out && (!a.out || !phase1_mfma_norm_fits(a.n, a.D))) return hipErrorInvalidValue;
   switch (a.D) {
     case 1024: return launch_phase1_mfma_k<8>(p, L);
@@ -3328,6 +3338,10 @@ hipError_t launch_phase1(int dtype, const Phase1Args& a, const Launch& L) {
 // it forms anyway; the register-tile kernel takes output 0's sum of squares
 // from the Gram matrix of the row's sources, reduced with the scores, so the
 // norm needs no exchange between waves of its own.
+bool phase1_out01_supported(int dtype, const Phase1Args& a, bool gemm) {
+  return !gemm && a.out && !phase1_single_eligible(dtype, a) && phase1_mfma_eligible(dtype, a.n, a.S, a.D);
+}
+
 bool phase1_norm_fused(int dtype, const Phase1Args& a, bool gemm) {
   if (gemm) return false;
   if (phase1_single_eligible(dtype, a)) return true;

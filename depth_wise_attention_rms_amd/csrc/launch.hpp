@@ -45,6 +45,11 @@ struct Phase1Args {
   const float* nf_g = nullptr;
   float nf_eps = 0.f;
   void* nf_out = nullptr;
+  // without nf_out: output 0 is written to out0 [R][D] instead of out's first
+  // slice, and output 1 to out1 instead of its second, by the kernels
+  // phase1_out01_supported() names (the others ignore both)
+  void* out0 = nullptr;
+  void* out1 = nullptr;
 };
 
 struct AggArgs {
@@ -201,6 +206,8 @@ bool phase1_supported(int dtype, int n, int S, int64_t D);
 // whether the kernel a Phase-1 launch runs writes the input norm of output 0
 // itself (Phase1Args::nf_out)
 bool phase1_norm_fused(int dtype, const Phase1Args& a, bool gemm);
+// whether the kernel a Phase-1 launch runs honours Phase1Args::out0 and out1
+bool phase1_out01_supported(int dtype, const Phase1Args& a, bool gemm);
 // name of the kernel(s) a Phase-1 launch runs (gemm: the scores/outputs path)
 const char* phase1_kernel_name(int dtype, const Phase1Args& a, bool gemm);
 // Phase 1 with out == null (statistics only) is available for these shapes

@@ -230,11 +230,14 @@ def test_stack_bruteforce_grid():
                     _check_stack(ds, np.arange(3))
 
 
-def test_stack_matrix_core_many_rows():
-    """Block stack whose Phase 1 runs on the matrix cores with several token
-    rows per workgroup and fused block closes: L = 20, S = 6, R = 600,
-    D = 2048, bf16; all rows."""
-    wl = inputs.Workload("mfma_rows", "stack", B=2, T=300, D=2048, dtype="bf16", L=20, S=6, seed=7)
+@pytest.mark.parametrize("B,T,D,L,S", [(2, 300, 2048, 20, 6), (1, 601, 4096, 13, 3), (1, 333, 3072, 9, 2)])
+def test_stack_matrix_core_many_rows(B, T, D, L, S):
+    """Block stacks whose Phase 1 runs on the matrix cores with several token
+    rows per workgroup and fused block closes, bf16, all rows. Phase 1 writes
+    output 0 into the sublayer-input buffer and output 1 into the partial
+    buffer that its own fused close reads (blocks of 3 and 6); blocks of 2
+    have no partial buffer."""
+    wl = inputs.Workload(f"mfma_rows_D{D}_S{S}", "stack", B=B, T=T, D=D, dtype="bf16", L=L, S=S, seed=7 + S)
     announce(wl.name)
     ds = DeviceStack(wl)
     _check_stack(ds, np.arange(wl.R), chunk=300)
