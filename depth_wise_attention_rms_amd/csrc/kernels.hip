@@ -958,7 +958,7 @@ struct AggParams {
   Geom g;
 };
 
-template <class T, int VPL, int G>
+template <class T, int VPL, int G, bool PK>
 __global__ __launch_bounds__(512) void aggregate_kernel(AggParams p) {
   extern __shared__ float lds[];
   constexpr int EPV = T::kEPV;
@@ -1037,7 +1037,6 @@ __global__ __launch_bounds__(512) void aggregate_kernel(AggParams p) {
     }
 
     for (int i0 = 0; i0 < p.n; i0 += G) {
-      float x[G][VPL][EPV];
       uint4 u[G][VPL];
       #pragma unroll
       for (int j = 0; j < G; ++j) {
@@ -1050,30 +1049,65 @@ __global__ __launch_bounds__(512) void aggregate_kernel(AggParams p) {
         for (int c = 0; c < VPL; ++c)
           u[j][c] = ld16_stream(live ? sp + voff[c] : reinterpret_cast<const char*>(g_store_sink));
       }
-      #pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const int i = i0 + j;
-        const bool closing = has_close && i == p.n - 1;
+      // With PK the group's sources stay packed and each use unpacks them
+      // again; otherwise they are unpacked once and held. Masked either way:
+      // slots past n and lanes past the row's end contribute zero. Packed, the
+      // 8-source group at 2 vectors per lane takes 160 VGPRs instead of 217
+      // (3 waves per SIMD instead of 2) for twice the unpacking.
+      float x[PK ? 1 : G][PK ? 1 : VPL][EPV];
+      if constexpr (PK) {
+        // the closing source takes its slot's registers once
         #pragma unroll
-        for (int c = 0; c < VPL; ++c) {
-          T::unpack(closing ? bcl[c] : u[j][c], x[j][c]);
-          const bool keep = i < p.n && in_row[c];
-          #pragma unroll
-          for (int e = 0; e < EPV; ++e) x[j][c][e] = keep ? x[j][c][e] : 0.f;
-        }
+        for (int j = 0; j < G; ++j)
+          if (has_close && i0 + j == p.n - 1)
+            #pragma unroll
+            for (int c = 0; c < VPL; ++c) u[j][c] = bcl[c];
       }
+      auto unpack_keep = [&](int j, int c, float* xo) {
+        const bool closing = !PK && has_close && i0 + j == p.n - 1;
+        T::unpack(closing ? bcl[c] : u[j][c], xo);
+        const bool keep = i0 + j < p.n && in_row[c];
+        #pragma unroll
+        for (int e = 0; e < EPV; ++e) xo[e] = keep ? xo[e] : 0.f;
+      };
       float red[NV];
       #pragma unroll
       for (int k = 0; k < NV; ++k) red[k] = 0.f;
-      #pragma unroll
-      for (int j = 0; j < G; ++j)
+      if constexpr (PK) {
         #pragma unroll
-        for (int c = 0; c < VPL; ++c)
+        for (int j = 0; j < G; ++j)
           #pragma unroll
-          for (int e = 0; e < EPV; ++e) {
-            red[j] += q[c][e] * x[j][c][e];
-            red[G + j] += x[j][c][e] * x[j][c][e];
+          for (int c = 0; c < VPL; ++c) {
+            float xt[EPV];
+            unpack_keep(j, c, xt);
+            #pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+              red[j] += q[c][e] * xt[e];
+              red[G + j] += xt[e] * xt[e];
+            }
           }
+        // the packed registers look new here, so the unpacked values above
+        // are not kept alive for the numerators below
+        #pragma unroll
+        for (int j = 0; j < G; ++j)
+          #pragma unroll
+          for (int c = 0; c < VPL; ++c)
+            asm volatile("" : "+v"(u[j][c].x), "+v"(u[j][c].y), "+v"(u[j][c].z), "+v"(u[j][c].w));
+      } else {
+        #pragma unroll
+        for (int j = 0; j < G; ++j)
+          #pragma unroll
+          for (int c = 0; c < VPL; ++c) unpack_keep(j, c, x[j][c]);
+        #pragma unroll
+        for (int j = 0; j < G; ++j)
+          #pragma unroll
+          for (int c = 0; c < VPL; ++c)
+            #pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+              red[j] += q[c][e] * x[j][c][e];
+              red[G + j] += x[j][c][e] * x[j][c][e];
+            }
+      }
       row_reduce<NV>(red, lds, ln.slot, ln.wr, g.W);
       float sc[G];
       float m_new = m_run;
@@ -1090,14 +1124,17 @@ __global__ __launch_bounds__(512) void aggregate_kernel(AggParams p) {
         z_run += sc[j];
       }
       #pragma unroll
-      for (int c = 0; c < VPL; ++c)
+      for (int c = 0; c < VPL; ++c) {
         #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          float a = num[c][e] * rescale;
+        for (int e = 0; e < EPV; ++e) num[c][e] *= rescale;
+        #pragma unroll
+        for (int j = 0; j < G; ++j) {
+          float xt[EPV];
+          if constexpr (PK) unpack_keep(j, c, xt);
           #pragma unroll
-          for (int j = 0; j < G; ++j) a += sc[j] * x[j][c][e];
-          num[c][e] = a;
+          for (int e = 0; e < EPV; ++e) num[c][e] += sc[j] * (PK ? xt[e] : x[PK ? 0 : j][PK ? 0 : c][e]);
         }
+      }
       m_run = m_new;
     }
     if (p.nf_out) {
@@ -3369,10 +3406,14 @@ bool phase1_supported(int dtype, int n, int S, int64_t D) {
   return stream_vpl(dtype == 1 ? 2 : 4, D, &E) != 0;
 }
 
-template <class T, int VPL, int G>
+#ifndef ATTNRES_AGG_PACKED_MIN_D
+#define ATTNRES_AGG_PACKED_MIN_D 2048  // narrower rows keep the 8-source group unpacked
+#endif
+
+template <class T, int VPL, int G, bool PK = false>
 static hipError_t launch_agg_t(AggParams& p, const Launch& L) {
   const size_t lds = p.g.W > 1 ? (size_t)p.g.RPW * p.g.W * 2 * G * sizeof(float) : 0;
-  return launch(L, aggregate_kernel<T, VPL, G>, dim3(grid_for(p.g)), dim3(64 * p.g.W * p.g.RPW),
+  return launch(L, aggregate_kernel<T, VPL, G, PK>, dim3(grid_for(p.g)), dim3(64 * p.g.W * p.g.RPW),
                 lds, p);
 }
 
@@ -3394,6 +3435,10 @@ static hipError_t launch_aggregate_dt(const AggArgs& a, const Launch& L) {
   }
   if (a.n <= 2) return launch_agg_t<T, 2, 2>(p, L);
   if (a.n <= 4) return launch_agg_t<T, 2, 4>(p, L);
+  // one group of 5..8 sources over rows of at least ATTNRES_AGG_PACKED_MIN_D
+  // elements: packed (config 3's final aggregate 244 -> 222 us); two or more
+  // groups, or narrower rows, measured slower that way
+  if (a.n <= 8 && a.D >= ATTNRES_AGG_PACKED_MIN_D) return launch_agg_t<T, 2, 8, true>(p, L);
   return launch_agg_t<T, 2, 8>(p, L);
 }
 
