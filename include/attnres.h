@@ -209,8 +209,12 @@ int attnres_block_stack_forward(const void* x, int L, int S, int64_t R, int64_t 
  * materialised (in Block AttnRes h_l feeds only its sublayer). Gamma_f
  * [L, D] fp32 or NULL for ones; eps_f finite and >= 0. Workspace, ownership,
  * limits and errors as attnres_block_stack_forward. The norm is fused into
- * Phase 2; a block's first sublayer (h = Phase-1 output 0) and one-sublayer
- * blocks take a separate RMSNorm pass. */
+ * Phase 2 and into the aggregate of a one-sublayer block. A block's first
+ * sublayer (h = Phase-1 output 0) gets it from the Phase-1 pass itself where
+ * that pass is the one-source statistics pass or the register-resident
+ * matrix-core pass (bf16, at most 8 queries, D in {1024, 2048, 3072, 4096},
+ * up to 7 sources at D = 4096); other Phase-1 passes are followed by a
+ * separate RMSNorm pass. */
 int attnres_block_stack_forward_norm(const void* x, int L, int S, int64_t R, int64_t D, int dtype,
                                      const float* W, const float* Gamma, float eps,
                                      const float* Gamma_f, float eps_f, attnres_sublayer_fn f,
