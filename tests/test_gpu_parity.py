@@ -268,16 +268,17 @@ def test_stack_decode_config():
     _check_stack(ds, np.arange(wl.R), chunk=64)
 
 
-@pytest.mark.parametrize("B,T,S", [(1, 200, 24), (2, 100, 12), (1, 40, 24)])
-def test_stack_streamed_phase1_passes(B, T, S):
+@pytest.mark.parametrize("B,T,S,dtype", [(1, 200, 24, "bf16"), (2, 100, 12, "bf16"), (1, 40, 24, "bf16"),
+                                          (1, 200, 24, "f32"), (1, 40, 12, "f32")])
+def test_stack_streamed_phase1_passes(B, T, S, dtype):
     """Streamed Phase 1 with more queries than one register tile at D = 7168
-    (4 per pass), with fused block closes: at 200 rows two passes run side by
-    side per launch and the later launches read the stored block sum; at 40
-    rows all six passes share one launch. L = 2 S + 3: block 2 runs all S
-    queries over two sources, one of them closed on the fly, and block 3 is
-    short."""
+    (4 per pass in bf16, fewer in fp32), with fused block closes: at 200
+    rows two passes run side by side per launch and the later launches read
+    the stored block sum; at 40 rows all the passes share one launch.
+    L = 2 S + 3: block 2 runs all S queries over two sources, one of them
+    closed on the fly, and block 3 is short."""
     L = 2 * S + 3
-    wl = inputs.Workload(f"p1_passes_R{B * T}_S{S}", "stack", B=B, T=T, D=7168, dtype="bf16", L=L, S=S,
+    wl = inputs.Workload(f"p1_passes_R{B * T}_S{S}_{dtype}", "stack", B=B, T=T, D=7168, dtype=dtype, L=L, S=S,
                          seed=S + T)
     announce(wl.name)
     ds = DeviceStack(wl)
@@ -321,19 +322,22 @@ def _a256(x):
     return (x + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("L,S,D", [(12, 12, 7168), (24, 12, 7168), (30, 12, 7168), (54, 12, 7168),
-                                   (39, 4, 1024), (62, 4, 1024)])
-def test_scores_pass_statistics(L, S, D):
-    """The matrix-core scores pass's fp32 statistics at the 1e-5 bar: a stack of
-    4100 rows whose last block's Phase 1 has nb sources: with 12 queries of
-    7168, L // 12 + 1 (1: statistics only, one column per row; 2, 3 and 5:
-    two, four and eight columns per row; the short last blocks hold 6
-    queries); with 4 queries of 1024, 10 and 16 (sixteen columns per row).
-    After the forward the workspace holds that block's m and lse [Sk, R] at
-    the offsets of the header's layout (folded queries, outputs, m, lse),
+@pytest.mark.parametrize("T,L,S,D", [(4100, 12, 12, 7168), (4100, 24, 12, 7168), (4100, 30, 12, 7168),
+                                     (4100, 54, 12, 7168), (4100, 39, 4, 1024), (4100, 62, 4, 1024),
+                                     (128, 24, 12, 7168), (128, 90, 12, 7168), (77, 40, 10, 512)])
+def test_scores_pass_statistics(T, L, S, D):
+    """Phase 1's fp32 statistics at the 1e-5 bar: a stack of T rows whose last
+    block's Phase 1 has nb sources. At 4100 rows, on the matrix-core scores
+    pass: with 12 queries of 7168, L // 12 + 1 (1: statistics only, one
+    column per row; 2, 3 and 5: two, four and eight columns per row; the
+    short last blocks hold 6 queries); with 4 queries of 1024, 10 and 16
+    (sixteen columns per row). With fewer rows, on the streamed kernel: 2 and
+    8 sources at decode's shape, and 4 sources over 77 rows of 512. After the
+    forward the workspace holds that block's m and lse [Sk, R] at the
+    offsets of the header's layout (folded queries, outputs, m, lse),
     compared on every row with the oracle's Phase 1 over the block sums the
     GPU stored."""
-    wl = inputs.Workload(f"scores_stats_L{L}_S{S}_D{D}", "stack", B=1, T=4100, D=D, dtype="bf16", L=L, S=S,
+    wl = inputs.Workload(f"scores_stats_T{T}_L{L}_S{S}_D{D}", "stack", B=1, T=T, D=D, dtype="bf16", L=L, S=S,
                          seed=L + 5)
     announce(wl.name)
     ds = DeviceStack(wl)
