@@ -146,6 +146,25 @@ def test_stack_forward_norm(wl):
         assert_close_scaled(rec[l], hn_ref, scale, wl.dtype, f"{wl.name} hn_{l + 1}")
 
 
+def test_stack_forward_norm_without_gains():
+    """Gamma_f = NULL (a gain of one): the matrix-core Phase 1 then stages ones
+    as its gain, and the merges and the statistics pass skip theirs. 300 rows
+    of 4096, blocks of 4 (Phase 1 over 2 and 3 sources)."""
+    wl = inputs.Workload("norm_nogain_4096", "stack", B=1, T=300, D=4096, dtype="bf16", L=12, S=4, seed=9)
+    announce(wl.name)
+    ds = DeviceStack(wl)
+    eps_f = 1e-6
+    rows = np.arange(wl.R)
+    ds.forward(ds.recorder(rows), norm=(None, eps_f))
+    torch.cuda.synchronize()
+    rec = to_host(ds.rec)
+    xr, vr = ds.host_rows(rows)
+    ref = oracle.block_stack(xr, vr, ds.W_host, wl.S, eps=EPS)
+    for l in range(wl.L):
+        hn_ref, scale = norm_reference(ref["h"][l], ref["h_scale"][l], wl.dtype, None, eps_f)
+        assert_close_scaled(rec[l], hn_ref, scale, wl.dtype, f"{wl.name} hn_{l + 1}")
+
+
 def test_stack_forward_norm_scores_pass():
     """The normed stack whose Phase 1 runs as the matrix-core scores pass and
     the outputs pass (4096 rows of 7168, 12 queries, a short last block):
