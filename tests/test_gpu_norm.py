@@ -116,6 +116,10 @@ STACK_NORM = [
     # more rows than workgroups, ragged
     inputs.Workload("norm_block_4096", "stack", B=1, T=600, D=4096, dtype="bf16", L=32, S=4, seed=7),
     inputs.Workload("norm_block_3072", "stack", B=3, T=100, D=3072, dtype="bf16", L=18, S=6, seed=8),
+    # 8 queries per block (two full query tiles, as config 3) and 3 (an odd
+    # count: the last query pair's upper half is empty)
+    inputs.Workload("norm_block_S8", "stack", B=1, T=270, D=2048, dtype="bf16", L=21, S=8, seed=10),
+    inputs.Workload("norm_block_S3", "stack", B=1, T=333, D=4096, dtype="bf16", L=11, S=3, seed=11),
 ]
 
 
