@@ -1763,19 +1763,45 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
     q[0] = v.x; q[1] = v.y; q[2] = v.z; q[3] = v.w;
   };
 
+  // With few enough sources and queries (PF), the next row's sources and
+  // upstream gradients are loaded while this row's gradients are formed
+  // (the registers of the two rows fit); otherwise each row's loads come
+  // first in that row.
+  constexpr bool PF = NC + SQ <= 10;
+  raw xn[PF ? NC : 1][VPL], dn[PF ? SQ : 1][VPL];
+  auto load_xd = [&](int64_t r, raw (&xs)[PF ? NC : 1][VPL], raw (&ds)[PF ? SQ : 1][VPL]) {
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+      const int64_t off = r * rowbytes + (int64_t)vec[c] * F::kBytes;
+      #pragma unroll
+      for (int i = 0; i < (PF ? NC : 1); ++i) xs[i][c] = F::load(static_cast<const char*>(p.src[i]) + off);
+      #pragma unroll
+      for (int j = 0; j < (PF ? SQ : 1); ++j) ds[j][c] = F::load(static_cast<const char*>(p.dh[j]) + off);
+    }
+  };
+  if constexpr (PF) load_xd(blockIdx.x < g.R ? (int64_t)blockIdx.x : 0, xn, dn);
+
   int parity = 0;
   for (int64_t row = blockIdx.x; row < g.R; row += gridDim.x, parity ^= 1) {
-    // every load of the row first: sources, upstream gradients, and the
-    // source gradients this row adds to (used after the reduction)
+    // every load of the row first: sources, upstream gradients (loaded
+    // during the previous row with PF), and the source gradients this row
+    // adds to (used after the reduction)
     raw x[NC][VPL], d[SQ][VPL];
     uint4 dv[NC][VPL];
     #pragma unroll
     for (int c = 0; c < VPL; ++c) {
       const int64_t off = row * rowbytes + (int64_t)vec[c] * F::kBytes;
-      #pragma unroll
-      for (int i = 0; i < NC; ++i) x[i][c] = F::load(static_cast<const char*>(p.src[i]) + off);
-      #pragma unroll
-      for (int j = 0; j < SQ; ++j) d[j][c] = F::load(static_cast<const char*>(p.dh[j]) + off);
+      if constexpr (PF) {
+        #pragma unroll
+        for (int i = 0; i < NC; ++i) x[i][c] = xn[PF ? i : 0][c];
+        #pragma unroll
+        for (int j = 0; j < SQ; ++j) d[j][c] = dn[PF ? j : 0][c];
+      } else {
+        #pragma unroll
+        for (int i = 0; i < NC; ++i) x[i][c] = F::load(static_cast<const char*>(p.src[i]) + off);
+        #pragma unroll
+        for (int j = 0; j < SQ; ++j) d[j][c] = F::load(static_cast<const char*>(p.dh[j]) + off);
+      }
       #pragma unroll
       for (int i = 0; i < NC; ++i) dv[i][c] = ld16_stream(p.dV[i] + row * g.D + (int64_t)vec[c] * 4);
     }
@@ -1851,6 +1877,12 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
     // parity, so a wave may write the next row's sums while another still
     // reads these
     __syncthreads();
+    if constexpr (PF) {
+      // the next row's sources and upstream gradients (this row again at the
+      // end: in bounds, unused)
+      const int64_t nr = row + gridDim.x;
+      load_xd(nr < g.R ? nr : row, xn, dn);
+    }
     // The per-row coefficients, one (query, source) pair per lane: lane
     // 8 j + i takes query j and source i; the softmax over a query's sources
     // is a reduction over its 8-lane group. (Computed as uniform values they
