@@ -2963,17 +2963,19 @@ __global__ void partials_kernel(PartialsParams p) {
 #ifndef ATTNRES_PHASE2_VPL
 #define ATTNRES_PHASE2_VPL 2  // preferred vectors per lane in Phase 2 (rows take up to 8 waves)
 #endif
-#ifndef ATTNRES_PHASE2_VPL_NORM
-// the same with the fused norm over at least ATTNRES_PHASE2_NORM_ROWS rows,
-// whose second row reduction (the sum of squares of the rounded h) costs
-// less across fewer waves: at config 3's shape 4 vectors per lane (2 waves
-// per row) took the normed merge from 106.6 to 98.5 us, while the plain merge
-// is fastest at 2; with few rows (decode, 128) the merge is a latency chain
-// and 4 vectors per lane took it from 4.7 to 5.2 us
-#define ATTNRES_PHASE2_VPL_NORM 4
+#ifndef ATTNRES_PHASE2_VPL_WIDE
+// Vectors per lane of the merges that do less memory work per row reduction
+// (the fused norm's second reduction; a block's first merge, which reads no
+// partial), over at least ATTNRES_PHASE2_WIDE_ROWS rows whose vectors fill
+// whole waves at this width: fewer waves per row cost less per reduction.
+// At config 3's shape (4 vectors per lane, 2 waves per row) the normed merge
+// went 106.6 -> 98.5 us and the first merge 68 -> 62 us, while the merge with
+// a partial is fastest at 2; with few rows (decode, 128) the merge is a
+// latency chain and 4 vectors per lane took it from 4.7 to 5.2 us.
+#define ATTNRES_PHASE2_VPL_WIDE 4
 #endif
-#ifndef ATTNRES_PHASE2_NORM_ROWS
-#define ATTNRES_PHASE2_NORM_ROWS 4096
+#ifndef ATTNRES_PHASE2_WIDE_ROWS
+#define ATTNRES_PHASE2_WIDE_ROWS 4096
 #endif
 
 static Geom make_geom(int64_t R, int64_t D, int esize, int vpl, int waves_per_group_max) {
@@ -3549,13 +3551,15 @@ static hipError_t launch_phase2_dt(const Phase2Args& a, const Launch& L) {
   p.o = a.o; p.lse = a.lse; p.w = a.w; p.gm = a.g; p.eps = a.eps;
   p.p_prev = a.p_prev; p.v_prev = a.v_prev; p.p_out = a.p_out; p.h_out = a.h_out;
   p.gf = a.gf; p.eps_f = a.eps_f; p.hn_out = a.hn_out; p.xs = a.xs;
-  // ATTNRES_PHASE2_VPL (with the norm over many rows ATTNRES_PHASE2_VPL_NORM)
-  // vectors per lane, more when a row would need over MW waves (rows are at most 2048
-  // vectors, so at most 8 per lane); with an extra source the next of 2, 4
-  // or 8
+  // ATTNRES_PHASE2_VPL vectors per lane (ATTNRES_PHASE2_VPL_WIDE for the
+  // normed and first merges over many rows), more when a row would need
+  // over MW waves (rows are at most 2048 vectors, so at most 8 per lane);
+  // with an extra source the next of 2, 4 or 8
   const int V = (int)(a.D * T::kBytes / 16);
   constexpr int MW = ATTNRES_PHASE2_MAX_WAVES;
-  int vpl = a.hn_out && a.R >= ATTNRES_PHASE2_NORM_ROWS ? ATTNRES_PHASE2_VPL_NORM : ATTNRES_PHASE2_VPL;
+  const bool wide = (a.hn_out || !a.p_prev) && a.R >= ATTNRES_PHASE2_WIDE_ROWS &&
+                    V % (64 * ATTNRES_PHASE2_VPL_WIDE) == 0;
+  int vpl = wide ? ATTNRES_PHASE2_VPL_WIDE : ATTNRES_PHASE2_VPL;
   if (64 * MW * vpl < V) vpl = (V + 64 * MW - 1) / (64 * MW);
   if (a.xs) vpl = vpl <= 2 ? 2 : vpl <= 4 ? 4 : 8;
   p.g = make_geom(a.R, a.D, T::kBytes, vpl, 4);
