@@ -3654,9 +3654,26 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 #define ATTNRES_BWD_F32_VPL 2  // four-element fp32 vectors per lane (32 bytes of a source)
 #endif
 
+#ifndef ATTNRES_BWD_AGG_BF16_VPL
+// The aggregate backward (one reduction of 3n sums per row, then the
+// gradient pass) over bf16 rows that 2 vectors per lane spread over 4..8
+// waves: 7 sources at 16384 x 4096 took 573 us at 4 vectors per lane and
+// 554 us at 2. The merge backward stays at ATTNRES_BWD_BF16_VPL (at 2 the
+// stack backward went 18.4 -> 19.6 ms).
+#define ATTNRES_BWD_AGG_BF16_VPL 2
+#endif
+
 // Four-element vectors (V = D / 4 per row): VPL of them per lane, doubled
-// (then quadrupled) for rows too wide for eight waves.
-static Geom bwd_geom(int dtype, int64_t R, int64_t D, int* vpl) {
+// (then quadrupled) for rows too wide for eight waves. The aggregate
+// backward over bf16 takes ATTNRES_BWD_AGG_BF16_VPL where that fills 4..8 waves.
+static Geom bwd_geom(int dtype, int64_t R, int64_t D, int* vpl, bool agg = false) {
+  if (agg && dtype == 1) {
+    const Geom ga = make_geom(R, D, 4, ATTNRES_BWD_AGG_BF16_VPL, 4);
+    if (ga.W >= 4 && ga.W <= 8) {
+      *vpl = ATTNRES_BWD_AGG_BF16_VPL;
+      return ga;
+    }
+  }
   int v = dtype == 1 ? ATTNRES_BWD_BF16_VPL : ATTNRES_BWD_F32_VPL;
   Geom g = make_geom(R, D, 4, v, 4);
   while (g.W > 8 && v < 16) {
@@ -3670,7 +3687,7 @@ static Geom bwd_geom(int dtype, int64_t R, int64_t D, int* vpl) {
 BwdPlan plan_aggregate_bwd(int dtype, int64_t R, int64_t D) {
   BwdPlan pl;
   int vpl = 0;
-  const Geom g = bwd_geom(dtype, R, D, &vpl);
+  const Geom g = bwd_geom(dtype, R, D, &vpl, true);
   pl.vpl = vpl;
   pl.supported = g.W <= 8;
   pl.grid = (unsigned)(g.groups < ATTNRES_BWD_MAX_GROUPS ? g.groups : ATTNRES_BWD_MAX_GROUPS);
@@ -3731,7 +3748,10 @@ static hipError_t launch_bwd_dt(const BwdArgs& a, const BwdPlan& pl, const Launc
   p.dh_scale = a.dh_scale; p.dlse = a.dlse;
   p.partial = static_cast<float*>(a.workspace);
   int vpl = 0;
-  p.g = bwd_geom(F::kBytes == 8 ? 1 : 0, a.R, a.D, &vpl);
+  p.g = bwd_geom(F::kBytes == 8 ? 1 : 0, a.R, a.D, &vpl, true);
+  if constexpr (F::kBytes == 8 && ATTNRES_BWD_AGG_BF16_VPL < SMALL) {
+    if (vpl == ATTNRES_BWD_AGG_BF16_VPL) return launch_bwd_vpl<F, ATTNRES_BWD_AGG_BF16_VPL, false>(p, a.n, pl.grid, L);
+  }
   if (vpl == SMALL) return launch_bwd_vpl<F, SMALL, false>(p, a.n, pl.grid, L);
   if (vpl == 2 * SMALL) return launch_bwd_vpl<F, 2 * SMALL, true>(p, a.n, pl.grid, L);
   if constexpr (SMALL * 4 <= 8) {
