@@ -1518,12 +1518,12 @@ ATTNRES_API int attnres_block_stack_backward(
     // and its log-sum-exp dlse_j; the gradients of b_0 .. b_k accumulate. Up
     // to 8 queries share one pass over the sources where the shape allows.
     if (attnres::phase1_bwd_eligible(dtype, n, D)) {
-      constexpr int QB = 4;  // queries per pass
+      const int QB = attnres::phase1_bwd_max_queries(n);  // queries per pass
       for (int j0 = 0; j0 < Sk; j0 += QB) {
         const int Sq = Sk - j0 < QB ? Sk - j0 : QB;
-        const float* scl[QB];
-        const float* dls[QB];
-        int accq[QB];
+        const float* scl[8];
+        const float* dls[8];
+        int accq[8];
         for (int j = 0; j < Sq; ++j) {
           scl[j] = j0 + j ? A + (int64_t)(j0 + j) * R : nullptr;
           dls[j] = j0 + j ? DL + (int64_t)(j0 + j) * R : nullptr;

@@ -1246,6 +1246,7 @@ __device__ __forceinline__ void pin(uint2& v) { asm volatile("" : "+v"(v.x), "+v
 // no gaps (with eight-element bf16 vectors each lane would write 32 bytes in
 // two strided halves, which measured 1.6x the algorithmic write traffic).
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) u32x2_t gu32x2_t;
 struct Bf16x4 {
   typedef uint2 raw;
   static constexpr int kBytes = 8;
@@ -1673,7 +1674,7 @@ __global__ __launch_bounds__(512) void merge_bwd_kernel(MergeBwdParams p) {
 //           - (sum_j ds_ji s_ji / (D r_i^2)) V_i
 //   dq~_j += sum_i (ds_ji / r_i) V_i   (per-workgroup partial rows)
 // One workgroup row at a time, two 4-element vectors per lane (rows of at
-// most 2 x 64 x 8 vectors), up to 4 queries per launch (a template
+// most 2 x 64 x 8 vectors), up to 8 queries per launch (a template
 // parameter, so no argument array is indexed at run time):
 //  - every load of a row is issued first, the dV_i it adds to included;
 //  - each wave reduces the 2 S n + n row sums one (query, source) pair at a
@@ -1683,13 +1684,14 @@ __global__ __launch_bounds__(512) void merge_bwd_kernel(MergeBwdParams p) {
 //    8 j + i; the softmax over a query's sources is an 8-lane reduction) and
 //    broadcast as scalars: computed as uniform values, every lane would run
 //    the whole table;
-//  - the folded queries and the dq~ sums live in LDS, each lane owning its
-//    elements (no barrier); from global memory, each use of a query would
-//    wait for its load.
+//  - the folded queries live in LDS, each lane owning its elements (no
+//    barrier); from global memory, each use of a query would wait for its
+//    load. The dq~ sums do too with up to 4 queries; with more, the queries
+//    alone fill 128 KiB at 4096 elements and the sums stay in registers.
 // Sources and upstream gradients are read once; each dV_i is read and written
 // once (added to), instead of once per query.
 // ---------------------------------------------------------------------------
-constexpr int kP1BwdQ = 4;  // queries per launch (their queries and dq~ sums in LDS)
+constexpr int kP1BwdQ = 8;  // queries per launch (the queries in LDS)
 constexpr int kP1BwdVpl = 2;  // four-element vectors per lane
 constexpr int kP1BwdMaxN = 8;  // sources
 
@@ -1727,15 +1729,19 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
   };
   // row sums: q~_j.x_i [SQ][NC], dh_j.x_i [SQ][NC], x_i.x_i [NC]
   constexpr int NR = (2 * SQ + 1) * NC;
-  // [SQ][D] folded queries, [SQ][D] dq~ sums of this workgroup's rows, then
-  // the wave sums [2 (row parity)][W][NR]
+  // the dq~ sums of this workgroup's rows in registers (more than 4 queries)
+  // or in LDS
+  constexpr bool DQR = SQ > 4;
+  // [SQ][D] folded queries, [SQ][D] dq~ sums (in LDS), then the wave sums
+  // [2 (row parity)][W][NR]
   extern __shared__ float lds[];
   const Geom& g = p.g;
   float* qs = lds;
   float* dqs = lds + SQ * g.D;
-  float* wsum = lds + 2 * SQ * g.D;
+  float* wsum = lds + (DQR ? 1 : 2) * SQ * g.D;
   const int t = threadIdx.x, wr = t >> 6, lane = t & 63, stride = 64 * g.W;
-  const int64_t rowbytes = (int64_t)g.V * F::kBytes;
+  const int64_t rowbytes = (int64_t)g.V * F::kBytes;  // a bf16 row
+  const int64_t growbytes = (int64_t)g.D * 4;         // an fp32 gradient row
   bool in_row[VPL];
   int vec[VPL];
   #pragma unroll
@@ -1744,6 +1750,16 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
     in_row[c] = vec[c] < g.V;
     if (!in_row[c]) vec[c] = 0;  // reads vector 0; its values are discarded
   }
+  // Every row of every stream is addressed as a wave-uniform base plus one
+  // 32-bit lane offset per vector (8 bytes a bf16 vector, 16 an fp32 one):
+  // 64-bit lane addresses per stream, hoisted out of the row loop, took two
+  // registers per stream and vector and spilled with 8 queries.
+  auto ld_x = [&](const void* base, int64_t r, int c) -> raw {
+    const gchar_t* b = uniform_ptr(static_cast<const char*>(base) + r * rowbytes);
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const gu32x2_t*>(b + (uint32_t)vec[c] * 8u));
+    return make_uint2(v.x, v.y);
+  };
+  auto g_row = [&](float* base, int64_t r) { return uniform_ptr(reinterpret_cast<char*>(base) + r * growbytes); };
   // each lane owns its elements of the queries and of the dq~ sums: no
   // barrier is needed for either. The queries are read from LDS in every
   // row (from global memory, each first use would wait for its load).
@@ -1755,8 +1771,15 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
         float q[4];
         query(j, (int64_t)vec[c] * 4, q);
         *reinterpret_cast<float4*>(qs + j * g.D + vec[c] * 4) = make_float4(q[0], q[1], q[2], q[3]);
-        *reinterpret_cast<float4*>(dqs + j * g.D + vec[c] * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (!DQR) *reinterpret_cast<float4*>(dqs + j * g.D + vec[c] * 4) = make_float4(0.f, 0.f, 0.f, 0.f);
       }
+  float dqr[DQR ? SQ : 1][VPL][4];
+  #pragma unroll
+  for (int j = 0; j < (DQR ? SQ : 1); ++j)
+    #pragma unroll
+    for (int c = 0; c < VPL; ++c)
+      #pragma unroll
+      for (int e = 0; e < 4; ++e) dqr[j][c][e] = 0.f;
   // this lane's query elements (lanes past the row's end read element 0)
   auto qload = [&](int j, int c, float* q) {
     const float4 v = *reinterpret_cast<const float4*>(qs + j * g.D + vec[c] * 4);
@@ -1772,11 +1795,10 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
   auto load_xd = [&](int64_t r, raw (&xs)[PF ? NC : 1][VPL], raw (&ds)[PF ? SQ : 1][VPL]) {
     #pragma unroll
     for (int c = 0; c < VPL; ++c) {
-      const int64_t off = r * rowbytes + (int64_t)vec[c] * F::kBytes;
       #pragma unroll
-      for (int i = 0; i < (PF ? NC : 1); ++i) xs[i][c] = F::load(static_cast<const char*>(p.src[i]) + off);
+      for (int i = 0; i < (PF ? NC : 1); ++i) xs[i][c] = ld_x(p.src[i], r, c);
       #pragma unroll
-      for (int j = 0; j < (PF ? SQ : 1); ++j) ds[j][c] = F::load(static_cast<const char*>(p.dh[j]) + off);
+      for (int j = 0; j < (PF ? SQ : 1); ++j) ds[j][c] = ld_x(p.dh[j], r, c);
     }
   };
   if constexpr (PF) load_xd(blockIdx.x < g.R ? (int64_t)blockIdx.x : 0, xn, dn);
@@ -1790,7 +1812,6 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
     uint4 dv[NC][VPL];
     #pragma unroll
     for (int c = 0; c < VPL; ++c) {
-      const int64_t off = row * rowbytes + (int64_t)vec[c] * F::kBytes;
       if constexpr (PF) {
         #pragma unroll
         for (int i = 0; i < NC; ++i) x[i][c] = xn[PF ? i : 0][c];
@@ -1798,12 +1819,16 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
         for (int j = 0; j < SQ; ++j) d[j][c] = dn[PF ? j : 0][c];
       } else {
         #pragma unroll
-        for (int i = 0; i < NC; ++i) x[i][c] = F::load(static_cast<const char*>(p.src[i]) + off);
+        for (int i = 0; i < NC; ++i) x[i][c] = ld_x(p.src[i], row, c);
         #pragma unroll
-        for (int j = 0; j < SQ; ++j) d[j][c] = F::load(static_cast<const char*>(p.dh[j]) + off);
+        for (int j = 0; j < SQ; ++j) d[j][c] = ld_x(p.dh[j], row, c);
       }
       #pragma unroll
-      for (int i = 0; i < NC; ++i) dv[i][c] = ld16_stream(p.dV[i] + row * g.D + (int64_t)vec[c] * 4);
+      for (int i = 0; i < NC; ++i) {
+        const u32x4_t v = __builtin_nontemporal_load(
+            reinterpret_cast<const gu32x4_t*>(g_row(p.dV[i], row) + (uint32_t)vec[c] * 16u));
+        dv[i][c] = make_uint4(v.x, v.y, v.z, v.w);
+      }
     }
     // lanes past the row's end read vector 0: a zero source there zeroes
     // every term those lanes add (scores, gradient dots, sums of squares, dq~)
@@ -1915,10 +1940,11 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
     const float gbar = group8_sum(al * (gs * tg));
     const float Al = al * gs;
     const float Bl = al * (gs * tg - gbar + dl) * rl;
-    // cc_i = sum over queries of B sc r / D: the lanes i, 8 + i, 16 + i, 24 + i
+    // cc_i = sum over queries of B sc r / D: the lanes 8 j + i
     float ccl = valid ? Bl * sc * rl * g.invD : 0.f;
-    ccl += __shfl_xor(ccl, 8);
-    ccl += __shfl_xor(ccl, 16);
+    if constexpr (SQ > 1) ccl += __shfl_xor(ccl, 8);
+    if constexpr (SQ > 2) ccl += __shfl_xor(ccl, 16);
+    if constexpr (SQ > 4) ccl += __shfl_xor(ccl, 32);
     auto lane_val = [&](float v, int k) {
       return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
     };
@@ -1927,11 +1953,16 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
     for (int i = 0; i < NC; ++i) cc[i] = lane_val(ccl, i);
     #pragma unroll
     for (int j = 0; j < SQ; ++j) {
+      // one query's coefficients at a time: the empty asm keeps the compiler
+      // from reading every query's ahead into scalar registers (which then
+      // spill into vector registers)
+      float Alj = Al, Blj = Bl;
+      asm volatile("" : "+v"(Alj), "+v"(Blj));
       float A[NC], B[NC];
       #pragma unroll
       for (int i = 0; i < NC; ++i) {
-        A[i] = lane_val(Al, 8 * j + i);
-        B[i] = lane_val(Bl, 8 * j + i);
+        A[i] = lane_val(Alj, 8 * j + i);
+        B[i] = lane_val(Blj, 8 * j + i);
       }
       launder();
       #pragma unroll
@@ -1953,7 +1984,10 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
           dv[i][c] = make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
                                 __float_as_uint(o[3]));
         }
-        if (in_row[c]) {
+        if constexpr (DQR) {
+          #pragma unroll
+          for (int e = 0; e < 4; ++e) dqr[DQR ? j : 0][c][e] += dq[e];
+        } else if (in_row[c]) {
           float4* acc = reinterpret_cast<float4*>(dqs + j * g.D + vec[c] * 4);
           float4 a = *acc;
           a.x += dq[0]; a.y += dq[1]; a.z += dq[2]; a.w += dq[3];
@@ -1972,7 +2006,10 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
                       __uint_as_float(dv[i][c].w)};
         #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] -= cc[i] * xf[e];
-        char* dst = store_target(in_row[c], reinterpret_cast<char*>(p.dV[i] + row * g.D + (int64_t)vec[c] * 4));
+        // lanes past the row's end store to the sink (a branch here costs
+        // the 8-query variants their registers)
+        gchar_t* dst = g_row(p.dV[i], row) + (uint32_t)vec[c] * 16u;
+        dst = in_row[c] ? dst : (gchar_t*)g_store_sink;
         st16_stream(dst, make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
                                     __float_as_uint(o[3])));
       }
@@ -1983,7 +2020,9 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
     for (int c = 0; c < VPL; ++c)
       if (in_row[c]) {
         float* prow = p.partial + ((int64_t)j * gridDim.x + blockIdx.x) * g.D + vec[c] * 4;
-        const float4 a = *reinterpret_cast<const float4*>(dqs + j * g.D + vec[c] * 4);
+        const float4 a = DQR ? make_float4(dqr[DQR ? j : 0][c][0], dqr[DQR ? j : 0][c][1], dqr[DQR ? j : 0][c][2],
+                                           dqr[DQR ? j : 0][c][3])
+                             : *reinterpret_cast<const float4*>(dqs + j * g.D + vec[c] * 4);
         st16(prow, make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z),
                               __float_as_uint(a.w)));
       }
@@ -3794,6 +3833,10 @@ bool phase1_bwd_eligible(int dtype, int n, int64_t D) {
   return dtype == 1 && n >= 1 && n <= kP1BwdMaxN && D % 4 == 0 && V <= 64 * 8 * kP1BwdVpl;
 }
 
+// With 8 queries, up to 6 sources fit the registers (244 VGPRs at 6); 7 and
+// 8 sources spill inside the row loop from 7 queries, so they take 4.
+int phase1_bwd_max_queries(int n) { return n <= 6 ? kP1BwdQ : 4; }
+
 size_t phase1_bwd_workspace(int64_t R, int64_t D) {
   const int64_t grid = R < ATTNRES_P1BWD_GROUPS ? (R > 0 ? R : 1) : ATTNRES_P1BWD_GROUPS;
   const int64_t chunks = (grid + ATTNRES_BWD_CHUNK - 1) / ATTNRES_BWD_CHUNK;
@@ -3802,7 +3845,7 @@ size_t phase1_bwd_workspace(int64_t R, int64_t D) {
 
 template <int NC, int SQ>
 static hipError_t launch_p1bwd_q(const P1BwdParams& p, unsigned grid, const Launch& L) {
-  const size_t lds = ((size_t)2 * SQ * p.g.D + (size_t)2 * p.g.W * (2 * SQ + 1) * NC) * sizeof(float);
+  const size_t lds = ((size_t)(SQ > 4 ? 1 : 2) * SQ * p.g.D + (size_t)2 * p.g.W * (2 * SQ + 1) * NC) * sizeof(float);
   return launch(L, phase1_bwd_kernel<NC, SQ>, dim3(grid), dim3(64 * p.g.W), lds, p);
 }
 
@@ -3812,7 +3855,11 @@ static hipError_t launch_p1bwd_t(const P1BwdParams& p, unsigned grid, const Laun
     case 1: return launch_p1bwd_q<NC, 1>(p, grid, L);
     case 2: return launch_p1bwd_q<NC, 2>(p, grid, L);
     case 3: return launch_p1bwd_q<NC, 3>(p, grid, L);
-    default: return launch_p1bwd_q<NC, 4>(p, grid, L);
+    case 4: return launch_p1bwd_q<NC, 4>(p, grid, L);
+    case 5: return launch_p1bwd_q<NC, 5>(p, grid, L);
+    case 6: return launch_p1bwd_q<NC, 6>(p, grid, L);
+    case 7: return launch_p1bwd_q<NC, 7>(p, grid, L);
+    default: return launch_p1bwd_q<NC, 8>(p, grid, L);
   }
 }
 

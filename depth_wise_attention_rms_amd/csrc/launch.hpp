@@ -159,7 +159,7 @@ hipError_t launch_aggregate_bwd(int dtype, const BwdArgs& a, const BwdPlan& pl, 
 hipError_t launch_bwd_reduce(const BwdArgs& a, const BwdPlan& pl, int stage, const Launch& L);
 hipError_t launch_merge_bwd(int dtype, const MergeBwdArgs& a, const BwdPlan& pl, const Launch& L);
 
-// Batched Phase-1 backward: S <= 4 queries (consecutive rows of w, g, dw,
+// Batched Phase-1 backward: S <= 8 queries (consecutive rows of w, g, dw,
 // dgamma) over the same n <= 8 bf16 sources in one pass; query j's upstream
 // gradient is dh_scale[j][r] * dh[j][r] (dh_scale[j] null: 1) and its
 // log-sum-exp's gradient dlse[j] (null: 0). dV[i] fp32 are added to; dw /
@@ -182,6 +182,8 @@ struct Phase1BwdArgs {
   const int* accumulate_q;  // [S]
 };
 bool phase1_bwd_eligible(int dtype, int n, int64_t D);
+// Queries one pass takes over n sources (8, or 4 where 8 would spill).
+int phase1_bwd_max_queries(int n);
 size_t phase1_bwd_workspace(int64_t R, int64_t D);
 hipError_t launch_phase1_bwd(const Phase1BwdArgs& a, void* ws, const Launch& L, const Launch& Lred);
 

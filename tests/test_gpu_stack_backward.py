@@ -110,6 +110,12 @@ BWD_STACKS = [
     # nine blocks of two: the batched Phase-1 backward over 7 and 8 sources,
     # one aggregate backward per query over 9
     (1, 70, 1024, 2, 17, "bf16", True),
+    # config 3's block shape at few rows: 8 queries per pass over 1..6 sources
+    (1, 130, 4096, 8, 48, "bf16", True),
+    # ragged rows (250 four-element vectors): 7 queries per pass, and 8
+    # queries over 7 and 8 sources, which take two passes of 4
+    (1, 90, 1000, 7, 30, "bf16", True),
+    (1, 50, 1000, 8, 64, "bf16", False),
 ]
 
 
