@@ -24,7 +24,7 @@ from depth_wise_attention_rms_amd import binding as b
 from depth_wise_attention_rms_amd import inputs
 from depth_wise_attention_rms_amd.workload import EPS, DeviceStack
 from tests.bwd_scale import bwd_scales
-from tests.parity import TOL, scaled_error, to_host, widen
+from tests.parity import TOL, sample_rows, scaled_error, to_host, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -126,6 +126,42 @@ def test_stack_backward_shapes(B, T, D, S, L, dtype, gains):
     announce(f"{wl.name} gains={gains}")
     worst = run_case(wl, gains)
     print(f"[gpu-case] {wl.name}: worst scaled error {worst:.3e}", flush=True)
+    torch.cuda.empty_cache()
+
+
+def test_stack_backward_benchmark_shape_sampled_rows():
+    """The stack backward at the benchmark's shape and launch configuration
+    (config 3's stack: R = 16384, D = 4096, L = 48, S = 8, bf16 inputs, fp32
+    gradients, the upstream gradients of the benchmark): dx and every dv_l on
+    64 sampled rows against the oracle's stack backward over those rows alone.
+    A row's gradients depend on that row's inputs only, so the sample gives
+    the same values as the whole; dW and dGamma sum over every row and are
+    checked at the smaller shapes above."""
+    wl = inputs.WORKLOADS["block_L48_S8"]
+    announce(f"{wl.name} stack backward, sampled rows")
+    ds = DeviceStack(wl)
+    ds.forward()
+    torch.cuda.synchronize()
+    R, D, L = wl.R, wl.D, wl.L
+    dh = [inputs.fill_normal(torch.empty((R, D), dtype=ds.dt, device="cuda"), wl.seed + 1, inputs.ROLE_AUX, l, 1.0)
+          for l in range(L)]
+    dy = inputs.fill_normal(torch.empty((R, D), dtype=ds.dt, device="cuda"), wl.seed + 2, inputs.ROLE_AUX, 99, 1.0)
+    dx, dv, _, _ = b.attnres_block_stack_backward(ds.x, ds.v, ds.W, wl.S, dy, dh, block_sums=ds.block_sums,
+                                                  eps=EPS)
+    torch.cuda.synchronize()
+    rows = sample_rows(R, 64, seed=3)
+    ids = torch.from_numpy(rows).to("cuda")
+    xr, vr = ds.host_rows(rows)
+    dhr = [to_host(t[ids]) for t in dh]
+    dyr = to_host(dy[ids])
+    ref = oracle.block_stack_backward(xr, vr, ds.W_host, wl.S, dhr, dyr, Gamma=None, eps=EPS)
+    sc = oracle.block_stack_backward(xr, vr, ds.W_host, wl.S, dhr, dyr, Gamma=None, eps=EPS, agg_fn=_scale_fn)
+    worst = _check(f"{wl.name} dx", to_host(dx[ids]), ref["dx"], sc["dx"], wl.dtype)
+    for l in range(L):
+        worst = max(worst, _check(f"{wl.name} dv_{l + 1}", to_host(dv[l][ids]), ref["dv"][l], sc["dv"][l],
+                                  wl.dtype))
+    print(f"[gpu-case] {wl.name} stack backward: worst scaled error {worst:.3e}", flush=True)
+    del ds, dh, dy, dx, dv
     torch.cuda.empty_cache()
 
 
