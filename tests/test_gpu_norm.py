@@ -169,6 +169,36 @@ def test_stack_forward_norm_without_gains():
         assert_close_scaled(rec[l], hn_ref, scale, wl.dtype, f"{wl.name} hn_{l + 1}")
 
 
+def test_stack_forward_norm_benchmark_shape():
+    """The normed stack at the benchmark's shape and launch configuration
+    (config 3's stack, 16384 rows of 4096, the gains and eps of the normed
+    benchmark): 128 sampled rows of every hn_l against the oracle; y and the
+    block sums bit-identical to the forward without the norm."""
+    wl = inputs.WORKLOADS["block_L48_S8"]
+    announce(f"{wl.name} normed")
+    ds = DeviceStack(wl)
+    Gf = np.stack([inputs.gains(wl.seed + 100, wl.D, layer=l) for l in range(wl.L)]).astype(np.float32)
+    eps_f = 1e-6
+    ds.forward()
+    torch.cuda.synchronize()
+    y_plain = to_host(ds.y)
+    bs_plain = [to_host(t) for t in ds.block_sums]
+    rows = sample_rows(wl.R, 128, seed=5)
+    ds.forward(ds.recorder(rows), norm=(torch.from_numpy(Gf).cuda(), eps_f))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(ds.y), y_plain), "the norm must not change y"
+    for k, t in enumerate(ds.block_sums):
+        assert np.array_equal(to_host(t), bs_plain[k]), f"the norm must not change b_{k + 1}"
+    rec = to_host(ds.rec)
+    xr, vr = ds.host_rows(rows)
+    ref = oracle.block_stack(xr, vr, ds.W_host, wl.S, eps=EPS)
+    for l in range(wl.L):
+        hn_ref, scale = norm_reference(ref["h"][l], ref["h_scale"][l], wl.dtype, Gf[l], eps_f)
+        assert_close_scaled(rec[l], hn_ref, scale, wl.dtype, f"{wl.name} hn_{l + 1}")
+    del ds
+    torch.cuda.empty_cache()
+
+
 def test_stack_forward_norm_scores_pass():
     """The normed stack whose Phase 1 runs as the matrix-core scores pass and
     the outputs pass (4096 rows of 7168, 12 queries, a short last block):
