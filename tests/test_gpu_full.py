@@ -12,7 +12,7 @@ import oracle
 from depth_wise_attention_rms_amd import binding as b
 from depth_wise_attention_rms_amd import inputs
 from depth_wise_attention_rms_amd.workload import EPS, DeviceStack
-from tests.parity import assert_close_scaled, assert_stats, to_device, to_host
+from tests.parity import assert_close_scaled, assert_stats, sample_rows, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -100,3 +100,29 @@ def test_full_two_phase_matches_naive(name, L, C, B, T, D, dtype):
             assert_close_scaled(recs[l], ref["h"][l], ref["h_scale"][l], dtype, f"{name} h_{l + 1}")
         assert_close_scaled(to_host(y[sl]), ref["y"], ref["y_scale"], dtype, f"{name} y")
         assert np.array_equal(recs[0], xr[sl]), "h_1 must equal the embedding bit for bit"
+
+
+@pytest.mark.parametrize("C", [4, 8])
+def test_full_schedule_benchmark_shape(C):
+    """The Full two-phase schedule at the benchmark's shape and launch
+    configuration (16384 rows of 4096, L = 16, bf16; schedule block sizes 4 and
+    8, the measured ones): 128 sampled rows of every h_l and y against the
+    oracle's naive Full forward."""
+    wl = inputs.WORKLOADS["full_L16_D4096"]
+    name = f"{wl.name}_C{C}"
+    announce(name)
+    ds = DeviceStack(wl)
+    rows = sample_rows(wl.R, 128, seed=C)
+    rec = ds.recorder(rows)
+    y = b.attnres_full_stack_forward(ds.x, ds.W, C, rec, Gamma=ds.Gamma, eps=EPS)
+    torch.cuda.synchronize()
+    xr, vr = ds.host_rows(rows)
+    ref = oracle.block_stack(xr, vr, ds.W_host, 1, Gamma=ds.Gamma_host, eps=EPS)
+    recs = to_host(ds.rec)
+    for l in range(wl.L):
+        assert_close_scaled(recs[l], ref["h"][l], ref["h_scale"][l], wl.dtype, f"{name} h_{l + 1}")
+    ids = torch.from_numpy(rows).to("cuda")
+    assert_close_scaled(to_host(y[ids]), ref["y"], ref["y_scale"], wl.dtype, f"{name} y")
+    assert np.array_equal(recs[0], xr), "h_1 must equal the embedding bit for bit"
+    del ds, y
+    torch.cuda.empty_cache()
