@@ -3704,20 +3704,23 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Four-element vectors (V = D / 4 per row): VPL of them per lane, doubled
 // (then quadrupled) for rows too wide for eight waves. The aggregate
-// backward over bf16 takes ATTNRES_BWD_AGG_BF16_VPL where that fills 4..8 waves.
+// backward over bf16 takes ATTNRES_BWD_AGG_BF16_VPL where that fills 4..8
+// waves and both widths take one row per workgroup: the merge backward
+// shares the plan's grid and dq~ partial rows (grid x rows per workgroup),
+// so the two geometries must agree on rows per workgroup.
 static Geom bwd_geom(int dtype, int64_t R, int64_t D, int* vpl, bool agg = false) {
-  if (agg && dtype == 1) {
-    const Geom ga = make_geom(R, D, 4, ATTNRES_BWD_AGG_BF16_VPL, 4);
-    if (ga.W >= 4 && ga.W <= 8) {
-      *vpl = ATTNRES_BWD_AGG_BF16_VPL;
-      return ga;
-    }
-  }
   int v = dtype == 1 ? ATTNRES_BWD_BF16_VPL : ATTNRES_BWD_F32_VPL;
   Geom g = make_geom(R, D, 4, v, 4);
   while (g.W > 8 && v < 16) {
     v *= 2;
     g = make_geom(R, D, 4, v, 4);
+  }
+  if (agg && dtype == 1) {
+    const Geom ga = make_geom(R, D, 4, ATTNRES_BWD_AGG_BF16_VPL, 4);
+    if (ga.W >= 4 && ga.W <= 8 && ga.RPW == g.RPW) {
+      *vpl = ATTNRES_BWD_AGG_BF16_VPL;
+      return ga;
+    }
   }
   *vpl = v;
   return g;

@@ -116,6 +116,10 @@ BWD_STACKS = [
     # queries over 7 and 8 sources, which take two passes of 4
     (1, 90, 1000, 7, 30, "bf16", True),
     (1, 50, 1000, 8, 64, "bf16", False),
+    # more rows than the backward's workgroup cap at D = 2048 (two rows per
+    # merge-backward workgroup): every workgroup walks several row groups and
+    # the query gradients sum every partial row
+    (1, 2100, 2048, 4, 9, "bf16", True),
 ]
 
 
