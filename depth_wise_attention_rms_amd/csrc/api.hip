@@ -1319,9 +1319,13 @@ BwdStackLayout bwd_stack_layout(int L, int S, int64_t R, int64_t D, int dtype) {
   if (ng) s.gbytes = attnres::phase1_gemm_workspace(Sk, R, D, ng);
   off = align256(off + s.gbytes);
   {
+    // one aggregate backward's plan, or one per merge of a block (its dq~
+    // partials reduced together), or the batched Phase-1 backward's
     const size_t a = attnres::plan_aggregate_bwd(dtype, R, D).bytes;
+    const size_t am = Sk > 1 ? (size_t)(Sk - 1) * a : a;
     const size_t b = attnres::phase1_bwd_workspace(R, D);
-    s.bw = off; off = align256(off + (a > b ? a : b));
+    const size_t ab = am > a ? am : a;
+    s.bw = off; off = align256(off + (ab > b ? ab : b));
   }
   s.total = off;
   return s;
@@ -1504,15 +1508,26 @@ ATTNRES_API int attnres_block_stack_backward(
     // Phase-2 merges in reverse: sublayer start + j merged (lse_j, o_j) with p_j;
     // its backward turns dh into the gradient of p_j, which (with the gradient
     // from the partial's later uses, dv[start + j - 1]) is that of v_{start+j-1}
+    // (each merge's dq~ partials in a slot of their own, reduced together below)
     for (int j = Sk - 1; j >= 1; --j) {
       const int l = start + j;
       MergeBwdArgs mb{o_slice(j), LSE + (int64_t)j * R, p_slice(j), qrow(W, l), qrow(Gamma, l), eps,
-                      dh[j], dv[l - 1], dv[l - 2], A + (int64_t)j * R, DL + (int64_t)j * R, R, D, bw};
+                      dh[j], dv[l - 1], dv[l - 2], A + (int64_t)j * R, DL + (int64_t)j * R, R, D,
+                      static_cast<char*>(bw) + (size_t)(j - 1) * pl.bytes};
       hipError_t e = attnres::launch_merge_bwd(
           dtype, mb, pl, timed_launch(K_BWD, rb * 3 + gb * 2 + R * 8.0, st, "merge_bwd_kernel"));
       if (e != hipSuccess) return hip_fail(fn, e);
-      TRY(reduce_q(qrow(W, l), qrow(Gamma, l), frow(dW, l), frow(dGamma, l), 0));
       TRY(callback(l - 1, dv[l - 2], &dh[j - 1]));
+    }
+    // the merges' query and gain gradients (rows start + 1 .. end), written
+    // before the Phase-1 backward adds to them and reuses the slots
+    {
+      const double qbytes = (double)(Sk - 1) * ((double)pl.P * D * 4 + (pl.P2 ? 2.0 * pl.P2 * D * 4 : 0.0) +
+                                                 D * 4.0 * (dGamma ? 2 : 1));
+      hipError_t e = attnres::launch_bwd_reduce_queries(
+          pl, bw, pl.bytes, Sk - 1, D, qrow(W, start + 1), qrow(Gamma, start + 1), frow(dW, start + 1),
+          frow(dGamma, start + 1), 0u, timed_launch(K_BWD_REDUCE, qbytes, st));
+      if (e != hipSuccess) return hip_fail(fn, e);
     }
     // Phase-1 backward: query j's output received a_j dh_j (dh_0 itself: h = o_0)
     // and its log-sum-exp dlse_j; the gradients of b_0 .. b_k accumulate. Up

@@ -3825,6 +3825,33 @@ hipError_t launch_bwd_reduce(const BwdArgs& a, const BwdPlan& pl, int stage, con
                 (unsigned)((a.accumulate_q < 0 ? a.accumulate : a.accumulate_q) ? 1 : 0), (int64_t)0, (int64_t)0);
 }
 
+// The query-gradient reductions of nq aggregates in one launch per stage:
+// query q's dq~ partial rows (the plan's layout, its first-stage sums after
+// them) start q * slot bytes into ws; w, g, dw and dgamma are the first
+// query's rows, the others D apart. Timed from the first stage's start to
+// the second's end.
+hipError_t launch_bwd_reduce_queries(const BwdPlan& pl, void* ws, size_t slot, int nq, int64_t D,
+                                     const float* w, const float* g, float* dw, float* dgamma,
+                                     unsigned acc_mask, const Launch& L) {
+  if (nq < 1 || nq > 32 || slot % sizeof(float)) return hipErrorInvalidValue;
+  const unsigned bx = (unsigned)((D / 4 + 255) / 256);
+  const int64_t qs = (int64_t)(slot / sizeof(float));
+  const float* partial = static_cast<const float*>(ws);
+  float* stage1 = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.partial_bytes);
+  if (pl.P2) {
+    hipError_t e = launch(Launch{L.stream, L.start, nullptr}, bwd_colsum_kernel<false>,
+                          dim3(bx, (unsigned)pl.P2, (unsigned)nq), dim3(256), 0, partial, pl.P, D, pl.chunk,
+                          stage1, (const float*)nullptr, (const float*)nullptr, (float*)nullptr, (float*)nullptr,
+                          0u, qs, qs);
+    if (e != hipSuccess) return e;
+  }
+  const float* in = pl.P2 ? stage1 : partial;
+  const int64_t rows = pl.P2 ? pl.P2 : pl.P;
+  return launch(Launch{L.stream, pl.P2 ? nullptr : L.start, L.stop}, bwd_colsum_kernel<true>,
+                dim3(bx, 1, (unsigned)nq), dim3(256), 0, in, rows, D, rows, (float*)nullptr, w, g, dw, dgamma,
+                acc_mask, qs, (int64_t)0);
+}
+
 #ifndef ATTNRES_P1BWD_GROUPS
 #define ATTNRES_P1BWD_GROUPS 512  // workgroups of the batched Phase-1 backward (each walks rows)
 #endif

@@ -157,6 +157,13 @@ hipError_t launch_aggregate_bwd(int dtype, const BwdArgs& a, const BwdPlan& pl, 
 // stage 0: partial rows -> chunk sums (no-op when P2 == 0); stage 1: final
 // sum, dw and dgamma
 hipError_t launch_bwd_reduce(const BwdArgs& a, const BwdPlan& pl, int stage, const Launch& L);
+// The query-gradient reductions of nq aggregates (1..32) at once: query q's
+// partials in the plan's layout at ws + q * slot (slot a multiple of 4
+// bytes); w, g, dw, dgamma the first query's rows, the others D apart; bit q
+// of acc_mask: query q adds to dw / dgamma instead of writing them.
+hipError_t launch_bwd_reduce_queries(const BwdPlan& pl, void* ws, size_t slot, int nq, int64_t D,
+                                     const float* w, const float* g, float* dw, float* dgamma,
+                                     unsigned acc_mask, const Launch& L);
 hipError_t launch_merge_bwd(int dtype, const MergeBwdArgs& a, const BwdPlan& pl, const Launch& L);
 
 // Batched Phase-1 backward: S <= 8 queries (consecutive rows of w, g, dw,
