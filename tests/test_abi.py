@@ -245,3 +245,18 @@ def test_noalloc_backward_validates_on_the_host():
     rc = L.attnres_aggregate_backward_noalloc(src, 1, 64, 1024, 1, FAKE, None, 1e-8, ctypes.c_void_p(0x30000),
                                               dv, 0, None, None, None)
     assert rc == -1 and "dw is NULL" in _last()
+
+
+@pytest.mark.parametrize("L_,S,R,D,dt", [(48, 8, 16384, 4096, 1), (20, 6, 600, 2048, 1), (13, 5, 65, 1024, 0),
+                                         (30, 7, 90, 1000, 1), (64, 8, 50, 1000, 1), (9, 4, 2100, 2048, 1)])
+def test_stack_backward_workspace_holds_a_slot_per_merge(L_, S, R, D, dt):
+    """The stack backward reduces a block's merge-backward query gradients
+    together, each merge's dq~ partial rows in a slot the size of one
+    aggregate backward's workspace: beyond the recomputed Phase-1 outputs
+    (min(S, L) rows of [R, D]) the workspace holds min(S, L) - 1 such slots."""
+    lib = b.lib()
+    slot = lib.attnres_aggregate_backward_workspace_bytes(R, D, dt)
+    total = lib.attnres_stack_backward_workspace_bytes(L_, S, R, D, dt)
+    sk = min(S, L_)
+    assert slot > 0 and total % 256 == 0
+    assert total >= (sk - 1) * slot + sk * R * D * (2 if dt == 1 else 4)
