@@ -1471,17 +1471,19 @@ ATTNRES_API int attnres_block_stack_backward(
       TRY(agg_bwd(b.data(), db.data(), n, start, dh[0], nullptr, nullptr, 1, 0));
       continue;
     }
-    // recompute the block's Phase 1 (o_j, lse_j) and its partials p_2 .. p_{Sk-1}
-    const bool one_source = n == 1 && attnres::phase1_stats_supported(dtype, 1, Sk, D);
+    // recompute the block's Phase 1 (o_j, lse_j) and its partials p_2 .. p_{Sk-1};
+    // only queries 1 .. Sk-1 are needed (the merges'; the Phase-1 backward forms
+    // its own softmax), so query 0's output is not written again
+    const bool one_source = n == 1 && attnres::phase1_stats_supported(dtype, 1, Sk - 1, D);
     char* O = ws + lay.o;
     float* LSE = reinterpret_cast<float*>(ws + lay.lse);
     float* A = reinterpret_cast<float*>(ws + lay.a);
     float* DL = reinterpret_cast<float*>(ws + lay.dl);
     {
-      const float* Wk = W + (int64_t)(start - 1) * D;
-      const float* Gk = Gamma ? Gamma + (int64_t)(start - 1) * D : nullptr;
-      Phase1Args a1{b.data(), n, R, D, Wk, Gk, Sk, eps, one_source ? nullptr : O,
-                    reinterpret_cast<float*>(ws + lay.m), LSE, nullptr, nullptr, nullptr,
+      const float* Wk = W + (int64_t)start * D;
+      const float* Gk = Gamma ? Gamma + (int64_t)start * D : nullptr;
+      Phase1Args a1{b.data(), n, R, D, Wk, Gk, Sk - 1, eps, one_source ? nullptr : O + tensor_bytes,
+                    reinterpret_cast<float*>(ws + lay.m) + R, LSE + R, nullptr, nullptr, nullptr,
                     lay.gbytes ? ws + lay.g : nullptr};
       TRY(do_phase1(fn, dtype, a1, st));
     }
