@@ -1692,6 +1692,9 @@ __global__ __launch_bounds__(512) void merge_bwd_kernel(MergeBwdParams p) {
 // once (added to), instead of once per query.
 // ---------------------------------------------------------------------------
 constexpr int kP1BwdQ = 8;  // queries per launch (the queries in LDS)
+#ifndef ATTNRES_P1BWD_LATE_MAXN
+#define ATTNRES_P1BWD_LATE_MAXN 2  // sources up to which more than 4 queries prefetch the next row
+#endif
 constexpr int kP1BwdVpl = 2;  // four-element vectors per lane
 constexpr int kP1BwdMaxN = 8;  // sources
 
@@ -1786,22 +1789,46 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
     q[0] = v.x; q[1] = v.y; q[2] = v.z; q[3] = v.w;
   };
 
-  // With few enough sources and queries (PF), the next row's sources and
-  // upstream gradients are loaded while this row's gradients are formed
-  // (the registers of the two rows fit); otherwise each row's loads come
-  // first in that row.
-  constexpr bool PF = NC + SQ <= 10;
-  raw xn[PF ? NC : 1][VPL], dn[PF ? SQ : 1][VPL];
-  auto load_xd = [&](int64_t r, raw (&xs)[PF ? NC : 1][VPL], raw (&ds)[PF ? SQ : 1][VPL]) {
+  // With few enough sources and queries, the next row's sources (PFX) and
+  // upstream gradients (PFD) are loaded while this row's gradients are
+  // formed (the registers of the two rows fit); otherwise each row's loads
+  // come first in that row. With more than 4 queries (LATE), the source
+  // gradients a row adds to are loaded after its row sums instead of with
+  // its sources, which frees their registers for the next row's loads,
+  // issued behind them. With 8 queries that fits up to 4 sources, but from 3
+  // sources the compiler then waits for each query's row scale on its own,
+  // so LATE stops at ATTNRES_P1BWD_LATE_MAXN sources (1..2 measured 0.7%
+  // faster over the stack backward; 3 and 4 keep the loads at the row start).
+  constexpr bool LATE = DQR && NC <= ATTNRES_P1BWD_LATE_MAXN;
+  constexpr bool PFD = NC + SQ <= 10 || LATE;
+  constexpr bool PFX = NC + SQ <= 10 || (LATE && NC + SQ <= 11);
+  constexpr bool PF = PFX || PFD;
+  raw xn[PFX ? NC : 1][VPL], dn[PFD ? SQ : 1][VPL];
+  auto load_xd = [&](int64_t r, raw (&xs)[PFX ? NC : 1][VPL], raw (&ds)[PFD ? SQ : 1][VPL]) {
     #pragma unroll
     for (int c = 0; c < VPL; ++c) {
-      #pragma unroll
-      for (int i = 0; i < (PF ? NC : 1); ++i) xs[i][c] = ld_x(p.src[i], r, c);
-      #pragma unroll
-      for (int j = 0; j < (PF ? SQ : 1); ++j) ds[j][c] = ld_x(p.dh[j], r, c);
+      if constexpr (PFX) {
+        #pragma unroll
+        for (int i = 0; i < NC; ++i) xs[i][c] = ld_x(p.src[i], r, c);
+      }
+      if constexpr (PFD) {
+        #pragma unroll
+        for (int j = 0; j < SQ; ++j) ds[j][c] = ld_x(p.dh[j], r, c);
+      }
     }
   };
   if constexpr (PF) load_xd(blockIdx.x < g.R ? (int64_t)blockIdx.x : 0, xn, dn);
+  if constexpr (LATE) {
+    // as many stores behind the first row's loads as every later row has
+    // behind its prefetch (its gradients'), each to its own 16 bytes of the
+    // sink so none is merged away: the wait for a row's data then counts the
+    // same on the loop's entry and on its back edge, and leaves those stores
+    // in flight
+    static_assert(NC * VPL * 16 <= sizeof(g_store_sink), "one sink slot per store");
+    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+    for (int k = 0; k < NC * VPL; ++k) st16_stream((gchar_t*)g_store_sink + 16 * k, make_uint4(0u, 0u, 0u, 0u));
+  }
 
   int parity = 0;
   for (int64_t row = blockIdx.x; row < g.R; row += gridDim.x, parity ^= 1) {
@@ -1812,22 +1839,17 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
     uint4 dv[NC][VPL];
     #pragma unroll
     for (int c = 0; c < VPL; ++c) {
-      if constexpr (PF) {
-        #pragma unroll
-        for (int i = 0; i < NC; ++i) x[i][c] = xn[PF ? i : 0][c];
-        #pragma unroll
-        for (int j = 0; j < SQ; ++j) d[j][c] = dn[PF ? j : 0][c];
-      } else {
-        #pragma unroll
-        for (int i = 0; i < NC; ++i) x[i][c] = ld_x(p.src[i], row, c);
-        #pragma unroll
-        for (int j = 0; j < SQ; ++j) d[j][c] = ld_x(p.dh[j], row, c);
-      }
       #pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        const u32x4_t v = __builtin_nontemporal_load(
-            reinterpret_cast<const gu32x4_t*>(g_row(p.dV[i], row) + (uint32_t)vec[c] * 16u));
-        dv[i][c] = make_uint4(v.x, v.y, v.z, v.w);
+      for (int i = 0; i < NC; ++i) x[i][c] = PFX ? xn[PFX ? i : 0][c] : ld_x(p.src[i], row, c);
+      #pragma unroll
+      for (int j = 0; j < SQ; ++j) d[j][c] = PFD ? dn[PFD ? j : 0][c] : ld_x(p.dh[j], row, c);
+      if constexpr (!LATE) {
+        #pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          const u32x4_t v = __builtin_nontemporal_load(
+              reinterpret_cast<const gu32x4_t*>(g_row(p.dV[i], row) + (uint32_t)vec[c] * 16u));
+          dv[i][c] = make_uint4(v.x, v.y, v.z, v.w);
+        }
       }
     }
     // lanes past the row's end read vector 0: a zero source there zeroes
@@ -1902,6 +1924,29 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
     // parity, so a wave may write the next row's sums while another still
     // reads these
     __syncthreads();
+    // each query's row scale and log-sum-exp gradient (uniform per query; 1
+    // and 0 where none is given), loaded ahead of the loads issued next, so
+    // waiting for them does not wait for those
+    const int jl = lane >> 3, il = lane & 7;
+    float gs = 1.f, dl = 0.f;
+    #pragma unroll
+    for (int j = 0; j < SQ; ++j) {
+      const float gj = p.dh_scale[j] ? p.dh_scale[j][row] : 1.f;
+      const float dj = p.dlse[j] ? p.dlse[j][row] : 0.f;
+      gs = jl == j ? gj : gs;
+      dl = jl == j ? dj : dl;
+    }
+    if constexpr (LATE) {
+      #pragma unroll
+      for (int c = 0; c < VPL; ++c)
+        #pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          const u32x4_t v = __builtin_nontemporal_load(
+              reinterpret_cast<const gu32x4_t*>(g_row(p.dV[i], row) + (uint32_t)vec[c] * 16u));
+          dv[i][c] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+      __builtin_amdgcn_sched_barrier(0);  // the gradients' loads ahead of the next row's
+    }
     if constexpr (PF) {
       // the next row's sources and upstream gradients (this row again at the
       // end: in bounds, unused)
@@ -1912,7 +1957,6 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
     // 8 j + i takes query j and source i; the softmax over a query's sources
     // is a reduction over its 8-lane group. (Computed as uniform values they
     // would cost every lane the whole table.)
-    const int jl = lane >> 3, il = lane & 7;
     const bool valid = jl < SQ && il < NC;
     float tq = 0.f, tg = 0.f, tv = 0.f;
     if (valid) {
@@ -1922,15 +1966,6 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
         tg += w0[w * NR + (SQ + jl) * NC + il];
         tv += w0[w * NR + 2 * SQ * NC + il];
       }
-    }
-    // the query's row scale and log-sum-exp gradient (uniform per query)
-    float gs = 1.f, dl = 0.f;
-    #pragma unroll
-    for (int j = 0; j < SQ; ++j) {
-      const float gj = p.dh_scale[j] ? p.dh_scale[j][row] : 1.f;
-      const float dj = p.dlse[j] ? p.dlse[j][row] : 0.f;
-      gs = jl == j ? gj : gs;
-      dl = jl == j ? dj : dl;
     }
     const float rl = rsqrtf(tv * g.invD + p.eps);
     const float sc = valid ? tq * rl : -FLT_MAX;
