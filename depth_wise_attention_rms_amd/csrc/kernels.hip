@@ -1988,16 +1988,11 @@ __global__ __launch_bounds__(512) void phase1_bwd_kernel(P1BwdParams p) {
     for (int i = 0; i < NC; ++i) cc[i] = lane_val(ccl, i);
     #pragma unroll
     for (int j = 0; j < SQ; ++j) {
-      // one query's coefficients at a time: the empty asm keeps the compiler
-      // from reading every query's ahead into scalar registers (which then
-      // spill into vector registers)
-      float Alj = Al, Blj = Bl;
-      asm volatile("" : "+v"(Alj), "+v"(Blj));
       float A[NC], B[NC];
       #pragma unroll
       for (int i = 0; i < NC; ++i) {
-        A[i] = lane_val(Alj, 8 * j + i);
-        B[i] = lane_val(Blj, 8 * j + i);
+        A[i] = lane_val(Al, 8 * j + i);
+        B[i] = lane_val(Bl, 8 * j + i);
       }
       launder();
       #pragma unroll
